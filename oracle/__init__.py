@@ -1,0 +1,177 @@
+"""CPU oracle for the SDM forward hot path (Phase 1 and the DW step).
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the benchmark's
+``cpu_baseline`` leg use it; the product path never imports it. It shares no code with the HIP
+implementation: the arithmetic lives in ``sdm_oracle.c`` (plain C, double precision), and this
+module only marshals numpy arrays into it.
+
+Definitions follow the page "sparse_delta_memory/cuda/phase1_cuda.py" (module docstring and the
+Outputs / Records comments) and the DW definition of "sparse_delta_memory/cuda/mover_da2_cuda.py"
+(module docstring). Every floating result is returned in float64.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sdm_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libsdm_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile sdm_oracle.c with gcc into oracle/libsdm_oracle.so (plain -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _ChunkIn(ctypes.Structure):
+    _fields_ = [
+        ("C", ctypes.c_int), ("W", ctypes.c_int), ("R", ctypes.c_int), ("t_valid", ctypes.c_int),
+        ("id_base", ctypes.c_int64),
+        ("k_idx", ctypes.c_void_p), ("q_idx", ctypes.c_void_p), ("k_val", ctypes.c_void_p),
+        ("q_val", ctypes.c_void_p), ("g", ctypes.c_void_p), ("tile_len", ctypes.c_int),
+    ]
+
+
+_OUT_FIELDS = [
+    "log_k", "rex", "cpe", "k_eff", "is_last", "is_only", "pos_k", "log_q", "q_w", "pos_q", "q_last", "q_only",
+    "spay_k", "spay_q", "krec_slot", "krec_sc", "krec_cpe", "tiles_k", "a", "qk", "perm", "repeats",
+]
+
+
+class _ChunkOut(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in _OUT_FIELDS]
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            lib = ctypes.CDLL(build())
+            lib.oracle_phase1_chunk.argtypes = [ctypes.POINTER(_ChunkIn), ctypes.POINTER(_ChunkOut)]
+            lib.oracle_phase1_chunk.restype = ctypes.c_int
+            lib.oracle_dw_slots.argtypes = [ctypes.POINTER(_ChunkIn), ctypes.c_void_p]
+            lib.oracle_dw_slots.restype = ctypes.c_int64
+            lib.oracle_dw_apply.argtypes = [ctypes.POINTER(_ChunkIn), ctypes.c_int, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+            lib.oracle_dw_apply.restype = ctypes.c_int64
+            _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _chunk_in(k_idx, q_idx, k_val, q_val, g, c, P, stream_offset, first_partial, valid_last, tile_len):
+    C, W = k_idx.shape[1], k_idx.shape[2]
+    R = q_idx.shape[2]
+    arrs = (np.ascontiguousarray(k_idx[c], dtype=np.int32), np.ascontiguousarray(q_idx[c], dtype=np.int32),
+            np.ascontiguousarray(k_val[c], dtype=np.float32), np.ascontiguousarray(q_val[c], dtype=np.float32),
+            np.ascontiguousarray(g[c], dtype=np.float32))
+    t_valid = valid_last if c >= first_partial else C
+    s = _ChunkIn(C, W, R, t_valid, (c % P) * stream_offset, *[_ptr(a) for a in arrs], tile_len)
+    return s, arrs
+
+
+def phase1(k_idx, q_idx, k_val, q_val, g, *, P=1, stream_offset=0, first_partial=None, valid_last=None,
+           tile_len=128, chunks=None, threads=1, fields=None):
+    """Phase 1 of the chunks `chunks` (default: all). Arrays are [N, C, W] / [N, C, R] / [N, C].
+
+    Returns a dict of numpy arrays whose first axis runs over the requested chunks. `fields`
+    restricts the outputs computed (default: all of them)."""
+    lib = _load()
+    N, C, W = k_idx.shape
+    R = q_idx.shape[2]
+    if first_partial is None:
+        first_partial = N
+    if valid_last is None:
+        valid_last = C
+    chunks = list(range(N)) if chunks is None else [int(c) for c in chunks]
+    m = len(chunks)
+    nk, nq, n = C * W, C * R, C * (W + R)
+    L = max(int(tile_len), 1)
+    ntk = (nk + L - 1) // L
+    shapes = {
+        "log_k": ((C, W), np.float64), "rex": ((C, W), np.float64), "cpe": ((C, W), np.float64),
+        "k_eff": ((C, W), np.float64), "is_last": ((C, W), np.int8), "is_only": ((C, W), np.int8),
+        "pos_k": ((C, W), np.int32), "log_q": ((C, R), np.float64), "q_w": ((C, R), np.float64),
+        "pos_q": ((C, R), np.int32), "q_last": ((C, R), np.int8), "q_only": ((C, R), np.int8),
+        "spay_k": ((nk,), np.int32), "spay_q": ((nq,), np.int32), "krec_slot": ((nk,), np.int32),
+        "krec_sc": ((nk,), np.float64), "krec_cpe": ((nk,), np.float64), "tiles_k": ((ntk + 1,), np.int32),
+        "a": ((C, C), np.float64), "qk": ((C, C), np.float64), "perm": ((n,), np.int32), "repeats": ((1,), np.int64),
+    }
+    want = set(shapes) if fields is None else set(fields)
+    if "tiles_k" in want:
+        want.add("spay_k")
+    res = {f: np.zeros((m,) + shapes[f][0], dtype=shapes[f][1]) for f in shapes if f in want}
+
+    def run(i):
+        c = chunks[i]
+        cin, keep = _chunk_in(k_idx, q_idx, k_val, q_val, g, c, P, stream_offset, first_partial, valid_last, L)
+        out = _ChunkOut(*[(_ptr(res[f][i]) if f in res else None) for f in _OUT_FIELDS])
+        rc = lib.oracle_phase1_chunk(ctypes.byref(cin), ctypes.byref(out))
+        del keep
+        if rc != 0:
+            raise MemoryError("oracle_phase1_chunk failed (%d)" % rc)
+
+    if threads > 1 and m > 1:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(run, range(m)))
+    else:
+        for i in range(m):
+            run(i)
+    if "repeats" in res:
+        res["repeats"] = res["repeats"][:, 0]
+    return res
+
+
+def dw_slots(k_idx, q_idx, k_val, q_val, g, c, *, P=1, stream_offset=0, first_partial=None, valid_last=None):
+    """Absolute slots of chunk c's valid K groups, ascending (int64)."""
+    lib = _load()
+    N, C, _ = k_idx.shape
+    first_partial = N if first_partial is None else first_partial
+    valid_last = C if valid_last is None else valid_last
+    cin, keep = _chunk_in(k_idx, q_idx, k_val, q_val, g, c, P, stream_offset, first_partial, valid_last, 1)
+    cnt = lib.oracle_dw_slots(ctypes.byref(cin), None)
+    if cnt < 0:
+        raise MemoryError("oracle_dw_slots failed")
+    out = np.zeros(max(cnt, 1), dtype=np.int64)
+    lib.oracle_dw_slots(ctypes.byref(cin), _ptr(out))
+    del keep
+    return out[:cnt]
+
+
+def dw_apply(k_idx, q_idx, k_val, q_val, g, c, dv_rows, base_rows, *, P=1, stream_offset=0, first_partial=None,
+             valid_last=None, with_magnitude=False):
+    """New rows of chunk c's valid K groups in float64: base * exp(G) + sum k exp(rex) dv.
+
+    dv_rows: [C, hd] token rows of the chunk; base_rows: [groups, hd] pre-step rows in the order of
+    dw_slots. With with_magnitude, also returns the per-element magnitude sum of the terms."""
+    lib = _load()
+    N, C, _ = k_idx.shape
+    first_partial = N if first_partial is None else first_partial
+    valid_last = C if valid_last is None else valid_last
+    dv = np.ascontiguousarray(dv_rows, dtype=np.float64)
+    base = np.ascontiguousarray(base_rows, dtype=np.float64)
+    hd = dv.shape[1]
+    out = np.zeros_like(base)
+    mag = np.zeros_like(base) if with_magnitude else None
+    cin, keep = _chunk_in(k_idx, q_idx, k_val, q_val, g, c, P, stream_offset, first_partial, valid_last, 1)
+    cnt = lib.oracle_dw_apply(ctypes.byref(cin), hd, _ptr(dv), _ptr(base), _ptr(out), _ptr(mag))
+    del keep
+    if cnt != base.shape[0]:
+        raise ValueError("dw_apply: %d groups, %d base rows" % (cnt, base.shape[0]))
+    return (out, mag) if with_magnitude else out
