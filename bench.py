@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the SDM forward hot path on one MI355X.
+
+One step = the whole hot path over one batch: Phase 1 of every chunk of the workload (sort, scans,
+records, tile bounds, A / QK) followed by every DW step of the workload, all enqueued on one stream
+with the inputs already in HBM. `value` is the step's throughput in Phase-1 K+Q entries per
+second; the DW bank GB/s and per-kernel HBM-roofline fractions ride along.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I] [--no-cpu-baseline]
+
+The default workload is the uniform bf16 shape (index 1); the others are parity cases that can
+also be timed with --workload. Prints ONE JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_BYTES = 8.0e12
+METRIC = "Phase-1 K+Q entries/sec and DW bank GB/s (fraction of HBM roofline), 1 GPU"
+KERNEL_SOURCES = ["phase1.hip", "dw.hip", "sdm_device.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def p1_main_bytes(C, W, R):
+    """Algorithmic bytes of the sort/scan kernel per chunk: per K entry id 4 + value 4 read and
+    log_k, rex, cpe, k_eff, pos_k, spay_k 4 each + is_last, is_only 1 each + krec 16 written
+    (50 B); per Q entry 8 read and log_q, q_w, pos_q, spay_q 4 each + 2 flag bytes (26 B); 4 B of
+    gate per token."""
+    return C * W * 50 + C * R * 26 + 4 * C
+
+
+def p1_pairs_bytes(C):
+    """The dense [C, C] float32 A and QK written per chunk."""
+    return 8 * C * C
+
+
+def dw_bytes(groups, C, W, hd, bank_es, dv_es):
+    """One DW launch (P chunks): base row read + new row written per valid group, each token row
+    read once, 16 B of record per K entry. Returns (total, bank part)."""
+    bank = 2 * groups * hd * bank_es
+    return bank + C * hd * dv_es + 16 * C * W, bank
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_delta_memory_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload_name, kernel):
+    """HBM bytes per launch of `kernel` from profiles/traffic_<workload>.txt (rocprofv3 FETCH_SIZE and
+    WRITE_SIZE, scaled by a copy-kernel calibration), or None when missing or taken on other sources."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload_name)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("src_sha") != source_digest():
+        return None
+    key = "bytes_per_launch." + kernel
+    return float(vals[key]) if key in vals else None
+
+
+def cpu_baseline(wl, bank0, n_chunks_target_s=15.0):
+    """The oracle, as it stands, on a bounded sample of the same workload (host cores)."""
+    import torch
+
+    import oracle
+
+    sh = wl.shape
+    threads = os.cpu_count() or 1
+    n = sh.C * (sh.W + sh.R)
+    # Calibrate on one chunk, then size the sample for about n_chunks_target_s seconds.
+    t0 = time.perf_counter()
+    oracle.phase1(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, P=wl.P, stream_offset=wl.stream_offset,
+                  first_partial=wl.first_partial, valid_last=wl.valid_last, chunks=[0])
+    one = max(time.perf_counter() - t0, 1e-4)
+    m = int(min(wl.N, max(threads, n_chunks_target_s * threads / one / 2)))
+    chunks = list(range(m))
+    t0 = time.perf_counter()
+    oracle.phase1(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, P=wl.P, stream_offset=wl.stream_offset,
+                  first_partial=wl.first_partial, valid_last=wl.valid_last, chunks=chunks, threads=threads)
+    t_p1 = time.perf_counter() - t0
+    # DW of the same chunks from the initial bank (rows gathered outside the timed region).
+    jobs = []
+    dv = wl.dv.reshape(-1, sh.hd)
+    for c in chunks:
+        slots = oracle.dw_slots(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, c, P=wl.P, stream_offset=sh.S,
+                                first_partial=wl.first_partial, valid_last=wl.valid_last)
+        base = bank0.index_select(0, torch.as_tensor(slots, device=bank0.device)).float().cpu().numpy()
+        jobs.append((c, base.astype(np.float64), dv[c * sh.C:(c + 1) * sh.C].astype(np.float64)))
+    from concurrent.futures import ThreadPoolExecutor
+
+    def run(job):
+        c, base, rows = job
+        oracle.dw_apply(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, c, rows, base, P=wl.P, stream_offset=sh.S,
+                        first_partial=wl.first_partial, valid_last=wl.valid_last)
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(run, jobs))
+    t_dw = time.perf_counter() - t0
+    return {
+        "value": m * n / (t_p1 + t_dw), "unit": "entries/s", "cores": threads, "kind": "oracle",
+        "sample": "%d of %d chunks (Phase 1 + the DW of the same chunks from the initial bank); "
+                  "phase1 %.2f s, dw %.2f s" % (m, wl.N, t_p1, t_dw),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (the hot path has no multi-GPU part); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_delta_memory_amd as sdm
+    from sparse_delta_memory_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.make(args.workload)
+    sh = wl.shape
+    log("workload %d %s: N=%d chunks, n=%d entries/chunk" % (args.workload, sh.name, wl.N, sh.C * (sh.W + sh.R)))
+    shape = sdm.make_shape(wl.N, sh.C, sh.W, sh.R, P=sh.P, key_bits=sh.key_bits, stream_offset=sh.S,
+                           first_partial=wl.first_partial, valid_last=wl.valid_last, tile_len=128)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    ins = dict(k_idx=t(wl.k_idx), q_idx=t(wl.q_idx), k_val=t(wl.k_val), q_val=t(wl.q_val), g=t(wl.g))
+    dv = t(wl.dv.reshape(-1, sh.hd))
+    if sh.dv_dtype == "bf16":
+        dv = dv.to(torch.bfloat16)
+    out = sdm.alloc_phase1_outputs(shape, device=dev)
+    ws = torch.empty(sdm.phase1_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    bank = W.make_bank(wl, dev)
+    bank0 = bank.clone() if not args.no_cpu_baseline else None
+    stream = torch.cuda.current_stream(dev)
+    P, C = sh.P, sh.C
+
+    def new_events(k):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
+        for e in evs:
+            e.record(stream)
+        return evs
+
+    torch.cuda.synchronize()
+
+    def step(p1_events=None, dw_events=None):
+        handles = None
+        if p1_events is not None:
+            import ctypes
+
+            arr = (ctypes.c_void_p * 3)(*[e.cuda_event for e in p1_events])
+            handles = ctypes.cast(arr, ctypes.c_void_p).value
+            step._keep = arr
+        sdm.phase1(shape, out=out, workspace=ws, events=handles, **ins)
+        if dw_events is not None:
+            dw_events[0].record(stream)
+        for ti in range(wl.steps):
+            sdm.dw_step(bank, dv, out["krec"], shape, ti, dv_step_rows=P * C)
+        if dw_events is not None:
+            dw_events[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    p1_ev = [new_events(3) for _ in range(args.steps)]
+    dw_ev = [new_events(2) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(p1_ev[k], dw_ev[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_main = float(np.mean([e[0].elapsed_time(e[1]) for e in p1_ev]))
+    ms_pairs = float(np.mean([e[1].elapsed_time(e[2]) for e in p1_ev]))
+    ms_dw_all = float(np.mean([e[0].elapsed_time(e[1]) for e in dw_ev]))
+    ms_dw = ms_dw_all / wl.steps
+
+    # Valid groups per step (for the DW's algorithmic bytes), from the records' FIRST flags.
+    first = (out["krec"][..., 0] & (W_FIRST | W_INVALID)) == W_FIRST
+    groups_per_chunk = first.sum(dim=1).cpu().numpy().astype(np.int64)
+    groups_per_step = groups_per_chunk.reshape(wl.steps, P).sum(axis=1)
+    bank_es = 2 if sh.bank_dtype == "bf16" else 4
+    dv_es = 2 if sh.dv_dtype == "bf16" else 4
+    dw_tot = [dw_bytes(int(gs), C * P, sh.W, sh.hd, bank_es, dv_es) for gs in groups_per_step]
+    dw_launch_bytes = float(np.mean([d[0] for d in dw_tot]))
+    dw_bank_bytes = float(np.mean([d[1] for d in dw_tot]))
+    main_bytes = wl.N * p1_main_bytes(sh.C, sh.W, sh.R)
+    pairs_bytes = wl.N * p1_pairs_bytes(sh.C)
+    kernels = {
+        "p1_main_kernel": (main_bytes, ms_main),
+        "p1_pairs_kernel": (pairs_bytes, ms_pairs),
+        "dw_kernel": (dw_launch_bytes, ms_dw),
+    }
+    per = {}
+    for name, (b, ms) in kernels.items():
+        ach = b / (ms * 1e-3)
+        per[name] = {"bytes_per_launch": b, "ms_per_launch": ms, "GBps": ach / 1e9, "frac": ach / HBM_PEAK_BYTES,
+                     "launches_per_step": wl.steps if name == "dw_kernel" else 1}
+    dom = max(per, key=lambda k: per[k]["ms_per_launch"] * per[k]["launches_per_step"])
+    traffic = read_traffic(sh.name, dom)
+    entries = wl.N * sh.C * (sh.W + sh.R)
+    ms_step = wall / args.steps * 1e3
+    res = {
+        "metric": METRIC,
+        "value": entries / (ms_step * 1e-3),
+        "unit": "entries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded generators; no dataset)",
+        "config": {
+            "workload": "%s: P=%d T=%d C=%d W=%d R=%d S=%d hd=%d bank %s dv %s slots %s" % (
+                sh.name, sh.P, sh.T, sh.C, sh.W, sh.R, sh.S, sh.hd, sh.bank_dtype, sh.dv_dtype, sh.slots),
+            "chunks": wl.N, "dw_steps": wl.steps, "global_batch": wl.N * sh.C, "seq_len": sh.T,
+            "parallelism": "single GPU",
+        },
+        "phase1_entries_per_s": entries / ((ms_main + ms_pairs) * 1e-3),
+        "phase1_hbm_frac": (main_bytes + pairs_bytes) / ((ms_main + ms_pairs) * 1e-3) / HBM_PEAK_BYTES,
+        "dw_bank_GBps": dw_bank_bytes / (ms_dw * 1e-3) / 1e9,
+        "dw_hbm_frac": dw_launch_bytes / (ms_dw * 1e-3) / HBM_PEAK_BYTES,
+        "kernels": per,
+        "roofline": {
+            "kernel": dom, "bound": "hbm", "achieved": per[dom]["GBps"], "peak": HBM_PEAK_BYTES / 1e9, "unit": "GB/s",
+            "frac": per[dom]["frac"], "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on host cores)...")
+        res["cpu_baseline"] = cpu_baseline(wl, bank0)
+    print(json.dumps(res), flush=True)
+
+
+W_FIRST = -(1 << 31)      # bit 31 of the int32 record element
+W_INVALID = 1 << 17
+
+if __name__ == "__main__":
+    main()

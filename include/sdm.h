@@ -1,0 +1,181 @@
+/*
+ * sdm.h - C ABI of the MI355X (gfx950) forward hot path of the chunked sparse-delta-memory
+ * (SDM) recurrence: Phase 1 (the memory-independent per-chunk quantities) and the DW
+ * decay-and-write step.
+ *
+ * Conventions shared by every entry point
+ *  - All array arguments are DEVICE pointers owned by the caller. The library allocates no
+ *    memory, keeps no pointer after returning and never synchronizes: work is enqueued on the
+ *    caller's stream `st` (hipStream_t; 0 = the null stream).
+ *  - The shape and argument checks run on the host before anything is enqueued. Any non-zero
+ *    status means nothing was launched; sdm_last_error() then returns a message naming the
+ *    failed check (thread-local, valid until the next call on that thread).
+ *  - Device code never traps on inputs that pass the checks. Slot ids outside the ranges
+ *    stated below are the caller's contract (results are unspecified, memory stays in bounds
+ *    for Phase 1; DW writes the rows the records name).
+ *  - Outputs are bitwise reproducible run to run for fixed inputs and shapes: sorts are
+ *    stable, scans combine in a fixed tree, every output element has one writer, and no
+ *    floating-point atomics are used.
+ *
+ * Notation (page "sparse_delta_memory/cuda/phase1_cuda.py", module docstring and the Outputs /
+ * Records comments): a chunk c holds C tokens; token t writes W slots (K entries, lanes 0..W-1)
+ * and reads R slots (Q entries). Entry r = t (W + R) + j of a chunk is K lane j when j < W and
+ * Q lane j - W otherwise. Chunk c is step c / P of stream c % P; stream p's local slot of an
+ * absolute id is id - p * stream_offset. Tokens t >= valid_last of chunks c >= first_partial
+ * are invalid (masked): their entries are sorted after all valid entries, in entry order, each
+ * as a group of its own, and their values / gates / token rows are never read.
+ */
+#ifndef SDM_H
+#define SDM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sdm_status {
+    SDM_OK = 0,
+    SDM_EINVAL = -1,       /* a required pointer is NULL, or an argument is out of range */
+    SDM_ESHAPE = -2,       /* shape outside the supported ranges (C, W, R, row length, ti) */
+    SDM_EALIGN = -3,       /* a pointer is not aligned as required */
+    SDM_EUNSUPPORTED = -4, /* a valid shape this build does not implement */
+    SDM_EWORKSPACE = -5,   /* workspace missing or smaller than sdm_phase1_workspace() */
+    SDM_EHIP = -6          /* a HIP launch or attribute call failed */
+} sdm_status;
+
+typedef enum sdm_dtype {
+    SDM_F32 = 0,
+    SDM_BF16 = 1
+} sdm_dtype;
+
+/* Shape of one Phase-1 call over N chunks. */
+typedef struct sdm_p1_shape {
+    int32_t N;              /* chunks, >= 0 */
+    int32_t C;              /* tokens per chunk, 1..256 */
+    int32_t W;              /* K entries per token, 1..256 */
+    int32_t R;              /* Q entries per token, 1..256 */
+    int32_t P;              /* independent streams, >= 1 */
+    int32_t key_bits;       /* every valid local slot is < 2^key_bits; 1..30 */
+    int64_t stream_offset;  /* slot offset between streams (>= 0) */
+    int32_t first_partial;  /* chunks c >= first_partial are ragged (0..N; N: none) */
+    int32_t valid_last;     /* valid tokens of a ragged chunk, 0..C */
+    int32_t tile_len;       /* L of the tile bounds tiles_k, >= 1 */
+} sdm_p1_shape;
+
+/*
+ * Phase-1 buffers. Entry-order fields are [N, C, W] (K) or [N, C, R] (Q), row-major.
+ * Sorted-kind fields follow the chunk's sorted order restricted to one kind ("K-only row",
+ * length C*W; "Q-only row", length C*R), padding (invalid) entries included.
+ * A NULL output pointer skips that output, except spay_k, krec and tiles_k, which the DW step
+ * consumes and which are always required.
+ */
+typedef struct sdm_p1_io {
+    /* inputs */
+    const int32_t* k_idx;   /* [N, C, W] absolute slot ids of the writes */
+    const int32_t* q_idx;   /* [N, C, R] absolute slot ids of the reads */
+    const float* k_val;     /* [N, C, W] write values */
+    const float* q_val;     /* [N, C, R] read values */
+    const float* g;         /* [N, C] per-token gates (log decays) */
+    /* entry-order outputs */
+    float* log_k;           /* [N, C, W] log-cumsum of the slot's gates up to and including the entry */
+    float* rex;             /* [N, C, W] sum of the slot's later gates in the chunk */
+    float* cpe;             /* [N, C, W] exp(total gate of the slot in the chunk) */
+    float* k_eff;           /* [N, C, W] k_val * exp(log_k) */
+    int8_t* is_last;        /* [N, C, W] last valid K entry of its slot */
+    int8_t* is_only;        /* [N, C, W] only valid K entry of its slot */
+    int32_t* pos_k;         /* [N, C, W] sorted position | min(after,127)<<17 | min(peers,127)<<24 */
+    float* log_q;           /* [N, C, R] log-cumsum seen by the read (its own token's writes included) */
+    float* q_w;             /* [N, C, R] q_val * exp(log_q) */
+    int32_t* pos_q;         /* [N, C, R] as pos_k, peers counted among valid Q entries */
+    int8_t* q_last;         /* [N, C, R] last valid Q entry of its slot */
+    int8_t* q_only;         /* [N, C, R] only valid Q entry of its slot */
+    /* sorted-kind outputs */
+    int32_t* spay_k;        /* [N, C*W] K-only row elements: entry bits 0-17 (lane 0-7, Q bit 8, token
+                               9-16, invalid 17), distance to the kind's first entry of the group in
+                               bits 18-29 (saturating at 4095), LAST bit 30, FIRST bit 31; padding is
+                               FIRST|LAST. REQUIRED. */
+    int32_t* spay_q;        /* [N, C*R] Q-only row elements, same layout */
+    int32_t* krec;          /* [N, C*W, 4] {spay_k element, absolute slot, f32 bits of k*exp(rex),
+                               f32 bits of cpe}; padding {element, 0, +0, 1.0f}. 16-byte aligned.
+                               REQUIRED. */
+    int32_t* tiles_k;       /* [N, ceil(C*W/L) + 1]: first index >= t*L of the K-only row holding a
+                               FIRST (C*W if none), then C*W. REQUIRED. */
+    float* a;               /* [N, C, C] A[i,j] (j < i), zeros elsewhere */
+    float* qk;              /* [N, C, C] QK[i,j] (j <= i), zeros elsewhere */
+    int32_t* repeats;       /* [N] per chunk: K entries whose group predecessor is a K entry of the
+                               same token (their gate is not applied again) */
+    void* workspace;        /* device scratch, 16-byte aligned, >= sdm_phase1_workspace(shape) */
+    size_t workspace_bytes;
+    hipEvent_t* events;     /* optional (NULL: none): 3 caller-created events, recorded on st before the
+                               sort/scan kernel, between it and the pair kernel, and after the pair kernel */
+} sdm_p1_io;
+
+/*
+ * Device workspace bytes one sdm_phase1 call needs (sorted-order pair records and the inverse
+ * permutation of every chunk). Returns 0 for a shape sdm_phase1 would refuse.
+ */
+size_t sdm_phase1_workspace(const sdm_p1_shape* shape);
+
+/*
+ * Phase 1 of N chunks (page "sparse_delta_memory/cuda/phase1_cuda.py": module docstring for the
+ * quantities; p1_keys_zw_kernel for keys and payloads; p1_scan_kernel for groups, repeats, packed
+ * positions, kind rows, records and tile bounds; p1_pairs_kernel's comment for A and QK).
+ *
+ * Per chunk: entries are sorted stably by local slot (invalid entries last, in entry order); a
+ * group is a run of valid entries with one slot. A valid K entry contributes its token's gate g,
+ * except a repeat (its group predecessor is a K entry of the same token), which contributes 0.
+ * log_k / log_q are the inclusive per-group cumsums of these contributions, rex the sum after the
+ * entry, cpe = exp(group total). A[i,j] sums k_e k_f exp(log_k_e - log_k_f) over K entries e of
+ * token i and earlier K entries f of token j != i in the same group; QK[i,j] sums
+ * q_e k_f exp(log_q_e - log_k_f) over Q entries e of token i and earlier K entries f of token j.
+ * Invalid entries: log 0, rex 0, cpe 1, k_eff / q_w 0, flags 0, pos = sorted position.
+ *
+ * Requirements: C*(W+R) <= 16384 (longer rows: SDM_EUNSUPPORTED); 4-byte aligned inputs;
+ * krec 16-byte aligned; for P > 1 every local slot of a stream is < stream_offset.
+ * Floating outputs agree with the exact (real-arithmetic) values within
+ * max(1e-5 |value|, 1e-6); integer outputs are exact.
+ */
+sdm_status sdm_phase1(const sdm_p1_shape* shape, const sdm_p1_io* io, hipStream_t st);
+
+/* One DW step: the chunks ti*P .. ti*P + P - 1 of the Phase-1 records. */
+typedef struct sdm_dw_io {
+    void* bank;             /* [rows, hd] SDM_F32 or SDM_BF16 bank, updated IN PLACE; 16-byte aligned */
+    int32_t bank_dtype;     /* sdm_dtype */
+    int64_t rows;           /* bank rows; every record slot is < rows */
+    int32_t hd;             /* row width, multiple of 4, 4..4096 */
+    const void* dv;         /* token rows: row (ti * dv_step_rows + p * C + t) of [*, hd]; 16-byte aligned */
+    int32_t dv_dtype;       /* sdm_dtype (bf16 rows are widened exactly) */
+    int64_t dv_step_rows;   /* rows between steps in dv (P*C when every step is stored, 0 for one step) */
+    int64_t dv_rows;        /* rows in dv; ti * dv_step_rows + P * C <= dv_rows */
+    const int32_t* krec;    /* [N, C*W, 4] records from sdm_phase1 */
+    int32_t P, C, W, N;     /* the Phase-1 shape of krec */
+} sdm_dw_io;
+
+/*
+ * DW decay-and-write (page "sparse_delta_memory/cuda/mover_da2_cuda.py", module docstring; bit
+ * contract of "sparse_delta_memory/cuda/mover_fx_cuda.py", module docstring): for every valid
+ * group of the K-only rows of chunks ti*P + p (p < P), in sorted order,
+ *   acc = fma(sc_m, dv[token_m], acc) over the members from +0,
+ *   bank[slot] = fma(bank[slot], cpe_last, acc)  (bf16 bank: rounded to nearest even).
+ * Rows of slots without a valid group are not touched. Within one call every slot has at most
+ * one writer (stream slot ranges must not overlap). bank must not alias dv or krec.
+ * Requires (ti + 1) * P <= N and ti * dv_step_rows + P * C <= dv_rows. A record whose slot is
+ * >= rows is skipped (its group writes nothing).
+ */
+sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st);
+
+/* Static text for a status code. */
+const char* sdm_status_string(sdm_status s);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* sdm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDM_H */

@@ -1,0 +1,105 @@
+"""MI355X (gfx950) forward hot path of the chunked sparse-delta-memory (SDM) recurrence.
+
+Python binding of the C ABI in include/sdm.h. Everything here is argument marshalling: torch
+provides device memory and the current stream; every step of the path runs in the HIP kernels of
+libsdm_amd.so. There is no CPU fallback: without the built library every call raises.
+
+    shape = P1Shape(N=..., C=..., W=..., R=..., P=..., key_bits=..., stream_offset=...)
+    out = phase1(shape, k_idx, q_idx, k_val, q_val, g)          # dict of device tensors
+    dw_step(bank, dv, out["krec"], shape, ti, dv_step_rows=P*C)  # bank updated in place
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+from . import _lib
+from ._lib import P1IO, P1Shape, SdmError  # noqa: F401
+
+__all__ = ["P1Shape", "phase1", "phase1_workspace_bytes", "alloc_phase1_outputs", "dw_step", "SdmError",
+           "make_shape"]
+
+
+def make_shape(N, C, W, R, P=1, key_bits=16, stream_offset=0, first_partial=None, valid_last=None, tile_len=128):
+    return P1Shape(int(N), int(C), int(W), int(R), int(P), int(key_bits), int(stream_offset),
+                   int(N if first_partial is None else first_partial), int(C if valid_last is None else valid_last),
+                   int(tile_len))
+
+
+def phase1_workspace_bytes(shape: P1Shape) -> int:
+    return int(_lib.load().sdm_phase1_workspace(ctypes.byref(shape)))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def alloc_phase1_outputs(shape: P1Shape, device="cuda", fields=None):
+    """Device tensors for the Phase-1 outputs (all of them, or `fields` plus the required ones)."""
+    import torch
+
+    N, C, W, R, L = shape.N, shape.C, shape.W, shape.R, shape.tile_len
+    ntk = (C * W + L - 1) // L
+    spec = {
+        "log_k": ((N, C, W), torch.float32), "rex": ((N, C, W), torch.float32), "cpe": ((N, C, W), torch.float32),
+        "k_eff": ((N, C, W), torch.float32), "is_last": ((N, C, W), torch.int8), "is_only": ((N, C, W), torch.int8),
+        "pos_k": ((N, C, W), torch.int32), "log_q": ((N, C, R), torch.float32), "q_w": ((N, C, R), torch.float32),
+        "pos_q": ((N, C, R), torch.int32), "q_last": ((N, C, R), torch.int8), "q_only": ((N, C, R), torch.int8),
+        "spay_k": ((N, C * W), torch.int32), "spay_q": ((N, C * R), torch.int32),
+        "krec": ((N, C * W, 4), torch.int32), "tiles_k": ((N, ntk + 1), torch.int32),
+        "a": ((N, C, C), torch.float32), "qk": ((N, C, C), torch.float32), "repeats": ((N,), torch.int32),
+    }
+    want = set(spec) if fields is None else set(fields) | {"spay_k", "krec", "tiles_k"}
+    return {k: torch.empty(s, dtype=dt, device=device) for k, (s, dt) in spec.items() if k in want}
+
+
+def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=None, stream=None, events=None):
+    """Enqueue Phase 1 of shape.N chunks on the current (or given) stream; returns the outputs.
+
+    Inputs are contiguous device tensors: k_idx [N,C,W] int32, q_idx [N,C,R] int32, k_val / q_val
+    float32 of the same shapes, g [N,C] float32. `out` is a dict from alloc_phase1_outputs (a
+    missing key skips that optional output)."""
+    import torch
+
+    lib = _lib.load()
+    if out is None:
+        out = alloc_phase1_outputs(shape, device=k_idx.device)
+    need = phase1_workspace_bytes(shape)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=k_idx.device)
+    io = P1IO()
+    for name, t in (("k_idx", k_idx), ("q_idx", q_idx), ("k_val", k_val), ("q_val", q_val), ("g", g)):
+        setattr(io, name, _ptr(t))
+    for name in _lib.P1_IO_FIELDS[5:]:
+        setattr(io, name, _ptr(out.get(name)))
+    io.workspace = workspace.data_ptr()
+    io.workspace_bytes = workspace.numel() * workspace.element_size()
+    io.events = events  # None, or the address of 3 hipEvent_t handles
+    st = torch.cuda.current_stream(k_idx.device) if stream is None else stream
+    _lib.check(lib.sdm_phase1(ctypes.byref(shape), ctypes.byref(io), ctypes.c_void_p(st.cuda_stream)))
+    return out
+
+
+def dw_step(bank, dv, krec, shape: P1Shape, ti: int, dv_step_rows: int, stream=None):
+    """Enqueue the DW step `ti` (chunks ti*P .. ti*P+P-1) on the current (or given) stream.
+
+    bank [rows, hd] float32 or bfloat16 (updated in place); dv [*, hd] float32 or bfloat16 token rows,
+    row ti*dv_step_rows + p*C + t; krec from phase1."""
+    import torch
+
+    lib = _lib.load()
+    io = _lib.DwIO()
+    io.bank = bank.data_ptr()
+    io.bank_dtype = _lib.SDM_BF16 if bank.dtype == torch.bfloat16 else _lib.SDM_F32
+    io.rows = bank.shape[0]
+    io.hd = bank.shape[1]
+    io.dv = dv.data_ptr()
+    io.dv_dtype = _lib.SDM_BF16 if dv.dtype == torch.bfloat16 else _lib.SDM_F32
+    io.dv_step_rows = int(dv_step_rows)
+    io.dv_rows = dv.shape[0]
+    io.krec = krec.data_ptr()
+    io.P, io.C, io.W, io.N = shape.P, shape.C, shape.W, shape.N
+    if bank.dtype not in (torch.float32, torch.bfloat16) or dv.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("dw_step: bank and dv must be float32 or bfloat16")
+    st = torch.cuda.current_stream(bank.device) if stream is None else stream
+    _lib.check(lib.sdm_dw_step(ctypes.byref(io), int(ti), ctypes.c_void_p(st.cuda_stream)))

@@ -1,0 +1,96 @@
+"""ctypes view of the C ABI declared in include/sdm.h (libsdm_amd.so next to this file)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsdm_amd.so")
+
+SDM_OK = 0
+SDM_EINVAL = -1
+SDM_ESHAPE = -2
+SDM_EALIGN = -3
+SDM_EUNSUPPORTED = -4
+SDM_EWORKSPACE = -5
+SDM_EHIP = -6
+SDM_F32 = 0
+SDM_BF16 = 1
+
+
+class P1Shape(ctypes.Structure):
+    _fields_ = [
+        ("N", ctypes.c_int32), ("C", ctypes.c_int32), ("W", ctypes.c_int32), ("R", ctypes.c_int32),
+        ("P", ctypes.c_int32), ("key_bits", ctypes.c_int32), ("stream_offset", ctypes.c_int64),
+        ("first_partial", ctypes.c_int32), ("valid_last", ctypes.c_int32), ("tile_len", ctypes.c_int32),
+    ]
+
+
+P1_IO_FIELDS = [
+    "k_idx", "q_idx", "k_val", "q_val", "g",
+    "log_k", "rex", "cpe", "k_eff", "is_last", "is_only", "pos_k",
+    "log_q", "q_w", "pos_q", "q_last", "q_only",
+    "spay_k", "spay_q", "krec", "tiles_k", "a", "qk", "repeats",
+]
+
+
+class P1IO(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in P1_IO_FIELDS] + [
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t), ("events", ctypes.c_void_p)]
+
+
+class DwIO(ctypes.Structure):
+    _fields_ = [
+        ("bank", ctypes.c_void_p), ("bank_dtype", ctypes.c_int32), ("rows", ctypes.c_int64),
+        ("hd", ctypes.c_int32), ("dv", ctypes.c_void_p), ("dv_dtype", ctypes.c_int32),
+        ("dv_step_rows", ctypes.c_int64), ("dv_rows", ctypes.c_int64), ("krec", ctypes.c_void_p),
+        ("P", ctypes.c_int32), ("C", ctypes.c_int32), ("W", ctypes.c_int32), ("N", ctypes.c_int32),
+    ]
+
+
+EXPORTS = ["sdm_phase1_workspace", "sdm_phase1", "sdm_dw_step", "sdm_status_string", "sdm_last_error"]
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libsdm_amd.so; raises if it has not been built (no fallback path exists)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        # torch first: its HIP runtime (same SONAME) is then the one this library binds to, so
+        # torch's streams and device pointers are valid here.
+        import torch  # noqa: F401
+
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libsdm_amd.so is not built (run `python -m sparse_delta_memory_amd.build`); "
+                "the SDM hot path has no CPU fallback")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.sdm_phase1_workspace.argtypes = [ctypes.POINTER(P1Shape)]
+        lib.sdm_phase1_workspace.restype = ctypes.c_size_t
+        lib.sdm_phase1.argtypes = [ctypes.POINTER(P1Shape), ctypes.POINTER(P1IO), ctypes.c_void_p]
+        lib.sdm_phase1.restype = ctypes.c_int
+        lib.sdm_dw_step.argtypes = [ctypes.POINTER(DwIO), ctypes.c_int64, ctypes.c_void_p]
+        lib.sdm_dw_step.restype = ctypes.c_int
+        lib.sdm_status_string.argtypes = [ctypes.c_int]
+        lib.sdm_status_string.restype = ctypes.c_char_p
+        lib.sdm_last_error.argtypes = []
+        lib.sdm_last_error.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+class SdmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s (status %d): %s" % (load().sdm_status_string(status).decode(), status, message))
+        self.status = status
+
+
+def check(status: int) -> None:
+    if status != SDM_OK:
+        raise SdmError(status, load().sdm_last_error().decode())

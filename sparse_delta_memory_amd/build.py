@@ -1,0 +1,55 @@
+"""Ahead-of-time build of the gfx950 library libsdm_amd.so (hipcc, no JIT).
+
+`python -m sparse_delta_memory_amd.build` compiles every source under csrc/ into one shared
+library next to this file. Device code is built for gfx950 only, with FP contraction off (only
+explicit fmaf calls fuse) and the packed-FP32 instructions disabled.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libsdm_amd.so")
+SOURCES = ["api.cpp", "phase1.hip", "dw.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def command(out: str = LIB) -> list[str]:
+    return [
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wno-unused-command-line-argument",
+        "-I", INCLUDE, "-I", CSRC, "-o", out,
+    ] + [os.path.join(CSRC, s) for s in SOURCES]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library (always; the caller decides when). Returns its path."""
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building %s" % LIB)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,160 @@
+// C ABI of the SDM forward hot path: argument checks on the host, then the kernel launches.
+// Preconditions follow the pages' host launchers ("sparse_delta_memory/cuda/mover_da2_cuda.py",
+// da2_dw: C <= 256, 16-byte rows and alignment; "sparse_delta_memory/cuda/phase1_cuda.py": 8-bit
+// token and lane fields, 17-bit positions) restated for this implementation.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+#include <string>
+
+#include "sdm.h"
+#include "sdm_launch.hpp"
+
+namespace sdm {
+int dw_cols_per_lane(int hd);
+}
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sdm_status fail(sdm_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+sdm_status check_p1_shape(const sdm_p1_shape* s) {
+    if (s == nullptr) return fail(SDM_EINVAL, "sdm_phase1: shape is NULL");
+    if (s->N < 0) return fail(SDM_ESHAPE, "sdm_phase1: N = %d < 0", s->N);
+    if (s->C < 1 || s->C > 256) return fail(SDM_ESHAPE, "sdm_phase1: C = %d outside 1..256", s->C);
+    if (s->W < 1 || s->W > 256) return fail(SDM_ESHAPE, "sdm_phase1: W = %d outside 1..256", s->W);
+    if (s->R < 1 || s->R > 256) return fail(SDM_ESHAPE, "sdm_phase1: R = %d outside 1..256", s->R);
+    if (s->P < 1) return fail(SDM_ESHAPE, "sdm_phase1: P = %d < 1", s->P);
+    if (s->key_bits < 1 || s->key_bits > 30) return fail(SDM_EINVAL, "sdm_phase1: key_bits = %d outside 1..30", s->key_bits);
+    if (s->stream_offset < 0) return fail(SDM_EINVAL, "sdm_phase1: stream_offset < 0");
+    if (s->first_partial < 0 || s->first_partial > s->N)
+        return fail(SDM_EINVAL, "sdm_phase1: first_partial = %d outside 0..N", s->first_partial);
+    if (s->valid_last < 0 || s->valid_last > s->C)
+        return fail(SDM_EINVAL, "sdm_phase1: valid_last = %d outside 0..C", s->valid_last);
+    if (s->tile_len < 1) return fail(SDM_EINVAL, "sdm_phase1: tile_len = %d < 1", s->tile_len);
+    const int64_t n = static_cast<int64_t>(s->C) * (s->W + s->R);
+    if (n > (1 << 17)) return fail(SDM_ESHAPE, "sdm_phase1: C*(W+R) = %lld > 2^17", static_cast<long long>(n));
+    if (n > sdm::kP1MaxRow)
+        return fail(SDM_EUNSUPPORTED, "sdm_phase1: C*(W+R) = %lld > %d (on-chip row limit of this build)",
+                    static_cast<long long>(n), sdm::kP1MaxRow);
+    return SDM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sdm_status_string(sdm_status s) {
+    switch (s) {
+        case SDM_OK: return "ok";
+        case SDM_EINVAL: return "invalid argument";
+        case SDM_ESHAPE: return "shape outside the supported ranges";
+        case SDM_EALIGN: return "misaligned pointer";
+        case SDM_EUNSUPPORTED: return "shape not implemented by this build";
+        case SDM_EWORKSPACE: return "workspace missing or too small";
+        case SDM_EHIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char* sdm_last_error(void) { return g_last_error.c_str(); }
+
+size_t sdm_phase1_workspace(const sdm_p1_shape* s) {
+    if (check_p1_shape(s) != SDM_OK) return 0;
+    return sdm::p1_workspace_layout(s).total;
+}
+
+sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st) {
+    g_last_error.clear();
+    sdm_status rc = check_p1_shape(s);
+    if (rc != SDM_OK) return rc;
+    if (io == nullptr) return fail(SDM_EINVAL, "sdm_phase1: io is NULL");
+    if (s->N == 0) return SDM_OK;
+    const void* req[] = {io->k_idx, io->q_idx, io->k_val, io->q_val, io->g, io->spay_k, io->krec, io->tiles_k};
+    const char* req_names[] = {"k_idx", "q_idx", "k_val", "q_val", "g", "spay_k", "krec", "tiles_k"};
+    for (int i = 0; i < 8; ++i) {
+        if (req[i] == nullptr) return fail(SDM_EINVAL, "sdm_phase1: %s is NULL", req_names[i]);
+    }
+    const void* a4[] = {io->k_idx, io->q_idx, io->k_val, io->q_val, io->g, io->log_k, io->rex, io->cpe,
+                        io->k_eff, io->pos_k, io->log_q, io->q_w, io->pos_q, io->spay_k, io->spay_q,
+                        io->tiles_k, io->a, io->qk, io->repeats};
+    for (const void* p : a4) {
+        if (!aligned(p, 4)) return fail(SDM_EALIGN, "sdm_phase1: a 4-byte field is misaligned");
+    }
+    if (!aligned(io->krec, 16)) return fail(SDM_EALIGN, "sdm_phase1: krec is not 16-byte aligned");
+    const sdm::P1Workspace ws = sdm::p1_workspace_layout(s);
+    if (io->workspace == nullptr || io->workspace_bytes < ws.total)
+        return fail(SDM_EWORKSPACE, "sdm_phase1: workspace needs %zu bytes, got %zu", ws.total,
+                    io->workspace == nullptr ? size_t(0) : io->workspace_bytes);
+    if (!aligned(io->workspace, 16)) return fail(SDM_EALIGN, "sdm_phase1: workspace is not 16-byte aligned");
+    int dev = 0, lds_max = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+        return fail(SDM_EHIP, "sdm_phase1: no HIP device");
+    const size_t tri = static_cast<size_t>(s->C) * (s->C + 1) / 2 * sizeof(float);
+    if ((io->a != nullptr || io->qk != nullptr) && tri > static_cast<size_t>(lds_max))
+        return fail(SDM_EUNSUPPORTED, "sdm_phase1: a C=%d triangle (%zu B) exceeds the %d B of LDS per block", s->C, tri,
+                    lds_max);
+    sdm::P1Launch L;
+    L.s = s;
+    L.io = io;
+    L.rec = static_cast<char*>(io->workspace) + ws.rec_off;
+    L.inv = static_cast<char*>(io->workspace) + ws.inv_off;
+    const hipError_t e = sdm::p1_launch(L, st);
+    if (e != hipSuccess) return fail(SDM_EHIP, "sdm_phase1: %s", hipGetErrorString(e));
+    return SDM_OK;
+}
+
+sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st) {
+    g_last_error.clear();
+    if (io == nullptr) return fail(SDM_EINVAL, "sdm_dw_step: io is NULL");
+    if (io->C < 1 || io->C > 256 || io->W < 1 || io->W > 256)
+        return fail(SDM_ESHAPE, "sdm_dw_step: C = %d, W = %d outside 1..256", io->C, io->W);
+    if (io->P < 1 || io->N < 0) return fail(SDM_ESHAPE, "sdm_dw_step: P = %d, N = %d", io->P, io->N);
+    if (ti < 0 || (ti + 1) * static_cast<int64_t>(io->P) > io->N)
+        return fail(SDM_ESHAPE, "sdm_dw_step: step %lld needs (ti+1)*P <= N = %d", static_cast<long long>(ti), io->N);
+    if (io->bank_dtype != SDM_F32 && io->bank_dtype != SDM_BF16)
+        return fail(SDM_EINVAL, "sdm_dw_step: bank_dtype %d", io->bank_dtype);
+    if (io->dv_dtype != SDM_F32 && io->dv_dtype != SDM_BF16)
+        return fail(SDM_EINVAL, "sdm_dw_step: dv_dtype %d", io->dv_dtype);
+    if (io->hd < 4 || io->hd % 4 != 0 || io->hd > 4096)
+        return fail(SDM_ESHAPE, "sdm_dw_step: hd = %d (multiple of 4 in 4..4096)", io->hd);
+    if (sdm::dw_cols_per_lane(io->hd) == 0)
+        return fail(SDM_EUNSUPPORTED, "sdm_dw_step: hd = %d (this build: multiple of 8 up to 512, or of 16 up to 1024)",
+                    io->hd);
+    if (io->rows < 1 || io->dv_step_rows < 0 || io->dv_rows < 0)
+        return fail(SDM_EINVAL, "sdm_dw_step: rows / dv_step_rows / dv_rows");
+    if (ti * io->dv_step_rows + static_cast<int64_t>(io->P) * io->C > io->dv_rows)
+        return fail(SDM_EINVAL, "sdm_dw_step: dv holds %lld rows, step %lld needs %lld", static_cast<long long>(io->dv_rows),
+                    static_cast<long long>(ti), static_cast<long long>(ti * io->dv_step_rows + static_cast<int64_t>(io->P) * io->C));
+    if (io->bank == nullptr || io->dv == nullptr || io->krec == nullptr)
+        return fail(SDM_EINVAL, "sdm_dw_step: bank, dv and krec are required");
+    if (!aligned(io->bank, 16) || !aligned(io->dv, 16) || !aligned(io->krec, 16))
+        return fail(SDM_EALIGN, "sdm_dw_step: bank, dv and krec must be 16-byte aligned");
+    const int bank_es = io->bank_dtype == SDM_BF16 ? 2 : 4;
+    const int dv_es = io->dv_dtype == SDM_BF16 ? 2 : 4;
+    if ((io->hd * bank_es) % 16 != 0 || (io->hd * dv_es) % 16 != 0)
+        return fail(SDM_EALIGN, "sdm_dw_step: rows of hd = %d are not 16-byte multiples", io->hd);
+    sdm::DwLaunch L;
+    L.io = io;
+    L.ti = ti;
+    const hipError_t e = sdm::dw_launch(L, st);
+    if (e != hipSuccess) return fail(SDM_EHIP, "sdm_dw_step: %s", hipGetErrorString(e));
+    return SDM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+// DW decay-and-write step on gfx950.
+//
+// Definition (page "sparse_delta_memory/cuda/mover_da2_cuda.py", module docstring; bit contract
+// on "sparse_delta_memory/cuda/mover_fx_cuda.py", module docstring): per valid slot group of a
+// chunk's K-only row, acc = fma(sc_m, dv[token_m], acc) over the members in sorted order from +0,
+// then bank[slot] = fma(base, cpe_last, acc), rounded to nearest-even bf16 for a bf16 bank.
+//
+// Mapping: a team of lanes per K-row position. The team whose position holds a valid FIRST owns
+// that group: it reads the group's base row straight from the bank (every slot has one group per
+// step, so no other team writes it), walks the members' records and token rows in sorted order
+// and writes the new row. Each lane owns CPL consecutive columns and moves them with 16-byte
+// vector accesses; row offsets are 64-bit. Teams on positions that are not a valid FIRST exit.
+#include "sdm_device.hpp"
+#include "sdm_launch.hpp"
+
+namespace sdm {
+namespace {
+
+constexpr int kDwThreads = 256;
+
+struct DwArgs {
+    void* bank;
+    const void* dv;
+    const uint4* krec;
+    int64_t dv_row0;   // ti * dv_step_rows
+    int64_t chunk0;    // ti * P
+    int64_t rows;      // bank rows
+    int P, C, CW, hd, ts_log2, teams_per_block;
+};
+
+template <int CPL, bool BF16>
+__device__ __forceinline__ void load_cols(const void* row, int col0, float (&x)[CPL]) {
+    if constexpr (BF16) {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + col0);
+#pragma unroll
+        for (int v = 0; v < CPL / 8; ++v) {
+            const uint4 u = p[v];
+            const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                x[v * 8 + 2 * h] = bf16_bits_to_f32(w4[h] & 0xFFFFu);
+                x[v * 8 + 2 * h + 1] = bf16_bits_to_f32(w4[h] >> 16);
+            }
+        }
+    } else {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(row) + col0);
+#pragma unroll
+        for (int v = 0; v < CPL / 4; ++v) {
+            const float4 f = p[v];
+            x[v * 4 + 0] = f.x;
+            x[v * 4 + 1] = f.y;
+            x[v * 4 + 2] = f.z;
+            x[v * 4 + 3] = f.w;
+        }
+    }
+}
+
+template <int CPL, bool BF16>
+__device__ __forceinline__ void store_cols(void* row, int col0, const float (&x)[CPL]) {
+    if constexpr (BF16) {
+        uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(row) + col0);
+#pragma unroll
+        for (int v = 0; v < CPL / 8; ++v) {
+            uint32_t w4[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                w4[h] = f32_to_bf16_rne(x[v * 8 + 2 * h]) | (f32_to_bf16_rne(x[v * 8 + 2 * h + 1]) << 16);
+            }
+            p[v] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        }
+    } else {
+        float4* p = reinterpret_cast<float4*>(static_cast<float*>(row) + col0);
+#pragma unroll
+        for (int v = 0; v < CPL / 4; ++v) p[v] = make_float4(x[v * 4], x[v * 4 + 1], x[v * 4 + 2], x[v * 4 + 3]);
+    }
+}
+
+template <int CPL, bool BANK_BF16, bool DV_BF16>
+__global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
+    static_assert(CPL % (BANK_BF16 ? 8 : 4) == 0 && CPL % (DV_BF16 ? 8 : 4) == 0, "16-byte column groups");
+    const int team = threadIdx.x >> a.ts_log2;
+    const int tl = threadIdx.x & ((1 << a.ts_log2) - 1);
+    const int64_t J = static_cast<int64_t>(blockIdx.x) * a.teams_per_block + team;
+    if (J >= static_cast<int64_t>(a.P) * a.CW) return;
+    const int p = static_cast<int>(J / a.CW);
+    const int j = static_cast<int>(J - static_cast<int64_t>(p) * a.CW);
+    const int col0 = tl * CPL;
+    if (col0 >= a.hd) return;
+    const uint4* kr = a.krec + (a.chunk0 + p) * a.CW;
+    uint4 r = kr[j];
+    if ((r.x & (kFirst | kInvalid)) != kFirst) return;
+    if (static_cast<int64_t>(r.y) >= a.rows) return;   // a slot outside the bank: the group is skipped
+    constexpr int kBankEs = BANK_BF16 ? 2 : 4;
+    constexpr int kDvEs = DV_BF16 ? 2 : 4;
+    unsigned char* bank_row =
+        static_cast<unsigned char*>(a.bank) + static_cast<int64_t>(r.y) * a.hd * kBankEs;
+    float base[CPL];
+    load_cols<CPL, BANK_BF16>(bank_row, col0, base);
+    const unsigned char* dv0 = static_cast<const unsigned char*>(a.dv) +
+                               (a.dv_row0 + static_cast<int64_t>(p) * a.C) * a.hd * kDvEs;
+    float acc[CPL];
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) acc[q] = 0.0f;
+    int m = j;
+    while (true) {
+        const int tok = static_cast<int>((r.x >> kTokShift) & 0xFFu);
+        const float sc = __uint_as_float(r.z);
+        float xv[CPL];
+        load_cols<CPL, DV_BF16>(dv0 + static_cast<int64_t>(tok) * a.hd * kDvEs, col0, xv);
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) acc[q] = fmaf(sc, xv[q], acc[q]);
+        if ((r.x & kLast) || m + 1 >= a.CW) break;   // records end at the row's end in any case
+        r = kr[++m];
+    }
+    const float cpe = __uint_as_float(r.w);
+    float o[CPL];
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) o[q] = fmaf(base[q], cpe, acc[q]);
+    store_cols<CPL, BANK_BF16>(bank_row, col0, o);
+}
+
+template <int CPL, bool BB, bool DB>
+hipError_t launch_dw(const DwArgs& a, hipStream_t st) {
+    const int64_t teams = static_cast<int64_t>(a.P) * a.CW;
+    const int64_t blocks = (teams + a.teams_per_block - 1) / a.teams_per_block;
+    hipLaunchKernelGGL((dw_kernel<CPL, BB, DB>), dim3(static_cast<unsigned>(blocks)), dim3(kDwThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int CPL>
+hipError_t launch_dw_types(const DwArgs& a, bool bank_bf16, bool dv_bf16, hipStream_t st) {
+    if (bank_bf16) return dv_bf16 ? launch_dw<CPL, true, true>(a, st) : launch_dw<CPL, true, false>(a, st);
+    return dv_bf16 ? launch_dw<CPL, false, true>(a, st) : launch_dw<CPL, false, false>(a, st);
+}
+
+}  // namespace
+
+int dw_cols_per_lane(int hd) {
+    if (hd % 8 == 0 && hd <= 8 * kWave) return 8;
+    if (hd % 16 == 0 && hd <= 16 * kWave) return 16;
+    return 0;
+}
+
+hipError_t dw_launch(const DwLaunch& Lc, hipStream_t st) {
+    const sdm_dw_io* io = Lc.io;
+    DwArgs a;
+    a.bank = io->bank;
+    a.dv = io->dv;
+    a.krec = reinterpret_cast<const uint4*>(io->krec);
+    a.dv_row0 = Lc.ti * io->dv_step_rows;
+    a.chunk0 = Lc.ti * io->P;
+    a.rows = io->rows;
+    a.P = io->P;
+    a.C = io->C;
+    a.CW = io->C * io->W;
+    a.hd = io->hd;
+    const int cpl = dw_cols_per_lane(io->hd);
+    const int lanes = (io->hd + cpl - 1) / cpl;
+    int ts = 1;
+    while (ts < lanes) ts <<= 1;
+    a.ts_log2 = __builtin_ctz(static_cast<unsigned>(ts));
+    a.teams_per_block = kDwThreads / ts;
+    if (static_cast<int64_t>(a.P) * a.CW == 0) return hipSuccess;
+    const bool bb = io->bank_dtype == SDM_BF16, db = io->dv_dtype == SDM_BF16;
+    if (cpl == 8) return launch_dw_types<8>(a, bb, db, st);
+    return launch_dw_types<16>(a, bb, db, st);
+}
+
+}  // namespace sdm

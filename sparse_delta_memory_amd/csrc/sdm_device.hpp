@@ -1,0 +1,42 @@
+// Device-side constants and helpers shared by the Phase-1 and DW kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdm {
+
+// Payload word of an entry (page "sparse_delta_memory/cuda/phase1_cuda.py", p1_keys_zw_kernel and
+// the sorted-row element comment of p1_scan_kernel): lane bits 0-7, Q bit 8, token bits 9-16,
+// invalid bit 17; the sorted kind rows add the distance to the kind's first entry of the group
+// (bits 18-29), LAST (bit 30) and FIRST (bit 31).
+constexpr uint32_t kFirst = 0x80000000u;
+constexpr uint32_t kLast = 0x40000000u;
+constexpr uint32_t kInvalid = 0x20000u;
+constexpr uint32_t kIsQ = 0x100u;
+constexpr int kTokShift = 9;
+constexpr uint32_t kEntryMask = 0x3FFFFu;
+constexpr int kDistShift = 18;
+constexpr uint32_t kDistMax = 4095u;
+// Packed positions: sorted position bits 0-16, peers after bits 17-23, peers in group 24-30.
+constexpr int kPosAfterShift = 17;
+constexpr int kPosSizeShift = 24;
+constexpr uint32_t kPosCountMax = 127u;
+// Head-of-group flag kept in bit 31 of the pair records' payload word.
+constexpr uint32_t kHead = 0x80000000u;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
+
+// float32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
+
+}  // namespace sdm

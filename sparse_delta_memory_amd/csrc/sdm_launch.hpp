@@ -1,0 +1,39 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sdm.h"
+
+namespace sdm {
+
+// Longest chunk row (C * (W + R)) one Phase-1 workgroup sorts and scans on chip.
+constexpr int kP1MaxRow = 16384;
+constexpr int kP1Threads = 1024;
+
+struct P1Launch {
+    const sdm_p1_shape* s;
+    const sdm_p1_io* io;
+    void* rec;        // [N, n] 16-byte pair records (workspace)
+    void* inv;        // [N, n] uint32 inverse permutation (workspace)
+};
+
+// Workspace layout of sdm_phase1: byte offsets of the two regions and the total.
+struct P1Workspace {
+    size_t rec_off, inv_off, total;
+};
+P1Workspace p1_workspace_layout(const sdm_p1_shape* s);
+
+// Enqueue the Phase-1 kernels; returns hipSuccess or the first launch error.
+hipError_t p1_launch(const P1Launch& L, hipStream_t st);
+
+struct DwLaunch {
+    const sdm_dw_io* io;
+    int64_t ti;
+};
+
+hipError_t dw_launch(const DwLaunch& L, hipStream_t st);
+
+}  // namespace sdm

@@ -198,3 +198,23 @@ def make_bank(wl: Workload, device="cpu", rows: int | None = None):
         blk = torch.randn((nb, sh.hd), generator=gen, device=device, dtype=torch.float32) * 0.1
         bank[b0:b0 + nb].copy_(blk.to(dt))
     return bank
+
+
+def make_bank_rows(wl: Workload, rows, device="cpu"):
+    """Initial values of the given bank rows, regenerated block by block exactly as make_bank."""
+    import torch
+
+    sh = wl.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    dt = torch.bfloat16 if sh.bank_dtype == "bf16" else torch.float32
+    out = torch.empty((rows.size, sh.hd), dtype=dt, device=device)
+    blk_of = rows // BANK_BLOCK_ROWS
+    for b in np.unique(blk_of):
+        b0 = int(b) * BANK_BLOCK_ROWS
+        nb = min(BANK_BLOCK_ROWS, wl.rows - b0)
+        gen = torch.Generator(device=device)
+        gen.manual_seed(wl.bank_seed + int(b))
+        blk = (torch.randn((nb, sh.hd), generator=gen, device=device, dtype=torch.float32) * 0.1).to(dt)
+        sel = np.nonzero(blk_of == b)[0]
+        out[torch.as_tensor(sel, device=device)] = blk[torch.as_tensor(rows[sel] - b0, device=device)]
+    return out

@@ -1,0 +1,198 @@
+"""Helpers shared by the GPU tests: run the HIP path on a workload and compare with the oracle.
+
+Inputs come from sparse_delta_memory_amd.workloads; expected values only from oracle/. The oracle
+never receives a value produced by the HIP path: for the DW check, the oracle's own bank state
+is copied INTO the GPU bank before a checked step, so both sides start that step from the same
+rows.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import sparse_delta_memory_amd as sdm
+from sparse_delta_memory_amd import workloads as W
+
+F32_REL, F32_ABS = 1e-5, 1e-6
+
+
+def shape_of(wl: W.Workload, tile_len: int = 128):
+    s = wl.shape
+    return sdm.make_shape(wl.N, s.C, s.W, s.R, P=s.P, key_bits=s.key_bits, stream_offset=s.S,
+                          first_partial=wl.first_partial, valid_last=wl.valid_last, tile_len=tile_len)
+
+
+def device_inputs(wl: W.Workload, dev="cuda"):
+    import torch
+
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    return dict(k_idx=t(wl.k_idx), q_idx=t(wl.q_idx), k_val=t(wl.k_val), q_val=t(wl.q_val), g=t(wl.g))
+
+
+def device_dv(wl: W.Workload, dev="cuda"):
+    import torch
+
+    dv = torch.from_numpy(np.ascontiguousarray(wl.dv.reshape(-1, wl.shape.hd))).to(dev)
+    return dv.to(torch.bfloat16) if wl.shape.dv_dtype == "bf16" else dv
+
+
+def run_phase1(wl: W.Workload, dev="cuda", tile_len=128):
+    import torch
+
+    shape = shape_of(wl, tile_len)
+    ins = device_inputs(wl, dev)
+    out = sdm.phase1(shape, **ins)
+    torch.cuda.synchronize()
+    return shape, out
+
+
+def oracle_phase1(wl: W.Workload, chunks, tile_len=128, threads=8):
+    return oracle.phase1(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, P=wl.P, stream_offset=wl.stream_offset,
+                         first_partial=wl.first_partial, valid_last=wl.valid_last, tile_len=tile_len, chunks=chunks,
+                         threads=threads)
+
+
+def f32_violations(gpu, ref):
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    tol = np.maximum(F32_REL * np.abs(r), F32_ABS)
+    return ~(np.abs(g - r) <= tol)
+
+
+def assert_f32(name, gpu, ref):
+    bad = f32_violations(gpu, ref)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        g = np.asarray(gpu, np.float64)
+        r = np.asarray(ref, np.float64)
+        det = ", ".join("%s: gpu %r oracle %r" % (tuple(i), g[tuple(i)], r[tuple(i)]) for i in idx)
+        raise AssertionError("%s: %d of %d elements outside max(1e-5|o|, 1e-6): %s" % (name, bad.sum(), bad.size, det))
+
+
+def assert_exact(name, gpu, ref):
+    g = np.asarray(gpu).astype(np.int64)
+    r = np.asarray(ref).astype(np.int64)
+    if g.shape != r.shape or not np.array_equal(g, r):
+        bad = np.argwhere(g != r)[:5] if g.shape == r.shape else []
+        det = ", ".join("%s: gpu %d oracle %d" % (tuple(i), g[tuple(i)], r[tuple(i)]) for i in bad)
+        raise AssertionError("%s differs (%s vs %s): %s" % (name, g.shape, r.shape, det))
+
+
+def compare_phase1(out, ref, chunks):
+    """Element-by-element comparison of GPU outputs (device dict) and oracle outputs (chunk list)."""
+    import torch
+
+    idx = torch.as_tensor(list(chunks), device=out["krec"].device, dtype=torch.long)
+    host = {k: v.index_select(0, idx).cpu().numpy() for k, v in out.items()}
+    u32 = lambda a: np.asarray(a).astype(np.int64) & 0xFFFFFFFF  # noqa: E731
+    for f in ("log_k", "rex", "cpe", "k_eff", "log_q", "q_w", "a", "qk"):
+        if f in host:
+            assert_f32(f, host[f], ref[f])
+    for f in ("is_last", "is_only", "q_last", "q_only", "pos_k", "pos_q", "tiles_k", "repeats"):
+        if f in host:
+            assert_exact(f, host[f], ref[f])
+    assert_exact("spay_k", u32(host["spay_k"]), u32(ref["spay_k"]))
+    if "spay_q" in host:
+        assert_exact("spay_q", u32(host["spay_q"]), u32(ref["spay_q"]))
+    kr = host["krec"]
+    assert_exact("krec.element", u32(kr[..., 0]), u32(ref["spay_k"]))
+    assert_exact("krec.slot", kr[..., 1], ref["krec_slot"])
+    assert_f32("krec.scale", kr[..., 2].view(np.float32), ref["krec_sc"])
+    assert_f32("krec.cpe", kr[..., 3].view(np.float32), ref["krec_cpe"])
+
+
+def ulp_bf16(x):
+    x = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(x, 2.0 ** -133)))
+    return 2.0 ** (np.maximum(e, -126) - 7)
+
+
+def bank_violations(gpu_rows, new, mag, members, bank_dtype):
+    """Rows of the GPU bank against the oracle's new rows (float64).
+
+    The float32 evaluation of an m-member chain with float32 scales is within
+    (m + 4) 2^-23 times the sum of the term magnitudes (`mag`) of the exact value. float32 bank:
+    max(1e-5|o|, 1e-6), or that evaluation bound where it is larger (long chains that cancel).
+    bf16 bank: one bf16 ulp of max(|gpu|, |o|) for the final rounding plus the evaluation bound."""
+    g = np.asarray(gpu_rows, np.float64)
+    arith = (np.asarray(members, np.float64)[:, None] + 4.0) * 2.0 ** -23 * mag
+    if bank_dtype == "f32":
+        tol = np.maximum(np.maximum(F32_REL * np.abs(new), F32_ABS), arith)
+        return ~(np.abs(g - new) <= tol)
+    tol = ulp_bf16(np.maximum(np.abs(g), np.abs(new))) + arith
+    return ~(np.abs(g - new) <= tol)
+
+
+def chunk_members(wl, c):
+    """Valid K members per valid group of chunk c, in dw_slots order (counts only)."""
+    C = wl.shape.C
+    tv = wl.valid_last if c >= wl.first_partial else C
+    ids = wl.k_idx[c, :tv].ravel().astype(np.int64)
+    u, cnt = np.unique(ids, return_counts=True)
+    return u, cnt
+
+
+def run_dw_check(wl: W.Workload, out, shape, check_steps, dev="cuda", sample_untouched=20000, seed=0):
+    """Run every DW step on the GPU; at the steps in check_steps, first copy the oracle's state of
+    the touched rows into the GPU bank, then compare the GPU result with the oracle's. Returns the
+    number of elements compared."""
+    import torch
+
+    sh = wl.shape
+    P, C, hd = sh.P, sh.C, sh.hd
+    bank = W.make_bank(wl, dev)
+    shadow = bank.clone()          # the oracle's bank state (generator rows, then oracle rows)
+    dv = device_dv(wl, dev)
+    dv_host = wl.dv.reshape(-1, hd).astype(np.float64)
+    touched = set()
+    compared = 0
+    for ti in range(wl.steps):
+        check = ti in check_steps
+        per = []
+        for p in range(P):
+            c = ti * P + p
+            slots = oracle.dw_slots(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, c, P=P, stream_offset=sh.S,
+                                    first_partial=wl.first_partial, valid_last=wl.valid_last)
+            per.append((c, slots))
+        all_slots = torch.as_tensor(np.concatenate([s for _, s in per]), device=dev, dtype=torch.long)
+        base_all = shadow.index_select(0, all_slots)
+        if check:
+            bank.index_copy_(0, all_slots, base_all)
+        sdm.dw_step(bank, dv, out["krec"], shape, ti, dv_step_rows=P * C)
+        base_host = base_all.float().cpu().numpy().astype(np.float64)
+        if check:
+            torch.cuda.synchronize()
+            got_all = bank.index_select(0, all_slots).float().cpu().numpy()
+        off = 0
+        news = []
+        for c, slots in per:
+            m = len(slots)
+            rows = dv_host[c * C:(c + 1) * C]
+            new, mag = oracle.dw_apply(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, c, rows, base_host[off:off + m],
+                                       P=P, stream_offset=sh.S, first_partial=wl.first_partial,
+                                       valid_last=wl.valid_last, with_magnitude=True)
+            if check:
+                u, cnt = chunk_members(wl, c)
+                assert np.array_equal(u, slots)
+                bad = bank_violations(got_all[off:off + m], new, mag, cnt, sh.bank_dtype)
+                if bad.any():
+                    i = np.argwhere(bad)[0]
+                    raise AssertionError("DW step %d chunk %d: %d of %d elements outside tolerance; slot %d col %d: "
+                                         "gpu %r oracle %r" % (ti, c, bad.sum(), bad.size, slots[i[0]], i[1],
+                                                               got_all[off + i[0], i[1]], new[i[0], i[1]]))
+                compared += bad.size
+            news.append(new)
+            touched.update(slots.tolist())
+            off += m
+        new_all = torch.from_numpy(np.concatenate(news).astype(np.float32)).to(dev)
+        shadow.index_copy_(0, all_slots, new_all.to(shadow.dtype))
+    # Rows no group touched keep their initial bits.
+    rng = np.random.default_rng(seed)
+    cand = rng.integers(0, wl.rows, size=sample_untouched * 2)
+    cand = np.array([r for r in cand if int(r) not in touched][:sample_untouched], dtype=np.int64)
+    if cand.size:
+        idx = torch.as_tensor(cand, device=dev)
+        init = W.make_bank_rows(wl, cand, dev)
+        assert torch.equal(bank.index_select(0, idx), init), "untouched rows changed"
+    return compared, bank

@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every function include/sdm.h declares, and refuses bad
+arguments on the host with the documented status codes (CPU only: nothing is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_delta_memory_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdm.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libsdm_amd.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(sdm_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def shape(**kw):
+    d = dict(N=4, C=64, W=4, R=4, P=1, key_bits=12, stream_offset=0, first_partial=4, valid_last=64, tile_len=128)
+    d.update(kw)
+    return _lib.P1Shape(*[d[f] for f, _ in _lib.P1Shape._fields_])
+
+
+FAKE = 0x10000  # never dereferenced: every check below fails before a launch
+
+
+def io(**kw):
+    o = _lib.P1IO()
+    for f in _lib.P1_IO_FIELDS:
+        setattr(o, f, FAKE)
+    o.workspace = FAKE
+    o.workspace_bytes = 1 << 40
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+def call_p1(s, o):
+    lib = _lib.load()
+    return lib.sdm_phase1(ctypes.byref(s) if s is not None else None, ctypes.byref(o) if o is not None else None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(C=0), _lib.SDM_ESHAPE), (dict(C=257), _lib.SDM_ESHAPE), (dict(W=0), _lib.SDM_ESHAPE),
+    (dict(R=300), _lib.SDM_ESHAPE), (dict(P=0), _lib.SDM_ESHAPE), (dict(N=-1), _lib.SDM_ESHAPE),
+    (dict(key_bits=0), _lib.SDM_EINVAL), (dict(key_bits=31), _lib.SDM_EINVAL),
+    (dict(first_partial=5), _lib.SDM_EINVAL), (dict(valid_last=65), _lib.SDM_EINVAL),
+    (dict(tile_len=0), _lib.SDM_EINVAL), (dict(stream_offset=-1), _lib.SDM_EINVAL),
+    (dict(C=256, W=256, R=256), _lib.SDM_EUNSUPPORTED), (dict(C=256, W=40, R=40), _lib.SDM_EUNSUPPORTED),
+])
+def test_phase1_shape_refusals(kw, status):
+    s = shape(**kw)
+    assert call_p1(s, io()) == status
+    assert _lib.load().sdm_phase1_workspace(ctypes.byref(s)) == 0
+    assert len(_lib.load().sdm_last_error()) > 0
+
+
+def test_phase1_argument_refusals():
+    s = shape()
+    assert call_p1(None, io()) == _lib.SDM_EINVAL
+    assert call_p1(s, None) == _lib.SDM_EINVAL
+    for f in ("k_idx", "q_idx", "k_val", "q_val", "g", "spay_k", "krec", "tiles_k"):
+        assert call_p1(s, io(**{f: None})) == _lib.SDM_EINVAL, f
+    assert call_p1(s, io(krec=FAKE + 4)) == _lib.SDM_EALIGN
+    assert call_p1(s, io(log_k=FAKE + 2)) == _lib.SDM_EALIGN
+    need = _lib.load().sdm_phase1_workspace(ctypes.byref(s))
+    assert need > 0
+    assert call_p1(s, io(workspace_bytes=need - 1)) == _lib.SDM_EWORKSPACE
+    assert call_p1(s, io(workspace=None)) == _lib.SDM_EWORKSPACE
+    # N = 0 is a valid no-op: nothing to launch, no device needed.
+    assert call_p1(shape(N=0, first_partial=0), io()) == _lib.SDM_OK
+
+
+def dw(**kw):
+    o = _lib.DwIO()
+    d = dict(bank=FAKE, bank_dtype=_lib.SDM_BF16, rows=1 << 20, hd=128, dv=FAKE, dv_dtype=_lib.SDM_F32,
+             dv_step_rows=64, dv_rows=256, krec=FAKE, P=1, C=64, W=4, N=4)
+    d.update(kw)
+    for k, v in d.items():
+        setattr(o, k, v)
+    return o
+
+
+@pytest.mark.parametrize("kw,ti,status", [
+    (dict(), -1, _lib.SDM_ESHAPE), (dict(), 4, _lib.SDM_ESHAPE), (dict(P=2), 2, _lib.SDM_ESHAPE),
+    (dict(C=0), 0, _lib.SDM_ESHAPE), (dict(W=257), 0, _lib.SDM_ESHAPE),
+    (dict(bank_dtype=7), 0, _lib.SDM_EINVAL), (dict(dv_dtype=3), 0, _lib.SDM_EINVAL),
+    (dict(hd=126), 0, _lib.SDM_ESHAPE), (dict(hd=8192), 0, _lib.SDM_ESHAPE),
+    (dict(hd=100), 0, _lib.SDM_EUNSUPPORTED), (dict(hd=2048), 0, _lib.SDM_EUNSUPPORTED),
+    (dict(bank=None), 0, _lib.SDM_EINVAL), (dict(krec=None), 0, _lib.SDM_EINVAL),
+    (dict(bank=FAKE + 8), 0, _lib.SDM_EALIGN), (dict(dv=FAKE + 4), 0, _lib.SDM_EALIGN),
+    (dict(krec=FAKE + 8), 0, _lib.SDM_EALIGN), (dict(rows=0), 0, _lib.SDM_EINVAL),
+    (dict(dv_rows=255), 3, _lib.SDM_EINVAL), (dict(dv_step_rows=-1), 0, _lib.SDM_EINVAL),
+])
+def test_dw_refusals(kw, ti, status):
+    lib = _lib.load()
+    assert lib.sdm_dw_step(ctypes.byref(dw(**kw)), ti, None) == status
+    assert len(lib.sdm_last_error()) > 0
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for s in range(-6, 1):
+        assert len(lib.sdm_status_string(s)) > 0

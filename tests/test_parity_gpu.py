@@ -1,0 +1,155 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Integer and index outputs must match bit for bit; float32 outputs within max(1e-5 |o|, 1e-6);
+bf16 banks within one bf16 ulp plus the float32 evaluation bound (tests/hip_harness.py). Every
+input comes from sparse_delta_memory_amd.workloads; every expected value from oracle/.
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import sparse_delta_memory_amd as sdm  # noqa: E402
+from sparse_delta_memory_amd import workloads as W  # noqa: E402
+
+sys.path.insert(0, os.path.dirname(__file__))
+import hip_harness as H  # noqa: E402
+
+# Workload index -> steps for the full comparison (the oracle finishes each in seconds; several
+# tiles of 1024 entries per chunk, the ragged last step of workload 4 included).
+SMALL_STEPS = {0: None, 1: 2, 2: 1, 3: 2, 4: 2}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_phase1_full_compare(idx):
+    wl = W.make(idx, steps=SMALL_STEPS[idx])
+    say("phase1 full compare: workload", idx, wl.shape.name, "N =", wl.N)
+    shape, out = H.run_phase1(wl)
+    ref = H.oracle_phase1(wl, list(range(wl.N)))
+    H.compare_phase1(out, ref, range(wl.N))
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+def test_phase1_full_size_sampled(idx):
+    """The full workload in one call (the benchmark's launch), checked on sampled chunks."""
+    wl = W.make(idx)
+    say("phase1 full size: workload", idx, wl.shape.name, "N =", wl.N)
+    shape, out = H.run_phase1(wl)
+    chunks = sorted({0, wl.P - 1, wl.N // 2 + 1, wl.N - 1})
+    ref = H.oracle_phase1(wl, chunks)
+    H.compare_phase1(out, ref, chunks)
+    # Properties over every chunk: sorted positions are permutations of the row.
+    n = wl.shape.C * (wl.shape.W + wl.shape.R)
+    pos = torch.cat([out["pos_k"].reshape(wl.N, -1), out["pos_q"].reshape(wl.N, -1)], 1) & ((1 << 17) - 1)
+    srt, _ = torch.sort(pos, dim=1)
+    assert torch.equal(srt, torch.arange(n, device=pos.device, dtype=pos.dtype).expand(wl.N, n))
+
+
+@pytest.mark.parametrize("idx,steps,check", [
+    (0, None, {0, 1, 2, 3}), (1, 4, {0, 1, 3}), (2, 2, {0, 1}), (3, 2, {0, 1}), (4, 3, {0, 2}),
+])
+def test_dw_steps(idx, steps, check):
+    wl = W.make(idx, steps=steps)
+    say("dw steps: workload", idx, wl.shape.name, "steps", wl.steps)
+    shape, out = H.run_phase1(wl)
+    n, _ = H.run_dw_check(wl, out, shape, check)
+    assert n > 0
+
+
+@pytest.mark.parametrize("idx,check", [(1, {0, 31}), (3, {0, 31}), (4, {0, 63})])
+def test_dw_full_size(idx, check):
+    """Every step of the full workload on the GPU; the oracle's state is carried through all steps
+    and the checked steps (the first and the last, ragged in workload 4) are compared."""
+    wl = W.make(idx)
+    say("dw full size: workload", idx, wl.shape.name, "steps", wl.steps)
+    shape, out = H.run_phase1(wl)
+    n, _ = H.run_dw_check(wl, out, shape, check, sample_untouched=5000)
+    assert n > 0
+
+
+def test_bitwise_reproducible():
+    wl = W.make(2, steps=1)
+    say("reproducibility: workload 2")
+    _, o1 = H.run_phase1(wl)
+    _, o2 = H.run_phase1(wl)
+    for k in o1:
+        assert torch.equal(o1[k].view(torch.uint8), o2[k].view(torch.uint8)), k
+    wl = W.make(1, steps=3)
+    shape, out = H.run_phase1(wl)
+    dv = H.device_dv(wl)
+    banks = []
+    for _ in range(2):
+        bank = W.make_bank(wl, "cuda")
+        for ti in range(wl.steps):
+            sdm.dw_step(bank, dv, out["krec"], shape, ti, dv_step_rows=wl.P * wl.shape.C)
+        torch.cuda.synchronize()
+        banks.append(bank)
+    assert torch.equal(banks[0].view(torch.uint16), banks[1].view(torch.uint16))
+
+
+def test_masked_tokens_do_not_leak():
+    """NaN in the values, gates and token rows of masked tokens changes no output bit."""
+    a = W.make(4, steps=2, nan_invalid=True)
+    b = W.make(4, steps=2, nan_invalid=False)
+    say("masking: workload 4, 2 steps")
+    shape, oa = H.run_phase1(a)
+    _, ob = H.run_phase1(b)
+    for k in oa:
+        assert torch.equal(oa[k].view(torch.uint8), ob[k].view(torch.uint8)), k
+    banks = []
+    for wl, out in ((a, oa), (b, ob)):
+        bank = W.make_bank(wl, "cuda")
+        dv = H.device_dv(wl)
+        for ti in range(wl.steps):
+            sdm.dw_step(bank, dv, out["krec"], shape, ti, dv_step_rows=wl.P * wl.shape.C)
+        torch.cuda.synchronize()
+        banks.append(bank)
+    assert torch.equal(banks[0].view(torch.uint16), banks[1].view(torch.uint16))
+    assert not torch.isnan(banks[0].float()).any()
+
+
+@pytest.mark.parametrize("case", [
+    dict(C=37, W=5, R=3, S=9, P=2, steps=2, vl=11),       # ragged row (296 entries), heavy sharing
+    dict(C=1, W=1, R=1, S=4, P=1, steps=3, vl=None),      # one token
+    dict(C=64, W=2, R=3, S=1, P=1, steps=2, vl=0),        # one slot; last chunk fully masked
+    dict(C=256, W=17, R=3, S=1, P=1, steps=1, vl=None),   # one group of 5120: saturated counts
+    dict(C=100, W=7, R=9, S=3000, P=3, steps=2, vl=50),   # 1600 entries: two radix tiles
+])
+def test_edge_shapes(case):
+    sh = W.Shape("edge", P=case["P"], T=case["C"] * case["steps"], C=case["C"], W=case["W"], R=case["R"],
+                 S=case["S"], hd=64, bank_dtype="f32", dv_dtype="f32", slots="uniform", valid_last=case["vl"])
+    wl = W.make(sh, seed=777)
+    say("edge shape", case)
+    shape, out = H.run_phase1(wl)
+    ref = H.oracle_phase1(wl, list(range(wl.N)))
+    H.compare_phase1(out, ref, range(wl.N))
+    H.run_dw_check(wl, out, shape, set(range(wl.steps)), sample_untouched=0)
+
+
+def test_tile_len_variants():
+    wl = W.make(1, steps=1)
+    for L in (1, 32, 100, 4096):
+        shape, out = H.run_phase1(wl, tile_len=L)
+        ref = H.oracle_phase1(wl, list(range(wl.N)), tile_len=L)
+        H.assert_exact("tiles_k L=%d" % L, out["tiles_k"].cpu().numpy(), ref["tiles_k"])
+
+
+def test_empty_call():
+    shape = sdm.make_shape(0, 16, 2, 2, key_bits=8)
+    e = torch.empty(0, dtype=torch.int32, device="cuda")
+    f = torch.empty(0, dtype=torch.float32, device="cuda")
+    out = sdm.phase1(shape, e, e, f, f, f)
+    torch.cuda.synchronize()
+    assert out["krec"].numel() == 0
