@@ -48,6 +48,7 @@ class _ChunkIn(ctypes.Structure):
 _OUT_FIELDS = [
     "log_k", "rex", "cpe", "k_eff", "is_last", "is_only", "pos_k", "log_q", "q_w", "pos_q", "q_last", "q_only",
     "spay_k", "spay_q", "krec_slot", "krec_sc", "krec_cpe", "tiles_k", "a", "qk", "perm", "repeats",
+    "a_mag", "qk_mag", "a_cnt", "qk_cnt",
 ]
 
 
@@ -91,7 +92,8 @@ def phase1(k_idx, q_idx, k_val, q_val, g, *, P=1, stream_offset=0, first_partial
     """Phase 1 of the chunks `chunks` (default: all). Arrays are [N, C, W] / [N, C, R] / [N, C].
 
     Returns a dict of numpy arrays whose first axis runs over the requested chunks. `fields`
-    restricts the outputs computed (default: all of them)."""
+    selects the outputs (default: every Phase-1 output; the per-cell term magnitudes a_mag /
+    qk_mag and term counts a_cnt / qk_cnt only when named)."""
     lib = _load()
     N, C, W = k_idx.shape
     R = q_idx.shape[2]
@@ -112,8 +114,11 @@ def phase1(k_idx, q_idx, k_val, q_val, g, *, P=1, stream_offset=0, first_partial
         "spay_k": ((nk,), np.int32), "spay_q": ((nq,), np.int32), "krec_slot": ((nk,), np.int32),
         "krec_sc": ((nk,), np.float64), "krec_cpe": ((nk,), np.float64), "tiles_k": ((ntk + 1,), np.int32),
         "a": ((C, C), np.float64), "qk": ((C, C), np.float64), "perm": ((n,), np.int32), "repeats": ((1,), np.int64),
+        "a_mag": ((C, C), np.float64), "qk_mag": ((C, C), np.float64), "a_cnt": ((C, C), np.int32),
+        "qk_cnt": ((C, C), np.int32),
     }
-    want = set(shapes) if fields is None else set(fields)
+    optional = {"a_mag", "qk_mag", "a_cnt", "qk_cnt"}   # evaluation-error scales: only when asked for
+    want = (set(shapes) - optional) if fields is None else set(fields)
     if "tiles_k" in want:
         want.add("spay_k")
     res = {f: np.zeros((m,) + shapes[f][0], dtype=shapes[f][1]) for f in shapes if f in want}

@@ -79,6 +79,10 @@ typedef struct {
     double* qk;         /* [C, C] */
     int32_t* perm;      /* [C*(W+R)] entry index r at sorted position rho */
     int64_t* repeats;   /* [1] repeated K entries of the chunk */
+    double* a_mag;      /* [C, C] sum of |term| per cell of A (the float evaluation error scale) */
+    double* qk_mag;     /* [C, C] the same for QK */
+    int32_t* a_cnt;     /* [C, C] number of terms per cell of A */
+    int32_t* qk_cnt;    /* [C, C] the same for QK */
 } oracle_chunk_out;
 
 typedef struct {
@@ -298,7 +302,11 @@ int oracle_phase1_chunk(const oracle_chunk_in* in, const oracle_chunk_out* out) 
      * token) or QK (e a Q entry). */
     if (out->a) memset(out->a, 0, sizeof(double) * (size_t)C * (size_t)C);
     if (out->qk) memset(out->qk, 0, sizeof(double) * (size_t)C * (size_t)C);
-    if (out->a || out->qk) {
+    if (out->a_mag) memset(out->a_mag, 0, sizeof(double) * (size_t)C * (size_t)C);
+    if (out->qk_mag) memset(out->qk_mag, 0, sizeof(double) * (size_t)C * (size_t)C);
+    if (out->a_cnt) memset(out->a_cnt, 0, sizeof(int32_t) * (size_t)C * (size_t)C);
+    if (out->qk_cnt) memset(out->qk_cnt, 0, sizeof(int32_t) * (size_t)C * (size_t)C);
+    if (out->a || out->qk || out->a_mag || out->qk_mag || out->a_cnt || out->qk_cnt) {
         for (int p = 0; p < n; ++p) {
             if (w.ent[p].invalid) continue;
             const int ti = w.tok[p];
@@ -311,8 +319,12 @@ int oracle_phase1_chunk(const oracle_chunk_in* in, const oracle_chunk_out* out) 
                 const double term = ve * vf * exp(w.L[p] - w.L[u]);
                 if (q) {
                     if (out->qk) out->qk[ti * C + tj] += term;
+                    if (out->qk_mag) out->qk_mag[ti * C + tj] += fabs(term);
+                    if (out->qk_cnt) out->qk_cnt[ti * C + tj] += 1;
                 } else if (tj != ti) {
                     if (out->a) out->a[ti * C + tj] += term;
+                    if (out->a_mag) out->a_mag[ti * C + tj] += fabs(term);
+                    if (out->a_cnt) out->a_cnt[ti * C + tj] += 1;
                 }
             }
         }

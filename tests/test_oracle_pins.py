@@ -178,12 +178,14 @@ def test_scan_fields_match_brute_force(seed):
 @pytest.mark.parametrize("seed", [6, 7])
 def test_pairs_match_brute_force(seed):
     d = tiny(seed, N=2, C=8, W=3, R=3, S=3, P=1, valid_last=5)
-    o = run_oracle(d, fields=["a", "qk"])
+    o = run_oracle(d, fields=["a", "qk", "a_mag", "qk_mag", "a_cnt", "qk_cnt"])
     C = d["k_idx"].shape[1]
     for c in range(2):
         E, res = brute(d, c)
         A = np.zeros((C, C))
         QK = np.zeros((C, C))
+        cnt = {"a": np.zeros((C, C), int), "qk": np.zeros((C, C), int)}
+        mag = {"a": np.zeros((C, C)), "qk": np.zeros((C, C))}
         for ei, e in enumerate(E):
             for fi, f in enumerate(E):
                 if not (e["valid"] and f["valid"]) or f["q"] or e["s"] != f["s"]:
@@ -191,10 +193,17 @@ def test_pairs_match_brute_force(seed):
                 term = e["v"] * f["v"] * math.exp(res[ei]["L"] - res[fi]["L"])
                 if e["q"] and f["t"] <= e["t"]:
                     QK[e["t"], f["t"]] += term
+                    cnt["qk"][e["t"], f["t"]] += 1
+                    mag["qk"][e["t"], f["t"]] += abs(term)
                 if not e["q"] and f["t"] < e["t"]:
                     A[e["t"], f["t"]] += term
+                    cnt["a"][e["t"], f["t"]] += 1
+                    mag["a"][e["t"], f["t"]] += abs(term)
         np.testing.assert_allclose(o["a"][c], A, rtol=1e-12, atol=1e-15)
         np.testing.assert_allclose(o["qk"][c], QK, rtol=1e-12, atol=1e-15)
+        for k in ("a", "qk"):
+            assert np.array_equal(o[k + "_cnt"][c], cnt[k])
+            np.testing.assert_allclose(o[k + "_mag"][c], mag[k], rtol=1e-12, atol=1e-15)
 
 
 def test_invariants_groups():

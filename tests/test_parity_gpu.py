@@ -133,7 +133,7 @@ def test_edge_shapes(case):
     wl = W.make(sh, seed=777)
     say("edge shape", case)
     shape, out = H.run_phase1(wl)
-    ref = H.oracle_phase1(wl, list(range(wl.N)))
+    ref = H.oracle_phase1(wl, list(range(wl.N)), with_magnitudes=True)
     H.compare_phase1(out, ref, range(wl.N))
     H.run_dw_check(wl, out, shape, set(range(wl.steps)), sample_untouched=0)
 
