@@ -105,6 +105,10 @@ sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
         return fail(SDM_EHIP, "sdm_phase1: no HIP device");
+    const size_t main_lds = sdm::p1_lds_bytes(s, io);
+    if (main_lds > static_cast<size_t>(lds_max))
+        return fail(SDM_EUNSUPPORTED, "sdm_phase1: the sort/scan kernel needs %zu B of LDS per block, the device has %d",
+                    main_lds, lds_max);
     const size_t tri = static_cast<size_t>(s->C) * (s->C + 1) / 2 * sizeof(float);
     if ((io->a != nullptr || io->qk != nullptr) && tri > static_cast<size_t>(lds_max))
         return fail(SDM_EUNSUPPORTED, "sdm_phase1: a C=%d triangle (%zu B) exceeds the %d B of LDS per block", s->C, tri,
@@ -113,6 +117,7 @@ sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st
     L.s = s;
     L.io = io;
     L.rec = static_cast<char*>(io->workspace) + ws.rec_off;
+    L.aux = static_cast<char*>(io->workspace) + ws.aux_off;
     L.inv = static_cast<char*>(io->workspace) + ws.inv_off;
     const hipError_t e = sdm::p1_launch(L, st);
     if (e != hipSuccess) return fail(SDM_EHIP, "sdm_phase1: %s", hipGetErrorString(e));

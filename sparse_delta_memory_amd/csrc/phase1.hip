@@ -1,13 +1,22 @@
-// Phase 1 of the chunked SDM recurrence on gfx950: one workgroup per chunk sorts the chunk's
-// entries by slot in LDS, runs the two segmented scans and writes every per-entry output, the
-// sorted kind rows, the mover records and the tile bounds; a second kernel sums the A / QK
-// triangles.
+// Phase 1 of the chunked SDM recurrence on gfx950.
+//
+// One 1024-thread workgroup per chunk:
+//   1. sort: the chunk's entries, keyed by local slot, are sorted stably in LDS by an LSD radix
+//      sort whose ranks come from ballot-built peer masks (no atomics, stable by construction);
+//   2. reverse scan: in tiles of 4096 positions, from the last tile to the first, a segmented
+//      scan of the gate contributions and peer counts gives every entry the sum and the peers
+//      after it in its group (written to the workspace record `aux`);
+//   3. forward scan: the same tiles in order give the inclusive log-cumsum, the peers before and
+//      the entry's index in its kind's sorted row (workspace records `rec`, `aux`);
+//   4. output rounds: the records are read back in sorted order (coalesced), every entry-order
+//      field is scattered into an LDS staging area at its entry index and copied out with 16-byte
+//      stores; the sorted-kind rows, mover records and tile bounds are written directly.
+// A second kernel sums the A / QK triangles from the records.
 //
 // Definitions: page "sparse_delta_memory/cuda/phase1_cuda.py" (module docstring; keys and payloads
 // of p1_keys_zw_kernel; the scan semantics of p1_scan_kernel; the pair terms of p1_pairs_kernel).
-// The kernels here are an independent gfx950 design: a wave64 LSD radix sort whose ranks come
-// from ballot-built peer masks (stable by construction, no atomics), TwoSum-compensated
-// segmented scans combined in a fixed tree, and a pair kernel with one writer per output cell.
+// Scans combine TwoSum-compensated float sums in a fixed tree; every output element has one
+// writer; no floating-point atomics are used, so results are bitwise reproducible.
 #include "sdm_device.hpp"
 #include "sdm_launch.hpp"
 
@@ -16,7 +25,25 @@ namespace {
 
 constexpr int kNT = kP1Threads;   // 1024 threads = 16 waves per chunk
 constexpr int kNW = kNT / kWave;
-constexpr int kRadix = 256;       // 8-bit digits
+constexpr int kTileItems = 4;     // scan items per thread per tile
+constexpr int kTile = kNT * kTileItems;
+constexpr uint32_t kFlagHead = 1u << 14;   // group head, kept beside r (< 2^14) in the sorted row
+constexpr uint32_t kFlagRep = 1u << 15;    // repeated K entry (its gate is not applied again)
+constexpr uint32_t kRMask = kFlagHead - 1u;
+
+// Entry-order fields assembled in LDS and copied out with wide stores (plus the inverse
+// permutation for the pair kernel).
+enum Field : int {
+    kFLogK, kFRex, kFCpe, kFKEff, kFIsLast, kFIsOnly, kFPosK,
+    kFLogQ, kFQW, kFPosQ, kFQLast, kFQOnly, kFInv, kNumFields
+};
+constexpr int kMaxRounds = 8;
+
+struct Rounds {
+    int count;
+    uint32_t mask[kMaxRounds];
+    int offset[kNumFields];   // byte offset of a field inside the staging area of its round
+};
 
 struct P1Args {
     const int32_t* k_idx;
@@ -24,28 +51,31 @@ struct P1Args {
     const float* k_val;
     const float* q_val;
     const float* g;
-    float* log_k;
-    float* rex;
-    float* cpe;
-    float* k_eff;
-    int8_t* is_last;
-    int8_t* is_only;
-    int32_t* pos_k;
-    float* log_q;
-    float* q_w;
-    int32_t* pos_q;
-    int8_t* q_last;
-    int8_t* q_only;
+    void* field[kNumFields];   // entry-order destinations (NULL: skipped); kFInv: workspace
     int32_t* spay_k;
     int32_t* spay_q;
     int4* krec;
     int32_t* tiles_k;
     int32_t* repeats;
     uint4* rec;
-    uint32_t* inv;
-    int C, W, R, P, key_bits, first_partial, valid_last, tile_len;
+    uint4* aux;
+    int C, W, R, P, key_bits, first_partial, valid_last, tile_len, digit_bits;
+    int stage_bytes;
+    uint32_t wr_magic;   // ceil(2^32 / (W + R)): r / (W + R) == umulhi(r, wr_magic) for r < 2^17
     int64_t stream_offset;
+    Rounds rounds;
 };
+
+// r / (W + R) for entry indices r < 2^17 and W + R <= 512 (multiply-high by a rounded-up
+// reciprocal; the error term r / 2^32 stays below 1 / (W + R)).
+__device__ __forceinline__ int token_of_entry(int r, uint32_t magic) {
+    return static_cast<int>(__umulhi(static_cast<uint32_t>(r), magic));
+}
+
+__host__ __device__ constexpr int field_bytes(int f) {
+    return (f == kFIsLast || f == kFIsOnly || f == kFQLast || f == kFQOnly) ? 1 : f == kFInv ? 2 : 4;
+}
+__host__ __device__ constexpr bool field_is_q(int f) { return f >= kFLogQ && f <= kFQOnly; }
 
 // Segmented-scan element: a TwoSum-compensated float sum (s + c), the valid K count (bits 0-15),
 // the valid Q count (bits 16-30) and a segment-start flag (bit 31).
@@ -84,10 +114,10 @@ __device__ __forceinline__ Seg seg_shfl(Seg v, int d) {
 }
 
 // Exclusive segmented scan of one element per thread over the block, in thread order
-// (REV: descending thread order). Fixed combine tree: lane doubling, then the wave totals in
-// wave order. wtot: kNW elements of LDS.
+// (REV: descending). Fixed tree: lane doubling, then the wave totals in scan order. `total`
+// receives the block's combined element. wtot: kNW elements of LDS.
 template <bool REV>
-__device__ __forceinline__ Seg block_exclusive_seg(Seg agg, Seg* wtot) {
+__device__ __forceinline__ Seg block_exclusive_seg(Seg agg, Seg* wtot, Seg& total) {
     const int lane = static_cast<int>(lane_id());
     const int w = threadIdx.x / kWave;
     Seg incl = agg;
@@ -100,13 +130,14 @@ __device__ __forceinline__ Seg block_exclusive_seg(Seg agg, Seg* wtot) {
     if (REV ? (lane == kWave - 1) : (lane == 0)) ex = seg_zero();
     if (REV ? (lane == 0) : (lane == kWave - 1)) wtot[w] = incl;
     __syncthreads();
-    Seg pre = seg_zero();
-    if (REV) {
-        for (int ww = kNW - 1; ww > w; --ww) pre = seg_combine(pre, wtot[ww]);
-    } else {
-        for (int ww = 0; ww < w; ++ww) pre = seg_combine(pre, wtot[ww]);
+    Seg pre = seg_zero(), tot = seg_zero();
+    for (int i = 0; i < kNW; ++i) {
+        const int ww = REV ? kNW - 1 - i : i;
+        if (ww == w) pre = tot;
+        tot = seg_combine(tot, wtot[ww]);
     }
     __syncthreads();
+    total = tot;
     return seg_combine(pre, ex);
 }
 
@@ -133,25 +164,29 @@ __device__ __forceinline__ uint32_t block_exclusive_add(uint32_t v, uint32_t* ws
     return pre + incl - v;
 }
 
-// Stable LSD radix sort of the block's kNT * IPT (key, value) pairs over bits [0, bits).
-// Items live in registers in striped order (item k of lane l of wave w is element
-// w * 64 * IPT + k * 64 + l). Per 8-bit digit: ranks inside the wave from ballot-built peer
-// masks processed item slice by item slice (so equal digits keep element order), per-wave digit
-// counts in LDS, their exclusive prefix over (digit, wave), then a scatter into skey / sval.
-// On return skey / sval hold the sorted sequence.
+// Stable LSD radix sort of the block's kNT * IPT (key, value) pairs over key bits [0, bits), in
+// digits of up to `dmax` bits. Items live in registers in striped order (item k of lane l of wave
+// w is element w * 64 * IPT + k * 64 + l). Per digit: ranks inside the wave from ballot-built
+// peer masks, slice by slice (equal digits keep element order); per-wave digit counts in LDS
+// (rows of 2^dmax); one block scan over (digit, wave) gives every (wave, digit) its start; a
+// scatter into skey / sval. On return skey / sval hold the sorted sequence.
 template <int IPT>
-__device__ void block_radix_sort(uint32_t (&key)[IPT], uint32_t (&val)[IPT], int bits, uint32_t* skey,
-                                 uint16_t* sval, uint32_t* hist, uint32_t* dtot, uint32_t* wsum) {
+__device__ void block_radix_sort(uint32_t (&key)[IPT], uint32_t (&val)[IPT], int bits, int dmax, uint32_t* skey,
+                                 uint16_t* sval, uint32_t* hist, uint32_t* wsum) {
     const int lane = static_cast<int>(lane_id());
     const int w = threadIdx.x / kWave;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-    uint32_t* my_hist = hist + w * kRadix;
-    for (int sh = 0; sh < bits; sh += 8) {
-        const int db = min(8, bits - sh);
-        const uint32_t dmask = (1u << db) - 1u;
-        for (int d = lane; d < kRadix; d += kWave) my_hist[d] = 0u;
+    const int stride = 1 << dmax;
+    uint32_t* my_hist = hist + w * stride;
+    const int passes = (bits + dmax - 1) / dmax;
+    for (int pass = 0; pass < passes; ++pass) {
+        const int sh = pass * dmax;
+        const int db = min(dmax, bits - sh);
+        const int nd = 1 << db;
+        const uint32_t dmask = static_cast<uint32_t>(nd - 1);
+        for (int d = lane; d < nd; d += kWave) my_hist[d] = 0u;
         __syncthreads();
-        uint32_t rank[IPT];
+        // The rank inside the wave (< 2^16) rides in the upper half of val (values are < 2^16).
 #pragma unroll
         for (int k = 0; k < IPT; ++k) {
             const uint32_t d = (key[k] >> sh) & dmask;
@@ -164,50 +199,39 @@ __device__ void block_radix_sort(uint32_t (&key)[IPT], uint32_t (&val)[IPT], int
             const uint32_t below = static_cast<uint32_t>(__popcll(peers & lt_mask));
             const uint32_t cnt = static_cast<uint32_t>(__popcll(peers));
             const uint32_t base = my_hist[d];
-            rank[k] = base + below;
+            val[k] = (val[k] & 0xFFFFu) | (base + below) << 16;
             if (below == 0) my_hist[d] = base + cnt;   // the slice's lowest lane of this digit
         }
         __syncthreads();
-        if (threadIdx.x < kRadix) {
-            const int d = threadIdx.x;
-            uint32_t run = 0;
-            for (int ww = 0; ww < kNW; ++ww) {
-                const uint32_t cnt = hist[ww * kRadix + d];
-                hist[ww * kRadix + d] = run;
+        // Exclusive scan over the counts in (digit, wave) order: thread x owns the `per`
+        // consecutive elements e = x * per + u, element e being (digit e / kNW, wave e % kNW).
+        const int per = (nd * kNW + kNT - 1) / kNT;
+        uint32_t local = 0;
+        for (int u = 0; u < per; ++u) {
+            const int e = threadIdx.x * per + u;
+            if (e < nd * kNW) local += hist[(e % kNW) * stride + e / kNW];
+        }
+        uint32_t tot;
+        uint32_t run = block_exclusive_add(local, wsum, tot);
+        for (int u = 0; u < per; ++u) {
+            const int e = threadIdx.x * per + u;
+            if (e < nd * kNW) {
+                uint32_t* h = hist + (e % kNW) * stride + e / kNW;
+                const uint32_t cnt = *h;
+                *h = run;
                 run += cnt;
             }
-            dtot[d] = run;
-        }
-        __syncthreads();
-        uint32_t dv = 0, dincl = 0;
-        if (threadIdx.x < kRadix) {
-            dv = dtot[threadIdx.x];
-            dincl = dv;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const uint32_t x = __shfl_up(dincl, o, kWave);
-                if (lane >= o) dincl += x;
-            }
-            if (lane == kWave - 1) wsum[w] = dincl;
-        }
-        __syncthreads();
-        if (threadIdx.x < kRadix) {
-            const int d = threadIdx.x;
-            uint32_t pre = 0;
-            for (int ww = 0; ww < w; ++ww) pre += wsum[ww];
-            const uint32_t base = pre + dincl - dv;   // exclusive start of digit d
-            for (int ww = 0; ww < kNW; ++ww) hist[ww * kRadix + d] += base;
         }
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < IPT; ++k) {
             const uint32_t d = (key[k] >> sh) & dmask;
-            const uint32_t pos = my_hist[d] + rank[k];
+            const uint32_t pos = my_hist[d] + (val[k] >> 16);
             skey[pos] = key[k];
-            sval[pos] = static_cast<uint16_t>(val[k]);
+            sval[pos] = static_cast<uint16_t>(val[k] & 0xFFFFu);
         }
         __syncthreads();
-        if (sh + 8 < bits) {
+        if (pass + 1 < passes) {
 #pragma unroll
             for (int k = 0; k < IPT; ++k) {
                 const int i = w * kWave * IPT + k * kWave + lane;
@@ -219,17 +243,31 @@ __device__ void block_radix_sort(uint32_t (&key)[IPT], uint32_t (&val)[IPT], int
     }
 }
 
+// Copies `bytes` bytes from LDS to global memory with the whole block: 16-byte accesses when
+// the global destination is 16-byte aligned (the LDS source always is), bytes otherwise.
+__device__ __forceinline__ void block_copy_out(void* dst, const unsigned char* src, int bytes) {
+    int done = 0;
+    if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+        const int vecs = bytes >> 4;
+        for (int i = threadIdx.x; i < vecs; i += kNT) {
+            reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(src)[i];
+        }
+        done = vecs << 4;
+    }
+    for (int i = done + threadIdx.x; i < bytes; i += kNT) static_cast<unsigned char*>(dst)[i] = src[i];
+}
+
 template <int IPT>
 __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int NP = kNT * IPT;
     uint32_t* skey = reinterpret_cast<uint32_t*>(smem);
-    uint16_t* sval = reinterpret_cast<uint16_t*>(skey + NP);
-    uint32_t* hist = reinterpret_cast<uint32_t*>(sval + NP);
-    float* gates = reinterpret_cast<float*>(hist + kNW * kRadix);
+    uint16_t* sval = reinterpret_cast<uint16_t*>(smem + NP * 4);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(smem + NP * 6);
+    unsigned char* stage = smem;   // aliases the sort arrays once the scans are done
+    float* gates = reinterpret_cast<float*>(smem + a.stage_bytes);
     __shared__ Seg wtot[kNW];
     __shared__ uint32_t wsum[kNW];
-    __shared__ uint32_t dtot[kRadix];
 
     const int c = blockIdx.x;
     const int C = a.C, W = a.W, R = a.R;
@@ -237,8 +275,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     const int n = C * wr;
     const int tv = c >= a.first_partial ? a.valid_last : C;
     const int kb = a.key_bits;
-    const uint32_t key_lim = 1u << kb;          // valid keys are below; invalid = key_lim
-    const uint32_t pad_key = (2u << kb) - 1u;   // padding past the row sorts last
+    const uint32_t key_lim = 1u << kb;       // valid keys are below; invalid = key_lim
+    const uint32_t pad_key = 0xFFFFFFFFu;    // padding past the row sorts last
     const int64_t id_base = static_cast<int64_t>(c % a.P) * a.stream_offset;
     const int64_t cw = static_cast<int64_t>(c) * C * W;
     const int64_t cr = static_cast<int64_t>(c) * C * R;
@@ -248,197 +286,277 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
 
     for (int t = threadIdx.x; t < C; t += kNT) gates[t] = t < tv ? a.g[static_cast<int64_t>(c) * C + t] : 0.0f;
 
-    // ---- keys: element i of the striped layout is entry r = i of the chunk.
-    uint32_t key[IPT], val[IPT];
+    // ---- 1. keys (element i of the striped layout is entry r = i) and the sort.
+    {
+        uint32_t key[IPT], val[IPT];
 #pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-        const int i = w * kWave * IPT + k * kWave + lane;
-        val[k] = static_cast<uint32_t>(i);
-        key[k] = pad_key;
-        if (i < n) {
-            const int t = i / wr;
-            const int j = i - t * wr;
-            const int64_t id = j < W ? static_cast<int64_t>(a.k_idx[cw + t * W + j])
-                                     : static_cast<int64_t>(a.q_idx[cr + t * R + (j - W)]);
-            key[k] = t < tv ? static_cast<uint32_t>(id - id_base) & (key_lim - 1u) : key_lim;
+        for (int k = 0; k < IPT; ++k) {
+            const int i = w * kWave * IPT + k * kWave + lane;
+            val[k] = static_cast<uint32_t>(i);
+            key[k] = pad_key;
+            // Branch-free address: every item loads (padding items re-read entry 0), so all the
+            // loads of a thread are in flight together.
+            const int ic = i < n ? i : 0;
+            const int t = token_of_entry(ic, a.wr_magic);
+            const int j = ic - t * wr;
+            const int32_t* src = j < W ? a.k_idx + cw + t * W + j : a.q_idx + cr + t * R + (j - W);
+            const int64_t id = static_cast<int64_t>(*src);
+            const uint32_t kv = t < tv ? static_cast<uint32_t>(id - id_base) & (key_lim - 1u) : key_lim;
+            key[k] = i < n ? kv : pad_key;
+        }
+        // Invalid entries need one more key bit only in a ragged chunk.
+        block_radix_sort<IPT>(key, val, tv < C ? kb + 1 : kb, a.digit_bits, skey, sval, hist, wsum);
+    }
+
+    const int ntiles = (n + kTile - 1) / kTile;
+    uint32_t repeat_count = 0;
+
+    // ---- 2. reverse scan: sums and peer counts after each entry in its group.
+    Seg rcarry = seg_zero();
+    for (int T = ntiles - 1; T >= 0; --T) {
+        const int p0 = T * kTile + threadIdx.x * kTileItems;
+        uint32_t kk[kTileItems], rr[kTileItems];
+#pragma unroll
+        for (int k = 0; k < kTileItems; ++k) {
+            const int p = p0 + k;
+            kk[k] = p < n ? skey[p] : pad_key;
+            rr[k] = p < n ? (sval[p] & kRMask) : 0u;
+        }
+        const bool has_prev = p0 > 0 && p0 <= n;
+        const uint32_t prev_key = has_prev ? skey[p0 - 1] : pad_key;
+        const uint32_t prev_r = has_prev ? (sval[p0 - 1] & kRMask) : 0u;
+        const uint32_t next_key = p0 + kTileItems < n ? skey[p0 + kTileItems] : pad_key;
+        uint32_t heads = 0, ends = 0, reps = 0;
+        float x[kTileItems];
+#pragma unroll
+        for (int k = 0; k < kTileItems; ++k) {
+            const uint32_t pk = k ? kk[k - 1] : prev_key;
+            const uint32_t pr = k ? rr[k - 1] : prev_r;
+            const bool valid = kk[k] < key_lim;
+            const bool pvalid = pk < key_lim && (p0 + k) > 0;
+            const bool head = !valid || !pvalid || kk[k] != pk;
+            const int t = token_of_entry(static_cast<int>(rr[k]), a.wr_magic);
+            const int j = static_cast<int>(rr[k]) - t * wr;
+            const bool is_k = valid && j < W;
+            const int pt = token_of_entry(static_cast<int>(pr), a.wr_magic);
+            const int pj = static_cast<int>(pr) - pt * wr;
+            const bool rep = !head && is_k && pj < W && pt == t;
+            heads |= (head ? 1u : 0u) << k;
+            reps |= (rep ? 1u : 0u) << k;
+            x[k] = (is_k && !rep) ? gates[t] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < kTileItems; ++k) {
+            const bool end = k + 1 < kTileItems ? ((heads >> (k + 1)) & 1u)
+                                                : (!(kk[k] < key_lim) || !(next_key < key_lim) || next_key != kk[k]);
+            ends |= (end ? 1u : 0u) << k;
+        }
+        auto item = [&](int k, bool seg_start) {
+            const bool valid = kk[k] < key_lim;
+            const int t = token_of_entry(static_cast<int>(rr[k]), a.wr_magic);
+            const bool q = static_cast<int>(rr[k]) - t * wr >= W;
+            return Seg{x[k], 0.0f, (valid ? (q ? kSegQOne : 1u) : 0u) | (seg_start ? kSegHead : 0u)};
+        };
+        Seg agg = seg_zero();
+#pragma unroll
+        for (int k = kTileItems - 1; k >= 0; --k) agg = seg_combine(agg, item(k, (ends >> k) & 1u));
+        Seg total;
+        Seg run = seg_combine(rcarry, block_exclusive_seg<true>(agg, wtot, total));
+        rcarry = seg_combine(rcarry, total);
+#pragma unroll
+        for (int k = kTileItems - 1; k >= 0; --k) {
+            const int p = p0 + k;
+            const bool end = (ends >> k) & 1u;
+            const Seg after = end ? seg_zero() : run;
+            run = seg_combine(run, item(k, end));
+            if (p < n) {
+                const bool valid = kk[k] < key_lim;
+                const uint32_t slot = valid ? static_cast<uint32_t>(static_cast<int64_t>(kk[k]) + id_base) : 0u;
+                a.aux[crow + p] = make_uint4(__float_as_uint(after.s + after.c), after.f & ~kSegHead, slot, 0u);
+                sval[p] = static_cast<uint16_t>(rr[k] | (((heads >> k) & 1u) ? kFlagHead : 0u) |
+                                                (((reps >> k) & 1u) ? kFlagRep : 0u));
+                repeat_count += (reps >> k) & 1u;
+            }
         }
     }
-    block_radix_sort<IPT>(key, val, kb + 1, skey, sval, hist, dtot, wsum);
 
-    // ---- scans over the sorted row, blocked layout: thread x holds positions x*IPT .. +IPT-1.
-    const int p0 = threadIdx.x * IPT;
-    uint32_t kk[IPT], rr[IPT];
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-        kk[k] = skey[p0 + k];
-        rr[k] = sval[p0 + k];
-    }
-    const uint32_t prev_key = p0 > 0 ? skey[p0 - 1] : pad_key;
-    const uint32_t prev_r = p0 > 0 ? sval[p0 - 1] : 0u;
-    const uint32_t next_key = p0 + IPT < NP ? skey[p0 + IPT] : pad_key;
+    __syncthreads();   // every flag of the sorted row is set before the forward pass reads it
 
-    // Group heads and ends, gate contributions, repeats.
-    uint32_t heads = 0, ends = 0, repeat_count = 0;
-    float x[IPT];
+    // ---- 3. forward scan: inclusive log-cumsums, peers before, kind-row indices.
+    Seg fcarry = seg_zero();
+    uint32_t kind_carry = 0;
+    for (int T = 0; T < ntiles; ++T) {
+        const int p0 = T * kTile + threadIdx.x * kTileItems;
+        uint32_t rr[kTileItems];
+        float x[kTileItems];
+        uint32_t kind_cnt = 0;
 #pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-        const uint32_t pk = k ? kk[k - 1] : prev_key;
-        const uint32_t pr = k ? rr[k - 1] : prev_r;
-        const bool valid = kk[k] < key_lim;
-        const bool pvalid = pk < key_lim && (p0 + k) > 0;
-        const bool head = !valid || !pvalid || kk[k] != pk;
-        heads |= (head ? 1u : 0u) << k;
-        const int t = static_cast<int>(rr[k]) / wr;
-        const int j = static_cast<int>(rr[k]) - t * wr;
-        const bool is_k = valid && j < W;
-        const int pt = static_cast<int>(pr) / wr;
-        const int pj = static_cast<int>(pr) - pt * wr;
-        const bool rep = !head && is_k && pj < W && pt == t;
-        repeat_count += rep ? 1u : 0u;
-        x[k] = (is_k && !rep) ? gates[t] : 0.0f;
-    }
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-        bool end;
-        if (k + 1 < IPT) {
-            end = (heads >> (k + 1)) & 1u;
-        } else {
-            end = !(kk[k] < key_lim) || !(next_key < key_lim) || next_key != kk[k];
+        for (int k = 0; k < kTileItems; ++k) {
+            const int p = p0 + k;
+            rr[k] = p < n ? sval[p] : kFlagHead;   // padding: a group of its own
+            const int r = static_cast<int>(rr[k] & kRMask);
+            const int t = token_of_entry(r, a.wr_magic);
+            const bool q = r - t * wr >= W;
+            const bool valid = p < n && t < tv;
+            x[k] = (valid && !q && !(rr[k] & kFlagRep)) ? gates[t] : 0.0f;
+            if (p < n) kind_cnt += q ? kSegQOne : 1u;
         }
-        ends |= (end ? 1u : 0u) << k;
-    }
-    auto item = [&](int k, bool seg_start) {
-        const bool valid = kk[k] < key_lim;
-        const int t = static_cast<int>(rr[k]) / wr;
-        const bool q = static_cast<int>(rr[k]) - t * wr >= W;
-        const uint32_t f = (valid ? (q ? kSegQOne : 1u) : 0u) | (seg_start ? kSegHead : 0u);
-        return Seg{x[k], 0.0f, f};
-    };
-
-    // Reverse pass: sums and peer counts after each entry inside its group.
-    Seg agg = seg_zero();
+        auto item = [&](int k) {
+            const int p = p0 + k;
+            const int r = static_cast<int>(rr[k] & kRMask);
+            const int t = token_of_entry(r, a.wr_magic);
+            const bool q = r - t * wr >= W;
+            const bool valid = p < n && t < tv;
+            return Seg{x[k], 0.0f, (valid ? (q ? kSegQOne : 1u) : 0u) | ((rr[k] & kFlagHead) ? kSegHead : 0u)};
+        };
+        Seg agg = seg_zero();
 #pragma unroll
-    for (int k = IPT - 1; k >= 0; --k) agg = seg_combine(agg, item(k, (ends >> k) & 1u));
-    Seg run = block_exclusive_seg<true>(agg, wtot);
-    float rexv[IPT];
-    uint32_t aft[IPT];
+        for (int k = 0; k < kTileItems; ++k) agg = seg_combine(agg, item(k));
+        Seg total;
+        Seg run = seg_combine(fcarry, block_exclusive_seg<false>(agg, wtot, total));
+        fcarry = seg_combine(fcarry, total);
+        uint32_t kind_total;
+        const uint32_t kind_base = kind_carry + block_exclusive_add(kind_cnt, wsum, kind_total);
+        kind_carry += kind_total;
+        uint32_t jk = kind_base & 0xFFFFu, jq = kind_base >> 16;
 #pragma unroll
-    for (int k = IPT - 1; k >= 0; --k) {
-        const Seg after = ((ends >> k) & 1u) ? seg_zero() : run;
-        rexv[k] = after.s + after.c;
-        aft[k] = after.f & ~kSegHead;
-        run = seg_combine(run, item(k, (ends >> k) & 1u));
-    }
-
-    // Forward pass: inclusive log-cumsums, peers before, and every output.
-    agg = seg_zero();
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) agg = seg_combine(agg, item(k, (heads >> k) & 1u));
-    run = block_exclusive_seg<false>(agg, wtot);
-    // Index of each entry in its kind's sorted row: plain counts of K-kind and Q-kind entries.
-    uint32_t kind_cnt = 0;
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-        if (p0 + k < n) {
-            const int t = static_cast<int>(rr[k]) / wr;
-            kind_cnt += (static_cast<int>(rr[k]) - t * wr >= W) ? kSegQOne : 1u;
+        for (int k = 0; k < kTileItems; ++k) {
+            const int p = p0 + k;
+            const bool head = rr[k] & kFlagHead;
+            const Seg before = head ? seg_zero() : run;
+            run = seg_combine(run, item(k));
+            if (p >= n) continue;
+            const int r = static_cast<int>(rr[k] & kRMask);
+            const int t = token_of_entry(r, a.wr_magic);
+            const int j = r - t * wr;
+            const bool q = j >= W;
+            const int ln = q ? j - W : j;
+            const bool valid = t < tv;
+            const uint32_t pay = static_cast<uint32_t>(ln) | (q ? kIsQ : 0u) | (static_cast<uint32_t>(t) << kTokShift) |
+                                 (valid ? 0u : kInvalid);
+            const float v = valid ? (q ? a.q_val[cr + t * R + ln] : a.k_val[cw + t * W + ln]) : 0.0f;
+            const uint32_t bcnt = q ? ((before.f >> 16) & 0x7FFFu) : (before.f & 0xFFFFu);
+            const uint32_t jkind = q ? jq : jk;
+            a.rec[crow + p] = make_uint4(pay | (head ? kHead : 0u), __float_as_uint(run.s), __float_as_uint(run.c),
+                                         __float_as_uint(v));
+            reinterpret_cast<uint32_t*>(a.aux + crow + p)[3] = bcnt | jkind << 16;
+            jq += q ? 1u : 0u;
+            jk += q ? 0u : 1u;
         }
     }
-    uint32_t kind_total;
-    const uint32_t kind_base = block_exclusive_add(kind_cnt, wsum, kind_total);
-    uint32_t jk = kind_base & 0xFFFFu, jq = kind_base >> 16;
-    uint32_t rep_total;
-    (void)block_exclusive_add(repeat_count, wsum, rep_total);
-    if (threadIdx.x == 0 && a.repeats != nullptr) a.repeats[c] = static_cast<int32_t>(rep_total);
+    {
+        uint32_t rep_total;
+        (void)block_exclusive_add(repeat_count, wsum, rep_total);
+        if (threadIdx.x == 0 && a.repeats != nullptr) a.repeats[c] = static_cast<int32_t>(rep_total);
+    }
+    __syncthreads();   // the records are complete (and the sort arrays free for staging)
 
+    // ---- 4. output rounds over the sorted positions (striped: coalesced record reads).
     const int nk = C * W;
     const int L = a.tile_len;
     const int ntk = (nk + L - 1) / L;
     const int64_t tb = static_cast<int64_t>(c) * (ntk + 1);
     if (threadIdx.x == 0) a.tiles_k[tb + ntk] = nk;
-
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-        const bool head = (heads >> k) & 1u;
-        const Seg before = head ? seg_zero() : run;
-        run = seg_combine(run, item(k, head));
-        const int rho = p0 + k;
-        if (rho >= n) continue;
-        const bool valid = kk[k] < key_lim;
-        const int t = static_cast<int>(rr[k]) / wr;
-        const int j = static_cast<int>(rr[k]) - t * wr;
-        const bool q = j >= W;
-        const int ln = q ? j - W : j;
-        const uint32_t bcnt = q ? ((before.f >> 16) & 0x7FFFu) : (before.f & 0xFFFFu);
-        const uint32_t acnt = q ? ((aft[k] >> 16) & 0x7FFFu) : (aft[k] & 0xFFFFu);
-        const uint32_t pay = static_cast<uint32_t>(ln) | (q ? kIsQ : 0u) | (static_cast<uint32_t>(t) << kTokShift) |
-                             (valid ? 0u : kInvalid);
-        const uint32_t packed = valid ? (static_cast<uint32_t>(rho) | min(acnt, kPosCountMax) << kPosAfterShift |
-                                         min(bcnt + 1u + acnt, kPosCountMax) << kPosSizeShift)
-                                      : static_cast<uint32_t>(rho);
-        const uint32_t elem = valid ? ((pay & kEntryMask) | min(bcnt, kDistMax) << kDistShift |
-                                       (bcnt == 0 ? kFirst : 0u) | (acnt == 0 ? kLast : 0u))
-                                    : (pay | kFirst | kLast);
-        const float Lv = run.s + run.c;
-        const float v = valid ? (q ? a.q_val[cr + t * R + ln] : a.k_val[cw + t * W + ln]) : 0.0f;
-        const float ef = expf(Lv);
-        if (q) {
-            const int64_t o = cr + t * R + ln;
-            if (a.log_q) a.log_q[o] = Lv;
-            if (a.q_w) a.q_w[o] = v * ef;
-            if (a.pos_q) a.pos_q[o] = static_cast<int32_t>(packed);
-            const bool ql = valid && acnt == 0;
-            if (a.q_last) a.q_last[o] = ql ? 1 : 0;
-            if (a.q_only) a.q_only[o] = (ql && bcnt == 0) ? 1 : 0;
-            if (a.spay_q) a.spay_q[cr + jq] = static_cast<int32_t>(elem);
-            ++jq;
-        } else {
-            const int64_t o = cw + t * W + ln;
+    for (int rd = 0; rd < a.rounds.count; ++rd) {
+        const uint32_t mask = a.rounds.mask[rd];
+        for (int p = threadIdx.x; p < n; p += kNT) {
+            const uint4 re = a.rec[crow + p];
+            const uint4 ax = a.aux[crow + p];
+            const uint32_t pay = re.x & kEntryMask;
+            const bool q = pay & kIsQ;
+            const bool valid = !(pay & kInvalid);
+            const int t = static_cast<int>((pay >> kTokShift) & 0xFFu);
+            const int ln = static_cast<int>(pay & 0xFFu);
+            const float rs = __uint_as_float(re.y), rc = __uint_as_float(re.z), v = __uint_as_float(re.w);
+            const float Lv = rs + rc;
+            const float rexv = __uint_as_float(ax.x);
+            const uint32_t acnt = q ? ((ax.y >> 16) & 0x7FFFu) : (ax.y & 0xFFFFu);
+            const uint32_t bcnt = ax.w & 0xFFFFu;
+            const uint32_t jkind = ax.w >> 16;
+            auto stage_at = [&](int f, int idx) { return stage + a.rounds.offset[f] + idx * field_bytes(f); };
             // exp of the group total: the compensated log-cumsum plus the sum after (TwoSum).
-            const float gs = run.s + rexv[k];
-            const float gb = gs - run.s;
-            const float ge = (run.s - (gs - gb)) + (rexv[k] - gb);
-            const float G = gs + (run.c + ge);
-            const float cpe_v = valid ? expf(G) : 1.0f;
-            const bool last = valid && acnt == 0;
-            if (a.log_k) a.log_k[o] = Lv;
-            if (a.rex) a.rex[o] = rexv[k];
-            if (a.cpe) a.cpe[o] = cpe_v;
-            if (a.k_eff) a.k_eff[o] = v * ef;
-            if (a.is_last) a.is_last[o] = last ? 1 : 0;
-            if (a.is_only) a.is_only[o] = (last && bcnt == 0) ? 1 : 0;
-            if (a.pos_k) a.pos_k[o] = static_cast<int32_t>(packed);
-            a.spay_k[cw + jk] = static_cast<int32_t>(elem);
-            const float sc = valid ? v * expf(rexv[k]) : 0.0f;
-            const int32_t slot = valid ? static_cast<int32_t>(static_cast<int64_t>(kk[k]) + id_base) : 0;
-            a.krec[cw + jk] = make_int4(static_cast<int32_t>(elem), slot, __float_as_int(sc), __float_as_int(cpe_v));
-            if (static_cast<int>(jk) % L == 0) {
-                const int ti = static_cast<int>(jk) / L;
-                a.tiles_k[tb + ti] = (elem & kFirst) ? static_cast<int>(jk) : min(static_cast<int>(jk + acnt + 1u), nk);
+            auto group_exp = [&]() {
+                const float gs = rs + rexv;
+                const float gb = gs - rs;
+                const float ge = (rs - (gs - gb)) + (rexv - gb);
+                return valid ? expf(gs + (rc + ge)) : 1.0f;
+            };
+            const uint32_t packed =
+                valid ? (static_cast<uint32_t>(p) | min(acnt, kPosCountMax) << kPosAfterShift |
+                         min(bcnt + 1u + acnt, kPosCountMax) << kPosSizeShift)
+                      : static_cast<uint32_t>(p);
+            if (q) {
+                const int o = t * R + ln;
+                if (mask & (1u << kFLogQ)) *reinterpret_cast<float*>(stage_at(kFLogQ, o)) = Lv;
+                if (mask & (1u << kFQW)) *reinterpret_cast<float*>(stage_at(kFQW, o)) = v * expf(Lv);
+                if (mask & (1u << kFPosQ)) *reinterpret_cast<uint32_t*>(stage_at(kFPosQ, o)) = packed;
+                const bool ql = valid && acnt == 0;
+                if (mask & (1u << kFQLast)) *stage_at(kFQLast, o) = ql ? 1 : 0;
+                if (mask & (1u << kFQOnly)) *stage_at(kFQOnly, o) = (ql && bcnt == 0) ? 1 : 0;
+            } else {
+                const int o = t * W + ln;
+                const bool last = valid && acnt == 0;
+                if (mask & (1u << kFLogK)) *reinterpret_cast<float*>(stage_at(kFLogK, o)) = Lv;
+                if (mask & (1u << kFRex)) *reinterpret_cast<float*>(stage_at(kFRex, o)) = rexv;
+                if (mask & (1u << kFCpe)) *reinterpret_cast<float*>(stage_at(kFCpe, o)) = group_exp();
+                if (mask & (1u << kFKEff)) *reinterpret_cast<float*>(stage_at(kFKEff, o)) = v * expf(Lv);
+                if (mask & (1u << kFIsLast)) *stage_at(kFIsLast, o) = last ? 1 : 0;
+                if (mask & (1u << kFIsOnly)) *stage_at(kFIsOnly, o) = (last && bcnt == 0) ? 1 : 0;
+                if (mask & (1u << kFPosK)) *reinterpret_cast<uint32_t*>(stage_at(kFPosK, o)) = packed;
             }
-            ++jk;
+            if (mask & (1u << kFInv)) {
+                *reinterpret_cast<uint16_t*>(stage_at(kFInv, t * wr + (q ? W + ln : ln))) = static_cast<uint16_t>(p);
+            }
+            if (rd == 0) {
+                // Sorted kind rows, mover records and tile bounds (consecutive positions of a kind
+                // have consecutive indices, so these stores are nearly contiguous).
+                const uint32_t elem = valid ? (pay | min(bcnt, kDistMax) << kDistShift | (bcnt == 0 ? kFirst : 0u) |
+                                               (acnt == 0 ? kLast : 0u))
+                                            : (pay | kFirst | kLast);
+                if (q) {
+                    if (a.spay_q) a.spay_q[cr + jkind] = static_cast<int32_t>(elem);
+                } else {
+                    a.spay_k[cw + jkind] = static_cast<int32_t>(elem);
+                    const float sc = valid ? v * expf(rexv) : 0.0f;
+                    a.krec[cw + jkind] = make_int4(static_cast<int32_t>(elem), static_cast<int32_t>(ax.z),
+                                                   __float_as_int(sc), __float_as_int(group_exp()));
+                    if (static_cast<int>(jkind) % L == 0) {
+                        a.tiles_k[tb + static_cast<int>(jkind) / L] =
+                            (elem & kFirst) ? static_cast<int>(jkind) : min(static_cast<int>(jkind + acnt + 1u), nk);
+                    }
+                }
+            }
         }
-        a.rec[crow + rho] = make_uint4(pay | (head ? kHead : 0u), __float_as_uint(run.s), __float_as_uint(run.c),
-                                       __float_as_uint(v));
-        a.inv[crow + rr[k]] = static_cast<uint32_t>(rho);
+        __syncthreads();
+        for (int f = 0; f < kNumFields; ++f) {
+            if (!(mask & (1u << f))) continue;
+            const int cnt = f == kFInv ? n : field_is_q(f) ? C * R : C * W;
+            const int64_t base = f == kFInv ? crow : field_is_q(f) ? cr : cw;
+            unsigned char* dst = static_cast<unsigned char*>(a.field[f]) + base * field_bytes(f);
+            block_copy_out(dst, stage + a.rounds.offset[f], cnt * field_bytes(f));
+        }
+        __syncthreads();
     }
 }
 
-// Pair sums. Block (chunk, triangle): one thread per row i walks the entries of token i of its
-// kind (K for A, Q for QK) in lane order; each walk goes from the entry's nearest earlier entry of
-// its group back to the group head and adds, per earlier K entry f of token j (j != i for A),
-// val_e * val_f * exp(L_e - L_f) to cell (i, j) with its own rounding. Every cell has one writer
-// thread and a fixed term order. The triangle lives in LDS and is written out as a dense [C, C]
-// matrix with zeros outside it.
+// Pair sums. Block (chunk, triangle): one thread per row i. Token i's entries of the block's kind
+// (K for A, Q for QK) that share a slot sit next to each other in the sorted row and share one
+// log-cumsum, and so do the K entries of any earlier token j in that group. For every group the
+// row meets, the thread sums token i's values (w_i) once, then walks the group from just before
+// token i's entries back to its head, summing each earlier token's K values (k_j) over its run,
+// and adds w_i * k_j * exp(L_i - L_j) to cell (i, j) (j != i for A). Every cell has one writer
+// thread and a term order fixed by the input; the triangle lives in LDS and is written out as a
+// dense [C, C] matrix with zeros outside it.
 struct PairArgs {
     const uint4* rec;
-    const uint32_t* inv;
+    const uint16_t* inv;
     float* a;
     float* qk;
     int C, W, R, first_partial, valid_last;
 };
 
 constexpr int kPairThreads = 256;
+constexpr int kWalkBatch = 8;
 
 __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -456,49 +574,145 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
     __syncthreads();
     const int64_t crow = static_cast<int64_t>(c) * n;
     const uint4* rec = a.rec + crow;
+    const uint16_t* inv = a.inv + crow;
     const int i = threadIdx.x;
     if (i < tv) {
         float* row = tri + i * (i + 1) / 2;
         const int lanes = q ? R : W;
+        // Token i's entries of this kind: (Q flag, token) bits of the payload.
+        const uint32_t own_tag = (q ? kIsQ : 0u) | (static_cast<uint32_t>(i) << kTokShift);
+        const uint32_t tag_mask = kIsQ | (0xFFu << kTokShift);
         for (int ln = 0; ln < lanes; ++ln) {
-            const int r = i * wr + (q ? W + ln : ln);
-            const uint32_t rho = a.inv[crow + r];
+            const int rho = inv[i * wr + (q ? W + ln : ln)];
             const uint4 own = rec[rho];
-            if (own.x & kHead) continue;
-            const float se = __uint_as_float(own.y), ce = __uint_as_float(own.z), ve = __uint_as_float(own.w);
-            for (int p = static_cast<int>(rho) - 1; p >= 0; --p) {
-                const uint4 f = rec[p];
-                if (!(f.x & (kIsQ | kInvalid))) {
-                    const int jt = static_cast<int>((f.x >> kTokShift) & 0xFFu);
-                    if (q || jt != i) {
-                        const float d = (se - __uint_as_float(f.y)) + (ce - __uint_as_float(f.z));
-                        const float term = (ve * __uint_as_float(f.w)) * expf(d);
-                        row[jt] = row[jt] + term;
-                    }
-                }
-                if (f.x & kHead) break;
+            if (own.x & kHead) continue;   // first of its group: nothing earlier
+            if ((rec[rho - 1].x & tag_mask) == own_tag) continue;   // not the first of token i's run
+            // rho starts token i's run of this kind in its group: sum the run's values.
+            float wi = __uint_as_float(own.w);
+            for (int p = rho + 1; p < n; ++p) {
+                const uint4 nx = rec[p];
+                if ((nx.x & kHead) || (nx.x & tag_mask) != own_tag) break;
+                wi = wi + __uint_as_float(nx.w);
             }
+            const float se = __uint_as_float(own.y), ce = __uint_as_float(own.z);
+            // Walk back to the head; the K runs of earlier tokens are summed, then one term each.
+            int cur_j = -1;
+            float kj = 0.0f, sj = 0.0f, cj = 0.0f;
+            bool done = false;
+            for (int top = rho - 1; !done; top -= kWalkBatch) {
+                uint4 rb[kWalkBatch];
+#pragma unroll
+                for (int k = 0; k < kWalkBatch; ++k) rb[k] = rec[max(top - k, 0)];
+#pragma unroll
+                for (int k = 0; k < kWalkBatch; ++k) {
+                    if (done) break;
+                    const uint32_t px = rb[k].x;
+                    if (!(px & (kIsQ | kInvalid))) {
+                        const int jt = static_cast<int>((px >> kTokShift) & 0xFFu);
+                        if (jt != cur_j) {
+                            if (cur_j >= 0 && (q || cur_j != i)) {
+                                row[cur_j] = row[cur_j] + (wi * kj) * expf((se - sj) + (ce - cj));
+                            }
+                            cur_j = jt;
+                            kj = 0.0f;
+                            sj = __uint_as_float(rb[k].y);
+                            cj = __uint_as_float(rb[k].z);
+                        }
+                        kj = kj + __uint_as_float(rb[k].w);
+                    }
+                    done = (px & kHead) != 0;
+                }
+            }
+            if (cur_j >= 0 && (q || cur_j != i)) row[cur_j] = row[cur_j] + (wi * kj) * expf((se - sj) + (ce - cj));
         }
     }
     __syncthreads();
     const int64_t ob = static_cast<int64_t>(c) * C * C;
-    for (int e = threadIdx.x; e < C * C; e += kPairThreads) {
-        const int ii = e / C;
-        const int jj = e - ii * C;
-        const bool inside = q ? (jj <= ii) : (jj < ii);
-        out[ob + e] = inside ? tri[ii * (ii + 1) / 2 + jj] : 0.0f;
+    if ((C & 3) == 0 && ((reinterpret_cast<uintptr_t>(out + ob) & 15u) == 0)) {
+        const int c4 = C >> 2;
+        for (int e = threadIdx.x; e < C * c4; e += kPairThreads) {
+            const int ii = e / c4;
+            const int j0 = (e - ii * c4) << 2;
+            const float* trow = tri + ii * (ii + 1) / 2;
+            float v4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int jj = j0 + u;
+                v4[u] = (q ? jj <= ii : jj < ii) ? trow[jj] : 0.0f;
+            }
+            reinterpret_cast<float4*>(out + ob)[e] = make_float4(v4[0], v4[1], v4[2], v4[3]);
+        }
+    } else {
+        for (int e = threadIdx.x; e < C * C; e += kPairThreads) {
+            const int ii = e / C;
+            const int jj = e - ii * C;
+            out[ob + e] = (q ? jj <= ii : jj < ii) ? tri[ii * (ii + 1) / 2 + jj] : 0.0f;
+        }
     }
 }
 
-template <int IPT>
-size_t main_lds_bytes() {
-    return static_cast<size_t>(kNT) * IPT * (sizeof(uint32_t) + sizeof(uint16_t)) + kNW * kRadix * sizeof(uint32_t) +
-           256 * sizeof(float);
+// Host-side plan of one Phase-1 launch: sort items per thread, digit width, staging rounds.
+struct MainPlan {
+    int ipt;
+    int digit_bits;
+    int stage_bytes;
+    size_t lds_bytes;
+    Rounds rounds;
+};
+
+constexpr int kLdsBudget = 160 * 1024 - 2048;   // dynamic LDS per block (static scratch aside)
+
+int field_count(const sdm_p1_shape* s, int f) {
+    const int n = s->C * (s->W + s->R);
+    return f == kFInv ? n : field_is_q(f) ? s->C * s->R : s->C * s->W;
+}
+
+MainPlan plan_main(const sdm_p1_shape* s, const sdm_p1_io* io, void* inv) {
+    MainPlan m;
+    const int n = s->C * (s->W + s->R);
+    m.ipt = n <= kNT ? 1 : n <= 2 * kNT ? 2 : n <= 4 * kNT ? 4 : n <= 8 * kNT ? 8 : 16;
+    const int np = kNT * m.ipt;
+    const int gate_bytes = 256 * static_cast<int>(sizeof(float));
+    // Widest digit (<= 10 bits) whose per-wave counts fit beside the sort arrays.
+    int d = 10;
+    while (d > 4 && np * 6 + kNW * (1 << d) * 4 + gate_bytes > kLdsBudget) --d;
+    m.digit_bits = d;
+    const int sort_bytes = np * 6 + kNW * (1 << d) * 4;
+    const void* dst[kNumFields] = {io->log_k, io->rex, io->cpe, io->k_eff, io->is_last, io->is_only, io->pos_k,
+                                   io->log_q, io->q_w, io->pos_q, io->q_last, io->q_only, inv};
+    // Staging capacity: the sort's bytes, raised to hold four of the largest field when LDS allows.
+    int big = 0;
+    for (int f = 0; f < kNumFields; ++f) big = max(big, (field_count(s, f) * field_bytes(f) + 15) / 16 * 16);
+    int cap = max(sort_bytes, min(4 * big, kLdsBudget - gate_bytes));
+    cap = max(cap, big) / 16 * 16;
+    // Greedy packing of the requested fields, in order, into rounds of `cap` bytes.
+    m.rounds.count = 0;
+    for (int r = 0; r < kMaxRounds; ++r) m.rounds.mask[r] = 0u;
+    int used = cap;   // forces a new round for the first field
+    for (int f = 0; f < kNumFields; ++f) {
+        m.rounds.offset[f] = 0;
+        if (dst[f] == nullptr) continue;
+        const int bytes = (field_count(s, f) * field_bytes(f) + 15) / 16 * 16;
+        if (used + bytes > cap) {
+            if (m.rounds.count == kMaxRounds) {   // cannot happen for n <= 16384 (>= 2 fields a round)
+                m.rounds.count = kMaxRounds + 1;
+                return m;
+            }
+            ++m.rounds.count;
+            used = 0;
+        }
+        m.rounds.offset[f] = used;
+        m.rounds.mask[m.rounds.count - 1] |= 1u << f;
+        used += bytes;
+    }
+    if (m.rounds.count == 0) m.rounds.count = 1;   // round 0 also writes the kind rows
+    m.stage_bytes = (max(cap, sort_bytes) + 15) / 16 * 16;
+    m.lds_bytes = static_cast<size_t>(m.stage_bytes) + gate_bytes;
+    return m;
 }
 
 template <int IPT>
-hipError_t launch_main(const P1Args& args, int N, hipStream_t st) {
-    const size_t lds = main_lds_bytes<IPT>();
+hipError_t launch_main(const P1Args& args, size_t lds, int N, hipStream_t st) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&p1_main_kernel<IPT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
@@ -511,13 +725,17 @@ hipError_t launch_main(const P1Args& args, int N, hipStream_t st) {
 P1Workspace p1_workspace_layout(const sdm_p1_shape* s) {
     const size_t n = static_cast<size_t>(s->C) * static_cast<size_t>(s->W + s->R);
     const size_t N = static_cast<size_t>(s->N);
+    auto up = [](size_t b) { return (b + 255) / 256 * 256; };
     P1Workspace w;
     w.rec_off = 0;
-    const size_t rec_bytes = N * n * sizeof(uint4);
-    w.inv_off = (rec_bytes + 255) / 256 * 256;
-    const size_t inv_bytes = N * n * sizeof(uint32_t);
-    w.total = w.inv_off + (inv_bytes + 255) / 256 * 256;
+    w.aux_off = up(N * n * sizeof(uint4));
+    w.inv_off = w.aux_off + up(N * n * sizeof(uint4));
+    w.total = w.inv_off + up(N * n * sizeof(uint16_t));
     return w;
+}
+
+size_t p1_lds_bytes(const sdm_p1_shape* s, const sdm_p1_io* io) {
+    return plan_main(s, io, reinterpret_cast<void*>(uintptr_t(1))).lds_bytes;
 }
 
 hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
@@ -530,25 +748,16 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     a.k_val = io->k_val;
     a.q_val = io->q_val;
     a.g = io->g;
-    a.log_k = io->log_k;
-    a.rex = io->rex;
-    a.cpe = io->cpe;
-    a.k_eff = io->k_eff;
-    a.is_last = io->is_last;
-    a.is_only = io->is_only;
-    a.pos_k = io->pos_k;
-    a.log_q = io->log_q;
-    a.q_w = io->q_w;
-    a.pos_q = io->pos_q;
-    a.q_last = io->q_last;
-    a.q_only = io->q_only;
+    void* fields[kNumFields] = {io->log_k, io->rex, io->cpe, io->k_eff, io->is_last, io->is_only, io->pos_k,
+                                io->log_q, io->q_w, io->pos_q, io->q_last, io->q_only, Lc.inv};
+    for (int f = 0; f < kNumFields; ++f) a.field[f] = fields[f];
     a.spay_k = io->spay_k;
     a.spay_q = io->spay_q;
     a.krec = reinterpret_cast<int4*>(io->krec);
     a.tiles_k = io->tiles_k;
     a.repeats = io->repeats;
     a.rec = static_cast<uint4*>(Lc.rec);
-    a.inv = static_cast<uint32_t*>(Lc.inv);
+    a.aux = static_cast<uint4*>(Lc.aux);
     a.C = s->C;
     a.W = s->W;
     a.R = s->R;
@@ -558,19 +767,21 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     a.valid_last = s->valid_last;
     a.tile_len = s->tile_len;
     a.stream_offset = s->stream_offset;
-    const int n = s->C * (s->W + s->R);
+    a.wr_magic = static_cast<uint32_t>(((uint64_t(1) << 32) + static_cast<uint64_t>(s->W + s->R) - 1) /
+                                       static_cast<uint64_t>(s->W + s->R));
+    const MainPlan m = plan_main(s, io, Lc.inv);
+    if (m.rounds.count > kMaxRounds) return hipErrorInvalidValue;
+    a.digit_bits = m.digit_bits;
+    a.stage_bytes = m.stage_bytes;
+    a.rounds = m.rounds;
     hipError_t e;
     if (io->events != nullptr && (e = hipEventRecord(io->events[0], st)) != hipSuccess) return e;
-    if (n <= kNT) {
-        e = launch_main<1>(a, s->N, st);
-    } else if (n <= 2 * kNT) {
-        e = launch_main<2>(a, s->N, st);
-    } else if (n <= 4 * kNT) {
-        e = launch_main<4>(a, s->N, st);
-    } else if (n <= 8 * kNT) {
-        e = launch_main<8>(a, s->N, st);
-    } else {
-        e = launch_main<16>(a, s->N, st);
+    switch (m.ipt) {
+        case 1: e = launch_main<1>(a, m.lds_bytes, s->N, st); break;
+        case 2: e = launch_main<2>(a, m.lds_bytes, s->N, st); break;
+        case 4: e = launch_main<4>(a, m.lds_bytes, s->N, st); break;
+        case 8: e = launch_main<8>(a, m.lds_bytes, s->N, st); break;
+        default: e = launch_main<16>(a, m.lds_bytes, s->N, st); break;
     }
     if (e != hipSuccess) return e;
     if (io->events != nullptr && (e = hipEventRecord(io->events[1], st)) != hipSuccess) return e;
@@ -579,7 +790,7 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     }
     PairArgs pa;
     pa.rec = a.rec;
-    pa.inv = a.inv;
+    pa.inv = static_cast<const uint16_t*>(Lc.inv);
     pa.a = io->a;
     pa.qk = io->qk;
     pa.C = s->C;

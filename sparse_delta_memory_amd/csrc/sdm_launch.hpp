@@ -16,15 +16,19 @@ constexpr int kP1Threads = 1024;
 struct P1Launch {
     const sdm_p1_shape* s;
     const sdm_p1_io* io;
-    void* rec;        // [N, n] 16-byte pair records (workspace)
-    void* inv;        // [N, n] uint32 inverse permutation (workspace)
+    void* rec;        // [N, n] 16-byte records in sorted order: payload | head, log-cumsum (s, c), value
+    void* aux;        // [N, n] 16-byte records: sum after, peers after, slot, peers before | kind index
+    void* inv;        // [N, n] uint16 sorted position of every entry (entry order)
 };
 
-// Workspace layout of sdm_phase1: byte offsets of the two regions and the total.
+// Workspace layout of sdm_phase1: byte offsets of the three regions and the total.
 struct P1Workspace {
-    size_t rec_off, inv_off, total;
+    size_t rec_off, aux_off, inv_off, total;
 };
 P1Workspace p1_workspace_layout(const sdm_p1_shape* s);
+
+// Dynamic LDS bytes of the Phase-1 sort/scan kernel for this shape and output set.
+size_t p1_lds_bytes(const sdm_p1_shape* s, const sdm_p1_io* io);
 
 // Enqueue the Phase-1 kernels; returns hipSuccess or the first launch error.
 hipError_t p1_launch(const P1Launch& L, hipStream_t st);
