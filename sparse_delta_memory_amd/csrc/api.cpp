@@ -117,8 +117,8 @@ sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st
     L.s = s;
     L.io = io;
     L.rec = static_cast<char*>(io->workspace) + ws.rec_off;
-    L.aux = static_cast<char*>(io->workspace) + ws.aux_off;
     L.inv = static_cast<char*>(io->workspace) + ws.inv_off;
+    L.walk = static_cast<char*>(io->workspace) + ws.walk_off;
     const hipError_t e = sdm::p1_launch(L, st);
     if (e != hipSuccess) return fail(SDM_EHIP, "sdm_phase1: %s", hipGetErrorString(e));
     return SDM_OK;

@@ -3,15 +3,16 @@
 // One 1024-thread workgroup per chunk:
 //   1. sort: the chunk's entries, keyed by local slot, are sorted stably in LDS by an LSD radix
 //      sort whose ranks come from ballot-built peer masks (no atomics, stable by construction);
-//   2. reverse scan: in tiles of 4096 positions, from the last tile to the first, a segmented
-//      scan of the gate contributions and peer counts gives every entry the sum and the peers
-//      after it in its group (written to the workspace record `aux`);
-//   3. forward scan: the same tiles in order give the inclusive log-cumsum, the peers before and
-//      the entry's index in its kind's sorted row (workspace records `rec`, `aux`);
-//   4. output rounds: the records are read back in sorted order (coalesced), every entry-order
-//      field is scattered into an LDS staging area at its entry index and copied out with 16-byte
-//      stores; the sorted-kind rows, mover records and tile bounds are written directly.
-// A second kernel sums the A / QK triangles from the records.
+//   2. reverse scan: in tiles of 4096 sorted positions (4 per thread), last tile first, a
+//      segmented scan of gate contributions and peer counts; each thread keeps its exclusive
+//      prefix per tile in registers, plus its entries' values;
+//   3. forward scan: the same tiles in order; each thread keeps its forward prefix and kind-row
+//      base per tile. After these two passes every per-entry quantity can be recomputed by a
+//      thread from its own registers and the sorted row, with no further block-wide work;
+//   4. output rounds: entry-order fields are scattered into LDS at their entry index and copied
+//      out with 16-byte stores; sorted-order records (for the pair kernel), the sorted kind rows
+//      and the mover records are staged tile by tile (their indices are contiguous per tile).
+// A second kernel sums the A / QK triangles.
 //
 // Definitions: page "sparse_delta_memory/cuda/phase1_cuda.py" (module docstring; keys and payloads
 // of p1_keys_zw_kernel; the scan semantics of p1_scan_kernel; the pair terms of p1_pairs_kernel).
@@ -31,11 +32,12 @@ constexpr uint32_t kFlagHead = 1u << 14;   // group head, kept beside r (< 2^14)
 constexpr uint32_t kFlagRep = 1u << 15;    // repeated K entry (its gate is not applied again)
 constexpr uint32_t kRMask = kFlagHead - 1u;
 
-// Entry-order fields assembled in LDS and copied out with wide stores (plus the inverse
-// permutation for the pair kernel).
+// Entry-order fields assembled in LDS and copied out with wide stores: the outputs, then two
+// workspace arrays for the pair kernel (sorted position of every entry; "starts a run with
+// earlier K entries in its group").
 enum Field : int {
     kFLogK, kFRex, kFCpe, kFKEff, kFIsLast, kFIsOnly, kFPosK,
-    kFLogQ, kFQW, kFPosQ, kFQLast, kFQOnly, kFInv, kNumFields
+    kFLogQ, kFQW, kFPosQ, kFQLast, kFQOnly, kFInv, kFWalk, kNumFields
 };
 constexpr int kMaxRounds = 8;
 
@@ -51,14 +53,13 @@ struct P1Args {
     const float* k_val;
     const float* q_val;
     const float* g;
-    void* field[kNumFields];   // entry-order destinations (NULL: skipped); kFInv: workspace
+    void* field[kNumFields];   // entry-order destinations (NULL: skipped); kFInv, kFWalk: workspace
     int32_t* spay_k;
     int32_t* spay_q;
     int4* krec;
     int32_t* tiles_k;
     int32_t* repeats;
     uint4* rec;
-    uint4* aux;
     int C, W, R, P, key_bits, first_partial, valid_last, tile_len, digit_bits;
     int stage_bytes;
     uint32_t wr_magic;   // ceil(2^32 / (W + R)): r / (W + R) == umulhi(r, wr_magic) for r < 2^17
@@ -66,16 +67,17 @@ struct P1Args {
     Rounds rounds;
 };
 
+__host__ __device__ constexpr int field_bytes(int f) {
+    return (f == kFIsLast || f == kFIsOnly || f == kFQLast || f == kFQOnly || f == kFWalk) ? 1 : f == kFInv ? 2 : 4;
+}
+__host__ __device__ constexpr bool field_is_q(int f) { return f >= kFLogQ && f <= kFQOnly; }
+__host__ __device__ constexpr bool field_is_all(int f) { return f == kFInv || f == kFWalk; }
+
 // r / (W + R) for entry indices r < 2^17 and W + R <= 512 (multiply-high by a rounded-up
 // reciprocal; the error term r / 2^32 stays below 1 / (W + R)).
 __device__ __forceinline__ int token_of_entry(int r, uint32_t magic) {
     return static_cast<int>(__umulhi(static_cast<uint32_t>(r), magic));
 }
-
-__host__ __device__ constexpr int field_bytes(int f) {
-    return (f == kFIsLast || f == kFIsOnly || f == kFQLast || f == kFQOnly) ? 1 : f == kFInv ? 2 : 4;
-}
-__host__ __device__ constexpr bool field_is_q(int f) { return f >= kFLogQ && f <= kFQOnly; }
 
 // Segmented-scan element: a TwoSum-compensated float sum (s + c), the valid K count (bits 0-15),
 // the valid Q count (bits 16-30) and a segment-start flag (bit 31).
@@ -113,6 +115,11 @@ __device__ __forceinline__ Seg seg_shfl(Seg v, int d) {
     return o;
 }
 
+// Barrier for LDS hazards only: LDS operations complete, global stores may stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Exclusive segmented scan of one element per thread over the block, in thread order
 // (REV: descending). Fixed tree: lane doubling, then the wave totals in scan order. `total`
 // receives the block's combined element. wtot: kNW elements of LDS.
@@ -129,14 +136,14 @@ __device__ __forceinline__ Seg block_exclusive_seg(Seg agg, Seg* wtot, Seg& tota
     Seg ex = seg_shfl<REV>(incl, 1);
     if (REV ? (lane == kWave - 1) : (lane == 0)) ex = seg_zero();
     if (REV ? (lane == 0) : (lane == kWave - 1)) wtot[w] = incl;
-    __syncthreads();
+    lds_barrier();
     Seg pre = seg_zero(), tot = seg_zero();
     for (int i = 0; i < kNW; ++i) {
         const int ww = REV ? kNW - 1 - i : i;
         if (ww == w) pre = tot;
         tot = seg_combine(tot, wtot[ww]);
     }
-    __syncthreads();
+    lds_barrier();
     total = tot;
     return seg_combine(pre, ex);
 }
@@ -152,14 +159,14 @@ __device__ __forceinline__ uint32_t block_exclusive_add(uint32_t v, uint32_t* ws
         if (lane >= d) incl += o;
     }
     if (lane == kWave - 1) wsum[w] = incl;
-    __syncthreads();
+    lds_barrier();
     uint32_t pre = 0, tot = 0;
     for (int ww = 0; ww < kNW; ++ww) {
         const uint32_t x = wsum[ww];
         pre += ww < w ? x : 0u;
         tot += x;
     }
-    __syncthreads();
+    lds_barrier();
     total = tot;
     return pre + incl - v;
 }
@@ -185,7 +192,7 @@ __device__ void block_radix_sort(uint32_t (&key)[IPT], uint32_t (&val)[IPT], int
         const int nd = 1 << db;
         const uint32_t dmask = static_cast<uint32_t>(nd - 1);
         for (int d = lane; d < nd; d += kWave) my_hist[d] = 0u;
-        __syncthreads();
+        lds_barrier();
         // The rank inside the wave (< 2^16) rides in the upper half of val (values are < 2^16).
 #pragma unroll
         for (int k = 0; k < IPT; ++k) {
@@ -202,7 +209,7 @@ __device__ void block_radix_sort(uint32_t (&key)[IPT], uint32_t (&val)[IPT], int
             val[k] = (val[k] & 0xFFFFu) | (base + below) << 16;
             if (below == 0) my_hist[d] = base + cnt;   // the slice's lowest lane of this digit
         }
-        __syncthreads();
+        lds_barrier();
         // Exclusive scan over the counts in (digit, wave) order: thread x owns the `per`
         // consecutive elements e = x * per + u, element e being (digit e / kNW, wave e % kNW).
         const int per = (nd * kNW + kNT - 1) / kNT;
@@ -222,7 +229,7 @@ __device__ void block_radix_sort(uint32_t (&key)[IPT], uint32_t (&val)[IPT], int
                 run += cnt;
             }
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int k = 0; k < IPT; ++k) {
             const uint32_t d = (key[k] >> sh) & dmask;
@@ -230,7 +237,7 @@ __device__ void block_radix_sort(uint32_t (&key)[IPT], uint32_t (&val)[IPT], int
             skey[pos] = key[k];
             sval[pos] = static_cast<uint16_t>(val[k] & 0xFFFFu);
         }
-        __syncthreads();
+        lds_barrier();
         if (pass + 1 < passes) {
 #pragma unroll
             for (int k = 0; k < IPT; ++k) {
@@ -238,14 +245,16 @@ __device__ void block_radix_sort(uint32_t (&key)[IPT], uint32_t (&val)[IPT], int
                 key[k] = skey[i];
                 val[k] = sval[i];
             }
-            __syncthreads();
+            lds_barrier();
         }
     }
 }
 
-// Copies `bytes` bytes from LDS to global memory with the whole block: 16-byte accesses when
-// the global destination is 16-byte aligned (the LDS source always is), bytes otherwise.
-__device__ __forceinline__ void block_copy_out(void* dst, const unsigned char* src, int bytes) {
+// Copies `count` elements of `es` bytes from LDS (16-byte aligned) to global memory with the
+// whole block: 16-byte accesses when the destination is 16-byte aligned, element-sized ones
+// otherwise.
+__device__ __forceinline__ void block_copy_out(void* dst, const unsigned char* src, int count, int es) {
+    const int bytes = count * es;
     int done = 0;
     if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
         const int vecs = bytes >> 4;
@@ -254,20 +263,45 @@ __device__ __forceinline__ void block_copy_out(void* dst, const unsigned char* s
         }
         done = vecs << 4;
     }
+    if (es == 4 && (reinterpret_cast<uintptr_t>(dst) & 3u) == 0) {
+        for (int i = (done >> 2) + threadIdx.x; i < count; i += kNT) {
+            reinterpret_cast<uint32_t*>(dst)[i] = reinterpret_cast<const uint32_t*>(src)[i];
+        }
+        return;
+    }
     for (int i = done + threadIdx.x; i < bytes; i += kNT) static_cast<unsigned char*>(dst)[i] = src[i];
 }
 
+// Everything one sorted position yields, recomputed by its owner thread from its tile prefixes.
+struct Entry {
+    bool live;       // position < n
+    bool valid;      // token inside the chunk's valid count
+    bool q;          // read entry
+    bool head;       // first of its group
+    bool walk;       // starts its token's run of its kind and has earlier valid K entries in the group
+    int t, ln, r;
+    uint32_t pay;    // entry bits of the payload
+    float s, c;      // inclusive log-cumsum (compensated)
+    float rex;       // sum after (K: rex)
+    uint32_t bcnt;   // own-kind valid peers before
+    uint32_t acnt;   // own-kind valid peers after
+    uint32_t jkind;  // index in its kind's sorted row
+    float v;
+};
+
 template <int IPT>
 __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
-    extern __shared__ __align__(16) unsigned char smem[];
     constexpr int NP = kNT * IPT;
-    uint32_t* skey = reinterpret_cast<uint32_t*>(smem);
-    uint16_t* sval = reinterpret_cast<uint16_t*>(smem + NP * 4);
-    uint32_t* hist = reinterpret_cast<uint32_t*>(smem + NP * 6);
-    unsigned char* stage = smem;   // aliases the sort arrays once the scans are done
-    float* gates = reinterpret_cast<float*>(smem + a.stage_bytes);
+    constexpr int NTILE = (NP + kTile - 1) / kTile;
+    extern __shared__ __align__(16) unsigned char smem[];
+    unsigned char* stage = smem;                                   // staging, after the scans
+    uint32_t* skey = reinterpret_cast<uint32_t*>(smem);           // sort keys (inside staging)
+    uint32_t* hist = reinterpret_cast<uint32_t*>(smem + NP * 4);  // digit counts (inside staging)
+    uint16_t* sval = reinterpret_cast<uint16_t*>(smem + a.stage_bytes);
+    float* gates = reinterpret_cast<float*>(smem + a.stage_bytes + NP * 2);
     __shared__ Seg wtot[kNW];
     __shared__ uint32_t wsum[kNW];
+    __shared__ uint32_t tile_kind[NTILE + 1];   // kind counts (K | Q << 16) before each tile
 
     const int c = blockIdx.x;
     const int C = a.C, W = a.W, R = a.R;
@@ -283,6 +317,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     const int64_t crow = static_cast<int64_t>(c) * n;
     const int lane = static_cast<int>(lane_id());
     const int w = threadIdx.x / kWave;
+    const int ntiles = (n + kTile - 1) / kTile;
 
     for (int t = threadIdx.x; t < C; t += kNT) gates[t] = t < tv ? a.g[static_cast<int64_t>(c) * C + t] : 0.0f;
 
@@ -293,7 +328,6 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
         for (int k = 0; k < IPT; ++k) {
             const int i = w * kWave * IPT + k * kWave + lane;
             val[k] = static_cast<uint32_t>(i);
-            key[k] = pad_key;
             // Branch-free address: every item loads (padding items re-read entry 0), so all the
             // loads of a thread are in flight together.
             const int ic = i < n ? i : 0;
@@ -308,88 +342,95 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
         block_radix_sort<IPT>(key, val, tv < C ? kb + 1 : kb, a.digit_bits, skey, sval, hist, wsum);
     }
 
-    const int ntiles = (n + kTile - 1) / kTile;
+    // Per-thread state carried from the scans to the output rounds (registers, tile-indexed).
+    Seg rpre[NTILE], fpre[NTILE];
+    uint32_t kpre[NTILE];
+    float vv[NTILE][kTileItems];
     uint32_t repeat_count = 0;
 
     // ---- 2. reverse scan: sums and peer counts after each entry in its group.
-    Seg rcarry = seg_zero();
-    for (int T = ntiles - 1; T >= 0; --T) {
-        const int p0 = T * kTile + threadIdx.x * kTileItems;
-        uint32_t kk[kTileItems], rr[kTileItems];
+    {
+        Seg rcarry = seg_zero();
 #pragma unroll
-        for (int k = 0; k < kTileItems; ++k) {
-            const int p = p0 + k;
-            kk[k] = p < n ? skey[p] : pad_key;
-            rr[k] = p < n ? (sval[p] & kRMask) : 0u;
-        }
-        const bool has_prev = p0 > 0 && p0 <= n;
-        const uint32_t prev_key = has_prev ? skey[p0 - 1] : pad_key;
-        const uint32_t prev_r = has_prev ? (sval[p0 - 1] & kRMask) : 0u;
-        const uint32_t next_key = p0 + kTileItems < n ? skey[p0 + kTileItems] : pad_key;
-        uint32_t heads = 0, ends = 0, reps = 0;
-        float x[kTileItems];
+        for (int Ti = 0; Ti < NTILE; ++Ti) {
+            const int T = NTILE - 1 - Ti;
+            rpre[T] = seg_zero();
+            if (T >= ntiles) continue;   // block-uniform
+            const int p0 = T * kTile + threadIdx.x * kTileItems;
+            uint32_t kk[kTileItems], rr[kTileItems];
 #pragma unroll
-        for (int k = 0; k < kTileItems; ++k) {
-            const uint32_t pk = k ? kk[k - 1] : prev_key;
-            const uint32_t pr = k ? rr[k - 1] : prev_r;
-            const bool valid = kk[k] < key_lim;
-            const bool pvalid = pk < key_lim && (p0 + k) > 0;
-            const bool head = !valid || !pvalid || kk[k] != pk;
-            const int t = token_of_entry(static_cast<int>(rr[k]), a.wr_magic);
-            const int j = static_cast<int>(rr[k]) - t * wr;
-            const bool is_k = valid && j < W;
-            const int pt = token_of_entry(static_cast<int>(pr), a.wr_magic);
-            const int pj = static_cast<int>(pr) - pt * wr;
-            const bool rep = !head && is_k && pj < W && pt == t;
-            heads |= (head ? 1u : 0u) << k;
-            reps |= (rep ? 1u : 0u) << k;
-            x[k] = (is_k && !rep) ? gates[t] : 0.0f;
-        }
+            for (int k = 0; k < kTileItems; ++k) {
+                const int p = p0 + k;
+                kk[k] = p < n ? skey[p] : pad_key;
+                rr[k] = p < n ? (sval[p] & kRMask) : 0u;
+            }
+            const bool has_prev = p0 > 0 && p0 <= n;
+            const uint32_t prev_key = has_prev ? skey[p0 - 1] : pad_key;
+            const uint32_t prev_r = has_prev ? (sval[p0 - 1] & kRMask) : 0u;
+            const uint32_t next_key = p0 + kTileItems < n ? skey[p0 + kTileItems] : pad_key;
+            uint32_t heads = 0, ends = 0, reps = 0;
+            float x[kTileItems];
 #pragma unroll
-        for (int k = 0; k < kTileItems; ++k) {
-            const bool end = k + 1 < kTileItems ? ((heads >> (k + 1)) & 1u)
-                                                : (!(kk[k] < key_lim) || !(next_key < key_lim) || next_key != kk[k]);
-            ends |= (end ? 1u : 0u) << k;
-        }
-        auto item = [&](int k, bool seg_start) {
-            const bool valid = kk[k] < key_lim;
-            const int t = token_of_entry(static_cast<int>(rr[k]), a.wr_magic);
-            const bool q = static_cast<int>(rr[k]) - t * wr >= W;
-            return Seg{x[k], 0.0f, (valid ? (q ? kSegQOne : 1u) : 0u) | (seg_start ? kSegHead : 0u)};
-        };
-        Seg agg = seg_zero();
-#pragma unroll
-        for (int k = kTileItems - 1; k >= 0; --k) agg = seg_combine(agg, item(k, (ends >> k) & 1u));
-        Seg total;
-        Seg run = seg_combine(rcarry, block_exclusive_seg<true>(agg, wtot, total));
-        rcarry = seg_combine(rcarry, total);
-#pragma unroll
-        for (int k = kTileItems - 1; k >= 0; --k) {
-            const int p = p0 + k;
-            const bool end = (ends >> k) & 1u;
-            const Seg after = end ? seg_zero() : run;
-            run = seg_combine(run, item(k, end));
-            if (p < n) {
+            for (int k = 0; k < kTileItems; ++k) {
+                const uint32_t pk = k ? kk[k - 1] : prev_key;
+                const uint32_t pr = k ? rr[k - 1] : prev_r;
                 const bool valid = kk[k] < key_lim;
-                const uint32_t slot = valid ? static_cast<uint32_t>(static_cast<int64_t>(kk[k]) + id_base) : 0u;
-                a.aux[crow + p] = make_uint4(__float_as_uint(after.s + after.c), after.f & ~kSegHead, slot, 0u);
-                sval[p] = static_cast<uint16_t>(rr[k] | (((heads >> k) & 1u) ? kFlagHead : 0u) |
-                                                (((reps >> k) & 1u) ? kFlagRep : 0u));
-                repeat_count += (reps >> k) & 1u;
+                const bool pvalid = pk < key_lim && (p0 + k) > 0;
+                const bool head = !valid || !pvalid || kk[k] != pk;
+                const int t = token_of_entry(static_cast<int>(rr[k]), a.wr_magic);
+                const int j = static_cast<int>(rr[k]) - t * wr;
+                const bool is_k = valid && j < W;
+                const int pt = token_of_entry(static_cast<int>(pr), a.wr_magic);
+                const int pj = static_cast<int>(pr) - pt * wr;
+                const bool rep = !head && is_k && pj < W && pt == t;
+                heads |= (head ? 1u : 0u) << k;
+                reps |= (rep ? 1u : 0u) << k;
+                x[k] = (is_k && !rep) ? gates[t] : 0.0f;
+                // Keep the slot and the value for the outputs (one branch-free load per entry).
+                const bool q = j >= W;
+                const int ln = q ? j - W : j;
+                const float* vsrc = q ? a.q_val + cr + t * R + ln : a.k_val + cw + t * W + ln;
+                const float vl = *(p0 + k < n ? vsrc : a.k_val + cw);
+                vv[T][k] = valid ? vl : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < kTileItems; ++k) {
+                const bool end = k + 1 < kTileItems
+                                     ? ((heads >> (k + 1)) & 1u)
+                                     : (!(kk[k] < key_lim) || !(next_key < key_lim) || next_key != kk[k]);
+                ends |= (end ? 1u : 0u) << k;
+            }
+            Seg agg = seg_zero();
+#pragma unroll
+            for (int k = kTileItems - 1; k >= 0; --k) {
+                const bool valid = kk[k] < key_lim;
+                const int t = token_of_entry(static_cast<int>(rr[k]), a.wr_magic);
+                const bool q = static_cast<int>(rr[k]) - t * wr >= W;
+                agg = seg_combine(agg, Seg{x[k], 0.0f, (valid ? (q ? kSegQOne : 1u) : 0u) |
+                                                           (((ends >> k) & 1u) ? kSegHead : 0u)});
+            }
+            Seg total;
+            rpre[T] = seg_combine(rcarry, block_exclusive_seg<true>(agg, wtot, total));
+            rcarry = seg_combine(rcarry, total);
+#pragma unroll
+            for (int k = 0; k < kTileItems; ++k) {
+                const int p = p0 + k;
+                if (p < n) {
+                    sval[p] = static_cast<uint16_t>(rr[k] | (((heads >> k) & 1u) ? kFlagHead : 0u) |
+                                                    (((reps >> k) & 1u) ? kFlagRep : 0u));
+                    repeat_count += (reps >> k) & 1u;
+                }
             }
         }
     }
+    __syncthreads();   // every flag of the sorted row is set; the keys are no longer needed
 
-    __syncthreads();   // every flag of the sorted row is set before the forward pass reads it
-
-    // ---- 3. forward scan: inclusive log-cumsums, peers before, kind-row indices.
-    Seg fcarry = seg_zero();
-    uint32_t kind_carry = 0;
-    for (int T = 0; T < ntiles; ++T) {
+    // The tile's entries as the scans see them, from the flagged sorted row.
+    auto load_tile = [&](int T, uint32_t (&rr)[kTileItems], float (&x)[kTileItems], uint32_t& heads,
+                         uint32_t& ends) {
         const int p0 = T * kTile + threadIdx.x * kTileItems;
-        uint32_t rr[kTileItems];
-        float x[kTileItems];
-        uint32_t kind_cnt = 0;
+        heads = 0;
+        ends = 0;
 #pragma unroll
         for (int k = 0; k < kTileItems; ++k) {
             const int p = p0 + k;
@@ -399,157 +440,245 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             const bool q = r - t * wr >= W;
             const bool valid = p < n && t < tv;
             x[k] = (valid && !q && !(rr[k] & kFlagRep)) ? gates[t] : 0.0f;
-            if (p < n) kind_cnt += q ? kSegQOne : 1u;
+            heads |= ((rr[k] & kFlagHead) ? 1u : 0u) << k;
         }
-        auto item = [&](int k) {
-            const int p = p0 + k;
-            const int r = static_cast<int>(rr[k] & kRMask);
-            const int t = token_of_entry(r, a.wr_magic);
-            const bool q = r - t * wr >= W;
-            const bool valid = p < n && t < tv;
-            return Seg{x[k], 0.0f, (valid ? (q ? kSegQOne : 1u) : 0u) | ((rr[k] & kFlagHead) ? kSegHead : 0u)};
-        };
-        Seg agg = seg_zero();
-#pragma unroll
-        for (int k = 0; k < kTileItems; ++k) agg = seg_combine(agg, item(k));
-        Seg total;
-        Seg run = seg_combine(fcarry, block_exclusive_seg<false>(agg, wtot, total));
-        fcarry = seg_combine(fcarry, total);
-        uint32_t kind_total;
-        const uint32_t kind_base = kind_carry + block_exclusive_add(kind_cnt, wsum, kind_total);
-        kind_carry += kind_total;
-        uint32_t jk = kind_base & 0xFFFFu, jq = kind_base >> 16;
+        const int pn = p0 + kTileItems;
+        const bool next_head = pn >= n || (sval[pn] & kFlagHead);
 #pragma unroll
         for (int k = 0; k < kTileItems; ++k) {
-            const int p = p0 + k;
-            const bool head = rr[k] & kFlagHead;
-            const Seg before = head ? seg_zero() : run;
-            run = seg_combine(run, item(k));
-            if (p >= n) continue;
-            const int r = static_cast<int>(rr[k] & kRMask);
-            const int t = token_of_entry(r, a.wr_magic);
-            const int j = r - t * wr;
-            const bool q = j >= W;
-            const int ln = q ? j - W : j;
-            const bool valid = t < tv;
-            const uint32_t pay = static_cast<uint32_t>(ln) | (q ? kIsQ : 0u) | (static_cast<uint32_t>(t) << kTokShift) |
-                                 (valid ? 0u : kInvalid);
-            const float v = valid ? (q ? a.q_val[cr + t * R + ln] : a.k_val[cw + t * W + ln]) : 0.0f;
-            const uint32_t bcnt = q ? ((before.f >> 16) & 0x7FFFu) : (before.f & 0xFFFFu);
-            const uint32_t jkind = q ? jq : jk;
-            a.rec[crow + p] = make_uint4(pay | (head ? kHead : 0u), __float_as_uint(run.s), __float_as_uint(run.c),
-                                         __float_as_uint(v));
-            reinterpret_cast<uint32_t*>(a.aux + crow + p)[3] = bcnt | jkind << 16;
-            jq += q ? 1u : 0u;
-            jk += q ? 0u : 1u;
+            const bool end = k + 1 < kTileItems ? ((heads >> (k + 1)) & 1u) : next_head;
+            ends |= (end ? 1u : 0u) << k;
         }
-    }
+    };
+    auto tile_item = [&](int T, int k, const uint32_t (&rr)[kTileItems], const float (&x)[kTileItems],
+                         bool seg_start) {
+        const int p = T * kTile + threadIdx.x * kTileItems + k;
+        const int r = static_cast<int>(rr[k] & kRMask);
+        const int t = token_of_entry(r, a.wr_magic);
+        const bool q = r - t * wr >= W;
+        const bool valid = p < n && t < tv;
+        return Seg{x[k], 0.0f, (valid ? (q ? kSegQOne : 1u) : 0u) | (seg_start ? kSegHead : 0u)};
+    };
+
+    // ---- 3. forward scan: per-tile forward prefixes and kind-row bases.
     {
+        Seg fcarry = seg_zero();
+        uint32_t kind_carry = 0;
+#pragma unroll
+        for (int T = 0; T < NTILE; ++T) {
+            fpre[T] = seg_zero();
+            kpre[T] = 0;
+            if (T >= ntiles) continue;   // block-uniform
+            const int p0 = T * kTile + threadIdx.x * kTileItems;
+            uint32_t rr[kTileItems], heads, ends;
+            float x[kTileItems];
+            load_tile(T, rr, x, heads, ends);
+            uint32_t kind_cnt = 0;
+            Seg agg = seg_zero();
+#pragma unroll
+            for (int k = 0; k < kTileItems; ++k) {
+                agg = seg_combine(agg, tile_item(T, k, rr, x, (heads >> k) & 1u));
+                const int r = static_cast<int>(rr[k] & kRMask);
+                const int t = token_of_entry(r, a.wr_magic);
+                if (p0 + k < n) kind_cnt += (r - t * wr >= W) ? kSegQOne : 1u;
+            }
+            Seg total;
+            fpre[T] = seg_combine(fcarry, block_exclusive_seg<false>(agg, wtot, total));
+            fcarry = seg_combine(fcarry, total);
+            uint32_t kind_total;
+            kpre[T] = kind_carry + block_exclusive_add(kind_cnt, wsum, kind_total);
+            if (threadIdx.x == 0) tile_kind[T] = kind_carry;
+            kind_carry += kind_total;
+        }
+        if (threadIdx.x == 0) tile_kind[ntiles] = kind_carry;
         uint32_t rep_total;
         (void)block_exclusive_add(repeat_count, wsum, rep_total);
         if (threadIdx.x == 0 && a.repeats != nullptr) a.repeats[c] = static_cast<int32_t>(rep_total);
     }
-    __syncthreads();   // the records are complete (and the sort arrays free for staging)
+    __syncthreads();
 
-    // ---- 4. output rounds over the sorted positions (striped: coalesced record reads).
+    // Recomputes the four entries of tile T owned by this thread and calls f(k, entry).
+    auto for_tile = [&](int T, const Seg& rp, const Seg& fp, uint32_t kp, const float (&vl)[kTileItems], auto&& f) {
+        const int p0 = T * kTile + threadIdx.x * kTileItems;
+        uint32_t rr[kTileItems], heads, ends;
+        float x[kTileItems];
+        load_tile(T, rr, x, heads, ends);
+        float rexs[kTileItems];
+        uint32_t afts[kTileItems];
+        Seg run = rp;
+#pragma unroll
+        for (int k = kTileItems - 1; k >= 0; --k) {
+            const bool end = (ends >> k) & 1u;
+            const Seg after = end ? seg_zero() : run;
+            rexs[k] = after.s + after.c;
+            afts[k] = after.f & ~kSegHead;
+            run = seg_combine(run, tile_item(T, k, rr, x, end));
+        }
+        const uint32_t prev_r = p0 > 0 && p0 <= n ? (sval[p0 - 1] & kRMask) : 0xFFFFu;
+        run = fp;
+        uint32_t jk = kp & 0xFFFFu, jq = kp >> 16;
+#pragma unroll
+        for (int k = 0; k < kTileItems; ++k) {
+            const bool head = (heads >> k) & 1u;
+            const Seg before = head ? seg_zero() : run;
+            run = seg_combine(run, tile_item(T, k, rr, x, head));
+            Entry e;
+            e.live = p0 + k < n;
+            e.r = static_cast<int>(rr[k] & kRMask);
+            e.t = token_of_entry(e.r, a.wr_magic);
+            const int j = e.r - e.t * wr;
+            e.q = j >= W;
+            e.ln = e.q ? j - W : j;
+            e.valid = e.live && e.t < tv;
+            e.head = head;
+            e.pay = static_cast<uint32_t>(e.ln) | (e.q ? kIsQ : 0u) | (static_cast<uint32_t>(e.t) << kTokShift) |
+                    (e.valid ? 0u : kInvalid);
+            e.s = run.s;
+            e.c = run.c;
+            e.rex = rexs[k];
+            e.bcnt = e.q ? ((before.f >> 16) & 0x7FFFu) : (before.f & 0xFFFFu);
+            e.acnt = e.q ? ((afts[k] >> 16) & 0x7FFFu) : (afts[k] & 0xFFFFu);
+            e.jkind = e.q ? jq : jk;
+            e.v = vl[k];
+            // Same token and kind as the previous position (inside the group): not a run start.
+            const uint32_t pr = k ? (rr[k - 1] & kRMask) : prev_r;
+            const int pt = token_of_entry(static_cast<int>(pr), a.wr_magic);
+            const bool pq = static_cast<int>(pr) - pt * wr >= W;
+            const bool same_run = !head && pt == e.t && pq == e.q;
+            e.walk = e.valid && !same_run && (before.f & 0xFFFFu) != 0u;
+            if (e.live) {
+                jq += e.q ? 1u : 0u;
+                jk += e.q ? 0u : 1u;
+            }
+            f(k, p0 + k, e);
+        }
+    };
+    // exp of the group total: the compensated log-cumsum plus the sum after (TwoSum).
+    auto group_exp = [](const Entry& e) {
+        const float gs = e.s + e.rex;
+        const float gb = gs - e.s;
+        const float ge = (e.s - (gs - gb)) + (e.rex - gb);
+        return e.valid ? expf(gs + (e.c + ge)) : 1.0f;
+    };
+
+    // ---- 4a. entry-order rounds.
+    for (int rd = 0; rd < a.rounds.count; ++rd) {
+        const uint32_t mask = a.rounds.mask[rd];
+        auto stage_at = [&](int f, int idx) { return stage + a.rounds.offset[f] + idx * field_bytes(f); };
+#pragma unroll
+        for (int T = 0; T < NTILE; ++T) {
+            if (T >= ntiles) continue;
+            for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
+                if (!e.live) return;
+                const float Lv = e.s + e.c;
+                const uint32_t packed =
+                    e.valid ? (static_cast<uint32_t>(p) | min(e.acnt, kPosCountMax) << kPosAfterShift |
+                               min(e.bcnt + 1u + e.acnt, kPosCountMax) << kPosSizeShift)
+                            : static_cast<uint32_t>(p);
+                if (e.q) {
+                    const int o = e.t * R + e.ln;
+                    if (mask & (1u << kFLogQ)) *reinterpret_cast<float*>(stage_at(kFLogQ, o)) = Lv;
+                    if (mask & (1u << kFQW)) *reinterpret_cast<float*>(stage_at(kFQW, o)) = e.v * expf(Lv);
+                    if (mask & (1u << kFPosQ)) *reinterpret_cast<uint32_t*>(stage_at(kFPosQ, o)) = packed;
+                    const bool ql = e.valid && e.acnt == 0;
+                    if (mask & (1u << kFQLast)) *stage_at(kFQLast, o) = ql ? 1 : 0;
+                    if (mask & (1u << kFQOnly)) *stage_at(kFQOnly, o) = (ql && e.bcnt == 0) ? 1 : 0;
+                } else {
+                    const int o = e.t * W + e.ln;
+                    const bool last = e.valid && e.acnt == 0;
+                    if (mask & (1u << kFLogK)) *reinterpret_cast<float*>(stage_at(kFLogK, o)) = Lv;
+                    if (mask & (1u << kFRex)) *reinterpret_cast<float*>(stage_at(kFRex, o)) = e.rex;
+                    if (mask & (1u << kFCpe)) *reinterpret_cast<float*>(stage_at(kFCpe, o)) = group_exp(e);
+                    if (mask & (1u << kFKEff)) *reinterpret_cast<float*>(stage_at(kFKEff, o)) = e.v * expf(Lv);
+                    if (mask & (1u << kFIsLast)) *stage_at(kFIsLast, o) = last ? 1 : 0;
+                    if (mask & (1u << kFIsOnly)) *stage_at(kFIsOnly, o) = (last && e.bcnt == 0) ? 1 : 0;
+                    if (mask & (1u << kFPosK)) *reinterpret_cast<uint32_t*>(stage_at(kFPosK, o)) = packed;
+                }
+                if (mask & (1u << kFInv)) *reinterpret_cast<uint16_t*>(stage_at(kFInv, e.r)) = static_cast<uint16_t>(p);
+                if (mask & (1u << kFWalk)) *stage_at(kFWalk, e.r) = e.walk ? 1 : 0;
+            });
+        }
+        lds_barrier();
+        for (int f = 0; f < kNumFields; ++f) {
+            if (!(mask & (1u << f))) continue;
+            const int cnt = field_is_all(f) ? n : field_is_q(f) ? C * R : C * W;
+            const int64_t base = field_is_all(f) ? crow : field_is_q(f) ? cr : cw;
+            unsigned char* dst = static_cast<unsigned char*>(a.field[f]) + base * field_bytes(f);
+            block_copy_out(dst, stage + a.rounds.offset[f], cnt, field_bytes(f));
+        }
+        lds_barrier();
+    }
+
+    // ---- 4b. sorted-order outputs, staged per tile: pair records, then kind rows and krec.
     const int nk = C * W;
     const int L = a.tile_len;
     const int ntk = (nk + L - 1) / L;
     const int64_t tb = static_cast<int64_t>(c) * (ntk + 1);
     if (threadIdx.x == 0) a.tiles_k[tb + ntk] = nk;
-    for (int rd = 0; rd < a.rounds.count; ++rd) {
-        const uint32_t mask = a.rounds.mask[rd];
-        for (int p = threadIdx.x; p < n; p += kNT) {
-            const uint4 re = a.rec[crow + p];
-            const uint4 ax = a.aux[crow + p];
-            const uint32_t pay = re.x & kEntryMask;
-            const bool q = pay & kIsQ;
-            const bool valid = !(pay & kInvalid);
-            const int t = static_cast<int>((pay >> kTokShift) & 0xFFu);
-            const int ln = static_cast<int>(pay & 0xFFu);
-            const float rs = __uint_as_float(re.y), rc = __uint_as_float(re.z), v = __uint_as_float(re.w);
-            const float Lv = rs + rc;
-            const float rexv = __uint_as_float(ax.x);
-            const uint32_t acnt = q ? ((ax.y >> 16) & 0x7FFFu) : (ax.y & 0xFFFFu);
-            const uint32_t bcnt = ax.w & 0xFFFFu;
-            const uint32_t jkind = ax.w >> 16;
-            auto stage_at = [&](int f, int idx) { return stage + a.rounds.offset[f] + idx * field_bytes(f); };
-            // exp of the group total: the compensated log-cumsum plus the sum after (TwoSum).
-            auto group_exp = [&]() {
-                const float gs = rs + rexv;
-                const float gb = gs - rs;
-                const float ge = (rs - (gs - gb)) + (rexv - gb);
-                return valid ? expf(gs + (rc + ge)) : 1.0f;
-            };
-            const uint32_t packed =
-                valid ? (static_cast<uint32_t>(p) | min(acnt, kPosCountMax) << kPosAfterShift |
-                         min(bcnt + 1u + acnt, kPosCountMax) << kPosSizeShift)
-                      : static_cast<uint32_t>(p);
-            if (q) {
-                const int o = t * R + ln;
-                if (mask & (1u << kFLogQ)) *reinterpret_cast<float*>(stage_at(kFLogQ, o)) = Lv;
-                if (mask & (1u << kFQW)) *reinterpret_cast<float*>(stage_at(kFQW, o)) = v * expf(Lv);
-                if (mask & (1u << kFPosQ)) *reinterpret_cast<uint32_t*>(stage_at(kFPosQ, o)) = packed;
-                const bool ql = valid && acnt == 0;
-                if (mask & (1u << kFQLast)) *stage_at(kFQLast, o) = ql ? 1 : 0;
-                if (mask & (1u << kFQOnly)) *stage_at(kFQOnly, o) = (ql && bcnt == 0) ? 1 : 0;
+#pragma unroll
+    for (int T = 0; T < NTILE; ++T) {
+        if (T >= ntiles) continue;
+        const int pbase = T * kTile;
+        const int pcount = min(kTile, n - pbase);
+        // Pair records {payload | head, log-cumsum s, c, value}.
+        for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
+            if (!e.live) return;
+            reinterpret_cast<uint4*>(stage)[p - pbase] =
+                make_uint4(e.pay | (e.head ? kHead : 0u), __float_as_uint(e.s), __float_as_uint(e.c), __float_as_uint(e.v));
+        });
+        lds_barrier();
+        block_copy_out(a.rec + crow + pbase, stage, pcount, 16);
+        lds_barrier();
+        // Kind rows and mover records: the tile's K (Q) entries have consecutive kind indices.
+        const uint32_t k0 = tile_kind[T] & 0xFFFFu, q0 = tile_kind[T] >> 16;
+        const int nk_t = static_cast<int>((tile_kind[T + 1] & 0xFFFFu) - k0);
+        const int nq_t = static_cast<int>((tile_kind[T + 1] >> 16) - q0);
+        unsigned char* st_krec = stage;
+        unsigned char* st_spk = stage + nk_t * 16;
+        unsigned char* st_spq = st_spk + (nk_t * 4 + 15) / 16 * 16;
+        for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
+            if (!e.live) return;
+            const uint32_t elem = e.valid ? (e.pay | min(e.bcnt, kDistMax) << kDistShift | (e.bcnt == 0 ? kFirst : 0u) |
+                                             (e.acnt == 0 ? kLast : 0u))
+                                          : (e.pay | kFirst | kLast);
+            if (e.q) {
+                reinterpret_cast<uint32_t*>(st_spq)[e.jkind - q0] = elem;
             } else {
-                const int o = t * W + ln;
-                const bool last = valid && acnt == 0;
-                if (mask & (1u << kFLogK)) *reinterpret_cast<float*>(stage_at(kFLogK, o)) = Lv;
-                if (mask & (1u << kFRex)) *reinterpret_cast<float*>(stage_at(kFRex, o)) = rexv;
-                if (mask & (1u << kFCpe)) *reinterpret_cast<float*>(stage_at(kFCpe, o)) = group_exp();
-                if (mask & (1u << kFKEff)) *reinterpret_cast<float*>(stage_at(kFKEff, o)) = v * expf(Lv);
-                if (mask & (1u << kFIsLast)) *stage_at(kFIsLast, o) = last ? 1 : 0;
-                if (mask & (1u << kFIsOnly)) *stage_at(kFIsOnly, o) = (last && bcnt == 0) ? 1 : 0;
-                if (mask & (1u << kFPosK)) *reinterpret_cast<uint32_t*>(stage_at(kFPosK, o)) = packed;
-            }
-            if (mask & (1u << kFInv)) {
-                *reinterpret_cast<uint16_t*>(stage_at(kFInv, t * wr + (q ? W + ln : ln))) = static_cast<uint16_t>(p);
-            }
-            if (rd == 0) {
-                // Sorted kind rows, mover records and tile bounds (consecutive positions of a kind
-                // have consecutive indices, so these stores are nearly contiguous).
-                const uint32_t elem = valid ? (pay | min(bcnt, kDistMax) << kDistShift | (bcnt == 0 ? kFirst : 0u) |
-                                               (acnt == 0 ? kLast : 0u))
-                                            : (pay | kFirst | kLast);
-                if (q) {
-                    if (a.spay_q) a.spay_q[cr + jkind] = static_cast<int32_t>(elem);
-                } else {
-                    a.spay_k[cw + jkind] = static_cast<int32_t>(elem);
-                    const float sc = valid ? v * expf(rexv) : 0.0f;
-                    a.krec[cw + jkind] = make_int4(static_cast<int32_t>(elem), static_cast<int32_t>(ax.z),
-                                                   __float_as_int(sc), __float_as_int(group_exp()));
-                    if (static_cast<int>(jkind) % L == 0) {
-                        a.tiles_k[tb + static_cast<int>(jkind) / L] =
-                            (elem & kFirst) ? static_cast<int>(jkind) : min(static_cast<int>(jkind + acnt + 1u), nk);
-                    }
+                reinterpret_cast<uint32_t*>(st_spk)[e.jkind - k0] = elem;
+                const float sc = e.valid ? e.v * expf(e.rex) : 0.0f;
+                // The slot: the entry's id read again (the chunk's ids are cache-resident by now).
+                const int64_t id = static_cast<int64_t>(a.k_idx[cw + (e.valid ? e.t * W + e.ln : 0)]);
+                const uint32_t slot =
+                    e.valid ? static_cast<uint32_t>((static_cast<uint32_t>(id - id_base) & (key_lim - 1u)) + id_base) : 0u;
+                reinterpret_cast<int4*>(st_krec)[e.jkind - k0] =
+                    make_int4(static_cast<int32_t>(elem), static_cast<int32_t>(slot), __float_as_int(sc),
+                              __float_as_int(group_exp(e)));
+                if (static_cast<int>(e.jkind) % L == 0) {
+                    a.tiles_k[tb + static_cast<int>(e.jkind) / L] =
+                        (elem & kFirst) ? static_cast<int>(e.jkind) : min(static_cast<int>(e.jkind + e.acnt + 1u), nk);
                 }
             }
-        }
-        __syncthreads();
-        for (int f = 0; f < kNumFields; ++f) {
-            if (!(mask & (1u << f))) continue;
-            const int cnt = f == kFInv ? n : field_is_q(f) ? C * R : C * W;
-            const int64_t base = f == kFInv ? crow : field_is_q(f) ? cr : cw;
-            unsigned char* dst = static_cast<unsigned char*>(a.field[f]) + base * field_bytes(f);
-            block_copy_out(dst, stage + a.rounds.offset[f], cnt * field_bytes(f));
-        }
-        __syncthreads();
+        });
+        lds_barrier();
+        block_copy_out(a.krec + cw + k0, st_krec, nk_t, 16);
+        block_copy_out(a.spay_k + cw + k0, st_spk, nk_t, 4);
+        if (a.spay_q != nullptr) block_copy_out(a.spay_q + cr + q0, st_spq, nq_t, 4);
+        lds_barrier();
     }
 }
 
 // Pair sums. Block (chunk, triangle): one thread per row i. Token i's entries of the block's kind
 // (K for A, Q for QK) that share a slot sit next to each other in the sorted row and share one
-// log-cumsum, and so do the K entries of any earlier token j in that group. For every group the
-// row meets, the thread sums token i's values (w_i) once, then walks the group from just before
-// token i's entries back to its head, summing each earlier token's K values (k_j) over its run,
-// and adds w_i * k_j * exp(L_i - L_j) to cell (i, j) (j != i for A). Every cell has one writer
-// thread and a term order fixed by the input; the triangle lives in LDS and is written out as a
-// dense [C, C] matrix with zeros outside it.
+// log-cumsum, and so do the K entries of any earlier token j in that group. For every group in
+// which token i's run has earlier K entries (flagged by the sort/scan kernel), the thread sums
+// the run's values (w_i) once, then walks the group from just before the run back to its head,
+// summing each earlier token's K values (k_j) over its run, and adds w_i * k_j * exp(L_i - L_j)
+// to cell (i, j) (j != i for A). Every cell has one writer thread and a term order fixed by the
+// input; the triangle lives in LDS and is written out as a dense [C, C] matrix, zeros outside it.
 struct PairArgs {
     const uint4* rec;
     const uint16_t* inv;
+    const uint8_t* walk;
     float* a;
     float* qk;
     int C, W, R, first_partial, valid_last;
@@ -574,20 +703,21 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
     __syncthreads();
     const int64_t crow = static_cast<int64_t>(c) * n;
     const uint4* rec = a.rec + crow;
-    const uint16_t* inv = a.inv + crow;
     const int i = threadIdx.x;
     if (i < tv) {
         float* row = tri + i * (i + 1) / 2;
         const int lanes = q ? R : W;
+        const int r0 = i * wr + (q ? W : 0);
+        const uint8_t* wf = a.walk + crow + r0;
+        const uint16_t* iv = a.inv + crow + r0;
         // Token i's entries of this kind: (Q flag, token) bits of the payload.
         const uint32_t own_tag = (q ? kIsQ : 0u) | (static_cast<uint32_t>(i) << kTokShift);
         const uint32_t tag_mask = kIsQ | (0xFFu << kTokShift);
         for (int ln = 0; ln < lanes; ++ln) {
-            const int rho = inv[i * wr + (q ? W + ln : ln)];
+            if (!wf[ln]) continue;
+            const int rho = iv[ln];
             const uint4 own = rec[rho];
-            if (own.x & kHead) continue;   // first of its group: nothing earlier
-            if ((rec[rho - 1].x & tag_mask) == own_tag) continue;   // not the first of token i's run
-            // rho starts token i's run of this kind in its group: sum the run's values.
+            // Sum the run's values.
             float wi = __uint_as_float(own.w);
             for (int p = rho + 1; p < n; ++p) {
                 const uint4 nx = rec[p];
@@ -660,31 +790,36 @@ struct MainPlan {
     Rounds rounds;
 };
 
-constexpr int kLdsBudget = 160 * 1024 - 2048;   // dynamic LDS per block (static scratch aside)
+constexpr int kLdsTotal = 160 * 1024;
+constexpr int kStaticReserve = 1024;   // static LDS of the kernel (scan totals, tile counts)
 
 int field_count(const sdm_p1_shape* s, int f) {
     const int n = s->C * (s->W + s->R);
-    return f == kFInv ? n : field_is_q(f) ? s->C * s->R : s->C * s->W;
+    return field_is_all(f) ? n : field_is_q(f) ? s->C * s->R : s->C * s->W;
 }
 
-MainPlan plan_main(const sdm_p1_shape* s, const sdm_p1_io* io, void* inv) {
+MainPlan plan_main(const sdm_p1_shape* s, const sdm_p1_io* io, bool with_pairs_ws) {
     MainPlan m;
     const int n = s->C * (s->W + s->R);
     m.ipt = n <= kNT ? 1 : n <= 2 * kNT ? 2 : n <= 4 * kNT ? 4 : n <= 8 * kNT ? 8 : 16;
     const int np = kNT * m.ipt;
-    const int gate_bytes = 256 * static_cast<int>(sizeof(float));
-    // Widest digit (<= 10 bits) whose per-wave counts fit beside the sort arrays.
+    const int fixed = np * 2 + 256 * static_cast<int>(sizeof(float));   // sorted row + gates
+    const int cap_max = (kLdsTotal - kStaticReserve - fixed) / 16 * 16;
+    // Widest digit (<= 10 bits) whose per-wave counts fit beside the keys.
     int d = 10;
-    while (d > 4 && np * 6 + kNW * (1 << d) * 4 + gate_bytes > kLdsBudget) --d;
+    while (d > 4 && np * 4 + kNW * (1 << d) * 4 > cap_max) --d;
     m.digit_bits = d;
-    const int sort_bytes = np * 6 + kNW * (1 << d) * 4;
+    const int sort_bytes = np * 4 + kNW * (1 << d) * 4;
+    // The per-tile sorted stages: 16-byte records of one tile; krec + both kind rows of one tile.
+    const int tile = n < kTile ? n : kTile;
+    const int sorted_bytes = tile * 20 + 32;
     const void* dst[kNumFields] = {io->log_k, io->rex, io->cpe, io->k_eff, io->is_last, io->is_only, io->pos_k,
-                                   io->log_q, io->q_w, io->pos_q, io->q_last, io->q_only, inv};
-    // Staging capacity: the sort's bytes, raised to hold four of the largest field when LDS allows.
-    int big = 0;
-    for (int f = 0; f < kNumFields; ++f) big = max(big, (field_count(s, f) * field_bytes(f) + 15) / 16 * 16);
-    int cap = max(sort_bytes, min(4 * big, kLdsBudget - gate_bytes));
-    cap = max(cap, big) / 16 * 16;
+                                   io->log_q, io->q_w, io->pos_q, io->q_last, io->q_only,
+                                   with_pairs_ws ? io : nullptr, with_pairs_ws ? io : nullptr};
+    int need = 0;
+    for (int f = 0; f < kNumFields; ++f) need += (field_count(s, f) * field_bytes(f) + 15) / 16 * 16;
+    int cap = max(max(sort_bytes, sorted_bytes), min(need, cap_max));
+    cap = min(cap, cap_max) / 16 * 16;
     // Greedy packing of the requested fields, in order, into rounds of `cap` bytes.
     m.rounds.count = 0;
     for (int r = 0; r < kMaxRounds; ++r) m.rounds.mask[r] = 0u;
@@ -705,9 +840,8 @@ MainPlan plan_main(const sdm_p1_shape* s, const sdm_p1_io* io, void* inv) {
         m.rounds.mask[m.rounds.count - 1] |= 1u << f;
         used += bytes;
     }
-    if (m.rounds.count == 0) m.rounds.count = 1;   // round 0 also writes the kind rows
-    m.stage_bytes = (max(cap, sort_bytes) + 15) / 16 * 16;
-    m.lds_bytes = static_cast<size_t>(m.stage_bytes) + gate_bytes;
+    m.stage_bytes = cap;
+    m.lds_bytes = static_cast<size_t>(cap) + static_cast<size_t>(fixed);
     return m;
 }
 
@@ -728,20 +862,21 @@ P1Workspace p1_workspace_layout(const sdm_p1_shape* s) {
     auto up = [](size_t b) { return (b + 255) / 256 * 256; };
     P1Workspace w;
     w.rec_off = 0;
-    w.aux_off = up(N * n * sizeof(uint4));
-    w.inv_off = w.aux_off + up(N * n * sizeof(uint4));
-    w.total = w.inv_off + up(N * n * sizeof(uint16_t));
+    w.inv_off = up(N * n * sizeof(uint4));
+    w.walk_off = w.inv_off + up(N * n * sizeof(uint16_t));
+    w.total = w.walk_off + up(N * n);
     return w;
 }
 
 size_t p1_lds_bytes(const sdm_p1_shape* s, const sdm_p1_io* io) {
-    return plan_main(s, io, reinterpret_cast<void*>(uintptr_t(1))).lds_bytes;
+    return plan_main(s, io, io->a != nullptr || io->qk != nullptr).lds_bytes;
 }
 
 hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     const sdm_p1_shape* s = Lc.s;
     const sdm_p1_io* io = Lc.io;
     if (s->N == 0) return hipSuccess;
+    const bool pairs = io->a != nullptr || io->qk != nullptr;
     P1Args a;
     a.k_idx = io->k_idx;
     a.q_idx = io->q_idx;
@@ -749,7 +884,8 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     a.q_val = io->q_val;
     a.g = io->g;
     void* fields[kNumFields] = {io->log_k, io->rex, io->cpe, io->k_eff, io->is_last, io->is_only, io->pos_k,
-                                io->log_q, io->q_w, io->pos_q, io->q_last, io->q_only, Lc.inv};
+                                io->log_q, io->q_w, io->pos_q, io->q_last, io->q_only,
+                                pairs ? Lc.inv : nullptr, pairs ? Lc.walk : nullptr};
     for (int f = 0; f < kNumFields; ++f) a.field[f] = fields[f];
     a.spay_k = io->spay_k;
     a.spay_q = io->spay_q;
@@ -757,7 +893,6 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     a.tiles_k = io->tiles_k;
     a.repeats = io->repeats;
     a.rec = static_cast<uint4*>(Lc.rec);
-    a.aux = static_cast<uint4*>(Lc.aux);
     a.C = s->C;
     a.W = s->W;
     a.R = s->R;
@@ -769,7 +904,7 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     a.stream_offset = s->stream_offset;
     a.wr_magic = static_cast<uint32_t>(((uint64_t(1) << 32) + static_cast<uint64_t>(s->W + s->R) - 1) /
                                        static_cast<uint64_t>(s->W + s->R));
-    const MainPlan m = plan_main(s, io, Lc.inv);
+    const MainPlan m = plan_main(s, io, pairs);
     if (m.rounds.count > kMaxRounds) return hipErrorInvalidValue;
     a.digit_bits = m.digit_bits;
     a.stage_bytes = m.stage_bytes;
@@ -785,12 +920,11 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     }
     if (e != hipSuccess) return e;
     if (io->events != nullptr && (e = hipEventRecord(io->events[1], st)) != hipSuccess) return e;
-    if (io->a == nullptr && io->qk == nullptr) {
-        return io->events != nullptr ? hipEventRecord(io->events[2], st) : hipSuccess;
-    }
+    if (!pairs) return io->events != nullptr ? hipEventRecord(io->events[2], st) : hipSuccess;
     PairArgs pa;
     pa.rec = a.rec;
     pa.inv = static_cast<const uint16_t*>(Lc.inv);
+    pa.walk = static_cast<const uint8_t*>(Lc.walk);
     pa.a = io->a;
     pa.qk = io->qk;
     pa.C = s->C;

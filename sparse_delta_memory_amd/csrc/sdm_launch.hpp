@@ -17,13 +17,13 @@ struct P1Launch {
     const sdm_p1_shape* s;
     const sdm_p1_io* io;
     void* rec;        // [N, n] 16-byte records in sorted order: payload | head, log-cumsum (s, c), value
-    void* aux;        // [N, n] 16-byte records: sum after, peers after, slot, peers before | kind index
     void* inv;        // [N, n] uint16 sorted position of every entry (entry order)
+    void* walk;       // [N, n] uint8 1 where an entry starts its token's run with earlier K entries
 };
 
 // Workspace layout of sdm_phase1: byte offsets of the three regions and the total.
 struct P1Workspace {
-    size_t rec_off, aux_off, inv_off, total;
+    size_t rec_off, inv_off, walk_off, total;
 };
 P1Workspace p1_workspace_layout(const sdm_p1_shape* s);
 
