@@ -156,6 +156,7 @@ def main():
         dv = dv.to(torch.bfloat16)
     out = sdm.alloc_phase1_outputs(shape, device=dev)
     ws = torch.empty(sdm.phase1_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    dw_ws = sdm.alloc_dw_workspace(shape, sh.hd, device=dev)
     bank = W.make_bank(wl, dev)
     bank0 = bank.clone() if not args.no_cpu_baseline else None
     stream = torch.cuda.current_stream(dev)
@@ -181,7 +182,7 @@ def main():
         if dw_events is not None:
             dw_events[0].record(stream)
         for ti in range(wl.steps):
-            sdm.dw_step(bank, dv, out["krec"], shape, ti, dv_step_rows=P * C)
+            sdm.dw_step(bank, dv, out["krec"], shape, ti, dv_step_rows=P * C, workspace=dw_ws)
         if dw_events is not None:
             dw_events[1].record(stream)
 

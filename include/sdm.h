@@ -153,7 +153,17 @@ typedef struct sdm_dw_io {
     int64_t dv_rows;        /* rows in dv; ti * dv_step_rows + P * C <= dv_rows */
     const int32_t* krec;    /* [N, C*W, 4] records from sdm_phase1 */
     int32_t P, C, W, N;     /* the Phase-1 shape of krec */
+    void* workspace;        /* optional (NULL: every group is walked by one team of lanes): device
+                               memory of sdm_dw_workspace() bytes, 16-byte aligned, ZERO-FILLED before
+                               its first use; every call leaves it zero-filled where it must be. With it,
+                               groups longer than 32 members are split into 32-member segments summed
+                               in parallel and combined in segment order. Calls sharing one workspace
+                               must not run concurrently. */
+    size_t workspace_bytes;
 } sdm_dw_io;
+
+/* Workspace bytes sdm_dw_step can use for this shape (P * C * W * (4 * hd + 12), rounded). */
+size_t sdm_dw_workspace(const sdm_dw_io* io);
 
 /*
  * DW decay-and-write (page "sparse_delta_memory/cuda/mover_da2_cuda.py", module docstring; bit
@@ -161,6 +171,8 @@ typedef struct sdm_dw_io {
  * group of the K-only rows of chunks ti*P + p (p < P), in sorted order,
  *   acc = fma(sc_m, dv[token_m], acc) over the members from +0,
  *   bank[slot] = fma(bank[slot], cpe_last, acc)  (bf16 bank: rounded to nearest even).
+ * With a workspace, a group longer than 32 members is summed as 32-member segment partials (each
+ * an fma chain from +0) added in segment order, then the same final fma.
  * Rows of slots without a valid group are not touched. Within one call every slot has at most
  * one writer (stream slot ranges must not overlap). bank must not alias dv or krec.
  * Requires (ti + 1) * P <= N and ti * dv_step_rows + P * C <= dv_rows. A record whose slot is

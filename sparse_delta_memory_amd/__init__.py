@@ -16,8 +16,8 @@ import ctypes
 from . import _lib
 from ._lib import P1IO, P1Shape, SdmError  # noqa: F401
 
-__all__ = ["P1Shape", "phase1", "phase1_workspace_bytes", "alloc_phase1_outputs", "dw_step", "SdmError",
-           "make_shape"]
+__all__ = ["P1Shape", "phase1", "phase1_workspace_bytes", "alloc_phase1_outputs", "dw_step", "dw_workspace_bytes",
+           "alloc_dw_workspace", "SdmError", "make_shape"]
 
 
 def make_shape(N, C, W, R, P=1, key_bits=16, stream_offset=0, first_partial=None, valid_last=None, tile_len=128):
@@ -80,11 +80,26 @@ def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=No
     return out
 
 
-def dw_step(bank, dv, krec, shape: P1Shape, ti: int, dv_step_rows: int, stream=None):
+def dw_workspace_bytes(shape: P1Shape, hd: int) -> int:
+    """Bytes of the (zero-filled) DW workspace that lets long groups be split across lanes."""
+    io = _lib.DwIO()
+    io.P, io.C, io.W, io.N, io.hd = shape.P, shape.C, shape.W, shape.N, int(hd)
+    return int(_lib.load().sdm_dw_workspace(ctypes.byref(io)))
+
+
+def alloc_dw_workspace(shape: P1Shape, hd: int, device="cuda"):
+    """A zero-filled DW workspace (reusable by every step of the same shape)."""
+    import torch
+
+    return torch.zeros(max(dw_workspace_bytes(shape, hd), 1), dtype=torch.uint8, device=device)
+
+
+def dw_step(bank, dv, krec, shape: P1Shape, ti: int, dv_step_rows: int, stream=None, workspace=None):
     """Enqueue the DW step `ti` (chunks ti*P .. ti*P+P-1) on the current (or given) stream.
 
     bank [rows, hd] float32 or bfloat16 (updated in place); dv [*, hd] float32 or bfloat16 token rows,
-    row ti*dv_step_rows + p*C + t; krec from phase1."""
+    row ti*dv_step_rows + p*C + t; krec from phase1; workspace from alloc_dw_workspace (optional:
+    without it every group is walked by one team of lanes)."""
     import torch
 
     lib = _lib.load()
@@ -99,6 +114,9 @@ def dw_step(bank, dv, krec, shape: P1Shape, ti: int, dv_step_rows: int, stream=N
     io.dv_rows = dv.shape[0]
     io.krec = krec.data_ptr()
     io.P, io.C, io.W, io.N = shape.P, shape.C, shape.W, shape.N
+    if workspace is not None:
+        io.workspace = workspace.data_ptr()
+        io.workspace_bytes = workspace.numel() * workspace.element_size()
     if bank.dtype not in (torch.float32, torch.bfloat16) or dv.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("dw_step: bank and dv must be float32 or bfloat16")
     st = torch.cuda.current_stream(bank.device) if stream is None else stream

@@ -47,10 +47,12 @@ class DwIO(ctypes.Structure):
         ("hd", ctypes.c_int32), ("dv", ctypes.c_void_p), ("dv_dtype", ctypes.c_int32),
         ("dv_step_rows", ctypes.c_int64), ("dv_rows", ctypes.c_int64), ("krec", ctypes.c_void_p),
         ("P", ctypes.c_int32), ("C", ctypes.c_int32), ("W", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
-EXPORTS = ["sdm_phase1_workspace", "sdm_phase1", "sdm_dw_step", "sdm_status_string", "sdm_last_error"]
+EXPORTS = ["sdm_phase1_workspace", "sdm_phase1", "sdm_dw_workspace", "sdm_dw_step", "sdm_status_string",
+           "sdm_last_error"]
 
 _lock = threading.Lock()
 _lib = None
@@ -75,6 +77,8 @@ def load() -> ctypes.CDLL:
         lib.sdm_phase1_workspace.restype = ctypes.c_size_t
         lib.sdm_phase1.argtypes = [ctypes.POINTER(P1Shape), ctypes.POINTER(P1IO), ctypes.c_void_p]
         lib.sdm_phase1.restype = ctypes.c_int
+        lib.sdm_dw_workspace.argtypes = [ctypes.POINTER(DwIO)]
+        lib.sdm_dw_workspace.restype = ctypes.c_size_t
         lib.sdm_dw_step.argtypes = [ctypes.POINTER(DwIO), ctypes.c_int64, ctypes.c_void_p]
         lib.sdm_dw_step.restype = ctypes.c_int
         lib.sdm_status_string.argtypes = [ctypes.c_int]

@@ -73,6 +73,11 @@ const char* sdm_status_string(sdm_status s) {
 
 const char* sdm_last_error(void) { return g_last_error.c_str(); }
 
+size_t sdm_dw_workspace(const sdm_dw_io* io) {
+    if (io == nullptr || io->P < 1 || io->C < 1 || io->W < 1 || io->hd < 1) return 0;
+    return sdm::dw_workspace_layout(io).total;
+}
+
 size_t sdm_phase1_workspace(const sdm_p1_shape* s) {
     if (check_p1_shape(s) != SDM_OK) return 0;
     return sdm::p1_workspace_layout(s).total;
@@ -154,6 +159,12 @@ sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st) {
     const int dv_es = io->dv_dtype == SDM_BF16 ? 2 : 4;
     if ((io->hd * bank_es) % 16 != 0 || (io->hd * dv_es) % 16 != 0)
         return fail(SDM_EALIGN, "sdm_dw_step: rows of hd = %d are not 16-byte multiples", io->hd);
+    if (io->workspace != nullptr) {
+        if (!aligned(io->workspace, 16)) return fail(SDM_EALIGN, "sdm_dw_step: workspace is not 16-byte aligned");
+        const size_t need = sdm::dw_workspace_layout(io).total;
+        if (io->workspace_bytes < need)
+            return fail(SDM_EWORKSPACE, "sdm_dw_step: workspace needs %zu bytes, got %zu", need, io->workspace_bytes);
+    }
     sdm::DwLaunch L;
     L.io = io;
     L.ti = ti;

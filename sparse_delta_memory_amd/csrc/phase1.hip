@@ -620,24 +620,35 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
         if (T >= ntiles) continue;
         const int pbase = T * kTile;
         const int pcount = min(kTile, n - pbase);
-        // Pair records {payload | head, log-cumsum s, c, value}.
-        for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
-            if (!e.live) return;
-            reinterpret_cast<uint4*>(stage)[p - pbase] =
-                make_uint4(e.pay | (e.head ? kHead : 0u), __float_as_uint(e.s), __float_as_uint(e.c), __float_as_uint(e.v));
-        });
-        lds_barrier();
-        block_copy_out(a.rec + crow + pbase, stage, pcount, 16);
-        lds_barrier();
         // Kind rows and mover records: the tile's K (Q) entries have consecutive kind indices.
         const uint32_t k0 = tile_kind[T] & 0xFFFFu, q0 = tile_kind[T] >> 16;
         const int nk_t = static_cast<int>((tile_kind[T + 1] & 0xFFFFu) - k0);
         const int nq_t = static_cast<int>((tile_kind[T + 1] >> 16) - q0);
-        unsigned char* st_krec = stage;
-        unsigned char* st_spk = stage + nk_t * 16;
+        const int rec_bytes = a.rec != nullptr ? pcount * 16 : 0;
+        const int kind_bytes = nk_t * 16 + (nk_t * 4 + 15) / 16 * 16 + nq_t * 4;
+        // One pass when the pair records, krec and both kind rows of the tile fit together.
+        const bool joint = rec_bytes + kind_bytes <= a.stage_bytes;   // block-uniform
+        if (rec_bytes > 0 && !joint) {
+            for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
+                if (!e.live) return;
+                reinterpret_cast<uint4*>(stage)[p - pbase] = make_uint4(
+                    e.pay | (e.head ? kHead : 0u), __float_as_uint(e.s), __float_as_uint(e.c), __float_as_uint(e.v));
+            });
+            lds_barrier();
+            block_copy_out(a.rec + crow + pbase, stage, pcount, 16);
+            lds_barrier();
+        }
+        unsigned char* st_rec = stage;
+        unsigned char* st_krec = stage + (joint ? rec_bytes : 0);
+        unsigned char* st_spk = st_krec + nk_t * 16;
         unsigned char* st_spq = st_spk + (nk_t * 4 + 15) / 16 * 16;
         for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
             if (!e.live) return;
+            if (joint && rec_bytes > 0) {
+                // Pair records {payload | head, log-cumsum s, c, value}.
+                reinterpret_cast<uint4*>(st_rec)[p - pbase] = make_uint4(
+                    e.pay | (e.head ? kHead : 0u), __float_as_uint(e.s), __float_as_uint(e.c), __float_as_uint(e.v));
+            }
             const uint32_t elem = e.valid ? (e.pay | min(e.bcnt, kDistMax) << kDistShift | (e.bcnt == 0 ? kFirst : 0u) |
                                              (e.acnt == 0 ? kLast : 0u))
                                           : (e.pay | kFirst | kLast);
@@ -660,6 +671,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             }
         });
         lds_barrier();
+        if (joint && rec_bytes > 0) block_copy_out(a.rec + crow + pbase, st_rec, pcount, 16);
         block_copy_out(a.krec + cw + k0, st_krec, nk_t, 16);
         block_copy_out(a.spay_k + cw + k0, st_spk, nk_t, 4);
         if (a.spay_q != nullptr) block_copy_out(a.spay_q + cr + q0, st_spq, nq_t, 4);
@@ -684,7 +696,7 @@ struct PairArgs {
     int C, W, R, first_partial, valid_last;
 };
 
-constexpr int kPairThreads = 256;
+constexpr int kPairThreads = 512;   // rows walk on the first C threads; all write the output
 constexpr int kWalkBatch = 8;
 
 __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
@@ -713,8 +725,16 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
         // Token i's entries of this kind: (Q flag, token) bits of the payload.
         const uint32_t own_tag = (q ? kIsQ : 0u) | (static_cast<uint32_t>(i) << kTokShift);
         const uint32_t tag_mask = kIsQ | (0xFFu << kTokShift);
-        for (int ln = 0; ln < lanes; ++ln) {
-            if (!wf[ln]) continue;
+        for (int lb = 0; lb < lanes; lb += 32) {
+          // The flags of up to 32 lanes, loaded together, then only the flagged lanes.
+          uint32_t flags = 0;
+#pragma unroll
+          for (int u = 0; u < 32; ++u) {
+              const int ln = lb + u;
+              flags |= (ln < lanes && wf[min(ln, lanes - 1)] != 0) ? (1u << u) : 0u;
+          }
+          for (; flags != 0u; flags &= flags - 1u) {
+            const int ln = lb + __builtin_ctz(flags);
             const int rho = iv[ln];
             const uint4 own = rec[rho];
             // Sum the run's values.
@@ -754,6 +774,7 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
                 }
             }
             if (cur_j >= 0 && (q || cur_j != i)) row[cur_j] = row[cur_j] + (wi * kj) * expf((se - sj) + (ce - cj));
+          }
         }
     }
     __syncthreads();
@@ -892,7 +913,7 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     a.krec = reinterpret_cast<int4*>(io->krec);
     a.tiles_k = io->tiles_k;
     a.repeats = io->repeats;
-    a.rec = static_cast<uint4*>(Lc.rec);
+    a.rec = pairs ? static_cast<uint4*>(Lc.rec) : nullptr;
     a.C = s->C;
     a.W = s->W;
     a.R = s->R;
@@ -922,7 +943,7 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     if (io->events != nullptr && (e = hipEventRecord(io->events[1], st)) != hipSuccess) return e;
     if (!pairs) return io->events != nullptr ? hipEventRecord(io->events[2], st) : hipSuccess;
     PairArgs pa;
-    pa.rec = a.rec;
+    pa.rec = static_cast<const uint4*>(Lc.rec);
     pa.inv = static_cast<const uint16_t*>(Lc.inv);
     pa.walk = static_cast<const uint8_t*>(Lc.walk);
     pa.a = io->a;

@@ -40,4 +40,10 @@ struct DwLaunch {
 
 hipError_t dw_launch(const DwLaunch& L, hipStream_t st);
 
+// Workspace of sdm_dw_step: arrival counters (zero between calls), group metadata, partial rows.
+struct DwWorkspace {
+    size_t cnt_off, meta_off, part_off, total;
+};
+DwWorkspace dw_workspace_layout(const sdm_dw_io* io);
+
 }  // namespace sdm

@@ -155,7 +155,8 @@ def chunk_members(wl, c):
     return u, cnt
 
 
-def run_dw_check(wl: W.Workload, out, shape, check_steps, dev="cuda", sample_untouched=20000, seed=0):
+def run_dw_check(wl: W.Workload, out, shape, check_steps, dev="cuda", sample_untouched=20000, seed=0,
+                 split=True):
     """Run every DW step on the GPU; at the steps in check_steps, first copy the oracle's state of
     the touched rows into the GPU bank, then compare the GPU result with the oracle's. Returns the
     number of elements compared."""
@@ -167,6 +168,7 @@ def run_dw_check(wl: W.Workload, out, shape, check_steps, dev="cuda", sample_unt
     shadow = bank.clone()          # the oracle's bank state (generator rows, then oracle rows)
     dv = device_dv(wl, dev)
     dv_host = wl.dv.reshape(-1, hd).astype(np.float64)
+    ws = sdm.alloc_dw_workspace(shape, hd, device=dev) if split else None
     touched = set()
     compared = 0
     for ti in range(wl.steps):
@@ -181,7 +183,7 @@ def run_dw_check(wl: W.Workload, out, shape, check_steps, dev="cuda", sample_unt
         base_all = shadow.index_select(0, all_slots)
         if check:
             bank.index_copy_(0, all_slots, base_all)
-        sdm.dw_step(bank, dv, out["krec"], shape, ti, dv_step_rows=P * C)
+        sdm.dw_step(bank, dv, out["krec"], shape, ti, dv_step_rows=P * C, workspace=ws)
         base_host = base_all.float().cpu().numpy().astype(np.float64)
         if check:
             torch.cuda.synchronize()
@@ -217,4 +219,8 @@ def run_dw_check(wl: W.Workload, out, shape, check_steps, dev="cuda", sample_unt
         idx = torch.as_tensor(cand, device=dev)
         init = W.make_bank_rows(wl, cand, dev)
         assert torch.equal(bank.index_select(0, idx), init), "untouched rows changed"
+    if ws is not None:   # the split path leaves its counters at zero
+        torch.cuda.synchronize()
+        cnt_bytes = shape.P * shape.C * shape.W * 4
+        assert int(ws[:cnt_bytes].view(torch.int32).abs().sum()) == 0, "DW arrival counters not reset"
     return compared, bank

@@ -105,6 +105,8 @@ def dw(**kw):
     (dict(bank=FAKE + 8), 0, _lib.SDM_EALIGN), (dict(dv=FAKE + 4), 0, _lib.SDM_EALIGN),
     (dict(krec=FAKE + 8), 0, _lib.SDM_EALIGN), (dict(rows=0), 0, _lib.SDM_EINVAL),
     (dict(dv_rows=255), 3, _lib.SDM_EINVAL), (dict(dv_step_rows=-1), 0, _lib.SDM_EINVAL),
+    (dict(workspace=FAKE, workspace_bytes=16), 0, _lib.SDM_EWORKSPACE),
+    (dict(workspace=FAKE + 4, workspace_bytes=1 << 40), 0, _lib.SDM_EALIGN),
 ])
 def test_dw_refusals(kw, ti, status):
     lib = _lib.load()
@@ -116,3 +118,11 @@ def test_status_strings():
     lib = _lib.load()
     for s in range(-6, 1):
         assert len(lib.sdm_status_string(s)) > 0
+
+
+def test_dw_workspace_size():
+    lib = _lib.load()
+    o = dw(P=2, C=64, W=4, hd=128)
+    need = lib.sdm_dw_workspace(ctypes.byref(o))
+    assert need >= 2 * 64 * 4 * (4 * 128 + 12)
+    assert lib.sdm_dw_workspace(ctypes.byref(dw(P=0))) == 0

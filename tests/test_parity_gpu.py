@@ -79,6 +79,16 @@ def test_dw_full_size(idx, check):
     assert n > 0
 
 
+@pytest.mark.parametrize("idx,steps", [(2, 2), (0, None)])
+def test_dw_unsplit(idx, steps):
+    """Without a workspace every group is one FMA chain: also within tolerance."""
+    wl = W.make(idx, steps=steps)
+    say("dw without workspace: workload", idx)
+    shape, out = H.run_phase1(wl)
+    n, _ = H.run_dw_check(wl, out, shape, set(range(wl.steps)), split=False)
+    assert n > 0
+
+
 def test_bitwise_reproducible():
     wl = W.make(2, steps=1)
     say("reproducibility: workload 2")
@@ -97,6 +107,20 @@ def test_bitwise_reproducible():
         torch.cuda.synchronize()
         banks.append(bank)
     assert torch.equal(banks[0].view(torch.uint16), banks[1].view(torch.uint16))
+    # Split long groups (Zipf hot slots): whichever segment team arrives last, the same bits.
+    wl = W.make(2, steps=2)
+    shape, out = H.run_phase1(wl)
+    dv = H.device_dv(wl)
+    banks = []
+    for _ in range(3):
+        bank = W.make_bank(wl, "cuda")
+        ws = sdm.alloc_dw_workspace(shape, wl.shape.hd)
+        for ti in range(wl.steps):
+            sdm.dw_step(bank, dv, out["krec"], shape, ti, dv_step_rows=wl.P * wl.shape.C, workspace=ws)
+        torch.cuda.synchronize()
+        banks.append(bank)
+    assert torch.equal(banks[0].view(torch.uint16), banks[1].view(torch.uint16))
+    assert torch.equal(banks[0].view(torch.uint16), banks[2].view(torch.uint16))
 
 
 def test_masked_tokens_do_not_leak():
