@@ -3,10 +3,12 @@
 
 One step = the whole hot path over one batch: Phase 1 of every chunk of the workload (sort, scans,
 records, tile bounds, A / QK) followed by every DW step of the workload, all enqueued on one stream
-with the inputs already in HBM. `value` is the step's throughput in Phase-1 K+Q entries per
-second; the DW bank GB/s and per-kernel HBM-roofline fractions ride along.
+with the inputs already in HBM, launched eagerly (--graph: replayed from a HIP graph). `value` is the step's throughput in Phase-1 K+Q entries per second. Kernel
+durations for the roofline come from a second, eager pass of the same steps with HIP events
+bound to each kernel's own start and end.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I] [--no-cpu-baseline] [--graph]
+    python bench.py --copy-calibration MIB   # a plain device copy, for scaling HBM byte counters
 
 The default workload is the uniform bf16 shape (index 1); the others are parity cases that can
 also be timed with --workload. Prints ONE JSON line.
@@ -26,7 +28,11 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_BYTES = 8.0e12
 METRIC = "Phase-1 K+Q entries/sec and DW bank GB/s (fraction of HBM roofline), 1 GPU"
-KERNEL_SOURCES = ["phase1.hip", "dw.hip", "sdm_device.hpp"]
+KERNEL_SOURCES = {   # the files each kernel's code comes from (traffic counters are keyed on them)
+    "p1_main_kernel": ["phase1.hip", "sdm_device.hpp"],
+    "p1_pairs_kernel": ["phase1.hip", "sdm_device.hpp"],
+    "dw_kernel": ["dw.hip", "sdm_device.hpp"],
+}
 
 
 def log(*a):
@@ -53,9 +59,9 @@ def dw_bytes(groups, C, W, hd, bank_es, dv_es):
     return bank + C * hd * dv_es + 16 * C * W, bank
 
 
-def source_digest():
+def source_digest(kernel):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "sparse_delta_memory_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -63,7 +69,8 @@ def source_digest():
 
 def read_traffic(workload_name, kernel):
     """HBM bytes per launch of `kernel` from profiles/traffic_<workload>.txt (rocprofv3 FETCH_SIZE and
-    WRITE_SIZE, scaled by a copy-kernel calibration), or None when missing or taken on other sources."""
+    WRITE_SIZE, each scaled by what the counter reads for a plain copy of known size), or None when
+    missing or taken on other kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload_name)
     if not os.path.exists(path):
         return None
@@ -72,7 +79,7 @@ def read_traffic(workload_name, kernel):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("src_sha") != source_digest():
+    if vals.get("src_sha." + kernel) != source_digest(kernel):
         return None
     key = "bytes_per_launch." + kernel
     return float(vals[key]) if key in vals else None
@@ -131,6 +138,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay the step from a HIP graph in the timed region")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-MiB device buffer 3 times (a known-traffic kernel for HBM counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only (the hot path has no multi-GPU part); "
@@ -144,6 +154,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration > 0:
+        src = torch.ones(args.copy_calibration << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied %d MiB 3 times" % args.copy_calibration)
+        return
     wl = W.make(args.workload)
     sh = wl.shape
     log("workload %d %s: N=%d chunks, n=%d entries/chunk" % (args.workload, sh.name, wl.N, sh.C * (sh.W + sh.R)))
@@ -161,46 +180,48 @@ def main():
     bank0 = bank.clone() if not args.no_cpu_baseline else None
     stream = torch.cuda.current_stream(dev)
     P, C = sh.P, sh.C
+    plan = sdm.DwPlan(bank, dv, out["krec"], shape, dv_step_rows=P * C, workspace=dw_ws)
+    n_ev = 4 + 2 * wl.steps   # start / end of the sort-scan kernel, the pair kernel, every DW launch
 
-    def new_events(k):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
-        for e in evs:
-            e.record(stream)
-        return evs
-
-    torch.cuda.synchronize()
-
-    def step(p1_events=None, dw_events=None):
-        handles = None
-        if p1_events is not None:
-            import ctypes
-
-            arr = (ctypes.c_void_p * 3)(*[e.cuda_event for e in p1_events])
-            handles = ctypes.cast(arr, ctypes.c_void_p).value
-            step._keep = arr
-        sdm.phase1(shape, out=out, workspace=ws, events=handles, **ins)
-        if dw_events is not None:
-            dw_events[0].record(stream)
+    def step(ev=None):
+        sdm.phase1(shape, out=out, workspace=ws, events=None if ev is None else ev[0:4], **ins)
         for ti in range(wl.steps):
-            sdm.dw_step(bank, dv, out["krec"], shape, ti, dv_step_rows=P * C, workspace=dw_ws)
-        if dw_events is not None:
-            dw_events[1].record(stream)
+            plan.step(ti, events=None if ev is None else ev[4 + 2 * ti:6 + 2 * ti])
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    p1_ev = [new_events(3) for _ in range(args.steps)]
-    dw_ev = [new_events(2) for _ in range(args.steps)]
+    graph = None
+    if args.graph:
+        # The whole step (2 Phase-1 kernels and every DW launch) captured once and replayed: the
+        # launches then cost no host time. Captured launches take no timing events.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+    # Timed region: exactly `steps` steps.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(p1_ev[k], dw_ev[k])
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_main = float(np.mean([e[0].elapsed_time(e[1]) for e in p1_ev]))
-    ms_pairs = float(np.mean([e[1].elapsed_time(e[2]) for e in p1_ev]))
-    ms_dw_all = float(np.mean([e[0].elapsed_time(e[1]) for e in dw_ev]))
-    ms_dw = ms_dw_all / wl.steps
+    # Kernel durations: the same steps again, launched eagerly with events bound to each kernel's
+    # own start and end (binding them costs host time per launch, so they stay out of the timed
+    # region above).
+    evs = [sdm.timing_events(n_ev, stream) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    ms_main = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_pairs = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    ms_dw = float(np.mean([e[4 + 2 * ti].elapsed_time(e[5 + 2 * ti]) for e in evs for ti in range(wl.steps)]))
 
     # Valid groups per step (for the DW's algorithmic bytes), from the records' FIRST flags.
     first = (out["krec"][..., 0] & (W_FIRST | W_INVALID)) == W_FIRST
@@ -244,7 +265,7 @@ def main():
             "workload": "%s: P=%d T=%d C=%d W=%d R=%d S=%d hd=%d bank %s dv %s slots %s" % (
                 sh.name, sh.P, sh.T, sh.C, sh.W, sh.R, sh.S, sh.hd, sh.bank_dtype, sh.dv_dtype, sh.slots),
             "chunks": wl.N, "dw_steps": wl.steps, "global_batch": wl.N * sh.C, "seq_len": sh.T,
-            "parallelism": "single GPU",
+            "parallelism": "single GPU", "launch": "hipGraph replay" if args.graph else "eager",
         },
         "phase1_entries_per_s": entries / ((ms_main + ms_pairs) * 1e-3),
         "phase1_hbm_frac": (main_bytes + pairs_bytes) / ((ms_main + ms_pairs) * 1e-3) / HBM_PEAK_BYTES,

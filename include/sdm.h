@@ -110,8 +110,10 @@ typedef struct sdm_p1_io {
                                same token (their gate is not applied again) */
     void* workspace;        /* device scratch, 16-byte aligned, >= sdm_phase1_workspace(shape) */
     size_t workspace_bytes;
-    hipEvent_t* events;     /* optional (NULL: none): 3 caller-created events, recorded on st before the
-                               sort/scan kernel, between it and the pair kernel, and after the pair kernel */
+    hipEvent_t* events;     /* optional (NULL: none): 4 caller-created events bound to the kernels'
+                               own start and end (hipExtLaunchKernel): [0], [1] the sort/scan kernel,
+                               [2], [3] the pair kernel (an event of a kernel that is not launched,
+                               such as the pair kernel when a and qk are both NULL, is not recorded) */
 } sdm_p1_io;
 
 /*
@@ -160,6 +162,8 @@ typedef struct sdm_dw_io {
                                in parallel and combined in segment order. Calls sharing one workspace
                                must not run concurrently. */
     size_t workspace_bytes;
+    hipEvent_t* events;     /* optional (NULL: none): 2 caller-created events bound to the start and end
+                               of this call's kernel (hipExtLaunchKernel) */
 } sdm_dw_io;
 
 /* Workspace bytes sdm_dw_step can use for this shape (P * C * W * (4 * hd + 12), rounded). */

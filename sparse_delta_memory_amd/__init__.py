@@ -17,7 +17,8 @@ from . import _lib
 from ._lib import P1IO, P1Shape, SdmError  # noqa: F401
 
 __all__ = ["P1Shape", "phase1", "phase1_workspace_bytes", "alloc_phase1_outputs", "dw_step", "dw_workspace_bytes",
-           "alloc_dw_workspace", "SdmError", "make_shape"]
+           "alloc_dw_workspace", "DwPlan", "SdmError", "make_shape",
+           "timing_events"]
 
 
 def make_shape(N, C, W, R, P=1, key_bits=16, stream_offset=0, first_partial=None, valid_last=None, tile_len=128):
@@ -74,7 +75,8 @@ def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=No
         setattr(io, name, _ptr(out.get(name)))
     io.workspace = workspace.data_ptr()
     io.workspace_bytes = workspace.numel() * workspace.element_size()
-    io.events = events  # None, or the address of 3 hipEvent_t handles
+    arr = _event_array(events, 4, "phase1")
+    io.events = None if arr is None else ctypes.cast(arr, ctypes.c_void_p).value
     st = torch.cuda.current_stream(k_idx.device) if stream is None else stream
     _lib.check(lib.sdm_phase1(ctypes.byref(shape), ctypes.byref(io), ctypes.c_void_p(st.cuda_stream)))
     return out
@@ -94,30 +96,76 @@ def alloc_dw_workspace(shape: P1Shape, hd: int, device="cuda"):
     return torch.zeros(max(dw_workspace_bytes(shape, hd), 1), dtype=torch.uint8, device=device)
 
 
-def dw_step(bank, dv, krec, shape: P1Shape, ti: int, dv_step_rows: int, stream=None, workspace=None):
-    """Enqueue the DW step `ti` (chunks ti*P .. ti*P+P-1) on the current (or given) stream.
+def timing_events(count, stream=None):
+    """`count` timing torch.cuda.Events, each recorded once on `stream` so that its HIP event exists
+    (torch creates it at the first record); a kernel launch then records them again."""
+    import torch
+
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(count)]
+    for e in evs:
+        e.record(stream)
+    return evs
+
+
+def _event_array(events, count, name):
+    """A ctypes array of `count` hipEvent_t handles from torch.cuda.Event objects (read at enqueue time)."""
+    if events is None:
+        return None
+    events = list(events)
+    if len(events) != count:
+        raise ValueError("%s: expected %d events, got %d" % (name, count, len(events)))
+    handles = [e.cuda_event for e in events]
+    if not all(handles):
+        raise ValueError("%s: an event has no HIP event yet; record it once first (see timing_events)" % name)
+    return (ctypes.c_void_p * count)(*handles)
+
+
+class DwPlan:
+    """The DW step planned once for a bank, token rows, records and shape, launched per step.
 
     bank [rows, hd] float32 or bfloat16 (updated in place); dv [*, hd] float32 or bfloat16 token rows,
     row ti*dv_step_rows + p*C + t; krec from phase1; workspace from alloc_dw_workspace (optional:
-    without it every group is walked by one team of lanes)."""
-    import torch
+    without it every group is walked by one team of lanes). The plan keeps the tensors alive."""
 
-    lib = _lib.load()
-    io = _lib.DwIO()
-    io.bank = bank.data_ptr()
-    io.bank_dtype = _lib.SDM_BF16 if bank.dtype == torch.bfloat16 else _lib.SDM_F32
-    io.rows = bank.shape[0]
-    io.hd = bank.shape[1]
-    io.dv = dv.data_ptr()
-    io.dv_dtype = _lib.SDM_BF16 if dv.dtype == torch.bfloat16 else _lib.SDM_F32
-    io.dv_step_rows = int(dv_step_rows)
-    io.dv_rows = dv.shape[0]
-    io.krec = krec.data_ptr()
-    io.P, io.C, io.W, io.N = shape.P, shape.C, shape.W, shape.N
-    if workspace is not None:
-        io.workspace = workspace.data_ptr()
-        io.workspace_bytes = workspace.numel() * workspace.element_size()
-    if bank.dtype not in (torch.float32, torch.bfloat16) or dv.dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError("dw_step: bank and dv must be float32 or bfloat16")
-    st = torch.cuda.current_stream(bank.device) if stream is None else stream
-    _lib.check(lib.sdm_dw_step(ctypes.byref(io), int(ti), ctypes.c_void_p(st.cuda_stream)))
+    def __init__(self, bank, dv, krec, shape: P1Shape, dv_step_rows: int, workspace=None):
+        import torch
+
+        if bank.dtype not in (torch.float32, torch.bfloat16) or dv.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("DwPlan: bank and dv must be float32 or bfloat16")
+        self._lib = _lib.load()
+        self._keep = (bank, dv, krec, workspace)
+        io = _lib.DwIO()
+        io.bank = bank.data_ptr()
+        io.bank_dtype = _lib.SDM_BF16 if bank.dtype == torch.bfloat16 else _lib.SDM_F32
+        io.rows = bank.shape[0]
+        io.hd = bank.shape[1]
+        io.dv = dv.data_ptr()
+        io.dv_dtype = _lib.SDM_BF16 if dv.dtype == torch.bfloat16 else _lib.SDM_F32
+        io.dv_step_rows = int(dv_step_rows)
+        io.dv_rows = dv.shape[0]
+        io.krec = krec.data_ptr()
+        io.P, io.C, io.W, io.N = shape.P, shape.C, shape.W, shape.N
+        if workspace is not None:
+            io.workspace = workspace.data_ptr()
+            io.workspace_bytes = workspace.numel() * workspace.element_size()
+        self.io = io
+        self._io_ref = ctypes.byref(io)
+        self._device = bank.device
+
+    def step(self, ti: int, stream=None, events=None):
+        """Enqueue step `ti` (chunks ti*P .. ti*P+P-1) on the current (or given) stream. events:
+        optional (start, end) torch.cuda.Event pair bound to the kernel's own start and end."""
+        import torch
+
+        st = torch.cuda.current_stream(self._device) if stream is None else stream
+        arr = _event_array(events, 2, "DwPlan.step")
+        self.io.events = None if arr is None else ctypes.cast(arr, ctypes.c_void_p).value
+        try:
+            _lib.check(self._lib.sdm_dw_step(self._io_ref, int(ti), ctypes.c_void_p(st.cuda_stream)))
+        finally:
+            self.io.events = None
+
+
+def dw_step(bank, dv, krec, shape: P1Shape, ti: int, dv_step_rows: int, stream=None, workspace=None, events=None):
+    """One DW step `ti` through a plan built for this call (see DwPlan)."""
+    DwPlan(bank, dv, krec, shape, dv_step_rows, workspace).step(ti, stream=stream, events=events)

@@ -48,6 +48,7 @@ class DwIO(ctypes.Structure):
         ("dv_step_rows", ctypes.c_int64), ("dv_rows", ctypes.c_int64), ("krec", ctypes.c_void_p),
         ("P", ctypes.c_int32), ("C", ctypes.c_int32), ("W", ctypes.c_int32), ("N", ctypes.c_int32),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("events", ctypes.c_void_p),
     ]
 
 

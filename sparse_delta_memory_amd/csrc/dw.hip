@@ -10,6 +10,8 @@
 // step, so no other team writes it), walks the members' records and token rows in sorted order
 // and writes the new row. Each lane owns CPL consecutive columns and moves them with 16-byte
 // vector accesses; row offsets are 64-bit. Teams on positions that are not a valid FIRST exit.
+#include <hip/hip_ext.h>
+
 #include "sdm_device.hpp"
 #include "sdm_launch.hpp"
 
@@ -215,17 +217,18 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
 }
 
 template <int CPL, bool BB, bool DB>
-hipError_t launch_dw(const DwArgs& a, hipStream_t st) {
+hipError_t launch_dw(DwArgs a, hipStream_t st, const hipEvent_t* ev) {
     const int64_t teams = static_cast<int64_t>(a.P) * a.CW;
     const int64_t blocks = (teams + a.teams_per_block - 1) / a.teams_per_block;
-    hipLaunchKernelGGL((dw_kernel<CPL, BB, DB>), dim3(static_cast<unsigned>(blocks)), dim3(kDwThreads), 0, st, a);
-    return hipGetLastError();
+    void* kargs[] = {&a};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB>), dim3(static_cast<unsigned>(blocks)),
+                              dim3(kDwThreads), kargs, 0, st, ev[0], ev[1], 0);
 }
 
 template <int CPL>
-hipError_t launch_dw_types(const DwArgs& a, bool bank_bf16, bool dv_bf16, hipStream_t st) {
-    if (bank_bf16) return dv_bf16 ? launch_dw<CPL, true, true>(a, st) : launch_dw<CPL, true, false>(a, st);
-    return dv_bf16 ? launch_dw<CPL, false, true>(a, st) : launch_dw<CPL, false, false>(a, st);
+hipError_t launch_dw_types(const DwArgs& a, bool bank_bf16, bool dv_bf16, hipStream_t st, const hipEvent_t* ev) {
+    if (bank_bf16) return dv_bf16 ? launch_dw<CPL, true, true>(a, st, ev) : launch_dw<CPL, true, false>(a, st, ev);
+    return dv_bf16 ? launch_dw<CPL, false, true>(a, st, ev) : launch_dw<CPL, false, false>(a, st, ev);
 }
 
 }  // namespace
@@ -277,8 +280,10 @@ hipError_t dw_launch(const DwLaunch& Lc, hipStream_t st) {
     a.teams_per_block = kDwThreads / ts;
     if (static_cast<int64_t>(a.P) * a.CW == 0) return hipSuccess;
     const bool bb = io->bank_dtype == SDM_BF16, db = io->dv_dtype == SDM_BF16;
-    if (cpl == 8) return launch_dw_types<8>(a, bb, db, st);
-    return launch_dw_types<16>(a, bb, db, st);
+    const hipEvent_t ev[2] = {io->events != nullptr ? io->events[0] : nullptr,
+                              io->events != nullptr ? io->events[1] : nullptr};
+    if (cpl == 8) return launch_dw_types<8>(a, bb, db, st, ev);
+    return launch_dw_types<16>(a, bb, db, st, ev);
 }
 
 }  // namespace sdm

@@ -18,6 +18,8 @@
 // of p1_keys_zw_kernel; the scan semantics of p1_scan_kernel; the pair terms of p1_pairs_kernel).
 // Scans combine TwoSum-compensated float sums in a fixed tree; every output element has one
 // writer; no floating-point atomics are used, so results are bitwise reproducible.
+#include <hip/hip_ext.h>
+
 #include "sdm_device.hpp"
 #include "sdm_launch.hpp"
 
@@ -867,12 +869,12 @@ MainPlan plan_main(const sdm_p1_shape* s, const sdm_p1_io* io, bool with_pairs_w
 }
 
 template <int IPT>
-hipError_t launch_main(const P1Args& args, size_t lds, int N, hipStream_t st) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&p1_main_kernel<IPT>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+hipError_t launch_main(P1Args args, size_t lds, int N, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+    const void* fn = reinterpret_cast<const void*>(&p1_main_kernel<IPT>);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(p1_main_kernel<IPT>, dim3(N), dim3(kNT), lds, st, args);
-    return hipGetLastError();
+    void* kargs[] = {&args};
+    return hipExtLaunchKernel(fn, dim3(N), dim3(kNT), kargs, lds, st, start, stop, 0);
 }
 
 }  // namespace
@@ -930,18 +932,19 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     a.digit_bits = m.digit_bits;
     a.stage_bytes = m.stage_bytes;
     a.rounds = m.rounds;
-    hipError_t e;
-    if (io->events != nullptr && (e = hipEventRecord(io->events[0], st)) != hipSuccess) return e;
-    switch (m.ipt) {
-        case 1: e = launch_main<1>(a, m.lds_bytes, s->N, st); break;
-        case 2: e = launch_main<2>(a, m.lds_bytes, s->N, st); break;
-        case 4: e = launch_main<4>(a, m.lds_bytes, s->N, st); break;
-        case 8: e = launch_main<8>(a, m.lds_bytes, s->N, st); break;
-        default: e = launch_main<16>(a, m.lds_bytes, s->N, st); break;
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+    if (io->events != nullptr) {
+        for (int k = 0; k < 4; ++k) ev[k] = io->events[k];
     }
-    if (e != hipSuccess) return e;
-    if (io->events != nullptr && (e = hipEventRecord(io->events[1], st)) != hipSuccess) return e;
-    if (!pairs) return io->events != nullptr ? hipEventRecord(io->events[2], st) : hipSuccess;
+    hipError_t e;
+    switch (m.ipt) {
+        case 1: e = launch_main<1>(a, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        case 2: e = launch_main<2>(a, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        case 4: e = launch_main<4>(a, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        case 8: e = launch_main<8>(a, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        default: e = launch_main<16>(a, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+    }
+    if (e != hipSuccess || !pairs) return e;
     PairArgs pa;
     pa.rec = static_cast<const uint4*>(Lc.rec);
     pa.inv = static_cast<const uint16_t*>(Lc.inv);
@@ -957,10 +960,9 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&p1_pairs_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(lds));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(p1_pairs_kernel, dim3(s->N, 2), dim3(kPairThreads), lds, st, pa);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return io->events != nullptr ? hipEventRecord(io->events[2], st) : hipSuccess;
+    void* kargs[] = {&pa};
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(&p1_pairs_kernel), dim3(s->N, 2), dim3(kPairThreads), kargs,
+                              lds, st, ev[2], ev[3], 0);
 }
 
 }  // namespace sdm

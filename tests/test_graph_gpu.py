@@ -1,0 +1,104 @@
+"""Phase 1 and the DW steps captured in a HIP graph (torch.cuda.CUDAGraph) and replayed.
+
+Every replay must reproduce the eager launches bit for bit: the path enqueues no memset node
+(the DW arrival counters return to zero by themselves), and replays are separated by eager work
+and synchronisations. The expected values are the eager results of the same library, whose
+parity with the oracle the other GPU tests establish.
+"""
+
+import os
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import sparse_delta_memory_amd as sdm  # noqa: E402
+from sparse_delta_memory_amd import workloads as W  # noqa: E402
+
+sys.path.insert(0, os.path.dirname(__file__))
+import hip_harness as H  # noqa: E402
+
+
+@pytest.mark.parametrize("idx,steps", [(1, 4), (2, 2)])
+def test_graph_replays_match_eager(idx, steps):
+    wl = W.make(idx, steps=steps)
+    sh = wl.shape
+    print("graph replay: workload", idx, sh.name, "N =", wl.N, flush=True)
+    shape = H.shape_of(wl)
+    ins = H.device_inputs(wl)
+    dv = H.device_dv(wl)
+    bank0 = W.make_bank(wl, "cuda")
+
+    def make_state():
+        out = sdm.alloc_phase1_outputs(shape, device="cuda")
+        ws = torch.empty(sdm.phase1_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+        dw_ws = sdm.alloc_dw_workspace(shape, sh.hd, device="cuda")
+        bank = bank0.clone()
+        plan = sdm.DwPlan(bank, dv, out["krec"], shape, dv_step_rows=wl.P * sh.C, workspace=dw_ws)
+
+        def step():
+            sdm.phase1(shape, out=out, workspace=ws, **ins)
+            for ti in range(wl.steps):
+                plan.step(ti)
+
+        return out, bank, step
+
+    out_e, bank_e, step_e = make_state()
+    step_e()
+    torch.cuda.synchronize()
+
+    out_g, bank_g, step_g = make_state()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step_g()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        bank_g.copy_(bank0)
+        for t in out_g.values():
+            t.view(torch.uint8).fill_(0xA5)
+        # Eager work of the same library between replays.
+        step_e()
+        bank_e.copy_(bank0)
+        step_e()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in out_e:
+            assert torch.equal(out_g[k].view(torch.uint8), out_e[k].view(torch.uint8)), (rep, k)
+        assert torch.equal(bank_g.view(torch.uint8), bank_e.view(torch.uint8)), rep
+
+
+def test_kernel_bound_events():
+    """Events handed to the launches are recorded at the kernels' start and end; results unchanged."""
+    wl = W.make(1, steps=2)
+    sh = wl.shape
+    shape = H.shape_of(wl)
+    ins = H.device_inputs(wl)
+    dv = H.device_dv(wl)
+    ref_out = sdm.phase1(shape, **ins)
+    ref_bank = W.make_bank(wl, "cuda")
+    for ti in range(wl.steps):
+        sdm.dw_step(ref_bank, dv, ref_out["krec"], shape, ti, dv_step_rows=wl.P * sh.C)
+    ev = sdm.timing_events(4)
+    out = sdm.phase1(shape, events=ev, **ins)
+    bank = W.make_bank(wl, "cuda")
+    plan = sdm.DwPlan(bank, dv, out["krec"], shape, dv_step_rows=wl.P * sh.C)
+    dw_ev = [sdm.timing_events(2) for _ in range(wl.steps)]
+    for ti in range(wl.steps):
+        plan.step(ti, events=dw_ev[ti])
+    torch.cuda.synchronize()
+    for a, b in ((ev[0], ev[1]), (ev[2], ev[3])) + tuple((e[0], e[1]) for e in dw_ev):
+        ms = a.elapsed_time(b)
+        assert 0.0 < ms < 1000.0, ms
+    # The sort/scan kernel ends before the pair kernel starts (same stream).
+    assert ev[1].elapsed_time(ev[2]) >= 0.0
+    for k in ref_out:
+        assert torch.equal(out[k].view(torch.uint8), ref_out[k].view(torch.uint8)), k
+    assert torch.equal(bank.view(torch.uint8), ref_bank.view(torch.uint8))
+    with pytest.raises(ValueError):
+        sdm.phase1(shape, events=[torch.cuda.Event(enable_timing=True) for _ in range(4)], **ins)
