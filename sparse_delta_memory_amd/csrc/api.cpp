@@ -135,6 +135,9 @@ sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st) {
     if (io->C < 1 || io->C > 256 || io->W < 1 || io->W > 256)
         return fail(SDM_ESHAPE, "sdm_dw_step: C = %d, W = %d outside 1..256", io->C, io->W);
     if (io->P < 1 || io->N < 0) return fail(SDM_ESHAPE, "sdm_dw_step: P = %d, N = %d", io->P, io->N);
+    if (static_cast<int64_t>(io->P) * io->C * io->W > (int64_t(1) << 30))
+        return fail(SDM_ESHAPE, "sdm_dw_step: P*C*W = %lld > 2^30 positions per step",
+                    static_cast<long long>(static_cast<int64_t>(io->P) * io->C * io->W));
     if (ti < 0 || (ti + 1) * static_cast<int64_t>(io->P) > io->N)
         return fail(SDM_ESHAPE, "sdm_dw_step: step %lld needs (ti+1)*P <= N = %d", static_cast<long long>(ti), io->N);
     if (io->bank_dtype != SDM_F32 && io->bank_dtype != SDM_BF16)

@@ -5,11 +5,12 @@
 // chunk's K-only row, acc = fma(sc_m, dv[token_m], acc) over the members in sorted order from +0,
 // then bank[slot] = fma(base, cpe_last, acc), rounded to nearest-even bf16 for a bf16 bank.
 //
-// Mapping: a team of lanes per K-row position. The team whose position holds a valid FIRST owns
-// that group: it reads the group's base row straight from the bank (every slot has one group per
-// step, so no other team writes it), walks the members' records and token rows in sorted order
-// and writes the new row. Each lane owns CPL consecutive columns and moves them with 16-byte
-// vector accesses; row offsets are 64-bit. Teams on positions that are not a valid FIRST exit.
+// Mapping: a team of lanes per U consecutive K-row positions. The team whose position holds a
+// valid FIRST owns that group: it reads the group's base row straight from the bank (every slot
+// has one group per step, so no other team writes it), walks the members' records and token rows
+// in sorted order and writes the new row. Each lane owns CPL consecutive columns and moves them
+// with 16-byte vector accesses; row offsets are 64-bit. One-member groups take a short path with
+// every load issued before the first use; positions that start no work exit.
 #include <hip/hip_ext.h>
 
 #include "sdm_device.hpp"
@@ -33,51 +34,81 @@ struct DwArgs {
     int P, C, CW, hd, ts_log2, teams_per_block;
 };
 
+// CPL consecutive columns of a row as raw 16-byte vectors: loads are issued apart from their
+// unpacking, so that several rows can be in flight before the first is used.
 template <int CPL, bool BF16>
-__device__ __forceinline__ void load_cols(const void* row, int col0, float (&x)[CPL]) {
-    if constexpr (BF16) {
-        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + col0);
+struct RawCols {
+    static constexpr int kVec = CPL * (BF16 ? 2 : 4) / 16;
+    uint4 v[kVec];
+};
+
+template <int CPL, bool BF16>
+__device__ __forceinline__ RawCols<CPL, BF16> load_raw(const void* row, int col0) {
+    RawCols<CPL, BF16> r;
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(row) + col0 * (BF16 ? 2 : 4));
 #pragma unroll
-        for (int v = 0; v < CPL / 8; ++v) {
-            const uint4 u = p[v];
-            const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+    for (int v = 0; v < RawCols<CPL, BF16>::kVec; ++v) r.v[v] = p[v];
+    return r;
+}
+
+template <int CPL, bool BF16>
+__device__ __forceinline__ void unpack_cols(const RawCols<CPL, BF16>& r, float (&x)[CPL]) {
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {
+    for (int v = 0; v < RawCols<CPL, BF16>::kVec; ++v) {
+        const uint32_t w4[4] = {r.v[v].x, r.v[v].y, r.v[v].z, r.v[v].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            if constexpr (BF16) {
                 x[v * 8 + 2 * h] = bf16_bits_to_f32(w4[h] & 0xFFFFu);
                 x[v * 8 + 2 * h + 1] = bf16_bits_to_f32(w4[h] >> 16);
+            } else {
+                x[v * 4 + h] = __uint_as_float(w4[h]);
             }
-        }
-    } else {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(row) + col0);
-#pragma unroll
-        for (int v = 0; v < CPL / 4; ++v) {
-            const float4 f = p[v];
-            x[v * 4 + 0] = f.x;
-            x[v * 4 + 1] = f.y;
-            x[v * 4 + 2] = f.z;
-            x[v * 4 + 3] = f.w;
         }
     }
 }
 
 template <int CPL, bool BF16>
-__device__ __forceinline__ void store_cols(void* row, int col0, const float (&x)[CPL]) {
-    if constexpr (BF16) {
-        uint4* p = reinterpret_cast<uint4*>(static_cast<uint16_t*>(row) + col0);
+__device__ __forceinline__ void load_cols(const void* row, int col0, float (&x)[CPL]) {
+    unpack_cols<CPL, BF16>(load_raw<CPL, BF16>(row, col0), x);
+}
+
+template <int CPL, bool BF16>
+__device__ __forceinline__ RawCols<CPL, BF16> pack_cols(const float (&x)[CPL]) {
+    RawCols<CPL, BF16> r;
 #pragma unroll
-        for (int v = 0; v < CPL / 8; ++v) {
-            uint32_t w4[4];
+    for (int v = 0; v < RawCols<CPL, BF16>::kVec; ++v) {
+        uint32_t w4[4];
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                w4[h] = f32_to_bf16_rne(x[v * 8 + 2 * h]) | (f32_to_bf16_rne(x[v * 8 + 2 * h + 1]) << 16);
-            }
-            p[v] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+        for (int h = 0; h < 4; ++h) {
+            w4[h] = BF16 ? (f32_to_bf16_rne(x[v * 8 + 2 * h]) | (f32_to_bf16_rne(x[v * 8 + 2 * h + 1]) << 16))
+                         : __float_as_uint(x[v * 4 + h]);
         }
-    } else {
-        float4* p = reinterpret_cast<float4*>(static_cast<float*>(row) + col0);
-#pragma unroll
-        for (int v = 0; v < CPL / 4; ++v) p[v] = make_float4(x[v * 4], x[v * 4 + 1], x[v * 4 + 2], x[v * 4 + 3]);
+        r.v[v] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }
+    return r;
+}
+
+template <int CPL, bool BF16>
+__device__ __forceinline__ void store_raw(void* row, int col0, const RawCols<CPL, BF16>& r) {
+    uint4* p = reinterpret_cast<uint4*>(static_cast<unsigned char*>(row) + col0 * (BF16 ? 2 : 4));
+#pragma unroll
+    for (int v = 0; v < RawCols<CPL, BF16>::kVec; ++v) p[v] = r.v[v];
+}
+
+// Pins computed values in registers at this point of the program (no code is emitted): later
+// memory operations cannot move above it, nor the computation below it.
+template <int CPL, bool BF16>
+__device__ __forceinline__ void pin_raw(const RawCols<CPL, BF16>& r) {
+#pragma unroll
+    for (int v = 0; v < RawCols<CPL, BF16>::kVec; ++v) {
+        asm volatile("" ::"v"(r.v[v].x), "v"(r.v[v].y), "v"(r.v[v].z), "v"(r.v[v].w) : "memory");
+    }
+}
+
+template <int CPL, bool BF16>
+__device__ __forceinline__ void store_cols(void* row, int col0, const float (&x)[CPL]) {
+    store_raw<CPL, BF16>(row, col0, pack_cols<CPL, BF16>(x));
 }
 
 // Members of a group per segment when the group is split (a workspace is given), and the last
@@ -85,22 +116,13 @@ __device__ __forceinline__ void store_cols(void* row, int col0, const float (&x)
 constexpr int kSeg = 32;
 constexpr int kSegLimit = (4095 / kSeg) * kSeg;
 
+// The general walk of the team at K-row position j of stream p (record r0, valid): a group's FIRST
+// or, when groups are split, a segment start; other positions return at once.
 template <int CPL, bool BANK_BF16, bool DV_BF16>
-__global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
-    static_assert(CPL % (BANK_BF16 ? 8 : 4) == 0 && CPL % (DV_BF16 ? 8 : 4) == 0, "16-byte column groups");
+__device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0, int col0, int tl) {
     // Member records and token rows loaded together (fewer when the rows take more registers).
     constexpr int kBatch = (CPL == 8 && DV_BF16) ? 4 : 2;
-    const int team = threadIdx.x >> a.ts_log2;
-    const int tl = threadIdx.x & ((1 << a.ts_log2) - 1);
-    const int64_t J = static_cast<int64_t>(blockIdx.x) * a.teams_per_block + team;
-    if (J >= static_cast<int64_t>(a.P) * a.CW) return;
-    const int p = static_cast<int>(J / a.CW);
-    const int j = static_cast<int>(J - static_cast<int64_t>(p) * a.CW);
-    const int col0 = tl * CPL;
-    if (col0 >= a.hd) return;   // lanes past the row (the team's lane 0 always stays)
     const uint4* kr = a.krec + (a.chunk0 + p) * a.CW;
-    const uint4 r0 = kr[j];
-    if (r0.x & kInvalid) return;
     // A team starts work at a group's FIRST, and, when groups are split, at every kSeg-th member.
     const bool split = a.part != nullptr;
     const int dist = static_cast<int>((r0.x >> kDistShift) & kDistMax);   // valid K entries before, in the group
@@ -111,8 +133,8 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
     constexpr int kBankEs = BANK_BF16 ? 2 : 4;
     constexpr int kDvEs = DV_BF16 ? 2 : 4;
     unsigned char* bank_row = static_cast<unsigned char*>(a.bank) + static_cast<int64_t>(r0.y) * a.hd * kBankEs;
-    float base[CPL];
-    if (first) load_cols<CPL, BANK_BF16>(bank_row, col0, base);   // in flight during the walk
+    // The base row (a group's FIRST only) stays in flight during the walk.
+    RawCols<CPL, BANK_BF16> base_raw = load_raw<CPL, BANK_BF16>(first ? bank_row : static_cast<unsigned char*>(a.bank), col0);
     const unsigned char* dv0 = static_cast<const unsigned char*>(a.dv) +
                                (a.dv_row0 + static_cast<int64_t>(p) * a.C) * a.hd * kDvEs;
     float acc[CPL];
@@ -142,11 +164,11 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
         uint4 rb[kBatch];
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) rb[b] = kr[min(m + b, a.CW - 1)];
-        float xv[kBatch][CPL];
+        RawCols<CPL, DV_BF16> xr[kBatch];
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
             const int tok = static_cast<int>((rb[b].x >> kTokShift) & 0xFFu);
-            load_cols<CPL, DV_BF16>(dv0 + static_cast<int64_t>(tok) * a.hd * kDvEs, col0, xv[b]);
+            xr[b] = load_raw<CPL, DV_BF16>(dv0 + static_cast<int64_t>(tok) * a.hd * kDvEs, col0);
         }
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
@@ -155,8 +177,10 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
                 break;
             }
             const float sc = __uint_as_float(rb[b].z);
+            float xv[CPL];
+            unpack_cols<CPL, DV_BF16>(xr[b], xv);
 #pragma unroll
-            for (int q = 0; q < CPL; ++q) acc[q] = fmaf(sc, xv[b][q], acc[q]);
+            for (int q = 0; q < CPL; ++q) acc[q] = fmaf(sc, xv[q], acc[q]);
             ++taken;
             if (rb[b].x & kLast) {
                 last_seen = true;
@@ -169,6 +193,8 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
         }
     }
     if (first && last_seen) {   // the whole group in one segment
+        float base[CPL];
+        unpack_cols<CPL, BANK_BF16>(base_raw, base);
         float o[CPL];
 #pragma unroll
         for (int q = 0; q < CPL; ++q) o[q] = fmaf(base[q], cpe, acc[q]);
@@ -216,13 +242,109 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
     store_cols<CPL, BANK_BF16>(brow, col0, o);
 }
 
-template <int CPL, bool BB, bool DB>
-hipError_t launch_dw(DwArgs a, hipStream_t st, const hipEvent_t* ev) {
-    const int64_t teams = static_cast<int64_t>(a.P) * a.CW;
+// Teams take U consecutive K-row positions. Groups of one member (the common case) are done
+// together: their records, base rows and token rows are all in flight at once. Every other valid
+// position goes through the general walk, one after the other.
+template <int CPL, bool BANK_BF16, bool DV_BF16, int U>
+__global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
+    static_assert(CPL % (BANK_BF16 ? 8 : 4) == 0 && CPL % (DV_BF16 ? 8 : 4) == 0, "16-byte column groups");
+    constexpr int kBankEs = BANK_BF16 ? 2 : 4;
+    constexpr int kDvEs = DV_BF16 ? 2 : 4;
+    const int team = threadIdx.x >> a.ts_log2;
+    const int tl = threadIdx.x & ((1 << a.ts_log2) - 1);
+    const int total = a.P * a.CW;   // < 2^31 (host checked)
+    const int J0 = (static_cast<int>(blockIdx.x) * a.teams_per_block + team) * U;
+    if (J0 >= total) return;
+    const int col0 = tl * CPL;
+    if (col0 >= a.hd) return;   // lanes past the row (the team's lane 0 always stays)
+    const uint4* kr_step = a.krec + a.chunk0 * a.CW;
+    if constexpr (U == 1) {   // one position: straight into the walk (its first member is the short path)
+        const uint4 r0 = kr_step[J0];
+        const int p = J0 / a.CW;
+        if (!(r0.x & kInvalid)) dw_walk<CPL, BANK_BF16, DV_BF16>(a, p, J0 - p * a.CW, r0, col0, tl);
+        return;
+    }
+    // The records of positions J0 .. J0+U-1 (the steps' chunks are contiguous in krec), then the
+    // base and token rows of the one-member groups among them, all in flight before any is used.
+    uint4 r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        r[u] = kr_step[min(J0 + u, total - 1)];
+        if (J0 + u >= total) r[u].x = kInvalid;
+    }
+    // Which positions hold one-member groups, decided for all of them (one wait for every record)
+    // before any row load is issued.
+    uint32_t ones = 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const bool one = (r[u].x & (kInvalid | kFirst | kLast)) == (kFirst | kLast) && static_cast<int64_t>(r[u].y) < a.rows;
+        ones |= one ? 1u << u : 0u;
+    }
+    // Keeps the compiler from sinking the record waits between the row loads (where the wait for a
+    // later record would also wait for the rows already in flight).
+    asm volatile("" ::"v"(ones) : "memory");
+    RawCols<CPL, BANK_BF16> braw[U] = {};
+    RawCols<CPL, DV_BF16> xraw[U] = {};
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (ones & (1u << u)) {
+            const int pu = (J0 + u) / a.CW;
+            const int64_t tok_row = static_cast<int64_t>(pu) * a.C + ((r[u].x >> kTokShift) & 0xFFu);
+            braw[u] = load_raw<CPL, BANK_BF16>(static_cast<const unsigned char*>(a.bank) +
+                                                   static_cast<int64_t>(r[u].y) * a.hd * kBankEs,
+                                               col0);
+            xraw[u] = load_raw<CPL, DV_BF16>(static_cast<const unsigned char*>(a.dv) + (a.dv_row0 + tok_row) * a.hd * kDvEs,
+                                             col0);
+        }
+    }
+    // Every new row first (rows of other positions are computed on zeros and dropped), then the
+    // stores: gfx9 counts stores in vmcnt, so a wait placed between stores would hold them up.
+    RawCols<CPL, BANK_BF16> oraw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const float sc = __uint_as_float(r[u].z), cpe = __uint_as_float(r[u].w);
+        float b[CPL], x[CPL], o[CPL];
+        unpack_cols<CPL, BANK_BF16>(braw[u], b);
+        unpack_cols<CPL, DV_BF16>(xraw[u], x);
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) o[q] = fmaf(b[q], cpe, fmaf(sc, x[q], 0.0f));
+        oraw[u] = pack_cols<CPL, BANK_BF16>(o);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) pin_raw<CPL, BANK_BF16>(oraw[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (ones & (1u << u)) {
+            store_raw<CPL, BANK_BF16>(static_cast<unsigned char*>(a.bank) + static_cast<int64_t>(r[u].y) * a.hd * kBankEs,
+                                      col0, oraw[u]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (!(ones & (1u << u)) && !(r[u].x & kInvalid)) {
+            const int pu = (J0 + u) / a.CW;
+            dw_walk<CPL, BANK_BF16, DV_BF16>(a, pu, J0 + u - pu * a.CW, r[u], col0, tl);
+        }
+    }
+}
+
+// Positions per team: 2 once the launch has at least 32 waves per compute unit (two rows in flight
+// per team then outweigh the shorter grid), else 1.
+constexpr int64_t kDwWavesForPairs = 32 * 256;
+
+template <int CPL, bool BB, bool DB, int U>
+hipError_t launch_dw_u(DwArgs a, hipStream_t st, const hipEvent_t* ev) {
+    const int64_t teams = (static_cast<int64_t>(a.P) * a.CW + U - 1) / U;
     const int64_t blocks = (teams + a.teams_per_block - 1) / a.teams_per_block;
     void* kargs[] = {&a};
-    return hipExtLaunchKernel(reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB>), dim3(static_cast<unsigned>(blocks)),
-                              dim3(kDwThreads), kargs, 0, st, ev[0], ev[1], 0);
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U>),
+                              dim3(static_cast<unsigned>(blocks)), dim3(kDwThreads), kargs, 0, st, ev[0], ev[1], 0);
+}
+
+template <int CPL, bool BB, bool DB>
+hipError_t launch_dw(const DwArgs& a, hipStream_t st, const hipEvent_t* ev) {
+    const int64_t waves = static_cast<int64_t>(a.P) * a.CW * (int64_t(1) << a.ts_log2) / kWave;
+    return waves >= kDwWavesForPairs ? launch_dw_u<CPL, BB, DB, 2>(a, st, ev) : launch_dw_u<CPL, BB, DB, 1>(a, st, ev);
 }
 
 template <int CPL>

@@ -150,10 +150,13 @@ def test_masked_tokens_do_not_leak():
     dict(C=64, W=2, R=3, S=1, P=1, steps=2, vl=0),        # one slot; last chunk fully masked
     dict(C=256, W=17, R=3, S=1, P=1, steps=1, vl=None),   # one group of 5120: saturated counts
     dict(C=100, W=7, R=9, S=3000, P=3, steps=2, vl=50),   # 1600 entries: two radix tiles
+    # An odd K row (8415 positions) in a DW launch wide enough for two positions per team of lanes.
+    dict(C=255, W=33, R=2, S=5000, P=1, steps=1, vl=None, hd=960, bank="bf16"),
 ])
 def test_edge_shapes(case):
     sh = W.Shape("edge", P=case["P"], T=case["C"] * case["steps"], C=case["C"], W=case["W"], R=case["R"],
-                 S=case["S"], hd=64, bank_dtype="f32", dv_dtype="f32", slots="uniform", valid_last=case["vl"])
+                 S=case["S"], hd=case.get("hd", 64), bank_dtype=case.get("bank", "f32"), dv_dtype="f32",
+                 slots="uniform", valid_last=case["vl"])
     wl = W.make(sh, seed=777)
     say("edge shape", case)
     shape, out = H.run_phase1(wl)
