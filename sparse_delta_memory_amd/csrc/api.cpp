@@ -114,16 +114,18 @@ sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st
     if (main_lds > static_cast<size_t>(lds_max))
         return fail(SDM_EUNSUPPORTED, "sdm_phase1: the sort/scan kernel needs %zu B of LDS per block, the device has %d",
                     main_lds, lds_max);
-    const size_t tri = static_cast<size_t>(s->C) * (s->C + 1) / 2 * sizeof(float);
+    const size_t tri = sdm::p1_pair_lds_min(s);
     if ((io->a != nullptr || io->qk != nullptr) && tri > static_cast<size_t>(lds_max))
-        return fail(SDM_EUNSUPPORTED, "sdm_phase1: a C=%d triangle (%zu B) exceeds the %d B of LDS per block", s->C, tri,
-                    lds_max);
+        return fail(SDM_EUNSUPPORTED, "sdm_phase1: the C=%d pair kernel (%zu B) exceeds the %d B of LDS per block", s->C,
+                    tri, lds_max);
     sdm::P1Launch L;
     L.s = s;
     L.io = io;
     L.rec = static_cast<char*>(io->workspace) + ws.rec_off;
     L.inv = static_cast<char*>(io->workspace) + ws.inv_off;
     L.walk = static_cast<char*>(io->workspace) + ws.walk_off;
+    L.hot = static_cast<char*>(io->workspace) + ws.hot_off;
+    L.lds_max = lds_max;
     const hipError_t e = sdm::p1_launch(L, st);
     if (e != hipSuccess) return fail(SDM_EHIP, "sdm_phase1: %s", hipGetErrorString(e));
     return SDM_OK;

@@ -62,8 +62,11 @@ struct P1Args {
     int32_t* tiles_k;
     int32_t* repeats;
     uint4* rec;
+    uint2* hot;          // per chunk: {count, 0}, then {head position, size} of each hot group (NULL: none)
     int C, W, R, P, key_bits, first_partial, valid_last, tile_len, digit_bits;
     int stage_bytes;
+    int hot_min;         // valid K entries that make a group hot for the pair kernel
+    int hot_cap;         // hot groups one chunk can have (list entries after the count)
     uint32_t wr_magic;   // ceil(2^32 / (W + R)): r / (W + R) == umulhi(r, wr_magic) for r < 2^17
     int64_t stream_offset;
     Rounds rounds;
@@ -288,6 +291,8 @@ struct Entry {
     uint32_t bcnt;   // own-kind valid peers before
     uint32_t acnt;   // own-kind valid peers after
     uint32_t jkind;  // index in its kind's sorted row
+    uint32_t kg;     // valid K entries of its group
+    uint32_t gsize;  // valid entries of its group
     float v;
 };
 
@@ -304,6 +309,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     __shared__ Seg wtot[kNW];
     __shared__ uint32_t wsum[kNW];
     __shared__ uint32_t tile_kind[NTILE + 1];   // kind counts (K | Q << 16) before each tile
+    __shared__ uint32_t hot_n;                   // hot groups found so far
+    uint2* hot_buf = reinterpret_cast<uint2*>(smem + a.stage_bytes + NP * 2 + 256 * sizeof(float));
 
     const int c = blockIdx.x;
     const int C = a.C, W = a.W, R = a.R;
@@ -322,6 +329,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     const int ntiles = (n + kTile - 1) / kTile;
 
     for (int t = threadIdx.x; t < C; t += kNT) gates[t] = t < tv ? a.g[static_cast<int64_t>(c) * C + t] : 0.0f;
+    if (threadIdx.x == 0) hot_n = 0u;
 
     // ---- 1. keys (element i of the striped layout is entry r = i) and the sort.
     {
@@ -548,6 +556,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             const bool pq = static_cast<int>(pr) - pt * wr >= W;
             const bool same_run = !head && pt == e.t && pq == e.q;
             e.walk = e.valid && !same_run && (before.f & 0xFFFFu) != 0u;
+            e.kg = (before.f & 0xFFFFu) + (afts[k] & 0xFFFFu) + ((e.valid && !e.q) ? 1u : 0u);
+            e.gsize = e.kg + ((before.f >> 16) & 0x7FFFu) + ((afts[k] >> 16) & 0x7FFFu) + ((e.valid && e.q) ? 1u : 0u);
             if (e.live) {
                 jq += e.q ? 1u : 0u;
                 jk += e.q ? 0u : 1u;
@@ -597,7 +607,9 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                     if (mask & (1u << kFPosK)) *reinterpret_cast<uint32_t*>(stage_at(kFPosK, o)) = packed;
                 }
                 if (mask & (1u << kFInv)) *reinterpret_cast<uint16_t*>(stage_at(kFInv, e.r)) = static_cast<uint16_t>(p);
-                if (mask & (1u << kFWalk)) *stage_at(kFWalk, e.r) = e.walk ? 1 : 0;
+                if (mask & (1u << kFWalk)) {   // 1: walked by the pair kernel, 2: summed by its hot-group pass
+                    *stage_at(kFWalk, e.r) = e.walk ? (e.kg >= static_cast<uint32_t>(a.hot_min) ? 2 : 1) : 0;
+                }
             });
         }
         lds_barrier();
@@ -646,6 +658,10 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
         unsigned char* st_spq = st_spk + (nk_t * 4 + 15) / 16 * 16;
         for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
             if (!e.live) return;
+            // Hot groups (the pair kernel sums them densely): appended in any order, sorted below.
+            if (a.hot != nullptr && e.valid && e.head && e.kg >= static_cast<uint32_t>(a.hot_min)) {
+                hot_buf[atomicAdd(&hot_n, 1u)] = make_uint2(static_cast<uint32_t>(p), e.gsize);
+            }
             if (joint && rec_bytes > 0) {
                 // Pair records {payload | head, log-cumsum s, c, value}.
                 reinterpret_cast<uint4*>(st_rec)[p - pbase] = make_uint4(
@@ -679,31 +695,73 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
         if (a.spay_q != nullptr) block_copy_out(a.spay_q + cr + q0, st_spq, nq_t, 4);
         lds_barrier();
     }
+    if (a.hot != nullptr) {
+        // The hot list in position order: each entry's rank is the number of heads before it.
+        const int nh = static_cast<int>(hot_n);   // every append happened before the last barrier
+        uint2* out = a.hot + static_cast<int64_t>(c) * (a.hot_cap + 1);
+        for (int x = threadIdx.x; x < nh; x += kNT) {
+            const uint2 me = hot_buf[x];
+            int rank = 0;
+            for (int y = 0; y < nh; ++y) rank += hot_buf[y].x < me.x ? 1 : 0;
+            out[1 + rank] = me;
+        }
+        if (threadIdx.x == 0) out[0] = make_uint2(static_cast<uint32_t>(nh), 0u);
+    }
 }
 
-// Pair sums. Block (chunk, triangle): one thread per row i. Token i's entries of the block's kind
-// (K for A, Q for QK) that share a slot sit next to each other in the sorted row and share one
-// log-cumsum, and so do the K entries of any earlier token j in that group. For every group in
-// which token i's run has earlier K entries (flagged by the sort/scan kernel), the thread sums
-// the run's values (w_i) once, then walks the group from just before the run back to its head,
-// summing each earlier token's K values (k_j) over its run, and adds w_i * k_j * exp(L_i - L_j)
-// to cell (i, j) (j != i for A). Every cell has one writer thread and a term order fixed by the
-// input; the triangle lives in LDS and is written out as a dense [C, C] matrix, zeros outside it.
+// Pair sums. Block (chunk, triangle): the triangle of the block's matrix lives in LDS and every
+// cell has one writer at a time, so no floating-point atomics are needed. Token i's entries of
+// the block's kind (K for A, Q for QK) that share a slot sit next to each other in the sorted row
+// and share one log-cumsum L, and so do the K entries of any earlier token j in that group. One
+// term per (group, run of token i, K run of token j): w_i * k_j * exp(L_i - L_j), the run sums w
+// and k taken over the run's values, L as the compensated pair (s, c).
+//
+// Hot groups (many K entries; listed by the sort/scan kernel) are summed densely: their runs are
+// gathered into LDS tables (K runs, and the runs of the block's kind as rows, each with the number
+// of K runs before it), then the threads that own row i sweep, group after group, the K runs
+// before each of row i's runs. The other groups are walked
+// by thread i from each flagged run back to the group's head. Terms reach a cell in an order fixed
+// by the input (hot groups in position order, then the walks).
 struct PairArgs {
     const uint4* rec;
     const uint16_t* inv;
     const uint8_t* walk;
+    const uint2* hot;   // per chunk: {count, 0}, then {head position, size} in position order (NULL: none)
     float* a;
     float* qk;
-    int C, W, R, first_partial, valid_last;
+    int C, W, R, first_partial, valid_last, hot_cap, tab_cap;
 };
 
-constexpr int kPairThreads = 512;   // rows walk on the first C threads; all write the output
+// Threads per pair block: 512, or 1024 where the LDS allows one block per compute unit anyway.
+constexpr size_t kPairStaticLds = 256;   // room left for the kernel's static LDS (scan partials)
 constexpr int kWalkBatch = 8;
 
+// Hot groups per batch (a group bit in one 32-bit mask per token).
+constexpr int kPairBatchGroups = 32;
+
+// LDS of the pair kernel: the triangle, the hot list, per-group table bases, per-token group
+// masks, per-group token bitmaps, the two run tables.
+struct PairLds {
+    size_t tri, hot, gbase, tmask, pres, ktab, rtab, total;
+};
+__host__ __device__ inline PairLds pair_lds_layout(int C, int hot_cap, int tab_cap) {
+    auto up = [](size_t b) { return (b + 15) / 16 * 16; };
+    PairLds l;
+    l.tri = 0;
+    l.hot = up(static_cast<size_t>(C) * (C + 1) / 2 * sizeof(float));
+    l.gbase = l.hot + up(static_cast<size_t>(hot_cap) * 2 * sizeof(uint32_t) + 16);   // + batch bounds
+    l.tmask = l.gbase + up(static_cast<size_t>(hot_cap + 1) * 3 * sizeof(uint32_t));
+    l.pres = l.tmask + up(static_cast<size_t>(C) * sizeof(uint32_t));
+    l.ktab = l.pres + static_cast<size_t>(kPairBatchGroups) * 8 * sizeof(uint32_t);
+    l.rtab = l.ktab + static_cast<size_t>(tab_cap) * 16;
+    l.total = l.rtab + static_cast<size_t>(tab_cap) * 16;
+    return l;
+}
+
+template <int kPairThreads>
 __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
+    constexpr int kPairWaves = kPairThreads / kWave;
     extern __shared__ __align__(16) unsigned char smem[];
-    float* tri = reinterpret_cast<float*>(smem);
     const bool q = blockIdx.y == 1;
     float* out = q ? a.qk : a.a;
     if (out == nullptr) return;   // block-uniform
@@ -712,11 +770,235 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
     const int wr = W + R;
     const int n = C * wr;
     const int tv = c >= a.first_partial ? a.valid_last : C;
+    const PairLds lay = pair_lds_layout(C, a.hot_cap, a.tab_cap);
+    float* tri = reinterpret_cast<float*>(smem + lay.tri);
+    uint2* hl = reinterpret_cast<uint2*>(smem + lay.hot);               // hot list of the chunk
+    int* bounds = reinterpret_cast<int*>(smem + lay.hot) + 2 * a.hot_cap;   // batch end, positions
+    uint32_t* ubase = reinterpret_cast<uint32_t*>(smem + lay.gbase);    // batch-local first position
+    uint32_t* gk = ubase + (a.hot_cap + 1);                              // first K-run index per group
+    uint32_t* gr = gk + (a.hot_cap + 1);                                 // first row-run index per group
+    uint32_t* tmask = reinterpret_cast<uint32_t*>(smem + lay.tmask);     // batch groups with a row run of token t
+    uint32_t* pres = reinterpret_cast<uint32_t*>(smem + lay.pres);       // per group: tokens with a row run
+    uint4* ktab = reinterpret_cast<uint4*>(smem + lay.ktab);
+    uint4* rtab = reinterpret_cast<uint4*>(smem + lay.rtab);
     const int tri_size = C * (C + 1) / 2;
     for (int e = threadIdx.x; e < tri_size; e += kPairThreads) tri[e] = 0.0f;
-    __syncthreads();
     const int64_t crow = static_cast<int64_t>(c) * n;
     const uint4* rec = a.rec + crow;
+    const uint32_t row_q = q ? kIsQ : 0u;
+    const int lane = static_cast<int>(lane_id());
+    const int wave = threadIdx.x / kWave;
+
+    // ---- Hot groups, in batches whose runs fit the tables.
+    const int nh = a.hot != nullptr ? static_cast<int>(a.hot[static_cast<int64_t>(c) * (a.hot_cap + 1)].x) : 0;
+    if (nh > 0) {
+        const uint2* hsrc = a.hot + static_cast<int64_t>(c) * (a.hot_cap + 1) + 1;
+        for (int g = threadIdx.x; g < nh; g += kPairThreads) hl[g] = hsrc[g];
+    }
+    __syncthreads();
+    for (int g0 = 0; g0 < nh;) {
+        if (threadIdx.x == 0) {   // the batch: groups g0 .. g1-1, at most tab_cap runs of each table
+            int g1 = g0, runs = 0;
+            uint32_t pos = 0;
+            while (g1 < nh) {
+                const int r = min(static_cast<int>(hl[g1].y), C);   // runs of one kind in a group <= tokens
+                if (g1 > g0 && (runs + r > a.tab_cap || g1 - g0 == kPairBatchGroups)) break;
+                ubase[g1 - g0] = pos;
+                pos += hl[g1].y;
+                runs += r;
+                ++g1;
+            }
+            ubase[g1 - g0] = pos;
+            bounds[0] = g1;
+            bounds[1] = static_cast<int>(pos);
+        }
+        __syncthreads();
+        const int g1 = bounds[0];
+        const int np = bounds[1];
+        const int ng = g1 - g0;
+        // Thread x takes the batch positions [u0, u1) (group by group); run starts are counted, then
+        // numbered with one block scan, then written.
+        const int per = (np + kPairThreads - 1) / kPairThreads;
+        const int u0 = min(np, static_cast<int>(threadIdx.x) * per), u1 = min(np, u0 + per);
+        int g = 0;
+        while (g + 1 < ng && static_cast<int>(ubase[g + 1]) <= u0) ++g;
+        // Positions are read kWin at a time (all loads in flight together). Per window: the sorted
+        // position, whether it starts its group, its group, and the group's end position.
+        constexpr int kWin = 8;
+        constexpr uint32_t kTag = kIsQ | (0xFFu << kTokShift);   // (kind, token) of an entry
+        struct Cursor {
+            int gg, gstart, gnext, ghead, gend;
+        };
+        auto cursor_at = [&](int gg) {
+            Cursor cu;
+            cu.gg = gg;
+            cu.gstart = static_cast<int>(ubase[gg]);
+            cu.gnext = static_cast<int>(ubase[gg + 1]);
+            cu.ghead = static_cast<int>(hl[g0 + gg].x);
+            cu.gend = cu.ghead + static_cast<int>(hl[g0 + gg].y);
+            return cu;
+        };
+        auto window = [&](int ub, int cnt, Cursor& cu, int (&rho)[kWin], bool (&fst)[kWin], int (&grp)[kWin],
+                          int (&gend)[kWin]) {
+#pragma unroll
+            for (int b = 0; b < kWin; ++b) {
+                const int u = ub + min(b, cnt - 1);
+                if (u >= cu.gnext) cu = cursor_at(cu.gg + 1);   // positions advance by at most one group
+                rho[b] = cu.ghead + (u - cu.gstart);
+                fst[b] = u == cu.gstart && b < cnt;
+                grp[b] = cu.gg;
+                gend[b] = cu.gend;
+            }
+        };
+        for (int t = threadIdx.x; t < C; t += kPairThreads) tmask[t] = 0u;
+        for (int t = threadIdx.x; t < kPairBatchGroups * 8; t += kPairThreads) pres[t] = 0u;
+        uint32_t counts = 0;   // K-run starts | row-run starts << 16
+        {
+            Cursor cu = cursor_at(g);
+            uint32_t prev = 0xFFFFFFFFu;
+            for (int ub = u0; ub < u1; ub += kWin) {
+                const int cnt = min(kWin, u1 - ub);
+                int rho[kWin], grp[kWin], gend[kWin];
+                bool fst[kWin];
+                window(ub, cnt, cu, rho, fst, grp, gend);
+                uint32_t x[kWin];
+#pragma unroll
+                for (int b = 0; b < kWin; ++b) x[b] = rec[rho[b]].x;
+                if (prev == 0xFFFFFFFFu && !fst[0]) prev = rec[rho[0] - 1].x;
+#pragma unroll
+                for (int b = 0; b < kWin; ++b) {
+                    if (b >= cnt) break;
+                    const bool cont = !fst[b] && (prev & kTag) == (x[b] & kTag);
+                    counts += (!(x[b] & kIsQ) && !cont) ? 1u : 0u;
+                    counts += ((x[b] & kIsQ) == row_q && !cont) ? (1u << 16) : 0u;
+                    prev = x[b];
+                }
+            }
+        }
+        __shared__ uint32_t psum[kPairWaves];
+        uint32_t incl = counts;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const uint32_t o = __shfl_up(incl, d, kWave);
+            if (lane >= d) incl += o;
+        }
+        if (lane == kWave - 1) psum[wave] = incl;
+        __syncthreads();
+        uint32_t base = incl - counts;
+        for (int w = 0; w < wave; ++w) base += psum[w];
+        {
+            Cursor cu = cursor_at(g);
+            uint32_t kx = base & 0xFFFFu, rx = base >> 16;
+            uint32_t prev = 0xFFFFFFFFu;
+            for (int ub = u0; ub < u1; ub += kWin) {
+                const int cnt = min(kWin, u1 - ub);
+                int rho[kWin], grp[kWin], gend[kWin];
+                bool fst[kWin];
+                window(ub, cnt, cu, rho, fst, grp, gend);
+                uint4 r[kWin];
+#pragma unroll
+                for (int b = 0; b < kWin; ++b) r[b] = rec[rho[b]];
+                // The entry after the window's last, when still in its group (a run may go on).
+                const int last_rho = rho[kWin - 1];   // the window's last valid position (clamped)
+                const bool more = last_rho + 1 < gend[kWin - 1];
+                const uint4 nx0 = rec[more ? last_rho + 1 : last_rho];
+                if (prev == 0xFFFFFFFFu && !fst[0]) prev = rec[rho[0] - 1].x;
+                // Run sums inside the window, from the back: suf[b] = value of b plus the rest of its run.
+                // (Elements past cnt repeat the last one, so r[kWin - 1] is the window's last entry.)
+                const uint32_t last_tag = r[kWin - 1].x & kTag;
+                float tail = 0.0f;
+                if (more && (nx0.x & kTag) == last_tag) {
+                    tail = __uint_as_float(nx0.w);
+                    for (int p2 = last_rho + 2; p2 < gend[kWin - 1]; ++p2) {
+                        const uint4 nx = rec[p2];
+                        if ((nx.x & kTag) != last_tag) break;
+                        tail = tail + __uint_as_float(nx.w);
+                    }
+                }
+                float suf[kWin];
+                float after = tail;   // the run sum that continues past element b
+#pragma unroll
+                for (int b = kWin - 1; b >= 0; --b) {
+                    if (b >= cnt) continue;
+                    suf[b] = __uint_as_float(r[b].w) + after;
+                    // element b continues the run of element b-1?
+                    const bool joins_prev = b > 0 && !fst[b] && (r[b].x & kTag) == (r[b - 1].x & kTag);
+                    after = joins_prev ? suf[b] : 0.0f;
+                }
+#pragma unroll
+                for (int b = 0; b < kWin; ++b) {
+                    if (b >= cnt) break;
+                    if (fst[b]) {   // group bases (the thread holding a group's first position)
+                        gk[grp[b]] = kx;
+                        gr[grp[b]] = rx;
+                    }
+                    const bool cont = !fst[b] && (prev & kTag) == (r[b].x & kTag);
+                    prev = r[b].x;
+                    if (cont) continue;
+                    const bool is_k = !(r[b].x & kIsQ), is_row = (r[b].x & kIsQ) == row_q;
+                    const uint32_t tok = (r[b].x >> kTokShift) & 0xFFu;
+                    if (is_row) {
+                        rtab[rx] = make_uint4(tok | (kx << 8), __float_as_uint(suf[b]), r[b].y, r[b].z);
+                        atomicOr(tmask + tok, 1u << grp[b]);
+                        atomicOr(pres + grp[b] * 8 + (tok >> 5), 1u << (tok & 31u));
+                    }
+                    if (is_k) ktab[kx] = make_uint4(tok, __float_as_uint(suf[b]), r[b].y, r[b].z);
+                    kx += is_k ? 1u : 0u;
+                    rx += is_row ? 1u : 0u;
+                }
+            }
+        }
+        if (threadIdx.x == kPairThreads - 1) {   // end bases: the batch totals
+            gk[ng] = (base & 0xFFFFu) + (counts & 0xFFFFu);
+            gr[ng] = (base >> 16) + (counts >> 16);
+        }
+        __syncthreads();
+        // Dense terms: kRowThreads threads own row i across every group of the batch (no barrier
+        // between groups), each taking every kRowThreads-th K run of the row run's prefix,
+        // kColBlock at a time (table reads, then cell reads, then cell writes: the cells of a block
+        // are distinct, a group holding one K run per token). A row run's table index is its
+        // group's first row index plus the group's row tokens below i.
+        constexpr int kRowThreads = kPairThreads / 256, kColBlock = 8;
+        for (int i = static_cast<int>(threadIdx.x) / kRowThreads; i < tv; i += kPairThreads / kRowThreads) {
+            const int sub = static_cast<int>(threadIdx.x) % kRowThreads;
+            float* row = tri + i * (i + 1) / 2;
+            for (uint32_t gm = tmask[i]; gm != 0u; gm &= gm - 1u) {
+                const int gg = __builtin_ctz(gm);
+                const uint32_t* pg = pres + gg * 8;
+                int below = 0;
+#pragma unroll
+                for (int wd = 0; wd < 8; ++wd) {
+                    const uint32_t bits = pg[wd];
+                    const int lo = wd * 32;
+                    below += i >= lo + 32 ? __popc(bits) : (i > lo ? __popc(bits & ((1u << (i - lo)) - 1u)) : 0);
+                }
+                const uint32_t kb = gk[gg];
+                const uint4 me = rtab[gr[gg] + below];
+                const int ncol = static_cast<int>((me.x >> 8) - kb);
+                const float wi = __uint_as_float(me.y), si = __uint_as_float(me.z), ci = __uint_as_float(me.w);
+                for (int c0 = sub; c0 < ncol; c0 += kRowThreads * kColBlock) {
+                    uint4 kt[kColBlock];
+#pragma unroll
+                    for (int b = 0; b < kColBlock; ++b) kt[b] = ktab[kb + min(c0 + b * kRowThreads, ncol - 1)];
+                    float term[kColBlock], cell[kColBlock];
+#pragma unroll
+                    for (int b = 0; b < kColBlock; ++b) {
+                        term[b] = (wi * __uint_as_float(kt[b].y)) *
+                                  expf((si - __uint_as_float(kt[b].z)) + (ci - __uint_as_float(kt[b].w)));
+                        cell[b] = row[kt[b].x];
+                    }
+#pragma unroll
+                    for (int b = 0; b < kColBlock; ++b) {
+                        if (c0 + b * kRowThreads < ncol) row[kt[b].x] = cell[b] + term[b];
+                    }
+                }
+            }
+        }
+        __syncthreads();   // the tables are rebuilt for the next batch
+        g0 = g1;
+    }
+
+    // ---- Other groups: thread i walks its flagged runs back to the group head.
     const int i = threadIdx.x;
     if (i < tv) {
         float* row = tri + i * (i + 1) / 2;
@@ -728,12 +1010,12 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
         const uint32_t own_tag = (q ? kIsQ : 0u) | (static_cast<uint32_t>(i) << kTokShift);
         const uint32_t tag_mask = kIsQ | (0xFFu << kTokShift);
         for (int lb = 0; lb < lanes; lb += 32) {
-          // The flags of up to 32 lanes, loaded together, then only the flagged lanes.
+          // The flags of up to 32 lanes, loaded together, then only the lanes walked here.
           uint32_t flags = 0;
 #pragma unroll
           for (int u = 0; u < 32; ++u) {
               const int ln = lb + u;
-              flags |= (ln < lanes && wf[min(ln, lanes - 1)] != 0) ? (1u << u) : 0u;
+              flags |= (ln < lanes && wf[min(ln, lanes - 1)] == 1) ? (1u << u) : 0u;
           }
           for (; flags != 0u; flags &= flags - 1u) {
             const int ln = lb + __builtin_ctz(flags);
@@ -826,7 +1108,9 @@ MainPlan plan_main(const sdm_p1_shape* s, const sdm_p1_io* io, bool with_pairs_w
     const int n = s->C * (s->W + s->R);
     m.ipt = n <= kNT ? 1 : n <= 2 * kNT ? 2 : n <= 4 * kNT ? 4 : n <= 8 * kNT ? 8 : 16;
     const int np = kNT * m.ipt;
-    const int fixed = np * 2 + 256 * static_cast<int>(sizeof(float));   // sorted row + gates
+    // Sorted row, gates and (with pair sums) the chunk's hot-group list.
+    const int fixed = np * 2 + 256 * static_cast<int>(sizeof(float)) +
+                      (with_pairs_ws ? s->C * s->W / kHotMin * static_cast<int>(sizeof(uint2)) : 0);
     const int cap_max = (kLdsTotal - kStaticReserve - fixed) / 16 * 16;
     // Widest digit (<= 10 bits) whose per-wave counts fit beside the keys.
     int d = 10;
@@ -887,8 +1171,14 @@ P1Workspace p1_workspace_layout(const sdm_p1_shape* s) {
     w.rec_off = 0;
     w.inv_off = up(N * n * sizeof(uint4));
     w.walk_off = w.inv_off + up(N * n * sizeof(uint16_t));
-    w.total = w.walk_off + up(N * n);
+    w.hot_cap = s->C * s->W / kHotMin;
+    w.hot_off = w.walk_off + up(N * n);
+    w.total = w.hot_off + up(N * static_cast<size_t>(w.hot_cap + 1) * sizeof(uint2));
     return w;
+}
+
+size_t p1_pair_lds_min(const sdm_p1_shape* s) {
+    return pair_lds_layout(s->C, s->C * s->W / kHotMin, 0).total + kPairStaticLds;
 }
 
 size_t p1_lds_bytes(const sdm_p1_shape* s, const sdm_p1_io* io) {
@@ -916,6 +1206,20 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     a.tiles_k = io->tiles_k;
     a.repeats = io->repeats;
     a.rec = pairs ? static_cast<uint4*>(Lc.rec) : nullptr;
+    // Hot groups only when the pair kernel's run tables (at least C runs of each kind) fit in LDS.
+    const int hot_cap = s->C * s->W / kHotMin;
+    // Table capacity: as large as the blocks per compute unit that the smallest tables (C runs of
+    // each kind) allow still fit; at least C when hot groups are on.
+    const size_t pair_fixed = pair_lds_layout(s->C, hot_cap, 0).total + kPairStaticLds;
+    const size_t pair_min = pair_fixed + static_cast<size_t>(s->C) * 32;
+    const int blocks_cu = pair_min <= static_cast<size_t>(Lc.lds_max) ? static_cast<int>(Lc.lds_max / pair_min) : 0;
+    const int tab_cap = blocks_cu > 0
+                            ? min(4096, static_cast<int>((static_cast<size_t>(Lc.lds_max) / blocks_cu - pair_fixed) / 32))
+                            : 0;
+    const bool hot_on = pairs && hot_cap > 0 && tab_cap >= s->C;
+    a.hot = pairs ? static_cast<uint2*>(Lc.hot) : nullptr;
+    a.hot_min = hot_on ? kHotMin : 0x7FFFFFFF;
+    a.hot_cap = hot_cap;
     a.C = s->C;
     a.W = s->W;
     a.R = s->R;
@@ -949,6 +1253,9 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     pa.rec = static_cast<const uint4*>(Lc.rec);
     pa.inv = static_cast<const uint16_t*>(Lc.inv);
     pa.walk = static_cast<const uint8_t*>(Lc.walk);
+    pa.hot = static_cast<const uint2*>(Lc.hot);
+    pa.hot_cap = hot_cap;
+    pa.tab_cap = hot_on ? tab_cap : 0;
     pa.a = io->a;
     pa.qk = io->qk;
     pa.C = s->C;
@@ -956,13 +1263,14 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     pa.R = s->R;
     pa.first_partial = s->first_partial;
     pa.valid_last = s->valid_last;
-    const size_t lds = static_cast<size_t>(s->C) * (s->C + 1) / 2 * sizeof(float);
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&p1_pairs_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(lds));
+    const size_t lds = pair_lds_layout(s->C, hot_cap, pa.tab_cap).total;
+    const int threads = blocks_cu == 1 ? 1024 : 512;
+    const void* fn = threads == 1024 ? reinterpret_cast<const void*>(&p1_pairs_kernel<1024>)
+                                     : reinterpret_cast<const void*>(&p1_pairs_kernel<512>);
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     void* kargs[] = {&pa};
-    return hipExtLaunchKernel(reinterpret_cast<const void*>(&p1_pairs_kernel), dim3(s->N, 2), dim3(kPairThreads), kargs,
-                              lds, st, ev[2], ev[3], 0);
+    return hipExtLaunchKernel(fn, dim3(s->N, 2), dim3(threads), kargs, lds, st, ev[2], ev[3], 0);
 }
 
 }  // namespace sdm

@@ -13,22 +13,32 @@ namespace sdm {
 constexpr int kP1MaxRow = 16384;
 constexpr int kP1Threads = 1024;
 
+// Valid K entries that make a slot group "hot": the pair kernel sums such groups densely.
+constexpr int kHotMin = 32;
+
 struct P1Launch {
     const sdm_p1_shape* s;
     const sdm_p1_io* io;
     void* rec;        // [N, n] 16-byte records in sorted order: payload | head, log-cumsum (s, c), value
     void* inv;        // [N, n] uint16 sorted position of every entry (entry order)
-    void* walk;       // [N, n] uint8 1 where an entry starts its token's run with earlier K entries
+    void* walk;       // [N, n] uint8, where an entry starts its token's run with earlier K entries:
+                      // 1 in an ordinary group, 2 in a hot one
+    void* hot;        // [N, hot_cap + 1] uint2: count, then {head position, size} of each hot group
+    int lds_max;      // LDS bytes per block of the device
 };
 
-// Workspace layout of sdm_phase1: byte offsets of the three regions and the total.
+// Workspace layout of sdm_phase1: byte offsets of the regions and the total.
 struct P1Workspace {
-    size_t rec_off, inv_off, walk_off, total;
+    size_t rec_off, inv_off, walk_off, hot_off, total;
+    int hot_cap;      // hot groups a chunk can hold: C * W / kHotMin
 };
 P1Workspace p1_workspace_layout(const sdm_p1_shape* s);
 
 // Dynamic LDS bytes of the Phase-1 sort/scan kernel for this shape and output set.
 size_t p1_lds_bytes(const sdm_p1_shape* s, const sdm_p1_io* io);
+
+// LDS bytes the pair kernel needs without hot-group tables (the triangle and the hot list).
+size_t p1_pair_lds_min(const sdm_p1_shape* s);
 
 // Enqueue the Phase-1 kernels; returns hipSuccess or the first launch error.
 hipError_t p1_launch(const P1Launch& L, hipStream_t st);
