@@ -3,11 +3,12 @@
 
 One step = the whole hot path over one batch: Phase 1 of every chunk of the workload (sort, scans,
 records, tile bounds, A / QK) followed by every DW step of the workload, all enqueued on one stream
-with the inputs already in HBM, launched eagerly (--graph: replayed from a HIP graph). `value` is the step's throughput in Phase-1 K+Q entries per second. Kernel
+with the inputs already in HBM, launched eagerly (--graph: replayed from a HIP graph;
+--pair-stream: the pair kernel on a second stream beside the DW steps). `value` is the step's throughput in Phase-1 K+Q entries per second. Kernel
 durations for the roofline come from a second, eager pass of the same steps with HIP events
 bound to each kernel's own start and end.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I] [--no-cpu-baseline] [--graph]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I] [--no-cpu-baseline] [--graph] [--pair-stream]
     python bench.py --copy-calibration MIB   # a plain device copy, for scaling HBM byte counters
 
 The default workload is the uniform bf16 shape (index 1); the others are parity cases that can
@@ -139,6 +140,8 @@ def main():
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step from a HIP graph in the timed region")
+    ap.add_argument("--pair-stream", action="store_true",
+                    help="run the pair kernel on a second stream beside the DW steps (slower on uniform_bf16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB device buffer 3 times (a known-traffic kernel for HBM counter scaling)")
     args = ap.parse_args()
@@ -182,11 +185,20 @@ def main():
     P, C = sh.P, sh.C
     plan = sdm.DwPlan(bank, dv, out["krec"], shape, dv_step_rows=P * C, workspace=dw_ws)
     n_ev = 4 + 2 * wl.steps   # start / end of the sort-scan kernel, the pair kernel, every DW launch
+    # Optionally the pair kernel (it reads only what the sort/scan kernel wrote; the DW steps never
+    # read its output) on a second stream beside the DW steps; the step then ends with a join.
+    pair_stream = torch.cuda.Stream(device=dev) if args.pair_stream else None
+    pair_ready, joined = torch.cuda.Event(), torch.cuda.Event()
+    pair_ready.record(stream)
 
     def step(ev=None):
-        sdm.phase1(shape, out=out, workspace=ws, events=None if ev is None else ev[0:4], **ins)
+        sdm.phase1(shape, out=out, workspace=ws, events=None if ev is None else ev[0:4], pair_stream=pair_stream,
+                   pair_ready=pair_ready if pair_stream is not None else None, **ins)
         for ti in range(wl.steps):
             plan.step(ti, events=None if ev is None else ev[4 + 2 * ti:6 + 2 * ti])
+        if pair_stream is not None:
+            joined.record(pair_stream)
+            stream.wait_event(joined)
 
     for _ in range(args.warmup):
         step()
@@ -265,7 +277,8 @@ def main():
             "workload": "%s: P=%d T=%d C=%d W=%d R=%d S=%d hd=%d bank %s dv %s slots %s" % (
                 sh.name, sh.P, sh.T, sh.C, sh.W, sh.R, sh.S, sh.hd, sh.bank_dtype, sh.dv_dtype, sh.slots),
             "chunks": wl.N, "dw_steps": wl.steps, "global_batch": wl.N * sh.C, "seq_len": sh.T,
-            "parallelism": "single GPU", "launch": "hipGraph replay" if args.graph else "eager",
+            "parallelism": "single GPU", "launch": ("hipGraph replay" if args.graph else "eager") +
+            ("; pair kernel on a second stream beside the DW steps" if args.pair_stream else ""),
         },
         "phase1_entries_per_s": entries / ((ms_main + ms_pairs) * 1e-3),
         "phase1_hbm_frac": (main_bytes + pairs_bytes) / ((ms_main + ms_pairs) * 1e-3) / HBM_PEAK_BYTES,

@@ -114,6 +114,12 @@ typedef struct sdm_p1_io {
                                own start and end (hipExtLaunchKernel): [0], [1] the sort/scan kernel,
                                [2], [3] the pair kernel (an event of a kernel that is not launched,
                                such as the pair kernel when a and qk are both NULL, is not recorded) */
+    hipStream_t pair_stream; /* optional (NULL: st): stream for the pair kernel, which then waits for
+                               the sort/scan kernel through pair_ready and may run beside work the
+                               caller enqueues on st next (the DW steps read nothing it writes). The
+                               caller must make st wait for pair_stream before reusing the workspace
+                               or reading a / qk. Default priority, same device. */
+    hipEvent_t pair_ready;  /* caller-created event, required with pair_stream (recorded on st) */
 } sdm_p1_io;
 
 /*

@@ -54,12 +54,16 @@ def alloc_phase1_outputs(shape: P1Shape, device="cuda", fields=None):
     return {k: torch.empty(s, dtype=dt, device=device) for k, (s, dt) in spec.items() if k in want}
 
 
-def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=None, stream=None, events=None):
+def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=None, stream=None, events=None,
+           pair_stream=None, pair_ready=None):
     """Enqueue Phase 1 of shape.N chunks on the current (or given) stream; returns the outputs.
 
     Inputs are contiguous device tensors: k_idx [N,C,W] int32, q_idx [N,C,R] int32, k_val / q_val
     float32 of the same shapes, g [N,C] float32. `out` is a dict from alloc_phase1_outputs (a
-    missing key skips that optional output)."""
+    missing key skips that optional output). events: optional 4 torch.cuda.Events (timing_events)
+    bound to the two kernels. pair_stream / pair_ready: optional torch stream and recorded event:
+    the pair kernel then runs on pair_stream after the sort/scan kernel; the caller makes the main
+    stream wait for pair_stream before reusing the workspace or reading a / qk."""
     import torch
 
     lib = _lib.load()
@@ -77,6 +81,10 @@ def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=No
     io.workspace_bytes = workspace.numel() * workspace.element_size()
     arr = _event_array(events, 4, "phase1")
     io.events = None if arr is None else ctypes.cast(arr, ctypes.c_void_p).value
+    if pair_stream is not None:
+        ready = _event_array([pair_ready] if pair_ready is not None else [], 1, "phase1 pair_ready")
+        io.pair_stream = pair_stream.cuda_stream
+        io.pair_ready = ready[0]
     st = torch.cuda.current_stream(k_idx.device) if stream is None else stream
     _lib.check(lib.sdm_phase1(ctypes.byref(shape), ctypes.byref(io), ctypes.c_void_p(st.cuda_stream)))
     return out

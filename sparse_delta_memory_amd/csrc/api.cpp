@@ -118,6 +118,8 @@ sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st
     if ((io->a != nullptr || io->qk != nullptr) && tri > static_cast<size_t>(lds_max))
         return fail(SDM_EUNSUPPORTED, "sdm_phase1: the C=%d pair kernel (%zu B) exceeds the %d B of LDS per block", s->C,
                     tri, lds_max);
+    if (io->pair_stream != nullptr && io->pair_ready == nullptr)
+        return fail(SDM_EINVAL, "sdm_phase1: pair_stream needs a pair_ready event");
     sdm::P1Launch L;
     L.s = s;
     L.io = io;

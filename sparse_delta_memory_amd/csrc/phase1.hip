@@ -1263,6 +1263,13 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     pa.R = s->R;
     pa.first_partial = s->first_partial;
     pa.valid_last = s->valid_last;
+    // The pair kernel on its own stream, after the sort/scan kernel, when the caller gives one.
+    hipStream_t pst = st;
+    if (io->pair_stream != nullptr) {
+        if ((e = hipEventRecord(io->pair_ready, st)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(io->pair_stream, io->pair_ready, 0)) != hipSuccess) return e;
+        pst = io->pair_stream;
+    }
     const size_t lds = pair_lds_layout(s->C, hot_cap, pa.tab_cap).total;
     const int threads = blocks_cu == 1 ? 1024 : 512;
     const void* fn = threads == 1024 ? reinterpret_cast<const void*>(&p1_pairs_kernel<1024>)
@@ -1270,7 +1277,7 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     void* kargs[] = {&pa};
-    return hipExtLaunchKernel(fn, dim3(s->N, 2), dim3(threads), kargs, lds, st, ev[2], ev[3], 0);
+    return hipExtLaunchKernel(fn, dim3(s->N, 2), dim3(threads), kargs, lds, pst, ev[2], ev[3], 0);
 }
 
 }  // namespace sdm
