@@ -225,10 +225,23 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
     float tot[CPL];
 #pragma unroll
     for (int q = 0; q < CPL; ++q) tot[q] = 0.0f;
-    for (int sgi = 0; sgi < nseg; ++sgi) {
-        const float* pp = a.part + (prow + first_pos + sgi * kSeg) * a.hd + col0;
+    // The partials kPartBatch at a time (all loads in flight), added in segment order.
+    constexpr int kPartBatch = CPL == 8 ? 4 : 2;
+    for (int sg0 = 0; sg0 < nseg; sg0 += kPartBatch) {
+        float pv[kPartBatch][CPL];
 #pragma unroll
-        for (int q = 0; q < CPL; ++q) tot[q] = tot[q] + __builtin_nontemporal_load(pp + q);
+        for (int b = 0; b < kPartBatch; ++b) {
+            const float* pp = a.part + (prow + first_pos + min(sg0 + b, nseg - 1) * kSeg) * a.hd + col0;
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) pv[b][q] = __builtin_nontemporal_load(pp + q);
+        }
+#pragma unroll
+        for (int b = 0; b < kPartBatch; ++b) {
+            if (sg0 + b < nseg) {
+#pragma unroll
+                for (int q = 0; q < CPL; ++q) tot[q] = tot[q] + pv[b][q];
+            }
+        }
     }
     const uint4 rf = kr[first_pos];
     const uint4 rl = kr[meta.y];
