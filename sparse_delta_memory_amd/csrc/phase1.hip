@@ -718,8 +718,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
 //
 // Hot groups (many K entries; listed by the sort/scan kernel) are summed densely: their runs are
 // gathered into LDS tables (K runs, and the runs of the block's kind as rows, each with the number
-// of K runs before it), then the threads that own row i sweep, group after group, the K runs
-// before each of row i's runs. The other groups are walked
+// of K runs before it; L kept in base 2 as a compensated pair), then the threads that own row i
+// sweep, group after group, the K runs before each of row i's runs, each term one hardware exp2. The other groups are walked
 // by thread i from each flagged run back to the group's head. Terms reach a cell in an order fixed
 // by the input (hot groups in position order, then the walks).
 struct PairArgs {
@@ -733,6 +733,7 @@ struct PairArgs {
 };
 
 // Threads per pair block: 512, or 1024 where the LDS allows one block per compute unit anyway.
+constexpr float kLog2E = 1.44269504088896340736f;
 constexpr size_t kPairStaticLds = 256;   // room left for the kernel's static LDS (scan partials)
 constexpr int kWalkBatch = 8;
 
@@ -750,7 +751,7 @@ __host__ __device__ inline PairLds pair_lds_layout(int C, int hot_cap, int tab_c
     l.tri = 0;
     l.hot = up(static_cast<size_t>(C) * (C + 1) / 2 * sizeof(float));
     l.gbase = l.hot + up(static_cast<size_t>(hot_cap) * 2 * sizeof(uint32_t) + 16);   // + batch bounds
-    l.tmask = l.gbase + up(static_cast<size_t>(hot_cap + 1) * 3 * sizeof(uint32_t));
+    l.tmask = l.gbase + up(static_cast<size_t>(kPairBatchGroups + 1) * 3 * sizeof(uint32_t));
     l.pres = l.tmask + up(static_cast<size_t>(C) * sizeof(uint32_t));
     l.ktab = l.pres + static_cast<size_t>(kPairBatchGroups) * 8 * sizeof(uint32_t);
     l.rtab = l.ktab + static_cast<size_t>(tab_cap) * 16;
@@ -775,8 +776,8 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
     uint2* hl = reinterpret_cast<uint2*>(smem + lay.hot);               // hot list of the chunk
     int* bounds = reinterpret_cast<int*>(smem + lay.hot) + 2 * a.hot_cap;   // batch end, positions
     uint32_t* ubase = reinterpret_cast<uint32_t*>(smem + lay.gbase);    // batch-local first position
-    uint32_t* gk = ubase + (a.hot_cap + 1);                              // first K-run index per group
-    uint32_t* gr = gk + (a.hot_cap + 1);                                 // first row-run index per group
+    uint32_t* gk = ubase + (kPairBatchGroups + 1);                       // first K-run index per group
+    uint32_t* gr = gk + (kPairBatchGroups + 1);                          // first row-run index per group
     uint32_t* tmask = reinterpret_cast<uint32_t*>(smem + lay.tmask);     // batch groups with a row run of token t
     uint32_t* pres = reinterpret_cast<uint32_t*>(smem + lay.pres);       // per group: tokens with a row run
     uint4* ktab = reinterpret_cast<uint4*>(smem + lay.ktab);
@@ -937,12 +938,18 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
                     if (cont) continue;
                     const bool is_k = !(r[b].x & kIsQ), is_row = (r[b].x & kIsQ) == row_q;
                     const uint32_t tok = (r[b].x >> kTokShift) & 0xFFu;
+                    // L in base 2 as a compensated pair: hi = s log2(e), lo = the product's rounding error
+                    // plus c log2(e). Differences of such pairs keep the exponent as accurate as (s, c).
+                    const float ls = __uint_as_float(r[b].y), lc = __uint_as_float(r[b].z);
+                    const float l2hi = ls * kLog2E;
+                    const float l2lo = fmaf(ls, kLog2E, -l2hi) + lc * kLog2E;
                     if (is_row) {
-                        rtab[rx] = make_uint4(tok | (kx << 8), __float_as_uint(suf[b]), r[b].y, r[b].z);
+                        rtab[rx] = make_uint4(tok | (kx << 8), __float_as_uint(suf[b]), __float_as_uint(l2hi),
+                                              __float_as_uint(l2lo));
                         atomicOr(tmask + tok, 1u << grp[b]);
                         atomicOr(pres + grp[b] * 8 + (tok >> 5), 1u << (tok & 31u));
                     }
-                    if (is_k) ktab[kx] = make_uint4(tok, __float_as_uint(suf[b]), r[b].y, r[b].z);
+                    if (is_k) ktab[kx] = make_uint4(tok, __float_as_uint(suf[b]), __float_as_uint(l2hi), __float_as_uint(l2lo));
                     kx += is_k ? 1u : 0u;
                     rx += is_row ? 1u : 0u;
                 }
@@ -975,7 +982,7 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
                 const uint32_t kb = gk[gg];
                 const uint4 me = rtab[gr[gg] + below];
                 const int ncol = static_cast<int>((me.x >> 8) - kb);
-                const float wi = __uint_as_float(me.y), si = __uint_as_float(me.z), ci = __uint_as_float(me.w);
+                const float wi = __uint_as_float(me.y), hi_i = __uint_as_float(me.z), lo_i = __uint_as_float(me.w);
                 for (int c0 = sub; c0 < ncol; c0 += kRowThreads * kColBlock) {
                     uint4 kt[kColBlock];
 #pragma unroll
@@ -983,8 +990,10 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
                     float term[kColBlock], cell[kColBlock];
 #pragma unroll
                     for (int b = 0; b < kColBlock; ++b) {
+                        // exp(L_i - L_j) = 2^((hi_i - hi_j) + (lo_i - lo_j)); the exponent is <= 0 for
+                        // log-sigmoid gates, and underflow to 0 only drops terms below 2^-126.
                         term[b] = (wi * __uint_as_float(kt[b].y)) *
-                                  expf((si - __uint_as_float(kt[b].z)) + (ci - __uint_as_float(kt[b].w)));
+                                  __builtin_amdgcn_exp2f((hi_i - __uint_as_float(kt[b].z)) + (lo_i - __uint_as_float(kt[b].w)));
                         cell[b] = row[kt[b].x];
                     }
 #pragma unroll

@@ -14,7 +14,7 @@ constexpr int kP1MaxRow = 16384;
 constexpr int kP1Threads = 1024;
 
 // Valid K entries that make a slot group "hot": the pair kernel sums such groups densely.
-constexpr int kHotMin = 32;
+constexpr int kHotMin = 16;
 
 struct P1Launch {
     const sdm_p1_shape* s;

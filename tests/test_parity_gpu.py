@@ -152,6 +152,10 @@ def test_masked_tokens_do_not_leak():
     dict(C=100, W=7, R=9, S=3000, P=3, steps=2, vl=50),   # 1600 entries: two radix tiles
     # An odd K row (8415 positions) in a DW launch wide enough for two positions per team of lanes.
     dict(C=255, W=33, R=2, S=5000, P=1, steps=1, vl=None, hd=960, bank="bf16"),
+    # Every slot group hot (about 43 K entries each): more hot groups than one pair-kernel batch holds.
+    dict(C=256, W=8, R=8, S=48, P=1, steps=1, vl=None),
+    # Hot groups in 512-thread pair blocks (C = 120), a ragged last chunk.
+    dict(C=120, W=16, R=4, S=70, P=2, steps=1, vl=100),
 ])
 def test_edge_shapes(case):
     sh = W.Shape("edge", P=case["P"], T=case["C"] * case["steps"], C=case["C"], W=case["W"], R=case["R"],
