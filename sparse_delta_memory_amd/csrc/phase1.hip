@@ -334,19 +334,44 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     // ---- 1. keys (element i of the striped layout is entry r = i) and the sort.
     {
         uint32_t key[IPT], val[IPT];
+        if constexpr (IPT <= 8) {
+            int32_t ids[IPT];
+            // Every item loads (padding items re-read entry 0) before any id is used: the asm
+            // below keeps the compiler from sinking a load into the select that uses it, where
+            // each load would get a wait of its own. (With 16 items per thread the registers are
+            // better spent otherwise: measured slower there.)
 #pragma unroll
-        for (int k = 0; k < IPT; ++k) {
-            const int i = w * kWave * IPT + k * kWave + lane;
-            val[k] = static_cast<uint32_t>(i);
-            // Branch-free address: every item loads (padding items re-read entry 0), so all the
-            // loads of a thread are in flight together.
-            const int ic = i < n ? i : 0;
-            const int t = token_of_entry(ic, a.wr_magic);
-            const int j = ic - t * wr;
-            const int32_t* src = j < W ? a.k_idx + cw + t * W + j : a.q_idx + cr + t * R + (j - W);
-            const int64_t id = static_cast<int64_t>(*src);
-            const uint32_t kv = t < tv ? static_cast<uint32_t>(id - id_base) & (key_lim - 1u) : key_lim;
-            key[k] = i < n ? kv : pad_key;
+            for (int k = 0; k < IPT; ++k) {
+                const int i = w * kWave * IPT + k * kWave + lane;
+                val[k] = static_cast<uint32_t>(i);
+                const int ic = i < n ? i : 0;
+                const int t = token_of_entry(ic, a.wr_magic);
+                const int j = ic - t * wr;
+                ids[k] = *(j < W ? a.k_idx + cw + t * W + j : a.q_idx + cr + t * R + (j - W));
+            }
+#pragma unroll
+            for (int k = 0; k < IPT; ++k) asm volatile("" ::"v"(ids[k]));
+#pragma unroll
+            for (int k = 0; k < IPT; ++k) {
+                const int i = w * kWave * IPT + k * kWave + lane;
+                const int t = token_of_entry(i < n ? i : 0, a.wr_magic);
+                const uint32_t kv =
+                    t < tv ? static_cast<uint32_t>(static_cast<int64_t>(ids[k]) - id_base) & (key_lim - 1u) : key_lim;
+                key[k] = i < n ? kv : pad_key;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < IPT; ++k) {
+                const int i = w * kWave * IPT + k * kWave + lane;
+                val[k] = static_cast<uint32_t>(i);
+                const int ic = i < n ? i : 0;
+                const int t = token_of_entry(ic, a.wr_magic);
+                const int j = ic - t * wr;
+                const int32_t* src = j < W ? a.k_idx + cw + t * W + j : a.q_idx + cr + t * R + (j - W);
+                const int64_t id = static_cast<int64_t>(*src);
+                const uint32_t kv = t < tv ? static_cast<uint32_t>(id - id_base) & (key_lim - 1u) : key_lim;
+                key[k] = i < n ? kv : pad_key;
+            }
         }
         // Invalid entries need one more key bit only in a ragged chunk.
         block_radix_sort<IPT>(key, val, tv < C ? kb + 1 : kb, a.digit_bits, skey, sval, hist, wsum);
@@ -573,128 +598,248 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
         return e.valid ? expf(gs + (e.c + ge)) : 1.0f;
     };
 
-    // ---- 4a. entry-order rounds.
-    for (int rd = 0; rd < a.rounds.count; ++rd) {
-        const uint32_t mask = a.rounds.mask[rd];
-        auto stage_at = [&](int f, int idx) { return stage + a.rounds.offset[f] + idx * field_bytes(f); };
+    // ---- 4. Outputs: one pass per round over the thread's tile entries. Entry-order fields are
+    // staged in LDS by entry index and copied out with 16-byte stores. Sorted-order outputs (pair
+    // records, kind rows, mover records, tile bounds, the hot-group list) are written straight
+    // from registers in the first pass: a thread owns consecutive sorted positions and its K (Q)
+    // entries have consecutive kind indices, so these stores stay close to contiguous. With 16
+    // items per thread that pass would not fit the registers; there the sorted-order outputs get
+    // a pass of their own, staged tile by tile (4b).
+    constexpr bool kMerged = IPT <= 8;
+    // Tile bounds of the K-only row (values computed where they are used, to keep scalar
+    // registers free through the rounds).
+    auto tile_bounds = [&](int& nk, int& L, int64_t& tb) {
+        nk = C * W;
+        L = a.tile_len;
+        const int ntk = (nk + L - 1) / L;
+        tb = static_cast<int64_t>(c) * (ntk + 1);
+        if (threadIdx.x == 0) a.tiles_k[tb + ntk] = nk;
+    };
+    if constexpr (kMerged) {
+        int nk, L;
+        int64_t tb;
+        tile_bounds(nk, L, tb);
+        const int npass = a.rounds.count > 0 ? a.rounds.count : 1;
+        for (int rd = 0; rd < npass; ++rd) {
+            const uint32_t mask = a.rounds.count > 0 ? a.rounds.mask[rd] : 0u;
+            const bool sorted_pass = rd == 0;   // block-uniform
+            auto stage_at = [&](int f, int idx) { return stage + a.rounds.offset[f] + idx * field_bytes(f); };
+    #pragma unroll
+            for (int T = 0; T < NTILE; ++T) {
+                if (T >= ntiles) continue;
+                // The ids of this thread's K entries in the tile (for the mover-record slots), all loads
+                // in flight before the first use.
+                int32_t kid[kTileItems];
+                if (sorted_pass) {
+                    const int p0 = T * kTile + static_cast<int>(threadIdx.x) * kTileItems;
+    #pragma unroll
+                    for (int k = 0; k < kTileItems; ++k) {
+                        const int p = p0 + k;
+                        const int r = p < n ? static_cast<int>(sval[p] & kRMask) : 0;
+                        const int t = token_of_entry(r, a.wr_magic);
+                        const int j = r - t * wr;
+                        kid[k] = a.k_idx[cw + ((j < W && t < tv) ? t * W + j : 0)];
+                    }
+    #pragma unroll
+                    for (int k = 0; k < kTileItems; ++k) asm volatile("" ::"v"(kid[k]));
+                }
+                for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
+                    if (!e.live) return;
+                    const float Lv = e.s + e.c;
+                    if (mask != 0u) {
+                        const uint32_t packed =
+                            e.valid ? (static_cast<uint32_t>(p) | min(e.acnt, kPosCountMax) << kPosAfterShift |
+                                       min(e.bcnt + 1u + e.acnt, kPosCountMax) << kPosSizeShift)
+                                    : static_cast<uint32_t>(p);
+                        if (e.q) {
+                            const int o = e.t * R + e.ln;
+                            if (mask & (1u << kFLogQ)) *reinterpret_cast<float*>(stage_at(kFLogQ, o)) = Lv;
+                            if (mask & (1u << kFQW)) *reinterpret_cast<float*>(stage_at(kFQW, o)) = e.v * expf(Lv);
+                            if (mask & (1u << kFPosQ)) *reinterpret_cast<uint32_t*>(stage_at(kFPosQ, o)) = packed;
+                            const bool ql = e.valid && e.acnt == 0;
+                            if (mask & (1u << kFQLast)) *stage_at(kFQLast, o) = ql ? 1 : 0;
+                            if (mask & (1u << kFQOnly)) *stage_at(kFQOnly, o) = (ql && e.bcnt == 0) ? 1 : 0;
+                        } else {
+                            const int o = e.t * W + e.ln;
+                            const bool last = e.valid && e.acnt == 0;
+                            if (mask & (1u << kFLogK)) *reinterpret_cast<float*>(stage_at(kFLogK, o)) = Lv;
+                            if (mask & (1u << kFRex)) *reinterpret_cast<float*>(stage_at(kFRex, o)) = e.rex;
+                            if (mask & (1u << kFCpe)) *reinterpret_cast<float*>(stage_at(kFCpe, o)) = group_exp(e);
+                            if (mask & (1u << kFKEff)) *reinterpret_cast<float*>(stage_at(kFKEff, o)) = e.v * expf(Lv);
+                            if (mask & (1u << kFIsLast)) *stage_at(kFIsLast, o) = last ? 1 : 0;
+                            if (mask & (1u << kFIsOnly)) *stage_at(kFIsOnly, o) = (last && e.bcnt == 0) ? 1 : 0;
+                            if (mask & (1u << kFPosK)) *reinterpret_cast<uint32_t*>(stage_at(kFPosK, o)) = packed;
+                        }
+                        if (mask & (1u << kFInv)) *reinterpret_cast<uint16_t*>(stage_at(kFInv, e.r)) = static_cast<uint16_t>(p);
+                        if (mask & (1u << kFWalk)) {   // 1: walked by the pair kernel, 2: summed by its hot-group pass
+                            *stage_at(kFWalk, e.r) = e.walk ? (e.kg >= static_cast<uint32_t>(a.hot_min) ? 2 : 1) : 0;
+                        }
+                    }
+                    if (!sorted_pass) return;
+                    // Hot groups (the pair kernel sums them densely): appended in any order, sorted below.
+                    if (a.hot != nullptr && e.valid && e.head && e.kg >= static_cast<uint32_t>(a.hot_min)) {
+                        hot_buf[atomicAdd(&hot_n, 1u)] = make_uint2(static_cast<uint32_t>(p), e.gsize);
+                    }
+                    if (a.rec != nullptr) {   // pair records {payload | head, log-cumsum s, c, value}
+                        a.rec[crow + p] = make_uint4(e.pay | (e.head ? kHead : 0u), __float_as_uint(e.s),
+                                                     __float_as_uint(e.c), __float_as_uint(e.v));
+                    }
+                    const uint32_t elem = e.valid ? (e.pay | min(e.bcnt, kDistMax) << kDistShift |
+                                                     (e.bcnt == 0 ? kFirst : 0u) | (e.acnt == 0 ? kLast : 0u))
+                                                  : (e.pay | kFirst | kLast);
+                    if (e.q) {
+                        if (a.spay_q != nullptr) a.spay_q[cr + e.jkind] = static_cast<int32_t>(elem);
+                    } else {
+                        a.spay_k[cw + e.jkind] = static_cast<int32_t>(elem);
+                        const float sc = e.valid ? e.v * expf(e.rex) : 0.0f;
+                        const int64_t id = static_cast<int64_t>(kid[k]);
+                        const uint32_t slot =
+                            e.valid ? static_cast<uint32_t>((static_cast<uint32_t>(id - id_base) & (key_lim - 1u)) + id_base)
+                                    : 0u;
+                        a.krec[cw + e.jkind] = make_int4(static_cast<int32_t>(elem), static_cast<int32_t>(slot),
+                                                         __float_as_int(sc), __float_as_int(group_exp(e)));
+                        if (static_cast<int>(e.jkind) % L == 0) {
+                            a.tiles_k[tb + static_cast<int>(e.jkind) / L] =
+                                (elem & kFirst) ? static_cast<int>(e.jkind) : min(static_cast<int>(e.jkind + e.acnt + 1u), nk);
+                        }
+                    }
+                });
+            }
+            if (mask != 0u) {   // block-uniform
+                lds_barrier();
+                for (int f = 0; f < kNumFields; ++f) {
+                    if (!(mask & (1u << f))) continue;
+                    const int cnt = field_is_all(f) ? n : field_is_q(f) ? C * R : C * W;
+                    const int64_t base = field_is_all(f) ? crow : field_is_q(f) ? cr : cw;
+                    unsigned char* dst = static_cast<unsigned char*>(a.field[f]) + base * field_bytes(f);
+                    block_copy_out(dst, stage + a.rounds.offset[f], cnt, field_bytes(f));
+                }
+                lds_barrier();
+            }
+        }
+    } else {
+        // Entry-order rounds only (4a).
+        for (int rd = 0; rd < a.rounds.count; ++rd) {
+            const uint32_t mask = a.rounds.mask[rd];
+            auto stage_at = [&](int f, int idx) { return stage + a.rounds.offset[f] + idx * field_bytes(f); };
+    #pragma unroll
+            for (int T = 0; T < NTILE; ++T) {
+                if (T >= ntiles) continue;
+                for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
+                    if (!e.live) return;
+                    const float Lv = e.s + e.c;
+                    const uint32_t packed =
+                        e.valid ? (static_cast<uint32_t>(p) | min(e.acnt, kPosCountMax) << kPosAfterShift |
+                                   min(e.bcnt + 1u + e.acnt, kPosCountMax) << kPosSizeShift)
+                                : static_cast<uint32_t>(p);
+                    if (e.q) {
+                        const int o = e.t * R + e.ln;
+                        if (mask & (1u << kFLogQ)) *reinterpret_cast<float*>(stage_at(kFLogQ, o)) = Lv;
+                        if (mask & (1u << kFQW)) *reinterpret_cast<float*>(stage_at(kFQW, o)) = e.v * expf(Lv);
+                        if (mask & (1u << kFPosQ)) *reinterpret_cast<uint32_t*>(stage_at(kFPosQ, o)) = packed;
+                        const bool ql = e.valid && e.acnt == 0;
+                        if (mask & (1u << kFQLast)) *stage_at(kFQLast, o) = ql ? 1 : 0;
+                        if (mask & (1u << kFQOnly)) *stage_at(kFQOnly, o) = (ql && e.bcnt == 0) ? 1 : 0;
+                    } else {
+                        const int o = e.t * W + e.ln;
+                        const bool last = e.valid && e.acnt == 0;
+                        if (mask & (1u << kFLogK)) *reinterpret_cast<float*>(stage_at(kFLogK, o)) = Lv;
+                        if (mask & (1u << kFRex)) *reinterpret_cast<float*>(stage_at(kFRex, o)) = e.rex;
+                        if (mask & (1u << kFCpe)) *reinterpret_cast<float*>(stage_at(kFCpe, o)) = group_exp(e);
+                        if (mask & (1u << kFKEff)) *reinterpret_cast<float*>(stage_at(kFKEff, o)) = e.v * expf(Lv);
+                        if (mask & (1u << kFIsLast)) *stage_at(kFIsLast, o) = last ? 1 : 0;
+                        if (mask & (1u << kFIsOnly)) *stage_at(kFIsOnly, o) = (last && e.bcnt == 0) ? 1 : 0;
+                        if (mask & (1u << kFPosK)) *reinterpret_cast<uint32_t*>(stage_at(kFPosK, o)) = packed;
+                    }
+                    if (mask & (1u << kFInv)) *reinterpret_cast<uint16_t*>(stage_at(kFInv, e.r)) = static_cast<uint16_t>(p);
+                    if (mask & (1u << kFWalk)) {   // 1: walked by the pair kernel, 2: summed by its hot-group pass
+                        *stage_at(kFWalk, e.r) = e.walk ? (e.kg >= static_cast<uint32_t>(a.hot_min) ? 2 : 1) : 0;
+                    }
+                });
+            }
+            lds_barrier();
+            for (int f = 0; f < kNumFields; ++f) {
+                if (!(mask & (1u << f))) continue;
+                const int cnt = field_is_all(f) ? n : field_is_q(f) ? C * R : C * W;
+                const int64_t base = field_is_all(f) ? crow : field_is_q(f) ? cr : cw;
+                unsigned char* dst = static_cast<unsigned char*>(a.field[f]) + base * field_bytes(f);
+                block_copy_out(dst, stage + a.rounds.offset[f], cnt, field_bytes(f));
+            }
+            lds_barrier();
+        }
+    }
+    if constexpr (!kMerged) {
+        // ---- 4b. sorted-order outputs, staged per tile: pair records, then kind rows and krec.
+        int nk, L;
+        int64_t tb;
+        tile_bounds(nk, L, tb);
 #pragma unroll
         for (int T = 0; T < NTILE; ++T) {
             if (T >= ntiles) continue;
+            const int pbase = T * kTile;
+            const int pcount = min(kTile, n - pbase);
+            // Kind rows and mover records: the tile's K (Q) entries have consecutive kind indices.
+            const uint32_t k0 = tile_kind[T] & 0xFFFFu, q0 = tile_kind[T] >> 16;
+            const int nk_t = static_cast<int>((tile_kind[T + 1] & 0xFFFFu) - k0);
+            const int nq_t = static_cast<int>((tile_kind[T + 1] >> 16) - q0);
+            const int rec_bytes = a.rec != nullptr ? pcount * 16 : 0;
+            const int kind_bytes = nk_t * 16 + (nk_t * 4 + 15) / 16 * 16 + nq_t * 4;
+            // One pass when the pair records, krec and both kind rows of the tile fit together.
+            const bool joint = rec_bytes + kind_bytes <= a.stage_bytes;   // block-uniform
+            if (rec_bytes > 0 && !joint) {
+                for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
+                    if (!e.live) return;
+                    reinterpret_cast<uint4*>(stage)[p - pbase] = make_uint4(
+                        e.pay | (e.head ? kHead : 0u), __float_as_uint(e.s), __float_as_uint(e.c), __float_as_uint(e.v));
+                });
+                lds_barrier();
+                block_copy_out(a.rec + crow + pbase, stage, pcount, 16);
+                lds_barrier();
+            }
+            unsigned char* st_rec = stage;
+            unsigned char* st_krec = stage + (joint ? rec_bytes : 0);
+            unsigned char* st_spk = st_krec + nk_t * 16;
+            unsigned char* st_spq = st_spk + (nk_t * 4 + 15) / 16 * 16;
             for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
                 if (!e.live) return;
-                const float Lv = e.s + e.c;
-                const uint32_t packed =
-                    e.valid ? (static_cast<uint32_t>(p) | min(e.acnt, kPosCountMax) << kPosAfterShift |
-                               min(e.bcnt + 1u + e.acnt, kPosCountMax) << kPosSizeShift)
-                            : static_cast<uint32_t>(p);
+                if (a.hot != nullptr && e.valid && e.head && e.kg >= static_cast<uint32_t>(a.hot_min)) {
+                    hot_buf[atomicAdd(&hot_n, 1u)] = make_uint2(static_cast<uint32_t>(p), e.gsize);
+                }
+                if (joint && rec_bytes > 0) {
+                    reinterpret_cast<uint4*>(st_rec)[p - pbase] = make_uint4(
+                        e.pay | (e.head ? kHead : 0u), __float_as_uint(e.s), __float_as_uint(e.c), __float_as_uint(e.v));
+                }
+                const uint32_t elem = e.valid ? (e.pay | min(e.bcnt, kDistMax) << kDistShift |
+                                                 (e.bcnt == 0 ? kFirst : 0u) | (e.acnt == 0 ? kLast : 0u))
+                                              : (e.pay | kFirst | kLast);
                 if (e.q) {
-                    const int o = e.t * R + e.ln;
-                    if (mask & (1u << kFLogQ)) *reinterpret_cast<float*>(stage_at(kFLogQ, o)) = Lv;
-                    if (mask & (1u << kFQW)) *reinterpret_cast<float*>(stage_at(kFQW, o)) = e.v * expf(Lv);
-                    if (mask & (1u << kFPosQ)) *reinterpret_cast<uint32_t*>(stage_at(kFPosQ, o)) = packed;
-                    const bool ql = e.valid && e.acnt == 0;
-                    if (mask & (1u << kFQLast)) *stage_at(kFQLast, o) = ql ? 1 : 0;
-                    if (mask & (1u << kFQOnly)) *stage_at(kFQOnly, o) = (ql && e.bcnt == 0) ? 1 : 0;
+                    reinterpret_cast<uint32_t*>(st_spq)[e.jkind - q0] = elem;
                 } else {
-                    const int o = e.t * W + e.ln;
-                    const bool last = e.valid && e.acnt == 0;
-                    if (mask & (1u << kFLogK)) *reinterpret_cast<float*>(stage_at(kFLogK, o)) = Lv;
-                    if (mask & (1u << kFRex)) *reinterpret_cast<float*>(stage_at(kFRex, o)) = e.rex;
-                    if (mask & (1u << kFCpe)) *reinterpret_cast<float*>(stage_at(kFCpe, o)) = group_exp(e);
-                    if (mask & (1u << kFKEff)) *reinterpret_cast<float*>(stage_at(kFKEff, o)) = e.v * expf(Lv);
-                    if (mask & (1u << kFIsLast)) *stage_at(kFIsLast, o) = last ? 1 : 0;
-                    if (mask & (1u << kFIsOnly)) *stage_at(kFIsOnly, o) = (last && e.bcnt == 0) ? 1 : 0;
-                    if (mask & (1u << kFPosK)) *reinterpret_cast<uint32_t*>(stage_at(kFPosK, o)) = packed;
-                }
-                if (mask & (1u << kFInv)) *reinterpret_cast<uint16_t*>(stage_at(kFInv, e.r)) = static_cast<uint16_t>(p);
-                if (mask & (1u << kFWalk)) {   // 1: walked by the pair kernel, 2: summed by its hot-group pass
-                    *stage_at(kFWalk, e.r) = e.walk ? (e.kg >= static_cast<uint32_t>(a.hot_min) ? 2 : 1) : 0;
+                    reinterpret_cast<uint32_t*>(st_spk)[e.jkind - k0] = elem;
+                    const float sc = e.valid ? e.v * expf(e.rex) : 0.0f;
+                    // The slot: the entry's id read again (the chunk's ids are cache-resident by now).
+                    const int64_t id = static_cast<int64_t>(a.k_idx[cw + (e.valid ? e.t * W + e.ln : 0)]);
+                    const uint32_t slot =
+                        e.valid ? static_cast<uint32_t>((static_cast<uint32_t>(id - id_base) & (key_lim - 1u)) + id_base)
+                                : 0u;
+                    reinterpret_cast<int4*>(st_krec)[e.jkind - k0] =
+                        make_int4(static_cast<int32_t>(elem), static_cast<int32_t>(slot), __float_as_int(sc),
+                                  __float_as_int(group_exp(e)));
+                    if (static_cast<int>(e.jkind) % L == 0) {
+                        a.tiles_k[tb + static_cast<int>(e.jkind) / L] =
+                            (elem & kFirst) ? static_cast<int>(e.jkind) : min(static_cast<int>(e.jkind + e.acnt + 1u), nk);
+                    }
                 }
             });
-        }
-        lds_barrier();
-        for (int f = 0; f < kNumFields; ++f) {
-            if (!(mask & (1u << f))) continue;
-            const int cnt = field_is_all(f) ? n : field_is_q(f) ? C * R : C * W;
-            const int64_t base = field_is_all(f) ? crow : field_is_q(f) ? cr : cw;
-            unsigned char* dst = static_cast<unsigned char*>(a.field[f]) + base * field_bytes(f);
-            block_copy_out(dst, stage + a.rounds.offset[f], cnt, field_bytes(f));
-        }
-        lds_barrier();
-    }
-
-    // ---- 4b. sorted-order outputs, staged per tile: pair records, then kind rows and krec.
-    const int nk = C * W;
-    const int L = a.tile_len;
-    const int ntk = (nk + L - 1) / L;
-    const int64_t tb = static_cast<int64_t>(c) * (ntk + 1);
-    if (threadIdx.x == 0) a.tiles_k[tb + ntk] = nk;
-#pragma unroll
-    for (int T = 0; T < NTILE; ++T) {
-        if (T >= ntiles) continue;
-        const int pbase = T * kTile;
-        const int pcount = min(kTile, n - pbase);
-        // Kind rows and mover records: the tile's K (Q) entries have consecutive kind indices.
-        const uint32_t k0 = tile_kind[T] & 0xFFFFu, q0 = tile_kind[T] >> 16;
-        const int nk_t = static_cast<int>((tile_kind[T + 1] & 0xFFFFu) - k0);
-        const int nq_t = static_cast<int>((tile_kind[T + 1] >> 16) - q0);
-        const int rec_bytes = a.rec != nullptr ? pcount * 16 : 0;
-        const int kind_bytes = nk_t * 16 + (nk_t * 4 + 15) / 16 * 16 + nq_t * 4;
-        // One pass when the pair records, krec and both kind rows of the tile fit together.
-        const bool joint = rec_bytes + kind_bytes <= a.stage_bytes;   // block-uniform
-        if (rec_bytes > 0 && !joint) {
-            for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
-                if (!e.live) return;
-                reinterpret_cast<uint4*>(stage)[p - pbase] = make_uint4(
-                    e.pay | (e.head ? kHead : 0u), __float_as_uint(e.s), __float_as_uint(e.c), __float_as_uint(e.v));
-            });
             lds_barrier();
-            block_copy_out(a.rec + crow + pbase, stage, pcount, 16);
+            if (joint && rec_bytes > 0) block_copy_out(a.rec + crow + pbase, st_rec, pcount, 16);
+            block_copy_out(a.krec + cw + k0, st_krec, nk_t, 16);
+            block_copy_out(a.spay_k + cw + k0, st_spk, nk_t, 4);
+            if (a.spay_q != nullptr) block_copy_out(a.spay_q + cr + q0, st_spq, nq_t, 4);
             lds_barrier();
         }
-        unsigned char* st_rec = stage;
-        unsigned char* st_krec = stage + (joint ? rec_bytes : 0);
-        unsigned char* st_spk = st_krec + nk_t * 16;
-        unsigned char* st_spq = st_spk + (nk_t * 4 + 15) / 16 * 16;
-        for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
-            if (!e.live) return;
-            // Hot groups (the pair kernel sums them densely): appended in any order, sorted below.
-            if (a.hot != nullptr && e.valid && e.head && e.kg >= static_cast<uint32_t>(a.hot_min)) {
-                hot_buf[atomicAdd(&hot_n, 1u)] = make_uint2(static_cast<uint32_t>(p), e.gsize);
-            }
-            if (joint && rec_bytes > 0) {
-                // Pair records {payload | head, log-cumsum s, c, value}.
-                reinterpret_cast<uint4*>(st_rec)[p - pbase] = make_uint4(
-                    e.pay | (e.head ? kHead : 0u), __float_as_uint(e.s), __float_as_uint(e.c), __float_as_uint(e.v));
-            }
-            const uint32_t elem = e.valid ? (e.pay | min(e.bcnt, kDistMax) << kDistShift | (e.bcnt == 0 ? kFirst : 0u) |
-                                             (e.acnt == 0 ? kLast : 0u))
-                                          : (e.pay | kFirst | kLast);
-            if (e.q) {
-                reinterpret_cast<uint32_t*>(st_spq)[e.jkind - q0] = elem;
-            } else {
-                reinterpret_cast<uint32_t*>(st_spk)[e.jkind - k0] = elem;
-                const float sc = e.valid ? e.v * expf(e.rex) : 0.0f;
-                // The slot: the entry's id read again (the chunk's ids are cache-resident by now).
-                const int64_t id = static_cast<int64_t>(a.k_idx[cw + (e.valid ? e.t * W + e.ln : 0)]);
-                const uint32_t slot =
-                    e.valid ? static_cast<uint32_t>((static_cast<uint32_t>(id - id_base) & (key_lim - 1u)) + id_base) : 0u;
-                reinterpret_cast<int4*>(st_krec)[e.jkind - k0] =
-                    make_int4(static_cast<int32_t>(elem), static_cast<int32_t>(slot), __float_as_int(sc),
-                              __float_as_int(group_exp(e)));
-                if (static_cast<int>(e.jkind) % L == 0) {
-                    a.tiles_k[tb + static_cast<int>(e.jkind) / L] =
-                        (elem & kFirst) ? static_cast<int>(e.jkind) : min(static_cast<int>(e.jkind + e.acnt + 1u), nk);
-                }
-            }
-        });
-        lds_barrier();
-        if (joint && rec_bytes > 0) block_copy_out(a.rec + crow + pbase, st_rec, pcount, 16);
-        block_copy_out(a.krec + cw + k0, st_krec, nk_t, 16);
-        block_copy_out(a.spay_k + cw + k0, st_spk, nk_t, 4);
-        if (a.spay_q != nullptr) block_copy_out(a.spay_q + cr + q0, st_spq, nq_t, 4);
-        lds_barrier();
     }
+    __syncthreads();   // every hot-group append is done
     if (a.hot != nullptr) {
         // The hot list in position order: each entry's rank is the number of heads before it.
         const int nh = static_cast<int>(hot_n);   // every append happened before the last barrier
@@ -1126,14 +1271,14 @@ MainPlan plan_main(const sdm_p1_shape* s, const sdm_p1_io* io, bool with_pairs_w
     while (d > 4 && np * 4 + kNW * (1 << d) * 4 > cap_max) --d;
     m.digit_bits = d;
     const int sort_bytes = np * 4 + kNW * (1 << d) * 4;
-    // The per-tile sorted stages: 16-byte records of one tile; krec + both kind rows of one tile.
-    const int tile = n < kTile ? n : kTile;
-    const int sorted_bytes = tile * 20 + 32;
     const void* dst[kNumFields] = {io->log_k, io->rex, io->cpe, io->k_eff, io->is_last, io->is_only, io->pos_k,
                                    io->log_q, io->q_w, io->pos_q, io->q_last, io->q_only,
                                    with_pairs_ws ? io : nullptr, with_pairs_ws ? io : nullptr};
     int need = 0;
     for (int f = 0; f < kNumFields; ++f) need += (field_count(s, f) * field_bytes(f) + 15) / 16 * 16;
+    // With 16 items per thread the sorted-order outputs are staged per tile (16-byte records of one
+    // tile; krec and both kind rows of one tile).
+    const int sorted_bytes = m.ipt == 16 ? kTile * 20 + 32 : 0;
     int cap = max(max(sort_bytes, sorted_bytes), min(need, cap_max));
     cap = min(cap, cap_max) / 16 * 16;
     // Greedy packing of the requested fields, in order, into rounds of `cap` bytes.
