@@ -46,7 +46,12 @@ constexpr int kMaxRounds = 8;
 struct Rounds {
     int count;
     uint32_t mask[kMaxRounds];
+    uint32_t flat;            // rounds copied out by one loop over all their 16-byte vectors
     int offset[kNumFields];   // byte offset of a field inside the staging area of its round
+    int vtotal[kMaxRounds];   // 16-byte vectors staged in a round
+    // Per round, the first vector of each of its fields (offset / 16); a large value for the other
+    // fields, so the field of vector v is the last one whose start is <= v.
+    int vstart[kMaxRounds][kNumFields];
 };
 
 struct P1Args {
@@ -277,6 +282,50 @@ __device__ __forceinline__ void block_copy_out(void* dst, const unsigned char* s
     for (int i = done + threadIdx.x; i < bytes; i += kNT) static_cast<unsigned char*>(dst)[i] = src[i];
 }
 
+// Copies the round's staged fields out. A flat round (every field's rows 16-byte aligned and a
+// multiple of 16 bytes long, so its vectors are contiguous in the staging area) is one loop over
+// all its vectors, two per thread in flight: the field of a vector is found by comparisons with
+// the round's field starts, its destination from a per-field table (`dtab[f]`: the chunk's row of
+// field f, minus the field's staging start). Otherwise each field is copied on its own.
+__device__ __forceinline__ void copy_round(const P1Args& a, int rd, uint32_t mask, const unsigned char* stage,
+                                           const uint2* dtab, int64_t crow, int64_t cr, int64_t cw, int C) {
+    if ((a.rounds.flat >> rd) & 1u) {   // block-uniform
+        const int total = a.rounds.vtotal[rd];
+        int vs[kNumFields];
+#pragma unroll
+        for (int k = 0; k < kNumFields; ++k) vs[k] = a.rounds.vstart[rd][k];
+        // Destination of vector v: the table holds plain integers, so the store names the global
+        // address space itself (a generic pointer would make it a flat store).
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(1))) u32x4 global_u32x4;
+        auto dst_of = [&](int v) {
+            int f = 0;
+#pragma unroll
+            for (int k = 0; k < kNumFields; ++k) f = v >= vs[k] ? k : f;
+            const uint2 d = dtab[f];
+            return reinterpret_cast<global_u32x4*>(static_cast<uintptr_t>(d.x) | static_cast<uintptr_t>(d.y) << 32) + v;
+        };
+        const u32x4* src = reinterpret_cast<const u32x4*>(stage);
+        for (int v0 = static_cast<int>(threadIdx.x); v0 < total; v0 += 2 * kNT) {
+            const int v1 = min(v0 + kNT, total - 1);   // a second vector in flight (a repeat at the end)
+            const u32x4 x0 = src[v0];
+            const u32x4 x1 = src[v1];
+            global_u32x4* d0 = dst_of(v0);
+            global_u32x4* d1 = dst_of(v1);
+            *d0 = x0;
+            if (v0 + kNT < total) *d1 = x1;
+        }
+        return;
+    }
+    for (int f = 0; f < kNumFields; ++f) {
+        if (!(mask & (1u << f))) continue;
+        const int cnt = field_is_all(f) ? a.C * (a.W + a.R) : field_is_q(f) ? C * a.R : C * a.W;
+        const int64_t base = field_is_all(f) ? crow : field_is_q(f) ? cr : cw;
+        unsigned char* d = static_cast<unsigned char*>(a.field[f]) + base * field_bytes(f);
+        block_copy_out(d, stage + a.rounds.offset[f], cnt, field_bytes(f));
+    }
+}
+
 // Everything one sorted position yields, recomputed by its owner thread from its tile prefixes.
 struct Entry {
     bool live;       // position < n
@@ -284,6 +333,8 @@ struct Entry {
     bool q;          // read entry
     bool head;       // first of its group
     bool walk;       // starts its token's run of its kind and has earlier valid K entries in the group
+    bool keep;       // its pair record is read: its group spans two or more positions, or it is the
+                     // head right after such a group (the run sums of the walks stop there)
     int t, ln, r;
     uint32_t pay;    // entry bits of the payload
     float s, c;      // inclusive log-cumsum (compensated)
@@ -310,6 +361,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     __shared__ uint32_t wsum[kNW];
     __shared__ uint32_t tile_kind[NTILE + 1];   // kind counts (K | Q << 16) before each tile
     __shared__ uint32_t hot_n;                   // hot groups found so far
+    __shared__ uint2 dtab[kNumFields];           // flat copy-out: per-field destination bases
     uint2* hot_buf = reinterpret_cast<uint2*>(smem + a.stage_bytes + NP * 2 + 256 * sizeof(float));
 
     const int c = blockIdx.x;
@@ -330,6 +382,17 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
 
     for (int t = threadIdx.x; t < C; t += kNT) gates[t] = t < tv ? a.g[static_cast<int64_t>(c) * C + t] : 0.0f;
     if (threadIdx.x == 0) hot_n = 0u;
+#pragma unroll
+    for (int f = 0; f < kNumFields; ++f) {
+        if (threadIdx.x == f) {
+            // The chunk's row of field f, less the field's start in its round's staging area (the
+            // flat copy adds the staged byte offset). Unused for skipped fields.
+            const int64_t base = field_is_all(f) ? crow : field_is_q(f) ? cr : cw;
+            const uintptr_t d = reinterpret_cast<uintptr_t>(a.field[f]) + base * field_bytes(f) -
+                                static_cast<uintptr_t>(a.rounds.offset[f]);
+            dtab[f] = make_uint2(static_cast<uint32_t>(d), static_cast<uint32_t>(d >> 32));
+        }
+    }
 
     // ---- 1. keys (element i of the striped layout is entry r = i) and the sort.
     {
@@ -549,7 +612,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             afts[k] = after.f & ~kSegHead;
             run = seg_combine(run, tile_item(T, k, rr, x, end));
         }
-        const uint32_t prev_r = p0 > 0 && p0 <= n ? (sval[p0 - 1] & kRMask) : 0xFFFFu;
+        const uint32_t prev_raw = p0 > 0 && p0 <= n ? sval[p0 - 1] : (0xFFFFu & ~kFlagHead);
+        const uint32_t prev_r = prev_raw & kRMask;
         run = fp;
         uint32_t jk = kp & 0xFFFFu, jq = kp >> 16;
 #pragma unroll
@@ -581,6 +645,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             const bool pq = static_cast<int>(pr) - pt * wr >= W;
             const bool same_run = !head && pt == e.t && pq == e.q;
             e.walk = e.valid && !same_run && (before.f & 0xFFFFu) != 0u;
+            const bool prev_head = k ? ((heads >> (k - 1)) & 1u) : ((prev_raw & kFlagHead) != 0u);
+            e.keep = !head || !((ends >> k) & 1u) || (p0 + k > 0 && !prev_head);
             e.kg = (before.f & 0xFFFFu) + (afts[k] & 0xFFFFu) + ((e.valid && !e.q) ? 1u : 0u);
             e.gsize = e.kg + ((before.f >> 16) & 0x7FFFu) + ((afts[k] >> 16) & 0x7FFFu) + ((e.valid && e.q) ? 1u : 0u);
             if (e.live) {
@@ -680,7 +746,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                     if (a.hot != nullptr && e.valid && e.head && e.kg >= static_cast<uint32_t>(a.hot_min)) {
                         hot_buf[atomicAdd(&hot_n, 1u)] = make_uint2(static_cast<uint32_t>(p), e.gsize);
                     }
-                    if (a.rec != nullptr) {   // pair records {payload | head, log-cumsum s, c, value}
+                    if (a.rec != nullptr && e.keep) {   // pair records {payload | head, log-cumsum s, c, value}
                         a.rec[crow + p] = make_uint4(e.pay | (e.head ? kHead : 0u), __float_as_uint(e.s),
                                                      __float_as_uint(e.c), __float_as_uint(e.v));
                     }
@@ -707,13 +773,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             }
             if (mask != 0u) {   // block-uniform
                 lds_barrier();
-                for (int f = 0; f < kNumFields; ++f) {
-                    if (!(mask & (1u << f))) continue;
-                    const int cnt = field_is_all(f) ? n : field_is_q(f) ? C * R : C * W;
-                    const int64_t base = field_is_all(f) ? crow : field_is_q(f) ? cr : cw;
-                    unsigned char* dst = static_cast<unsigned char*>(a.field[f]) + base * field_bytes(f);
-                    block_copy_out(dst, stage + a.rounds.offset[f], cnt, field_bytes(f));
-                }
+                copy_round(a, rd, mask, stage, dtab, crow, cr, cw, C);
                 lds_barrier();
             }
         }
@@ -758,18 +818,13 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                 });
             }
             lds_barrier();
-            for (int f = 0; f < kNumFields; ++f) {
-                if (!(mask & (1u << f))) continue;
-                const int cnt = field_is_all(f) ? n : field_is_q(f) ? C * R : C * W;
-                const int64_t base = field_is_all(f) ? crow : field_is_q(f) ? cr : cw;
-                unsigned char* dst = static_cast<unsigned char*>(a.field[f]) + base * field_bytes(f);
-                block_copy_out(dst, stage + a.rounds.offset[f], cnt, field_bytes(f));
-            }
+            copy_round(a, rd, mask, stage, dtab, crow, cr, cw, C);
             lds_barrier();
         }
     }
     if constexpr (!kMerged) {
-        // ---- 4b. sorted-order outputs, staged per tile: pair records, then kind rows and krec.
+        // ---- 4b. sorted-order outputs: kind rows and krec staged per tile, pair records straight
+        // from registers.
         int nk, L;
         int64_t tb;
         tile_bounds(nk, L, tb);
@@ -782,22 +837,22 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             const uint32_t k0 = tile_kind[T] & 0xFFFFu, q0 = tile_kind[T] >> 16;
             const int nk_t = static_cast<int>((tile_kind[T + 1] & 0xFFFFu) - k0);
             const int nq_t = static_cast<int>((tile_kind[T + 1] >> 16) - q0);
+            // Pair records (the kept ones) go out from registers: in the kind-row pass when a tile's
+            // records and kind rows would fit the staging area together, else in a pass of their own.
+            // (Both forms stay in the code: with either one alone the compiler spills the sort's
+            // registers at 16 items per thread.)
             const int rec_bytes = a.rec != nullptr ? pcount * 16 : 0;
             const int kind_bytes = nk_t * 16 + (nk_t * 4 + 15) / 16 * 16 + nq_t * 4;
-            // One pass when the pair records, krec and both kind rows of the tile fit together.
             const bool joint = rec_bytes + kind_bytes <= a.stage_bytes;   // block-uniform
             if (rec_bytes > 0 && !joint) {
                 for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
-                    if (!e.live) return;
-                    reinterpret_cast<uint4*>(stage)[p - pbase] = make_uint4(
+                    if (!e.live || !e.keep) return;
+                    a.rec[crow + p] = make_uint4(
                         e.pay | (e.head ? kHead : 0u), __float_as_uint(e.s), __float_as_uint(e.c), __float_as_uint(e.v));
                 });
-                lds_barrier();
-                block_copy_out(a.rec + crow + pbase, stage, pcount, 16);
-                lds_barrier();
+                __asm__ volatile("" ::: "memory");
             }
-            unsigned char* st_rec = stage;
-            unsigned char* st_krec = stage + (joint ? rec_bytes : 0);
+            unsigned char* st_krec = stage;
             unsigned char* st_spk = st_krec + nk_t * 16;
             unsigned char* st_spq = st_spk + (nk_t * 4 + 15) / 16 * 16;
             for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
@@ -805,8 +860,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                 if (a.hot != nullptr && e.valid && e.head && e.kg >= static_cast<uint32_t>(a.hot_min)) {
                     hot_buf[atomicAdd(&hot_n, 1u)] = make_uint2(static_cast<uint32_t>(p), e.gsize);
                 }
-                if (joint && rec_bytes > 0) {
-                    reinterpret_cast<uint4*>(st_rec)[p - pbase] = make_uint4(
+                if (joint && rec_bytes > 0 && e.keep) {
+                    a.rec[crow + p] = make_uint4(
                         e.pay | (e.head ? kHead : 0u), __float_as_uint(e.s), __float_as_uint(e.c), __float_as_uint(e.v));
                 }
                 const uint32_t elem = e.valid ? (e.pay | min(e.bcnt, kDistMax) << kDistShift |
@@ -832,7 +887,6 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                 }
             });
             lds_barrier();
-            if (joint && rec_bytes > 0) block_copy_out(a.rec + crow + pbase, st_rec, pcount, 16);
             block_copy_out(a.krec + cw + k0, st_krec, nk_t, 16);
             block_copy_out(a.spay_k + cw + k0, st_spk, nk_t, 4);
             if (a.spay_q != nullptr) block_copy_out(a.spay_q + cr + q0, st_spq, nq_t, 4);
@@ -1276,14 +1330,18 @@ MainPlan plan_main(const sdm_p1_shape* s, const sdm_p1_io* io, bool with_pairs_w
                                    with_pairs_ws ? io : nullptr, with_pairs_ws ? io : nullptr};
     int need = 0;
     for (int f = 0; f < kNumFields; ++f) need += (field_count(s, f) * field_bytes(f) + 15) / 16 * 16;
-    // With 16 items per thread the sorted-order outputs are staged per tile (16-byte records of one
-    // tile; krec and both kind rows of one tile).
+    // With 16 items per thread krec and both kind rows are staged per tile.
     const int sorted_bytes = m.ipt == 16 ? kTile * 20 + 32 : 0;
     int cap = max(max(sort_bytes, sorted_bytes), min(need, cap_max));
     cap = min(cap, cap_max) / 16 * 16;
     // Greedy packing of the requested fields, in order, into rounds of `cap` bytes.
     m.rounds.count = 0;
-    for (int r = 0; r < kMaxRounds; ++r) m.rounds.mask[r] = 0u;
+    m.rounds.flat = 0u;
+    for (int r = 0; r < kMaxRounds; ++r) {
+        m.rounds.mask[r] = 0u;
+        m.rounds.vtotal[r] = 0;
+        for (int f = 0; f < kNumFields; ++f) m.rounds.vstart[r][f] = 0x3FFFFFFF;
+    }
     int used = cap;   // forces a new round for the first field
     for (int f = 0; f < kNumFields; ++f) {
         m.rounds.offset[f] = 0;
@@ -1299,7 +1357,9 @@ MainPlan plan_main(const sdm_p1_shape* s, const sdm_p1_io* io, bool with_pairs_w
         }
         m.rounds.offset[f] = used;
         m.rounds.mask[m.rounds.count - 1] |= 1u << f;
+        m.rounds.vstart[m.rounds.count - 1][f] = used / 16;
         used += bytes;
+        m.rounds.vtotal[m.rounds.count - 1] = used / 16;
     }
     m.stage_bytes = cap;
     m.lds_bytes = static_cast<size_t>(cap) + static_cast<size_t>(fixed);
@@ -1390,6 +1450,16 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     a.digit_bits = m.digit_bits;
     a.stage_bytes = m.stage_bytes;
     a.rounds = m.rounds;
+    // Flat copy-out for the rounds whose fields all have 16-byte aligned rows of whole vectors.
+    for (int r = 0; r < a.rounds.count; ++r) {
+        bool flat = true;
+        for (int f = 0; f < kNumFields; ++f) {
+            if (!(a.rounds.mask[r] & (1u << f))) continue;
+            flat = flat && (reinterpret_cast<uintptr_t>(a.field[f]) & 15u) == 0 &&
+                   (field_count(s, f) * field_bytes(f)) % 16 == 0;
+        }
+        if (flat) a.rounds.flat |= 1u << r;
+    }
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     if (io->events != nullptr) {
         for (int k = 0; k < 4; ++k) ev[k] = io->events[k];
