@@ -9,9 +9,11 @@
 //   3. forward scan: the same tiles in order; each thread keeps its forward prefix and kind-row
 //      base per tile. After these two passes every per-entry quantity can be recomputed by a
 //      thread from its own registers and the sorted row, with no further block-wide work;
-//   4. output rounds: entry-order fields are scattered into LDS at their entry index and copied
-//      out with 16-byte stores; sorted-order records (for the pair kernel), the sorted kind rows
-//      and the mover records are staged tile by tile (their indices are contiguous per tile).
+//   4. output sweeps: each thread recomputes its entries once per sweep, writes the sorted-order
+//      outputs (kind rows, mover records, pair records, tile bounds) from registers and leaves a
+//      compact record per entry in LDS at its entry index; the block then expands the records
+//      into the entry-order fields with coalesced stores. One sweep when every record fits in
+//      LDS, else one per kind (and token range).
 // A second kernel sums the A / QK triangles.
 //
 // Definitions: page "sparse_delta_memory/cuda/phase1_cuda.py" (module docstring; keys and payloads
@@ -19,6 +21,8 @@
 // Scans combine TwoSum-compensated float sums in a fixed tree; every output element has one
 // writer; no floating-point atomics are used, so results are bitwise reproducible.
 #include <hip/hip_ext.h>
+
+#include <type_traits>
 
 #include "sdm_device.hpp"
 #include "sdm_launch.hpp"
@@ -34,25 +38,43 @@ constexpr uint32_t kFlagHead = 1u << 14;   // group head, kept beside r (< 2^14)
 constexpr uint32_t kFlagRep = 1u << 15;    // repeated K entry (its gate is not applied again)
 constexpr uint32_t kRMask = kFlagHead - 1u;
 
-// Entry-order fields assembled in LDS and copied out with wide stores: the outputs, then two
-// workspace arrays for the pair kernel (sorted position of every entry; "starts a run with
-// earlier K entries in its group").
-enum Field : int {
-    kFLogK, kFRex, kFCpe, kFKEff, kFIsLast, kFIsOnly, kFPosK,
-    kFLogQ, kFQW, kFPosQ, kFQLast, kFQOnly, kFInv, kFWalk, kNumFields
-};
-constexpr int kMaxRounds = 8;
-
-struct Rounds {
+// Output sweeps: the entries (kind, token range) whose records one sweep leaves in LDS.
+constexpr int kMaxSweeps = 8;
+constexpr uint32_t kSweepK = 1u, kSweepQ = 2u;
+struct Sweeps {
     int count;
-    uint32_t mask[kMaxRounds];
-    uint32_t flat;            // rounds copied out by one loop over all their 16-byte vectors
-    int offset[kNumFields];   // byte offset of a field inside the staging area of its round
-    int vtotal[kMaxRounds];   // 16-byte vectors staged in a round
-    // Per round, the first vector of each of its fields (offset / 16); a large value for the other
-    // fields, so the field of vector v is the last one whose start is <= v.
-    int vstart[kMaxRounds][kNumFields];
+    uint32_t kinds[kMaxSweeps];
+    int t0[kMaxSweeps], t1[kMaxSweeps];   // tokens [t0, t1); t0 a multiple of 4
 };
+
+// Compact record of an entry, in LDS at its entry index (arrays of a sweep): L = f32 log-cumsum,
+// rex (K only), and a metadata word: sorted position (bits 0-13), min(after, 127) (14-20),
+// min(peers, 127) (21-27), no own-kind peer before (28), pair-kernel walk code (29-30), valid (31).
+constexpr int kMetaAfterShift = 14;
+constexpr int kMetaSizeShift = 21;
+constexpr uint32_t kMetaFirst = 1u << 28;
+constexpr int kMetaWalkShift = 29;
+constexpr uint32_t kMetaValid = 1u << 31;
+constexpr uint32_t kMetaPos = (1u << 14) - 1u;
+
+// Entry-order destinations, kept in an LDS table from the kernel's start to the sweeps (their
+// kernel-argument copies would otherwise hold scalar registers through the sort and the scans).
+enum OutPtr : int {
+    kOLogK, kORex, kOCpe, kOKEff, kOIsLast, kOIsOnly, kOPosK, kOInvK, kOWalkK,
+    kOLogQ, kOQW, kOPosQ, kOQLast, kOQOnly, kOInvQ, kOWalkQ, kNumOut
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Store of element i (a 32-bit index) of a T array in the global address space (a pointer read from
+// the LDS table would otherwise make a flat store, and a 64-bit index 64-bit address arithmetic).
+template <typename T>
+__device__ __forceinline__ void gstore(const void* base, uint32_t i, T v) {
+    typedef __attribute__((address_space(1))) T GT;
+    reinterpret_cast<GT*>(reinterpret_cast<uintptr_t>(base))[i] = v;
+}
 
 struct P1Args {
     const int32_t* k_idx;
@@ -60,7 +82,26 @@ struct P1Args {
     const float* k_val;
     const float* q_val;
     const float* g;
-    void* field[kNumFields];   // entry-order destinations (NULL: skipped); kFInv, kFWalk: workspace
+    // entry-order outputs (NULL: skipped)
+    float* log_k;
+    float* rex;
+    float* cpe;
+    float* k_eff;
+    int8_t* is_last;
+    int8_t* is_only;
+    int32_t* pos_k;
+    float* log_q;
+    float* q_w;
+    int32_t* pos_q;
+    int8_t* q_last;
+    int8_t* q_only;
+    // pair-kernel workspace in entry order, per kind (NULL: no pair sums): sorted position of the
+    // entry, and its walk code (1: starts its token's run with earlier valid K entries in the
+    // group; 2: the same in a hot group)
+    uint16_t* inv_k;
+    uint16_t* inv_q;
+    uint8_t* walk_k;
+    uint8_t* walk_q;
     int32_t* spay_k;
     int32_t* spay_q;
     int4* krec;
@@ -69,19 +110,14 @@ struct P1Args {
     uint4* rec;
     uint2* hot;          // per chunk: {count, 0}, then {head position, size} of each hot group (NULL: none)
     int C, W, R, P, key_bits, first_partial, valid_last, tile_len, digit_bits;
-    int stage_bytes;
+    int stage_bytes;     // LDS before the sorted row: sort keys and counts, then the sweeps' records
+    uint32_t vec;        // bit 0 (1): K (Q) fields take 4-entry vector stores (aligned rows)
     int hot_min;         // valid K entries that make a group hot for the pair kernel
     int hot_cap;         // hot groups one chunk can have (list entries after the count)
     uint32_t wr_magic;   // ceil(2^32 / (W + R)): r / (W + R) == umulhi(r, wr_magic) for r < 2^17
     int64_t stream_offset;
-    Rounds rounds;
+    Sweeps sweeps;
 };
-
-__host__ __device__ constexpr int field_bytes(int f) {
-    return (f == kFIsLast || f == kFIsOnly || f == kFQLast || f == kFQOnly || f == kFWalk) ? 1 : f == kFInv ? 2 : 4;
-}
-__host__ __device__ constexpr bool field_is_q(int f) { return f >= kFLogQ && f <= kFQOnly; }
-__host__ __device__ constexpr bool field_is_all(int f) { return f == kFInv || f == kFWalk; }
 
 // r / (W + R) for entry indices r < 2^17 and W + R <= 512 (multiply-high by a rounded-up
 // reciprocal; the error term r / 2^32 stays below 1 / (W + R)).
@@ -260,72 +296,6 @@ __device__ void block_radix_sort(uint32_t (&key)[IPT], uint32_t (&val)[IPT], int
     }
 }
 
-// Copies `count` elements of `es` bytes from LDS (16-byte aligned) to global memory with the
-// whole block: 16-byte accesses when the destination is 16-byte aligned, element-sized ones
-// otherwise.
-__device__ __forceinline__ void block_copy_out(void* dst, const unsigned char* src, int count, int es) {
-    const int bytes = count * es;
-    int done = 0;
-    if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
-        const int vecs = bytes >> 4;
-        for (int i = threadIdx.x; i < vecs; i += kNT) {
-            reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(src)[i];
-        }
-        done = vecs << 4;
-    }
-    if (es == 4 && (reinterpret_cast<uintptr_t>(dst) & 3u) == 0) {
-        for (int i = (done >> 2) + threadIdx.x; i < count; i += kNT) {
-            reinterpret_cast<uint32_t*>(dst)[i] = reinterpret_cast<const uint32_t*>(src)[i];
-        }
-        return;
-    }
-    for (int i = done + threadIdx.x; i < bytes; i += kNT) static_cast<unsigned char*>(dst)[i] = src[i];
-}
-
-// Copies the round's staged fields out. A flat round (every field's rows 16-byte aligned and a
-// multiple of 16 bytes long, so its vectors are contiguous in the staging area) is one loop over
-// all its vectors, two per thread in flight: the field of a vector is found by comparisons with
-// the round's field starts, its destination from a per-field table (`dtab[f]`: the chunk's row of
-// field f, minus the field's staging start). Otherwise each field is copied on its own.
-__device__ __forceinline__ void copy_round(const P1Args& a, int rd, uint32_t mask, const unsigned char* stage,
-                                           const uint2* dtab, int64_t crow, int64_t cr, int64_t cw, int C) {
-    if ((a.rounds.flat >> rd) & 1u) {   // block-uniform
-        const int total = a.rounds.vtotal[rd];
-        int vs[kNumFields];
-#pragma unroll
-        for (int k = 0; k < kNumFields; ++k) vs[k] = a.rounds.vstart[rd][k];
-        // Destination of vector v: the table holds plain integers, so the store names the global
-        // address space itself (a generic pointer would make it a flat store).
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(1))) u32x4 global_u32x4;
-        auto dst_of = [&](int v) {
-            int f = 0;
-#pragma unroll
-            for (int k = 0; k < kNumFields; ++k) f = v >= vs[k] ? k : f;
-            const uint2 d = dtab[f];
-            return reinterpret_cast<global_u32x4*>(static_cast<uintptr_t>(d.x) | static_cast<uintptr_t>(d.y) << 32) + v;
-        };
-        const u32x4* src = reinterpret_cast<const u32x4*>(stage);
-        for (int v0 = static_cast<int>(threadIdx.x); v0 < total; v0 += 2 * kNT) {
-            const int v1 = min(v0 + kNT, total - 1);   // a second vector in flight (a repeat at the end)
-            const u32x4 x0 = src[v0];
-            const u32x4 x1 = src[v1];
-            global_u32x4* d0 = dst_of(v0);
-            global_u32x4* d1 = dst_of(v1);
-            *d0 = x0;
-            if (v0 + kNT < total) *d1 = x1;
-        }
-        return;
-    }
-    for (int f = 0; f < kNumFields; ++f) {
-        if (!(mask & (1u << f))) continue;
-        const int cnt = field_is_all(f) ? a.C * (a.W + a.R) : field_is_q(f) ? C * a.R : C * a.W;
-        const int64_t base = field_is_all(f) ? crow : field_is_q(f) ? cr : cw;
-        unsigned char* d = static_cast<unsigned char*>(a.field[f]) + base * field_bytes(f);
-        block_copy_out(d, stage + a.rounds.offset[f], cnt, field_bytes(f));
-    }
-}
-
 // Everything one sorted position yields, recomputed by its owner thread from its tile prefixes.
 struct Entry {
     bool live;       // position < n
@@ -352,7 +322,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     constexpr int NP = kNT * IPT;
     constexpr int NTILE = (NP + kTile - 1) / kTile;
     extern __shared__ __align__(16) unsigned char smem[];
-    unsigned char* stage = smem;                                   // staging, after the scans
+    unsigned char* stage = smem;                                   // records, after the scans
     uint32_t* skey = reinterpret_cast<uint32_t*>(smem);           // sort keys (inside staging)
     uint32_t* hist = reinterpret_cast<uint32_t*>(smem + NP * 4);  // digit counts (inside staging)
     uint16_t* sval = reinterpret_cast<uint16_t*>(smem + a.stage_bytes);
@@ -361,7 +331,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     __shared__ uint32_t wsum[kNW];
     __shared__ uint32_t tile_kind[NTILE + 1];   // kind counts (K | Q << 16) before each tile
     __shared__ uint32_t hot_n;                   // hot groups found so far
-    __shared__ uint2 dtab[kNumFields];           // flat copy-out: per-field destination bases
+    __shared__ uint64_t optr[kNumOut];           // entry-order destinations (0: skipped)
     uint2* hot_buf = reinterpret_cast<uint2*>(smem + a.stage_bytes + NP * 2 + 256 * sizeof(float));
 
     const int c = blockIdx.x;
@@ -382,15 +352,12 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
 
     for (int t = threadIdx.x; t < C; t += kNT) gates[t] = t < tv ? a.g[static_cast<int64_t>(c) * C + t] : 0.0f;
     if (threadIdx.x == 0) hot_n = 0u;
+    {
+        const void* outs[kNumOut] = {a.log_k, a.rex, a.cpe, a.k_eff, a.is_last, a.is_only, a.pos_k, a.inv_k, a.walk_k,
+                                     a.log_q, a.q_w, a.pos_q, a.q_last, a.q_only, a.inv_q, a.walk_q};
 #pragma unroll
-    for (int f = 0; f < kNumFields; ++f) {
-        if (threadIdx.x == f) {
-            // The chunk's row of field f, less the field's start in its round's staging area (the
-            // flat copy adds the staged byte offset). Unused for skipped fields.
-            const int64_t base = field_is_all(f) ? crow : field_is_q(f) ? cr : cw;
-            const uintptr_t d = reinterpret_cast<uintptr_t>(a.field[f]) + base * field_bytes(f) -
-                                static_cast<uintptr_t>(a.rounds.offset[f]);
-            dtab[f] = make_uint2(static_cast<uint32_t>(d), static_cast<uint32_t>(d >> 32));
+        for (int o = 0; o < kNumOut; ++o) {
+            if (threadIdx.x == o) optr[o] = reinterpret_cast<uintptr_t>(outs[o]);
         }
     }
 
@@ -440,10 +407,9 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
         block_radix_sort<IPT>(key, val, tv < C ? kb + 1 : kb, a.digit_bits, skey, sval, hist, wsum);
     }
 
-    // Per-thread state carried from the scans to the output rounds (registers, tile-indexed).
+    // Per-thread state carried from the scans to the output sweeps (registers, tile-indexed).
     Seg rpre[NTILE], fpre[NTILE];
     uint32_t kpre[NTILE];
-    float vv[NTILE][kTileItems];
     uint32_t repeat_count = 0;
 
     // ---- 2. reverse scan: sums and peer counts after each entry in its group.
@@ -484,12 +450,6 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                 heads |= (head ? 1u : 0u) << k;
                 reps |= (rep ? 1u : 0u) << k;
                 x[k] = (is_k && !rep) ? gates[t] : 0.0f;
-                // Keep the slot and the value for the outputs (one branch-free load per entry).
-                const bool q = j >= W;
-                const int ln = q ? j - W : j;
-                const float* vsrc = q ? a.q_val + cr + t * R + ln : a.k_val + cw + t * W + ln;
-                const float vl = *(p0 + k < n ? vsrc : a.k_val + cw);
-                vv[T][k] = valid ? vl : 0.0f;
             }
 #pragma unroll
             for (int k = 0; k < kTileItems; ++k) {
@@ -523,10 +483,14 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     }
     __syncthreads();   // every flag of the sorted row is set; the keys are no longer needed
 
+    // The thread index as the recomputations see it: each output sweep makes it opaque again, so the
+    // compiler cannot hoist per-position address arithmetic out of the sweeps (registers it would
+    // hold through them).
+    int otid = static_cast<int>(threadIdx.x);
     // The tile's entries as the scans see them, from the flagged sorted row.
     auto load_tile = [&](int T, uint32_t (&rr)[kTileItems], float (&x)[kTileItems], uint32_t& heads,
                          uint32_t& ends) {
-        const int p0 = T * kTile + threadIdx.x * kTileItems;
+        const int p0 = T * kTile + otid * kTileItems;
         heads = 0;
         ends = 0;
 #pragma unroll
@@ -597,7 +561,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
 
     // Recomputes the four entries of tile T owned by this thread and calls f(k, entry).
     auto for_tile = [&](int T, const Seg& rp, const Seg& fp, uint32_t kp, const float (&vl)[kTileItems], auto&& f) {
-        const int p0 = T * kTile + threadIdx.x * kTileItems;
+        const int p0 = T * kTile + otid * kTileItems;
         uint32_t rr[kTileItems], heads, ends;
         float x[kTileItems];
         load_tile(T, rr, x, heads, ends);
@@ -664,233 +628,285 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
         return e.valid ? expf(gs + (e.c + ge)) : 1.0f;
     };
 
-    // ---- 4. Outputs: one pass per round over the thread's tile entries. Entry-order fields are
-    // staged in LDS by entry index and copied out with 16-byte stores. Sorted-order outputs (pair
-    // records, kind rows, mover records, tile bounds, the hot-group list) are written straight
-    // from registers in the first pass: a thread owns consecutive sorted positions and its K (Q)
-    // entries have consecutive kind indices, so these stores stay close to contiguous. With 16
-    // items per thread that pass would not fit the registers; there the sorted-order outputs get
-    // a pass of their own, staged tile by tile (4b).
-    constexpr bool kMerged = IPT <= 8;
+    // ---- 4. Outputs, in sweeps. A sweep recomputes the thread's entries from its tile prefixes;
+    // for the entries of the sweep (its kinds, its token range) it writes the sorted-order outputs
+    // straight from registers (a thread owns consecutive sorted positions, and its K (Q) entries
+    // have consecutive kind indices, so these stores stay close to contiguous) and leaves a
+    // compact record in LDS at the entry's index. After a barrier the block expands the records
+    // into the entry-order fields, each thread four consecutive entries at a time.
     // Tile bounds of the K-only row (values computed where they are used, to keep scalar
-    // registers free through the rounds).
+    // registers free through the sweeps).
     auto tile_bounds = [&](int& nk, int& L, int64_t& tb) {
         nk = C * W;
         L = a.tile_len;
         const int ntk = (nk + L - 1) / L;
         tb = static_cast<int64_t>(c) * (ntk + 1);
-        if (threadIdx.x == 0) a.tiles_k[tb + ntk] = nk;
     };
-    if constexpr (kMerged) {
+    if (threadIdx.x == 0) {
         int nk, L;
         int64_t tb;
         tile_bounds(nk, L, tb);
-        const int npass = a.rounds.count > 0 ? a.rounds.count : 1;
-        for (int rd = 0; rd < npass; ++rd) {
-            const uint32_t mask = a.rounds.count > 0 ? a.rounds.mask[rd] : 0u;
-            const bool sorted_pass = rd == 0;   // block-uniform
-            auto stage_at = [&](int f, int idx) { return stage + a.rounds.offset[f] + idx * field_bytes(f); };
-    #pragma unroll
-            for (int T = 0; T < NTILE; ++T) {
-                if (T >= ntiles) continue;
-                // The ids of this thread's K entries in the tile (for the mover-record slots), all loads
-                // in flight before the first use.
-                int32_t kid[kTileItems];
-                if (sorted_pass) {
-                    const int p0 = T * kTile + static_cast<int>(threadIdx.x) * kTileItems;
-    #pragma unroll
-                    for (int k = 0; k < kTileItems; ++k) {
-                        const int p = p0 + k;
-                        const int r = p < n ? static_cast<int>(sval[p] & kRMask) : 0;
-                        const int t = token_of_entry(r, a.wr_magic);
-                        const int j = r - t * wr;
-                        kid[k] = a.k_idx[cw + ((j < W && t < tv) ? t * W + j : 0)];
-                    }
-    #pragma unroll
-                    for (int k = 0; k < kTileItems; ++k) asm volatile("" ::"v"(kid[k]));
-                }
-                for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
-                    if (!e.live) return;
-                    const float Lv = e.s + e.c;
-                    if (mask != 0u) {
-                        const uint32_t packed =
-                            e.valid ? (static_cast<uint32_t>(p) | min(e.acnt, kPosCountMax) << kPosAfterShift |
-                                       min(e.bcnt + 1u + e.acnt, kPosCountMax) << kPosSizeShift)
-                                    : static_cast<uint32_t>(p);
-                        if (e.q) {
-                            const int o = e.t * R + e.ln;
-                            if (mask & (1u << kFLogQ)) *reinterpret_cast<float*>(stage_at(kFLogQ, o)) = Lv;
-                            if (mask & (1u << kFQW)) *reinterpret_cast<float*>(stage_at(kFQW, o)) = e.v * expf(Lv);
-                            if (mask & (1u << kFPosQ)) *reinterpret_cast<uint32_t*>(stage_at(kFPosQ, o)) = packed;
-                            const bool ql = e.valid && e.acnt == 0;
-                            if (mask & (1u << kFQLast)) *stage_at(kFQLast, o) = ql ? 1 : 0;
-                            if (mask & (1u << kFQOnly)) *stage_at(kFQOnly, o) = (ql && e.bcnt == 0) ? 1 : 0;
-                        } else {
-                            const int o = e.t * W + e.ln;
-                            const bool last = e.valid && e.acnt == 0;
-                            if (mask & (1u << kFLogK)) *reinterpret_cast<float*>(stage_at(kFLogK, o)) = Lv;
-                            if (mask & (1u << kFRex)) *reinterpret_cast<float*>(stage_at(kFRex, o)) = e.rex;
-                            if (mask & (1u << kFCpe)) *reinterpret_cast<float*>(stage_at(kFCpe, o)) = group_exp(e);
-                            if (mask & (1u << kFKEff)) *reinterpret_cast<float*>(stage_at(kFKEff, o)) = e.v * expf(Lv);
-                            if (mask & (1u << kFIsLast)) *stage_at(kFIsLast, o) = last ? 1 : 0;
-                            if (mask & (1u << kFIsOnly)) *stage_at(kFIsOnly, o) = (last && e.bcnt == 0) ? 1 : 0;
-                            if (mask & (1u << kFPosK)) *reinterpret_cast<uint32_t*>(stage_at(kFPosK, o)) = packed;
-                        }
-                        if (mask & (1u << kFInv)) *reinterpret_cast<uint16_t*>(stage_at(kFInv, e.r)) = static_cast<uint16_t>(p);
-                        if (mask & (1u << kFWalk)) {   // 1: walked by the pair kernel, 2: summed by its hot-group pass
-                            *stage_at(kFWalk, e.r) = e.walk ? (e.kg >= static_cast<uint32_t>(a.hot_min) ? 2 : 1) : 0;
-                        }
-                    }
-                    if (!sorted_pass) return;
-                    // Hot groups (the pair kernel sums them densely): appended in any order, sorted below.
-                    if (a.hot != nullptr && e.valid && e.head && e.kg >= static_cast<uint32_t>(a.hot_min)) {
-                        hot_buf[atomicAdd(&hot_n, 1u)] = make_uint2(static_cast<uint32_t>(p), e.gsize);
-                    }
-                    if (a.rec != nullptr && e.keep) {   // pair records {payload | head, log-cumsum s, c, value}
-                        a.rec[crow + p] = make_uint4(e.pay | (e.head ? kHead : 0u), __float_as_uint(e.s),
-                                                     __float_as_uint(e.c), __float_as_uint(e.v));
-                    }
-                    const uint32_t elem = e.valid ? (e.pay | min(e.bcnt, kDistMax) << kDistShift |
-                                                     (e.bcnt == 0 ? kFirst : 0u) | (e.acnt == 0 ? kLast : 0u))
-                                                  : (e.pay | kFirst | kLast);
-                    if (e.q) {
-                        if (a.spay_q != nullptr) a.spay_q[cr + e.jkind] = static_cast<int32_t>(elem);
-                    } else {
-                        a.spay_k[cw + e.jkind] = static_cast<int32_t>(elem);
-                        const float sc = e.valid ? e.v * expf(e.rex) : 0.0f;
-                        const int64_t id = static_cast<int64_t>(kid[k]);
-                        const uint32_t slot =
-                            e.valid ? static_cast<uint32_t>((static_cast<uint32_t>(id - id_base) & (key_lim - 1u)) + id_base)
-                                    : 0u;
-                        a.krec[cw + e.jkind] = make_int4(static_cast<int32_t>(elem), static_cast<int32_t>(slot),
-                                                         __float_as_int(sc), __float_as_int(group_exp(e)));
-                        if (static_cast<int>(e.jkind) % L == 0) {
-                            a.tiles_k[tb + static_cast<int>(e.jkind) / L] =
-                                (elem & kFirst) ? static_cast<int>(e.jkind) : min(static_cast<int>(e.jkind + e.acnt + 1u), nk);
-                        }
-                    }
-                });
-            }
-            if (mask != 0u) {   // block-uniform
-                lds_barrier();
-                copy_round(a, rd, mask, stage, dtab, crow, cr, cw, C);
-                lds_barrier();
-            }
-        }
-    } else {
-        // Entry-order rounds only (4a).
-        for (int rd = 0; rd < a.rounds.count; ++rd) {
-            const uint32_t mask = a.rounds.mask[rd];
-            auto stage_at = [&](int f, int idx) { return stage + a.rounds.offset[f] + idx * field_bytes(f); };
-    #pragma unroll
-            for (int T = 0; T < NTILE; ++T) {
-                if (T >= ntiles) continue;
-                for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
-                    if (!e.live) return;
-                    const float Lv = e.s + e.c;
-                    const uint32_t packed =
-                        e.valid ? (static_cast<uint32_t>(p) | min(e.acnt, kPosCountMax) << kPosAfterShift |
-                                   min(e.bcnt + 1u + e.acnt, kPosCountMax) << kPosSizeShift)
-                                : static_cast<uint32_t>(p);
-                    if (e.q) {
-                        const int o = e.t * R + e.ln;
-                        if (mask & (1u << kFLogQ)) *reinterpret_cast<float*>(stage_at(kFLogQ, o)) = Lv;
-                        if (mask & (1u << kFQW)) *reinterpret_cast<float*>(stage_at(kFQW, o)) = e.v * expf(Lv);
-                        if (mask & (1u << kFPosQ)) *reinterpret_cast<uint32_t*>(stage_at(kFPosQ, o)) = packed;
-                        const bool ql = e.valid && e.acnt == 0;
-                        if (mask & (1u << kFQLast)) *stage_at(kFQLast, o) = ql ? 1 : 0;
-                        if (mask & (1u << kFQOnly)) *stage_at(kFQOnly, o) = (ql && e.bcnt == 0) ? 1 : 0;
-                    } else {
-                        const int o = e.t * W + e.ln;
-                        const bool last = e.valid && e.acnt == 0;
-                        if (mask & (1u << kFLogK)) *reinterpret_cast<float*>(stage_at(kFLogK, o)) = Lv;
-                        if (mask & (1u << kFRex)) *reinterpret_cast<float*>(stage_at(kFRex, o)) = e.rex;
-                        if (mask & (1u << kFCpe)) *reinterpret_cast<float*>(stage_at(kFCpe, o)) = group_exp(e);
-                        if (mask & (1u << kFKEff)) *reinterpret_cast<float*>(stage_at(kFKEff, o)) = e.v * expf(Lv);
-                        if (mask & (1u << kFIsLast)) *stage_at(kFIsLast, o) = last ? 1 : 0;
-                        if (mask & (1u << kFIsOnly)) *stage_at(kFIsOnly, o) = (last && e.bcnt == 0) ? 1 : 0;
-                        if (mask & (1u << kFPosK)) *reinterpret_cast<uint32_t*>(stage_at(kFPosK, o)) = packed;
-                    }
-                    if (mask & (1u << kFInv)) *reinterpret_cast<uint16_t*>(stage_at(kFInv, e.r)) = static_cast<uint16_t>(p);
-                    if (mask & (1u << kFWalk)) {   // 1: walked by the pair kernel, 2: summed by its hot-group pass
-                        *stage_at(kFWalk, e.r) = e.walk ? (e.kg >= static_cast<uint32_t>(a.hot_min) ? 2 : 1) : 0;
-                    }
-                });
-            }
-            lds_barrier();
-            copy_round(a, rd, mask, stage, dtab, crow, cr, cw, C);
-            lds_barrier();
-        }
+        a.tiles_k[tb + (nk + L - 1) / L] = nk;
     }
-    if constexpr (!kMerged) {
-        // ---- 4b. sorted-order outputs: kind rows and krec staged per tile, pair records straight
-        // from registers.
-        int nk, L;
-        int64_t tb;
-        tile_bounds(nk, L, tb);
+    // One sweep over tokens [t0, t1) of the kinds KINDS (a compile-time set: a sweep of one kind
+    // carries only that kind's code, which keeps registers free at 16 items per thread).
+    auto sweep = [&](auto kinds_c, int t0, int t1) {
+        constexpr uint32_t kinds = decltype(kinds_c)::value;
+        constexpr bool sk = (kinds & kSweepK) != 0u, sq = (kinds & kSweepQ) != 0u;
+        asm volatile("" : "+v"(otid));
+        // Record arrays of the sweep (16-byte aligned, lengths padded to 4 entries).
+        const int nke = sk ? (t1 - t0) * W : 0, nqe = sq ? (t1 - t0) * R : 0;
+        const int nkp = (nke + 3) & ~3, nqp = (nqe + 3) & ~3;
+        float* kl = reinterpret_cast<float*>(stage);
+        float* kx = kl + nkp;
+        uint32_t* km = reinterpret_cast<uint32_t*>(kx + nkp);
+        float* ql = reinterpret_cast<float*>(km + nkp);
+        uint32_t* qm = reinterpret_cast<uint32_t*>(ql + nqp);
 #pragma unroll
         for (int T = 0; T < NTILE; ++T) {
             if (T >= ntiles) continue;
-            const int pbase = T * kTile;
-            const int pcount = min(kTile, n - pbase);
-            // Kind rows and mover records: the tile's K (Q) entries have consecutive kind indices.
-            const uint32_t k0 = tile_kind[T] & 0xFFFFu, q0 = tile_kind[T] >> 16;
-            const int nk_t = static_cast<int>((tile_kind[T + 1] & 0xFFFFu) - k0);
-            const int nq_t = static_cast<int>((tile_kind[T + 1] >> 16) - q0);
-            // Pair records (the kept ones) go out from registers: in the kind-row pass when a tile's
-            // records and kind rows would fit the staging area together, else in a pass of their own.
-            // (Both forms stay in the code: with either one alone the compiler spills the sort's
-            // registers at 16 items per thread.)
-            const int rec_bytes = a.rec != nullptr ? pcount * 16 : 0;
-            const int kind_bytes = nk_t * 16 + (nk_t * 4 + 15) / 16 * 16 + nq_t * 4;
-            const bool joint = rec_bytes + kind_bytes <= a.stage_bytes;   // block-uniform
-            if (rec_bytes > 0 && !joint) {
-                for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
-                    if (!e.live || !e.keep) return;
-                    a.rec[crow + p] = make_uint4(
-                        e.pay | (e.head ? kHead : 0u), __float_as_uint(e.s), __float_as_uint(e.c), __float_as_uint(e.v));
-                });
-                __asm__ volatile("" ::: "memory");
+            // The values of this thread's entries in the tile and the ids of its K entries (for the
+            // mover-record slots), all loads in flight before the first use.
+            int32_t kid[kTileItems];
+            float vl[kTileItems];
+            {
+                const int p0 = T * kTile + static_cast<int>(threadIdx.x) * kTileItems;
+#pragma unroll
+                for (int k = 0; k < kTileItems; ++k) {
+                    const int p = p0 + k;
+                    const int r = p < n ? static_cast<int>(sval[p] & kRMask) : 0;
+                    const int t = token_of_entry(r, a.wr_magic);
+                    const int j = r - t * wr;
+                    const bool q = j >= W;
+                    vl[k] = *(q ? a.q_val + cr + t * R + (j - W) : a.k_val + cw + t * W + j);
+                    if constexpr (sk) kid[k] = a.k_idx[cw + ((!q && t < tv) ? t * W + j : 0)];
+                }
+#pragma unroll
+                for (int k = 0; k < kTileItems; ++k) {
+                    asm volatile("" ::"v"(vl[k]));
+                    if constexpr (sk) asm volatile("" ::"v"(kid[k]));
+                }
+#pragma unroll
+                for (int k = 0; k < kTileItems; ++k) {   // invalid tokens' values are not used
+                    const int p = p0 + k;
+                    const int r = p < n ? static_cast<int>(sval[p] & kRMask) : 0;
+                    vl[k] = (p < n && token_of_entry(r, a.wr_magic) < tv) ? vl[k] : 0.0f;
+                }
             }
-            unsigned char* st_krec = stage;
-            unsigned char* st_spk = st_krec + nk_t * 16;
-            unsigned char* st_spq = st_spk + (nk_t * 4 + 15) / 16 * 16;
-            for_tile(T, rpre[T], fpre[T], kpre[T], vv[T], [&](int k, int p, const Entry& e) {
-                if (!e.live) return;
+            for_tile(T, rpre[T], fpre[T], kpre[T], vl, [&](int k, int p, const Entry& e) {
+                if (!e.live || (sk && !sq && e.q) || (sq && !sk && !e.q) || e.t < t0 || e.t >= t1) return;
+                const uint32_t walk = e.walk ? (e.kg >= static_cast<uint32_t>(a.hot_min) ? 2u : 1u) : 0u;
+                const uint32_t meta = static_cast<uint32_t>(p) | min(e.acnt, kPosCountMax) << kMetaAfterShift |
+                                      min(e.bcnt + 1u + e.acnt, kPosCountMax) << kMetaSizeShift |
+                                      (e.bcnt == 0u ? kMetaFirst : 0u) | walk << kMetaWalkShift |
+                                      (e.valid ? kMetaValid : 0u);
+                const float Lv = e.s + e.c;
+                // Hot groups (the pair kernel sums them densely): appended in any order, sorted below.
                 if (a.hot != nullptr && e.valid && e.head && e.kg >= static_cast<uint32_t>(a.hot_min)) {
                     hot_buf[atomicAdd(&hot_n, 1u)] = make_uint2(static_cast<uint32_t>(p), e.gsize);
                 }
-                if (joint && rec_bytes > 0 && e.keep) {
-                    a.rec[crow + p] = make_uint4(
-                        e.pay | (e.head ? kHead : 0u), __float_as_uint(e.s), __float_as_uint(e.c), __float_as_uint(e.v));
+                if (a.rec != nullptr && e.keep) {   // pair records {payload | head, log-cumsum s, c, value}
+                    gstore<u32x4>(a.rec + crow, static_cast<uint32_t>(p),
+                                  u32x4{e.pay | (e.head ? kHead : 0u), __float_as_uint(e.s), __float_as_uint(e.c),
+                                        __float_as_uint(e.v)});
                 }
                 const uint32_t elem = e.valid ? (e.pay | min(e.bcnt, kDistMax) << kDistShift |
                                                  (e.bcnt == 0 ? kFirst : 0u) | (e.acnt == 0 ? kLast : 0u))
                                               : (e.pay | kFirst | kLast);
-                if (e.q) {
-                    reinterpret_cast<uint32_t*>(st_spq)[e.jkind - q0] = elem;
+                if (sq && (!sk || e.q)) {
+                    const int o = (e.t - t0) * R + e.ln;
+                    ql[o] = Lv;
+                    qm[o] = meta;
+                    if (a.spay_q != nullptr) gstore<uint32_t>(a.spay_q + cr, e.jkind, elem);
                 } else {
-                    reinterpret_cast<uint32_t*>(st_spk)[e.jkind - k0] = elem;
+                    const int o = (e.t - t0) * W + e.ln;
+                    kl[o] = Lv;
+                    kx[o] = e.rex;
+                    km[o] = meta;
+                    gstore<uint32_t>(a.spay_k + cw, e.jkind, elem);
                     const float sc = e.valid ? e.v * expf(e.rex) : 0.0f;
-                    // The slot: the entry's id read again (the chunk's ids are cache-resident by now).
-                    const int64_t id = static_cast<int64_t>(a.k_idx[cw + (e.valid ? e.t * W + e.ln : 0)]);
+                    const int64_t id = static_cast<int64_t>(kid[k]);
                     const uint32_t slot =
                         e.valid ? static_cast<uint32_t>((static_cast<uint32_t>(id - id_base) & (key_lim - 1u)) + id_base)
                                 : 0u;
-                    reinterpret_cast<int4*>(st_krec)[e.jkind - k0] =
-                        make_int4(static_cast<int32_t>(elem), static_cast<int32_t>(slot), __float_as_int(sc),
-                                  __float_as_int(group_exp(e)));
+                    gstore<u32x4>(a.krec + cw, e.jkind,
+                                  u32x4{elem, slot, __float_as_uint(sc), __float_as_uint(group_exp(e))});
+                    int nk, L;
+                    int64_t tb;
+                    tile_bounds(nk, L, tb);
                     if (static_cast<int>(e.jkind) % L == 0) {
-                        a.tiles_k[tb + static_cast<int>(e.jkind) / L] =
-                            (elem & kFirst) ? static_cast<int>(e.jkind) : min(static_cast<int>(e.jkind + e.acnt + 1u), nk);
+                        gstore<int32_t>(a.tiles_k + tb, e.jkind / static_cast<uint32_t>(L),
+                                        (elem & kFirst) ? static_cast<int>(e.jkind)
+                                                        : min(static_cast<int>(e.jkind + e.acnt + 1u), nk));
                     }
                 }
             });
-            lds_barrier();
-            block_copy_out(a.krec + cw + k0, st_krec, nk_t, 16);
-            block_copy_out(a.spay_k + cw + k0, st_spk, nk_t, 4);
-            if (a.spay_q != nullptr) block_copy_out(a.spay_q + cr + q0, st_spq, nq_t, 4);
-            lds_barrier();
+        }
+        lds_barrier();
+        // Entry-order fields from the records: entries i0 .. i0 + 3 of the sweep's kind rows.
+        auto pos_of = [](uint32_t m) {
+            const uint32_t p = m & kMetaPos;
+            return (m & kMetaValid) ? (p | ((m >> kMetaAfterShift) & kPosCountMax) << kPosAfterShift |
+                                       ((m >> kMetaSizeShift) & kPosCountMax) << kPosSizeShift)
+                                    : p;
+        };
+        auto is_last_of = [](uint32_t m) { return (m & kMetaValid) && ((m >> kMetaAfterShift) & kPosCountMax) == 0u; };
+        // A destination from the table, as a wave-uniform pointer (nullptr: skipped).
+        // The sweep's first entry of the row is element `first` (es bytes each) of the chunk's row.
+        auto out_ptr = [&](int o, int64_t first, int es) {
+            const uint64_t v = optr[o];
+            const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+            const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+            const uintptr_t b = static_cast<uintptr_t>(lo) | static_cast<uintptr_t>(hi) << 32;
+            return b != 0 ? reinterpret_cast<void*>(b + static_cast<uintptr_t>(first * es)) : nullptr;
+        };
+        if constexpr (sk) {
+            const int64_t gb = cw + static_cast<int64_t>(t0) * W;   // the chunk's entry index of record 0
+            void* const log_k = out_ptr(kOLogK, gb, 4);
+            void* const rex_o = out_ptr(kORex, gb, 4);
+            void* const cpe_o = out_ptr(kOCpe, gb, 4);
+            void* const k_eff = out_ptr(kOKEff, gb, 4);
+            void* const is_last = out_ptr(kOIsLast, gb, 1);
+            void* const is_only = out_ptr(kOIsOnly, gb, 1);
+            void* const pos_k = out_ptr(kOPosK, gb, 4);
+            void* const inv_k = out_ptr(kOInvK, gb, 2);
+            void* const walk_k = out_ptr(kOWalkK, gb, 1);
+            const bool vec = (a.vec & 1u) != 0u;
+            for (int i0 = 4 * static_cast<int>(threadIdx.x); i0 < nke; i0 += 4 * kNT) {
+                const int cnt = min(4, nke - i0);
+                const f32x4 L4 = *reinterpret_cast<const f32x4*>(kl + i0);
+                const f32x4 X4 = *reinterpret_cast<const f32x4*>(kx + i0);
+                const u32x4 M4 = *reinterpret_cast<const u32x4*>(km + i0);
+                const uint32_t g = static_cast<uint32_t>(i0);
+                f32x4 v4;
+                if (vec && cnt == 4) {
+                    v4 = *reinterpret_cast<const f32x4*>(a.k_val + gb + g);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) v4[u] = a.k_val[gb + g + min(u, cnt - 1)];
+                }
+                f32x4 cp, ke;
+                u32x4 ps;
+                uint32_t fl = 0u, fo = 0u, wk = 0u;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t m = M4[u];
+                    const bool valid = (m & kMetaValid) != 0u;
+                    cp[u] = valid ? expf(L4[u] + X4[u]) : 1.0f;
+                    ke[u] = valid ? v4[u] * expf(L4[u]) : 0.0f;
+                    ps[u] = pos_of(m);
+                    const bool last = is_last_of(m);
+                    fl |= (last ? 1u : 0u) << (8 * u);
+                    fo |= ((last && (m & kMetaFirst)) ? 1u : 0u) << (8 * u);
+                    wk |= ((m >> kMetaWalkShift) & 3u) << (8 * u);
+                }
+                if (vec && cnt == 4) {
+                    const uint32_t g4 = g / 4;
+                    if (log_k != nullptr) gstore<f32x4>(log_k, g4, L4);
+                    if (rex_o != nullptr) gstore<f32x4>(rex_o, g4, X4);
+                    if (cpe_o != nullptr) gstore<f32x4>(cpe_o, g4, cp);
+                    if (k_eff != nullptr) gstore<f32x4>(k_eff, g4, ke);
+                    if (pos_k != nullptr) gstore<u32x4>(pos_k, g4, ps);
+                    if (is_last != nullptr) gstore<uint32_t>(is_last, g4, fl);
+                    if (is_only != nullptr) gstore<uint32_t>(is_only, g4, fo);
+                    if (inv_k != nullptr) {
+                        gstore<u32x2>(inv_k, g4, u32x2{(M4[0] & kMetaPos) | (M4[1] & kMetaPos) << 16,
+                                                      (M4[2] & kMetaPos) | (M4[3] & kMetaPos) << 16});
+                        gstore<uint32_t>(walk_k, g4, wk);
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        if (u >= cnt) break;
+                        if (log_k != nullptr) gstore<float>(log_k, g + u, L4[u]);
+                        if (rex_o != nullptr) gstore<float>(rex_o, g + u, X4[u]);
+                        if (cpe_o != nullptr) gstore<float>(cpe_o, g + u, cp[u]);
+                        if (k_eff != nullptr) gstore<float>(k_eff, g + u, ke[u]);
+                        if (pos_k != nullptr) gstore<uint32_t>(pos_k, g + u, ps[u]);
+                        if (is_last != nullptr) gstore<uint8_t>(is_last, g + u, static_cast<uint8_t>((fl >> (8 * u)) & 1u));
+                        if (is_only != nullptr) gstore<uint8_t>(is_only, g + u, static_cast<uint8_t>((fo >> (8 * u)) & 1u));
+                        if (inv_k != nullptr) {
+                            gstore<uint16_t>(inv_k, g + u, static_cast<uint16_t>(M4[u] & kMetaPos));
+                            gstore<uint8_t>(walk_k, g + u, static_cast<uint8_t>((wk >> (8 * u)) & 3u));
+                        }
+                    }
+                }
+            }
+        }
+        if constexpr (sq) {
+            const int64_t gb = cr + static_cast<int64_t>(t0) * R;
+            void* const log_q = out_ptr(kOLogQ, gb, 4);
+            void* const q_w = out_ptr(kOQW, gb, 4);
+            void* const pos_q = out_ptr(kOPosQ, gb, 4);
+            void* const q_last = out_ptr(kOQLast, gb, 1);
+            void* const q_only = out_ptr(kOQOnly, gb, 1);
+            void* const inv_q = out_ptr(kOInvQ, gb, 2);
+            void* const walk_q = out_ptr(kOWalkQ, gb, 1);
+            const bool vec = (a.vec & 2u) != 0u;
+            for (int i0 = 4 * static_cast<int>(threadIdx.x); i0 < nqe; i0 += 4 * kNT) {
+                const int cnt = min(4, nqe - i0);
+                const f32x4 L4 = *reinterpret_cast<const f32x4*>(ql + i0);
+                const u32x4 M4 = *reinterpret_cast<const u32x4*>(qm + i0);
+                const uint32_t g = static_cast<uint32_t>(i0);
+                f32x4 v4;
+                if (vec && cnt == 4) {
+                    v4 = *reinterpret_cast<const f32x4*>(a.q_val + gb + g);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) v4[u] = a.q_val[gb + g + min(u, cnt - 1)];
+                }
+                f32x4 qw;
+                u32x4 ps;
+                uint32_t fl = 0u, fo = 0u, wk = 0u;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t m = M4[u];
+                    const bool valid = (m & kMetaValid) != 0u;
+                    qw[u] = valid ? v4[u] * expf(L4[u]) : 0.0f;
+                    ps[u] = pos_of(m);
+                    const bool last = is_last_of(m);
+                    fl |= (last ? 1u : 0u) << (8 * u);
+                    fo |= ((last && (m & kMetaFirst)) ? 1u : 0u) << (8 * u);
+                    wk |= ((m >> kMetaWalkShift) & 3u) << (8 * u);
+                }
+                if (vec && cnt == 4) {
+                    const uint32_t g4 = g / 4;
+                    if (log_q != nullptr) gstore<f32x4>(log_q, g4, L4);
+                    if (q_w != nullptr) gstore<f32x4>(q_w, g4, qw);
+                    if (pos_q != nullptr) gstore<u32x4>(pos_q, g4, ps);
+                    if (q_last != nullptr) gstore<uint32_t>(q_last, g4, fl);
+                    if (q_only != nullptr) gstore<uint32_t>(q_only, g4, fo);
+                    if (inv_q != nullptr) {
+                        gstore<u32x2>(inv_q, g4, u32x2{(M4[0] & kMetaPos) | (M4[1] & kMetaPos) << 16,
+                                                      (M4[2] & kMetaPos) | (M4[3] & kMetaPos) << 16});
+                        gstore<uint32_t>(walk_q, g4, wk);
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        if (u >= cnt) break;
+                        if (log_q != nullptr) gstore<float>(log_q, g + u, L4[u]);
+                        if (q_w != nullptr) gstore<float>(q_w, g + u, qw[u]);
+                        if (pos_q != nullptr) gstore<uint32_t>(pos_q, g + u, ps[u]);
+                        if (q_last != nullptr) gstore<uint8_t>(q_last, g + u, static_cast<uint8_t>((fl >> (8 * u)) & 1u));
+                        if (q_only != nullptr) gstore<uint8_t>(q_only, g + u, static_cast<uint8_t>((fo >> (8 * u)) & 1u));
+                        if (inv_q != nullptr) {
+                            gstore<uint16_t>(inv_q, g + u, static_cast<uint16_t>(M4[u] & kMetaPos));
+                            gstore<uint8_t>(walk_q, g + u, static_cast<uint8_t>((wk >> (8 * u)) & 3u));
+                        }
+                    }
+                }
+            }
+        }
+        lds_barrier();   // the records are read before the next sweep writes its own
+    };
+    if constexpr (IPT <= 8) {   // every record fits in LDS (the host checks): one sweep
+        sweep(std::integral_constant<uint32_t, kSweepK | kSweepQ>{}, 0, C);
+    } else {   // one kind per sweep (a planned joint sweep runs as its K part, then its Q part)
+        for (int sw = 0; sw < a.sweeps.count; ++sw) {
+            const uint32_t kinds = a.sweeps.kinds[sw];
+            if (kinds & kSweepK) sweep(std::integral_constant<uint32_t, kSweepK>{}, a.sweeps.t0[sw], a.sweeps.t1[sw]);
+            if (kinds & kSweepQ) sweep(std::integral_constant<uint32_t, kSweepQ>{}, a.sweeps.t0[sw], a.sweeps.t1[sw]);
         }
     }
     __syncthreads();   // every hot-group append is done
@@ -923,8 +939,10 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
 // by the input (hot groups in position order, then the walks).
 struct PairArgs {
     const uint4* rec;
-    const uint16_t* inv;
-    const uint8_t* walk;
+    const uint16_t* inv_k;   // entry-order sorted positions and walk codes, per kind
+    const uint16_t* inv_q;
+    const uint8_t* walk_k;
+    const uint8_t* walk_q;
     const uint2* hot;   // per chunk: {count, 0}, then {head position, size} in position order (NULL: none)
     float* a;
     float* qk;
@@ -1211,9 +1229,9 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
     if (i < tv) {
         float* row = tri + i * (i + 1) / 2;
         const int lanes = q ? R : W;
-        const int r0 = i * wr + (q ? W : 0);
-        const uint8_t* wf = a.walk + crow + r0;
-        const uint16_t* iv = a.inv + crow + r0;
+        const int64_t e0 = (static_cast<int64_t>(c) * C + i) * lanes;   // token i's first entry of the kind
+        const uint8_t* wf = (q ? a.walk_q : a.walk_k) + e0;
+        const uint16_t* iv = (q ? a.inv_q : a.inv_k) + e0;
         // Token i's entries of this kind: (Q flag, token) bits of the payload.
         const uint32_t own_tag = (q ? kIsQ : 0u) | (static_cast<uint32_t>(i) << kTokShift);
         const uint32_t tag_mask = kIsQ | (0xFFu << kTokShift);
@@ -1227,7 +1245,7 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
           }
           for (; flags != 0u; flags &= flags - 1u) {
             const int ln = lb + __builtin_ctz(flags);
-            const int rho = iv[ln];
+            const int rho = min(static_cast<int>(iv[ln]), n - 1);   // (a position < n; the clamp only guards)
             const uint4 own = rec[rho];
             // Sum the run's values.
             float wi = __uint_as_float(own.w);
@@ -1294,24 +1312,26 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
     }
 }
 
-// Host-side plan of one Phase-1 launch: sort items per thread, digit width, staging rounds.
+// Host-side plan of one Phase-1 launch: sort items per thread, digit width, output sweeps.
 struct MainPlan {
     int ipt;
     int digit_bits;
     int stage_bytes;
     size_t lds_bytes;
-    Rounds rounds;
+    Sweeps sweeps;
 };
 
 constexpr int kLdsTotal = 160 * 1024;
 constexpr int kStaticReserve = 1024;   // static LDS of the kernel (scan totals, tile counts)
 
-int field_count(const sdm_p1_shape* s, int f) {
-    const int n = s->C * (s->W + s->R);
-    return field_is_all(f) ? n : field_is_q(f) ? s->C * s->R : s->C * s->W;
+// LDS bytes of the records of one sweep (arrays padded to 4 entries): K 12 B, Q 8 B per entry.
+int sweep_bytes(const sdm_p1_shape* s, uint32_t kinds, int tokens) {
+    const int nk = (kinds & kSweepK) ? (tokens * s->W + 3) & ~3 : 0;
+    const int nq = (kinds & kSweepQ) ? (tokens * s->R + 3) & ~3 : 0;
+    return nk * 12 + nq * 8;
 }
 
-MainPlan plan_main(const sdm_p1_shape* s, const sdm_p1_io* io, bool with_pairs_ws) {
+MainPlan plan_main(const sdm_p1_shape* s, bool with_pairs_ws) {
     MainPlan m;
     const int n = s->C * (s->W + s->R);
     m.ipt = n <= kNT ? 1 : n <= 2 * kNT ? 2 : n <= 4 * kNT ? 4 : n <= 8 * kNT ? 8 : 16;
@@ -1324,45 +1344,32 @@ MainPlan plan_main(const sdm_p1_shape* s, const sdm_p1_io* io, bool with_pairs_w
     int d = 10;
     while (d > 4 && np * 4 + kNW * (1 << d) * 4 > cap_max) --d;
     m.digit_bits = d;
-    const int sort_bytes = np * 4 + kNW * (1 << d) * 4;
-    const void* dst[kNumFields] = {io->log_k, io->rex, io->cpe, io->k_eff, io->is_last, io->is_only, io->pos_k,
-                                   io->log_q, io->q_w, io->pos_q, io->q_last, io->q_only,
-                                   with_pairs_ws ? io : nullptr, with_pairs_ws ? io : nullptr};
-    int need = 0;
-    for (int f = 0; f < kNumFields; ++f) need += (field_count(s, f) * field_bytes(f) + 15) / 16 * 16;
-    // With 16 items per thread krec and both kind rows are staged per tile.
-    const int sorted_bytes = m.ipt == 16 ? kTile * 20 + 32 : 0;
-    int cap = max(max(sort_bytes, sorted_bytes), min(need, cap_max));
-    cap = min(cap, cap_max) / 16 * 16;
-    // Greedy packing of the requested fields, in order, into rounds of `cap` bytes.
-    m.rounds.count = 0;
-    m.rounds.flat = 0u;
-    for (int r = 0; r < kMaxRounds; ++r) {
-        m.rounds.mask[r] = 0u;
-        m.rounds.vtotal[r] = 0;
-        for (int f = 0; f < kNumFields; ++f) m.rounds.vstart[r][f] = 0x3FFFFFFF;
-    }
-    int used = cap;   // forces a new round for the first field
-    for (int f = 0; f < kNumFields; ++f) {
-        m.rounds.offset[f] = 0;
-        if (dst[f] == nullptr) continue;
-        const int bytes = (field_count(s, f) * field_bytes(f) + 15) / 16 * 16;
-        if (used + bytes > cap) {
-            if (m.rounds.count == kMaxRounds) {   // cannot happen for n <= 16384 (>= 2 fields a round)
-                m.rounds.count = kMaxRounds + 1;
-                return m;
-            }
-            ++m.rounds.count;
-            used = 0;
+    int cap = np * 4 + kNW * (1 << d) * 4;
+    // Sweeps: every record at once up to 8 items per thread, else each kind in token ranges
+    // (multiples of 4 tokens, so every range starts 16-byte aligned in the entry-order rows).
+    Sweeps& sw = m.sweeps;
+    sw.count = 0;
+    auto add = [&](uint32_t kinds, int t0, int t1) {
+        if (sw.count < kMaxSweeps) {
+            sw.kinds[sw.count] = kinds;
+            sw.t0[sw.count] = t0;
+            sw.t1[sw.count] = t1;
+            cap = max(cap, sweep_bytes(s, kinds, t1 - t0));
         }
-        m.rounds.offset[f] = used;
-        m.rounds.mask[m.rounds.count - 1] |= 1u << f;
-        m.rounds.vstart[m.rounds.count - 1][f] = used / 16;
-        used += bytes;
-        m.rounds.vtotal[m.rounds.count - 1] = used / 16;
+        ++sw.count;
+    };
+    if (m.ipt <= 8) {   // fits: n <= 8192 entries of at most 12 B beside at most 21 KB of the rest
+        add(kSweepK | kSweepQ, 0, s->C);
+        if (sweep_bytes(s, kSweepK | kSweepQ, s->C) > cap_max) sw.count = kMaxSweeps + 1;   // refused
+    } else {   // the kernel sweeps one kind at a time here
+        for (uint32_t kind : {kSweepK, kSweepQ}) {
+            int step = 4;
+            while (step + 4 <= s->C && sweep_bytes(s, kind, step + 4) <= cap_max) step += 4;
+            for (int t0 = 0; t0 < s->C; t0 += step) add(kind, t0, min(s->C, t0 + step));
+        }
     }
-    m.stage_bytes = cap;
-    m.lds_bytes = static_cast<size_t>(cap) + static_cast<size_t>(fixed);
+    m.stage_bytes = (cap + 15) / 16 * 16;
+    m.lds_bytes = static_cast<size_t>(m.stage_bytes) + static_cast<size_t>(fixed);
     return m;
 }
 
@@ -1380,13 +1387,17 @@ hipError_t launch_main(P1Args args, size_t lds, int N, hipStream_t st, hipEvent_
 P1Workspace p1_workspace_layout(const sdm_p1_shape* s) {
     const size_t n = static_cast<size_t>(s->C) * static_cast<size_t>(s->W + s->R);
     const size_t N = static_cast<size_t>(s->N);
+    const size_t nk = N * static_cast<size_t>(s->C) * static_cast<size_t>(s->W);
+    const size_t nq = N * static_cast<size_t>(s->C) * static_cast<size_t>(s->R);
     auto up = [](size_t b) { return (b + 255) / 256 * 256; };
     P1Workspace w;
     w.rec_off = 0;
-    w.inv_off = up(N * n * sizeof(uint4));
-    w.walk_off = w.inv_off + up(N * n * sizeof(uint16_t));
+    w.inv_k_off = up(N * n * sizeof(uint4));
+    w.inv_q_off = w.inv_k_off + up(nk * sizeof(uint16_t));
+    w.walk_k_off = w.inv_q_off + up(nq * sizeof(uint16_t));
+    w.walk_q_off = w.walk_k_off + up(nk);
     w.hot_cap = s->C * s->W / kHotMin;
-    w.hot_off = w.walk_off + up(N * n);
+    w.hot_off = w.walk_q_off + up(nq);
     w.total = w.hot_off + up(N * static_cast<size_t>(w.hot_cap + 1) * sizeof(uint2));
     return w;
 }
@@ -1396,7 +1407,7 @@ size_t p1_pair_lds_min(const sdm_p1_shape* s) {
 }
 
 size_t p1_lds_bytes(const sdm_p1_shape* s, const sdm_p1_io* io) {
-    return plan_main(s, io, io->a != nullptr || io->qk != nullptr).lds_bytes;
+    return plan_main(s, io->a != nullptr || io->qk != nullptr).lds_bytes;
 }
 
 hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
@@ -1410,10 +1421,31 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     a.k_val = io->k_val;
     a.q_val = io->q_val;
     a.g = io->g;
-    void* fields[kNumFields] = {io->log_k, io->rex, io->cpe, io->k_eff, io->is_last, io->is_only, io->pos_k,
-                                io->log_q, io->q_w, io->pos_q, io->q_last, io->q_only,
-                                pairs ? Lc.inv : nullptr, pairs ? Lc.walk : nullptr};
-    for (int f = 0; f < kNumFields; ++f) a.field[f] = fields[f];
+    a.log_k = io->log_k;
+    a.rex = io->rex;
+    a.cpe = io->cpe;
+    a.k_eff = io->k_eff;
+    a.is_last = io->is_last;
+    a.is_only = io->is_only;
+    a.pos_k = io->pos_k;
+    a.log_q = io->log_q;
+    a.q_w = io->q_w;
+    a.pos_q = io->pos_q;
+    a.q_last = io->q_last;
+    a.q_only = io->q_only;
+    a.inv_k = pairs ? static_cast<uint16_t*>(Lc.inv_k) : nullptr;
+    a.inv_q = pairs ? static_cast<uint16_t*>(Lc.inv_q) : nullptr;
+    a.walk_k = pairs ? static_cast<uint8_t*>(Lc.walk_k) : nullptr;
+    a.walk_q = pairs ? static_cast<uint8_t*>(Lc.walk_q) : nullptr;
+    // Four-entry vector stores where every row of the kind's fields is 16-byte aligned (4-byte for
+    // the flag bytes; the workspace rows follow from C * W or C * R being a multiple of 4).
+    auto al = [](const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & (m - 1)) == 0; };
+    const bool vk = (s->C * s->W) % 4 == 0 && al(io->k_val, 16) && al(io->log_k, 16) && al(io->rex, 16) &&
+                    al(io->cpe, 16) && al(io->k_eff, 16) && al(io->pos_k, 16) && al(io->is_last, 4) &&
+                    al(io->is_only, 4);
+    const bool vq = (s->C * s->R) % 4 == 0 && al(io->q_val, 16) && al(io->log_q, 16) && al(io->q_w, 16) &&
+                    al(io->pos_q, 16) && al(io->q_last, 4) && al(io->q_only, 4);
+    a.vec = (vk ? 1u : 0u) | (vq ? 2u : 0u);
     a.spay_k = io->spay_k;
     a.spay_q = io->spay_q;
     a.krec = reinterpret_cast<int4*>(io->krec);
@@ -1445,21 +1477,11 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     a.stream_offset = s->stream_offset;
     a.wr_magic = static_cast<uint32_t>(((uint64_t(1) << 32) + static_cast<uint64_t>(s->W + s->R) - 1) /
                                        static_cast<uint64_t>(s->W + s->R));
-    const MainPlan m = plan_main(s, io, pairs);
-    if (m.rounds.count > kMaxRounds) return hipErrorInvalidValue;
+    const MainPlan m = plan_main(s, pairs);
+    if (m.sweeps.count > kMaxSweeps) return hipErrorInvalidValue;
     a.digit_bits = m.digit_bits;
     a.stage_bytes = m.stage_bytes;
-    a.rounds = m.rounds;
-    // Flat copy-out for the rounds whose fields all have 16-byte aligned rows of whole vectors.
-    for (int r = 0; r < a.rounds.count; ++r) {
-        bool flat = true;
-        for (int f = 0; f < kNumFields; ++f) {
-            if (!(a.rounds.mask[r] & (1u << f))) continue;
-            flat = flat && (reinterpret_cast<uintptr_t>(a.field[f]) & 15u) == 0 &&
-                   (field_count(s, f) * field_bytes(f)) % 16 == 0;
-        }
-        if (flat) a.rounds.flat |= 1u << r;
-    }
+    a.sweeps = m.sweeps;
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     if (io->events != nullptr) {
         for (int k = 0; k < 4; ++k) ev[k] = io->events[k];
@@ -1475,8 +1497,10 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     if (e != hipSuccess || !pairs) return e;
     PairArgs pa;
     pa.rec = static_cast<const uint4*>(Lc.rec);
-    pa.inv = static_cast<const uint16_t*>(Lc.inv);
-    pa.walk = static_cast<const uint8_t*>(Lc.walk);
+    pa.inv_k = static_cast<const uint16_t*>(Lc.inv_k);
+    pa.inv_q = static_cast<const uint16_t*>(Lc.inv_q);
+    pa.walk_k = static_cast<const uint8_t*>(Lc.walk_k);
+    pa.walk_q = static_cast<const uint8_t*>(Lc.walk_q);
     pa.hot = static_cast<const uint2*>(Lc.hot);
     pa.hot_cap = hot_cap;
     pa.tab_cap = hot_on ? tab_cap : 0;
