@@ -364,44 +364,28 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     // ---- 1. keys (element i of the striped layout is entry r = i) and the sort.
     {
         uint32_t key[IPT], val[IPT];
-        if constexpr (IPT <= 8) {
-            int32_t ids[IPT];
-            // Every item loads (padding items re-read entry 0) before any id is used: the asm
-            // below keeps the compiler from sinking a load into the select that uses it, where
-            // each load would get a wait of its own. (With 16 items per thread the registers are
-            // better spent otherwise: measured slower there.)
+        int32_t ids[IPT];
+        // Every item loads (padding items re-read entry 0) before any id is used: the asm below
+        // keeps the compiler from sinking a load into the select that uses it, where each load
+        // would get a wait of its own.
 #pragma unroll
-            for (int k = 0; k < IPT; ++k) {
-                const int i = w * kWave * IPT + k * kWave + lane;
-                val[k] = static_cast<uint32_t>(i);
-                const int ic = i < n ? i : 0;
-                const int t = token_of_entry(ic, a.wr_magic);
-                const int j = ic - t * wr;
-                ids[k] = *(j < W ? a.k_idx + cw + t * W + j : a.q_idx + cr + t * R + (j - W));
-            }
+        for (int k = 0; k < IPT; ++k) {
+            const int i = w * kWave * IPT + k * kWave + lane;
+            val[k] = static_cast<uint32_t>(i);
+            const int ic = i < n ? i : 0;
+            const int t = token_of_entry(ic, a.wr_magic);
+            const int j = ic - t * wr;
+            ids[k] = *(j < W ? a.k_idx + cw + t * W + j : a.q_idx + cr + t * R + (j - W));
+        }
 #pragma unroll
-            for (int k = 0; k < IPT; ++k) asm volatile("" ::"v"(ids[k]));
+        for (int k = 0; k < IPT; ++k) asm volatile("" ::"v"(ids[k]));
 #pragma unroll
-            for (int k = 0; k < IPT; ++k) {
-                const int i = w * kWave * IPT + k * kWave + lane;
-                const int t = token_of_entry(i < n ? i : 0, a.wr_magic);
-                const uint32_t kv =
-                    t < tv ? static_cast<uint32_t>(static_cast<int64_t>(ids[k]) - id_base) & (key_lim - 1u) : key_lim;
-                key[k] = i < n ? kv : pad_key;
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < IPT; ++k) {
-                const int i = w * kWave * IPT + k * kWave + lane;
-                val[k] = static_cast<uint32_t>(i);
-                const int ic = i < n ? i : 0;
-                const int t = token_of_entry(ic, a.wr_magic);
-                const int j = ic - t * wr;
-                const int32_t* src = j < W ? a.k_idx + cw + t * W + j : a.q_idx + cr + t * R + (j - W);
-                const int64_t id = static_cast<int64_t>(*src);
-                const uint32_t kv = t < tv ? static_cast<uint32_t>(id - id_base) & (key_lim - 1u) : key_lim;
-                key[k] = i < n ? kv : pad_key;
-            }
+        for (int k = 0; k < IPT; ++k) {
+            const int i = w * kWave * IPT + k * kWave + lane;
+            const int t = token_of_entry(i < n ? i : 0, a.wr_magic);
+            const uint32_t kv =
+                t < tv ? static_cast<uint32_t>(static_cast<int64_t>(ids[k]) - id_base) & (key_lim - 1u) : key_lim;
+            key[k] = i < n ? kv : pad_key;
         }
         // Invalid entries need one more key bit only in a ragged chunk.
         block_radix_sort<IPT>(key, val, tv < C ? kb + 1 : kb, a.digit_bits, skey, sval, hist, wsum);
@@ -666,7 +650,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
         for (int T = 0; T < NTILE; ++T) {
             if (T >= ntiles) continue;
             // The values of this thread's entries in the tile and the ids of its K entries (for the
-            // mover-record slots), all loads in flight before the first use.
+            // mover-record slots), issued before the tile's recomputation (their waits fall at the
+            // first use, inside it).
             int32_t kid[kTileItems];
             float vl[kTileItems];
             {
@@ -680,11 +665,6 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                     const bool q = j >= W;
                     vl[k] = *(q ? a.q_val + cr + t * R + (j - W) : a.k_val + cw + t * W + j);
                     if constexpr (sk) kid[k] = a.k_idx[cw + ((!q && t < tv) ? t * W + j : 0)];
-                }
-#pragma unroll
-                for (int k = 0; k < kTileItems; ++k) {
-                    asm volatile("" ::"v"(vl[k]));
-                    if constexpr (sk) asm volatile("" ::"v"(kid[k]));
                 }
 #pragma unroll
                 for (int k = 0; k < kTileItems; ++k) {   // invalid tokens' values are not used
