@@ -126,8 +126,6 @@ sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st
     L.rec = static_cast<char*>(io->workspace) + ws.rec_off;
     L.inv_k = static_cast<char*>(io->workspace) + ws.inv_k_off;
     L.inv_q = static_cast<char*>(io->workspace) + ws.inv_q_off;
-    L.walk_k = static_cast<char*>(io->workspace) + ws.walk_k_off;
-    L.walk_q = static_cast<char*>(io->workspace) + ws.walk_q_off;
     L.hot = static_cast<char*>(io->workspace) + ws.hot_off;
     L.lds_max = lds_max;
     const hipError_t e = sdm::p1_launch(L, st);

@@ -56,12 +56,15 @@ constexpr uint32_t kMetaFirst = 1u << 28;
 constexpr int kMetaWalkShift = 29;
 constexpr uint32_t kMetaValid = 1u << 31;
 constexpr uint32_t kMetaPos = (1u << 14) - 1u;
+// Entry-order workspace word of the pair kernel: sorted position | kInvWalk when the entry starts
+// its token's run with earlier valid K entries in an ordinary (not hot) group.
+constexpr uint32_t kInvWalk = 1u << 15;
 
 // Entry-order destinations, kept in an LDS table from the kernel's start to the sweeps (their
 // kernel-argument copies would otherwise hold scalar registers through the sort and the scans).
 enum OutPtr : int {
-    kOLogK, kORex, kOCpe, kOKEff, kOIsLast, kOIsOnly, kOPosK, kOInvK, kOWalkK,
-    kOLogQ, kOQW, kOPosQ, kOQLast, kOQOnly, kOInvQ, kOWalkQ, kNumOut
+    kOLogK, kORex, kOCpe, kOKEff, kOIsLast, kOIsOnly, kOPosK, kOInvK,
+    kOLogQ, kOQW, kOPosQ, kOQLast, kOQOnly, kOInvQ, kNumOut
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -95,13 +98,10 @@ struct P1Args {
     int32_t* pos_q;
     int8_t* q_last;
     int8_t* q_only;
-    // pair-kernel workspace in entry order, per kind (NULL: no pair sums): sorted position of the
-    // entry, and its walk code (1: starts its token's run with earlier valid K entries in the
-    // group; 2: the same in a hot group)
+    // pair-kernel workspace in entry order, per kind (NULL: no pair sums): the entry's sorted
+    // position (bits 0-13) and kInvWalk where the pair kernel walks it
     uint16_t* inv_k;
     uint16_t* inv_q;
-    uint8_t* walk_k;
-    uint8_t* walk_q;
     int32_t* spay_k;
     int32_t* spay_q;
     int4* krec;
@@ -353,8 +353,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     for (int t = threadIdx.x; t < C; t += kNT) gates[t] = t < tv ? a.g[static_cast<int64_t>(c) * C + t] : 0.0f;
     if (threadIdx.x == 0) hot_n = 0u;
     {
-        const void* outs[kNumOut] = {a.log_k, a.rex, a.cpe, a.k_eff, a.is_last, a.is_only, a.pos_k, a.inv_k, a.walk_k,
-                                     a.log_q, a.q_w, a.pos_q, a.q_last, a.q_only, a.inv_q, a.walk_q};
+        const void* outs[kNumOut] = {a.log_k, a.rex, a.cpe, a.k_eff, a.is_last, a.is_only, a.pos_k, a.inv_k,
+                                     a.log_q, a.q_w, a.pos_q, a.q_last, a.q_only, a.inv_q};
 #pragma unroll
         for (int o = 0; o < kNumOut; ++o) {
             if (threadIdx.x == o) optr[o] = reinterpret_cast<uintptr_t>(outs[o]);
@@ -750,7 +750,6 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             void* const is_only = out_ptr(kOIsOnly, gb, 1);
             void* const pos_k = out_ptr(kOPosK, gb, 4);
             void* const inv_k = out_ptr(kOInvK, gb, 2);
-            void* const walk_k = out_ptr(kOWalkK, gb, 1);
             const bool vec = (a.vec & 1u) != 0u;
             for (int i0 = 4 * static_cast<int>(threadIdx.x); i0 < nke; i0 += 4 * kNT) {
                 const int cnt = min(4, nke - i0);
@@ -767,7 +766,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                 }
                 f32x4 cp, ke;
                 u32x4 ps;
-                uint32_t fl = 0u, fo = 0u, wk = 0u;
+                uint32_t fl = 0u, fo = 0u;
+                uint32_t iw[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const uint32_t m = M4[u];
@@ -778,7 +778,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                     const bool last = is_last_of(m);
                     fl |= (last ? 1u : 0u) << (8 * u);
                     fo |= ((last && (m & kMetaFirst)) ? 1u : 0u) << (8 * u);
-                    wk |= ((m >> kMetaWalkShift) & 3u) << (8 * u);
+                    iw[u] = (m & kMetaPos) | (((m >> kMetaWalkShift) & 3u) == 1u ? kInvWalk : 0u);
                 }
                 if (vec && cnt == 4) {
                     const uint32_t g4 = g / 4;
@@ -789,11 +789,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                     if (pos_k != nullptr) gstore<u32x4>(pos_k, g4, ps);
                     if (is_last != nullptr) gstore<uint32_t>(is_last, g4, fl);
                     if (is_only != nullptr) gstore<uint32_t>(is_only, g4, fo);
-                    if (inv_k != nullptr) {
-                        gstore<u32x2>(inv_k, g4, u32x2{(M4[0] & kMetaPos) | (M4[1] & kMetaPos) << 16,
-                                                      (M4[2] & kMetaPos) | (M4[3] & kMetaPos) << 16});
-                        gstore<uint32_t>(walk_k, g4, wk);
-                    }
+                    if (inv_k != nullptr) gstore<u32x2>(inv_k, g4, u32x2{iw[0] | iw[1] << 16, iw[2] | iw[3] << 16});
                 } else {
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
@@ -805,10 +801,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                         if (pos_k != nullptr) gstore<uint32_t>(pos_k, g + u, ps[u]);
                         if (is_last != nullptr) gstore<uint8_t>(is_last, g + u, static_cast<uint8_t>((fl >> (8 * u)) & 1u));
                         if (is_only != nullptr) gstore<uint8_t>(is_only, g + u, static_cast<uint8_t>((fo >> (8 * u)) & 1u));
-                        if (inv_k != nullptr) {
-                            gstore<uint16_t>(inv_k, g + u, static_cast<uint16_t>(M4[u] & kMetaPos));
-                            gstore<uint8_t>(walk_k, g + u, static_cast<uint8_t>((wk >> (8 * u)) & 3u));
-                        }
+                        if (inv_k != nullptr) gstore<uint16_t>(inv_k, g + u, static_cast<uint16_t>(iw[u]));
                     }
                 }
             }
@@ -821,7 +814,6 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             void* const q_last = out_ptr(kOQLast, gb, 1);
             void* const q_only = out_ptr(kOQOnly, gb, 1);
             void* const inv_q = out_ptr(kOInvQ, gb, 2);
-            void* const walk_q = out_ptr(kOWalkQ, gb, 1);
             const bool vec = (a.vec & 2u) != 0u;
             for (int i0 = 4 * static_cast<int>(threadIdx.x); i0 < nqe; i0 += 4 * kNT) {
                 const int cnt = min(4, nqe - i0);
@@ -837,7 +829,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                 }
                 f32x4 qw;
                 u32x4 ps;
-                uint32_t fl = 0u, fo = 0u, wk = 0u;
+                uint32_t fl = 0u, fo = 0u;
+                uint32_t iw[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const uint32_t m = M4[u];
@@ -847,7 +840,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                     const bool last = is_last_of(m);
                     fl |= (last ? 1u : 0u) << (8 * u);
                     fo |= ((last && (m & kMetaFirst)) ? 1u : 0u) << (8 * u);
-                    wk |= ((m >> kMetaWalkShift) & 3u) << (8 * u);
+                    iw[u] = (m & kMetaPos) | (((m >> kMetaWalkShift) & 3u) == 1u ? kInvWalk : 0u);
                 }
                 if (vec && cnt == 4) {
                     const uint32_t g4 = g / 4;
@@ -856,11 +849,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                     if (pos_q != nullptr) gstore<u32x4>(pos_q, g4, ps);
                     if (q_last != nullptr) gstore<uint32_t>(q_last, g4, fl);
                     if (q_only != nullptr) gstore<uint32_t>(q_only, g4, fo);
-                    if (inv_q != nullptr) {
-                        gstore<u32x2>(inv_q, g4, u32x2{(M4[0] & kMetaPos) | (M4[1] & kMetaPos) << 16,
-                                                      (M4[2] & kMetaPos) | (M4[3] & kMetaPos) << 16});
-                        gstore<uint32_t>(walk_q, g4, wk);
-                    }
+                    if (inv_q != nullptr) gstore<u32x2>(inv_q, g4, u32x2{iw[0] | iw[1] << 16, iw[2] | iw[3] << 16});
                 } else {
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
@@ -870,10 +859,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                         if (pos_q != nullptr) gstore<uint32_t>(pos_q, g + u, ps[u]);
                         if (q_last != nullptr) gstore<uint8_t>(q_last, g + u, static_cast<uint8_t>((fl >> (8 * u)) & 1u));
                         if (q_only != nullptr) gstore<uint8_t>(q_only, g + u, static_cast<uint8_t>((fo >> (8 * u)) & 1u));
-                        if (inv_q != nullptr) {
-                            gstore<uint16_t>(inv_q, g + u, static_cast<uint16_t>(M4[u] & kMetaPos));
-                            gstore<uint8_t>(walk_q, g + u, static_cast<uint8_t>((wk >> (8 * u)) & 3u));
-                        }
+                        if (inv_q != nullptr) gstore<uint16_t>(inv_q, g + u, static_cast<uint16_t>(iw[u]));
                     }
                 }
             }
@@ -919,10 +905,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
 // by the input (hot groups in position order, then the walks).
 struct PairArgs {
     const uint4* rec;
-    const uint16_t* inv_k;   // entry-order sorted positions and walk codes, per kind
+    const uint16_t* inv_k;   // entry-order sorted positions | kInvWalk, per kind
     const uint16_t* inv_q;
-    const uint8_t* walk_k;
-    const uint8_t* walk_q;
     const uint2* hot;   // per chunk: {count, 0}, then {head position, size} in position order (NULL: none)
     float* a;
     float* qk;
@@ -1204,63 +1188,78 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
         g0 = g1;
     }
 
-    // ---- Other groups: thread i walks its flagged runs back to the group head.
+    // ---- Other groups: thread i walks its flagged runs back to the group head. The entry words of
+    // 32 lanes are loaded together; a walk then loads the record window around its start (one
+    // record after, the own record, kWalkBatch before) in one go, which covers a small group.
     const int i = threadIdx.x;
     if (i < tv) {
         float* row = tri + i * (i + 1) / 2;
         const int lanes = q ? R : W;
-        const int64_t e0 = (static_cast<int64_t>(c) * C + i) * lanes;   // token i's first entry of the kind
-        const uint8_t* wf = (q ? a.walk_q : a.walk_k) + e0;
-        const uint16_t* iv = (q ? a.inv_q : a.inv_k) + e0;
+        const uint16_t* iv = (q ? a.inv_q : a.inv_k) + (static_cast<int64_t>(c) * C + i) * lanes;
         // Token i's entries of this kind: (Q flag, token) bits of the payload.
         const uint32_t own_tag = (q ? kIsQ : 0u) | (static_cast<uint32_t>(i) << kTokShift);
         const uint32_t tag_mask = kIsQ | (0xFFu << kTokShift);
         for (int lb = 0; lb < lanes; lb += 32) {
-          // The flags of up to 32 lanes, loaded together, then only the lanes walked here.
           uint32_t flags = 0;
 #pragma unroll
           for (int u = 0; u < 32; ++u) {
               const int ln = lb + u;
-              flags |= (ln < lanes && wf[min(ln, lanes - 1)] == 1) ? (1u << u) : 0u;
+              flags |= (ln < lanes && (iv[min(ln, lanes - 1)] & kInvWalk)) ? (1u << u) : 0u;
           }
           for (; flags != 0u; flags &= flags - 1u) {
             const int ln = lb + __builtin_ctz(flags);
-            const int rho = min(static_cast<int>(iv[ln]), n - 1);   // (a position < n; the clamp only guards)
-            const uint4 own = rec[rho];
-            // Sum the run's values.
+            // A walk start has an earlier entry in its group, so 1 <= rho (the clamp only guards).
+            const int rho = min(static_cast<int>(iv[ln] & (kInvWalk - 1u)), n - 1);
+            constexpr int kWin = kWalkBatch + 2;
+            uint4 rb[kWin];   // positions rho + 1, rho, rho - 1, ..., rho - kWalkBatch
+#pragma unroll
+            for (int k = 0; k < kWin; ++k) rb[k] = rec[min(max(rho + 1 - k, 0), n - 1)];
+            const uint4 own = rb[1];
+            // Sum the run's values (the run goes on past rho only for repeated lanes of the token).
             float wi = __uint_as_float(own.w);
-            for (int p = rho + 1; p < n; ++p) {
-                const uint4 nx = rec[p];
-                if ((nx.x & kHead) || (nx.x & tag_mask) != own_tag) break;
-                wi = wi + __uint_as_float(nx.w);
+            if (rho + 1 < n && !(rb[0].x & kHead) && (rb[0].x & tag_mask) == own_tag) {
+                wi = wi + __uint_as_float(rb[0].w);
+                for (int p = rho + 2; p < n; ++p) {
+                    const uint4 nx = rec[p];
+                    if ((nx.x & kHead) || (nx.x & tag_mask) != own_tag) break;
+                    wi = wi + __uint_as_float(nx.w);
+                }
             }
             const float se = __uint_as_float(own.y), ce = __uint_as_float(own.z);
             // Walk back to the head; the K runs of earlier tokens are summed, then one term each.
             int cur_j = -1;
             float kj = 0.0f, sj = 0.0f, cj = 0.0f;
             bool done = false;
-            for (int top = rho - 1; !done; top -= kWalkBatch) {
-                uint4 rb[kWalkBatch];
+            auto visit = [&](const uint4& r) {
+                const uint32_t px = r.x;
+                if (!(px & (kIsQ | kInvalid))) {
+                    const int jt = static_cast<int>((px >> kTokShift) & 0xFFu);
+                    if (jt != cur_j) {
+                        if (cur_j >= 0 && (q || cur_j != i)) {
+                            row[cur_j] = row[cur_j] + (wi * kj) * expf((se - sj) + (ce - cj));
+                        }
+                        cur_j = jt;
+                        kj = 0.0f;
+                        sj = __uint_as_float(r.y);
+                        cj = __uint_as_float(r.z);
+                    }
+                    kj = kj + __uint_as_float(r.w);
+                }
+                done = (px & kHead) != 0;
+            };
 #pragma unroll
-                for (int k = 0; k < kWalkBatch; ++k) rb[k] = rec[max(top - k, 0)];
+            for (int k = 2; k < kWin; ++k) {
+                if (done) break;
+                visit(rb[k]);
+            }
+            for (int top = rho - 1 - kWalkBatch; !done; top -= kWalkBatch) {
+                uint4 rc[kWalkBatch];
+#pragma unroll
+                for (int k = 0; k < kWalkBatch; ++k) rc[k] = rec[max(top - k, 0)];
 #pragma unroll
                 for (int k = 0; k < kWalkBatch; ++k) {
                     if (done) break;
-                    const uint32_t px = rb[k].x;
-                    if (!(px & (kIsQ | kInvalid))) {
-                        const int jt = static_cast<int>((px >> kTokShift) & 0xFFu);
-                        if (jt != cur_j) {
-                            if (cur_j >= 0 && (q || cur_j != i)) {
-                                row[cur_j] = row[cur_j] + (wi * kj) * expf((se - sj) + (ce - cj));
-                            }
-                            cur_j = jt;
-                            kj = 0.0f;
-                            sj = __uint_as_float(rb[k].y);
-                            cj = __uint_as_float(rb[k].z);
-                        }
-                        kj = kj + __uint_as_float(rb[k].w);
-                    }
-                    done = (px & kHead) != 0;
+                    visit(rc[k]);
                 }
             }
             if (cur_j >= 0 && (q || cur_j != i)) row[cur_j] = row[cur_j] + (wi * kj) * expf((se - sj) + (ce - cj));
@@ -1374,10 +1373,8 @@ P1Workspace p1_workspace_layout(const sdm_p1_shape* s) {
     w.rec_off = 0;
     w.inv_k_off = up(N * n * sizeof(uint4));
     w.inv_q_off = w.inv_k_off + up(nk * sizeof(uint16_t));
-    w.walk_k_off = w.inv_q_off + up(nq * sizeof(uint16_t));
-    w.walk_q_off = w.walk_k_off + up(nk);
     w.hot_cap = s->C * s->W / kHotMin;
-    w.hot_off = w.walk_q_off + up(nq);
+    w.hot_off = w.inv_q_off + up(nq * sizeof(uint16_t));
     w.total = w.hot_off + up(N * static_cast<size_t>(w.hot_cap + 1) * sizeof(uint2));
     return w;
 }
@@ -1415,8 +1412,6 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     a.q_only = io->q_only;
     a.inv_k = pairs ? static_cast<uint16_t*>(Lc.inv_k) : nullptr;
     a.inv_q = pairs ? static_cast<uint16_t*>(Lc.inv_q) : nullptr;
-    a.walk_k = pairs ? static_cast<uint8_t*>(Lc.walk_k) : nullptr;
-    a.walk_q = pairs ? static_cast<uint8_t*>(Lc.walk_q) : nullptr;
     // Four-entry vector stores where every row of the kind's fields is 16-byte aligned (4-byte for
     // the flag bytes; the workspace rows follow from C * W or C * R being a multiple of 4).
     auto al = [](const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & (m - 1)) == 0; };
@@ -1479,8 +1474,6 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     pa.rec = static_cast<const uint4*>(Lc.rec);
     pa.inv_k = static_cast<const uint16_t*>(Lc.inv_k);
     pa.inv_q = static_cast<const uint16_t*>(Lc.inv_q);
-    pa.walk_k = static_cast<const uint8_t*>(Lc.walk_k);
-    pa.walk_q = static_cast<const uint8_t*>(Lc.walk_q);
     pa.hot = static_cast<const uint2*>(Lc.hot);
     pa.hot_cap = hot_cap;
     pa.tab_cap = hot_on ? tab_cap : 0;

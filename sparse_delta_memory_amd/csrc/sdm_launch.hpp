@@ -20,18 +20,17 @@ struct P1Launch {
     const sdm_p1_shape* s;
     const sdm_p1_io* io;
     void* rec;        // [N, n] 16-byte records in sorted order: payload | head, log-cumsum (s, c), value
-    void* inv_k;      // [N, C*W] uint16 sorted position of every K entry (entry order)
+    void* inv_k;      // [N, C*W] uint16 per K entry (entry order): sorted position (bits 0-13), bit 15
+                      // where the entry starts its token's run with earlier valid K entries of an
+                      // ordinary (not hot) group
     void* inv_q;      // [N, C*R] the same for the Q entries
-    void* walk_k;     // [N, C*W] uint8, where a K entry starts its token's run with earlier K entries
-                      // of its group: 1 in an ordinary group, 2 in a hot one
-    void* walk_q;     // [N, C*R] the same for the Q entries
     void* hot;        // [N, hot_cap + 1] uint2: count, then {head position, size} of each hot group
     int lds_max;      // LDS bytes per block of the device
 };
 
 // Workspace layout of sdm_phase1: byte offsets of the regions and the total.
 struct P1Workspace {
-    size_t rec_off, inv_k_off, inv_q_off, walk_k_off, walk_q_off, hot_off, total;
+    size_t rec_off, inv_k_off, inv_q_off, hot_off, total;
     int hot_cap;      // hot groups a chunk can hold: C * W / kHotMin
 };
 P1Workspace p1_workspace_layout(const sdm_p1_shape* s);
