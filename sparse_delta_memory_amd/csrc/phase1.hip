@@ -57,8 +57,10 @@ constexpr int kMetaWalkShift = 29;
 constexpr uint32_t kMetaValid = 1u << 31;
 constexpr uint32_t kMetaPos = (1u << 14) - 1u;
 // Entry-order workspace word of the pair kernel: sorted position | kInvWalk when the entry starts
-// its token's run with earlier valid K entries in an ordinary (not hot) group.
+// its token's run with earlier valid K entries in an ordinary group, kInvHot when it does so in a
+// hot group (walked only if the pair kernel cannot sum that group densely).
 constexpr uint32_t kInvWalk = 1u << 15;
+constexpr uint32_t kInvHot = 1u << 14;
 
 // Entry-order destinations, kept in an LDS table from the kernel's start to the sweeps (their
 // kernel-argument copies would otherwise hold scalar registers through the sort and the scans).
@@ -778,7 +780,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                     const bool last = is_last_of(m);
                     fl |= (last ? 1u : 0u) << (8 * u);
                     fo |= ((last && (m & kMetaFirst)) ? 1u : 0u) << (8 * u);
-                    iw[u] = (m & kMetaPos) | (((m >> kMetaWalkShift) & 3u) == 1u ? kInvWalk : 0u);
+                    const uint32_t wc = (m >> kMetaWalkShift) & 3u;
+                    iw[u] = (m & kMetaPos) | (wc == 1u ? kInvWalk : 0u) | (wc == 2u ? kInvHot : 0u);
                 }
                 if (vec && cnt == 4) {
                     const uint32_t g4 = g / 4;
@@ -840,7 +843,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                     const bool last = is_last_of(m);
                     fl |= (last ? 1u : 0u) << (8 * u);
                     fo |= ((last && (m & kMetaFirst)) ? 1u : 0u) << (8 * u);
-                    iw[u] = (m & kMetaPos) | (((m >> kMetaWalkShift) & 3u) == 1u ? kInvWalk : 0u);
+                    const uint32_t wc = (m >> kMetaWalkShift) & 3u;
+                    iw[u] = (m & kMetaPos) | (wc == 1u ? kInvWalk : 0u) | (wc == 2u ? kInvHot : 0u);
                 }
                 if (vec && cnt == 4) {
                     const uint32_t g4 = g / 4;
@@ -897,12 +901,15 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
 // term per (group, run of token i, K run of token j): w_i * k_j * exp(L_i - L_j), the run sums w
 // and k taken over the run's values, L as the compensated pair (s, c).
 //
-// Hot groups (many K entries; listed by the sort/scan kernel) are summed densely: their runs are
-// gathered into LDS tables (K runs, and the runs of the block's kind as rows, each with the number
-// of K runs before it; L kept in base 2 as a compensated pair), then the threads that own row i
-// sweep, group after group, the K runs before each of row i's runs, each term one hardware exp2. The other groups are walked
-// by thread i from each flagged run back to the group's head. Terms reach a cell in an order fixed
-// by the input (hot groups in position order, then the walks).
+// Hot groups (many K entries; listed by the sort/scan kernel) are summed as a dense contraction. A
+// token has at most one run of each kind in a group, and earlier tokens come first in it, so a
+// group's terms are the lower triangle of the outer product x y^T with x[i] = w_i 2^(L_i - c) over
+// the row runs and y[j] = k_j 2^(c - L_j) over the K runs (L in base 2 as a compensated pair, c
+// the midpoint of the group's L range, so neither factor leaves the float range). A batch of hot
+// groups fills x and y tables in LDS; each thread then adds sum_g x_g y_g^T into its own 4 x 4
+// blocks of the triangle. A group whose L range is too wide for this is walked instead, as are the
+// other groups: thread i walks each flagged run back to the group's head. Terms reach a cell in an
+// order fixed by the input (hot batches in position order, then the walks).
 struct PairArgs {
     const uint4* rec;
     const uint16_t* inv_k;   // entry-order sorted positions | kInvWalk, per kind
@@ -910,33 +917,40 @@ struct PairArgs {
     const uint2* hot;   // per chunk: {count, 0}, then {head position, size} in position order (NULL: none)
     float* a;
     float* qk;
-    int C, W, R, first_partial, valid_last, hot_cap, tab_cap;
+    int C, W, R, first_partial, valid_last, hot_cap;
+    int gb;             // hot groups per batch (x and y tables in LDS); 0: hot groups off
 };
 
 // Threads per pair block: 512, or 1024 where the LDS allows one block per compute unit anyway.
 constexpr float kLog2E = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
 constexpr size_t kPairStaticLds = 256;   // room left for the kernel's static LDS (scan partials)
 constexpr int kWalkBatch = 8;
 
-// Hot groups per batch (a group bit in one 32-bit mask per token).
+// Hot groups per batch at most.
 constexpr int kPairBatchGroups = 32;
+// A hot group whose L range (base 2) exceeds this is walked: the factors 2^(+-range/2) stay finite.
+constexpr float kDenseRange = 200.0f;
+constexpr uint32_t kHotWide = 0x80000000u;   // in a hot-list size word: the group is walked
 
-// LDS of the pair kernel: the triangle, the hot list, per-group table bases, per-token group
-// masks, per-group token bitmaps, the two run tables.
+// LDS of the pair kernel: the triangle, the hot list (+ batch bounds), per batch group its first
+// batch position, its reference c and its 4-token block masks (x, y), then the x and y tables
+// (gb groups of Cp = C rounded up to 4 floats each).
 struct PairLds {
-    size_t tri, hot, gbase, tmask, pres, ktab, rtab, total;
+    size_t tri, hot, gbase, gref, bmask, xt, yt, total;
 };
-__host__ __device__ inline PairLds pair_lds_layout(int C, int hot_cap, int tab_cap) {
+__host__ __device__ inline PairLds pair_lds_layout(int C, int hot_cap, int gb) {
     auto up = [](size_t b) { return (b + 15) / 16 * 16; };
+    const size_t cp = static_cast<size_t>((C + 3) & ~3);
     PairLds l;
     l.tri = 0;
     l.hot = up(static_cast<size_t>(C) * (C + 1) / 2 * sizeof(float));
     l.gbase = l.hot + up(static_cast<size_t>(hot_cap) * 2 * sizeof(uint32_t) + 16);   // + batch bounds
-    l.tmask = l.gbase + up(static_cast<size_t>(kPairBatchGroups + 1) * 3 * sizeof(uint32_t));
-    l.pres = l.tmask + up(static_cast<size_t>(C) * sizeof(uint32_t));
-    l.ktab = l.pres + static_cast<size_t>(kPairBatchGroups) * 8 * sizeof(uint32_t);
-    l.rtab = l.ktab + static_cast<size_t>(tab_cap) * 16;
-    l.total = l.rtab + static_cast<size_t>(tab_cap) * 16;
+    l.gref = l.gbase + up(static_cast<size_t>(kPairBatchGroups + 1) * sizeof(uint32_t));
+    l.bmask = l.gref + up(static_cast<size_t>(kPairBatchGroups) * sizeof(float));
+    l.xt = l.bmask + static_cast<size_t>(kPairBatchGroups) * 4 * sizeof(uint32_t);
+    l.yt = l.xt + static_cast<size_t>(gb) * cp * sizeof(float);
+    l.total = l.yt + static_cast<size_t>(gb) * cp * sizeof(float);
     return l;
 }
 
@@ -952,54 +966,85 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
     const int wr = W + R;
     const int n = C * wr;
     const int tv = c >= a.first_partial ? a.valid_last : C;
-    const PairLds lay = pair_lds_layout(C, a.hot_cap, a.tab_cap);
+    const PairLds lay = pair_lds_layout(C, a.hot_cap, a.gb);
+    const int cp = (C + 3) & ~3;
     float* tri = reinterpret_cast<float*>(smem + lay.tri);
     uint2* hl = reinterpret_cast<uint2*>(smem + lay.hot);               // hot list of the chunk
-    int* bounds = reinterpret_cast<int*>(smem + lay.hot) + 2 * a.hot_cap;   // batch end, positions
+    int* bounds = reinterpret_cast<int*>(smem + lay.hot) + 2 * a.hot_cap;   // batch end, positions, any wide
     uint32_t* ubase = reinterpret_cast<uint32_t*>(smem + lay.gbase);    // batch-local first position
-    uint32_t* gk = ubase + (kPairBatchGroups + 1);                       // first K-run index per group
-    uint32_t* gr = gk + (kPairBatchGroups + 1);                          // first row-run index per group
-    uint32_t* tmask = reinterpret_cast<uint32_t*>(smem + lay.tmask);     // batch groups with a row run of token t
-    uint32_t* pres = reinterpret_cast<uint32_t*>(smem + lay.pres);       // per group: tokens with a row run
-    uint4* ktab = reinterpret_cast<uint4*>(smem + lay.ktab);
-    uint4* rtab = reinterpret_cast<uint4*>(smem + lay.rtab);
+    float* gref = reinterpret_cast<float*>(smem + lay.gref);            // reference c per batch group
+    uint32_t* bmask = reinterpret_cast<uint32_t*>(smem + lay.bmask);    // per group: x blocks (2 words), y blocks (2)
+    float* xt = reinterpret_cast<float*>(smem + lay.xt);
+    float* yt = reinterpret_cast<float*>(smem + lay.yt);
     const int tri_size = C * (C + 1) / 2;
     for (int e = threadIdx.x; e < tri_size; e += kPairThreads) tri[e] = 0.0f;
     const int64_t crow = static_cast<int64_t>(c) * n;
     const uint4* rec = a.rec + crow;
     const uint32_t row_q = q ? kIsQ : 0u;
-    const int lane = static_cast<int>(lane_id());
-    const int wave = threadIdx.x / kWave;
 
-    // ---- Hot groups, in batches whose runs fit the tables.
+    // ---- Hot groups, in batches of at most gb groups.
     const int nh = a.hot != nullptr ? static_cast<int>(a.hot[static_cast<int64_t>(c) * (a.hot_cap + 1)].x) : 0;
     if (nh > 0) {
         const uint2* hsrc = a.hot + static_cast<int64_t>(c) * (a.hot_cap + 1) + 1;
         for (int g = threadIdx.x; g < nh; g += kPairThreads) hl[g] = hsrc[g];
     }
+    if (threadIdx.x == 0) bounds[2] = 0;   // any group walked instead
     __syncthreads();
+    // L of a record in base 2 as a compensated pair: hi = s log2(e), lo = the product's rounding
+    // error plus c log2(e). Sums and differences of such pairs keep the exponent accurate.
+    auto l2pair = [](const uint4& r, float& hi, float& lo) {
+        const float ls = __uint_as_float(r.y), lc = __uint_as_float(r.z);
+        hi = ls * kLog2E;
+        lo = fmaf(ls, kLog2E, -hi) + lc * kLog2E;
+    };
+    // 2^(hi + lo - c) to about two ulps: hi - c is split exactly (TwoSum) into its rounded value d,
+    // whose power of two the hardware takes, and an error that joins lo in a first-order factor
+    // (|err + lo| is below an ulp of hi).
+    auto pow2 = [](float hi, float lo, float cg) {
+        const float d = hi - cg;
+        const float bb = d - hi;
+        const float err = (hi - (d - bb)) + (-cg - bb);
+        return __builtin_amdgcn_exp2f(d) * fmaf(err + lo, kLn2, 1.0f);
+    };
     for (int g0 = 0; g0 < nh;) {
-        if (threadIdx.x == 0) {   // the batch: groups g0 .. g1-1, at most tab_cap runs of each table
-            int g1 = g0, runs = 0;
+        if (threadIdx.x == 0) {   // the batch: groups g0 .. g1-1
+            const int g1 = min(nh, g0 + a.gb);
             uint32_t pos = 0;
-            while (g1 < nh) {
-                const int r = min(static_cast<int>(hl[g1].y), C);   // runs of one kind in a group <= tokens
-                if (g1 > g0 && (runs + r > a.tab_cap || g1 - g0 == kPairBatchGroups)) break;
-                ubase[g1 - g0] = pos;
-                pos += hl[g1].y;
-                runs += r;
-                ++g1;
+            for (int g = g0; g < g1; ++g) {
+                ubase[g - g0] = pos;
+                pos += hl[g].y & ~kHotWide;
             }
             ubase[g1 - g0] = pos;
             bounds[0] = g1;
             bounds[1] = static_cast<int>(pos);
         }
+        if (threadIdx.x < kPairBatchGroups) {   // the batch group's reference c and range check
+            const int gg = threadIdx.x;
+            if (g0 + gg < nh && gg < a.gb) {
+                const int head = static_cast<int>(hl[g0 + gg].x);
+                const int last = head + static_cast<int>(hl[g0 + gg].y & ~kHotWide) - 1;
+                float h0, l0, h1, l1;
+                l2pair(rec[head], h0, l0);
+                l2pair(rec[last], h1, l1);
+                gref[gg] = 0.5f * (h0 + h1);
+                if (fabsf(h0 - h1) > kDenseRange) {
+                    hl[g0 + gg].y |= kHotWide;
+                    bounds[2] = 1;
+                }
+            }
+#pragma unroll
+            for (int w = 0; w < 4; ++w) bmask[gg * 4 + w] = 0u;
+        }
+        for (int e = threadIdx.x; e < a.gb * cp; e += kPairThreads) {
+            xt[e] = 0.0f;
+            yt[e] = 0.0f;
+        }
         __syncthreads();
         const int g1 = bounds[0];
         const int np = bounds[1];
         const int ng = g1 - g0;
-        // Thread x takes the batch positions [u0, u1) (group by group); run starts are counted, then
-        // numbered with one block scan, then written.
+        // Thread x takes the batch positions [u0, u1) (group by group) and writes the x (y) entry of
+        // every row (K) run that starts there: the run's value sum times 2^(L - c) (2^(c - L)).
         const int per = (np + kPairThreads - 1) / kPairThreads;
         const int u0 = min(np, static_cast<int>(threadIdx.x) * per), u1 = min(np, u0 + per);
         int g = 0;
@@ -1017,7 +1062,7 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
             cu.gstart = static_cast<int>(ubase[gg]);
             cu.gnext = static_cast<int>(ubase[gg + 1]);
             cu.ghead = static_cast<int>(hl[g0 + gg].x);
-            cu.gend = cu.ghead + static_cast<int>(hl[g0 + gg].y);
+            cu.gend = cu.ghead + static_cast<int>(hl[g0 + gg].y & ~kHotWide);
             return cu;
         };
         auto window = [&](int ub, int cnt, Cursor& cu, int (&rho)[kWin], bool (&fst)[kWin], int (&grp)[kWin],
@@ -1032,45 +1077,8 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
                 gend[b] = cu.gend;
             }
         };
-        for (int t = threadIdx.x; t < C; t += kPairThreads) tmask[t] = 0u;
-        for (int t = threadIdx.x; t < kPairBatchGroups * 8; t += kPairThreads) pres[t] = 0u;
-        uint32_t counts = 0;   // K-run starts | row-run starts << 16
         {
             Cursor cu = cursor_at(g);
-            uint32_t prev = 0xFFFFFFFFu;
-            for (int ub = u0; ub < u1; ub += kWin) {
-                const int cnt = min(kWin, u1 - ub);
-                int rho[kWin], grp[kWin], gend[kWin];
-                bool fst[kWin];
-                window(ub, cnt, cu, rho, fst, grp, gend);
-                uint32_t x[kWin];
-#pragma unroll
-                for (int b = 0; b < kWin; ++b) x[b] = rec[rho[b]].x;
-                if (prev == 0xFFFFFFFFu && !fst[0]) prev = rec[rho[0] - 1].x;
-#pragma unroll
-                for (int b = 0; b < kWin; ++b) {
-                    if (b >= cnt) break;
-                    const bool cont = !fst[b] && (prev & kTag) == (x[b] & kTag);
-                    counts += (!(x[b] & kIsQ) && !cont) ? 1u : 0u;
-                    counts += ((x[b] & kIsQ) == row_q && !cont) ? (1u << 16) : 0u;
-                    prev = x[b];
-                }
-            }
-        }
-        __shared__ uint32_t psum[kPairWaves];
-        uint32_t incl = counts;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const uint32_t o = __shfl_up(incl, d, kWave);
-            if (lane >= d) incl += o;
-        }
-        if (lane == kWave - 1) psum[wave] = incl;
-        __syncthreads();
-        uint32_t base = incl - counts;
-        for (int w = 0; w < wave; ++w) base += psum[w];
-        {
-            Cursor cu = cursor_at(g);
-            uint32_t kx = base & 0xFFFFu, rx = base >> 16;
             uint32_t prev = 0xFFFFFFFFu;
             for (int ub = u0; ub < u1; ub += kWin) {
                 const int cnt = min(kWin, u1 - ub);
@@ -1110,76 +1118,68 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
 #pragma unroll
                 for (int b = 0; b < kWin; ++b) {
                     if (b >= cnt) break;
-                    if (fst[b]) {   // group bases (the thread holding a group's first position)
-                        gk[grp[b]] = kx;
-                        gr[grp[b]] = rx;
-                    }
                     const bool cont = !fst[b] && (prev & kTag) == (r[b].x & kTag);
                     prev = r[b].x;
-                    if (cont) continue;
+                    if (cont || (hl[g0 + grp[b]].y & kHotWide)) continue;
                     const bool is_k = !(r[b].x & kIsQ), is_row = (r[b].x & kIsQ) == row_q;
                     const uint32_t tok = (r[b].x >> kTokShift) & 0xFFu;
-                    // L in base 2 as a compensated pair: hi = s log2(e), lo = the product's rounding error
-                    // plus c log2(e). Differences of such pairs keep the exponent as accurate as (s, c).
-                    const float ls = __uint_as_float(r[b].y), lc = __uint_as_float(r[b].z);
-                    const float l2hi = ls * kLog2E;
-                    const float l2lo = fmaf(ls, kLog2E, -l2hi) + lc * kLog2E;
+                    float hi, lo;
+                    l2pair(r[b], hi, lo);
+                    const float cg = gref[grp[b]];
+                    uint32_t* bm = bmask + grp[b] * 4;
                     if (is_row) {
-                        rtab[rx] = make_uint4(tok | (kx << 8), __float_as_uint(suf[b]), __float_as_uint(l2hi),
-                                              __float_as_uint(l2lo));
-                        atomicOr(tmask + tok, 1u << grp[b]);
-                        atomicOr(pres + grp[b] * 8 + (tok >> 5), 1u << (tok & 31u));
+                        xt[grp[b] * cp + tok] = suf[b] * pow2(hi, lo, cg);
+                        atomicOr(bm + (tok >> 7), 1u << ((tok >> 2) & 31u));
                     }
-                    if (is_k) ktab[kx] = make_uint4(tok, __float_as_uint(suf[b]), __float_as_uint(l2hi), __float_as_uint(l2lo));
-                    kx += is_k ? 1u : 0u;
-                    rx += is_row ? 1u : 0u;
+                    if (is_k) {
+                        yt[grp[b] * cp + tok] = suf[b] * pow2(-hi, -lo, -cg);
+                        atomicOr(bm + 2 + (tok >> 7), 1u << ((tok >> 2) & 31u));
+                    }
                 }
             }
         }
-        if (threadIdx.x == kPairThreads - 1) {   // end bases: the batch totals
-            gk[ng] = (base & 0xFFFFu) + (counts & 0xFFFFu);
-            gr[ng] = (base >> 16) + (counts >> 16);
-        }
         __syncthreads();
-        // Dense terms: kRowThreads threads own row i across every group of the batch (no barrier
-        // between groups), each taking every kRowThreads-th K run of the row run's prefix,
-        // kColBlock at a time (table reads, then cell reads, then cell writes: the cells of a block
-        // are distinct, a group holding one K run per token). A row run's table index is its
-        // group's first row index plus the group's row tokens below i.
-        constexpr int kRowThreads = kPairThreads / 256, kColBlock = 8;
-        for (int i = static_cast<int>(threadIdx.x) / kRowThreads; i < tv; i += kPairThreads / kRowThreads) {
-            const int sub = static_cast<int>(threadIdx.x) % kRowThreads;
-            float* row = tri + i * (i + 1) / 2;
-            for (uint32_t gm = tmask[i]; gm != 0u; gm &= gm - 1u) {
-                const int gg = __builtin_ctz(gm);
-                const uint32_t* pg = pres + gg * 8;
-                int below = 0;
+        // Each thread owns 4 x 4 blocks (bi >= bj) of the triangle and adds sum_g x_g y_g^T into them,
+        // skipping groups with no row run in the block's rows or no K run in its columns.
+        {
+            const int nbr = (C + 3) >> 2;
+            const int nblk = nbr * (nbr + 1) / 2;
+            for (int blk = threadIdx.x; blk < nblk; blk += kPairThreads) {
+                int bi = static_cast<int>((sqrtf(8.0f * static_cast<float>(blk) + 1.0f) - 1.0f) * 0.5f);
+                while (bi * (bi + 1) / 2 > blk) --bi;
+                while ((bi + 1) * (bi + 2) / 2 <= blk) ++bi;
+                const int bj = blk - bi * (bi + 1) / 2;
+                float acc[4][4];
 #pragma unroll
-                for (int wd = 0; wd < 8; ++wd) {
-                    const uint32_t bits = pg[wd];
-                    const int lo = wd * 32;
-                    below += i >= lo + 32 ? __popc(bits) : (i > lo ? __popc(bits & ((1u << (i - lo)) - 1u)) : 0);
+                for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[u][v] = 0.0f;
                 }
-                const uint32_t kb = gk[gg];
-                const uint4 me = rtab[gr[gg] + below];
-                const int ncol = static_cast<int>((me.x >> 8) - kb);
-                const float wi = __uint_as_float(me.y), hi_i = __uint_as_float(me.z), lo_i = __uint_as_float(me.w);
-                for (int c0 = sub; c0 < ncol; c0 += kRowThreads * kColBlock) {
-                    uint4 kt[kColBlock];
+                bool any = false;
+                for (int gg = 0; gg < ng; ++gg) {
+                    const uint32_t* bm = bmask + gg * 4;
+                    if (!((bm[bi >> 5] >> (bi & 31)) & 1u) || !((bm[2 + (bj >> 5)] >> (bj & 31)) & 1u)) continue;
+                    any = true;
+                    const float4 x4 = *reinterpret_cast<const float4*>(xt + gg * cp + 4 * bi);
+                    const float4 y4 = *reinterpret_cast<const float4*>(yt + gg * cp + 4 * bj);
+                    const float xs[4] = {x4.x, x4.y, x4.z, x4.w}, ys[4] = {y4.x, y4.y, y4.z, y4.w};
 #pragma unroll
-                    for (int b = 0; b < kColBlock; ++b) kt[b] = ktab[kb + min(c0 + b * kRowThreads, ncol - 1)];
-                    float term[kColBlock], cell[kColBlock];
+                    for (int u = 0; u < 4; ++u) {
 #pragma unroll
-                    for (int b = 0; b < kColBlock; ++b) {
-                        // exp(L_i - L_j) = 2^((hi_i - hi_j) + (lo_i - lo_j)); the exponent is <= 0 for
-                        // log-sigmoid gates, and underflow to 0 only drops terms below 2^-126.
-                        term[b] = (wi * __uint_as_float(kt[b].y)) *
-                                  __builtin_amdgcn_exp2f((hi_i - __uint_as_float(kt[b].z)) + (lo_i - __uint_as_float(kt[b].w)));
-                        cell[b] = row[kt[b].x];
+                        for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(xs[u], ys[v], acc[u][v]);
                     }
+                }
+                if (!any) continue;
 #pragma unroll
-                    for (int b = 0; b < kColBlock; ++b) {
-                        if (c0 + b * kRowThreads < ncol) row[kt[b].x] = cell[b] + term[b];
+                for (int u = 0; u < 4; ++u) {
+                    const int ii = 4 * bi + u;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int jj = 4 * bj + v;
+                        if (ii < C && (q ? jj <= ii : jj < ii)) {
+                            float* cell = tri + ii * (ii + 1) / 2 + jj;
+                            *cell = *cell + acc[u][v];
+                        }
                     }
                 }
             }
@@ -1187,6 +1187,7 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
         __syncthreads();   // the tables are rebuilt for the next batch
         g0 = g1;
     }
+    const bool any_wide = bounds[2] != 0;   // (set before the last barrier)
 
     // ---- Other groups: thread i walks its flagged runs back to the group head. The entry words of
     // 32 lanes are loaded together; a walk then loads the record window around its start (one
@@ -1201,15 +1202,25 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
         const uint32_t tag_mask = kIsQ | (0xFFu << kTokShift);
         for (int lb = 0; lb < lanes; lb += 32) {
           uint32_t flags = 0;
+          const uint32_t walk_bits = any_wide ? (kInvWalk | kInvHot) : kInvWalk;
 #pragma unroll
           for (int u = 0; u < 32; ++u) {
               const int ln = lb + u;
-              flags |= (ln < lanes && (iv[min(ln, lanes - 1)] & kInvWalk)) ? (1u << u) : 0u;
+              flags |= (ln < lanes && (iv[min(ln, lanes - 1)] & walk_bits)) ? (1u << u) : 0u;
           }
           for (; flags != 0u; flags &= flags - 1u) {
             const int ln = lb + __builtin_ctz(flags);
+            const uint32_t word = iv[ln];
             // A walk start has an earlier entry in its group, so 1 <= rho (the clamp only guards).
-            const int rho = min(static_cast<int>(iv[ln] & (kInvWalk - 1u)), n - 1);
+            const int rho = min(static_cast<int>(word & kMetaPos), n - 1);
+            if (word & kInvHot) {   // a hot group's run: walked only if its group was too wide
+                int lo_g = 0, hi_g = nh - 1;   // the last hot group with head <= rho
+                while (lo_g < hi_g) {
+                    const int mid = (lo_g + hi_g + 1) >> 1;
+                    if (static_cast<int>(hl[mid].x) <= rho) lo_g = mid; else hi_g = mid - 1;
+                }
+                if (!(hl[lo_g].y & kHotWide)) continue;
+            }
             constexpr int kWin = kWalkBatch + 2;
             uint4 rb[kWin];   // positions rho + 1, rho, rho - 1, ..., rho - kWalkBatch
 #pragma unroll
@@ -1427,17 +1438,17 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     a.tiles_k = io->tiles_k;
     a.repeats = io->repeats;
     a.rec = pairs ? static_cast<uint4*>(Lc.rec) : nullptr;
-    // Hot groups only when the pair kernel's run tables (at least C runs of each kind) fit in LDS.
+    // Hot groups only when the pair kernel's x and y tables hold at least 4 groups beside the rest.
+    // Groups per batch: as many as the blocks per compute unit that 4 groups allow still fit.
     const int hot_cap = s->C * s->W / kHotMin;
-    // Table capacity: as large as the blocks per compute unit that the smallest tables (C runs of
-    // each kind) allow still fit; at least C when hot groups are on.
     const size_t pair_fixed = pair_lds_layout(s->C, hot_cap, 0).total + kPairStaticLds;
-    const size_t pair_min = pair_fixed + static_cast<size_t>(s->C) * 32;
+    const size_t per_group = 2 * static_cast<size_t>((s->C + 3) & ~3) * sizeof(float);
+    const size_t pair_min = pair_fixed + 4 * per_group;
     const int blocks_cu = pair_min <= static_cast<size_t>(Lc.lds_max) ? static_cast<int>(Lc.lds_max / pair_min) : 0;
-    const int tab_cap = blocks_cu > 0
-                            ? min(4096, static_cast<int>((static_cast<size_t>(Lc.lds_max) / blocks_cu - pair_fixed) / 32))
-                            : 0;
-    const bool hot_on = pairs && hot_cap > 0 && tab_cap >= s->C;
+    const int gb = blocks_cu > 0 ? min(kPairBatchGroups,
+                                       static_cast<int>((static_cast<size_t>(Lc.lds_max) / blocks_cu - pair_fixed) / per_group))
+                                 : 0;
+    const bool hot_on = pairs && hot_cap > 0 && gb >= 4;
     a.hot = pairs ? static_cast<uint2*>(Lc.hot) : nullptr;
     a.hot_min = hot_on ? kHotMin : 0x7FFFFFFF;
     a.hot_cap = hot_cap;
@@ -1476,7 +1487,7 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     pa.inv_q = static_cast<const uint16_t*>(Lc.inv_q);
     pa.hot = static_cast<const uint2*>(Lc.hot);
     pa.hot_cap = hot_cap;
-    pa.tab_cap = hot_on ? tab_cap : 0;
+    pa.gb = hot_on ? gb : 0;
     pa.a = io->a;
     pa.qk = io->qk;
     pa.C = s->C;
@@ -1491,7 +1502,7 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
         if ((e = hipStreamWaitEvent(io->pair_stream, io->pair_ready, 0)) != hipSuccess) return e;
         pst = io->pair_stream;
     }
-    const size_t lds = pair_lds_layout(s->C, hot_cap, pa.tab_cap).total;
+    const size_t lds = pair_lds_layout(s->C, hot_cap, pa.gb).total;
     const int threads = blocks_cu == 1 ? 1024 : 512;
     const void* fn = threads == 1024 ? reinterpret_cast<const void*>(&p1_pairs_kernel<1024>)
                                      : reinterpret_cast<const void*>(&p1_pairs_kernel<512>);

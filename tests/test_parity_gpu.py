@@ -156,11 +156,13 @@ def test_masked_tokens_do_not_leak():
     dict(C=256, W=8, R=8, S=48, P=1, steps=1, vl=None),
     # Hot groups in 512-thread pair blocks (C = 120), a ragged last chunk.
     dict(C=120, W=16, R=4, S=70, P=2, steps=1, vl=100),
+    # Hot groups whose log-cumsum spans more than the dense pass takes (gates near -4): walked.
+    dict(C=256, W=8, R=8, S=48, P=1, steps=1, vl=None, gmu=-4.0),
 ])
 def test_edge_shapes(case):
     sh = W.Shape("edge", P=case["P"], T=case["C"] * case["steps"], C=case["C"], W=case["W"], R=case["R"],
                  S=case["S"], hd=case.get("hd", 64), bank_dtype=case.get("bank", "f32"), dv_dtype="f32",
-                 slots="uniform", valid_last=case["vl"])
+                 slots="uniform", valid_last=case["vl"], gate_mu=case.get("gmu", 2.0))
     wl = W.make(sh, seed=777)
     say("edge shape", case)
     shape, out = H.run_phase1(wl)
