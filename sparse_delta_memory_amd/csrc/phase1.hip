@@ -933,9 +933,9 @@ constexpr int kPairBatchGroups = 32;
 constexpr float kDenseRange = 200.0f;
 constexpr uint32_t kHotWide = 0x80000000u;   // in a hot-list size word: the group is walked
 
-// LDS of the pair kernel: the triangle, the hot list (+ batch bounds), per batch group its first
-// batch position, its reference c and its 4-token block masks (x, y), then the x and y tables
-// (gb groups of Cp = C rounded up to 4 floats each).
+// LDS of the pair kernel: the triangle, the hot list (+ batch bounds), the reference c of every
+// hot group, per batch group its first batch position and its 4-token block masks (x, y), then
+// the x and y tables (gb groups of Cp = C rounded up to 4 floats each).
 struct PairLds {
     size_t tri, hot, gbase, gref, bmask, xt, yt, total;
 };
@@ -945,9 +945,9 @@ __host__ __device__ inline PairLds pair_lds_layout(int C, int hot_cap, int gb) {
     PairLds l;
     l.tri = 0;
     l.hot = up(static_cast<size_t>(C) * (C + 1) / 2 * sizeof(float));
-    l.gbase = l.hot + up(static_cast<size_t>(hot_cap) * 2 * sizeof(uint32_t) + 16);   // + batch bounds
-    l.gref = l.gbase + up(static_cast<size_t>(kPairBatchGroups + 1) * sizeof(uint32_t));
-    l.bmask = l.gref + up(static_cast<size_t>(kPairBatchGroups) * sizeof(float));
+    l.gref = l.hot + up(static_cast<size_t>(hot_cap) * 2 * sizeof(uint32_t) + 16);   // + batch bounds
+    l.gbase = l.gref + up(static_cast<size_t>(hot_cap) * sizeof(float));
+    l.bmask = l.gbase + up(static_cast<size_t>(kPairBatchGroups + 1) * sizeof(uint32_t));
     l.xt = l.bmask + static_cast<size_t>(kPairBatchGroups) * 4 * sizeof(uint32_t);
     l.yt = l.xt + static_cast<size_t>(gb) * cp * sizeof(float);
     l.total = l.yt + static_cast<size_t>(gb) * cp * sizeof(float);
@@ -972,7 +972,7 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
     uint2* hl = reinterpret_cast<uint2*>(smem + lay.hot);               // hot list of the chunk
     int* bounds = reinterpret_cast<int*>(smem + lay.hot) + 2 * a.hot_cap;   // batch end, positions, any wide
     uint32_t* ubase = reinterpret_cast<uint32_t*>(smem + lay.gbase);    // batch-local first position
-    float* gref = reinterpret_cast<float*>(smem + lay.gref);            // reference c per batch group
+    float* gref = reinterpret_cast<float*>(smem + lay.gref);            // reference c per hot group
     uint32_t* bmask = reinterpret_cast<uint32_t*>(smem + lay.bmask);    // per group: x blocks (2 words), y blocks (2)
     float* xt = reinterpret_cast<float*>(smem + lay.xt);
     float* yt = reinterpret_cast<float*>(smem + lay.yt);
@@ -984,12 +984,6 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
 
     // ---- Hot groups, in batches of at most gb groups.
     const int nh = a.hot != nullptr ? static_cast<int>(a.hot[static_cast<int64_t>(c) * (a.hot_cap + 1)].x) : 0;
-    if (nh > 0) {
-        const uint2* hsrc = a.hot + static_cast<int64_t>(c) * (a.hot_cap + 1) + 1;
-        for (int g = threadIdx.x; g < nh; g += kPairThreads) hl[g] = hsrc[g];
-    }
-    if (threadIdx.x == 0) bounds[2] = 0;   // any group walked instead
-    __syncthreads();
     // L of a record in base 2 as a compensated pair: hi = s log2(e), lo = the product's rounding
     // error plus c log2(e). Sums and differences of such pairs keep the exponent accurate.
     auto l2pair = [](const uint4& r, float& hi, float& lo) {
@@ -997,6 +991,24 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
         hi = ls * kLog2E;
         lo = fmaf(ls, kLog2E, -hi) + lc * kLog2E;
     };
+    if (threadIdx.x == 0) bounds[2] = 0;   // any group walked instead
+    __syncthreads();
+    if (nh > 0) {   // the hot list, each group's reference c (its L range's midpoint) and range check
+        const uint2* hsrc = a.hot + static_cast<int64_t>(c) * (a.hot_cap + 1) + 1;
+        for (int g = threadIdx.x; g < nh; g += kPairThreads) {
+            uint2 h = hsrc[g];
+            float h0, l0, h1, l1;
+            l2pair(rec[h.x], h0, l0);
+            l2pair(rec[h.x + h.y - 1u], h1, l1);
+            gref[g] = 0.5f * (h0 + h1);
+            if (fabsf(h0 - h1) > kDenseRange) {
+                h.y |= kHotWide;
+                bounds[2] = 1;
+            }
+            hl[g] = h;
+        }
+    }
+    __syncthreads();
     // 2^(hi + lo - c) to about two ulps: hi - c is split exactly (TwoSum) into its rounded value d,
     // whose power of two the hardware takes, and an error that joins lo in a first-order factor
     // (|err + lo| is below an ulp of hi).
@@ -1018,22 +1030,9 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
             bounds[0] = g1;
             bounds[1] = static_cast<int>(pos);
         }
-        if (threadIdx.x < kPairBatchGroups) {   // the batch group's reference c and range check
-            const int gg = threadIdx.x;
-            if (g0 + gg < nh && gg < a.gb) {
-                const int head = static_cast<int>(hl[g0 + gg].x);
-                const int last = head + static_cast<int>(hl[g0 + gg].y & ~kHotWide) - 1;
-                float h0, l0, h1, l1;
-                l2pair(rec[head], h0, l0);
-                l2pair(rec[last], h1, l1);
-                gref[gg] = 0.5f * (h0 + h1);
-                if (fabsf(h0 - h1) > kDenseRange) {
-                    hl[g0 + gg].y |= kHotWide;
-                    bounds[2] = 1;
-                }
-            }
+        if (threadIdx.x < kPairBatchGroups) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) bmask[gg * 4 + w] = 0u;
+            for (int w = 0; w < 4; ++w) bmask[threadIdx.x * 4 + w] = 0u;
         }
         for (int e = threadIdx.x; e < a.gb * cp; e += kPairThreads) {
             xt[e] = 0.0f;
@@ -1125,7 +1124,7 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
                     const uint32_t tok = (r[b].x >> kTokShift) & 0xFFu;
                     float hi, lo;
                     l2pair(r[b], hi, lo);
-                    const float cg = gref[grp[b]];
+                    const float cg = gref[g0 + grp[b]];
                     uint32_t* bm = bmask + grp[b] * 4;
                     if (is_row) {
                         xt[grp[b] * cp + tok] = suf[b] * pow2(hi, lo, cg);
