@@ -113,6 +113,14 @@ struct P1Args {
     uint2* hot;          // per chunk: {count, 0}, then {head position, size} of each hot group (NULL: none)
     int C, W, R, P, key_bits, first_partial, valid_last, tile_len, digit_bits;
     int stage_bytes;     // LDS before the sorted row: sort keys and counts, then the sweeps' records
+    // Resident layout (rows of up to 8 items per thread, when LDS holds it): the sorted keys stay
+    // in LDS through the sweeps (the mover records take their slots there) and the entries' values
+    // are staged in LDS at the start (K values [C*W], then Q values [C*R]); the digit counts and
+    // then the records follow them. 0: keys at 0, counts and then records over them.
+    int resident;
+    int vals_off;        // resident: byte offset of the staged values
+    int hist_off;        // byte offsets of the digit counts and (after the scans) the records
+    int rec_off;
     uint32_t vec;        // bit 0 (1): K (Q) fields take 4-entry vector stores (aligned rows)
     int hot_min;         // valid K entries that make a group hot for the pair kernel
     int hot_cap;         // hot groups one chunk can have (list entries after the count)
@@ -324,9 +332,10 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     constexpr int NP = kNT * IPT;
     constexpr int NTILE = (NP + kTile - 1) / kTile;
     extern __shared__ __align__(16) unsigned char smem[];
-    unsigned char* stage = smem;                                   // records, after the scans
-    uint32_t* skey = reinterpret_cast<uint32_t*>(smem);           // sort keys (inside staging)
-    uint32_t* hist = reinterpret_cast<uint32_t*>(smem + NP * 4);  // digit counts (inside staging)
+    uint32_t* skey = reinterpret_cast<uint32_t*>(smem);                   // sort keys
+    uint32_t* hist = reinterpret_cast<uint32_t*>(smem + a.hist_off);      // digit counts
+    unsigned char* stage = smem + a.rec_off;                              // records, after the scans
+    float* vals_k = reinterpret_cast<float*>(smem + a.vals_off);          // resident: staged values
     uint16_t* sval = reinterpret_cast<uint16_t*>(smem + a.stage_bytes);
     float* gates = reinterpret_cast<float*>(smem + a.stage_bytes + NP * 2);
     __shared__ Seg wtot[kNW];
@@ -338,6 +347,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
 
     const int c = blockIdx.x;
     const int C = a.C, W = a.W, R = a.R;
+    float* vals_q = vals_k + ((C * W + 3) & ~3);
     const int wr = W + R;
     const int n = C * wr;
     const int tv = c >= a.first_partial ? a.valid_last : C;
@@ -379,6 +389,18 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             const int j = ic - t * wr;
             ids[k] = *(j < W ? a.k_idx + cw + t * W + j : a.q_idx + cr + t * R + (j - W));
         }
+        // Resident layout: the entries' values in entry order (coalesced, issued beside the ids;
+        // the invalid tokens' values, which may be anything, are not used).
+        float vk[IPT], vq[IPT];   // (C*W, C*R < IPT * kNT)
+        const bool res = IPT <= 8 && a.resident;   // block-uniform
+        if (res) {
+#pragma unroll
+            for (int k = 0; k < IPT; ++k) {
+                const int i = static_cast<int>(threadIdx.x) + k * kNT;
+                vk[k] = a.k_val[cw + min(i, C * W - 1)];
+                vq[k] = a.q_val[cr + min(i, C * R - 1)];
+            }
+        }
 #pragma unroll
         for (int k = 0; k < IPT; ++k) asm volatile("" ::"v"(ids[k]));
 #pragma unroll
@@ -388,6 +410,14 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             const uint32_t kv =
                 t < tv ? static_cast<uint32_t>(static_cast<int64_t>(ids[k]) - id_base) & (key_lim - 1u) : key_lim;
             key[k] = i < n ? kv : pad_key;
+        }
+        if (res) {
+#pragma unroll
+            for (int k = 0; k < IPT; ++k) {
+                const int i = static_cast<int>(threadIdx.x) + k * kNT;
+                if (i < C * W) vals_k[i] = i < tv * W ? vk[k] : 0.0f;
+                if (i < C * R) vals_q[i] = i < tv * R ? vq[k] : 0.0f;
+            }
         }
         // Invalid entries need one more key bit only in a ragged chunk.
         block_radix_sort<IPT>(key, val, tv < C ? kb + 1 : kb, a.digit_bits, skey, sval, hist, wsum);
@@ -656,6 +686,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             // first use, inside it).
             int32_t kid[kTileItems];
             float vl[kTileItems];
+            const bool res = IPT <= 8 && a.resident;   // block-uniform
             {
                 const int p0 = T * kTile + static_cast<int>(threadIdx.x) * kTileItems;
 #pragma unroll
@@ -665,14 +696,21 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                     const int t = token_of_entry(r, a.wr_magic);
                     const int j = r - t * wr;
                     const bool q = j >= W;
-                    vl[k] = *(q ? a.q_val + cr + t * R + (j - W) : a.k_val + cw + t * W + j);
-                    if constexpr (sk) kid[k] = a.k_idx[cw + ((!q && t < tv) ? t * W + j : 0)];
+                    if (res) {   // staged values (zero for invalid tokens); the slot from the sorted key
+                        vl[k] = q ? vals_q[t * R + (j - W)] : vals_k[t * W + j];
+                        if constexpr (sk) kid[k] = static_cast<int32_t>(p < n ? skey[p] : 0u);
+                    } else {
+                        vl[k] = *(q ? a.q_val + cr + t * R + (j - W) : a.k_val + cw + t * W + j);
+                        if constexpr (sk) kid[k] = a.k_idx[cw + ((!q && t < tv) ? t * W + j : 0)];
+                    }
                 }
+                if (!res) {
 #pragma unroll
-                for (int k = 0; k < kTileItems; ++k) {   // invalid tokens' values are not used
-                    const int p = p0 + k;
-                    const int r = p < n ? static_cast<int>(sval[p] & kRMask) : 0;
-                    vl[k] = (p < n && token_of_entry(r, a.wr_magic) < tv) ? vl[k] : 0.0f;
+                    for (int k = 0; k < kTileItems; ++k) {   // invalid tokens' values are not used
+                        const int p = p0 + k;
+                        const int r = p < n ? static_cast<int>(sval[p] & kRMask) : 0;
+                        vl[k] = (p < n && token_of_entry(r, a.wr_magic) < tv) ? vl[k] : 0.0f;
+                    }
                 }
             }
             for_tile(T, rpre[T], fpre[T], kpre[T], vl, [&](int k, int p, const Entry& e) {
@@ -707,10 +745,10 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                     km[o] = meta;
                     gstore<uint32_t>(a.spay_k + cw, e.jkind, elem);
                     const float sc = e.valid ? e.v * expf(e.rex) : 0.0f;
-                    const int64_t id = static_cast<int64_t>(kid[k]);
-                    const uint32_t slot =
-                        e.valid ? static_cast<uint32_t>((static_cast<uint32_t>(id - id_base) & (key_lim - 1u)) + id_base)
-                                : 0u;
+                    // kid: the entry's id, or (resident layout) its sorted key, the local slot.
+                    const uint32_t local = res ? static_cast<uint32_t>(kid[k])
+                                               : static_cast<uint32_t>(static_cast<int64_t>(kid[k]) - id_base) & (key_lim - 1u);
+                    const uint32_t slot = e.valid ? static_cast<uint32_t>(local + id_base) : 0u;
                     gstore<u32x4>(a.krec + cw, e.jkind,
                                   u32x4{elem, slot, __float_as_uint(sc), __float_as_uint(group_exp(e))});
                     int nk, L;
@@ -760,7 +798,9 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                 const u32x4 M4 = *reinterpret_cast<const u32x4*>(km + i0);
                 const uint32_t g = static_cast<uint32_t>(i0);
                 f32x4 v4;
-                if (vec && cnt == 4) {
+                if (IPT <= 8 && a.resident) {   // (one sweep from token 0 here: record i is K entry i)
+                    v4 = *reinterpret_cast<const f32x4*>(vals_k + g);
+                } else if (vec && cnt == 4) {
                     v4 = *reinterpret_cast<const f32x4*>(a.k_val + gb + g);
                 } else {
 #pragma unroll
@@ -824,7 +864,9 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                 const u32x4 M4 = *reinterpret_cast<const u32x4*>(qm + i0);
                 const uint32_t g = static_cast<uint32_t>(i0);
                 f32x4 v4;
-                if (vec && cnt == 4) {
+                if (IPT <= 8 && a.resident) {
+                    v4 = *reinterpret_cast<const f32x4*>(vals_q + g);
+                } else if (vec && cnt == 4) {
                     v4 = *reinterpret_cast<const f32x4*>(a.q_val + gb + g);
                 } else {
 #pragma unroll
@@ -1306,6 +1348,7 @@ struct MainPlan {
     int ipt;
     int digit_bits;
     int stage_bytes;
+    int resident, vals_off, hist_off, rec_off;
     size_t lds_bytes;
     Sweeps sweeps;
 };
@@ -1329,11 +1372,24 @@ MainPlan plan_main(const sdm_p1_shape* s, bool with_pairs_ws) {
     const int fixed = np * 2 + 256 * static_cast<int>(sizeof(float)) +
                       (with_pairs_ws ? s->C * s->W / kHotMin * static_cast<int>(sizeof(uint2)) : 0);
     const int cap_max = (kLdsTotal - kStaticReserve - fixed) / 16 * 16;
-    // Widest digit (<= 10 bits) whose per-wave counts fit beside the keys.
+    // Widest digit (<= 10 bits) whose per-wave counts fit beside the keys (and, in the resident
+    // layout, beside the keys and the staged values, with the records fitting there too).
+    const int vals_bytes = (((s->C * s->W + 3) & ~3) + ((s->C * s->R + 3) & ~3)) * 4;
+    m.resident = 0;
     int d = 10;
-    while (d > 4 && np * 4 + kNW * (1 << d) * 4 > cap_max) --d;
+    if (m.ipt <= 8) {
+        while (d > 4 && np * 4 + vals_bytes + kNW * (1 << d) * 4 > cap_max) --d;
+        m.resident = np * 4 + vals_bytes + max(kNW * (1 << d) * 4, sweep_bytes(s, kSweepK | kSweepQ, s->C)) <= cap_max;
+    }
+    if (!m.resident) {
+        d = 10;
+        while (d > 4 && np * 4 + kNW * (1 << d) * 4 > cap_max) --d;
+    }
     m.digit_bits = d;
-    int cap = np * 4 + kNW * (1 << d) * 4;
+    m.vals_off = np * 4;
+    m.hist_off = np * 4 + (m.resident ? vals_bytes : 0);
+    m.rec_off = m.resident ? m.hist_off : 0;
+    int cap = m.hist_off + kNW * (1 << d) * 4;
     // Sweeps: every record at once up to 8 items per thread, else each kind in token ranges
     // (multiples of 4 tokens, so every range starts 16-byte aligned in the entry-order rows).
     Sweeps& sw = m.sweeps;
@@ -1343,13 +1399,13 @@ MainPlan plan_main(const sdm_p1_shape* s, bool with_pairs_ws) {
             sw.kinds[sw.count] = kinds;
             sw.t0[sw.count] = t0;
             sw.t1[sw.count] = t1;
-            cap = max(cap, sweep_bytes(s, kinds, t1 - t0));
+            cap = max(cap, m.rec_off + sweep_bytes(s, kinds, t1 - t0));
         }
         ++sw.count;
     };
     if (m.ipt <= 8) {   // fits: n <= 8192 entries of at most 12 B beside at most 21 KB of the rest
         add(kSweepK | kSweepQ, 0, s->C);
-        if (sweep_bytes(s, kSweepK | kSweepQ, s->C) > cap_max) sw.count = kMaxSweeps + 1;   // refused
+        if (m.rec_off + sweep_bytes(s, kSweepK | kSweepQ, s->C) > cap_max) sw.count = kMaxSweeps + 1;   // refused
     } else {   // the kernel sweeps one kind at a time here
         for (uint32_t kind : {kSweepK, kSweepQ}) {
             int step = 4;
@@ -1466,6 +1522,10 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     if (m.sweeps.count > kMaxSweeps) return hipErrorInvalidValue;
     a.digit_bits = m.digit_bits;
     a.stage_bytes = m.stage_bytes;
+    a.resident = m.resident;
+    a.vals_off = m.vals_off;
+    a.hist_off = m.hist_off;
+    a.rec_off = m.rec_off;
     a.sweeps = m.sweeps;
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     if (io->events != nullptr) {
