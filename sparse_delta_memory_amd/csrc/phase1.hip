@@ -228,7 +228,7 @@ __device__ __forceinline__ uint32_t block_exclusive_add(uint32_t v, uint32_t* ws
 }
 
 // Stable LSD radix sort of the block's kNT * IPT (key, value) pairs over key bits [0, bits), in
-// digits of up to `dmax` bits. Items live in registers in striped order (item k of lane l of wave
+// the fewest passes of at most `dmax` bits, the bits shared out evenly among them. Items live in registers in striped order (item k of lane l of wave
 // w is element w * 64 * IPT + k * 64 + l). Per digit: ranks inside the wave from ballot-built
 // peer masks, slice by slice (equal digits keep element order); per-wave digit counts in LDS
 // (rows of 2^dmax); one block scan over (digit, wave) gives every (wave, digit) its start; a
@@ -242,9 +242,10 @@ __device__ void block_radix_sort(uint32_t (&key)[IPT], uint32_t (&val)[IPT], int
     const int stride = 1 << dmax;
     uint32_t* my_hist = hist + w * stride;
     const int passes = (bits + dmax - 1) / dmax;
+    const int width = (bits + passes - 1) / passes;   // digits of (nearly) equal width, at most dmax
     for (int pass = 0; pass < passes; ++pass) {
-        const int sh = pass * dmax;
-        const int db = min(dmax, bits - sh);
+        const int sh = pass * width;
+        const int db = min(width, bits - sh);
         const int nd = 1 << db;
         const uint32_t dmask = static_cast<uint32_t>(nd - 1);
         for (int d = lane; d < nd; d += kWave) my_hist[d] = 0u;
