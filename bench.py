@@ -4,11 +4,14 @@
 One step = the whole hot path over one batch: Phase 1 of every chunk of the workload (sort, scans,
 records, tile bounds, A / QK) followed by every DW step of the workload, all enqueued on one stream
 with the inputs already in HBM, launched eagerly (--graph: replayed from a HIP graph;
---pair-stream: the pair kernel on a second stream beside the DW steps). `value` is the step's throughput in Phase-1 K+Q entries per second. Kernel
-durations for the roofline come from a second, eager pass of the same steps with HIP events
-bound to each kernel's own start and end.
+--pair-stream: the pair kernel on a second stream beside the DW steps). Before the W warmup
+steps, untimed steps run for about --settle seconds so that the GPU clocks leave idle. `value` is
+the step's throughput in Phase-1 K+Q entries per second. Kernel durations for the roofline come
+from a second, eager pass of the same steps with HIP events bound to each kernel's own start and
+end.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I] [--no-cpu-baseline] [--graph] [--pair-stream]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I] [--no-cpu-baseline] [--graph]
+                    [--pair-stream] [--settle S]
     python bench.py --copy-calibration MIB   # a plain device copy, for scaling HBM byte counters
 
 The default workload is the uniform bf16 shape (index 1); the others are parity cases that can
@@ -140,6 +143,8 @@ def main():
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step from a HIP graph in the timed region")
+    ap.add_argument("--settle", type=float, default=0.25, metavar="S",
+                    help="untimed steps for about S seconds before the warmup steps (clocks settle)")
     ap.add_argument("--pair-stream", action="store_true",
                     help="run the pair kernel on a second stream beside the DW steps (slower on uniform_bf16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -200,6 +205,14 @@ def main():
             joined.record(pair_stream)
             stream.wait_event(joined)
 
+    # Untimed settling: steps for about --settle seconds (the GPU leaves its idle clocks; a cold
+    # first timed region measured up to 20 % slow), then the W warmup steps proper.
+    t_settle = time.perf_counter()
+    for _ in range(100000):
+        step()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_settle >= args.settle:
+            break
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
