@@ -117,7 +117,9 @@ constexpr int kSeg = 32;
 constexpr int kSegLimit = (4095 / kSeg) * kSeg;
 
 // The general walk of the team at K-row position j of stream p (record r0, valid): a group's FIRST
-// or, when groups are split, a segment start; other positions return at once.
+// or, when groups are split, a segment start; other positions return at once. The members after
+// the first are read a team-wide batch at a time and summed per run of one token (the token row is
+// loaded once per run); the sum's order is fixed by the records, so results are reproducible.
 template <int CPL, bool BANK_BF16, bool DV_BF16>
 __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0, int col0, int tl) {
     // Member records and token rows loaded together (fewer when the rows take more registers).
@@ -160,7 +162,9 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
             done = true;
         }
     }
-    for (int m = j + 1; !done && m < a.CW; m += kBatch) {
+    // The next kBatch members (records and token rows together): small groups end here.
+    int m = j + 1;
+    if (!done && m < a.CW) {
         uint4 rb[kBatch];
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) rb[b] = kr[min(m + b, a.CW - 1)];
@@ -190,6 +194,75 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
             } else if (!unbounded && taken == kSeg) {
                 done = true;
             }
+        }
+        m += kBatch;
+    }
+    // Longer groups: the other members, a batch of `la` records at a time (one per active lane of
+    // the team, all in flight together). Inside a batch, consecutive members of one token form a run: the run's
+    // scales are summed first (a segmented scan across the team's lanes), so the token row is
+    // loaded and fused once per run, kBatch runs' rows at a time.
+    const int la = (a.hd + CPL - 1) / CPL;                        // active lanes of the team
+    const int tbase = static_cast<int>(lane_id()) & ~((1 << a.ts_log2) - 1);
+    for (; !done && m < a.CW; m += la) {
+        const int pos = m + tl;
+        const uint4 rb = kr[min(pos, a.CW - 1)];
+        // Members taken from this batch: up to LAST, within the segment's budget and the row.
+        int cnt = min(la, a.CW - m);
+        if (!unbounded) cnt = min(cnt, kSeg - taken);
+        const uint64_t team_lanes = la < 64 ? (1ull << la) - 1ull : ~0ull;   // this team's lanes, after the shift
+        const uint64_t lastm = (__ballot(tl < cnt && (rb.x & kLast)) >> tbase) & team_lanes;
+        const int last_lane = lastm != 0ull ? __builtin_ctzll(lastm) : -1;
+        if (last_lane >= 0) cnt = last_lane + 1;
+        const bool member = tl < cnt;
+        const int tok = static_cast<int>((rb.x >> kTokShift) & 0xFFu);
+        const int ptok = __shfl(tok, tbase + max(tl - 1, 0), kWave);
+        const bool start = member && (tl == 0 || tok != ptok);
+        // Run sums: inclusive segmented scan of the scales over the team's lanes (fixed tree).
+        float v = member ? __uint_as_float(rb.z) : 0.0f;
+        bool f = start;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            if (d >= la) break;
+            const float ov = __shfl(v, tbase + max(tl - d, 0), kWave);
+            const bool of = __shfl(static_cast<int>(f), tbase + max(tl - d, 0), kWave) != 0;
+            if (tl >= d && !f) v = ov + v;
+            if (tl >= d) f = f || of;
+        }
+        const int ntok = __shfl(tok, tbase + min(tl + 1, la - 1), kWave);
+        const bool end = member && (tl == cnt - 1 || ntok != tok);
+        uint64_t ends = (__ballot(end) >> tbase) & team_lanes;
+        // The runs in order, kBatch token rows in flight at a time.
+        while (ends != 0ull) {
+            float cb[kBatch];
+            RawCols<CPL, DV_BF16> xr[kBatch];
+            int nb = 0;
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int L = ends != 0ull ? __builtin_ctzll(ends) : 0;
+                const bool ok = ends != 0ull;
+                const int tk = __shfl(tok, tbase + L, kWave);
+                cb[b] = ok ? __shfl(v, tbase + L, kWave) : 0.0f;
+                xr[b] = load_raw<CPL, DV_BF16>(dv0 + static_cast<int64_t>(tk) * a.hd * kDvEs, col0);
+                nb += ok ? 1 : 0;
+                ends &= ends - 1ull;
+            }
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                if (b >= nb) break;
+                float xv[CPL];
+                unpack_cols<CPL, DV_BF16>(xr[b], xv);
+#pragma unroll
+                for (int q = 0; q < CPL; ++q) acc[q] = fmaf(cb[b], xv[q], acc[q]);
+            }
+        }
+        taken += cnt;
+        if (last_lane >= 0) {
+            last_seen = true;
+            last_pos = m + last_lane;
+            cpe = __uint_as_float(__shfl(rb.w, tbase + last_lane, kWave));
+            done = true;
+        } else if (!unbounded && taken == kSeg) {
+            done = true;
         }
     }
     if (first && last_seen) {   // the whole group in one segment
