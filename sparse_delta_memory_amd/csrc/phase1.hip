@@ -976,6 +976,10 @@ constexpr int kPairBatchGroups = 32;
 constexpr float kDenseRange = 200.0f;
 constexpr uint32_t kHotWide = 0x80000000u;   // in a hot-list size word: the group is walked
 
+// The triangle in LDS: row i holds cells 0..i padded to a multiple of 4 floats, so that every row
+// starts 16-byte aligned (4-cell reads of the write-out); rows 4a .. 4a+3 take 4(a+1) floats each.
+__host__ __device__ constexpr int tri_row(int i) { return 4 * ((i >> 2) + 1) * (2 * (i >> 2) + (i & 3)); }
+
 // LDS of the pair kernel: the triangle, the hot list (+ batch bounds), the reference c of every
 // hot group, per batch group its first batch position and its 4-token block masks (x, y), then
 // the x and y tables (gb groups of Cp = C rounded up to 4 floats each).
@@ -987,7 +991,7 @@ __host__ __device__ inline PairLds pair_lds_layout(int C, int hot_cap, int gb) {
     const size_t cp = static_cast<size_t>((C + 3) & ~3);
     PairLds l;
     l.tri = 0;
-    l.hot = up(static_cast<size_t>(C) * (C + 1) / 2 * sizeof(float));
+    l.hot = up(static_cast<size_t>(tri_row(C)) * sizeof(float));
     l.gref = l.hot + up(static_cast<size_t>(hot_cap) * 2 * sizeof(uint32_t) + 16);   // + batch bounds
     l.gbase = l.gref + up(static_cast<size_t>(hot_cap) * sizeof(float));
     l.bmask = l.gbase + up(static_cast<size_t>(kPairBatchGroups + 1) * sizeof(uint32_t));
@@ -1019,8 +1023,8 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
     uint32_t* bmask = reinterpret_cast<uint32_t*>(smem + lay.bmask);    // per group: x blocks (2 words), y blocks (2)
     float* xt = reinterpret_cast<float*>(smem + lay.xt);
     float* yt = reinterpret_cast<float*>(smem + lay.yt);
-    const int tri_size = C * (C + 1) / 2;
-    for (int e = threadIdx.x; e < tri_size; e += kPairThreads) tri[e] = 0.0f;
+    const int tri_size = tri_row(C);
+    for (int e = threadIdx.x; e < tri_size / 4; e += kPairThreads) reinterpret_cast<float4*>(tri)[e] = make_float4(0.f, 0.f, 0.f, 0.f);
     const int64_t crow = static_cast<int64_t>(c) * n;
     const uint4* rec = a.rec + crow;
     const uint32_t row_q = q ? kIsQ : 0u;
@@ -1219,7 +1223,7 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
                     for (int v = 0; v < 4; ++v) {
                         const int jj = 4 * bj + v;
                         if (ii < C && (q ? jj <= ii : jj < ii)) {
-                            float* cell = tri + ii * (ii + 1) / 2 + jj;
+                            float* cell = tri + tri_row(ii) + jj;
                             *cell = *cell + acc[u][v];
                         }
                     }
@@ -1236,7 +1240,7 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
     // record after, the own record, kWalkBatch before) in one go, which covers a small group.
     const int i = threadIdx.x;
     if (i < tv) {
-        float* row = tri + i * (i + 1) / 2;
+        float* row = tri + tri_row(i);
         const int lanes = q ? R : W;
         const uint16_t* iv = (q ? a.inv_q : a.inv_k) + (static_cast<int64_t>(c) * C + i) * lanes;
         // Token i's entries of this kind: (Q flag, token) bits of the payload.
@@ -1326,20 +1330,17 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
         for (int e = threadIdx.x; e < C * c4; e += kPairThreads) {
             const int ii = e / c4;
             const int j0 = (e - ii * c4) << 2;
-            const float* trow = tri + ii * (ii + 1) / 2;
-            float v4[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int jj = j0 + u;
-                v4[u] = (q ? jj <= ii : jj < ii) ? trow[jj] : 0.0f;
-            }
-            reinterpret_cast<float4*>(out + ob)[e] = make_float4(v4[0], v4[1], v4[2], v4[3]);
+            // Cells past the triangle read as zeros: the row padding is never written, and A's
+            // diagonal cell is never written either.
+            float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j0 <= ii) v4 = *reinterpret_cast<const float4*>(tri + tri_row(ii) + j0);
+            reinterpret_cast<float4*>(out + ob)[e] = v4;
         }
     } else {
         for (int e = threadIdx.x; e < C * C; e += kPairThreads) {
             const int ii = e / C;
             const int jj = e - ii * C;
-            out[ob + e] = (q ? jj <= ii : jj < ii) ? tri[ii * (ii + 1) / 2 + jj] : 0.0f;
+            out[ob + e] = (q ? jj <= ii : jj < ii) ? tri[tri_row(ii) + jj] : 0.0f;
         }
     }
 }
