@@ -158,6 +158,8 @@ def test_masked_tokens_do_not_leak():
     dict(C=120, W=16, R=4, S=70, P=2, steps=1, vl=100),
     # Hot groups whose log-cumsum spans more than the dense pass takes (gates near -4): walked.
     dict(C=256, W=8, R=8, S=48, P=1, steps=1, vl=None, gmu=-4.0),
+    # 8192 entries (8 per thread) whose keys, values and records do not all fit in LDS together.
+    dict(C=256, W=16, R=16, S=20000, P=1, steps=1, vl=200),
 ])
 def test_edge_shapes(case):
     sh = W.Shape("edge", P=case["P"], T=case["C"] * case["steps"], C=case["C"], W=case["W"], R=case["R"],
