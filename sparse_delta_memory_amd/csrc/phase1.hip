@@ -1236,8 +1236,9 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
     const bool any_wide = bounds[2] != 0;   // (set before the last barrier)
 
     // ---- Other groups: thread i walks its flagged runs back to the group head. The entry words of
-    // 32 lanes are loaded together; a walk then loads the record window around its start (one
-    // record after, the own record, kWalkBatch before) in one go, which covers a small group.
+    // 32 lanes are loaded together; walks go two at a time, each with the record window around its
+    // start (one record after, the own record, four before) loaded in one go, which covers a small
+    // group; longer groups read eight more records at a time.
     const int i = threadIdx.x;
     if (i < tv) {
         float* row = tri + tri_row(i);
@@ -1246,31 +1247,30 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
         // Token i's entries of this kind: (Q flag, token) bits of the payload.
         const uint32_t own_tag = (q ? kIsQ : 0u) | (static_cast<uint32_t>(i) << kTokShift);
         const uint32_t tag_mask = kIsQ | (0xFFu << kTokShift);
-        for (int lb = 0; lb < lanes; lb += 32) {
-          uint32_t flags = 0;
-          const uint32_t walk_bits = any_wide ? (kInvWalk | kInvHot) : kInvWalk;
-#pragma unroll
-          for (int u = 0; u < 32; ++u) {
-              const int ln = lb + u;
-              flags |= (ln < lanes && (iv[min(ln, lanes - 1)] & walk_bits)) ? (1u << u) : 0u;
-          }
-          for (; flags != 0u; flags &= flags - 1u) {
-            const int ln = lb + __builtin_ctz(flags);
+        // The sorted position of the walk starting at lane ln, or -1 for a hot group's run whose
+        // group was summed densely.
+        auto walk_start = [&](int ln) {
             const uint32_t word = iv[ln];
             // A walk start has an earlier entry in its group, so 1 <= rho (the clamp only guards).
             const int rho = min(static_cast<int>(word & kMetaPos), n - 1);
-            if (word & kInvHot) {   // a hot group's run: walked only if its group was too wide
+            if (word & kInvHot) {   // walked only if its group was too wide for the dense pass
                 int lo_g = 0, hi_g = nh - 1;   // the last hot group with head <= rho
                 while (lo_g < hi_g) {
                     const int mid = (lo_g + hi_g + 1) >> 1;
                     if (static_cast<int>(hl[mid].x) <= rho) lo_g = mid; else hi_g = mid - 1;
                 }
-                if (!(hl[lo_g].y & kHotWide)) continue;
+                if (!(hl[lo_g].y & kHotWide)) return -1;
             }
-            constexpr int kWin = kWalkBatch + 2;
-            uint4 rb[kWin];   // positions rho + 1, rho, rho - 1, ..., rho - kWalkBatch
+            return rho;
+        };
+        // The record window of a walk: positions rho + 1, rho, rho - 1, ..., rho - kBack.
+        constexpr int kBack = 4, kWin = kBack + 2;
+        auto load_window = [&](int rho, uint4 (&rb)[kWin]) {
+            const int r = max(rho, 0);
 #pragma unroll
-            for (int k = 0; k < kWin; ++k) rb[k] = rec[min(max(rho + 1 - k, 0), n - 1)];
+            for (int k = 0; k < kWin; ++k) rb[k] = rec[min(max(r + 1 - k, 0), n - 1)];
+        };
+        auto walk = [&](int rho, const uint4 (&rb)[kWin]) {
             const uint4 own = rb[1];
             // Sum the run's values (the run goes on past rho only for repeated lanes of the token).
             float wi = __uint_as_float(own.w);
@@ -1309,7 +1309,7 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
                 if (done) break;
                 visit(rb[k]);
             }
-            for (int top = rho - 1 - kWalkBatch; !done; top -= kWalkBatch) {
+            for (int top = rho - 1 - kBack; !done; top -= kWalkBatch) {
                 uint4 rc[kWalkBatch];
 #pragma unroll
                 for (int k = 0; k < kWalkBatch; ++k) rc[k] = rec[max(top - k, 0)];
@@ -1320,6 +1320,29 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
                 }
             }
             if (cur_j >= 0 && (q || cur_j != i)) row[cur_j] = row[cur_j] + (wi * kj) * expf((se - sj) + (ce - cj));
+        };
+        for (int lb = 0; lb < lanes; lb += 32) {
+          uint32_t flags = 0;
+          const uint32_t walk_bits = any_wide ? (kInvWalk | kInvHot) : kInvWalk;
+#pragma unroll
+          for (int u = 0; u < 32; ++u) {
+              const int ln = lb + u;
+              flags |= (ln < lanes && (iv[min(ln, lanes - 1)] & walk_bits)) ? (1u << u) : 0u;
+          }
+          // Walks two at a time: both record windows in flight before either is walked (the terms
+          // still reach the row in lane order).
+          for (; flags != 0u;) {
+            const int ln1 = lb + __builtin_ctz(flags);
+            flags &= flags - 1u;
+            const int ln2 = flags != 0u ? lb + __builtin_ctz(flags) : -1;
+            if (flags != 0u) flags &= flags - 1u;
+            const int rho1 = walk_start(ln1);
+            const int rho2 = ln2 >= 0 ? walk_start(ln2) : -1;
+            uint4 w1[kWin], w2[kWin];
+            load_window(rho1, w1);
+            load_window(rho2, w2);
+            if (rho1 >= 0) walk(rho1, w1);
+            if (rho2 >= 0) walk(rho2, w2);
           }
         }
     }
