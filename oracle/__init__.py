@@ -42,6 +42,7 @@ class _ChunkIn(ctypes.Structure):
         ("id_base", ctypes.c_int64),
         ("k_idx", ctypes.c_void_p), ("q_idx", ctypes.c_void_p), ("k_val", ctypes.c_void_p),
         ("q_val", ctypes.c_void_p), ("g", ctypes.c_void_p), ("tile_len", ctypes.c_int),
+        ("g_width", ctypes.c_int), ("g_lane_stride", ctypes.c_int),
     ]
 
 
@@ -83,7 +84,12 @@ def _chunk_in(k_idx, q_idx, k_val, q_val, g, c, P, stream_offset, first_partial,
             np.ascontiguousarray(k_val[c], dtype=np.float32), np.ascontiguousarray(q_val[c], dtype=np.float32),
             np.ascontiguousarray(g[c], dtype=np.float32))
     t_valid = valid_last if c >= first_partial else C
-    s = _ChunkIn(C, W, R, t_valid, (c % P) * stream_offset, *[_ptr(a) for a in arrs], tile_len)
+    # gates [N, C] (one per token) or [N, C, W] (one per token and K lane)
+    per_lane = np.ndim(g) == 3
+    if per_lane and np.shape(g)[2] != W:
+        raise ValueError("per-lane gates must be [N, C, W]")
+    s = _ChunkIn(C, W, R, t_valid, (c % P) * stream_offset, *[_ptr(a) for a in arrs], tile_len,
+                 W if per_lane else 1, 1 if per_lane else 0)
     return s, arrs
 
 

@@ -24,7 +24,9 @@
  *  - invalid entries (tokens at or past the chunk's valid count) sort after all valid
  *    entries in entry order and each forms a group of its own;
  *  - a K entry contributes its token's gate once per (token, slot): a K entry whose
- *    predecessor in the group is a K entry of the same token contributes 0 (a "repeat").
+ *    predecessor in the group is a K entry of the same token contributes 0 (a "repeat");
+ *  - gates are per token, or per (token, K lane) as the scan kernel's width / lane-stride
+ *    addressing allows; with per-lane gates the token's lowest lane writing the slot applies.
  */
 #include <math.h>
 #include <stdint.h>
@@ -51,8 +53,12 @@ typedef struct {
     const int32_t* q_idx;   /* [C, R] */
     const float* k_val;     /* [C, W] */
     const float* q_val;     /* [C, R] */
-    const float* g;         /* [C] per-token gate (log decay, <= 0) */
+    const float* g;         /* gates (log decays, <= 0): g[t * g_width + lane * g_lane_stride] is the
+                               gate of token t's K lane `lane` ([C] per token: width 1, stride 0;
+                               [C, W] per token and lane: width W, stride 1) */
     int tile_len;           /* L of tiles_k */
+    int g_width;
+    int g_lane_stride;
 } oracle_chunk_in;
 
 /* One chunk's outputs; any pointer may be NULL to skip that field. */
@@ -180,8 +186,9 @@ static int oracle_build(const oracle_chunk_in* in, oracle_row* w) {
         }
         p = e;
     }
-    /* Gate contributions: a valid K entry adds its token's gate unless the previous entry of
-     * its group is a K entry of the same token. */
+    /* Gate contributions: a valid K entry adds its gate unless the previous entry of its group is
+     * a K entry of the same token. A token's writes to one slot are adjacent in the group and in
+     * lane order, so the gate applied is that of the token's lowest lane writing the slot. */
     w->repeats = 0;
     for (int p = 0; p < n; ++p) {
         w->x[p] = 0.0;
@@ -190,7 +197,7 @@ static int oracle_build(const oracle_chunk_in* in, oracle_row* w) {
         if (rep) {
             ++w->repeats;
         } else {
-            w->x[p] = (double)in->g[w->tok[p]];
+            w->x[p] = (double)in->g[w->tok[p] * in->g_width + w->lane[p] * in->g_lane_stride];
         }
     }
     /* Inclusive log-cumsum, sum after, and the peers of each kind before / after. */

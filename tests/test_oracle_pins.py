@@ -21,7 +21,7 @@ import oracle
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def tiny(seed, N=2, C=10, W=3, R=2, S=4, P=1, g=None, valid_last=None, distinct=False):
+def tiny(seed, N=2, C=10, W=3, R=2, S=4, P=1, g=None, valid_last=None, distinct=False, lane_gates=False):
     rng = np.random.default_rng(seed)
     stream = (np.arange(N) % P)[:, None, None] * S
     if distinct:
@@ -34,7 +34,8 @@ def tiny(seed, N=2, C=10, W=3, R=2, S=4, P=1, g=None, valid_last=None, distinct=
     k_val = (rng.standard_normal((N, C, W)) / 2).astype(np.float32)
     q_val = (rng.standard_normal((N, C, R)) / 2).astype(np.float32)
     if g is None:
-        z = rng.standard_normal((N, C)) + 2.0
+        # one gate per token [N, C], or per (token, K lane) [N, C, W]
+        z = rng.standard_normal((N, C, W) if lane_gates else (N, C)) + 2.0
         g = (-np.log1p(np.exp(-z))).astype(np.float32)
     fp = N - P if valid_last is not None else N
     vl = C if valid_last is None else valid_last
@@ -77,10 +78,12 @@ def brute(d, c):
     for ei, e in enumerate(E):
         if not e["valid"] or e["q"]:
             continue
-        # A token's gate counts once per slot: at its lowest K lane on that slot.
+        # A token's gate counts once per slot: at its lowest K lane on that slot (per-lane gates:
+        # that lane's gate).
         lower = [f for f in E if f["valid"] and not f["q"] and f["t"] == e["t"] and f["s"] == e["s"]
                  and f["lane"] < e["lane"]]
-        e["x"] = 0.0 if lower else float(g[e["t"]])
+        gate = float(g[e["t"]]) if g.ndim == 1 else float(g[e["t"], e["lane"]])
+        e["x"] = 0.0 if lower else gate
     res = []
     for ei, e in enumerate(E):
         if not e["valid"]:
@@ -113,9 +116,9 @@ def test_sort_matches_brute_force_and_lexsort(seed):
         assert np.array_equal(np.lexsort((rr, slot, invalid)), o["perm"][c])
 
 
-@pytest.mark.parametrize("seed", [4, 5])
-def test_scan_fields_match_brute_force(seed):
-    d = tiny(seed, N=2, C=11, W=4, R=3, S=6, P=2, valid_last=7)
+@pytest.mark.parametrize("seed,lane_gates", [(4, False), (5, False), (41, True), (42, True)])
+def test_scan_fields_match_brute_force(seed, lane_gates):
+    d = tiny(seed, N=2, C=11, W=4, R=3, S=6, P=2, valid_last=7, lane_gates=lane_gates)
     o = run_oracle(d)
     C, W = d["k_idx"].shape[1:]
     R = d["q_idx"].shape[2]
@@ -175,9 +178,9 @@ def test_scan_fields_match_brute_force(seed):
         assert o["tiles_k"][c].tolist() == want
 
 
-@pytest.mark.parametrize("seed", [6, 7])
-def test_pairs_match_brute_force(seed):
-    d = tiny(seed, N=2, C=8, W=3, R=3, S=3, P=1, valid_last=5)
+@pytest.mark.parametrize("seed,lane_gates", [(6, False), (7, False), (61, True)])
+def test_pairs_match_brute_force(seed, lane_gates):
+    d = tiny(seed, N=2, C=8, W=3, R=3, S=3, P=1, valid_last=5, lane_gates=lane_gates)
     o = run_oracle(d, fields=["a", "qk", "a_mag", "qk_mag", "a_cnt", "qk_cnt"])
     C = d["k_idx"].shape[1]
     for c in range(2):
@@ -306,12 +309,15 @@ def test_dw_zero_gates_is_scatter_add():
         np.testing.assert_allclose(new, want[slots], rtol=1e-13, atol=1e-13)
 
 
-@pytest.mark.parametrize("seed,S,W,R,vl", [(21, 3, 3, 2, None), (22, 5, 4, 4, 9), (23, 2, 2, 1, None), (24, 9, 5, 3, 4)])
-def test_sequential_simulation_identities(seed, S, W, R, vl):
+@pytest.mark.parametrize("seed,S,W,R,vl,lane_gates", [(21, 3, 3, 2, None, False), (22, 5, 4, 4, 9, False),
+                                                      (23, 2, 2, 1, None, False), (24, 9, 5, 3, 4, False),
+                                                      (25, 3, 4, 2, None, True), (26, 6, 5, 3, 8, True)])
+def test_sequential_simulation_identities(seed, S, W, R, vl, lane_gates):
     """Token-by-token decay-then-write equals DW, and its predictions / reads equal the
-    Phase-1 decomposition through k_eff, q_w, A and QK."""
+    Phase-1 decomposition through k_eff, q_w, A and QK. With per-lane gates a token decays each
+    slot it writes once, by the gate of its lowest lane writing that slot."""
     C, hd = 14, 3
-    d = tiny(seed, N=2, C=C, W=W, R=R, S=S, P=1, valid_last=vl)
+    d = tiny(seed, N=2, C=C, W=W, R=R, S=S, P=1, valid_last=vl, lane_gates=lane_gates)
     o = run_oracle(d)
     rng = np.random.default_rng(seed)
     for c in range(2):
@@ -326,7 +332,8 @@ def test_sequential_simulation_identities(seed, S, W, R, vl):
         ks, qs = d["k_idx"][c], d["q_idx"][c]
         for t in range(tv):
             for s in np.unique(ks[t]):
-                M[s] *= math.exp(g[t])
+                lowest = int(np.flatnonzero(ks[t] == s)[0])
+                M[s] *= math.exp(g[t, lowest] if lane_gates else g[t])
             pred = sum(kv[t, e] * M[ks[t, e]] for e in range(W))
             for e in range(W):
                 M[ks[t, e]] += kv[t, e] * dv[t]
@@ -343,3 +350,39 @@ def test_sequential_simulation_identities(seed, S, W, R, vl):
         np.testing.assert_allclose(new, M[slots], rtol=1e-12, atol=1e-12)
         untouched = np.setdiff1d(np.arange(S), slots)
         assert np.array_equal(M[untouched], M0[untouched])
+
+
+def test_lane_gates_equal_to_token_gates():
+    """Per-lane gates that repeat the token's gate on every lane give exactly the per-token result."""
+    d = tiny(31, N=3, C=20, W=4, R=3, S=6, P=1, valid_last=13)
+    o = run_oracle(d)
+    d3 = dict(d, g=np.repeat(d["g"][:, :, None], 4, axis=2))
+    o3 = run_oracle(d3)
+    for k in o:
+        assert np.array_equal(o[k], o3[k]), k
+
+
+def test_closed_form_distinct_slots_lane_gates():
+    """All slots distinct: each K entry is alone in its group, so log_k = its own lane's gate."""
+    d = tiny(32, N=2, C=16, W=3, R=2, S=4096, P=1, distinct=True, lane_gates=True)
+    o = run_oracle(d)
+    g = d["g"].astype(np.float64)
+    for c in range(2):
+        np.testing.assert_array_equal(o["log_k"][c], g[c])
+        assert np.all(o["rex"][c] == 0) and np.all(o["log_q"][c] == 0)
+        np.testing.assert_allclose(o["cpe"][c], np.exp(g[c]), rtol=1e-15)
+
+
+def test_lane_gates_lowest_lane_applies():
+    """One token writing one slot from lanes 0 and 2 (lane 1 elsewhere): the slot's gate is lane 0's
+    and lane 2 is a repeat; lane 1's own slot takes lane 1's gate."""
+    k_idx = np.array([[[5, 7, 5]]], np.int32)
+    q_idx = np.array([[[5]]], np.int32)
+    g = np.array([[[-0.5, -0.25, -2.0]]], np.float32)
+    d = dict(k_idx=k_idx, q_idx=q_idx, k_val=np.ones((1, 1, 3), np.float32), q_val=np.ones((1, 1, 1), np.float32),
+             g=g, P=1, stream_offset=0, first_partial=1, valid_last=1)
+    o = run_oracle(d)
+    assert o["log_k"][0, 0].tolist() == [-0.5, -0.25, -0.5]
+    assert o["log_q"][0, 0, 0] == -0.5
+    assert o["repeats"][0] == 1
+    assert o["cpe"][0, 0, 0] == pytest.approx(math.exp(-0.5), rel=1e-15)
