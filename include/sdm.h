@@ -64,6 +64,11 @@ typedef struct sdm_p1_shape {
     int32_t first_partial;  /* chunks c >= first_partial are ragged (0..N; N: none) */
     int32_t valid_last;     /* valid tokens of a ragged chunk, 0..C */
     int32_t tile_len;       /* L of the tile bounds tiles_k, >= 1 */
+    int32_t g_lane_stride;  /* layout of the gates g: 0 = one gate per token, [N, C]; 1 = one gate per
+                               (token, K lane), [N, C, W] (page "sparse_delta_memory/cuda/phase1_cuda.py",
+                               p1_scan_kernel: the gate is read at token * width + lane * stride). With 1,
+                               a token that writes one slot from several lanes applies the gate of the
+                               lowest of those lanes (its other writes there are repeats). */
 } sdm_p1_shape;
 
 /*
@@ -79,7 +84,8 @@ typedef struct sdm_p1_io {
     const int32_t* q_idx;   /* [N, C, R] absolute slot ids of the reads */
     const float* k_val;     /* [N, C, W] write values */
     const float* q_val;     /* [N, C, R] read values */
-    const float* g;         /* [N, C] per-token gates (log decays) */
+    const float* g;         /* gates (log decays): [N, C] per token, or [N, C, W] per (token, K lane)
+                               when g_lane_stride = 1 */
     /* entry-order outputs */
     float* log_k;           /* [N, C, W] log-cumsum of the slot's gates up to and including the entry */
     float* rex;             /* [N, C, W] sum of the slot's later gates in the chunk */
@@ -108,6 +114,9 @@ typedef struct sdm_p1_io {
     float* qk;              /* [N, C, C] QK[i,j] (j <= i), zeros elsewhere */
     int32_t* repeats;       /* [N] per chunk: K entries whose group predecessor is a K entry of the
                                same token (their gate is not applied again) */
+    int32_t* perm;          /* [N, C*(W+R)] the chunk's sorted order: entry index r = t*(W+R) + j at
+                               each sorted position (the permutation the stable sort by slot makes;
+                               invalid entries last, in entry order) */
     void* workspace;        /* device scratch, 16-byte aligned, >= sdm_phase1_workspace(shape) */
     size_t workspace_bytes;
     hipEvent_t* events;     /* optional (NULL: none): 4 caller-created events bound to the kernels'

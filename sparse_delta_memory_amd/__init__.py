@@ -21,10 +21,12 @@ __all__ = ["P1Shape", "phase1", "phase1_workspace_bytes", "alloc_phase1_outputs"
            "timing_events"]
 
 
-def make_shape(N, C, W, R, P=1, key_bits=16, stream_offset=0, first_partial=None, valid_last=None, tile_len=128):
+def make_shape(N, C, W, R, P=1, key_bits=16, stream_offset=0, first_partial=None, valid_last=None, tile_len=128,
+               g_lane_stride=0):
+    """Phase-1 shape. g_lane_stride 0: gates g [N, C] (per token); 1: g [N, C, W] (per token and K lane)."""
     return P1Shape(int(N), int(C), int(W), int(R), int(P), int(key_bits), int(stream_offset),
                    int(N if first_partial is None else first_partial), int(C if valid_last is None else valid_last),
-                   int(tile_len))
+                   int(tile_len), int(g_lane_stride))
 
 
 def phase1_workspace_bytes(shape: P1Shape) -> int:
@@ -49,8 +51,10 @@ def alloc_phase1_outputs(shape: P1Shape, device="cuda", fields=None):
         "spay_k": ((N, C * W), torch.int32), "spay_q": ((N, C * R), torch.int32),
         "krec": ((N, C * W, 4), torch.int32), "tiles_k": ((N, ntk + 1), torch.int32),
         "a": ((N, C, C), torch.float32), "qk": ((N, C, C), torch.float32), "repeats": ((N,), torch.int32),
+        "perm": ((N, C * (W + R)), torch.int32),
     }
-    want = set(spec) if fields is None else set(fields) | {"spay_k", "krec", "tiles_k"}
+    # perm (the sorted order itself) only when asked for
+    want = (set(spec) - {"perm"}) if fields is None else set(fields) | {"spay_k", "krec", "tiles_k"}
     return {k: torch.empty(s, dtype=dt, device=device) for k, (s, dt) in spec.items() if k in want}
 
 
@@ -59,7 +63,7 @@ def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=No
     """Enqueue Phase 1 of shape.N chunks on the current (or given) stream; returns the outputs.
 
     Inputs are contiguous device tensors: k_idx [N,C,W] int32, q_idx [N,C,R] int32, k_val / q_val
-    float32 of the same shapes, g [N,C] float32. `out` is a dict from alloc_phase1_outputs (a
+    float32 of the same shapes, g [N,C] float32 ([N,C,W] when shape.g_lane_stride = 1). `out` is a dict from alloc_phase1_outputs (a
     missing key skips that optional output). events: optional 4 torch.cuda.Events (timing_events)
     bound to the two kernels. pair_stream / pair_ready: optional torch stream and recorded event:
     the pair kernel then runs on pair_stream after the sort/scan kernel; the caller makes the main

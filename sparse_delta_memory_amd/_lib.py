@@ -25,6 +25,7 @@ class P1Shape(ctypes.Structure):
         ("N", ctypes.c_int32), ("C", ctypes.c_int32), ("W", ctypes.c_int32), ("R", ctypes.c_int32),
         ("P", ctypes.c_int32), ("key_bits", ctypes.c_int32), ("stream_offset", ctypes.c_int64),
         ("first_partial", ctypes.c_int32), ("valid_last", ctypes.c_int32), ("tile_len", ctypes.c_int32),
+        ("g_lane_stride", ctypes.c_int32),
     ]
 
 
@@ -32,7 +33,7 @@ P1_IO_FIELDS = [
     "k_idx", "q_idx", "k_val", "q_val", "g",
     "log_k", "rex", "cpe", "k_eff", "is_last", "is_only", "pos_k",
     "log_q", "q_w", "pos_q", "q_last", "q_only",
-    "spay_k", "spay_q", "krec", "tiles_k", "a", "qk", "repeats",
+    "spay_k", "spay_q", "krec", "tiles_k", "a", "qk", "repeats", "perm",
 ]
 
 

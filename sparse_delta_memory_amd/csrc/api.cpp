@@ -46,6 +46,8 @@ sdm_status check_p1_shape(const sdm_p1_shape* s) {
     if (s->valid_last < 0 || s->valid_last > s->C)
         return fail(SDM_EINVAL, "sdm_phase1: valid_last = %d outside 0..C", s->valid_last);
     if (s->tile_len < 1) return fail(SDM_EINVAL, "sdm_phase1: tile_len = %d < 1", s->tile_len);
+    if (s->g_lane_stride != 0 && s->g_lane_stride != 1)
+        return fail(SDM_EINVAL, "sdm_phase1: g_lane_stride = %d (0: gates [N, C]; 1: gates [N, C, W])", s->g_lane_stride);
     const int64_t n = static_cast<int64_t>(s->C) * (s->W + s->R);
     if (n > (1 << 17)) return fail(SDM_ESHAPE, "sdm_phase1: C*(W+R) = %lld > 2^17", static_cast<long long>(n));
     if (n > sdm::kP1MaxRow)
@@ -96,7 +98,7 @@ sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st
     }
     const void* a4[] = {io->k_idx, io->q_idx, io->k_val, io->q_val, io->g, io->log_k, io->rex, io->cpe,
                         io->k_eff, io->pos_k, io->log_q, io->q_w, io->pos_q, io->spay_k, io->spay_q,
-                        io->tiles_k, io->a, io->qk, io->repeats};
+                        io->tiles_k, io->a, io->qk, io->repeats, io->perm};
     for (const void* p : a4) {
         if (!aligned(p, 4)) return fail(SDM_EALIGN, "sdm_phase1: a 4-byte field is misaligned");
     }

@@ -109,6 +109,7 @@ struct P1Args {
     int4* krec;
     int32_t* tiles_k;
     int32_t* repeats;
+    int32_t* perm;       // [N, n] entry index at each sorted position (NULL: skipped)
     uint4* rec;
     uint2* hot;          // per chunk: {count, 0}, then {head position, size} of each hot group (NULL: none)
     int C, W, R, P, key_bits, first_partial, valid_last, tile_len, digit_bits;
@@ -328,7 +329,9 @@ struct Entry {
     float v;
 };
 
-template <int IPT>
+// LG: gates per (token, K lane), [N, C, W], read from global memory where a scan needs one;
+// otherwise per token, [N, C], staged in LDS.
+template <int IPT, bool LG>
 __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     constexpr int NP = kNT * IPT;
     constexpr int NTILE = (NP + kTile - 1) / kTile;
@@ -363,7 +366,17 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     const int w = threadIdx.x / kWave;
     const int ntiles = (n + kTile - 1) / kTile;
 
-    for (int t = threadIdx.x; t < C; t += kNT) gates[t] = t < tv ? a.g[static_cast<int64_t>(c) * C + t] : 0.0f;
+    if constexpr (!LG) {
+        for (int t = threadIdx.x; t < C; t += kNT) gates[t] = t < tv ? a.g[static_cast<int64_t>(c) * C + t] : 0.0f;
+    }
+    // The gate of valid token t's K lane j (the scans read it for non-repeated valid K entries only).
+    auto gate = [&](int t, int j) -> float {
+        if constexpr (LG) {
+            return a.g[cw + t * W + j];
+        } else {
+            return gates[t];
+        }
+    };
     if (threadIdx.x == 0) hot_n = 0u;
     {
         const void* outs[kNumOut] = {a.log_k, a.rex, a.cpe, a.k_eff, a.is_last, a.is_only, a.pos_k, a.inv_k,
@@ -466,7 +479,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                 const bool rep = !head && is_k && pj < W && pt == t;
                 heads |= (head ? 1u : 0u) << k;
                 reps |= (rep ? 1u : 0u) << k;
-                x[k] = (is_k && !rep) ? gates[t] : 0.0f;
+                x[k] = (is_k && !rep) ? gate(t, j) : 0.0f;
             }
 #pragma unroll
             for (int k = 0; k < kTileItems; ++k) {
@@ -499,6 +512,9 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
         }
     }
     __syncthreads();   // every flag of the sorted row is set; the keys are no longer needed
+    if (a.perm != nullptr) {   // the sorted order itself: entry index at each sorted position
+        for (int p = threadIdx.x; p < n; p += kNT) a.perm[crow + p] = static_cast<int32_t>(sval[p] & kRMask);
+    }
 
     // The thread index as the recomputations see it: each output sweep makes it opaque again, so the
     // compiler cannot hoist per-position address arithmetic out of the sweeps (registers it would
@@ -518,7 +534,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             const int t = token_of_entry(r, a.wr_magic);
             const bool q = r - t * wr >= W;
             const bool valid = p < n && t < tv;
-            x[k] = (valid && !q && !(rr[k] & kFlagRep)) ? gates[t] : 0.0f;
+            x[k] = (valid && !q && !(rr[k] & kFlagRep)) ? gate(t, r - t * wr) : 0.0f;
             heads |= ((rr[k] & kFlagHead) ? 1u : 0u) << k;
         }
         const int pn = p0 + kTileItems;
@@ -1444,8 +1460,10 @@ MainPlan plan_main(const sdm_p1_shape* s, bool with_pairs_ws) {
 }
 
 template <int IPT>
-hipError_t launch_main(P1Args args, size_t lds, int N, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
-    const void* fn = reinterpret_cast<const void*>(&p1_main_kernel<IPT>);
+hipError_t launch_main(P1Args args, bool lane_gates, size_t lds, int N, hipStream_t st, hipEvent_t start,
+                       hipEvent_t stop) {
+    const void* fn = lane_gates ? reinterpret_cast<const void*>(&p1_main_kernel<IPT, true>)
+                                : reinterpret_cast<const void*>(&p1_main_kernel<IPT, false>);
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     void* kargs[] = {&args};
@@ -1517,6 +1535,7 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     a.krec = reinterpret_cast<int4*>(io->krec);
     a.tiles_k = io->tiles_k;
     a.repeats = io->repeats;
+    a.perm = io->perm;
     a.rec = pairs ? static_cast<uint4*>(Lc.rec) : nullptr;
     // Hot groups only when the pair kernel's x and y tables hold at least 4 groups beside the rest.
     // Groups per batch: as many as the blocks per compute unit that 4 groups allow still fit.
@@ -1558,11 +1577,11 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     }
     hipError_t e;
     switch (m.ipt) {
-        case 1: e = launch_main<1>(a, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
-        case 2: e = launch_main<2>(a, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
-        case 4: e = launch_main<4>(a, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
-        case 8: e = launch_main<8>(a, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
-        default: e = launch_main<16>(a, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        case 1: e = launch_main<1>(a, s->g_lane_stride != 0, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        case 2: e = launch_main<2>(a, s->g_lane_stride != 0, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        case 4: e = launch_main<4>(a, s->g_lane_stride != 0, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        case 8: e = launch_main<8>(a, s->g_lane_stride != 0, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        default: e = launch_main<16>(a, s->g_lane_stride != 0, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
     }
     if (e != hipSuccess || !pairs) return e;
     PairArgs pa;

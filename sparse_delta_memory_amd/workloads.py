@@ -84,7 +84,7 @@ class Workload:
     q_idx: np.ndarray   # [N, C, R] int32
     k_val: np.ndarray   # [N, C, W] float32
     q_val: np.ndarray   # [N, C, R] float32
-    g: np.ndarray       # [N, C] float32
+    g: np.ndarray       # [N, C] float32 per token, or [N, C, W] per (token, K lane)
     dv: np.ndarray      # [steps, P, C, hd] float32 (bf16-representable values when dv_dtype == "bf16")
     first_partial: int
     valid_last: int
@@ -139,9 +139,10 @@ def _slots(rng: np.random.Generator, sh: Shape, size, ctx: dict) -> np.ndarray:
 
 
 def make(index: int | Shape, steps: int | None = None, *, nan_invalid: bool = True, seed: int | None = None,
-         shape_overrides: dict | None = None) -> Workload:
+         shape_overrides: dict | None = None, lane_gates: bool = False) -> Workload:
     """Draw the inputs of workload `index` (or of a Shape). `steps` truncates the step count (the
-    last step stays ragged when the shape is). `shape_overrides` replaces Shape fields (tests)."""
+    last step stays ragged when the shape is). `shape_overrides` replaces Shape fields (tests).
+    `lane_gates`: one gate per (token, K lane), g [N, C, W], instead of one per token."""
     sh = SHAPES[index] if isinstance(index, int) else index
     if shape_overrides:
         sh = Shape(**{**sh.__dict__, **shape_overrides})
@@ -165,7 +166,8 @@ def make(index: int | Shape, steps: int | None = None, *, nan_invalid: bool = Tr
     q_idx = (_slots(np.random.default_rng(ch["q_idx"]), sh, (N, C, R), ctx) + stream).astype(np.int32)
     k_val = (np.random.default_rng(ch["k_val"]).standard_normal((N, C, W)) / 2.0).astype(np.float32)
     q_val = (np.random.default_rng(ch["q_val"]).standard_normal((N, C, R)) / 2.0).astype(np.float32)
-    g = _logsigmoid(np.random.default_rng(ch["g"]).standard_normal((N, C)) + sh.gate_mu).astype(np.float32)
+    g_shape = (N, C, W) if lane_gates else (N, C)
+    g = _logsigmoid(np.random.default_rng(ch["g"]).standard_normal(g_shape) + sh.gate_mu).astype(np.float32)
     dv = np.random.default_rng(ch["dv"]).standard_normal((nsteps, P, C, hd), dtype=np.float32)
     if sh.dv_dtype == "bf16":
         dv = round_bf16(dv)

@@ -20,7 +20,8 @@ F32_REL, F32_ABS = 1e-5, 1e-6
 def shape_of(wl: W.Workload, tile_len: int = 128):
     s = wl.shape
     return sdm.make_shape(wl.N, s.C, s.W, s.R, P=s.P, key_bits=s.key_bits, stream_offset=s.S,
-                          first_partial=wl.first_partial, valid_last=wl.valid_last, tile_len=tile_len)
+                          first_partial=wl.first_partial, valid_last=wl.valid_last, tile_len=tile_len,
+                          g_lane_stride=1 if wl.g.ndim == 3 else 0)
 
 
 def device_inputs(wl: W.Workload, dev="cuda"):
@@ -37,18 +38,22 @@ def device_dv(wl: W.Workload, dev="cuda"):
     return dv.to(torch.bfloat16) if wl.shape.dv_dtype == "bf16" else dv
 
 
-def run_phase1(wl: W.Workload, dev="cuda", tile_len=128):
+def run_phase1(wl: W.Workload, dev="cuda", tile_len=128, fields=None):
+    """Phase 1 of every chunk on the device; `fields` adds optional outputs (e.g. "perm")."""
     import torch
 
     shape = shape_of(wl, tile_len)
     ins = device_inputs(wl, dev)
-    out = sdm.phase1(shape, **ins)
+    out = None
+    if fields is not None:
+        every = set(sdm.alloc_phase1_outputs(sdm.make_shape(0, 1, 1, 1), device="cpu"))
+        out = sdm.alloc_phase1_outputs(shape, device=dev, fields=every | set(fields))
+    out = sdm.phase1(shape, out=out, **ins)
     torch.cuda.synchronize()
     return shape, out
 
 
-def oracle_phase1(wl: W.Workload, chunks, tile_len=128, threads=8, with_magnitudes=False):
-    fields = None
+def oracle_phase1(wl: W.Workload, chunks, tile_len=128, threads=8, with_magnitudes=False, fields=None):
     if with_magnitudes:
         fields = list(oracle._OUT_FIELDS)
     return oracle.phase1(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, P=wl.P, stream_offset=wl.stream_offset,
@@ -111,7 +116,7 @@ def compare_phase1(out, ref, chunks):
                 assert_pair_sums(f, host[f], ref[f], ref[f + "_mag"], ref[f + "_cnt"])
             else:
                 assert_f32(f, host[f], ref[f])
-    for f in ("is_last", "is_only", "q_last", "q_only", "pos_k", "pos_q", "tiles_k", "repeats"):
+    for f in ("is_last", "is_only", "q_last", "q_only", "pos_k", "pos_q", "tiles_k", "repeats", "perm"):
         if f in host:
             assert_exact(f, host[f], ref[f])
     assert_exact("spay_k", u32(host["spay_k"]), u32(ref["spay_k"]))

@@ -30,7 +30,8 @@ def test_exports_every_declared_function():
 
 
 def shape(**kw):
-    d = dict(N=4, C=64, W=4, R=4, P=1, key_bits=12, stream_offset=0, first_partial=4, valid_last=64, tile_len=128)
+    d = dict(N=4, C=64, W=4, R=4, P=1, key_bits=12, stream_offset=0, first_partial=4, valid_last=64, tile_len=128,
+             g_lane_stride=0)
     d.update(kw)
     return _lib.P1Shape(*[d[f] for f, _ in _lib.P1Shape._fields_])
 
@@ -60,6 +61,7 @@ def call_p1(s, o):
     (dict(key_bits=0), _lib.SDM_EINVAL), (dict(key_bits=31), _lib.SDM_EINVAL),
     (dict(first_partial=5), _lib.SDM_EINVAL), (dict(valid_last=65), _lib.SDM_EINVAL),
     (dict(tile_len=0), _lib.SDM_EINVAL), (dict(stream_offset=-1), _lib.SDM_EINVAL),
+    (dict(g_lane_stride=2), _lib.SDM_EINVAL), (dict(g_lane_stride=-1), _lib.SDM_EINVAL),
     (dict(C=256, W=256, R=256), _lib.SDM_EUNSUPPORTED), (dict(C=256, W=40, R=40), _lib.SDM_EUNSUPPORTED),
 ])
 def test_phase1_shape_refusals(kw, status):

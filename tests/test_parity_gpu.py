@@ -188,3 +188,40 @@ def test_empty_call():
     out = sdm.phase1(shape, e, e, f, f, f)
     torch.cuda.synchronize()
     assert out["krec"].numel() == 0
+
+
+@pytest.mark.parametrize("case", [
+    dict(idx=0),                                           # tiny workload, one gate per (token, K lane)
+    dict(C=37, W=5, R=3, S=9, P=2, steps=2, vl=11),        # heavy sharing (many repeats), ragged row and chunk
+    dict(C=256, W=8, R=8, S=48, P=1, steps=1, vl=None),   # every group hot: the dense pair pass
+    dict(idx=1, steps=2),                                  # the uniform bf16 shape (IPT 4)
+])
+def test_lane_gates(case):
+    """Per-(token, K lane) gates [N, C, W]: every Phase-1 output and the DW steps match the oracle."""
+    if "idx" in case:
+        wl = W.make(case["idx"], steps=case.get("steps"), lane_gates=True)
+    else:
+        sh = W.Shape("lane_gates", P=case["P"], T=case["C"] * case["steps"], C=case["C"], W=case["W"], R=case["R"],
+                     S=case["S"], hd=64, bank_dtype="f32", dv_dtype="f32", slots="uniform", valid_last=case["vl"])
+        wl = W.make(sh, seed=778, lane_gates=True)
+    say("lane gates", case)
+    shape, out = H.run_phase1(wl)
+    chunks = list(range(min(wl.N, 16)))
+    ref = H.oracle_phase1(wl, chunks, with_magnitudes=True)
+    H.compare_phase1(out, ref, chunks)
+    H.run_dw_check(wl, out, shape, set(range(min(wl.steps, 2))), sample_untouched=0)
+
+
+@pytest.mark.parametrize("idx,steps", [(0, None), (2, 1), (4, 1)])
+def test_perm_output(idx, steps):
+    """The optional sorted order (entry index at each sorted position) equals the oracle's, and
+    requesting it changes no other output bit."""
+    wl = W.make(idx, steps=steps)
+    say("perm", idx, steps)
+    shape, out = H.run_phase1(wl, fields=["perm"])
+    _, plain = H.run_phase1(wl)
+    for k in plain:
+        assert torch.equal(out[k].view(torch.uint8), plain[k].view(torch.uint8)), k
+    chunks = list(range(min(wl.N, 8))) + [wl.N - 1]
+    ref = H.oracle_phase1(wl, chunks, fields=["perm"])
+    H.assert_exact("perm", out["perm"].index_select(0, torch.as_tensor(chunks, device="cuda")).cpu().numpy(), ref["perm"])
