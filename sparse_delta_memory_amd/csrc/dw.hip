@@ -145,7 +145,7 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
     // Walk the members in sorted order: the first on its own (most groups have one member),
     // then kBatch records and token rows at a time.
     bool last_seen = false, done = false;
-    int last_pos = j, taken = 1;
+    int taken = 1;
     float cpe = 1.0f;
     {
         float x0[CPL];
@@ -188,7 +188,6 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
             ++taken;
             if (rb[b].x & kLast) {
                 last_seen = true;
-                last_pos = m + b;
                 cpe = __uint_as_float(rb[b].w);
                 done = true;
             } else if (!unbounded && taken == kSeg) {
@@ -258,7 +257,6 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
         taken += cnt;
         if (last_lane >= 0) {
             last_seen = true;
-            last_pos = m + last_lane;
             cpe = __uint_as_float(__shfl(rb.w, tbase + last_lane, kWave));
             done = true;
         } else if (!unbounded && taken == kSeg) {
@@ -283,7 +281,8 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
 #pragma unroll
     for (int q = 0; q < CPL; ++q) part[col0 + q] = acc[q];
     const int seg = dist / kSeg;
-    if (last_seen && tl == 0) a.meta[gslot] = make_int2(seg + 1, last_pos);
+    // The segment holding LAST publishes the segment count and the group's cpe (that of LAST).
+    if (last_seen && tl == 0) a.meta[gslot] = make_int2(seg + 1, static_cast<int>(__float_as_uint(cpe)));
     __threadfence();
     // The segment holding LAST adds 1 - (segments), every other adds 1: the counter returns to 0
     // exactly at the last arrival (and is left at 0 for the next call).
@@ -293,21 +292,30 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
     after = __shfl(after, static_cast<int>(lane_id()) & ~((1 << a.ts_log2) - 1), kWave);
     if (after != 0) return;
     __threadfence();
+    // The segment count, the base row (every segment's record names the group's slot) and the first
+    // batch of partials in one round trip; partials past the count are read from in-row positions
+    // and dropped.
+    constexpr int kPartBatch = CPL == 8 ? 4 : 2;
     const int2 meta = a.meta[gslot];
-    const int nseg = meta.x;
+    const RawCols<CPL, BANK_BF16> b2raw = load_raw<CPL, BANK_BF16>(bank_row, col0);
     float tot[CPL];
 #pragma unroll
     for (int q = 0; q < CPL; ++q) tot[q] = 0.0f;
-    // The partials kPartBatch at a time (all loads in flight), added in segment order.
-    constexpr int kPartBatch = CPL == 8 ? 4 : 2;
+    int nseg = kPartBatch;   // the true count once meta has arrived
     for (int sg0 = 0; sg0 < nseg; sg0 += kPartBatch) {
         float pv[kPartBatch][CPL];
 #pragma unroll
         for (int b = 0; b < kPartBatch; ++b) {
-            const float* pp = a.part + (prow + first_pos + min(sg0 + b, nseg - 1) * kSeg) * a.hd + col0;
+            const float* pp = a.part + (prow + min(first_pos + (sg0 + b) * kSeg, a.CW - 1)) * a.hd + col0;
 #pragma unroll
             for (int q = 0; q < CPL; ++q) pv[b][q] = __builtin_nontemporal_load(pp + q);
         }
+#pragma unroll
+        for (int b = 0; b < kPartBatch; ++b) {
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) asm volatile("" ::"v"(pv[b][q]));   // the batch in flight together
+        }
+        nseg = meta.x;
 #pragma unroll
         for (int b = 0; b < kPartBatch; ++b) {
             if (sg0 + b < nseg) {
@@ -316,16 +324,13 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
             }
         }
     }
-    const uint4 rf = kr[first_pos];
-    const uint4 rl = kr[meta.y];
-    unsigned char* brow = static_cast<unsigned char*>(a.bank) + static_cast<int64_t>(rf.y) * a.hd * kBankEs;
     float b2[CPL];
-    load_cols<CPL, BANK_BF16>(brow, col0, b2);
-    const float cpe_l = __uint_as_float(rl.w);
+    unpack_cols<CPL, BANK_BF16>(b2raw, b2);
+    const float cpe_l = __uint_as_float(static_cast<uint32_t>(meta.y));
     float o[CPL];
 #pragma unroll
     for (int q = 0; q < CPL; ++q) o[q] = fmaf(b2[q], cpe_l, tot[q]);
-    store_cols<CPL, BANK_BF16>(brow, col0, o);
+    store_cols<CPL, BANK_BF16>(bank_row, col0, o);
 }
 
 // Teams take U consecutive K-row positions. Groups of one member (the common case) are done
