@@ -199,6 +199,48 @@ size_t sdm_dw_workspace(const sdm_dw_io* io);
  */
 sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st);
 
+/* One read-side step: the chunks ti*P .. ti*P + P - 1, before their DW step. */
+typedef struct sdm_read_io {
+    const void* bank;       /* [rows, hd] SDM_F32 or SDM_BF16: the memory BEFORE this step's DW (read only) */
+    int32_t bank_dtype;     /* sdm_dtype */
+    int64_t rows;           /* bank rows (an id outside 0..rows-1 contributes nothing) */
+    int32_t hd;             /* row width, a multiple of 8 */
+    const int32_t* k_idx;   /* [N, C, W] absolute slot ids of the writes (Phase-1 input) */
+    const int32_t* q_idx;   /* [N, C, R] absolute slot ids of the reads */
+    const float* k_eff;     /* [N, C, W] from sdm_phase1 */
+    const float* q_w;       /* [N, C, R] from sdm_phase1 */
+    const float* a;         /* [N, C, C] from sdm_phase1 */
+    const float* qk;        /* [N, C, C] from sdm_phase1 */
+    const float* v;         /* value rows: row (ti * step_rows + p * C + t) of [*, hd], float32 */
+    const float* beta;      /* [N, C] per-token write strengths */
+    float* dv;              /* OUT token rows, same row indexing as v: feed sdm_dw_step (dv_step_rows =
+                               step_rows, dv_dtype SDM_F32) */
+    float* pred;            /* OUT predictions, same row indexing (also the call's scratch) */
+    float* read;            /* OUT reads, same row indexing (also the call's scratch) */
+    int64_t step_rows;      /* rows between steps in v / dv / pred / read (P*C, or 0 for one-step buffers) */
+    int64_t out_rows;       /* rows in each of v, dv, pred and read: ti * step_rows + P * C <= out_rows */
+    int32_t P, C, W, R, N;  /* the Phase-1 shape */
+    int32_t first_partial;  /* as in sdm_p1_shape: tokens >= valid_last of chunks >= first_partial are masked */
+    int32_t valid_last;
+    hipEvent_t* events;     /* optional (NULL: none): 4 caller-created events bound to the start and end of
+                               the gather kernel ([0], [1]) and of the substitution kernel ([2], [3]) */
+} sdm_read_io;
+
+/*
+ * Forward read side of one step (definitions: page "sparse_delta_memory/cuda/phase1_cuda.py",
+ * module docstring, for k_eff, q_w, A, QK; the delta rule dv = beta (v - prediction) as the write
+ * scale -beta k exp(log_k) of the backward records on the same page, p1_scan_kernel, and on page
+ * "sparse_delta_memory/cuda/pa_dc_cuda.py", module docstring, implies). Per chunk, from the bank
+ * rows M0 before the step:
+ *   p0[t] = sum_e k_eff[t,e] M0[k_idx[t,e]],   q0[t] = sum_r q_w[t,r] M0[q_idx[t,r]],
+ *   dv[t] = beta[t] (v[t] - p0[t] - sum_{j<t} A[t,j] dv[j])    (forward substitution),
+ *   pred[t] = p0[t] + sum_{j<t} A[t,j] dv[j],    read[t] = q0[t] + sum_{j<=t} QK[t,j] dv[j].
+ * pred and read are what a token-by-token decay / predict / write / read evaluation of the chunk
+ * sees; masked tokens get 0 in every output and none of their inputs is read. Two kernels on st.
+ * Requires (ti + 1) * P <= N, C <= 256, hd a multiple of 8, 16-byte aligned bank, v, dv, pred, read.
+ */
+sdm_status sdm_read_step(const sdm_read_io* io, int64_t ti, hipStream_t st);
+
 /* Static text for a status code. */
 const char* sdm_status_string(sdm_status s);
 

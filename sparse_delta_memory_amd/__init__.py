@@ -7,6 +7,7 @@ libsdm_amd.so. There is no CPU fallback: without the built library every call ra
     shape = P1Shape(N=..., C=..., W=..., R=..., P=..., key_bits=..., stream_offset=...)
     out = phase1(shape, k_idx, q_idx, k_val, q_val, g)          # dict of device tensors
     dw_step(bank, dv, out["krec"], shape, ti, dv_step_rows=P*C)  # bank updated in place
+    read_step(bank, out, k_idx, q_idx, v, beta, dv, pred, read, shape, ti, step_rows=P*C)  # before DW
 """
 
 from __future__ import annotations
@@ -17,7 +18,7 @@ from . import _lib
 from ._lib import P1IO, P1Shape, SdmError  # noqa: F401
 
 __all__ = ["P1Shape", "phase1", "phase1_workspace_bytes", "alloc_phase1_outputs", "dw_step", "dw_workspace_bytes",
-           "alloc_dw_workspace", "DwPlan", "SdmError", "make_shape",
+           "alloc_dw_workspace", "DwPlan", "ReadPlan", "read_step", "SdmError", "make_shape",
            "timing_events"]
 
 
@@ -181,3 +182,57 @@ class DwPlan:
 def dw_step(bank, dv, krec, shape: P1Shape, ti: int, dv_step_rows: int, stream=None, workspace=None, events=None):
     """One DW step `ti` through a plan built for this call (see DwPlan)."""
     DwPlan(bank, dv, krec, shape, dv_step_rows, workspace).step(ti, stream=stream, events=events)
+
+
+class ReadPlan:
+    """The read side of a step planned once, launched per step (before that step's DW).
+
+    bank [rows, hd] float32 or bfloat16, the memory before the step (read only); p1: the dict of
+    Phase-1 outputs (k_eff, q_w, a, qk); k_idx / q_idx the Phase-1 id inputs; v [*, hd] float32 value
+    rows and beta [N, C] float32; dv, pred, read [*, hd] float32 outputs (dv feeds DwPlan with
+    dv_step_rows = step_rows). Row of (step ti, stream p, token t): ti*step_rows + p*C + t. The plan
+    keeps the tensors alive."""
+
+    def __init__(self, bank, p1, k_idx, q_idx, v, beta, dv, pred, read, shape: P1Shape, step_rows: int):
+        import torch
+
+        if bank.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("ReadPlan: bank must be float32 or bfloat16")
+        for name, t in (("v", v), ("beta", beta), ("dv", dv), ("pred", pred), ("read", read)):
+            if t.dtype != torch.float32:
+                raise TypeError("ReadPlan: %s must be float32" % name)
+        self._lib = _lib.load()
+        self._keep = (bank, p1, k_idx, q_idx, v, beta, dv, pred, read)
+        io = _lib.ReadIO()
+        io.bank = bank.data_ptr()
+        io.bank_dtype = _lib.SDM_BF16 if bank.dtype == torch.bfloat16 else _lib.SDM_F32
+        io.rows = bank.shape[0]
+        io.hd = bank.shape[1]
+        io.k_idx, io.q_idx = k_idx.data_ptr(), q_idx.data_ptr()
+        io.k_eff, io.q_w, io.a, io.qk = (p1[k].data_ptr() for k in ("k_eff", "q_w", "a", "qk"))
+        io.v, io.beta, io.dv, io.pred, io.read = v.data_ptr(), beta.data_ptr(), dv.data_ptr(), pred.data_ptr(), read.data_ptr()
+        io.step_rows = int(step_rows)
+        io.out_rows = min(v.shape[0], dv.shape[0], pred.shape[0], read.shape[0])
+        io.P, io.C, io.W, io.R, io.N = shape.P, shape.C, shape.W, shape.R, shape.N
+        io.first_partial, io.valid_last = shape.first_partial, shape.valid_last
+        self.io = io
+        self._io_ref = ctypes.byref(io)
+        self._device = bank.device
+
+    def step(self, ti: int, stream=None, events=None):
+        """Enqueue the read side of step `ti` on the current (or given) stream. events: optional 4
+        torch.cuda.Events bound to the gather kernel's and the substitution kernel's start and end."""
+        import torch
+
+        st = torch.cuda.current_stream(self._device) if stream is None else stream
+        arr = _event_array(events, 4, "ReadPlan.step")
+        self.io.events = None if arr is None else ctypes.cast(arr, ctypes.c_void_p).value
+        try:
+            _lib.check(self._lib.sdm_read_step(self._io_ref, int(ti), ctypes.c_void_p(st.cuda_stream)))
+        finally:
+            self.io.events = None
+
+
+def read_step(bank, p1, k_idx, q_idx, v, beta, dv, pred, read, shape: P1Shape, ti: int, step_rows: int, stream=None):
+    """The read side of step `ti` through a plan built for this call (see ReadPlan)."""
+    ReadPlan(bank, p1, k_idx, q_idx, v, beta, dv, pred, read, shape, step_rows).step(ti, stream=stream)

@@ -54,8 +54,21 @@ class DwIO(ctypes.Structure):
     ]
 
 
-EXPORTS = ["sdm_phase1_workspace", "sdm_phase1", "sdm_dw_workspace", "sdm_dw_step", "sdm_status_string",
-           "sdm_last_error"]
+class ReadIO(ctypes.Structure):
+    _fields_ = [
+        ("bank", ctypes.c_void_p), ("bank_dtype", ctypes.c_int32), ("rows", ctypes.c_int64), ("hd", ctypes.c_int32),
+        ("k_idx", ctypes.c_void_p), ("q_idx", ctypes.c_void_p), ("k_eff", ctypes.c_void_p), ("q_w", ctypes.c_void_p),
+        ("a", ctypes.c_void_p), ("qk", ctypes.c_void_p), ("v", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+        ("dv", ctypes.c_void_p), ("pred", ctypes.c_void_p), ("read", ctypes.c_void_p),
+        ("step_rows", ctypes.c_int64), ("out_rows", ctypes.c_int64),
+        ("P", ctypes.c_int32), ("C", ctypes.c_int32), ("W", ctypes.c_int32), ("R", ctypes.c_int32),
+        ("N", ctypes.c_int32), ("first_partial", ctypes.c_int32), ("valid_last", ctypes.c_int32),
+        ("events", ctypes.c_void_p),
+    ]
+
+
+EXPORTS = ["sdm_phase1_workspace", "sdm_phase1", "sdm_dw_workspace", "sdm_dw_step", "sdm_read_step",
+           "sdm_status_string", "sdm_last_error"]
 
 _lock = threading.Lock()
 _lib = None
@@ -84,6 +97,8 @@ def load() -> ctypes.CDLL:
         lib.sdm_dw_workspace.restype = ctypes.c_size_t
         lib.sdm_dw_step.argtypes = [ctypes.POINTER(DwIO), ctypes.c_int64, ctypes.c_void_p]
         lib.sdm_dw_step.restype = ctypes.c_int
+        lib.sdm_read_step.argtypes = [ctypes.POINTER(ReadIO), ctypes.c_int64, ctypes.c_void_p]
+        lib.sdm_read_step.restype = ctypes.c_int
         lib.sdm_status_string.argtypes = [ctypes.c_int]
         lib.sdm_status_string.restype = ctypes.c_char_p
         lib.sdm_last_error.argtypes = []

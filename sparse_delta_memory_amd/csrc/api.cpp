@@ -135,6 +135,46 @@ sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st
     return SDM_OK;
 }
 
+sdm_status sdm_read_step(const sdm_read_io* io, int64_t ti, hipStream_t st) {
+    g_last_error.clear();
+    if (io == nullptr) return fail(SDM_EINVAL, "sdm_read_step: io is NULL");
+    if (io->C < 1 || io->C > 256 || io->W < 1 || io->W > 256 || io->R < 1 || io->R > 256)
+        return fail(SDM_ESHAPE, "sdm_read_step: C = %d, W = %d, R = %d outside 1..256", io->C, io->W, io->R);
+    if (io->P < 1 || io->N < 0) return fail(SDM_ESHAPE, "sdm_read_step: P = %d, N = %d", io->P, io->N);
+    if (ti < 0 || (ti + 1) * static_cast<int64_t>(io->P) > io->N)
+        return fail(SDM_ESHAPE, "sdm_read_step: step %lld needs (ti+1)*P <= N = %d", static_cast<long long>(ti), io->N);
+    if (io->first_partial < 0 || io->first_partial > io->N || io->valid_last < 0 || io->valid_last > io->C)
+        return fail(SDM_EINVAL, "sdm_read_step: first_partial = %d, valid_last = %d", io->first_partial, io->valid_last);
+    if (io->bank_dtype != SDM_F32 && io->bank_dtype != SDM_BF16)
+        return fail(SDM_EINVAL, "sdm_read_step: bank_dtype %d", io->bank_dtype);
+    if (io->hd < 8 || io->hd > 4096 || io->hd % 8 != 0)
+        return fail(SDM_ESHAPE, "sdm_read_step: hd = %d (multiple of 8 in 8..4096)", io->hd);
+    if (io->rows < 0 || io->step_rows < 0 || io->out_rows < 0)
+        return fail(SDM_EINVAL, "sdm_read_step: rows / step_rows / out_rows");
+    if (ti * io->step_rows + static_cast<int64_t>(io->P) * io->C > io->out_rows)
+        return fail(SDM_EINVAL, "sdm_read_step: %lld rows, step %lld needs %lld", static_cast<long long>(io->out_rows),
+                    static_cast<long long>(ti), static_cast<long long>(ti * io->step_rows + static_cast<int64_t>(io->P) * io->C));
+    const void* req[] = {io->bank, io->k_idx, io->q_idx, io->k_eff, io->q_w, io->a, io->qk, io->v, io->beta,
+                         io->dv, io->pred, io->read};
+    for (const void* p : req) {
+        if (p == nullptr) return fail(SDM_EINVAL, "sdm_read_step: every array is required");
+    }
+    const void* a16[] = {io->bank, io->v, io->dv, io->pred, io->read};
+    for (const void* p : a16) {
+        if (!aligned(p, 16)) return fail(SDM_EALIGN, "sdm_read_step: bank, v, dv, pred and read must be 16-byte aligned");
+    }
+    const void* a4[] = {io->k_idx, io->q_idx, io->k_eff, io->q_w, io->a, io->qk, io->beta};
+    for (const void* p : a4) {
+        if (!aligned(p, 4)) return fail(SDM_EALIGN, "sdm_read_step: a 4-byte field is misaligned");
+    }
+    sdm::ReadLaunch L;
+    L.io = io;
+    L.ti = ti;
+    const hipError_t e = sdm::read_launch(L, st);
+    if (e != hipSuccess) return fail(SDM_EHIP, "sdm_read_step: %s", hipGetErrorString(e));
+    return SDM_OK;
+}
+
 sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st) {
     g_last_error.clear();
     if (io == nullptr) return fail(SDM_EINVAL, "sdm_dw_step: io is NULL");

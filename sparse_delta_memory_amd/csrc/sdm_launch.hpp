@@ -57,4 +57,12 @@ struct DwWorkspace {
 };
 DwWorkspace dw_workspace_layout(const sdm_dw_io* io);
 
+struct ReadLaunch {
+    const sdm_read_io* io;
+    int64_t ti;
+};
+
+// Enqueue the read side of one step (gather kernel, then substitution kernel).
+hipError_t read_launch(const ReadLaunch& L, hipStream_t st);
+
 }  // namespace sdm

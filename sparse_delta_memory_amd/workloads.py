@@ -220,3 +220,20 @@ def make_bank_rows(wl: Workload, rows, device="cpu"):
         sel = np.nonzero(blk_of == b)[0]
         out[torch.as_tensor(sel, device=device)] = blk[torch.as_tensor(rows[sel] - b0, device=device)]
     return out
+
+
+def make_read_inputs(wl: Workload, nan_invalid: bool = True):
+    """Seeded inputs of the read side: value rows v [steps * P * C, hd] float32 ~ N(0, 1) (row
+    ti*P*C + p*C + t) and write strengths beta [N, C] float32 = sigmoid(N(0, 1)); masked tokens get
+    NaN (they must never be read)."""
+    ss = np.random.SeedSequence([wl.bank_seed, 1])
+    cv, cb = ss.spawn(2)
+    sh = wl.shape
+    v = np.random.default_rng(cv).standard_normal((wl.steps * sh.P * sh.C, sh.hd), dtype=np.float32)
+    z = np.random.default_rng(cb).standard_normal((wl.N, sh.C))
+    beta = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
+    if nan_invalid and wl.valid_last < sh.C:
+        beta[wl.first_partial:, wl.valid_last:] = np.nan
+        v3 = v.reshape(wl.steps, sh.P, sh.C, sh.hd)
+        v3[wl.steps - 1, :, wl.valid_last:, :] = np.nan
+    return v, beta

@@ -128,3 +128,32 @@ def test_dw_workspace_size():
     need = lib.sdm_dw_workspace(ctypes.byref(o))
     assert need >= 2 * 64 * 4 * (4 * 128 + 12)
     assert lib.sdm_dw_workspace(ctypes.byref(dw(P=0))) == 0
+
+
+def read_io(**kw):
+    o = _lib.ReadIO()
+    for f, _ in _lib.ReadIO._fields_:
+        if f not in ("events",):
+            setattr(o, f, FAKE if _ == ctypes.c_void_p else 0)
+    o.bank_dtype, o.rows, o.hd = _lib.SDM_BF16, 1 << 20, 128
+    o.step_rows, o.out_rows = 512, 1 << 20
+    o.P, o.C, o.W, o.R, o.N, o.first_partial, o.valid_last = 4, 128, 16, 16, 8, 8, 128
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+@pytest.mark.parametrize("kw,ti,status", [
+    (dict(C=0), 0, _lib.SDM_ESHAPE), (dict(C=257), 0, _lib.SDM_ESHAPE), (dict(R=0), 0, _lib.SDM_ESHAPE),
+    (dict(P=0), 0, _lib.SDM_ESHAPE), (dict(), 2, _lib.SDM_ESHAPE), (dict(), -1, _lib.SDM_ESHAPE),
+    (dict(hd=12), 0, _lib.SDM_ESHAPE), (dict(bank_dtype=7), 0, _lib.SDM_EINVAL),
+    (dict(valid_last=129), 0, _lib.SDM_EINVAL), (dict(first_partial=9), 0, _lib.SDM_EINVAL),
+    (dict(out_rows=100), 0, _lib.SDM_EINVAL), (dict(beta=None), 0, _lib.SDM_EINVAL),
+    (dict(dv=FAKE + 4), 0, _lib.SDM_EALIGN), (dict(a=FAKE + 2), 0, _lib.SDM_EALIGN),
+])
+def test_read_step_refusals(kw, ti, status):
+    lib = _lib.load()
+    o = read_io(**kw)
+    assert lib.sdm_read_step(ctypes.byref(o), ti, None) == status
+    assert len(lib.sdm_last_error()) > 0
+    assert lib.sdm_read_step(None, 0, None) == _lib.SDM_EINVAL
