@@ -63,6 +63,18 @@ def dw_bytes(groups, C, W, hd, bank_es, dv_es):
     return bank + C * hd * dv_es + 16 * C * W, bank
 
 
+def read_gather_bytes(P, C, W, R, hd, bank_es):
+    """One read-side gather launch: per entry its id and weight (8 B) and its bank row slice; p0 and
+    q0 written as float32 rows per token."""
+    return P * C * (W + R) * (hd * bank_es + 8) + 2 * P * C * hd * 4
+
+
+def read_solve_bytes(P, C, hd):
+    """One substitution launch: the A and QK triangles (dense float32), v, p0 and q0 read, dv, pred
+    and read written (float32 rows), beta."""
+    return 2 * P * C * C * 4 + 6 * P * C * hd * 4 + P * C * 4
+
+
 def source_digest(kernel):
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
@@ -128,10 +140,24 @@ def cpu_baseline(wl, bank0, n_chunks_target_s=15.0):
     with ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(run, jobs))
     t_dw = time.perf_counter() - t0
+    # A short sample (the whole workload can take well under a second) is repeated, whole passes
+    # only, until about 10 s of oracle work have been timed (at most 30 s).
+    passes = 1
+    one = t_p1 + t_dw
+    while t_p1 + t_dw < 10.0 and t_p1 + t_dw + one <= 30.0:
+        t0 = time.perf_counter()
+        oracle.phase1(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, P=wl.P, stream_offset=wl.stream_offset,
+                      first_partial=wl.first_partial, valid_last=wl.valid_last, chunks=chunks, threads=threads)
+        t_p1 += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(run, jobs))
+        t_dw += time.perf_counter() - t0
+        passes += 1
     return {
-        "value": m * n / (t_p1 + t_dw), "unit": "entries/s", "cores": threads, "kind": "oracle",
-        "sample": "%d of %d chunks (Phase 1 + the DW of the same chunks from the initial bank); "
-                  "phase1 %.2f s, dw %.2f s" % (m, wl.N, t_p1, t_dw),
+        "value": passes * m * n / (t_p1 + t_dw), "unit": "entries/s", "cores": threads, "kind": "oracle",
+        "sample": "%d of %d chunks (Phase 1 + the DW of the same chunks from the initial bank), %d passes; "
+                  "phase1 %.2f s, dw %.2f s" % (m, wl.N, passes, t_p1, t_dw),
     }
 
 
@@ -147,6 +173,8 @@ def main():
                     help="untimed steps for about S seconds before the warmup steps (clocks settle)")
     ap.add_argument("--pair-stream", action="store_true",
                     help="run the pair kernel on a second stream beside the DW steps (slower on uniform_bf16)")
+    ap.add_argument("--no-read-side", action="store_true",
+                    help="skip the separate measurement of the read side (gather + substitution) and the forward loop")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB device buffer 3 times (a known-traffic kernel for HBM counter scaling)")
     args = ap.parse_args()
@@ -304,10 +332,61 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if not args.no_read_side:
+        res["read_side"] = measure_read_side(args, wl, shape, out, ins, bank, plan, stream, W, sdm, torch)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on host cores)...")
         res["cpu_baseline"] = cpu_baseline(wl, bank0)
     print(json.dumps(res), flush=True)
+
+
+def measure_read_side(args, wl, shape, out, ins, bank, dw_plan, stream, W, sdm, torch):
+    """The read side of every step (gather + substitution kernels) timed by events bound to each
+    kernel, and the wall time of a forward loop: for each step the read side, then its DW step (the
+    DW then consumes the read side's token rows). Not part of the headline step."""
+    sh = wl.shape
+    P, C, hd = sh.P, sh.C, sh.hd
+    dev = bank.device
+    v_host, beta_host = W.make_read_inputs(wl)
+    v = torch.from_numpy(v_host).to(dev)
+    beta = torch.from_numpy(beta_host).to(dev)
+    dv = torch.zeros((v.shape[0], hd), dtype=torch.float32, device=dev)
+    pred, read = torch.zeros_like(dv), torch.zeros_like(dv)
+    rplan = sdm.ReadPlan(bank, out, ins["k_idx"], ins["q_idx"], v, beta, dv, pred, read, shape, step_rows=P * C)
+    fplan = sdm.DwPlan(bank, dv, out["krec"], shape, dv_step_rows=P * C)
+
+    def forward():
+        for ti in range(wl.steps):
+            rplan.step(ti)
+            fplan.step(ti)
+
+    for _ in range(2):
+        forward()
+    torch.cuda.synchronize()
+    reps = max(1, min(args.steps, 5))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        forward()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / reps
+    evs = [sdm.timing_events(4, stream) for _ in range(wl.steps)]
+    torch.cuda.synchronize()
+    for ti in range(wl.steps):
+        rplan.step(ti, events=evs[ti])
+    torch.cuda.synchronize()
+    ms_g = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_s = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    bank_es = 2 if sh.bank_dtype == "bf16" else 4
+    gb = read_gather_bytes(P, C, sh.W, sh.R, hd, bank_es)
+    sb = read_solve_bytes(P, C, hd)
+    return {
+        "gather_kernel": {"bytes_per_launch": gb, "ms_per_launch": ms_g, "GBps": gb / (ms_g * 1e-3) / 1e9,
+                          "frac": gb / (ms_g * 1e-3) / HBM_PEAK_BYTES},
+        "solve_kernel": {"bytes_per_launch": sb, "ms_per_launch": ms_s, "GBps": sb / (ms_s * 1e-3) / 1e9,
+                         "frac": sb / (ms_s * 1e-3) / HBM_PEAK_BYTES},
+        "forward_loop_ms": wall * 1e3,
+        "forward_loop": "every step: read side (2 kernels) then DW; %d steps, eager" % wl.steps,
+    }
 
 
 W_FIRST = -(1 << 31)      # bit 31 of the int32 record element

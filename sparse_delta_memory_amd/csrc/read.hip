@@ -12,10 +12,12 @@
 // Two kernels per step. read_gather_kernel: a team of 16 lanes per token, 8 columns per lane (16-byte
 // bf16 or two 16-byte float32 loads per row), entries taken 8 at a time with every row load in flight
 // before the first is used; p0 and q0 go to the pred and read outputs. read_solve_kernel: one block
-// per (chunk, 16 columns); the tokens are taken in blocks of 16: the A and QK rows of the block are
-// staged in LDS, every thread forms its token's right-hand side from the earlier blocks' dv, 16
-// threads (one per column) solve the block's unit triangle in order, then every thread adds its
-// token's pred and read terms. Sums run in a fixed order: results are reproducible.
+// per (chunk, 4 columns). It first inverts every 16 x 16 diagonal block of I + diag(beta) A (one
+// column of one block per lane, by substitution), then takes the tokens in blocks of 16: the
+// block's A and QK rows (loaded two blocks ahead) go to LDS; four lanes share each (token, column)
+// dot, every fourth term each, added by a fixed butterfly; the scaled right-hand side times the
+// block inverse's row gives dv, then the pred and read terms. Sums run in a fixed order: results
+// are reproducible.
 #include <hip/hip_ext.h>
 
 #include "sdm_device.hpp"
@@ -28,7 +30,7 @@ constexpr int kGTeam = 16;          // lanes per token in the gather
 constexpr int kGCols = 8;           // columns per lane
 constexpr int kGTok = 256 / kGTeam; // tokens per gather block
 constexpr int kGBatch = 8;          // entries whose rows are in flight together
-constexpr int kSB = 16;             // tokens per substitution block and columns per solve block
+constexpr int kSB = 16;             // tokens per substitution block
 
 struct ReadArgs {
     const void* bank;
@@ -132,65 +134,156 @@ __global__ void __launch_bounds__(256) read_gather_kernel(ReadArgs a) {
     oq[1] = make_float4(pq[4], pq[5], pq[6], pq[7]);
 }
 
+constexpr int kSC = 4;   // columns per substitution block
+constexpr int kKS = 4;   // lanes sharing one dot (each takes every kKS-th term)
+
+// Part of sum_{j0 <= j < j1} row[j] * col[j * kSC]: the terms with j = j0 + ks (mod kKS).
+__device__ __forceinline__ float lds_dot_part(const float* row, const float* col, int j0, int j1, int ks) {
+    float s = 0.0f;
+    for (int j = j0 + ks; j < j1; j += kKS) s = fmaf(row[j], col[j * kSC], s);
+    return s;
+}
+
+// The kKS parts of a dot (lanes 4 and 8 apart) added by a butterfly: every lane gets the same bits
+// ((p0 + p1) + (p2 + p3), float addition being commutative).
+__device__ __forceinline__ float dot_total(float s) {
+    s += __shfl_xor(s, kSC, kWave);
+    s += __shfl_xor(s, kSC * 2, kWave);
+    return s;
+}
+
+// Dynamic LDS of the substitution kernel (floats): dv of every token (C x kSC), the current block's
+// A and QK rows (16 x (C + 1) each, padded against bank conflicts), the inverses of the diagonal
+// blocks (C x 16) and the block's scaled right-hand sides (16 x kSC).
+size_t solve_lds_bytes(int C) {
+    return sizeof(float) * (static_cast<size_t>(C) * kSC + static_cast<size_t>(kSB) * (C + 1) * 2 +
+                            static_cast<size_t>(C) * kSB + kSB * kSC);
+}
+
 __global__ void __launch_bounds__(256) read_solve_kernel(ReadArgs a) {
-    __shared__ float sdv[256][kSB];        // dv of every token so far, this block's 16 columns
-    __shared__ float sA[kSB][256 + 1];      // A rows of the current token block (columns 0 .. b0+15)
-    __shared__ float sQ[kSB][256 + 1];      // QK rows of the current token block
-    __shared__ float srhs[kSB][kSB];        // right-hand sides of the current token block
-    const int col_blocks = (a.hd + kSB - 1) / kSB;
+    extern __shared__ float lds[];
+    const int C = a.C;
+    const int ld = C + 1;
+    float* sdv = lds;                   // [C][kSC]
+    float* sA = sdv + C * kSC;          // [16][ld]
+    float* sQ = sA + kSB * ld;          // [16][ld]
+    float* sT = sQ + kSB * ld;          // [C][16]: row t holds row (t mod 16) of its block's inverse
+    float* srhs = sT + C * kSB;         // [16][kSC]
+    const int tid = static_cast<int>(threadIdx.x);
+    // Lanes: token in block tl (tid / 16), dot part ks, column d (tid = tl * 16 + ks * kSC + d).
+    const int tl = tid / kSB;
+    const int ks = (tid / kSC) % kKS;
+    const int d = tid % kSC;
+    // Staging and inverse lanes: row / block sr (tid / 16), lane sl (tid % 16).
+    const int sr = tid / kSB, sl = tid % kSB;
+    const int col_blocks = (a.hd + kSC - 1) / kSC;
     const int p = blockIdx.x / col_blocks;
-    const int d = static_cast<int>(threadIdx.x) % kSB;       // column within the block
-    const int tl = static_cast<int>(threadIdx.x) / kSB;      // token within a token block
-    const int col = (blockIdx.x % col_blocks) * kSB + d;
+    const int col = (blockIdx.x % col_blocks) * kSC + d;
     const bool col_ok = col < a.hd;
     const int64_t c = a.chunk0 + p;
-    const int C = a.C;
     const int tv = c >= a.first_partial ? a.valid_last : C;
     const float* A = a.a + c * C * C;
     const float* QK = a.qk + c * C * C;
+    const float* beta = a.beta + c * C;
     const int64_t rbase = a.row0 + static_cast<int64_t>(p) * C;
-    for (int b0 = 0; b0 < C; b0 += kSB) {
+    const int nblk = (C + kSB - 1) / kSB;
+
+    // Inverse of every diagonal block T_b = I + diag(beta_b) A_bb (unit lower triangular): lane
+    // (block sr, column sl) solves T_b x = e_sl by substitution; masked tokens have beta taken as 0.
+    if (sr < nblk) {
+        const int t0 = sr * kSB;
+        float al[kSB][kSB];
+        float bt[kSB];
+#pragma unroll
+        for (int i = 0; i < kSB; ++i) {
+            const bool ok = t0 + i < tv;
+            bt[i] = ok ? beta[t0 + i] : 0.0f;
+#pragma unroll
+            for (int k = 0; k < i; ++k) al[i][k] = ok ? A[static_cast<int64_t>(t0 + i) * C + t0 + k] : 0.0f;
+        }
+        float x[kSB];
+#pragma unroll
+        for (int i = 0; i < kSB; ++i) {
+            float s = 0.0f;
+#pragma unroll
+            for (int k = 0; k < i; ++k) s = fmaf(al[i][k], x[k], s);
+            x[i] = (i == sl ? 1.0f : 0.0f) - bt[i] * s;
+            if (t0 + i < C) sT[(t0 + i) * kSB + sl] = x[i];
+        }
+    }
+
+    // Staged rows of token block b (row sr, columns sl + 16u) and this lane's token values, loaded
+    // two blocks ahead.
+    float stA[kSB], stQ[kSB], stA2[kSB], stQ2[kSB];
+    float nx_p0 = 0.0f, nx_v = 0.0f, nx_q0 = 0.0f, nx_b = 0.0f;
+    float nx2_p0 = 0.0f, nx2_v = 0.0f, nx2_q0 = 0.0f, nx2_b = 0.0f;
+    // Loads of block b into the second set (two blocks ahead of their use).
+    auto prefetch = [&](int b) {
+        const int b0 = b * kSB;
+        const int tr = b0 + sr;
+        const int groups = b + 1;                   // column groups of 16 up to the block's diagonal
+#pragma unroll
+        for (int u = 0; u < kSB; ++u) {
+            const int j = sl + kSB * u;
+            const bool in = tr < C && u < groups && j < C;
+            stA2[u] = in ? A[static_cast<int64_t>(tr) * C + j] : 0.0f;
+            stQ2[u] = in ? QK[static_cast<int64_t>(tr) * C + j] : 0.0f;
+        }
         const int t = b0 + tl;
         const bool valid = t < tv && col_ok;
-        // Stage the block's A and QK rows, columns 0 .. b0 + 15.
-        const int wcols = b0 + kSB;
-        for (int i = threadIdx.x; i < kSB * wcols; i += 256) {
-            const int r = i / wcols, j = i - r * wcols;
-            const bool in = b0 + r < C && j < C;   // the block's rows; columns past C are zero
-            sA[r][j] = in ? A[static_cast<int64_t>(b0 + r) * C + j] : 0.0f;
-            sQ[r][j] = in ? QK[static_cast<int64_t>(b0 + r) * C + j] : 0.0f;
+        nx2_p0 = valid ? a.pred[(rbase + t) * a.hd + col] : 0.0f;
+        nx2_v = valid ? a.v[(rbase + t) * a.hd + col] : 0.0f;
+        nx2_q0 = valid ? a.read[(rbase + t) * a.hd + col] : 0.0f;
+        nx2_b = valid ? beta[t] : 0.0f;
+    };
+    auto shift = [&]() {   // the second set becomes the next block's
+#pragma unroll
+        for (int u = 0; u < kSB; ++u) {
+            stA[u] = stA2[u];
+            stQ[u] = stQ2[u];
         }
-        __syncthreads();
-        // Right-hand side: v - p0 - (terms of earlier blocks).
-        float far = 0.0f;
-        for (int j = 0; j < b0; ++j) far = fmaf(sA[tl][j], sdv[j][d], far);
-        const float p0 = valid ? a.pred[(rbase + t) * a.hd + col] : 0.0f;
-        const float vv = valid ? a.v[(rbase + t) * a.hd + col] : 0.0f;
-        srhs[tl][d] = valid ? (vv - p0) - far : 0.0f;
-        __syncthreads();
-        // The block's unit triangle, in token order, one thread per column.
-        if (tl == 0) {
-            float x[kSB];
+        nx_p0 = nx2_p0;
+        nx_v = nx2_v;
+        nx_q0 = nx2_q0;
+        nx_b = nx2_b;
+    };
+    prefetch(0);
+    shift();
+    if (nblk > 1) prefetch(1);
+    for (int b = 0; b < nblk; ++b) {
+        const int b0 = b * kSB;
+        const int t = b0 + tl;
+        const bool valid = t < tv && col_ok;
+        const int groups = b + 1;
 #pragma unroll
-            for (int i = 0; i < kSB; ++i) {
-                float s = srhs[i][d];
-#pragma unroll
-                for (int k = 0; k < i; ++k) s = fmaf(-sA[i][b0 + k], x[k], s);
-                const bool ok = b0 + i < tv && col_ok;
-                x[i] = ok ? a.beta[c * C + b0 + i] * s : 0.0f;
-                if (b0 + i < C) sdv[b0 + i][d] = x[i];
+        for (int u = 0; u < kSB; ++u) {
+            if (u < groups && sl + kSB * u < C) {
+                sA[sr * ld + sl + kSB * u] = stA[u];
+                sQ[sr * ld + sl + kSB * u] = stQ[u];
             }
+        }
+        const float p0 = nx_p0, vv = nx_v, q0 = nx_q0, bt = nx_b;
+        if (b + 1 < nblk) shift();
+        if (b + 2 < nblk) prefetch(b + 2);
+        __syncthreads();   // the block's rows (and, first time, the inverses) are in LDS
+        // Scaled right-hand side: beta (v - p0 - terms of the earlier blocks).
+        const float far = dot_total(lds_dot_part(sA + tl * ld, sdv + d, 0, b0, ks));
+        if (ks == 0) srhs[tl * kSC + d] = valid ? bt * ((vv - p0) - far) : 0.0f;
+        __syncthreads();
+        // dv of the block: the inverse's row times the scaled right-hand sides.
+        float x = 0.0f;
+        if (t < C) {
+            for (int k = 0; k <= tl; ++k) x = fmaf(sT[t * kSB + k], srhs[k * kSC + d], x);
+            if (ks == 0) sdv[t * kSC + d] = valid ? x : 0.0f;
         }
         __syncthreads();
         // pred and read of the block's tokens.
-        if (t < C && col_ok) {
-            float near = 0.0f;
-            for (int j = b0; j < t; ++j) near = fmaf(sA[tl][j], sdv[j][d], near);
-            float rd = 0.0f;
-            for (int j = 0; j <= t; ++j) rd = fmaf(sQ[tl][j], sdv[j][d], rd);
-            const float q0 = valid ? a.read[(rbase + t) * a.hd + col] : 0.0f;
+        const int tt = t < C ? t : 0;
+        const float near = dot_total(lds_dot_part(sA + tl * ld, sdv + d, b0, t < C ? t : b0, ks));
+        const float rd = dot_total(lds_dot_part(sQ + tl * ld, sdv + d, 0, t < C ? tt + 1 : 0, ks));
+        if (ks == 0 && t < C && col_ok) {
             const int64_t o = (rbase + t) * a.hd + col;
-            a.dv[o] = sdv[t][d];
+            a.dv[o] = valid ? x : 0.0f;
             a.pred[o] = valid ? (p0 + far) + near : 0.0f;
             a.read[o] = valid ? q0 + rd : 0.0f;
         }
@@ -235,9 +328,13 @@ hipError_t read_launch(const ReadLaunch& L, hipStream_t st) {
     hipError_t e = hipExtLaunchKernel(g, dim3(static_cast<unsigned>(a.P * tok_blocks * col_blocks)), dim3(256), kargs, 0,
                                       st, ev[0], ev[1], 0);
     if (e != hipSuccess) return e;
-    const int solve_blocks = a.P * ((a.hd + kSB - 1) / kSB);
+    const int solve_blocks = a.P * ((a.hd + kSC - 1) / kSC);
+    const size_t lds = solve_lds_bytes(a.C);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&read_solve_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(lds));
+    if (e != hipSuccess) return e;
     return hipExtLaunchKernel(reinterpret_cast<const void*>(&read_solve_kernel), dim3(static_cast<unsigned>(solve_blocks)),
-                              dim3(256), kargs, 0, st, ev[2], ev[3], 0);
+                              dim3(256), kargs, lds, st, ev[2], ev[3], 0);
 }
 
 }  // namespace sdm
