@@ -36,6 +36,8 @@ KERNEL_SOURCES = {   # the files each kernel's code comes from (traffic counters
     "p1_main_kernel": ["phase1.hip", "sdm_device.hpp"],
     "p1_pairs_kernel": ["phase1.hip", "sdm_device.hpp"],
     "dw_kernel": ["dw.hip", "sdm_device.hpp"],
+    "read_gather_kernel": ["read.hip", "sdm_device.hpp"],
+    "read_solve_kernel": ["read.hip", "sdm_device.hpp"],
 }
 
 

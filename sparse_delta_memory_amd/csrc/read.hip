@@ -176,9 +176,11 @@ __global__ void __launch_bounds__(256) read_solve_kernel(ReadArgs a) {
     const int d = tid % kSC;
     // Staging and inverse lanes: row / block sr (tid / 16), lane sl (tid % 16).
     const int sr = tid / kSB, sl = tid % kSB;
-    const int col_blocks = (a.hd + kSC - 1) / kSC;
-    const int p = blockIdx.x / col_blocks;
-    const int col = (blockIdx.x % col_blocks) * kSC + d;
+    // Block b is (chunk b mod P, column group b / P): consecutive blocks go round the XCDs (8, each
+    // with its own L2), so a chunk's column groups share one XCD when P is a multiple of 8 (and
+    // 8 / gcd(P, 8) otherwise) and its A / QK rows are fetched from HBM once per XCD, not per block.
+    const int p = static_cast<int>(blockIdx.x) % a.P;
+    const int col = (static_cast<int>(blockIdx.x) / a.P) * kSC + d;
     const bool col_ok = col < a.hd;
     const int64_t c = a.chunk0 + p;
     const int tv = c >= a.first_partial ? a.valid_last : C;
