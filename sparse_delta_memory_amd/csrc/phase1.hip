@@ -232,7 +232,7 @@ __device__ __forceinline__ uint32_t block_exclusive_add(uint32_t v, uint32_t* ws
 // the fewest passes of at most `dmax` bits, the bits shared out evenly among them. Items live in registers in striped order (item k of lane l of wave
 // w is element w * 64 * IPT + k * 64 + l). Per digit: ranks inside the wave from ballot-built
 // peer masks, slice by slice (equal digits keep element order); per-wave digit counts in LDS
-// (rows of 2^dmax); one block scan over (digit, wave) gives every (wave, digit) its start; a
+// (rows of 2^dmax + 1); one block scan over (digit, wave) gives every (wave, digit) its start; a
 // scatter into skey / sval. On return skey / sval hold the sorted sequence.
 template <int IPT>
 __device__ void block_radix_sort(uint32_t (&key)[IPT], uint32_t (&val)[IPT], int bits, int dmax, uint32_t* skey,
@@ -240,7 +240,7 @@ __device__ void block_radix_sort(uint32_t (&key)[IPT], uint32_t (&val)[IPT], int
     const int lane = static_cast<int>(lane_id());
     const int w = threadIdx.x / kWave;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-    const int stride = 1 << dmax;
+    const int stride = (1 << dmax) + 1;   // rows padded by a word: the (digit, wave) scan spreads over the banks
     uint32_t* my_hist = hist + w * stride;
     const int passes = (bits + dmax - 1) / dmax;
     const int width = (bits + passes - 1) / passes;   // digits of (nearly) equal width, at most dmax
@@ -1404,6 +1404,9 @@ int sweep_bytes(const sdm_p1_shape* s, uint32_t kinds, int tokens) {
     return nk * 12 + nq * 8;
 }
 
+// LDS bytes of the per-wave digit counts: kNW rows of 2^d counts, each padded by one word.
+int hist_bytes(int d) { return kNW * ((1 << d) + 1) * 4; }
+
 MainPlan plan_main(const sdm_p1_shape* s, bool with_pairs_ws) {
     MainPlan m;
     const int n = s->C * (s->W + s->R);
@@ -1419,18 +1422,18 @@ MainPlan plan_main(const sdm_p1_shape* s, bool with_pairs_ws) {
     m.resident = 0;
     int d = 10;
     if (m.ipt <= 8) {
-        while (d > 4 && np * 4 + vals_bytes + kNW * (1 << d) * 4 > cap_max) --d;
-        m.resident = np * 4 + vals_bytes + max(kNW * (1 << d) * 4, sweep_bytes(s, kSweepK | kSweepQ, s->C)) <= cap_max;
+        while (d > 4 && np * 4 + vals_bytes + hist_bytes(d) > cap_max) --d;
+        m.resident = np * 4 + vals_bytes + max(hist_bytes(d), sweep_bytes(s, kSweepK | kSweepQ, s->C)) <= cap_max;
     }
     if (!m.resident) {
         d = 10;
-        while (d > 4 && np * 4 + kNW * (1 << d) * 4 > cap_max) --d;
+        while (d > 4 && np * 4 + hist_bytes(d) > cap_max) --d;
     }
     m.digit_bits = d;
     m.vals_off = np * 4;
     m.hist_off = np * 4 + (m.resident ? vals_bytes : 0);
     m.rec_off = m.resident ? m.hist_off : 0;
-    int cap = m.hist_off + kNW * (1 << d) * 4;
+    int cap = m.hist_off + hist_bytes(d);
     // Sweeps: every record at once up to 8 items per thread, else each kind in token ranges
     // (multiples of 4 tokens, so every range starts 16-byte aligned in the entry-order rows).
     Sweeps& sw = m.sweeps;
