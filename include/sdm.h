@@ -69,6 +69,8 @@ typedef struct sdm_p1_shape {
                                p1_scan_kernel: the gate is read at token * width + lane * stride). With 1,
                                a token that writes one slot from several lanes applies the gate of the
                                lowest of those lanes (its other writes there are repeats). */
+    int32_t idx_bytes;      /* width of the slot ids k_idx / q_idx: 0 or 4 = int32, 8 = int64 (every
+                               absolute slot is below 2^31 either way) */
 } sdm_p1_shape;
 
 /*
@@ -80,8 +82,8 @@ typedef struct sdm_p1_shape {
  */
 typedef struct sdm_p1_io {
     /* inputs */
-    const int32_t* k_idx;   /* [N, C, W] absolute slot ids of the writes */
-    const int32_t* q_idx;   /* [N, C, R] absolute slot ids of the reads */
+    const void* k_idx;      /* [N, C, W] absolute slot ids of the writes, int32 or int64 (idx_bytes) */
+    const void* q_idx;      /* [N, C, R] absolute slot ids of the reads, same type */
     const float* k_val;     /* [N, C, W] write values */
     const float* q_val;     /* [N, C, R] read values */
     const float* g;         /* gates (log decays): [N, C] per token, or [N, C, W] per (token, K lane)
@@ -205,8 +207,8 @@ typedef struct sdm_read_io {
     int32_t bank_dtype;     /* sdm_dtype */
     int64_t rows;           /* bank rows (an id outside 0..rows-1 contributes nothing) */
     int32_t hd;             /* row width, a multiple of 8 */
-    const int32_t* k_idx;   /* [N, C, W] absolute slot ids of the writes (Phase-1 input) */
-    const int32_t* q_idx;   /* [N, C, R] absolute slot ids of the reads */
+    const void* k_idx;      /* [N, C, W] absolute slot ids of the writes (Phase-1 input), int32 or int64 */
+    const void* q_idx;      /* [N, C, R] absolute slot ids of the reads, same type */
     const float* k_eff;     /* [N, C, W] from sdm_phase1 */
     const float* q_w;       /* [N, C, R] from sdm_phase1 */
     const float* a;         /* [N, C, C] from sdm_phase1 */
@@ -222,6 +224,7 @@ typedef struct sdm_read_io {
     int32_t P, C, W, R, N;  /* the Phase-1 shape */
     int32_t first_partial;  /* as in sdm_p1_shape: tokens >= valid_last of chunks >= first_partial are masked */
     int32_t valid_last;
+    int32_t idx_bytes;      /* width of k_idx / q_idx: 0 or 4 = int32, 8 = int64 */
     hipEvent_t* events;     /* optional (NULL: none): 4 caller-created events bound to the start and end of
                                the gather kernel ([0], [1]) and of the substitution kernel ([2], [3]) */
 } sdm_read_io;

@@ -23,11 +23,12 @@ __all__ = ["P1Shape", "phase1", "phase1_workspace_bytes", "alloc_phase1_outputs"
 
 
 def make_shape(N, C, W, R, P=1, key_bits=16, stream_offset=0, first_partial=None, valid_last=None, tile_len=128,
-               g_lane_stride=0):
-    """Phase-1 shape. g_lane_stride 0: gates g [N, C] (per token); 1: g [N, C, W] (per token and K lane)."""
+               g_lane_stride=0, idx_bytes=4):
+    """Phase-1 shape. g_lane_stride 0: gates g [N, C] (per token); 1: g [N, C, W] (per token and K lane).
+    idx_bytes 4: int32 slot ids; 8: int64."""
     return P1Shape(int(N), int(C), int(W), int(R), int(P), int(key_bits), int(stream_offset),
                    int(N if first_partial is None else first_partial), int(C if valid_last is None else valid_last),
-                   int(tile_len), int(g_lane_stride))
+                   int(tile_len), int(g_lane_stride), int(idx_bytes))
 
 
 def phase1_workspace_bytes(shape: P1Shape) -> int:
@@ -63,7 +64,8 @@ def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=No
            pair_stream=None, pair_ready=None):
     """Enqueue Phase 1 of shape.N chunks on the current (or given) stream; returns the outputs.
 
-    Inputs are contiguous device tensors: k_idx [N,C,W] int32, q_idx [N,C,R] int32, k_val / q_val
+    Inputs are contiguous device tensors: k_idx [N,C,W] / q_idx [N,C,R] int32 (int64 with
+    shape.idx_bytes = 8), k_val / q_val
     float32 of the same shapes, g [N,C] float32 ([N,C,W] when shape.g_lane_stride = 1). `out` is a dict from alloc_phase1_outputs (a
     missing key skips that optional output). events: optional 4 torch.cuda.Events (timing_events)
     bound to the two kernels. pair_stream / pair_ready: optional torch stream and recorded event:
@@ -72,6 +74,9 @@ def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=No
     import torch
 
     lib = _lib.load()
+    want = 8 if shape.idx_bytes == 8 else 4
+    if k_idx.element_size() != want or q_idx.element_size() != want:
+        raise TypeError("phase1: ids must be int%d (shape.idx_bytes = %d)" % (want * 8, shape.idx_bytes))
     if out is None:
         out = alloc_phase1_outputs(shape, device=k_idx.device)
     need = phase1_workspace_bytes(shape)
@@ -215,6 +220,9 @@ class ReadPlan:
         io.out_rows = min(v.shape[0], dv.shape[0], pred.shape[0], read.shape[0])
         io.P, io.C, io.W, io.R, io.N = shape.P, shape.C, shape.W, shape.R, shape.N
         io.first_partial, io.valid_last = shape.first_partial, shape.valid_last
+        io.idx_bytes = k_idx.element_size()
+        if q_idx.dtype != k_idx.dtype or k_idx.dtype not in (torch.int32, torch.int64):
+            raise TypeError("ReadPlan: k_idx and q_idx must both be int32 or both int64")
         self.io = io
         self._io_ref = ctypes.byref(io)
         self._device = bank.device

@@ -46,6 +46,8 @@ sdm_status check_p1_shape(const sdm_p1_shape* s) {
     if (s->valid_last < 0 || s->valid_last > s->C)
         return fail(SDM_EINVAL, "sdm_phase1: valid_last = %d outside 0..C", s->valid_last);
     if (s->tile_len < 1) return fail(SDM_EINVAL, "sdm_phase1: tile_len = %d < 1", s->tile_len);
+    if (s->idx_bytes != 0 && s->idx_bytes != 4 && s->idx_bytes != 8)
+        return fail(SDM_EINVAL, "sdm_phase1: idx_bytes = %d (0 or 4: int32 ids; 8: int64 ids)", s->idx_bytes);
     if (s->g_lane_stride != 0 && s->g_lane_stride != 1)
         return fail(SDM_EINVAL, "sdm_phase1: g_lane_stride = %d (0: gates [N, C]; 1: gates [N, C, W])", s->g_lane_stride);
     const int64_t n = static_cast<int64_t>(s->C) * (s->W + s->R);
@@ -103,6 +105,8 @@ sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st
         if (!aligned(p, 4)) return fail(SDM_EALIGN, "sdm_phase1: a 4-byte field is misaligned");
     }
     if (!aligned(io->krec, 16)) return fail(SDM_EALIGN, "sdm_phase1: krec is not 16-byte aligned");
+    if (s->idx_bytes == 8 && (!aligned(io->k_idx, 8) || !aligned(io->q_idx, 8)))
+        return fail(SDM_EALIGN, "sdm_phase1: int64 ids must be 8-byte aligned");
     const sdm::P1Workspace ws = sdm::p1_workspace_layout(s);
     if (io->workspace == nullptr || io->workspace_bytes < ws.total)
         return fail(SDM_EWORKSPACE, "sdm_phase1: workspace needs %zu bytes, got %zu", ws.total,
@@ -147,6 +151,10 @@ sdm_status sdm_read_step(const sdm_read_io* io, int64_t ti, hipStream_t st) {
         return fail(SDM_EINVAL, "sdm_read_step: first_partial = %d, valid_last = %d", io->first_partial, io->valid_last);
     if (io->bank_dtype != SDM_F32 && io->bank_dtype != SDM_BF16)
         return fail(SDM_EINVAL, "sdm_read_step: bank_dtype %d", io->bank_dtype);
+    if (io->idx_bytes != 0 && io->idx_bytes != 4 && io->idx_bytes != 8)
+        return fail(SDM_EINVAL, "sdm_read_step: idx_bytes = %d (0 or 4: int32 ids; 8: int64 ids)", io->idx_bytes);
+    if (io->idx_bytes == 8 && (!aligned(io->k_idx, 8) || !aligned(io->q_idx, 8)))
+        return fail(SDM_EALIGN, "sdm_read_step: int64 ids must be 8-byte aligned");
     if (io->hd < 8 || io->hd > 4096 || io->hd % 8 != 0)
         return fail(SDM_ESHAPE, "sdm_read_step: hd = %d (multiple of 8 in 8..4096)", io->hd);
     if (io->rows < 0 || io->step_rows < 0 || io->out_rows < 0)

@@ -82,8 +82,8 @@ __device__ __forceinline__ void gstore(const void* base, uint32_t i, T v) {
 }
 
 struct P1Args {
-    const int32_t* k_idx;
-    const int32_t* q_idx;
+    const void* k_idx;   // int32 or int64 ids
+    const void* q_idx;
     const float* k_val;
     const float* q_val;
     const float* g;
@@ -329,9 +329,19 @@ struct Entry {
     float v;
 };
 
+// Slot id i of an int32 or int64 id array (absolute slots are below 2^31 either way).
+template <bool ID64>
+__device__ __forceinline__ int64_t load_id(const void* ids, int64_t i) {
+    if constexpr (ID64) {
+        return static_cast<const int64_t*>(ids)[i];
+    } else {
+        return static_cast<const int32_t*>(ids)[i];
+    }
+}
+
 // LG: gates per (token, K lane), [N, C, W], read from global memory where a scan needs one;
-// otherwise per token, [N, C], staged in LDS.
-template <int IPT, bool LG>
+// otherwise per token, [N, C], staged in LDS. ID64: slot ids are int64 (else int32).
+template <int IPT, bool LG, bool ID64>
 __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     constexpr int NP = kNT * IPT;
     constexpr int NTILE = (NP + kTile - 1) / kTile;
@@ -390,7 +400,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     // ---- 1. keys (element i of the striped layout is entry r = i) and the sort.
     {
         uint32_t key[IPT], val[IPT];
-        int32_t ids[IPT];
+        int64_t ids[IPT];
         // Every item loads (padding items re-read entry 0) before any id is used: the asm below
         // keeps the compiler from sinking a load into the select that uses it, where each load
         // would get a wait of its own.
@@ -401,7 +411,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             const int ic = i < n ? i : 0;
             const int t = token_of_entry(ic, a.wr_magic);
             const int j = ic - t * wr;
-            ids[k] = *(j < W ? a.k_idx + cw + t * W + j : a.q_idx + cr + t * R + (j - W));
+            ids[k] = load_id<ID64>(j < W ? a.k_idx : a.q_idx, j < W ? cw + t * W + j : cr + t * R + (j - W));
         }
         // Resident layout: the entries' values in entry order (coalesced, issued beside the ids;
         // the invalid tokens' values, which may be anything, are not used).
@@ -416,13 +426,13 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             }
         }
 #pragma unroll
-        for (int k = 0; k < IPT; ++k) asm volatile("" ::"v"(ids[k]));
+        for (int k = 0; k < IPT; ++k) asm volatile("" ::"v"(ids[k]));   // (64-bit ids: a register pair)
 #pragma unroll
         for (int k = 0; k < IPT; ++k) {
             const int i = w * kWave * IPT + k * kWave + lane;
             const int t = token_of_entry(i < n ? i : 0, a.wr_magic);
             const uint32_t kv =
-                t < tv ? static_cast<uint32_t>(static_cast<int64_t>(ids[k]) - id_base) & (key_lim - 1u) : key_lim;
+                t < tv ? static_cast<uint32_t>(ids[k] - id_base) & (key_lim - 1u) : key_lim;
             key[k] = i < n ? kv : pad_key;
         }
         if (res) {
@@ -718,7 +728,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                         if constexpr (sk) kid[k] = static_cast<int32_t>(p < n ? skey[p] : 0u);
                     } else {
                         vl[k] = *(q ? a.q_val + cr + t * R + (j - W) : a.k_val + cw + t * W + j);
-                        if constexpr (sk) kid[k] = a.k_idx[cw + ((!q && t < tv) ? t * W + j : 0)];
+                        if constexpr (sk) kid[k] = static_cast<int32_t>(load_id<ID64>(a.k_idx, cw + ((!q && t < tv) ? t * W + j : 0)));
                     }
                 }
                 if (!res) {
@@ -1463,10 +1473,12 @@ MainPlan plan_main(const sdm_p1_shape* s, bool with_pairs_ws) {
 }
 
 template <int IPT>
-hipError_t launch_main(P1Args args, bool lane_gates, size_t lds, int N, hipStream_t st, hipEvent_t start,
+hipError_t launch_main(P1Args args, bool lane_gates, bool id64, size_t lds, int N, hipStream_t st, hipEvent_t start,
                        hipEvent_t stop) {
-    const void* fn = lane_gates ? reinterpret_cast<const void*>(&p1_main_kernel<IPT, true>)
-                                : reinterpret_cast<const void*>(&p1_main_kernel<IPT, false>);
+    const void* fn = lane_gates ? (id64 ? reinterpret_cast<const void*>(&p1_main_kernel<IPT, true, true>)
+                                        : reinterpret_cast<const void*>(&p1_main_kernel<IPT, true, false>))
+                                : (id64 ? reinterpret_cast<const void*>(&p1_main_kernel<IPT, false, true>)
+                                        : reinterpret_cast<const void*>(&p1_main_kernel<IPT, false, false>));
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     void* kargs[] = {&args};
@@ -1580,11 +1592,11 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     }
     hipError_t e;
     switch (m.ipt) {
-        case 1: e = launch_main<1>(a, s->g_lane_stride != 0, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
-        case 2: e = launch_main<2>(a, s->g_lane_stride != 0, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
-        case 4: e = launch_main<4>(a, s->g_lane_stride != 0, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
-        case 8: e = launch_main<8>(a, s->g_lane_stride != 0, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
-        default: e = launch_main<16>(a, s->g_lane_stride != 0, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        case 1: e = launch_main<1>(a, s->g_lane_stride != 0, s->idx_bytes == 8, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        case 2: e = launch_main<2>(a, s->g_lane_stride != 0, s->idx_bytes == 8, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        case 4: e = launch_main<4>(a, s->g_lane_stride != 0, s->idx_bytes == 8, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        case 8: e = launch_main<8>(a, s->g_lane_stride != 0, s->idx_bytes == 8, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        default: e = launch_main<16>(a, s->g_lane_stride != 0, s->idx_bytes == 8, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
     }
     if (e != hipSuccess || !pairs) return e;
     PairArgs pa;

@@ -35,8 +35,8 @@ constexpr int kSB = 16;             // tokens per substitution block
 struct ReadArgs {
     const void* bank;
     int64_t rows;
-    const int32_t* k_idx;
-    const int32_t* q_idx;
+    const void* k_idx;   // int32 or int64 ids
+    const void* q_idx;
     const float* k_eff;
     const float* q_w;
     const float* a;
@@ -74,24 +74,29 @@ __device__ __forceinline__ void widen_row8(const uint4 (&raw)[BF16 ? 1 : 2], flo
     }
 }
 
-// sum_e w[e] M0[idx[e]] over n entries, 8 columns of one token; entries kGBatch at a time.
-template <bool BF16>
-__device__ __forceinline__ void gather_sum(const ReadArgs& a, const int32_t* idx, const float* w, int n, int col0,
+// sum_e w[e] M0[idx[e]] over n entries (idx: int32, or int64 when ID64), 8 columns of one token;
+// entries kGBatch at a time.
+template <bool BF16, bool ID64>
+__device__ __forceinline__ void gather_sum(const ReadArgs& a, const void* idx, const float* w, int n, int col0,
                                            float (&acc)[kGCols]) {
     for (int e0 = 0; e0 < n; e0 += kGBatch) {
-        int32_t s[kGBatch];
+        int64_t s[kGBatch];
         float ws[kGBatch];
 #pragma unroll
         for (int b = 0; b < kGBatch; ++b) {
             const int e = min(e0 + b, n - 1);
-            s[b] = idx[e];
+            if constexpr (ID64) {
+                s[b] = static_cast<const int64_t*>(idx)[e];
+            } else {
+                s[b] = static_cast<const int32_t*>(idx)[e];
+            }
             ws[b] = e0 + b < n ? w[e] : 0.0f;
         }
         uint4 raw[kGBatch][BF16 ? 1 : 2];
 #pragma unroll
         for (int b = 0; b < kGBatch; ++b) {
             // A slot outside the bank contributes nothing (its row is not read).
-            const bool ok = s[b] >= 0 && static_cast<int64_t>(s[b]) < a.rows;
+            const bool ok = s[b] >= 0 && s[b] < a.rows;
             load_row8<BF16>(a.bank, ok ? s[b] : 0, a.hd, col0, raw[b]);
             if (!ok) ws[b] = 0.0f;
         }
@@ -105,7 +110,7 @@ __device__ __forceinline__ void gather_sum(const ReadArgs& a, const int32_t* idx
     }
 }
 
-template <bool BF16>
+template <bool BF16, bool ID64>
 __global__ void __launch_bounds__(256) read_gather_kernel(ReadArgs a) {
     const int tok_blocks = (a.C + kGTok - 1) / kGTok;
     const int col_blocks = (a.hd + kGTeam * kGCols - 1) / (kGTeam * kGCols);
@@ -123,8 +128,9 @@ __global__ void __launch_bounds__(256) read_gather_kernel(ReadArgs a) {
     for (int q = 0; q < kGCols; ++q) pk[q] = pq[q] = 0.0f;
     if (t < tv) {
         const int64_t ko = (c * a.C + t) * a.W, qo = (c * a.C + t) * a.R;
-        gather_sum<BF16>(a, a.k_idx + ko, a.k_eff + ko, a.W, col0, pk);
-        gather_sum<BF16>(a, a.q_idx + qo, a.q_w + qo, a.R, col0, pq);
+        const int es = ID64 ? 8 : 4;
+        gather_sum<BF16, ID64>(a, static_cast<const char*>(a.k_idx) + ko * es, a.k_eff + ko, a.W, col0, pk);
+        gather_sum<BF16, ID64>(a, static_cast<const char*>(a.q_idx) + qo * es, a.q_w + qo, a.R, col0, pq);
     }
     float4* op = reinterpret_cast<float4*>(a.pred + row * a.hd + col0);
     float4* oq = reinterpret_cast<float4*>(a.read + row * a.hd + col0);
@@ -325,8 +331,12 @@ hipError_t read_launch(const ReadLaunch& L, hipStream_t st) {
     const hipEvent_t ev[4] = {io->events ? io->events[0] : nullptr, io->events ? io->events[1] : nullptr,
                               io->events ? io->events[2] : nullptr, io->events ? io->events[3] : nullptr};
     void* kargs[] = {&a};
-    const void* g = io->bank_dtype == SDM_BF16 ? reinterpret_cast<const void*>(&read_gather_kernel<true>)
-                                               : reinterpret_cast<const void*>(&read_gather_kernel<false>);
+    const bool id64 = io->idx_bytes == 8;
+    const void* g = io->bank_dtype == SDM_BF16
+                        ? (id64 ? reinterpret_cast<const void*>(&read_gather_kernel<true, true>)
+                                : reinterpret_cast<const void*>(&read_gather_kernel<true, false>))
+                        : (id64 ? reinterpret_cast<const void*>(&read_gather_kernel<false, true>)
+                                : reinterpret_cast<const void*>(&read_gather_kernel<false, false>));
     hipError_t e = hipExtLaunchKernel(g, dim3(static_cast<unsigned>(a.P * tok_blocks * col_blocks)), dim3(256), kargs, 0,
                                       st, ev[0], ev[1], 0);
     if (e != hipSuccess) return e;

@@ -21,7 +21,7 @@ def shape_of(wl: W.Workload, tile_len: int = 128):
     s = wl.shape
     return sdm.make_shape(wl.N, s.C, s.W, s.R, P=s.P, key_bits=s.key_bits, stream_offset=s.S,
                           first_partial=wl.first_partial, valid_last=wl.valid_last, tile_len=tile_len,
-                          g_lane_stride=1 if wl.g.ndim == 3 else 0)
+                          g_lane_stride=1 if wl.g.ndim == 3 else 0, idx_bytes=wl.k_idx.dtype.itemsize)
 
 
 def device_inputs(wl: W.Workload, dev="cuda"):

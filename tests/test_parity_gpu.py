@@ -225,3 +225,32 @@ def test_perm_output(idx, steps):
     chunks = list(range(min(wl.N, 8))) + [wl.N - 1]
     ref = H.oracle_phase1(wl, chunks, fields=["perm"])
     H.assert_exact("perm", out["perm"].index_select(0, torch.as_tensor(chunks, device="cuda")).cpu().numpy(), ref["perm"])
+
+
+@pytest.mark.parametrize("idx,steps", [(1, 2), (4, 1)])
+def test_int64_ids(idx, steps):
+    """int64 slot ids give every Phase-1 output, and the read side's outputs, bit for bit as the
+    same ids in int32 do."""
+    import dataclasses
+
+    wl32 = W.make(idx, steps=steps)
+    wl64 = dataclasses.replace(wl32, k_idx=wl32.k_idx.astype(np.int64), q_idx=wl32.q_idx.astype(np.int64))
+    say("int64 ids", idx, steps)
+    outs = []
+    for wl in (wl32, wl64):
+        shape, out = H.run_phase1(wl, fields=["perm"])
+        ins = H.device_inputs(wl)
+        v_host, beta_host = W.make_read_inputs(wl32)
+        v = torch.from_numpy(v_host).cuda()
+        beta = torch.from_numpy(beta_host).cuda()
+        dv = torch.zeros((v.shape[0], wl.shape.hd), device="cuda")
+        pred, read = torch.zeros_like(dv), torch.zeros_like(dv)
+        bank = W.make_bank(wl32, "cuda")
+        plan = sdm.ReadPlan(bank, out, ins["k_idx"], ins["q_idx"], v, beta, dv, pred, read, shape,
+                            step_rows=wl.P * wl.shape.C)
+        plan.step(0)
+        torch.cuda.synchronize()
+        out.update(dv=dv, pred=pred, read=read)
+        outs.append(out)
+    for k in outs[0]:
+        assert torch.equal(outs[0][k].view(torch.uint8), outs[1][k].view(torch.uint8)), k
