@@ -11,10 +11,12 @@ from __future__ import annotations
 import numpy as np
 
 import oracle
+from oracle import read_side
 import sparse_delta_memory_amd as sdm
 from sparse_delta_memory_amd import workloads as W
 
 F32_REL, F32_ABS = 1e-5, 1e-6
+READ_RTOL_MAG = 1e-4   # read side: times the oracle's magnitude bound, plus 1e-6
 
 
 def shape_of(wl: W.Workload, tile_len: int = 128):
@@ -229,3 +231,53 @@ def run_dw_check(wl: W.Workload, out, shape, check_steps, dev="cuda", sample_unt
         cnt_bytes = shape.P * shape.C * shape.W * 4
         assert int(ws[:cnt_bytes].view(torch.int32).abs().sum()) == 0, "DW arrival counters not reset"
     return compared, bank
+
+
+def run_read_check(wl, steps_checked, chunks_per_step=None, dev="cuda"):
+    """Phase 1, then the read side of the checked steps from the initial bank; compare with the oracle
+    (tolerance READ_RTOL_MAG times the oracle's magnitude bound, plus 1e-6; masked tokens exactly 0).
+    Returns the worst error relative to the magnitude bound."""
+    import torch
+
+    sh = wl.shape
+    P, C, hd = sh.P, sh.C, sh.hd
+    shape, out = run_phase1(wl, dev=dev)
+    ins = device_inputs(wl, dev)
+    v_host, beta_host = W.make_read_inputs(wl)
+    v = torch.from_numpy(v_host).to(dev)
+    beta = torch.from_numpy(beta_host).to(dev)
+    rows = v.shape[0]
+    dv = torch.full((rows, hd), float("nan"), device=dev)
+    pred = torch.full_like(dv, float("nan"))
+    read = torch.full_like(dv, float("nan"))
+    bank = W.make_bank(wl, dev)
+    plan = sdm.ReadPlan(bank, out, ins["k_idx"], ins["q_idx"], v, beta, dv, pred, read, shape, step_rows=P * C)
+    for ti in steps_checked:
+        plan.step(ti)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for ti in steps_checked:
+        for p in range(P) if chunks_per_step is None else range(min(P, chunks_per_step)):
+            c = ti * P + p
+            o = oracle_phase1(wl, [c], fields=["k_eff", "q_w", "a", "qk"])
+            tv = wl.valid_last if c >= wl.first_partial else C
+            rows_of = lambda s: bank.index_select(0, torch.as_tensor(s, device=dev)).float().cpu().numpy().astype(np.float64)  # noqa: E731
+            r = read_side.read_step(wl.k_idx[c], wl.q_idx[c], o["k_eff"][0], o["q_w"][0], o["a"][0], o["qk"][0],
+                                    v_host[c * C:(c + 1) * C], beta_host[c], rows_of, tv)
+            sl = slice(ti * P * C + p * C, ti * P * C + (p + 1) * C)
+            for name, got in (("dv", dv), ("pred", pred), ("read", read)):
+                g = got[sl].cpu().numpy().astype(np.float64)
+                want = r[name]
+                tol = READ_RTOL_MAG * r["mag_" + name] + 1e-6
+                err = np.abs(g - want)
+                bad = ~(err <= tol)
+                if bad.any():
+                    i = np.argwhere(bad)[:4]
+                    raise AssertionError("%s step %d stream %d: %d of %d outside tolerance; e.g. %s" % (
+                        name, ti, p, bad.sum(), bad.size,
+                        ", ".join("%s gpu %r oracle %r mag %r" % (tuple(k), g[tuple(k)], want[tuple(k)],
+                                                                 r["mag_" + name][tuple(k)]) for k in i)))
+                worst = max(worst, float(np.max(err / (r["mag_" + name] + 1e-300))))
+                # masked tokens: exactly zero
+                assert np.all(g[tv:] == 0), name
+    return worst
