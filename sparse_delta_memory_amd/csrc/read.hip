@@ -12,12 +12,13 @@
 // Two kernels per step. read_gather_kernel: a team of 16 lanes per token, 8 columns per lane (16-byte
 // bf16 or two 16-byte float32 loads per row), entries taken 8 at a time with every row load in flight
 // before the first is used; p0 and q0 go to the pred and read outputs. read_solve_kernel: one block
-// per (chunk, 4 columns). It first inverts every 16 x 16 diagonal block of I + diag(beta) A (one
-// column of one block per lane, by substitution), then takes the tokens in blocks of 16: the
-// block's A and QK rows (loaded two blocks ahead) go to LDS; four lanes share each (token, column)
-// dot, every fourth term each, added by a fixed butterfly; the scaled right-hand side times the
-// block inverse's row gives dv, then the pred and read terms. Sums run in a fixed order: results
-// are reproducible.
+// per (chunk, 64 columns), one wave per 16 columns. It first inverts every 16 x 16 diagonal block of
+// I + diag(beta) A (one column of one block per lane, by substitution); then it takes the tokens in
+// blocks of 16: the block's A and QK rows (loaded one block ahead by all lanes) are staged in LDS,
+// and each wave forms with 16 x 16 x 4 float32 matrix (MFMA) steps the earlier blocks' terms
+// A[block, :b0] dv, the block's dv as its inverse times the scaled right-hand sides, the block's own
+// A terms for pred, and QK[block, :b0+16] dv for read; dv of every token stays in the wave's LDS.
+// Sums run in a fixed order: results are reproducible.
 #include <hip/hip_ext.h>
 
 #include "sdm_device.hpp"
@@ -140,53 +141,63 @@ __global__ void __launch_bounds__(256) read_gather_kernel(ReadArgs a) {
     oq[1] = make_float4(pq[4], pq[5], pq[6], pq[7]);
 }
 
-constexpr int kSC = 4;   // columns per substitution block
-constexpr int kKS = 4;   // lanes sharing one dot (each takes every kKS-th term)
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-// Part of sum_{j0 <= j < j1} row[j] * col[j * kSC]: the terms with j = j0 + ks (mod kKS).
-__device__ __forceinline__ float lds_dot_part(const float* row, const float* col, int j0, int j1, int ks) {
-    float s = 0.0f;
-    for (int j = j0 + ks; j < j1; j += kKS) s = fmaf(row[j], col[j * kSC], s);
-    return s;
+constexpr int kMW = 4;                // waves per substitution block, 16 columns each
+constexpr int kMCols = kMW * kSB;     // columns per substitution block
+
+// One 16 x 16 x 4 float32 matrix step: lane l gives A[l % 16][k] and B[k][l % 16] for the k its
+// lane group (l / 16) stands for; D row 4 (l / 16) + r, column l % 16 is register r of lane l.
+__device__ __forceinline__ floatx4 mfma4(float av, float bv, floatx4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
 }
 
-// The kKS parts of a dot (lanes 4 and 8 apart) added by a butterfly: every lane gets the same bits
-// ((p0 + p1) + (p2 + p3), float addition being commutative).
-__device__ __forceinline__ float dot_total(float s) {
-    s += __shfl_xor(s, kSC, kWave);
-    s += __shfl_xor(s, kSC * 2, kWave);
-    return s;
-}
+// Row stride of the staged panels: every column a token block reaches (C rounded up to 16) plus 4,
+// so that rows are 16-byte aligned and start 4 or 20 banks apart.
+__host__ __device__ inline int panel_ld(int C) { return (C + kSB - 1) / kSB * kSB + 4; }
 
-// Dynamic LDS of the substitution kernel (floats): dv of every token (C x kSC), the current block's
-// A and QK rows (16 x (C + 1) each, padded against bank conflicts), the inverses of the diagonal
-// blocks (C x 16) and the block's scaled right-hand sides (16 x kSC).
+// Dynamic LDS of the substitution kernel (floats): the inverses of the diagonal blocks (rows x 16),
+// per wave dv of every token for its 16 columns (rows x 16 each), and the current token block's A
+// and QK rows (16 x panel_ld each); rows = C rounded up to 16.
 size_t solve_lds_bytes(int C) {
-    return sizeof(float) * (static_cast<size_t>(C) * kSC + static_cast<size_t>(kSB) * (C + 1) * 2 +
-                            static_cast<size_t>(C) * kSB + kSB * kSC);
+    const size_t rows = static_cast<size_t>((C + kSB - 1) / kSB) * kSB;
+    return sizeof(float) * (rows * kSB * (1 + kMW) + 2 * static_cast<size_t>(kSB) * panel_ld(C));
+}
+
+// panel[0..16) x [0, K) times dv rows [0, K) of the wave's 16 columns, added to acc: lane (group g,
+// lane m) takes k = g * K/4 + s, s < K/4 (a contiguous run of its panel row), K a multiple of 16.
+__device__ __forceinline__ floatx4 panel_times_dv(const float* panel, int ld, int K, const float* wdv, int g, int m,
+                                                  floatx4 acc) {
+    const int kq = K / 4;
+    const float* prow = panel + m * ld + g * kq;
+    const float* dcol = wdv + g * kq * kSB + m;
+    for (int s0 = 0; s0 < kq; s0 += 4) {
+        const floatx4 av = *reinterpret_cast<const floatx4*>(prow + s0);   // 16-byte aligned: ld, kq, s0 multiples of 4
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mfma4(av[s], dcol[(s0 + s) * kSB], acc);
+    }
+    return acc;
 }
 
 __global__ void __launch_bounds__(256) read_solve_kernel(ReadArgs a) {
     extern __shared__ float lds[];
     const int C = a.C;
-    const int ld = C + 1;
-    float* sdv = lds;                   // [C][kSC]
-    float* sA = sdv + C * kSC;          // [16][ld]
-    float* sQ = sA + kSB * ld;          // [16][ld]
-    float* sT = sQ + kSB * ld;          // [C][16]: row t holds row (t mod 16) of its block's inverse
-    float* srhs = sT + C * kSB;         // [16][kSC]
+    const int nblk = (C + kSB - 1) / kSB;
+    const int rows = nblk * kSB;
+    const int ld = panel_ld(C);
+    float* sT = lds;                                    // [rows][16]: row t holds row (t mod 16) of its block's inverse
+    float* sdv = sT + rows * kSB;                       // [kMW][rows][16]
+    float* sA = sdv + kMW * rows * kSB;                 // [16][ld]: the current token block's A rows
+    float* sQ = sA + kSB * ld;                          // [16][ld]: its QK rows
     const int tid = static_cast<int>(threadIdx.x);
-    // Lanes: token in block tl (tid / 16), dot part ks, column d (tid = tl * 16 + ks * kSC + d).
-    const int tl = tid / kSB;
-    const int ks = (tid / kSC) % kKS;
-    const int d = tid % kSC;
-    // Staging and inverse lanes: row / block sr (tid / 16), lane sl (tid % 16).
-    const int sr = tid / kSB, sl = tid % kSB;
-    // Block b is (chunk b mod P, column group b / P): consecutive blocks go round the XCDs (8, each
-    // with its own L2), so a chunk's column groups share one XCD when P is a multiple of 8 (and
-    // 8 / gcd(P, 8) otherwise) and its A / QK rows are fetched from HBM once per XCD, not per block.
+    const int wv = tid / kWave, l = tid % kWave;
+    const int g = l / kSB, m = l % kSB;                 // lane group (k / D row quarter), lane in group
+    float* wdv = sdv + wv * rows * kSB;                 // this wave's dv [rows][16]
+    const int sr = tid / kSB, sl = tid % kSB;           // staging / inverse lanes: row (block) sr, lane sl
+    // Block b is (chunk b mod P, column group b / P): consecutive blocks go round the XCDs, so a
+    // chunk's column groups share an XCD's L2 when P is a multiple of 8.
     const int p = static_cast<int>(blockIdx.x) % a.P;
-    const int col = (static_cast<int>(blockIdx.x) / a.P) * kSC + d;
+    const int col = (static_cast<int>(blockIdx.x) / a.P) * kMCols + wv * kSB + m;   // this lane's column
     const bool col_ok = col < a.hd;
     const int64_t c = a.chunk0 + p;
     const int tv = c >= a.first_partial ? a.valid_last : C;
@@ -194,7 +205,6 @@ __global__ void __launch_bounds__(256) read_solve_kernel(ReadArgs a) {
     const float* QK = a.qk + c * C * C;
     const float* beta = a.beta + c * C;
     const int64_t rbase = a.row0 + static_cast<int64_t>(p) * C;
-    const int nblk = (C + kSB - 1) / kSB;
 
     // Inverse of every diagonal block T_b = I + diag(beta_b) A_bb (unit lower triangular): lane
     // (block sr, column sl) solves T_b x = e_sl by substitution; masked tokens have beta taken as 0.
@@ -212,90 +222,95 @@ __global__ void __launch_bounds__(256) read_solve_kernel(ReadArgs a) {
         float x[kSB];
 #pragma unroll
         for (int i = 0; i < kSB; ++i) {
-            float s = 0.0f;
+            float sacc = 0.0f;
 #pragma unroll
-            for (int k = 0; k < i; ++k) s = fmaf(al[i][k], x[k], s);
-            x[i] = (i == sl ? 1.0f : 0.0f) - bt[i] * s;
-            if (t0 + i < C) sT[(t0 + i) * kSB + sl] = x[i];
+            for (int k = 0; k < i; ++k) sacc = fmaf(al[i][k], x[k], sacc);
+            x[i] = (i == sl ? 1.0f : 0.0f) - bt[i] * sacc;
+            sT[(t0 + i) * kSB + sl] = t0 + i < C ? x[i] : 0.0f;
         }
     }
 
-    // Staged rows of token block b (row sr, columns sl + 16u) and this lane's token values, loaded
-    // two blocks ahead.
-    float stA[kSB], stQ[kSB], stA2[kSB], stQ2[kSB];
-    float nx_p0 = 0.0f, nx_v = 0.0f, nx_q0 = 0.0f, nx_b = 0.0f;
-    float nx2_p0 = 0.0f, nx2_v = 0.0f, nx2_q0 = 0.0f, nx2_b = 0.0f;
-    // Loads of block b into the second set (two blocks ahead of their use).
+    // Panel rows of token block b (row sr, columns sl + 16u up to the block's diagonal; zero past C)
+    // and this lane's token inputs (D rows b0 + 4g + r), loaded one block ahead.
+    float stA[kSB], stQ[kSB];
+    float nx_p0[4], nx_v[4], nx_q0[4], nx_b[4];
     auto prefetch = [&](int b) {
         const int b0 = b * kSB;
         const int tr = b0 + sr;
-        const int groups = b + 1;                   // column groups of 16 up to the block's diagonal
 #pragma unroll
         for (int u = 0; u < kSB; ++u) {
             const int j = sl + kSB * u;
-            const bool in = tr < C && u < groups && j < C;
-            stA2[u] = in ? A[static_cast<int64_t>(tr) * C + j] : 0.0f;
-            stQ2[u] = in ? QK[static_cast<int64_t>(tr) * C + j] : 0.0f;
+            const bool in = tr < C && u <= b && j < C;
+            stA[u] = in ? A[static_cast<int64_t>(tr) * C + j] : 0.0f;
+            stQ[u] = in ? QK[static_cast<int64_t>(tr) * C + j] : 0.0f;
         }
-        const int t = b0 + tl;
-        const bool valid = t < tv && col_ok;
-        nx2_p0 = valid ? a.pred[(rbase + t) * a.hd + col] : 0.0f;
-        nx2_v = valid ? a.v[(rbase + t) * a.hd + col] : 0.0f;
-        nx2_q0 = valid ? a.read[(rbase + t) * a.hd + col] : 0.0f;
-        nx2_b = valid ? beta[t] : 0.0f;
-    };
-    auto shift = [&]() {   // the second set becomes the next block's
 #pragma unroll
-        for (int u = 0; u < kSB; ++u) {
-            stA[u] = stA2[u];
-            stQ[u] = stQ2[u];
+        for (int r = 0; r < 4; ++r) {
+            const int t = b0 + 4 * g + r;
+            const bool ok = t < tv && col_ok;
+            const int64_t o = (rbase + (ok ? t : 0)) * a.hd + (col_ok ? col : 0);
+            nx_p0[r] = ok ? a.pred[o] : 0.0f;
+            nx_v[r] = ok ? a.v[o] : 0.0f;
+            nx_q0[r] = ok ? a.read[o] : 0.0f;
+            nx_b[r] = ok ? beta[t] : 0.0f;
         }
-        nx_p0 = nx2_p0;
-        nx_v = nx2_v;
-        nx_q0 = nx2_q0;
-        nx_b = nx2_b;
     };
     prefetch(0);
-    shift();
-    if (nblk > 1) prefetch(1);
     for (int b = 0; b < nblk; ++b) {
         const int b0 = b * kSB;
-        const int t = b0 + tl;
-        const bool valid = t < tv && col_ok;
-        const int groups = b + 1;
 #pragma unroll
         for (int u = 0; u < kSB; ++u) {
-            if (u < groups && sl + kSB * u < C) {
+            if (u <= b) {   // columns up to the block's diagonal (those past C hold zeros)
                 sA[sr * ld + sl + kSB * u] = stA[u];
                 sQ[sr * ld + sl + kSB * u] = stQ[u];
             }
         }
-        const float p0 = nx_p0, vv = nx_v, q0 = nx_q0, bt = nx_b;
-        if (b + 1 < nblk) shift();
-        if (b + 2 < nblk) prefetch(b + 2);
-        __syncthreads();   // the block's rows (and, first time, the inverses) are in LDS
-        // Scaled right-hand side: beta (v - p0 - terms of the earlier blocks).
-        const float far = dot_total(lds_dot_part(sA + tl * ld, sdv + d, 0, b0, ks));
-        if (ks == 0) srhs[tl * kSC + d] = valid ? bt * ((vv - p0) - far) : 0.0f;
-        __syncthreads();
-        // dv of the block: the inverse's row times the scaled right-hand sides.
-        float x = 0.0f;
-        if (t < C) {
-            for (int k = 0; k <= tl; ++k) x = fmaf(sT[t * kSB + k], srhs[k * kSC + d], x);
-            if (ks == 0) sdv[t * kSC + d] = valid ? x : 0.0f;
+        float p0[4], vv[4], q0[4], bt[4];
+        bool ok[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            p0[r] = nx_p0[r];
+            vv[r] = nx_v[r];
+            q0[r] = nx_q0[r];
+            bt[r] = nx_b[r];
+            ok[r] = b0 + 4 * g + r < tv && col_ok;
         }
-        __syncthreads();
-        // pred and read of the block's tokens.
-        const int tt = t < C ? t : 0;
-        const float near = dot_total(lds_dot_part(sA + tl * ld, sdv + d, b0, t < C ? t : b0, ks));
-        const float rd = dot_total(lds_dot_part(sQ + tl * ld, sdv + d, 0, t < C ? tt + 1 : 0, ks));
-        if (ks == 0 && t < C && col_ok) {
-            const int64_t o = (rbase + t) * a.hd + col;
-            a.dv[o] = valid ? x : 0.0f;
-            a.pred[o] = valid ? (p0 + far) + near : 0.0f;
-            a.read[o] = valid ? q0 + rd : 0.0f;
+        if (b + 1 < nblk) prefetch(b + 1);
+        __syncthreads();   // the block's panels (and, first time, the inverses) are in LDS
+        // Terms of the earlier blocks: A[block, :b0] dv.
+        floatx4 far = {0.0f, 0.0f, 0.0f, 0.0f};
+        far = panel_times_dv(sA, ld, b0, wdv, g, m, far);
+        // Scaled right-hand sides, then dv = (block inverse) x (right-hand sides): the B operand of
+        // step s is the lane's own register s (k = 4 g + s).
+        float rhs[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rhs[r] = ok[r] ? bt[r] * ((vv[r] - p0[r]) - far[r]) : 0.0f;
+        floatx4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) x = mfma4(sT[(b0 + m) * kSB + 4 * g + s], rhs[s], x);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            x[r] = ok[r] ? x[r] : 0.0f;
+            wdv[(b0 + 4 * g + r) * kSB + m] = x[r];
         }
-        __syncthreads();   // the staged rows are replaced next
+        // pred: the block's own A terms (B operand again the lane's registers).
+        floatx4 near = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) near = mfma4(sA[m * ld + b0 + 4 * g + s], x[s], near);
+        // read: QK[block, :b0+16] dv (this block's dv was just written by this wave).
+        floatx4 rd = {0.0f, 0.0f, 0.0f, 0.0f};
+        rd = panel_times_dv(sQ, ld, b0 + kSB, wdv, g, m, rd);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = b0 + 4 * g + r;
+            if (t < C && col_ok) {
+                const int64_t o = (rbase + t) * a.hd + col;
+                a.dv[o] = x[r];
+                a.pred[o] = ok[r] ? (p0[r] + far[r]) + near[r] : 0.0f;
+                a.read[o] = ok[r] ? q0[r] + rd[r] : 0.0f;
+            }
+        }
+        __syncthreads();   // the panels are replaced next
     }
 }
 
@@ -340,7 +355,7 @@ hipError_t read_launch(const ReadLaunch& L, hipStream_t st) {
     hipError_t e = hipExtLaunchKernel(g, dim3(static_cast<unsigned>(a.P * tok_blocks * col_blocks)), dim3(256), kargs, 0,
                                       st, ev[0], ev[1], 0);
     if (e != hipSuccess) return e;
-    const int solve_blocks = a.P * ((a.hd + kSC - 1) / kSC);
+    const int solve_blocks = a.P * ((a.hd + kMCols - 1) / kMCols);
     const size_t lds = solve_lds_bytes(a.C);
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&read_solve_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(lds));
