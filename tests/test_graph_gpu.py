@@ -133,3 +133,55 @@ def test_pair_stream_matches_one_stream():
     for k in ref_out:
         assert torch.equal(out[k].view(torch.uint8), ref_out[k].view(torch.uint8)), k
     assert torch.equal(bank.view(torch.uint8), ref_bank.view(torch.uint8))
+
+
+def test_graph_forward_loop_with_read_side():
+    """Phase 1 and, step after step, the read side then DW (the read side's dv feeding DW), captured
+    once and replayed: every replay equals the eager loop bit for bit."""
+    wl = W.make(1, steps=3)
+    sh = wl.shape
+    P, C, hd = sh.P, sh.C, sh.hd
+    shape = H.shape_of(wl)
+    ins = H.device_inputs(wl)
+    v_host, beta_host = W.make_read_inputs(wl)
+    v = torch.from_numpy(v_host).cuda()
+    beta = torch.from_numpy(beta_host).cuda()
+    bank0 = W.make_bank(wl, "cuda")
+
+    def make_state():
+        out = sdm.alloc_phase1_outputs(shape, device="cuda")
+        ws = torch.empty(sdm.phase1_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+        bank = bank0.clone()
+        dv = torch.zeros((v.shape[0], hd), device="cuda")
+        pred, read = torch.zeros_like(dv), torch.zeros_like(dv)
+        rplan = sdm.ReadPlan(bank, out, ins["k_idx"], ins["q_idx"], v, beta, dv, pred, read, shape, step_rows=P * C)
+        dplan = sdm.DwPlan(bank, dv, out["krec"], shape, dv_step_rows=P * C)
+
+        def loop():
+            sdm.phase1(shape, out=out, workspace=ws, **ins)
+            for ti in range(wl.steps):
+                rplan.step(ti)
+                dplan.step(ti)
+
+        return dict(out, bank=bank, dv=dv, pred=pred, read=read), loop
+
+    st_e, loop_e = make_state()
+    loop_e()
+    torch.cuda.synchronize()
+    st_g, loop_g = make_state()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        loop_g()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        st_g["bank"].copy_(bank0)
+        for k, t in st_g.items():
+            if k != "bank":
+                t.view(torch.uint8).fill_(0xA5)
+        st_e["bank"].copy_(bank0)
+        loop_e()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in st_e:
+            assert torch.equal(st_g[k].view(torch.uint8), st_e[k].view(torch.uint8)), (rep, k)
