@@ -51,6 +51,7 @@ class DwIO(ctypes.Structure):
         ("P", ctypes.c_int32), ("C", ctypes.c_int32), ("W", ctypes.c_int32), ("N", ctypes.c_int32),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("events", ctypes.c_void_p),
+        ("snap", ctypes.c_void_p), ("snap_step_rows", ctypes.c_int64), ("snap_rows", ctypes.c_int64),
     ]
 
 

@@ -222,6 +222,14 @@ sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st) {
         if (io->workspace_bytes < need)
             return fail(SDM_EWORKSPACE, "sdm_dw_step: workspace needs %zu bytes, got %zu", need, io->workspace_bytes);
     }
+    if (io->snap != nullptr) {
+        if (!aligned(io->snap, 16)) return fail(SDM_EALIGN, "sdm_dw_step: snap is not 16-byte aligned");
+        const int64_t pcw = static_cast<int64_t>(io->P) * io->C * io->W;
+        if (io->snap_step_rows < 0 || ti * io->snap_step_rows + pcw > io->snap_rows)
+            return fail(SDM_EINVAL, "sdm_dw_step: snap holds %lld rows, step %lld needs %lld",
+                        static_cast<long long>(io->snap_rows), static_cast<long long>(ti),
+                        static_cast<long long>(ti * io->snap_step_rows + pcw));
+    }
     sdm::DwLaunch L;
     L.io = io;
     L.ti = ti;

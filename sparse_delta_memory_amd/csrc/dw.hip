@@ -30,7 +30,9 @@ struct DwArgs {
     int64_t rows;      // bank rows
     float* part;       // split groups: one partial row per K-row position (NULL: groups are not split)
     int* cnt;          // per group FIRST: arrival counter, zero between calls
-    int2* meta;        // per group FIRST: {segments, LAST position}
+    int2* meta;        // per group FIRST: {segments, cpe bits of LAST}
+    void* snap;        // compact snapshot (NULL: none): row snap_row0 + p * CW + j_FIRST <- the group's pre-write row
+    int64_t snap_row0; // ti * snap_step_rows
     int P, C, CW, hd, ts_log2, teams_per_block;
 };
 
@@ -120,7 +122,7 @@ constexpr int kSegLimit = (4095 / kSeg) * kSeg;
 // or, when groups are split, a segment start; other positions return at once. The members after
 // the first are read a team-wide batch at a time and summed per run of one token (the token row is
 // loaded once per run); the sum's order is fixed by the records, so results are reproducible.
-template <int CPL, bool BANK_BF16, bool DV_BF16>
+template <int CPL, bool BANK_BF16, bool DV_BF16, bool SNAP>
 __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0, int col0, int tl) {
     // Member records and token rows loaded together (fewer when the rows take more registers).
     constexpr int kBatch = (CPL == 8 && DV_BF16) ? 4 : 2;
@@ -263,6 +265,11 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
             done = true;
         }
     }
+    if (SNAP && first) {   // the raw pre-write row, before this team's arrival or store
+        store_raw<CPL, BANK_BF16>(static_cast<unsigned char*>(a.snap) +
+                                      (a.snap_row0 + static_cast<int64_t>(p) * a.CW + j) * a.hd * kBankEs,
+                                  col0, base_raw);
+    }
     if (first && last_seen) {   // the whole group in one segment
         float base[CPL];
         unpack_cols<CPL, BANK_BF16>(base_raw, base);
@@ -336,7 +343,8 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
 // Teams take U consecutive K-row positions. Groups of one member (the common case) are done
 // together: their records, base rows and token rows are all in flight at once. Every other valid
 // position goes through the general walk, one after the other.
-template <int CPL, bool BANK_BF16, bool DV_BF16, int U>
+// SNAP: also write the compact snapshot (the raw pre-write row of every valid group at its FIRST).
+template <int CPL, bool BANK_BF16, bool DV_BF16, int U, bool SNAP>
 __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
     static_assert(CPL % (BANK_BF16 ? 8 : 4) == 0 && CPL % (DV_BF16 ? 8 : 4) == 0, "16-byte column groups");
     constexpr int kBankEs = BANK_BF16 ? 2 : 4;
@@ -352,7 +360,7 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
     if constexpr (U == 1) {   // one position: straight into the walk (its first member is the short path)
         const uint4 r0 = kr_step[J0];
         const int p = J0 / a.CW;
-        if (!(r0.x & kInvalid)) dw_walk<CPL, BANK_BF16, DV_BF16>(a, p, J0 - p * a.CW, r0, col0, tl);
+        if (!(r0.x & kInvalid)) dw_walk<CPL, BANK_BF16, DV_BF16, SNAP>(a, p, J0 - p * a.CW, r0, col0, tl);
         return;
     }
     // The records of positions J0 .. J0+U-1 (the steps' chunks are contiguous in krec), then the
@@ -395,6 +403,10 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
     for (int u = 0; u < U; ++u) {
         const float sc = __uint_as_float(r[u].z), cpe = __uint_as_float(r[u].w);
         float b[CPL], x[CPL], o[CPL];
+        if (SNAP && (ones & (1u << u))) {   // the raw pre-write row of a one-member group
+            store_raw<CPL, BANK_BF16>(static_cast<unsigned char*>(a.snap) + (a.snap_row0 + J0 + u) * a.hd * kBankEs,
+                                      col0, braw[u]);
+        }
         unpack_cols<CPL, BANK_BF16>(braw[u], b);
         unpack_cols<CPL, DV_BF16>(xraw[u], x);
 #pragma unroll
@@ -410,11 +422,12 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
                                       col0, oraw[u]);
         }
     }
+
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (!(ones & (1u << u)) && !(r[u].x & kInvalid)) {
             const int pu = (J0 + u) / a.CW;
-            dw_walk<CPL, BANK_BF16, DV_BF16>(a, pu, J0 + u - pu * a.CW, r[u], col0, tl);
+            dw_walk<CPL, BANK_BF16, DV_BF16, SNAP>(a, pu, J0 + u - pu * a.CW, r[u], col0, tl);
         }
     }
 }
@@ -425,11 +438,12 @@ constexpr int64_t kDwWavesForPairs = 32 * 256;
 
 template <int CPL, bool BB, bool DB, int U>
 hipError_t launch_dw_u(DwArgs a, hipStream_t st, const hipEvent_t* ev) {
+    const void* fn = a.snap != nullptr ? reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U, true>)
+                                       : reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U, false>);
     const int64_t teams = (static_cast<int64_t>(a.P) * a.CW + U - 1) / U;
     const int64_t blocks = (teams + a.teams_per_block - 1) / a.teams_per_block;
     void* kargs[] = {&a};
-    return hipExtLaunchKernel(reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U>),
-                              dim3(static_cast<unsigned>(blocks)), dim3(kDwThreads), kargs, 0, st, ev[0], ev[1], 0);
+    return hipExtLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kDwThreads), kargs, 0, st, ev[0], ev[1], 0);
 }
 
 template <int CPL, bool BB, bool DB>
@@ -475,6 +489,8 @@ hipError_t dw_launch(const DwLaunch& Lc, hipStream_t st) {
     a.part = nullptr;
     a.cnt = nullptr;
     a.meta = nullptr;
+    a.snap = io->snap;
+    a.snap_row0 = Lc.ti * io->snap_step_rows;
     if (io->workspace != nullptr) {
         const DwWorkspace w = dw_workspace_layout(io);
         a.part = reinterpret_cast<float*>(static_cast<char*>(io->workspace) + w.part_off);

@@ -110,6 +110,9 @@ def dw(**kw):
     (dict(dv_rows=255), 3, _lib.SDM_EINVAL), (dict(dv_step_rows=-1), 0, _lib.SDM_EINVAL),
     (dict(workspace=FAKE, workspace_bytes=16), 0, _lib.SDM_EWORKSPACE),
     (dict(workspace=FAKE + 4, workspace_bytes=1 << 40), 0, _lib.SDM_EALIGN),
+    (dict(snap=FAKE + 8, snap_rows=1 << 20), 0, _lib.SDM_EALIGN),
+    (dict(snap=FAKE, snap_step_rows=256, snap_rows=511), 1, _lib.SDM_EINVAL),
+    (dict(snap=FAKE, snap_step_rows=-1, snap_rows=1 << 20), 0, _lib.SDM_EINVAL),
 ])
 def test_dw_refusals(kw, ti, status):
     lib = _lib.load()

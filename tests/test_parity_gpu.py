@@ -254,3 +254,53 @@ def test_int64_ids(idx, steps):
         outs.append(out)
     for k in outs[0]:
         assert torch.equal(outs[0][k].view(torch.uint8), outs[1][k].view(torch.uint8)), k
+
+
+@pytest.mark.parametrize("idx,steps,case", [(0, 2, None), (1, 2, None), (2, 1, None),
+                                            (None, 1, dict(C=255, W=33, R=2, S=5000, P=1, vl=None, hd=960))])
+def test_dw_snapshot(idx, steps, case):
+    """The compact snapshot: row (ti*P*C*W + p*C*W + j) holds the raw pre-write bank row of the valid
+    group whose FIRST is at K-row position j (positions from the oracle's sorted K rows), every other
+    row keeps its sentinel, and writing it changes no bank bit."""
+    if case is None:
+        wl = W.make(idx, steps=steps)
+    else:
+        sh = W.Shape("snap_edge", P=case["P"], T=case["C"] * steps, C=case["C"], W=case["W"], R=case["R"],
+                     S=case["S"], hd=case["hd"], bank_dtype="bf16", dv_dtype="f32", slots="uniform",
+                     valid_last=case["vl"])
+        wl = W.make(sh, seed=780)
+    sh = wl.shape
+    P, C, hd, CW = sh.P, sh.C, sh.hd, sh.C * sh.W
+    say("dw snapshot", idx, case)
+    shape, out = H.run_phase1(wl)
+    dv = H.device_dv(wl)
+    bank0 = W.make_bank(wl, "cuda")
+    snap = torch.empty((wl.steps * P * CW, hd), dtype=bank0.dtype, device="cuda")
+    snap.view(torch.uint8).fill_(0xA5)
+    sentinel = snap[0].clone()
+    bank, bank_ref = bank0.clone(), bank0.clone()
+    plan_s = sdm.DwPlan(bank, dv, out["krec"], shape, dv_step_rows=P * C,
+                        workspace=sdm.alloc_dw_workspace(shape, hd, device="cuda"), snapshot=snap, snap_step_rows=P * CW)
+    plan_n = sdm.DwPlan(bank_ref, dv, out["krec"], shape, dv_step_rows=P * C,
+                        workspace=sdm.alloc_dw_workspace(shape, hd, device="cuda"))
+    ref = H.oracle_phase1(wl, list(range(wl.N)), fields=["spay_k", "krec_slot"])
+    for ti in range(wl.steps):
+        bank.copy_(bank0)
+        bank_ref.copy_(bank0)
+        plan_s.step(ti)
+        plan_n.step(ti)
+        torch.cuda.synchronize()
+        assert torch.equal(bank.view(torch.uint8), bank_ref.view(torch.uint8)), ti
+        for p in range(P):
+            c = ti * P + p
+            el = ref["spay_k"][c].astype(np.int64) & 0xFFFFFFFF
+            first = ((el >> 31) & 1).astype(bool) & ~((el >> 17) & 1).astype(bool)
+            js = np.flatnonzero(first)
+            rows = ti * P * CW + p * CW
+            got = snap[rows:rows + CW]
+            want = bank0.index_select(0, torch.as_tensor(ref["krec_slot"][c][js], dtype=torch.long, device="cuda"))
+            assert torch.equal(got[torch.as_tensor(js, device="cuda")].view(torch.uint8), want.view(torch.uint8)), (ti, p)
+            others = np.setdiff1d(np.arange(CW), js)
+            if others.size:
+                rest = got[torch.as_tensor(others, device="cuda")]
+                assert torch.equal(rest.view(torch.uint8), sentinel.expand_as(rest).view(torch.uint8)), (ti, p)
