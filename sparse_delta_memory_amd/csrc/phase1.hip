@@ -172,10 +172,6 @@ __device__ __forceinline__ Seg seg_shfl(Seg v, int d) {
     return o;
 }
 
-// Barrier for LDS hazards only: LDS operations complete, global stores may stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // Exclusive segmented scan of one element per thread over the block, in thread order
 // (REV: descending). Fixed tree: lane doubling, then the wave totals in scan order. `total`
@@ -600,7 +596,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
         (void)block_exclusive_add(repeat_count, wsum, rep_total);
         if (threadIdx.x == 0 && a.repeats != nullptr) a.repeats[c] = static_cast<int32_t>(rep_total);
     }
-    __syncthreads();
+    lds_barrier();   // LDS only: the repeats (and perm) stores stay in flight; nothing here reads them
 
     // Recomputes the four entries of tile T owned by this thread and calls f(k, entry).
     auto for_tile = [&](int T, const Seg& rp, const Seg& fp, uint32_t kp, const float (&vl)[kTileItems], auto&& f) {
@@ -948,7 +944,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             if (kinds & kSweepQ) sweep(std::integral_constant<uint32_t, kSweepQ>{}, a.sweeps.t0[sw], a.sweeps.t1[sw]);
         }
     }
-    __syncthreads();   // every hot-group append is done
+    lds_barrier();   // every hot-group append is done (the sweeps' global stores stay in flight)
     if (a.hot != nullptr) {
         // The hot list in position order: each entry's rank is the number of heads before it.
         const int nh = static_cast<int>(hot_n);   // every append happened before the last barrier

@@ -276,7 +276,7 @@ __global__ void __launch_bounds__(256) read_solve_kernel(ReadArgs a) {
             ok[r] = b0 + 4 * g + r < tv && col_ok;
         }
         if (b + 1 < nblk) prefetch(b + 1);
-        __syncthreads();   // the block's panels (and, first time, the inverses) are in LDS
+        lds_barrier();   // the block's panels (and, first time, the inverses) are in LDS (loads and stores stay in flight)
         // Terms of the earlier blocks: A[block, :b0] dv.
         floatx4 far = {0.0f, 0.0f, 0.0f, 0.0f};
         far = panel_times_dv(sA, ld, b0, wdv, g, m, far);
@@ -310,7 +310,7 @@ __global__ void __launch_bounds__(256) read_solve_kernel(ReadArgs a) {
                 a.read[o] = ok[r] ? q0[r] + rd[r] : 0.0f;
             }
         }
-        __syncthreads();   // the panels are replaced next
+        lds_barrier();   // the panels are replaced next
     }
 }
 

@@ -39,4 +39,9 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
 
+// Barrier for LDS hazards only: LDS operations complete, global stores may stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace sdm
