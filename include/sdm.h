@@ -131,6 +131,13 @@ typedef struct sdm_p1_io {
                                caller must make st wait for pair_stream before reusing the workspace
                                or reading a / qk. Default priority, same device. */
     hipEvent_t pair_ready;  /* caller-created event, required with pair_stream (recorded on st) */
+    int32_t* status;        /* debug, optional (NULL: off): when set, the sort/scan kernel checks every
+                               valid entry's slot id (local slot in [0, 2^key_bits), id >= 0) and sets bit
+                               0 of *status (an atomic OR) if one is out of range. The caller zeroes the
+                               word before the call and reads it once the stream has run the call (a
+                               device-side error cannot be a return code: nothing here synchronizes).
+                               Out-of-range ids only reach the sort as masked keys, so Phase 1 stays in
+                               bounds; the records they leave must not be given to sdm_dw_step. */
 } sdm_p1_io;
 
 /*

@@ -61,7 +61,7 @@ def alloc_phase1_outputs(shape: P1Shape, device="cuda", fields=None):
 
 
 def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=None, stream=None, events=None,
-           pair_stream=None, pair_ready=None):
+           pair_stream=None, pair_ready=None, status=None):
     """Enqueue Phase 1 of shape.N chunks on the current (or given) stream; returns the outputs.
 
     Inputs are contiguous device tensors: k_idx [N,C,W] / q_idx [N,C,R] int32 (int64 with
@@ -70,7 +70,8 @@ def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=No
     missing key skips that optional output). events: optional 4 torch.cuda.Events (timing_events)
     bound to the two kernels. pair_stream / pair_ready: optional torch stream and recorded event:
     the pair kernel then runs on pair_stream after the sort/scan kernel; the caller makes the main
-    stream wait for pair_stream before reusing the workspace or reading a / qk."""
+    stream wait for pair_stream before reusing the workspace or reading a / qk. status: optional
+    zeroed int32 device tensor (debug): bit 0 is set when a valid entry's slot id is out of range."""
     import torch
 
     lib = _lib.load()
@@ -91,6 +92,8 @@ def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=No
     io.workspace_bytes = workspace.numel() * workspace.element_size()
     arr = _event_array(events, 4, "phase1")
     io.events = None if arr is None else ctypes.cast(arr, ctypes.c_void_p).value
+    if status is not None:
+        io.status = status.data_ptr()
     if pair_stream is not None:
         ready = _event_array([pair_ready] if pair_ready is not None else [], 1, "phase1 pair_ready")
         io.pair_stream = pair_stream.cuda_stream

@@ -100,7 +100,7 @@ sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st
     }
     const void* a4[] = {io->k_idx, io->q_idx, io->k_val, io->q_val, io->g, io->log_k, io->rex, io->cpe,
                         io->k_eff, io->pos_k, io->log_q, io->q_w, io->pos_q, io->spay_k, io->spay_q,
-                        io->tiles_k, io->a, io->qk, io->repeats, io->perm};
+                        io->tiles_k, io->a, io->qk, io->repeats, io->perm, io->status};
     for (const void* p : a4) {
         if (!aligned(p, 4)) return fail(SDM_EALIGN, "sdm_phase1: a 4-byte field is misaligned");
     }

@@ -110,6 +110,7 @@ struct P1Args {
     int32_t* tiles_k;
     int32_t* repeats;
     int32_t* perm;       // [N, n] entry index at each sorted position (NULL: skipped)
+    int32_t* status;     // debug (NULL: off): bit 0 set when a valid entry's slot id is out of range
     uint4* rec;
     uint2* hot;          // per chunk: {count, 0}, then {head position, size} of each hot group (NULL: none)
     int C, W, R, P, key_bits, first_partial, valid_last, tile_len, digit_bits;
@@ -430,6 +431,17 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             const uint32_t kv =
                 t < tv ? static_cast<uint32_t>(ids[k] - id_base) & (key_lim - 1u) : key_lim;
             key[k] = i < n ? kv : pad_key;
+        }
+        if (a.status != nullptr) {   // debug: every valid entry's local slot in [0, 2^key_bits), id >= 0
+            bool bad = false;
+#pragma unroll
+            for (int k = 0; k < IPT; ++k) {
+                const int i = w * kWave * IPT + k * kWave + lane;
+                const int t = token_of_entry(i < n ? i : 0, a.wr_magic);
+                const int64_t local = ids[k] - id_base;
+                bad = bad || (i < n && t < tv && (ids[k] < 0 || local < 0 || local >= static_cast<int64_t>(key_lim)));
+            }
+            if (__any(bad) && lane == 0) atomicOr(a.status, 1);
         }
         if (res) {
 #pragma unroll
@@ -1547,6 +1559,7 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     a.tiles_k = io->tiles_k;
     a.repeats = io->repeats;
     a.perm = io->perm;
+    a.status = io->status;
     a.rec = pairs ? static_cast<uint4*>(Lc.rec) : nullptr;
     // Hot groups only when the pair kernel's x and y tables hold at least 4 groups beside the rest.
     // Groups per batch: as many as the blocks per compute unit that 4 groups allow still fit.

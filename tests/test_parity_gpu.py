@@ -304,3 +304,35 @@ def test_dw_snapshot(idx, steps, case):
             if others.size:
                 rest = got[torch.as_tensor(others, device="cuda")]
                 assert torch.equal(rest.view(torch.uint8), sentinel.expand_as(rest).view(torch.uint8)), (ti, p)
+
+
+def test_slot_id_check():
+    """The debug status word: 0 for valid inputs; bit 0 once a valid entry's slot id is out of range
+    (past 2^key_bits, negative, or in another stream's range); ids of masked tokens are not checked.
+    Only Phase 1 runs on the planted ids (their keys are masked into range, so it stays in bounds)."""
+    sh = W.Shape("idcheck", P=2, T=74, C=37, W=5, R=3, S=9, hd=64, bank_dtype="f32", dv_dtype="f32",
+                 slots="uniform", valid_last=11)
+    wl = W.make(sh, seed=781)
+    shape = H.shape_of(wl)
+    assert shape.key_bits >= 4
+
+    def run(k_idx, q_idx):
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+        sdm.phase1(shape, t(k_idx), t(q_idx), t(wl.k_val), t(wl.q_val), t(wl.g), status=status)
+        torch.cuda.synchronize()
+        return int(status.item())
+
+    assert run(wl.k_idx, wl.q_idx) == 0
+    big = wl.k_idx.copy()
+    big[1, 5, 2] = 1 * sh.S + (1 << shape.key_bits) + 3          # stream 1, local slot past 2^key_bits
+    assert run(big, wl.q_idx) == 1
+    neg = wl.q_idx.copy()
+    neg[0, 7, 1] = -3
+    assert run(wl.k_idx, neg) == 1
+    other = wl.q_idx.copy()
+    other[3, 2, 0] = 4                                            # chunk 3 is stream 1: local slot -5
+    assert run(wl.k_idx, other) == 1
+    masked = wl.k_idx.copy()
+    masked[wl.first_partial, wl.valid_last + 2, 0] = -7           # a masked token of the ragged chunk
+    assert run(masked, wl.q_idx) == 0
