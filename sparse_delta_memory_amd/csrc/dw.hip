@@ -280,17 +280,27 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
         return;
     }
     // Split group: publish this segment's partial; the last segment team to arrive combines the
-    // partials in segment order (the same sums whichever team arrives last).
+    // partials in segment order (the same sums whichever team arrives last). The segments of a group
+    // run in blocks on different XCDs, whose L2 caches are not coherent with each other: the partial
+    // and the group's metadata are written as device-scope atomic stores (coherent at the device
+    // level without a write-back of the whole L2), the wave waits until they have completed, and
+    // only then adds to the arrival counter; the combining team reads them with device-scope atomic
+    // loads after seeing the last arrival.
     const int64_t prow = static_cast<int64_t>(p) * a.CW;
     const int first_pos = j - dist;
     const int64_t gslot = prow + first_pos;
     float* part = a.part + (prow + j) * a.hd;
 #pragma unroll
-    for (int q = 0; q < CPL; ++q) part[col0 + q] = acc[q];
+    for (int q = 0; q < CPL; ++q) __hip_atomic_store(part + col0 + q, acc[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int seg = dist / kSeg;
     // The segment holding LAST publishes the segment count and the group's cpe (that of LAST).
-    if (last_seen && tl == 0) a.meta[gslot] = make_int2(seg + 1, static_cast<int>(__float_as_uint(cpe)));
-    __threadfence();
+    if (last_seen && tl == 0) {
+        const unsigned long long m = static_cast<uint32_t>(seg + 1) |
+                                     static_cast<unsigned long long>(__float_as_uint(cpe)) << 32;
+        __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.meta + gslot), m, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stores above have completed
     // The segment holding LAST adds 1 - (segments), every other adds 1: the counter returns to 0
     // exactly at the last arrival (and is left at 0 for the next call).
     const int delta = last_seen ? -seg : 1;
@@ -298,12 +308,13 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
     if (tl == 0) after = atomicAdd(a.cnt + gslot, delta) + delta;
     after = __shfl(after, static_cast<int>(lane_id()) & ~((1 << a.ts_log2) - 1), kWave);
     if (after != 0) return;
-    __threadfence();
     // The segment count, the base row (every segment's record names the group's slot) and the first
     // batch of partials in one round trip; partials past the count are read from in-row positions
     // and dropped.
     constexpr int kPartBatch = CPL == 8 ? 4 : 2;
-    const int2 meta = a.meta[gslot];
+    const unsigned long long mw = __hip_atomic_load(reinterpret_cast<const unsigned long long*>(a.meta + gslot),
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int2 meta = make_int2(static_cast<int>(mw & 0xFFFFFFFFull), static_cast<int>(mw >> 32));
     const RawCols<CPL, BANK_BF16> b2raw = load_raw<CPL, BANK_BF16>(bank_row, col0);
     float tot[CPL];
 #pragma unroll
@@ -315,7 +326,7 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
         for (int b = 0; b < kPartBatch; ++b) {
             const float* pp = a.part + (prow + min(first_pos + (sg0 + b) * kSeg, a.CW - 1)) * a.hd + col0;
 #pragma unroll
-            for (int q = 0; q < CPL; ++q) pv[b][q] = __builtin_nontemporal_load(pp + q);
+            for (int q = 0; q < CPL; ++q) pv[b][q] = __hip_atomic_load(pp + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
 #pragma unroll
         for (int b = 0; b < kPartBatch; ++b) {
