@@ -42,7 +42,7 @@ class _ChunkIn(ctypes.Structure):
         ("id_base", ctypes.c_int64),
         ("k_idx", ctypes.c_void_p), ("q_idx", ctypes.c_void_p), ("k_val", ctypes.c_void_p),
         ("q_val", ctypes.c_void_p), ("g", ctypes.c_void_p), ("tile_len", ctypes.c_int),
-        ("g_width", ctypes.c_int), ("g_lane_stride", ctypes.c_int),
+        ("g_width", ctypes.c_int), ("g_lane_stride", ctypes.c_int), ("val_bf16", ctypes.c_int),
     ]
 
 
@@ -69,6 +69,8 @@ def _load():
             lib.oracle_dw_apply.argtypes = [ctypes.POINTER(_ChunkIn), ctypes.c_int, ctypes.c_void_p,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
             lib.oracle_dw_apply.restype = ctypes.c_int64
+            lib.oracle_round_bf16.argtypes = [ctypes.c_double]
+            lib.oracle_round_bf16.restype = ctypes.c_double
             _lib = lib
     return _lib
 
@@ -77,7 +79,7 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
-def _chunk_in(k_idx, q_idx, k_val, q_val, g, c, P, stream_offset, first_partial, valid_last, tile_len):
+def _chunk_in(k_idx, q_idx, k_val, q_val, g, c, P, stream_offset, first_partial, valid_last, tile_len, val_bf16=False):
     C, W = k_idx.shape[1], k_idx.shape[2]
     R = q_idx.shape[2]
     arrs = (np.ascontiguousarray(k_idx[c], dtype=np.int32), np.ascontiguousarray(q_idx[c], dtype=np.int32),
@@ -89,17 +91,19 @@ def _chunk_in(k_idx, q_idx, k_val, q_val, g, c, P, stream_offset, first_partial,
     if per_lane and np.shape(g)[2] != W:
         raise ValueError("per-lane gates must be [N, C, W]")
     s = _ChunkIn(C, W, R, t_valid, (c % P) * stream_offset, *[_ptr(a) for a in arrs], tile_len,
-                 W if per_lane else 1, 1 if per_lane else 0)
+                 W if per_lane else 1, 1 if per_lane else 0, 1 if val_bf16 else 0)
     return s, arrs
 
 
 def phase1(k_idx, q_idx, k_val, q_val, g, *, P=1, stream_offset=0, first_partial=None, valid_last=None,
-           tile_len=128, chunks=None, threads=1, fields=None):
+           tile_len=128, chunks=None, threads=1, fields=None, val_bf16=False):
     """Phase 1 of the chunks `chunks` (default: all). Arrays are [N, C, W] / [N, C, R] / [N, C].
 
     Returns a dict of numpy arrays whose first axis runs over the requested chunks. `fields`
     selects the outputs (default: every Phase-1 output; the per-cell term magnitudes a_mag /
-    qk_mag and term counts a_cnt / qk_cnt only when named)."""
+    qk_mag and term counts a_cnt / qk_cnt only when named). val_bf16: the values are bfloat16
+    (k_val / q_val hold their exact values); cpe, k_eff, q_w and krec_cpe are then the exact
+    values rounded to bfloat16."""
     lib = _load()
     N, C, W = k_idx.shape
     R = q_idx.shape[2]
@@ -131,7 +135,8 @@ def phase1(k_idx, q_idx, k_val, q_val, g, *, P=1, stream_offset=0, first_partial
 
     def run(i):
         c = chunks[i]
-        cin, keep = _chunk_in(k_idx, q_idx, k_val, q_val, g, c, P, stream_offset, first_partial, valid_last, L)
+        cin, keep = _chunk_in(k_idx, q_idx, k_val, q_val, g, c, P, stream_offset, first_partial, valid_last, L,
+                              val_bf16)
         out = _ChunkOut(*[(_ptr(res[f][i]) if f in res else None) for f in _OUT_FIELDS])
         rc = lib.oracle_phase1_chunk(ctypes.byref(cin), ctypes.byref(out))
         del keep
@@ -166,11 +171,12 @@ def dw_slots(k_idx, q_idx, k_val, q_val, g, c, *, P=1, stream_offset=0, first_pa
 
 
 def dw_apply(k_idx, q_idx, k_val, q_val, g, c, dv_rows, base_rows, *, P=1, stream_offset=0, first_partial=None,
-             valid_last=None, with_magnitude=False):
+             valid_last=None, with_magnitude=False, val_bf16=False):
     """New rows of chunk c's valid K groups in float64: base * exp(G) + sum k exp(rex) dv.
 
     dv_rows: [C, hd] token rows of the chunk; base_rows: [groups, hd] pre-step rows in the order of
-    dw_slots. With with_magnitude, also returns the per-element magnitude sum of the terms."""
+    dw_slots. With with_magnitude, also returns the per-element magnitude sum of the terms. With
+    val_bf16 the base row is scaled by exp(G) rounded to bfloat16 (the records' cpe)."""
     lib = _load()
     N, C, _ = k_idx.shape
     first_partial = N if first_partial is None else first_partial
@@ -180,9 +186,17 @@ def dw_apply(k_idx, q_idx, k_val, q_val, g, c, dv_rows, base_rows, *, P=1, strea
     hd = dv.shape[1]
     out = np.zeros_like(base)
     mag = np.zeros_like(base) if with_magnitude else None
-    cin, keep = _chunk_in(k_idx, q_idx, k_val, q_val, g, c, P, stream_offset, first_partial, valid_last, 1)
+    cin, keep = _chunk_in(k_idx, q_idx, k_val, q_val, g, c, P, stream_offset, first_partial, valid_last, 1,
+                          val_bf16)
     cnt = lib.oracle_dw_apply(ctypes.byref(cin), hd, _ptr(dv), _ptr(base), _ptr(out), _ptr(mag))
     del keep
     if cnt != base.shape[0]:
         raise ValueError("dw_apply: %d groups, %d base rows" % (cnt, base.shape[0]))
     return (out, mag) if with_magnitude else out
+
+
+def round_bf16(x):
+    """x (float64 array) rounded to the nearest bfloat16 value, ties to even (oracle_round_bf16)."""
+    lib = _load()
+    a = np.asarray(x, dtype=np.float64)
+    return np.array([lib.oracle_round_bf16(float(v)) for v in a.ravel()], dtype=np.float64).reshape(a.shape)

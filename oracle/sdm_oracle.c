@@ -59,7 +59,30 @@ typedef struct {
     int tile_len;           /* L of tiles_k */
     int g_width;
     int g_lane_stride;
+    int val_bf16;           /* 1: the values are bfloat16 (k_val / q_val hold their exact float
+                               values); cpe, k_eff, q_w and the records' cpe are then bfloat16 too
+                               (each the exact value rounded once, to nearest even), and the DW step
+                               scales the base row by that rounded cpe (page
+                               "sparse_delta_memory/cuda/phase1_cuda.py": the value type of the
+                               Outputs struct, and the mover record comment "cpe as the ValT value
+                               widened") */
 } oracle_chunk_in;
+
+/* x rounded to the nearest bfloat16 value (8 significant bits, float's exponent range), ties to
+ * even: x = m 2^e with 0.5 <= |m| < 1 has the quantum 2^(e - 8) in the normal range and 2^-133
+ * below it; nearbyint rounds to the nearest integer, ties to even, in the default rounding mode.
+ * Finite inputs only (the values here are far from bfloat16's overflow). */
+double oracle_round_bf16(double x) {
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    (void)frexp(x, &e);
+    const int qe = (e > -125 ? e : -125) - 8;
+    return ldexp(nearbyint(ldexp(x, -qe)), qe);
+}
+
+static double oracle_val_round(const oracle_chunk_in* in, double x) {
+    return in->val_bf16 ? oracle_round_bf16(x) : x;
+}
 
 /* One chunk's outputs; any pointer may be NULL to skip that field. */
 typedef struct {
@@ -264,7 +287,7 @@ int oracle_phase1_chunk(const oracle_chunk_in* in, const oracle_chunk_out* out) 
         if (q) {
             const int o = t * R + lane;
             if (out->log_q) out->log_q[o] = L;
-            if (out->q_w) out->q_w[o] = valid ? v * exp(L) : 0.0;
+            if (out->q_w) out->q_w[o] = valid ? oracle_val_round(in, v * exp(L)) : 0.0;
             if (out->pos_q) out->pos_q[o] = (int32_t)packed;
             if (out->q_last) out->q_last[o] = (int8_t)(valid && after == 0);
             if (out->q_only) out->q_only[o] = (int8_t)(valid && after == 0 && before == 0);
@@ -273,11 +296,11 @@ int oracle_phase1_chunk(const oracle_chunk_in* in, const oracle_chunk_out* out) 
         } else {
             const int o = t * W + lane;
             const double rexv = valid ? w.rexv[p] : 0.0;
-            const double cpe = valid ? exp(L + rexv) : 1.0;
+            const double cpe = valid ? oracle_val_round(in, exp(L + rexv)) : 1.0;
             if (out->log_k) out->log_k[o] = L;
             if (out->rex) out->rex[o] = rexv;
             if (out->cpe) out->cpe[o] = cpe;
-            if (out->k_eff) out->k_eff[o] = valid ? v * exp(L) : 0.0;
+            if (out->k_eff) out->k_eff[o] = valid ? oracle_val_round(in, v * exp(L)) : 0.0;
             if (out->is_last) out->is_last[o] = (int8_t)(valid && after == 0);
             if (out->is_only) out->is_only[o] = (int8_t)(valid && after == 0 && before == 0);
             if (out->pos_k) out->pos_k[o] = (int32_t)packed;
@@ -371,8 +394,9 @@ int64_t oracle_dw_apply(const oracle_chunk_in* in, int hd, const double* dv, con
         if (w.ent[p].invalid || w.isq[p]) continue;
         if (w.kb[p] == 0) {
             ++gi;
-            /* exp of the group's total gate: L at this entry plus the sum after it. */
-            const double cpe = exp(w.L[p] + w.rexv[p]);
+            /* exp of the group's total gate: L at this entry plus the sum after it (rounded to
+             * bfloat16 with bfloat16 values, as the records carry it). */
+            const double cpe = oracle_val_round(in, exp(w.L[p] + w.rexv[p]));
             for (int d = 0; d < hd; ++d) {
                 out[gi * hd + d] = base[gi * hd + d] * cpe;
                 if (mag) mag[gi * hd + d] = fabs(base[gi * hd + d] * cpe);
