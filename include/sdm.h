@@ -71,6 +71,13 @@ typedef struct sdm_p1_shape {
                                lowest of those lanes (its other writes there are repeats). */
     int32_t idx_bytes;      /* width of the slot ids k_idx / q_idx: 0 or 4 = int32, 8 = int64 (every
                                absolute slot is below 2^31 either way) */
+    int32_t val_bytes;      /* type of the values k_val / q_val and of the value-typed outputs cpe,
+                               k_eff, q_w: 0 or 4 = float32, 2 = bfloat16 (page
+                               "sparse_delta_memory/cuda/phase1_cuda.py": the value type of the Outputs
+                               struct). With bfloat16, each of those outputs is its float32 result
+                               rounded to bfloat16 (nearest even), krec's cpe field holds that rounded
+                               cpe widened to float32 (so sdm_dw_step scales by it), and every other
+                               output is computed from the values widened exactly to float32. */
 } sdm_p1_shape;
 
 /*
@@ -84,20 +91,20 @@ typedef struct sdm_p1_io {
     /* inputs */
     const void* k_idx;      /* [N, C, W] absolute slot ids of the writes, int32 or int64 (idx_bytes) */
     const void* q_idx;      /* [N, C, R] absolute slot ids of the reads, same type */
-    const float* k_val;     /* [N, C, W] write values */
-    const float* q_val;     /* [N, C, R] read values */
+    const void* k_val;      /* [N, C, W] write values, float32 or bfloat16 (val_bytes) */
+    const void* q_val;      /* [N, C, R] read values, same type */
     const float* g;         /* gates (log decays): [N, C] per token, or [N, C, W] per (token, K lane)
                                when g_lane_stride = 1 */
     /* entry-order outputs */
     float* log_k;           /* [N, C, W] log-cumsum of the slot's gates up to and including the entry */
     float* rex;             /* [N, C, W] sum of the slot's later gates in the chunk */
-    float* cpe;             /* [N, C, W] exp(total gate of the slot in the chunk) */
-    float* k_eff;           /* [N, C, W] k_val * exp(log_k) */
+    void* cpe;              /* [N, C, W] exp(total gate of the slot in the chunk); value type */
+    void* k_eff;            /* [N, C, W] k_val * exp(log_k); value type */
     int8_t* is_last;        /* [N, C, W] last valid K entry of its slot */
     int8_t* is_only;        /* [N, C, W] only valid K entry of its slot */
     int32_t* pos_k;         /* [N, C, W] sorted position | min(after,127)<<17 | min(peers,127)<<24 */
     float* log_q;           /* [N, C, R] log-cumsum seen by the read (its own token's writes included) */
-    float* q_w;             /* [N, C, R] q_val * exp(log_q) */
+    void* q_w;              /* [N, C, R] q_val * exp(log_q); value type */
     int32_t* pos_q;         /* [N, C, R] as pos_k, peers counted among valid Q entries */
     int8_t* q_last;         /* [N, C, R] last valid Q entry of its slot */
     int8_t* q_only;         /* [N, C, R] only valid Q entry of its slot */
@@ -160,10 +167,13 @@ size_t sdm_phase1_workspace(const sdm_p1_shape* shape);
  * q_e k_f exp(log_q_e - log_k_f) over Q entries e of token i and earlier K entries f of token j.
  * Invalid entries: log 0, rex 0, cpe 1, k_eff / q_w 0, flags 0, pos = sorted position.
  *
- * Requirements: C*(W+R) <= 16384 (longer rows: SDM_EUNSUPPORTED); 4-byte aligned inputs;
- * krec 16-byte aligned; for P > 1 every local slot of a stream is < stream_offset.
+ * Requirements: C*(W+R) <= 16384 (longer rows: SDM_EUNSUPPORTED); 4-byte aligned inputs
+ * (bfloat16 value-typed fields: 2-byte); krec 16-byte aligned; for P > 1 every local slot of a
+ * stream is < stream_offset.
  * Floating outputs agree with the exact (real-arithmetic) values within
- * max(1e-5 |value|, 1e-6); integer outputs are exact.
+ * max(1e-5 |value|, 1e-6); integer outputs are exact. A bfloat16 output is one of the two bfloat16
+ * values next to the exact value (its float32 evaluation may fall on the other side of a rounding
+ * midpoint), and so is the cpe in krec.
  */
 sdm_status sdm_phase1(const sdm_p1_shape* shape, const sdm_p1_io* io, hipStream_t st);
 
@@ -225,8 +235,8 @@ typedef struct sdm_read_io {
     int32_t hd;             /* row width, a multiple of 8 */
     const void* k_idx;      /* [N, C, W] absolute slot ids of the writes (Phase-1 input), int32 or int64 */
     const void* q_idx;      /* [N, C, R] absolute slot ids of the reads, same type */
-    const float* k_eff;     /* [N, C, W] from sdm_phase1 */
-    const float* q_w;       /* [N, C, R] from sdm_phase1 */
+    const void* k_eff;      /* [N, C, W] from sdm_phase1, float32 or bfloat16 (val_bytes) */
+    const void* q_w;        /* [N, C, R] from sdm_phase1, same type */
     const float* a;         /* [N, C, C] from sdm_phase1 */
     const float* qk;        /* [N, C, C] from sdm_phase1 */
     const float* v;         /* value rows: row (ti * step_rows + p * C + t) of [*, hd], float32 */
@@ -241,6 +251,7 @@ typedef struct sdm_read_io {
     int32_t first_partial;  /* as in sdm_p1_shape: tokens >= valid_last of chunks >= first_partial are masked */
     int32_t valid_last;
     int32_t idx_bytes;      /* width of k_idx / q_idx: 0 or 4 = int32, 8 = int64 */
+    int32_t val_bytes;      /* type of k_eff / q_w as sdm_phase1 wrote them: 0 or 4 = float32, 2 = bfloat16 */
     hipEvent_t* events;     /* optional (NULL: none): 4 caller-created events bound to the start and end of
                                the gather kernel ([0], [1]) and of the substitution kernel ([2], [3]) */
 } sdm_read_io;

@@ -23,12 +23,13 @@ __all__ = ["P1Shape", "phase1", "phase1_workspace_bytes", "alloc_phase1_outputs"
 
 
 def make_shape(N, C, W, R, P=1, key_bits=16, stream_offset=0, first_partial=None, valid_last=None, tile_len=128,
-               g_lane_stride=0, idx_bytes=4):
+               g_lane_stride=0, idx_bytes=4, val_bytes=4):
     """Phase-1 shape. g_lane_stride 0: gates g [N, C] (per token); 1: g [N, C, W] (per token and K lane).
-    idx_bytes 4: int32 slot ids; 8: int64."""
+    idx_bytes 4: int32 slot ids; 8: int64. val_bytes 4: float32 values; 2: bfloat16 values (and
+    bfloat16 cpe, k_eff, q_w)."""
     return P1Shape(int(N), int(C), int(W), int(R), int(P), int(key_bits), int(stream_offset),
                    int(N if first_partial is None else first_partial), int(C if valid_last is None else valid_last),
-                   int(tile_len), int(g_lane_stride), int(idx_bytes))
+                   int(tile_len), int(g_lane_stride), int(idx_bytes), int(val_bytes))
 
 
 def phase1_workspace_bytes(shape: P1Shape) -> int:
@@ -45,10 +46,11 @@ def alloc_phase1_outputs(shape: P1Shape, device="cuda", fields=None):
 
     N, C, W, R, L = shape.N, shape.C, shape.W, shape.R, shape.tile_len
     ntk = (C * W + L - 1) // L
+    vt = torch.bfloat16 if shape.val_bytes == 2 else torch.float32   # value-typed fields
     spec = {
-        "log_k": ((N, C, W), torch.float32), "rex": ((N, C, W), torch.float32), "cpe": ((N, C, W), torch.float32),
-        "k_eff": ((N, C, W), torch.float32), "is_last": ((N, C, W), torch.int8), "is_only": ((N, C, W), torch.int8),
-        "pos_k": ((N, C, W), torch.int32), "log_q": ((N, C, R), torch.float32), "q_w": ((N, C, R), torch.float32),
+        "log_k": ((N, C, W), torch.float32), "rex": ((N, C, W), torch.float32), "cpe": ((N, C, W), vt),
+        "k_eff": ((N, C, W), vt), "is_last": ((N, C, W), torch.int8), "is_only": ((N, C, W), torch.int8),
+        "pos_k": ((N, C, W), torch.int32), "log_q": ((N, C, R), torch.float32), "q_w": ((N, C, R), vt),
         "pos_q": ((N, C, R), torch.int32), "q_last": ((N, C, R), torch.int8), "q_only": ((N, C, R), torch.int8),
         "spay_k": ((N, C * W), torch.int32), "spay_q": ((N, C * R), torch.int32),
         "krec": ((N, C * W, 4), torch.int32), "tiles_k": ((N, ntk + 1), torch.int32),
@@ -66,7 +68,7 @@ def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=No
 
     Inputs are contiguous device tensors: k_idx [N,C,W] / q_idx [N,C,R] int32 (int64 with
     shape.idx_bytes = 8), k_val / q_val
-    float32 of the same shapes, g [N,C] float32 ([N,C,W] when shape.g_lane_stride = 1). `out` is a dict from alloc_phase1_outputs (a
+    float32 (bfloat16 with shape.val_bytes = 2) of the same shapes, g [N,C] float32 ([N,C,W] when shape.g_lane_stride = 1). `out` is a dict from alloc_phase1_outputs (a
     missing key skips that optional output). events: optional 4 torch.cuda.Events (timing_events)
     bound to the two kernels. pair_stream / pair_ready: optional torch stream and recorded event:
     the pair kernel then runs on pair_stream after the sort/scan kernel; the caller makes the main
@@ -78,6 +80,13 @@ def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=No
     want = 8 if shape.idx_bytes == 8 else 4
     if k_idx.element_size() != want or q_idx.element_size() != want:
         raise TypeError("phase1: ids must be int%d (shape.idx_bytes = %d)" % (want * 8, shape.idx_bytes))
+    vt = torch.bfloat16 if shape.val_bytes == 2 else torch.float32
+    if k_val.dtype != vt or q_val.dtype != vt:
+        raise TypeError("phase1: values must be %s (shape.val_bytes = %d)" % (vt, shape.val_bytes))
+    if out is not None:
+        for name in ("cpe", "k_eff", "q_w"):
+            if out.get(name) is not None and out[name].dtype != vt:
+                raise TypeError("phase1: %s must be %s (shape.val_bytes = %d)" % (name, vt, shape.val_bytes))
     if out is None:
         out = alloc_phase1_outputs(shape, device=k_idx.device)
     need = phase1_workspace_bytes(shape)
@@ -205,7 +214,7 @@ class ReadPlan:
     """The read side of a step planned once, launched per step (before that step's DW).
 
     bank [rows, hd] float32 or bfloat16, the memory before the step (read only); p1: the dict of
-    Phase-1 outputs (k_eff, q_w, a, qk); k_idx / q_idx the Phase-1 id inputs; v [*, hd] float32 value
+    Phase-1 outputs (k_eff, q_w: float32 or bfloat16; a, qk); k_idx / q_idx the Phase-1 id inputs; v [*, hd] float32 value
     rows and beta [N, C] float32; dv, pred, read [*, hd] float32 outputs (dv feeds DwPlan with
     dv_step_rows = step_rows). Row of (step ti, stream p, token t): ti*step_rows + p*C + t. The plan
     keeps the tensors alive."""
@@ -233,6 +242,9 @@ class ReadPlan:
         io.P, io.C, io.W, io.R, io.N = shape.P, shape.C, shape.W, shape.R, shape.N
         io.first_partial, io.valid_last = shape.first_partial, shape.valid_last
         io.idx_bytes = k_idx.element_size()
+        if p1["k_eff"].dtype != p1["q_w"].dtype or p1["k_eff"].dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("ReadPlan: k_eff and q_w must both be float32 or both bfloat16")
+        io.val_bytes = p1["k_eff"].element_size()
         if q_idx.dtype != k_idx.dtype or k_idx.dtype not in (torch.int32, torch.int64):
             raise TypeError("ReadPlan: k_idx and q_idx must both be int32 or both int64")
         self.io = io

@@ -25,7 +25,7 @@ class P1Shape(ctypes.Structure):
         ("N", ctypes.c_int32), ("C", ctypes.c_int32), ("W", ctypes.c_int32), ("R", ctypes.c_int32),
         ("P", ctypes.c_int32), ("key_bits", ctypes.c_int32), ("stream_offset", ctypes.c_int64),
         ("first_partial", ctypes.c_int32), ("valid_last", ctypes.c_int32), ("tile_len", ctypes.c_int32),
-        ("g_lane_stride", ctypes.c_int32), ("idx_bytes", ctypes.c_int32),
+        ("g_lane_stride", ctypes.c_int32), ("idx_bytes", ctypes.c_int32), ("val_bytes", ctypes.c_int32),
     ]
 
 
@@ -64,7 +64,7 @@ class ReadIO(ctypes.Structure):
         ("step_rows", ctypes.c_int64), ("out_rows", ctypes.c_int64),
         ("P", ctypes.c_int32), ("C", ctypes.c_int32), ("W", ctypes.c_int32), ("R", ctypes.c_int32),
         ("N", ctypes.c_int32), ("first_partial", ctypes.c_int32), ("valid_last", ctypes.c_int32),
-        ("idx_bytes", ctypes.c_int32), ("events", ctypes.c_void_p),
+        ("idx_bytes", ctypes.c_int32), ("val_bytes", ctypes.c_int32), ("events", ctypes.c_void_p),
     ]
 
 

@@ -48,6 +48,8 @@ sdm_status check_p1_shape(const sdm_p1_shape* s) {
     if (s->tile_len < 1) return fail(SDM_EINVAL, "sdm_phase1: tile_len = %d < 1", s->tile_len);
     if (s->idx_bytes != 0 && s->idx_bytes != 4 && s->idx_bytes != 8)
         return fail(SDM_EINVAL, "sdm_phase1: idx_bytes = %d (0 or 4: int32 ids; 8: int64 ids)", s->idx_bytes);
+    if (s->val_bytes != 0 && s->val_bytes != 4 && s->val_bytes != 2)
+        return fail(SDM_EINVAL, "sdm_phase1: val_bytes = %d (0 or 4: float32 values; 2: bfloat16)", s->val_bytes);
     if (s->g_lane_stride != 0 && s->g_lane_stride != 1)
         return fail(SDM_EINVAL, "sdm_phase1: g_lane_stride = %d (0: gates [N, C]; 1: gates [N, C, W])", s->g_lane_stride);
     const int64_t n = static_cast<int64_t>(s->C) * (s->W + s->R);
@@ -98,11 +100,14 @@ sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st
     for (int i = 0; i < 8; ++i) {
         if (req[i] == nullptr) return fail(SDM_EINVAL, "sdm_phase1: %s is NULL", req_names[i]);
     }
-    const void* a4[] = {io->k_idx, io->q_idx, io->k_val, io->q_val, io->g, io->log_k, io->rex, io->cpe,
-                        io->k_eff, io->pos_k, io->log_q, io->q_w, io->pos_q, io->spay_k, io->spay_q,
-                        io->tiles_k, io->a, io->qk, io->repeats, io->perm, io->status};
+    const void* a4[] = {io->k_idx, io->q_idx, io->g, io->log_k, io->rex, io->pos_k, io->log_q, io->pos_q,
+                        io->spay_k, io->spay_q, io->tiles_k, io->a, io->qk, io->repeats, io->perm, io->status};
     for (const void* p : a4) {
         if (!aligned(p, 4)) return fail(SDM_EALIGN, "sdm_phase1: a 4-byte field is misaligned");
+    }
+    const void* av[] = {io->k_val, io->q_val, io->cpe, io->k_eff, io->q_w};   // value-typed fields
+    for (const void* p : av) {
+        if (!aligned(p, s->val_bytes == 2 ? 2 : 4)) return fail(SDM_EALIGN, "sdm_phase1: a value-typed field is misaligned");
     }
     if (!aligned(io->krec, 16)) return fail(SDM_EALIGN, "sdm_phase1: krec is not 16-byte aligned");
     if (s->idx_bytes == 8 && (!aligned(io->k_idx, 8) || !aligned(io->q_idx, 8)))
@@ -153,6 +158,8 @@ sdm_status sdm_read_step(const sdm_read_io* io, int64_t ti, hipStream_t st) {
         return fail(SDM_EINVAL, "sdm_read_step: bank_dtype %d", io->bank_dtype);
     if (io->idx_bytes != 0 && io->idx_bytes != 4 && io->idx_bytes != 8)
         return fail(SDM_EINVAL, "sdm_read_step: idx_bytes = %d (0 or 4: int32 ids; 8: int64 ids)", io->idx_bytes);
+    if (io->val_bytes != 0 && io->val_bytes != 4 && io->val_bytes != 2)
+        return fail(SDM_EINVAL, "sdm_read_step: val_bytes = %d (0 or 4: float32 k_eff / q_w; 2: bfloat16)", io->val_bytes);
     if (io->idx_bytes == 8 && (!aligned(io->k_idx, 8) || !aligned(io->q_idx, 8)))
         return fail(SDM_EALIGN, "sdm_read_step: int64 ids must be 8-byte aligned");
     if (io->hd < 8 || io->hd > 4096 || io->hd % 8 != 0)
@@ -171,10 +178,12 @@ sdm_status sdm_read_step(const sdm_read_io* io, int64_t ti, hipStream_t st) {
     for (const void* p : a16) {
         if (!aligned(p, 16)) return fail(SDM_EALIGN, "sdm_read_step: bank, v, dv, pred and read must be 16-byte aligned");
     }
-    const void* a4[] = {io->k_idx, io->q_idx, io->k_eff, io->q_w, io->a, io->qk, io->beta};
+    const void* a4[] = {io->k_idx, io->q_idx, io->a, io->qk, io->beta};
     for (const void* p : a4) {
         if (!aligned(p, 4)) return fail(SDM_EALIGN, "sdm_read_step: a 4-byte field is misaligned");
     }
+    if (!aligned(io->k_eff, io->val_bytes == 2 ? 2 : 4) || !aligned(io->q_w, io->val_bytes == 2 ? 2 : 4))
+        return fail(SDM_EALIGN, "sdm_read_step: k_eff / q_w misaligned for their type");
     sdm::ReadLaunch L;
     L.io = io;
     L.ti = ti;

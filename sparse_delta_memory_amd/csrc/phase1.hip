@@ -81,22 +81,46 @@ __device__ __forceinline__ void gstore(const void* base, uint32_t i, T v) {
     reinterpret_cast<GT*>(reinterpret_cast<uintptr_t>(base))[i] = v;
 }
 
+// Value-typed outputs (cpe, k_eff, q_w) with bfloat16 values: the float32 result rounded to
+// bfloat16, nearest even.
+__device__ __forceinline__ uint32_t bf16_rn(float x) { return f32_to_bf16_rne(x); }
+// Four values from element i (a multiple of 4; 16-byte / 8-byte aligned rows).
+__device__ __forceinline__ f32x4 load_val4(const void* p, int64_t i, int bf) {
+    if (bf) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p) + i);
+        return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+                     __uint_as_float(w.y & 0xFFFF0000u)};
+    }
+    return *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
+}
+// The 32-bit pattern a float32 record field holds for a value-typed quantity.
+__device__ __forceinline__ uint32_t val_bits32(float x, int bf) { return bf ? bf16_rn(x) << 16 : __float_as_uint(x); }
+__device__ __forceinline__ void store_val(const void* base, uint32_t i, float v, int bf) {
+    if (bf) gstore<uint16_t>(base, i, static_cast<uint16_t>(bf16_rn(v)));
+    else gstore<float>(base, i, v);
+}
+// Entries 4 i4 .. 4 i4 + 3.
+__device__ __forceinline__ void store_val4(const void* base, uint32_t i4, f32x4 v, int bf) {
+    if (bf) gstore<u32x2>(base, i4, u32x2{bf16_rn(v.x) | bf16_rn(v.y) << 16, bf16_rn(v.z) | bf16_rn(v.w) << 16});
+    else gstore<f32x4>(base, i4, v);
+}
+
 struct P1Args {
     const void* k_idx;   // int32 or int64 ids
     const void* q_idx;
-    const float* k_val;
-    const float* q_val;
+    const void* k_val;   // float32, or bfloat16 (the kernel's VBF)
+    const void* q_val;
     const float* g;
     // entry-order outputs (NULL: skipped)
     float* log_k;
     float* rex;
-    float* cpe;
-    float* k_eff;
+    void* cpe;           // float32, or bfloat16 with VBF (as k_eff and q_w)
+    void* k_eff;
     int8_t* is_last;
     int8_t* is_only;
     int32_t* pos_k;
     float* log_q;
-    float* q_w;
+    void* q_w;
     int32_t* pos_q;
     int8_t* q_last;
     int8_t* q_only;
@@ -338,7 +362,7 @@ __device__ __forceinline__ int64_t load_id(const void* ids, int64_t i) {
 
 // LG: gates per (token, K lane), [N, C, W], read from global memory where a scan needs one;
 // otherwise per token, [N, C], staged in LDS. ID64: slot ids are int64 (else int32).
-template <int IPT, bool LG, bool ID64>
+template <int IPT, bool LG, bool ID64, bool VBF>
 __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     constexpr int NP = kNT * IPT;
     constexpr int NTILE = (NP + kTile - 1) / kTile;
@@ -418,8 +442,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
 #pragma unroll
             for (int k = 0; k < IPT; ++k) {
                 const int i = static_cast<int>(threadIdx.x) + k * kNT;
-                vk[k] = a.k_val[cw + min(i, C * W - 1)];
-                vq[k] = a.q_val[cr + min(i, C * R - 1)];
+                vk[k] = load_val(a.k_val, cw + min(i, C * W - 1), VBF);
+                vq[k] = load_val(a.q_val, cr + min(i, C * R - 1), VBF);
             }
         }
 #pragma unroll
@@ -735,7 +759,11 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                         vl[k] = q ? vals_q[t * R + (j - W)] : vals_k[t * W + j];
                         if constexpr (sk) kid[k] = static_cast<int32_t>(p < n ? skey[p] : 0u);
                     } else {
-                        vl[k] = *(q ? a.q_val + cr + t * R + (j - W) : a.k_val + cw + t * W + j);
+                        // (a select of the entry's address, then one load)
+                        using VT = std::conditional_t<VBF, uint16_t, float>;
+                        const VT* vp = q ? static_cast<const VT*>(a.q_val) + cr + t * R + (j - W)
+                                         : static_cast<const VT*>(a.k_val) + cw + t * W + j;
+                        vl[k] = load_val(vp, 0, VBF);
                         if constexpr (sk) kid[k] = static_cast<int32_t>(load_id<ID64>(a.k_idx, cw + ((!q && t < tv) ? t * W + j : 0)));
                     }
                 }
@@ -785,7 +813,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                                                : static_cast<uint32_t>(static_cast<int64_t>(kid[k]) - id_base) & (key_lim - 1u);
                     const uint32_t slot = e.valid ? static_cast<uint32_t>(local + id_base) : 0u;
                     gstore<u32x4>(a.krec + cw, e.jkind,
-                                  u32x4{elem, slot, __float_as_uint(sc), __float_as_uint(group_exp(e))});
+                                  u32x4{elem, slot, __float_as_uint(sc), val_bits32(group_exp(e), VBF)});
                     int nk, L;
                     int64_t tb;
                     tile_bounds(nk, L, tb);
@@ -819,8 +847,9 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             const int64_t gb = cw + static_cast<int64_t>(t0) * W;   // the chunk's entry index of record 0
             void* const log_k = out_ptr(kOLogK, gb, 4);
             void* const rex_o = out_ptr(kORex, gb, 4);
-            void* const cpe_o = out_ptr(kOCpe, gb, 4);
-            void* const k_eff = out_ptr(kOKEff, gb, 4);
+            const int ves = (VBF ? 2 : 4);   // value-typed fields: cpe, k_eff
+            void* const cpe_o = out_ptr(kOCpe, gb, ves);
+            void* const k_eff = out_ptr(kOKEff, gb, ves);
             void* const is_last = out_ptr(kOIsLast, gb, 1);
             void* const is_only = out_ptr(kOIsOnly, gb, 1);
             void* const pos_k = out_ptr(kOPosK, gb, 4);
@@ -836,10 +865,10 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                 if (IPT <= 8 && a.resident) {   // (one sweep from token 0 here: record i is K entry i)
                     v4 = *reinterpret_cast<const f32x4*>(vals_k + g);
                 } else if (vec && cnt == 4) {
-                    v4 = *reinterpret_cast<const f32x4*>(a.k_val + gb + g);
+                    v4 = load_val4(a.k_val, gb + g, VBF);
                 } else {
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) v4[u] = a.k_val[gb + g + min(u, cnt - 1)];
+                    for (int u = 0; u < 4; ++u) v4[u] = load_val(a.k_val, gb + g + min(u, cnt - 1), VBF);
                 }
                 f32x4 cp, ke;
                 u32x4 ps;
@@ -862,8 +891,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                     const uint32_t g4 = g / 4;
                     if (log_k != nullptr) gstore<f32x4>(log_k, g4, L4);
                     if (rex_o != nullptr) gstore<f32x4>(rex_o, g4, X4);
-                    if (cpe_o != nullptr) gstore<f32x4>(cpe_o, g4, cp);
-                    if (k_eff != nullptr) gstore<f32x4>(k_eff, g4, ke);
+                    if (cpe_o != nullptr) store_val4(cpe_o, g4, cp, VBF);
+                    if (k_eff != nullptr) store_val4(k_eff, g4, ke, VBF);
                     if (pos_k != nullptr) gstore<u32x4>(pos_k, g4, ps);
                     if (is_last != nullptr) gstore<uint32_t>(is_last, g4, fl);
                     if (is_only != nullptr) gstore<uint32_t>(is_only, g4, fo);
@@ -874,8 +903,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                         if (u >= cnt) break;
                         if (log_k != nullptr) gstore<float>(log_k, g + u, L4[u]);
                         if (rex_o != nullptr) gstore<float>(rex_o, g + u, X4[u]);
-                        if (cpe_o != nullptr) gstore<float>(cpe_o, g + u, cp[u]);
-                        if (k_eff != nullptr) gstore<float>(k_eff, g + u, ke[u]);
+                        if (cpe_o != nullptr) store_val(cpe_o, g + u, cp[u], VBF);
+                        if (k_eff != nullptr) store_val(k_eff, g + u, ke[u], VBF);
                         if (pos_k != nullptr) gstore<uint32_t>(pos_k, g + u, ps[u]);
                         if (is_last != nullptr) gstore<uint8_t>(is_last, g + u, static_cast<uint8_t>((fl >> (8 * u)) & 1u));
                         if (is_only != nullptr) gstore<uint8_t>(is_only, g + u, static_cast<uint8_t>((fo >> (8 * u)) & 1u));
@@ -887,7 +916,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
         if constexpr (sq) {
             const int64_t gb = cr + static_cast<int64_t>(t0) * R;
             void* const log_q = out_ptr(kOLogQ, gb, 4);
-            void* const q_w = out_ptr(kOQW, gb, 4);
+            void* const q_w = out_ptr(kOQW, gb, (VBF ? 2 : 4));
             void* const pos_q = out_ptr(kOPosQ, gb, 4);
             void* const q_last = out_ptr(kOQLast, gb, 1);
             void* const q_only = out_ptr(kOQOnly, gb, 1);
@@ -902,10 +931,10 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                 if (IPT <= 8 && a.resident) {
                     v4 = *reinterpret_cast<const f32x4*>(vals_q + g);
                 } else if (vec && cnt == 4) {
-                    v4 = *reinterpret_cast<const f32x4*>(a.q_val + gb + g);
+                    v4 = load_val4(a.q_val, gb + g, VBF);
                 } else {
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) v4[u] = a.q_val[gb + g + min(u, cnt - 1)];
+                    for (int u = 0; u < 4; ++u) v4[u] = load_val(a.q_val, gb + g + min(u, cnt - 1), VBF);
                 }
                 f32x4 qw;
                 u32x4 ps;
@@ -926,7 +955,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                 if (vec && cnt == 4) {
                     const uint32_t g4 = g / 4;
                     if (log_q != nullptr) gstore<f32x4>(log_q, g4, L4);
-                    if (q_w != nullptr) gstore<f32x4>(q_w, g4, qw);
+                    if (q_w != nullptr) store_val4(q_w, g4, qw, VBF);
                     if (pos_q != nullptr) gstore<u32x4>(pos_q, g4, ps);
                     if (q_last != nullptr) gstore<uint32_t>(q_last, g4, fl);
                     if (q_only != nullptr) gstore<uint32_t>(q_only, g4, fo);
@@ -936,7 +965,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                     for (int u = 0; u < 4; ++u) {
                         if (u >= cnt) break;
                         if (log_q != nullptr) gstore<float>(log_q, g + u, L4[u]);
-                        if (q_w != nullptr) gstore<float>(q_w, g + u, qw[u]);
+                        if (q_w != nullptr) store_val(q_w, g + u, qw[u], VBF);
                         if (pos_q != nullptr) gstore<uint32_t>(pos_q, g + u, ps[u]);
                         if (q_last != nullptr) gstore<uint8_t>(q_last, g + u, static_cast<uint8_t>((fl >> (8 * u)) & 1u));
                         if (q_only != nullptr) gstore<uint8_t>(q_only, g + u, static_cast<uint8_t>((fo >> (8 * u)) & 1u));
@@ -1480,13 +1509,20 @@ MainPlan plan_main(const sdm_p1_shape* s, bool with_pairs_ws) {
     return m;
 }
 
+template <int IPT, bool VBF>
+const void* main_fn(bool lane_gates, bool id64) {
+    return lane_gates ? (id64 ? reinterpret_cast<const void*>(&p1_main_kernel<IPT, true, true, VBF>)
+                              : reinterpret_cast<const void*>(&p1_main_kernel<IPT, true, false, VBF>))
+                      : (id64 ? reinterpret_cast<const void*>(&p1_main_kernel<IPT, false, true, VBF>)
+                              : reinterpret_cast<const void*>(&p1_main_kernel<IPT, false, false, VBF>));
+}
+
 template <int IPT>
-hipError_t launch_main(P1Args args, bool lane_gates, bool id64, size_t lds, int N, hipStream_t st, hipEvent_t start,
-                       hipEvent_t stop) {
-    const void* fn = lane_gates ? (id64 ? reinterpret_cast<const void*>(&p1_main_kernel<IPT, true, true>)
-                                        : reinterpret_cast<const void*>(&p1_main_kernel<IPT, true, false>))
-                                : (id64 ? reinterpret_cast<const void*>(&p1_main_kernel<IPT, false, true>)
-                                        : reinterpret_cast<const void*>(&p1_main_kernel<IPT, false, false>));
+hipError_t launch_main(P1Args args, bool lane_gates, bool id64, bool vbf, size_t lds, int N, hipStream_t st,
+                       hipEvent_t start, hipEvent_t stop) {
+    // (The value type is a template parameter: a run-time switch in the staging loads costs the
+    // float32 path about a sixth of its time.)
+    const void* fn = vbf ? main_fn<IPT, true>(lane_gates, id64) : main_fn<IPT, false>(lane_gates, id64);
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     void* kargs[] = {&args};
@@ -1547,10 +1583,13 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     // Four-entry vector stores where every row of the kind's fields is 16-byte aligned (4-byte for
     // the flag bytes; the workspace rows follow from C * W or C * R being a multiple of 4).
     auto al = [](const void* p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) & (m - 1)) == 0; };
-    const bool vk = (s->C * s->W) % 4 == 0 && al(io->k_val, 16) && al(io->log_k, 16) && al(io->rex, 16) &&
-                    al(io->cpe, 16) && al(io->k_eff, 16) && al(io->pos_k, 16) && al(io->is_last, 4) &&
+    // (Value-typed fields, bfloat16 values: four entries are 8 bytes.)
+    const bool vbf = s->val_bytes == 2;
+    const uintptr_t va = vbf ? 8 : 16;
+    const bool vk = (s->C * s->W) % 4 == 0 && al(io->k_val, va) && al(io->log_k, 16) && al(io->rex, 16) &&
+                    al(io->cpe, va) && al(io->k_eff, va) && al(io->pos_k, 16) && al(io->is_last, 4) &&
                     al(io->is_only, 4);
-    const bool vq = (s->C * s->R) % 4 == 0 && al(io->q_val, 16) && al(io->log_q, 16) && al(io->q_w, 16) &&
+    const bool vq = (s->C * s->R) % 4 == 0 && al(io->q_val, va) && al(io->log_q, 16) && al(io->q_w, va) &&
                     al(io->pos_q, 16) && al(io->q_last, 4) && al(io->q_only, 4);
     a.vec = (vk ? 1u : 0u) | (vq ? 2u : 0u);
     a.spay_k = io->spay_k;
@@ -1601,11 +1640,11 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     }
     hipError_t e;
     switch (m.ipt) {
-        case 1: e = launch_main<1>(a, s->g_lane_stride != 0, s->idx_bytes == 8, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
-        case 2: e = launch_main<2>(a, s->g_lane_stride != 0, s->idx_bytes == 8, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
-        case 4: e = launch_main<4>(a, s->g_lane_stride != 0, s->idx_bytes == 8, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
-        case 8: e = launch_main<8>(a, s->g_lane_stride != 0, s->idx_bytes == 8, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
-        default: e = launch_main<16>(a, s->g_lane_stride != 0, s->idx_bytes == 8, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        case 1: e = launch_main<1>(a, s->g_lane_stride != 0, s->idx_bytes == 8, vbf, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        case 2: e = launch_main<2>(a, s->g_lane_stride != 0, s->idx_bytes == 8, vbf, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        case 4: e = launch_main<4>(a, s->g_lane_stride != 0, s->idx_bytes == 8, vbf, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        case 8: e = launch_main<8>(a, s->g_lane_stride != 0, s->idx_bytes == 8, vbf, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+        default: e = launch_main<16>(a, s->g_lane_stride != 0, s->idx_bytes == 8, vbf, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
     }
     if (e != hipSuccess || !pairs) return e;
     PairArgs pa;

@@ -38,8 +38,8 @@ struct ReadArgs {
     int64_t rows;
     const void* k_idx;   // int32 or int64 ids
     const void* q_idx;
-    const float* k_eff;
-    const float* q_w;
+    const void* k_eff;   // float32, or bfloat16 when vbf
+    const void* q_w;
     const float* a;
     const float* qk;
     const float* v;
@@ -50,6 +50,7 @@ struct ReadArgs {
     int64_t chunk0;      // ti * P
     int64_t row0;        // ti * step_rows: row of (p, t) is row0 + p * C + t
     int P, C, W, R, hd, first_partial, valid_last;
+    int vbf;             // 1: k_eff / q_w are bfloat16
 };
 
 template <bool BF16>
@@ -78,7 +79,7 @@ __device__ __forceinline__ void widen_row8(const uint4 (&raw)[BF16 ? 1 : 2], flo
 // sum_e w[e] M0[idx[e]] over n entries (idx: int32, or int64 when ID64), 8 columns of one token;
 // entries kGBatch at a time.
 template <bool BF16, bool ID64>
-__device__ __forceinline__ void gather_sum(const ReadArgs& a, const void* idx, const float* w, int n, int col0,
+__device__ __forceinline__ void gather_sum(const ReadArgs& a, const void* idx, const void* w, int n, int col0,
                                            float (&acc)[kGCols]) {
     for (int e0 = 0; e0 < n; e0 += kGBatch) {
         int64_t s[kGBatch];
@@ -91,7 +92,7 @@ __device__ __forceinline__ void gather_sum(const ReadArgs& a, const void* idx, c
             } else {
                 s[b] = static_cast<const int32_t*>(idx)[e];
             }
-            ws[b] = e0 + b < n ? w[e] : 0.0f;
+            ws[b] = e0 + b < n ? load_val(w, e, a.vbf) : 0.0f;
         }
         uint4 raw[kGBatch][BF16 ? 1 : 2];
 #pragma unroll
@@ -130,8 +131,11 @@ __global__ void __launch_bounds__(256) read_gather_kernel(ReadArgs a) {
     if (t < tv) {
         const int64_t ko = (c * a.C + t) * a.W, qo = (c * a.C + t) * a.R;
         const int es = ID64 ? 8 : 4;
-        gather_sum<BF16, ID64>(a, static_cast<const char*>(a.k_idx) + ko * es, a.k_eff + ko, a.W, col0, pk);
-        gather_sum<BF16, ID64>(a, static_cast<const char*>(a.q_idx) + qo * es, a.q_w + qo, a.R, col0, pq);
+        const int vs = a.vbf ? 2 : 4;   // bytes per weight
+        gather_sum<BF16, ID64>(a, static_cast<const char*>(a.k_idx) + ko * es,
+                               static_cast<const char*>(a.k_eff) + ko * vs, a.W, col0, pk);
+        gather_sum<BF16, ID64>(a, static_cast<const char*>(a.q_idx) + qo * es,
+                               static_cast<const char*>(a.q_w) + qo * vs, a.R, col0, pq);
     }
     float4* op = reinterpret_cast<float4*>(a.pred + row * a.hd + col0);
     float4* oq = reinterpret_cast<float4*>(a.read + row * a.hd + col0);
@@ -325,6 +329,7 @@ hipError_t read_launch(const ReadLaunch& L, hipStream_t st) {
     a.q_idx = io->q_idx;
     a.k_eff = io->k_eff;
     a.q_w = io->q_w;
+    a.vbf = io->val_bytes == 2 ? 1 : 0;
     a.a = io->a;
     a.qk = io->qk;
     a.v = io->v;

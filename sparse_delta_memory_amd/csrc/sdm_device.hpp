@@ -1,4 +1,4 @@
-// Device-side constants and helpers shared by the Phase-1 and DW kernels (gfx950, wave64).
+// Device-side constants and helpers shared by the Phase-1, DW and read-side kernels (gfx950, wave64).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,6 +35,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     const uint32_t u = __float_as_uint(f);
     const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
     return (u & 0x7FFFFFFFu) > 0x7F800000u ? ((u >> 16) | 0x40u) : rounded;
+}
+
+// Element i of a value array: float32, or bfloat16 (bf set) widened exactly to float32.
+__device__ __forceinline__ float load_val(const void* p, int64_t i, int bf) {
+    if (bf) return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
+    return static_cast<const float*>(p)[i];
 }
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }

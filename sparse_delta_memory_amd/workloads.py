@@ -96,6 +96,11 @@ class Workload:
         return self.k_idx.shape[0]
 
     @property
+    def val_bf16(self) -> bool:
+        """The values are bfloat16 (k_val / q_val hold bfloat16-representable float32 values)."""
+        return bool(self.meta.get("val_bf16", False))
+
+    @property
     def P(self) -> int:
         return self.shape.P
 
@@ -139,10 +144,11 @@ def _slots(rng: np.random.Generator, sh: Shape, size, ctx: dict) -> np.ndarray:
 
 
 def make(index: int | Shape, steps: int | None = None, *, nan_invalid: bool = True, seed: int | None = None,
-         shape_overrides: dict | None = None, lane_gates: bool = False) -> Workload:
+         shape_overrides: dict | None = None, lane_gates: bool = False, val_bf16: bool = False) -> Workload:
     """Draw the inputs of workload `index` (or of a Shape). `steps` truncates the step count (the
     last step stays ragged when the shape is). `shape_overrides` replaces Shape fields (tests).
-    `lane_gates`: one gate per (token, K lane), g [N, C, W], instead of one per token."""
+    `lane_gates`: one gate per (token, K lane), g [N, C, W], instead of one per token. `val_bf16`:
+    the values are drawn as before and rounded to bfloat16 (the device then takes them as bfloat16)."""
     sh = SHAPES[index] if isinstance(index, int) else index
     if shape_overrides:
         sh = Shape(**{**sh.__dict__, **shape_overrides})
@@ -166,6 +172,9 @@ def make(index: int | Shape, steps: int | None = None, *, nan_invalid: bool = Tr
     q_idx = (_slots(np.random.default_rng(ch["q_idx"]), sh, (N, C, R), ctx) + stream).astype(np.int32)
     k_val = (np.random.default_rng(ch["k_val"]).standard_normal((N, C, W)) / 2.0).astype(np.float32)
     q_val = (np.random.default_rng(ch["q_val"]).standard_normal((N, C, R)) / 2.0).astype(np.float32)
+    if val_bf16:
+        k_val, q_val = round_bf16(k_val), round_bf16(q_val)
+        ctx["val_bf16"] = True
     g_shape = (N, C, W) if lane_gates else (N, C)
     g = _logsigmoid(np.random.default_rng(ch["g"]).standard_normal(g_shape) + sh.gate_mu).astype(np.float32)
     dv = np.random.default_rng(ch["dv"]).standard_normal((nsteps, P, C, hd), dtype=np.float32)

@@ -23,14 +23,16 @@ def shape_of(wl: W.Workload, tile_len: int = 128):
     s = wl.shape
     return sdm.make_shape(wl.N, s.C, s.W, s.R, P=s.P, key_bits=s.key_bits, stream_offset=s.S,
                           first_partial=wl.first_partial, valid_last=wl.valid_last, tile_len=tile_len,
-                          g_lane_stride=1 if wl.g.ndim == 3 else 0, idx_bytes=wl.k_idx.dtype.itemsize)
+                          g_lane_stride=1 if wl.g.ndim == 3 else 0, idx_bytes=wl.k_idx.dtype.itemsize,
+                          val_bytes=2 if wl.val_bf16 else 4)
 
 
 def device_inputs(wl: W.Workload, dev="cuda"):
     import torch
 
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
-    return dict(k_idx=t(wl.k_idx), q_idx=t(wl.q_idx), k_val=t(wl.k_val), q_val=t(wl.q_val), g=t(wl.g))
+    vt = torch.bfloat16 if wl.val_bf16 else torch.float32   # (bfloat16-representable values: exact)
+    return dict(k_idx=t(wl.k_idx), q_idx=t(wl.q_idx), k_val=t(wl.k_val).to(vt), q_val=t(wl.q_val).to(vt), g=t(wl.g))
 
 
 def device_dv(wl: W.Workload, dev="cuda"):
@@ -60,7 +62,7 @@ def oracle_phase1(wl: W.Workload, chunks, tile_len=128, threads=8, with_magnitud
         fields = list(oracle._OUT_FIELDS)
     return oracle.phase1(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, P=wl.P, stream_offset=wl.stream_offset,
                          first_partial=wl.first_partial, valid_last=wl.valid_last, tile_len=tile_len, chunks=chunks,
-                         threads=threads, fields=fields)
+                         threads=threads, fields=fields, val_bf16=wl.val_bf16)
 
 
 def f32_violations(gpu, ref):
@@ -102,19 +104,41 @@ def assert_pair_sums(name, gpu, ref, mag, cnt):
             name, bad.sum(), i, g[i], r[i], cnt[i], mag[i]))
 
 
+def assert_bf16(name, gpu, ref):
+    """bfloat16 results against the oracle's (the exact value rounded to bfloat16): the GPU rounds
+    its float32 evaluation, which may sit on the other side of a rounding midpoint, so either
+    bfloat16 neighbour of the exact value is correct: |gpu - o| <= one bfloat16 ulp of o."""
+    g = np.asarray(gpu, np.float64)
+    r = np.asarray(ref, np.float64)
+    assert np.array_equal(g, oracle.round_bf16(g)), name + ": not bfloat16 values"
+    bad = ~(np.abs(g - r) <= ulp_bf16(r))
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError("%s: %d of %d elements more than one bfloat16 ulp away; %s: gpu %r oracle %r" % (
+            name, bad.sum(), bad.size, i, g[i], r[i]))
+
+
+VALUE_TYPED = ("cpe", "k_eff", "q_w")
+
+
 def compare_phase1(out, ref, chunks):
     """Element-by-element comparison of GPU outputs (device dict) and oracle outputs (chunk list).
 
     With the oracle's per-cell magnitudes in `ref` (stress shapes), A and QK use the evaluation
-    bound of assert_pair_sums; otherwise every float field uses max(1e-5|o|, 1e-6)."""
+    bound of assert_pair_sums; otherwise every float field uses max(1e-5|o|, 1e-6). bfloat16
+    outputs (bfloat16 values: cpe, k_eff, q_w and krec's cpe) use assert_bf16."""
     import torch
 
     idx = torch.as_tensor(list(chunks), device=out["krec"].device, dtype=torch.long)
-    host = {k: v.index_select(0, idx).cpu().numpy() for k, v in out.items()}
+    bf = out["k_eff"].dtype == torch.bfloat16 if "k_eff" in out else False
+    host = {k: (v.index_select(0, idx).float() if v.dtype == torch.bfloat16 else v.index_select(0, idx)).cpu().numpy()
+            for k, v in out.items()}
     u32 = lambda a: np.asarray(a).astype(np.int64) & 0xFFFFFFFF  # noqa: E731
     for f in ("log_k", "rex", "cpe", "k_eff", "log_q", "q_w", "a", "qk"):
         if f in host:
-            if f in ("a", "qk") and (f + "_mag") in ref:
+            if bf and f in VALUE_TYPED:
+                assert_bf16(f, host[f], ref[f])
+            elif f in ("a", "qk") and (f + "_mag") in ref:
                 assert_pair_sums(f, host[f], ref[f], ref[f + "_mag"], ref[f + "_cnt"])
             else:
                 assert_f32(f, host[f], ref[f])
@@ -128,7 +152,7 @@ def compare_phase1(out, ref, chunks):
     assert_exact("krec.element", u32(kr[..., 0]), u32(ref["spay_k"]))
     assert_exact("krec.slot", kr[..., 1], ref["krec_slot"])
     assert_f32("krec.scale", kr[..., 2].view(np.float32), ref["krec_sc"])
-    assert_f32("krec.cpe", kr[..., 3].view(np.float32), ref["krec_cpe"])
+    (assert_bf16 if bf else assert_f32)("krec.cpe", kr[..., 3].view(np.float32), ref["krec_cpe"])
 
 
 def ulp_bf16(x):
@@ -137,15 +161,19 @@ def ulp_bf16(x):
     return 2.0 ** (np.maximum(e, -126) - 7)
 
 
-def bank_violations(gpu_rows, new, mag, members, bank_dtype):
+def bank_violations(gpu_rows, new, mag, members, bank_dtype, cpe_slack=None):
     """Rows of the GPU bank against the oracle's new rows (float64).
 
     The float32 evaluation of an m-member chain with float32 scales is within
     (m + 4) 2^-23 times the sum of the term magnitudes (`mag`) of the exact value. float32 bank:
     max(1e-5|o|, 1e-6), or that evaluation bound where it is larger (long chains that cancel).
-    bf16 bank: one bf16 ulp of max(|gpu|, |o|) for the final rounding plus the evaluation bound."""
+    bf16 bank: one bf16 ulp of max(|gpu|, |o|) for the final rounding plus the evaluation bound.
+    cpe_slack (bfloat16 values): per element, |base| times one bfloat16 ulp of the group's cpe,
+    added to both bounds (the record's cpe may be the other bfloat16 neighbour of exp(G))."""
     g = np.asarray(gpu_rows, np.float64)
     arith = (np.asarray(members, np.float64)[:, None] + 4.0) * 2.0 ** -23 * mag
+    if cpe_slack is not None:
+        arith = arith + cpe_slack
     if bank_dtype == "f32":
         tol = np.maximum(np.maximum(F32_REL * np.abs(new), F32_ABS), arith)
         return ~(np.abs(g - new) <= tol)
@@ -200,13 +228,19 @@ def run_dw_check(wl: W.Workload, out, shape, check_steps, dev="cuda", sample_unt
         for c, slots in per:
             m = len(slots)
             rows = dv_host[c * C:(c + 1) * C]
+            okw = dict(P=P, stream_offset=sh.S, first_partial=wl.first_partial, valid_last=wl.valid_last,
+                       val_bf16=wl.val_bf16)
             new, mag = oracle.dw_apply(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, c, rows, base_host[off:off + m],
-                                       P=P, stream_offset=sh.S, first_partial=wl.first_partial,
-                                       valid_last=wl.valid_last, with_magnitude=True)
+                                       with_magnitude=True, **okw)
+            slack = None
+            if wl.val_bf16 and check:   # the groups' rounded cpe: base rows of ones, no token rows
+                cpe = oracle.dw_apply(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, c, np.zeros((C, 1)),
+                                      np.ones((m, 1)), **okw)
+                slack = np.abs(base_host[off:off + m]) * ulp_bf16(cpe)
             if check:
                 u, cnt = chunk_members(wl, c)
                 assert np.array_equal(u, slots)
-                bad = bank_violations(got_all[off:off + m], new, mag, cnt, sh.bank_dtype)
+                bad = bank_violations(got_all[off:off + m], new, mag, cnt, sh.bank_dtype, slack)
                 if bad.any():
                     i = np.argwhere(bad)[0]
                     raise AssertionError("DW step %d chunk %d: %d of %d elements outside tolerance; slot %d col %d: "

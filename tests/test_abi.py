@@ -31,7 +31,7 @@ def test_exports_every_declared_function():
 
 def shape(**kw):
     d = dict(N=4, C=64, W=4, R=4, P=1, key_bits=12, stream_offset=0, first_partial=4, valid_last=64, tile_len=128,
-             g_lane_stride=0, idx_bytes=4)
+             g_lane_stride=0, idx_bytes=4, val_bytes=4)
     d.update(kw)
     return _lib.P1Shape(*[d[f] for f, _ in _lib.P1Shape._fields_])
 
@@ -63,6 +63,7 @@ def call_p1(s, o):
     (dict(tile_len=0), _lib.SDM_EINVAL), (dict(stream_offset=-1), _lib.SDM_EINVAL),
     (dict(g_lane_stride=2), _lib.SDM_EINVAL), (dict(g_lane_stride=-1), _lib.SDM_EINVAL),
     (dict(idx_bytes=2), _lib.SDM_EINVAL), (dict(idx_bytes=16), _lib.SDM_EINVAL),
+    (dict(val_bytes=1), _lib.SDM_EINVAL), (dict(val_bytes=8), _lib.SDM_EINVAL),
     (dict(C=256, W=256, R=256), _lib.SDM_EUNSUPPORTED), (dict(C=256, W=40, R=40), _lib.SDM_EUNSUPPORTED),
 ])
 def test_phase1_shape_refusals(kw, status):
@@ -155,6 +156,8 @@ def read_io(**kw):
     (dict(out_rows=100), 0, _lib.SDM_EINVAL), (dict(beta=None), 0, _lib.SDM_EINVAL),
     (dict(dv=FAKE + 4), 0, _lib.SDM_EALIGN), (dict(a=FAKE + 2), 0, _lib.SDM_EALIGN),
     (dict(idx_bytes=3), 0, _lib.SDM_EINVAL), (dict(idx_bytes=8, k_idx=FAKE + 4), 0, _lib.SDM_EALIGN),
+    (dict(val_bytes=3), 0, _lib.SDM_EINVAL), (dict(k_eff=FAKE + 2), 0, _lib.SDM_EALIGN),
+    (dict(val_bytes=2, q_w=FAKE + 1), 0, _lib.SDM_EALIGN),
 ])
 def test_read_step_refusals(kw, ti, status):
     lib = _lib.load()
@@ -167,3 +170,10 @@ def test_read_step_refusals(kw, ti, status):
 def test_phase1_int64_ids_alignment():
     s = shape(idx_bytes=8)
     assert call_p1(s, io(k_idx=FAKE + 4)) == _lib.SDM_EALIGN
+
+
+def test_phase1_value_alignment():
+    """float32 values need 4-byte alignment, bfloat16 values 2-byte."""
+    assert call_p1(shape(), io(k_val=FAKE + 2)) == _lib.SDM_EALIGN
+    assert call_p1(shape(), io(cpe=FAKE + 2)) == _lib.SDM_EALIGN
+    assert call_p1(shape(val_bytes=2), io(q_w=FAKE + 1)) == _lib.SDM_EALIGN

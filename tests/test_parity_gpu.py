@@ -212,6 +212,43 @@ def test_lane_gates(case):
     H.run_dw_check(wl, out, shape, set(range(min(wl.steps, 2))), sample_untouched=0)
 
 
+@pytest.mark.parametrize("case", [
+    dict(C=37, W=5, R=3, S=9, P=2, steps=2, vl=11, lg=False),   # ragged rows: scalar value loads and stores
+    dict(idx=0, lg=False),                                      # tiny shape, every chunk
+    dict(idx=1, steps=2, lg=False),                             # resident layout, 4-entry vector paths
+    dict(idx=2, steps=1, lg=False),                             # Zipf rows of 16384 entries (several sweeps)
+    dict(idx=4, steps=1, lg=True),                              # large ragged shape, per-lane gates
+])
+def test_bf16_values(case):
+    """bfloat16 k_val / q_val: cpe, k_eff, q_w and krec's cpe are bfloat16 within one bfloat16 ulp of
+    the oracle's, every other output matches the oracle as usual, and DW (which scales by the
+    bfloat16 cpe) matches the oracle's bfloat16-value DW. Also: every output that is not value-typed
+    is bitwise the float32-value path's on the same (bfloat16-representable) values."""
+    if "idx" in case:
+        wl = W.make(case["idx"], steps=case.get("steps"), lane_gates=case["lg"], val_bf16=True)
+    else:
+        sh = W.Shape("bf16_values", P=case["P"], T=case["C"] * case["steps"], C=case["C"], W=case["W"], R=case["R"],
+                     S=case["S"], hd=64, bank_dtype="f32", dv_dtype="f32", slots="uniform", valid_last=case["vl"])
+        wl = W.make(sh, seed=781, lane_gates=case["lg"], val_bf16=True)
+    say("bf16 values", case)
+    shape, out = H.run_phase1(wl)
+    assert out["k_eff"].dtype == torch.bfloat16 and out["cpe"].dtype == torch.bfloat16
+    chunks = list(range(min(wl.N, 12))) + ([wl.N - 1] if wl.N > 12 else [])
+    ref = H.oracle_phase1(wl, chunks, with_magnitudes=True)
+    H.compare_phase1(out, ref, chunks)
+    # The float32-value path on the same values: identical except the value-typed fields.
+    f32_wl = W.Workload(**{**wl.__dict__, "meta": {k: v for k, v in wl.meta.items() if k != "val_bf16"}})
+    _, plain = H.run_phase1(f32_wl)
+    for k in plain:
+        if k in H.VALUE_TYPED:
+            continue
+        if k == "krec":
+            assert torch.equal(out[k][..., :3], plain[k][..., :3]), "krec element / slot / scale"
+            continue
+        assert torch.equal(out[k].view(torch.uint8), plain[k].view(torch.uint8)), k
+    H.run_dw_check(wl, out, shape, set(range(min(wl.steps, 2))), sample_untouched=0)
+
+
 @pytest.mark.parametrize("idx,steps", [(0, None), (2, 1), (4, 1)])
 def test_perm_output(idx, steps):
     """The optional sorted order (entry index at each sorted position) equals the oracle's, and

@@ -77,3 +77,33 @@ def test_read_side_feeds_dw_reproducibly():
         res.append((bank.clone(), dv.clone(), read.clone()))
     for a, b in zip(res[0], res[1]):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+@pytest.mark.parametrize("idx,steps", [(1, 1), (4, 1)])
+def test_read_side_bf16_weights(idx, steps):
+    """bfloat16 k_eff / q_w (bfloat16 values): the read side gives bitwise the results it gives for
+    the same weights widened to float32 (the float32-weight path is checked against the oracle
+    above), and those are finite for the valid tokens."""
+    wl = W.make(idx, steps=steps, val_bf16=True)
+    sh = wl.shape
+    P, C, hd = sh.P, sh.C, sh.hd
+    shape, out = H.run_phase1(wl)
+    assert out["k_eff"].dtype == torch.bfloat16
+    ins = H.device_inputs(wl)
+    v_host, beta_host = W.make_read_inputs(wl)
+    v = torch.from_numpy(v_host).cuda()
+    beta = torch.from_numpy(beta_host).cuda()
+    say("read side bf16 weights", idx, steps)
+    res = []
+    for p1 in (out, {**out, "k_eff": out["k_eff"].float(), "q_w": out["q_w"].float()}):
+        dv = torch.zeros((v.shape[0], hd), device="cuda")
+        pred, read = torch.zeros_like(dv), torch.zeros_like(dv)
+        bank = W.make_bank(wl, "cuda")
+        plan = sdm.ReadPlan(bank, p1, ins["k_idx"], ins["q_idx"], v, beta, dv, pred, read, shape, step_rows=P * C)
+        for ti in range(wl.steps):
+            plan.step(ti)
+        torch.cuda.synchronize()
+        res.append((dv, pred, read))
+    for a, b in zip(res[0], res[1]):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.isfinite(res[0][0]).all() and torch.isfinite(res[0][2]).all()   # (masked tokens: 0)
