@@ -179,11 +179,14 @@ sdm_status sdm_phase1(const sdm_p1_shape* shape, const sdm_p1_io* io, hipStream_
 
 /* One DW step: the chunks ti*P .. ti*P + P - 1 of the Phase-1 records. */
 typedef struct sdm_dw_io {
-    void* bank;             /* [rows, hd] SDM_F32 or SDM_BF16 bank, updated IN PLACE; 16-byte aligned */
+    void* bank;             /* [rows, hd] SDM_F32 or SDM_BF16 bank, updated IN PLACE; 16-byte aligned when
+                               hd is a vector width (below), else element-aligned */
     int32_t bank_dtype;     /* sdm_dtype */
     int64_t rows;           /* bank rows; every record slot is < rows */
-    int32_t hd;             /* row width, multiple of 4, 4..4096 */
-    const void* dv;         /* token rows: row (ti * dv_step_rows + p * C + t) of [*, hd]; 16-byte aligned */
+    int32_t hd;             /* row width, 1..1024. Multiples of 8 up to 512 and of 16 up to 1024 take 16-byte
+                               vector accesses; any other width takes element accesses (the mover pages'
+                               scalar tail variant: same values and roundings, element-aligned rows) */
+    const void* dv;         /* token rows: row (ti * dv_step_rows + p * C + t) of [*, hd]; aligned as bank */
     int32_t dv_dtype;       /* sdm_dtype (bf16 rows are widened exactly) */
     int64_t dv_step_rows;   /* rows between steps in dv (P*C when every step is stored, 0 for one step) */
     int64_t dv_rows;        /* rows in dv; ti * dv_step_rows + P * C <= dv_rows */
@@ -198,8 +201,8 @@ typedef struct sdm_dw_io {
     size_t workspace_bytes;
     hipEvent_t* events;     /* optional (NULL: none): 2 caller-created events bound to the start and end
                                of this call's kernel (hipExtLaunchKernel) */
-    void* snap;             /* optional (NULL: none) compact snapshot, [*, hd] in the bank dtype, 16-byte
-                               aligned: for every valid group of chunk ti*P + p whose FIRST is at K-row
+    void* snap;             /* optional (NULL: none) compact snapshot, [*, hd] in the bank dtype, aligned
+                               as bank: for every valid group of chunk ti*P + p whose FIRST is at K-row
                                position j, row (ti * snap_step_rows + p * C * W + j) receives the group's raw
                                pre-write bank row (page "sparse_delta_memory/cuda/mover_da2_cuda.py", the
                                da2_dw kernel's compact snapshot; page "sparse_delta_memory/cuda/mover_fx_cuda.py",

@@ -14,6 +14,7 @@
 
 namespace sdm {
 int dw_cols_per_lane(int hd);
+bool dw_tail(int hd);
 }
 
 namespace {
@@ -207,11 +208,9 @@ sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st) {
         return fail(SDM_EINVAL, "sdm_dw_step: bank_dtype %d", io->bank_dtype);
     if (io->dv_dtype != SDM_F32 && io->dv_dtype != SDM_BF16)
         return fail(SDM_EINVAL, "sdm_dw_step: dv_dtype %d", io->dv_dtype);
-    if (io->hd < 4 || io->hd % 4 != 0 || io->hd > 4096)
-        return fail(SDM_ESHAPE, "sdm_dw_step: hd = %d (multiple of 4 in 4..4096)", io->hd);
+    if (io->hd < 1 || io->hd > 4096) return fail(SDM_ESHAPE, "sdm_dw_step: hd = %d outside 1..4096", io->hd);
     if (sdm::dw_cols_per_lane(io->hd) == 0)
-        return fail(SDM_EUNSUPPORTED, "sdm_dw_step: hd = %d (this build: multiple of 8 up to 512, or of 16 up to 1024)",
-                    io->hd);
+        return fail(SDM_EUNSUPPORTED, "sdm_dw_step: hd = %d (this build: up to 1024)", io->hd);
     if (io->rows < 1 || io->dv_step_rows < 0 || io->dv_rows < 0)
         return fail(SDM_EINVAL, "sdm_dw_step: rows / dv_step_rows / dv_rows");
     if (ti * io->dv_step_rows + static_cast<int64_t>(io->P) * io->C > io->dv_rows)
@@ -219,12 +218,14 @@ sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st) {
                     static_cast<long long>(ti), static_cast<long long>(ti * io->dv_step_rows + static_cast<int64_t>(io->P) * io->C));
     if (io->bank == nullptr || io->dv == nullptr || io->krec == nullptr)
         return fail(SDM_EINVAL, "sdm_dw_step: bank, dv and krec are required");
-    if (!aligned(io->bank, 16) || !aligned(io->dv, 16) || !aligned(io->krec, 16))
-        return fail(SDM_EALIGN, "sdm_dw_step: bank, dv and krec must be 16-byte aligned");
+    // Head dims that 16-byte vectors divide (multiples of 8 up to 512, of 16 up to 1024) use vector
+    // accesses and need 16-byte aligned rows; any other takes element accesses (element alignment).
+    const bool tail = sdm::dw_tail(io->hd);
     const int bank_es = io->bank_dtype == SDM_BF16 ? 2 : 4;
     const int dv_es = io->dv_dtype == SDM_BF16 ? 2 : 4;
-    if ((io->hd * bank_es) % 16 != 0 || (io->hd * dv_es) % 16 != 0)
-        return fail(SDM_EALIGN, "sdm_dw_step: rows of hd = %d are not 16-byte multiples", io->hd);
+    if (!aligned(io->krec, 16)) return fail(SDM_EALIGN, "sdm_dw_step: krec must be 16-byte aligned");
+    if (!aligned(io->bank, tail ? bank_es : 16) || !aligned(io->dv, tail ? dv_es : 16))
+        return fail(SDM_EALIGN, "sdm_dw_step: bank and dv must be %s aligned", tail ? "element" : "16-byte");
     if (io->workspace != nullptr) {
         if (!aligned(io->workspace, 16)) return fail(SDM_EALIGN, "sdm_dw_step: workspace is not 16-byte aligned");
         const size_t need = sdm::dw_workspace_layout(io).total;
@@ -232,7 +233,7 @@ sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st) {
             return fail(SDM_EWORKSPACE, "sdm_dw_step: workspace needs %zu bytes, got %zu", need, io->workspace_bytes);
     }
     if (io->snap != nullptr) {
-        if (!aligned(io->snap, 16)) return fail(SDM_EALIGN, "sdm_dw_step: snap is not 16-byte aligned");
+        if (!aligned(io->snap, tail ? bank_es : 16)) return fail(SDM_EALIGN, "sdm_dw_step: snap is misaligned");
         const int64_t pcw = static_cast<int64_t>(io->P) * io->C * io->W;
         if (io->snap_step_rows < 0 || ti * io->snap_step_rows + pcw > io->snap_rows)
             return fail(SDM_EINVAL, "sdm_dw_step: snap holds %lld rows, step %lld needs %lld",

@@ -44,12 +44,34 @@ struct RawCols {
     uint4 v[kVec];
 };
 
-template <int CPL, bool BF16>
-__device__ __forceinline__ RawCols<CPL, BF16> load_raw(const void* row, int col0) {
+// TAIL (a head dim the 16-byte vectors do not divide, as in the mover pages' scalar variant): rows
+// are only element-aligned, so a lane moves its first nv (1..CPL) columns element by element, with
+// zeros in the rest of the raw vector; the values and roundings are those of the vector path.
+template <int CPL, bool BF16, bool TAIL>
+__device__ __forceinline__ RawCols<CPL, BF16> load_raw(const void* row, int col0, int nv) {
     RawCols<CPL, BF16> r;
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(row) + col0 * (BF16 ? 2 : 4));
+    if constexpr (TAIL) {
+        uint32_t w[RawCols<CPL, BF16>::kVec * 4];
+        if constexpr (BF16) {
+            const uint16_t* p = reinterpret_cast<const uint16_t*>(static_cast<const unsigned char*>(row) + col0 * 2);
 #pragma unroll
-    for (int v = 0; v < RawCols<CPL, BF16>::kVec; ++v) r.v[v] = p[v];
+            for (int e = 0; e < CPL; e += 2) {
+                const uint32_t lo = e < nv ? p[e] : 0u;
+                const uint32_t hi = e + 1 < nv ? p[e + 1] : 0u;
+                w[e / 2] = lo | hi << 16;
+            }
+        } else {
+            const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const unsigned char*>(row) + col0 * 4);
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) w[e] = e < nv ? p[e] : 0u;
+        }
+#pragma unroll
+        for (int v = 0; v < RawCols<CPL, BF16>::kVec; ++v) r.v[v] = make_uint4(w[4 * v], w[4 * v + 1], w[4 * v + 2], w[4 * v + 3]);
+    } else {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(row) + col0 * (BF16 ? 2 : 4));
+#pragma unroll
+        for (int v = 0; v < RawCols<CPL, BF16>::kVec; ++v) r.v[v] = p[v];
+    }
     return r;
 }
 
@@ -70,9 +92,9 @@ __device__ __forceinline__ void unpack_cols(const RawCols<CPL, BF16>& r, float (
     }
 }
 
-template <int CPL, bool BF16>
-__device__ __forceinline__ void load_cols(const void* row, int col0, float (&x)[CPL]) {
-    unpack_cols<CPL, BF16>(load_raw<CPL, BF16>(row, col0), x);
+template <int CPL, bool BF16, bool TAIL>
+__device__ __forceinline__ void load_cols(const void* row, int col0, int nv, float (&x)[CPL]) {
+    unpack_cols<CPL, BF16>(load_raw<CPL, BF16, TAIL>(row, col0, nv), x);
 }
 
 template <int CPL, bool BF16>
@@ -91,11 +113,35 @@ __device__ __forceinline__ RawCols<CPL, BF16> pack_cols(const float (&x)[CPL]) {
     return r;
 }
 
-template <int CPL, bool BF16>
-__device__ __forceinline__ void store_raw(void* row, int col0, const RawCols<CPL, BF16>& r) {
-    uint4* p = reinterpret_cast<uint4*>(static_cast<unsigned char*>(row) + col0 * (BF16 ? 2 : 4));
+template <int CPL, bool BF16, bool TAIL>
+__device__ __forceinline__ void store_raw(void* row, int col0, int nv, const RawCols<CPL, BF16>& r) {
+    if constexpr (TAIL) {
+        uint32_t w[RawCols<CPL, BF16>::kVec * 4];
 #pragma unroll
-    for (int v = 0; v < RawCols<CPL, BF16>::kVec; ++v) p[v] = r.v[v];
+        for (int v = 0; v < RawCols<CPL, BF16>::kVec; ++v) {
+            w[4 * v] = r.v[v].x;
+            w[4 * v + 1] = r.v[v].y;
+            w[4 * v + 2] = r.v[v].z;
+            w[4 * v + 3] = r.v[v].w;
+        }
+        if constexpr (BF16) {
+            uint16_t* p = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(row) + col0 * 2);
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) {
+                if (e < nv) p[e] = static_cast<uint16_t>(w[e / 2] >> (16 * (e % 2)));
+            }
+        } else {
+            uint32_t* p = reinterpret_cast<uint32_t*>(static_cast<unsigned char*>(row) + col0 * 4);
+#pragma unroll
+            for (int e = 0; e < CPL; ++e) {
+                if (e < nv) p[e] = w[e];
+            }
+        }
+    } else {
+        uint4* p = reinterpret_cast<uint4*>(static_cast<unsigned char*>(row) + col0 * (BF16 ? 2 : 4));
+#pragma unroll
+        for (int v = 0; v < RawCols<CPL, BF16>::kVec; ++v) p[v] = r.v[v];
+    }
 }
 
 // Pins computed values in registers at this point of the program (no code is emitted): later
@@ -108,9 +154,9 @@ __device__ __forceinline__ void pin_raw(const RawCols<CPL, BF16>& r) {
     }
 }
 
-template <int CPL, bool BF16>
-__device__ __forceinline__ void store_cols(void* row, int col0, const float (&x)[CPL]) {
-    store_raw<CPL, BF16>(row, col0, pack_cols<CPL, BF16>(x));
+template <int CPL, bool BF16, bool TAIL>
+__device__ __forceinline__ void store_cols(void* row, int col0, int nv, const float (&x)[CPL]) {
+    store_raw<CPL, BF16, TAIL>(row, col0, nv, pack_cols<CPL, BF16>(x));
 }
 
 // Members of a group per segment when the group is split (a workspace is given), and the last
@@ -122,8 +168,8 @@ constexpr int kSegLimit = (4095 / kSeg) * kSeg;
 // or, when groups are split, a segment start; other positions return at once. The members after
 // the first are read a team-wide batch at a time and summed per run of one token (the token row is
 // loaded once per run); the sum's order is fixed by the records, so results are reproducible.
-template <int CPL, bool BANK_BF16, bool DV_BF16, bool SNAP>
-__device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0, int col0, int tl) {
+template <int CPL, bool BANK_BF16, bool DV_BF16, bool SNAP, bool TAIL>
+__device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0, int col0, int nv, int tl) {
     // Member records and token rows loaded together (fewer when the rows take more registers).
     constexpr int kBatch = (CPL == 8 && DV_BF16) ? 4 : 2;
     const uint4* kr = a.krec + (a.chunk0 + p) * a.CW;
@@ -138,7 +184,7 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
     constexpr int kDvEs = DV_BF16 ? 2 : 4;
     unsigned char* bank_row = static_cast<unsigned char*>(a.bank) + static_cast<int64_t>(r0.y) * a.hd * kBankEs;
     // The base row (a group's FIRST only) stays in flight during the walk.
-    RawCols<CPL, BANK_BF16> base_raw = load_raw<CPL, BANK_BF16>(first ? bank_row : static_cast<unsigned char*>(a.bank), col0);
+    RawCols<CPL, BANK_BF16> base_raw = load_raw<CPL, BANK_BF16, TAIL>(first ? bank_row : static_cast<unsigned char*>(a.bank), col0, nv);
     const unsigned char* dv0 = static_cast<const unsigned char*>(a.dv) +
                                (a.dv_row0 + static_cast<int64_t>(p) * a.C) * a.hd * kDvEs;
     float acc[CPL];
@@ -152,7 +198,7 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
     {
         float x0[CPL];
         const int tok = static_cast<int>((r0.x >> kTokShift) & 0xFFu);
-        load_cols<CPL, DV_BF16>(dv0 + static_cast<int64_t>(tok) * a.hd * kDvEs, col0, x0);
+        load_cols<CPL, DV_BF16, TAIL>(dv0 + static_cast<int64_t>(tok) * a.hd * kDvEs, col0, nv, x0);
         const float sc = __uint_as_float(r0.z);
 #pragma unroll
         for (int q = 0; q < CPL; ++q) acc[q] = fmaf(sc, x0[q], acc[q]);
@@ -174,7 +220,7 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
             const int tok = static_cast<int>((rb[b].x >> kTokShift) & 0xFFu);
-            xr[b] = load_raw<CPL, DV_BF16>(dv0 + static_cast<int64_t>(tok) * a.hd * kDvEs, col0);
+            xr[b] = load_raw<CPL, DV_BF16, TAIL>(dv0 + static_cast<int64_t>(tok) * a.hd * kDvEs, col0, nv);
         }
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
@@ -243,7 +289,7 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
                 const bool ok = ends != 0ull;
                 const int tk = __shfl(tok, tbase + L, kWave);
                 cb[b] = ok ? __shfl(v, tbase + L, kWave) : 0.0f;
-                xr[b] = load_raw<CPL, DV_BF16>(dv0 + static_cast<int64_t>(tk) * a.hd * kDvEs, col0);
+                xr[b] = load_raw<CPL, DV_BF16, TAIL>(dv0 + static_cast<int64_t>(tk) * a.hd * kDvEs, col0, nv);
                 nb += ok ? 1 : 0;
                 ends &= ends - 1ull;
             }
@@ -266,9 +312,9 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
         }
     }
     if (SNAP && first) {   // the raw pre-write row, before this team's arrival or store
-        store_raw<CPL, BANK_BF16>(static_cast<unsigned char*>(a.snap) +
-                                      (a.snap_row0 + static_cast<int64_t>(p) * a.CW + j) * a.hd * kBankEs,
-                                  col0, base_raw);
+        store_raw<CPL, BANK_BF16, TAIL>(static_cast<unsigned char*>(a.snap) +
+                                            (a.snap_row0 + static_cast<int64_t>(p) * a.CW + j) * a.hd * kBankEs,
+                                        col0, nv, base_raw);
     }
     if (first && last_seen) {   // the whole group in one segment
         float base[CPL];
@@ -276,7 +322,7 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
         float o[CPL];
 #pragma unroll
         for (int q = 0; q < CPL; ++q) o[q] = fmaf(base[q], cpe, acc[q]);
-        store_cols<CPL, BANK_BF16>(bank_row, col0, o);
+        store_cols<CPL, BANK_BF16, TAIL>(bank_row, col0, nv, o);
         return;
     }
     // Split group: publish this segment's partial; the last segment team to arrive combines the
@@ -291,7 +337,9 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
     const int64_t gslot = prow + first_pos;
     float* part = a.part + (prow + j) * a.hd;
 #pragma unroll
-    for (int q = 0; q < CPL; ++q) __hip_atomic_store(part + col0 + q, acc[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int q = 0; q < CPL; ++q) {
+        if (!TAIL || q < nv) __hip_atomic_store(part + col0 + q, acc[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     const int seg = dist / kSeg;
     // The segment holding LAST publishes the segment count and the group's cpe (that of LAST).
     if (last_seen && tl == 0) {
@@ -315,7 +363,7 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
     const unsigned long long mw = __hip_atomic_load(reinterpret_cast<const unsigned long long*>(a.meta + gslot),
                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int2 meta = make_int2(static_cast<int>(mw & 0xFFFFFFFFull), static_cast<int>(mw >> 32));
-    const RawCols<CPL, BANK_BF16> b2raw = load_raw<CPL, BANK_BF16>(bank_row, col0);
+    const RawCols<CPL, BANK_BF16> b2raw = load_raw<CPL, BANK_BF16, TAIL>(bank_row, col0, nv);
     float tot[CPL];
 #pragma unroll
     for (int q = 0; q < CPL; ++q) tot[q] = 0.0f;
@@ -326,7 +374,9 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
         for (int b = 0; b < kPartBatch; ++b) {
             const float* pp = a.part + (prow + min(first_pos + (sg0 + b) * kSeg, a.CW - 1)) * a.hd + col0;
 #pragma unroll
-            for (int q = 0; q < CPL; ++q) pv[b][q] = __hip_atomic_load(pp + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int q = 0; q < CPL; ++q) {
+                pv[b][q] = (!TAIL || q < nv) ? __hip_atomic_load(pp + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
+            }
         }
 #pragma unroll
         for (int b = 0; b < kPartBatch; ++b) {
@@ -348,14 +398,14 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
     float o[CPL];
 #pragma unroll
     for (int q = 0; q < CPL; ++q) o[q] = fmaf(b2[q], cpe_l, tot[q]);
-    store_cols<CPL, BANK_BF16>(bank_row, col0, o);
+    store_cols<CPL, BANK_BF16, TAIL>(bank_row, col0, nv, o);
 }
 
 // Teams take U consecutive K-row positions. Groups of one member (the common case) are done
 // together: their records, base rows and token rows are all in flight at once. Every other valid
 // position goes through the general walk, one after the other.
 // SNAP: also write the compact snapshot (the raw pre-write row of every valid group at its FIRST).
-template <int CPL, bool BANK_BF16, bool DV_BF16, int U, bool SNAP>
+template <int CPL, bool BANK_BF16, bool DV_BF16, int U, bool SNAP, bool TAIL>
 __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
     static_assert(CPL % (BANK_BF16 ? 8 : 4) == 0 && CPL % (DV_BF16 ? 8 : 4) == 0, "16-byte column groups");
     constexpr int kBankEs = BANK_BF16 ? 2 : 4;
@@ -367,11 +417,12 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
     if (J0 >= total) return;
     const int col0 = tl * CPL;
     if (col0 >= a.hd) return;   // lanes past the row (the team's lane 0 always stays)
+    const int nv = TAIL ? min(CPL, a.hd - col0) : CPL;   // the lane's columns
     const uint4* kr_step = a.krec + a.chunk0 * a.CW;
     if constexpr (U == 1) {   // one position: straight into the walk (its first member is the short path)
         const uint4 r0 = kr_step[J0];
         const int p = J0 / a.CW;
-        if (!(r0.x & kInvalid)) dw_walk<CPL, BANK_BF16, DV_BF16, SNAP>(a, p, J0 - p * a.CW, r0, col0, tl);
+        if (!(r0.x & kInvalid)) dw_walk<CPL, BANK_BF16, DV_BF16, SNAP, TAIL>(a, p, J0 - p * a.CW, r0, col0, nv, tl);
         return;
     }
     // The records of positions J0 .. J0+U-1 (the steps' chunks are contiguous in krec), then the
@@ -400,11 +451,11 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
         if (ones & (1u << u)) {
             const int pu = (J0 + u) / a.CW;
             const int64_t tok_row = static_cast<int64_t>(pu) * a.C + ((r[u].x >> kTokShift) & 0xFFu);
-            braw[u] = load_raw<CPL, BANK_BF16>(static_cast<const unsigned char*>(a.bank) +
-                                                   static_cast<int64_t>(r[u].y) * a.hd * kBankEs,
-                                               col0);
-            xraw[u] = load_raw<CPL, DV_BF16>(static_cast<const unsigned char*>(a.dv) + (a.dv_row0 + tok_row) * a.hd * kDvEs,
-                                             col0);
+            braw[u] = load_raw<CPL, BANK_BF16, TAIL>(static_cast<const unsigned char*>(a.bank) +
+                                                         static_cast<int64_t>(r[u].y) * a.hd * kBankEs,
+                                                     col0, nv);
+            xraw[u] = load_raw<CPL, DV_BF16, TAIL>(
+                static_cast<const unsigned char*>(a.dv) + (a.dv_row0 + tok_row) * a.hd * kDvEs, col0, nv);
         }
     }
     // Every new row first (rows of other positions are computed on zeros and dropped), then the
@@ -415,8 +466,8 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
         const float sc = __uint_as_float(r[u].z), cpe = __uint_as_float(r[u].w);
         float b[CPL], x[CPL], o[CPL];
         if (SNAP && (ones & (1u << u))) {   // the raw pre-write row of a one-member group
-            store_raw<CPL, BANK_BF16>(static_cast<unsigned char*>(a.snap) + (a.snap_row0 + J0 + u) * a.hd * kBankEs,
-                                      col0, braw[u]);
+            store_raw<CPL, BANK_BF16, TAIL>(static_cast<unsigned char*>(a.snap) + (a.snap_row0 + J0 + u) * a.hd * kBankEs,
+                                            col0, nv, braw[u]);
         }
         unpack_cols<CPL, BANK_BF16>(braw[u], b);
         unpack_cols<CPL, DV_BF16>(xraw[u], x);
@@ -429,8 +480,8 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (ones & (1u << u)) {
-            store_raw<CPL, BANK_BF16>(static_cast<unsigned char*>(a.bank) + static_cast<int64_t>(r[u].y) * a.hd * kBankEs,
-                                      col0, oraw[u]);
+            store_raw<CPL, BANK_BF16, TAIL>(static_cast<unsigned char*>(a.bank) + static_cast<int64_t>(r[u].y) * a.hd * kBankEs,
+                                            col0, nv, oraw[u]);
         }
     }
 
@@ -438,7 +489,7 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
     for (int u = 0; u < U; ++u) {
         if (!(ones & (1u << u)) && !(r[u].x & kInvalid)) {
             const int pu = (J0 + u) / a.CW;
-            dw_walk<CPL, BANK_BF16, DV_BF16, SNAP>(a, pu, J0 + u - pu * a.CW, r[u], col0, tl);
+            dw_walk<CPL, BANK_BF16, DV_BF16, SNAP, TAIL>(a, pu, J0 + u - pu * a.CW, r[u], col0, nv, tl);
         }
     }
 }
@@ -447,10 +498,10 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
 // per team then outweigh the shorter grid), else 1.
 constexpr int64_t kDwWavesForPairs = 32 * 256;
 
-template <int CPL, bool BB, bool DB, int U>
+template <int CPL, bool BB, bool DB, int U, bool TAIL>
 hipError_t launch_dw_u(DwArgs a, hipStream_t st, const hipEvent_t* ev) {
-    const void* fn = a.snap != nullptr ? reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U, true>)
-                                       : reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U, false>);
+    const void* fn = a.snap != nullptr ? reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U, true, TAIL>)
+                                       : reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U, false, TAIL>);
     const int64_t teams = (static_cast<int64_t>(a.P) * a.CW + U - 1) / U;
     const int64_t blocks = (teams + a.teams_per_block - 1) / a.teams_per_block;
     void* kargs[] = {&a};
@@ -458,15 +509,18 @@ hipError_t launch_dw_u(DwArgs a, hipStream_t st, const hipEvent_t* ev) {
 }
 
 template <int CPL, bool BB, bool DB>
-hipError_t launch_dw(const DwArgs& a, hipStream_t st, const hipEvent_t* ev) {
+hipError_t launch_dw(const DwArgs& a, bool tail, hipStream_t st, const hipEvent_t* ev) {
+    if (tail) return launch_dw_u<CPL, BB, DB, 1, true>(a, st, ev);   // (element accesses: one position per team)
     const int64_t waves = static_cast<int64_t>(a.P) * a.CW * (int64_t(1) << a.ts_log2) / kWave;
-    return waves >= kDwWavesForPairs ? launch_dw_u<CPL, BB, DB, 2>(a, st, ev) : launch_dw_u<CPL, BB, DB, 1>(a, st, ev);
+    return waves >= kDwWavesForPairs ? launch_dw_u<CPL, BB, DB, 2, false>(a, st, ev)
+                                     : launch_dw_u<CPL, BB, DB, 1, false>(a, st, ev);
 }
 
 template <int CPL>
-hipError_t launch_dw_types(const DwArgs& a, bool bank_bf16, bool dv_bf16, hipStream_t st, const hipEvent_t* ev) {
-    if (bank_bf16) return dv_bf16 ? launch_dw<CPL, true, true>(a, st, ev) : launch_dw<CPL, true, false>(a, st, ev);
-    return dv_bf16 ? launch_dw<CPL, false, true>(a, st, ev) : launch_dw<CPL, false, false>(a, st, ev);
+hipError_t launch_dw_types(const DwArgs& a, bool bank_bf16, bool dv_bf16, bool tail, hipStream_t st,
+                           const hipEvent_t* ev) {
+    if (bank_bf16) return dv_bf16 ? launch_dw<CPL, true, true>(a, tail, st, ev) : launch_dw<CPL, true, false>(a, tail, st, ev);
+    return dv_bf16 ? launch_dw<CPL, false, true>(a, tail, st, ev) : launch_dw<CPL, false, false>(a, tail, st, ev);
 }
 
 }  // namespace
@@ -485,8 +539,12 @@ DwWorkspace dw_workspace_layout(const sdm_dw_io* io) {
 int dw_cols_per_lane(int hd) {
     if (hd % 8 == 0 && hd <= 8 * kWave) return 8;
     if (hd % 16 == 0 && hd <= 16 * kWave) return 16;
+    if (hd >= 1 && hd <= 8 * kWave) return 8;      // tail variant (element accesses)
+    if (hd >= 1 && hd <= 16 * kWave) return 16;
     return 0;
 }
+
+bool dw_tail(int hd) { return !(hd % 8 == 0 && hd <= 8 * kWave) && !(hd % 16 == 0 && hd <= 16 * kWave); }
 
 hipError_t dw_launch(const DwLaunch& Lc, hipStream_t st) {
     const sdm_dw_io* io = Lc.io;
@@ -522,8 +580,9 @@ hipError_t dw_launch(const DwLaunch& Lc, hipStream_t st) {
     const bool bb = io->bank_dtype == SDM_BF16, db = io->dv_dtype == SDM_BF16;
     const hipEvent_t ev[2] = {io->events != nullptr ? io->events[0] : nullptr,
                               io->events != nullptr ? io->events[1] : nullptr};
-    if (cpl == 8) return launch_dw_types<8>(a, bb, db, st, ev);
-    return launch_dw_types<16>(a, bb, db, st, ev);
+    const bool tail = dw_tail(io->hd);
+    if (cpl == 8) return launch_dw_types<8>(a, bb, db, tail, st, ev);
+    return launch_dw_types<16>(a, bb, db, tail, st, ev);
 }
 
 }  // namespace sdm

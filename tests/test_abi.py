@@ -103,8 +103,10 @@ def dw(**kw):
     (dict(), -1, _lib.SDM_ESHAPE), (dict(), 4, _lib.SDM_ESHAPE), (dict(P=2), 2, _lib.SDM_ESHAPE),
     (dict(C=0), 0, _lib.SDM_ESHAPE), (dict(W=257), 0, _lib.SDM_ESHAPE),
     (dict(bank_dtype=7), 0, _lib.SDM_EINVAL), (dict(dv_dtype=3), 0, _lib.SDM_EINVAL),
-    (dict(hd=126), 0, _lib.SDM_ESHAPE), (dict(hd=8192), 0, _lib.SDM_ESHAPE),
-    (dict(hd=100), 0, _lib.SDM_EUNSUPPORTED), (dict(hd=2048), 0, _lib.SDM_EUNSUPPORTED),
+    (dict(hd=0), 0, _lib.SDM_ESHAPE), (dict(hd=8192), 0, _lib.SDM_ESHAPE),
+    (dict(hd=1032), 0, _lib.SDM_EUNSUPPORTED), (dict(hd=2048), 0, _lib.SDM_EUNSUPPORTED),
+    (dict(hd=126, bank=FAKE + 1), 0, _lib.SDM_EALIGN), (dict(hd=126, dv=FAKE + 2), 0, _lib.SDM_EALIGN),
+    (dict(hd=37, snap=FAKE + 1, snap_rows=1 << 20), 0, _lib.SDM_EALIGN),   # (bf16 bank: 2-byte rows)
     (dict(bank=None), 0, _lib.SDM_EINVAL), (dict(krec=None), 0, _lib.SDM_EINVAL),
     (dict(bank=FAKE + 8), 0, _lib.SDM_EALIGN), (dict(dv=FAKE + 4), 0, _lib.SDM_EALIGN),
     (dict(krec=FAKE + 8), 0, _lib.SDM_EALIGN), (dict(rows=0), 0, _lib.SDM_EINVAL),

@@ -249,6 +249,26 @@ def test_bf16_values(case):
     H.run_dw_check(wl, out, shape, set(range(min(wl.steps, 2))), sample_untouched=0)
 
 
+@pytest.mark.parametrize("case", [
+    dict(hd=1, bank="f32", dv="f32", S=64, C=32, W=4, P=1, vl=None, split=True),
+    dict(hd=37, bank="bf16", dv="f32", S=8, C=64, W=6, P=2, vl=50, split=True),     # long groups: split path
+    dict(hd=37, bank="bf16", dv="f32", S=8, C=64, W=6, P=2, vl=50, split=False),    # ... one team per group
+    dict(hd=100, bank="f32", dv="bf16", S=200, C=128, W=8, P=2, vl=None, split=True),
+    dict(hd=126, bank="bf16", dv="bf16", S=16, C=128, W=4, P=1, vl=None, split=True),
+    dict(hd=520, bank="f32", dv="f32", S=300, C=64, W=4, P=1, vl=None, split=True),  # 16 columns per lane
+    dict(hd=1000, bank="bf16", dv="f32", S=30, C=64, W=4, P=1, vl=None, split=True),
+])
+def test_dw_tail_head_dims(case):
+    """Head dims that 16-byte vectors do not divide (element accesses, element-aligned rows): every
+    checked DW step matches the oracle, and rows no group touches keep their bits."""
+    sh = W.Shape("tail_hd", P=case["P"], T=case["C"] * 3, C=case["C"], W=case["W"], R=2, S=case["S"], hd=case["hd"],
+                 bank_dtype=case["bank"], dv_dtype=case["dv"], slots="uniform", valid_last=case["vl"])
+    wl = W.make(sh, seed=783)
+    say("dw tail", case)
+    shape, out = H.run_phase1(wl)
+    H.run_dw_check(wl, out, shape, set(range(wl.steps)), sample_untouched=200, split=case["split"])
+
+
 @pytest.mark.parametrize("idx,steps", [(0, None), (2, 1), (4, 1)])
 def test_perm_output(idx, steps):
     """The optional sorted order (entry index at each sorted position) equals the oracle's, and
@@ -294,7 +314,8 @@ def test_int64_ids(idx, steps):
 
 
 @pytest.mark.parametrize("idx,steps,case", [(0, 2, None), (1, 2, None), (2, 1, None),
-                                            (None, 1, dict(C=255, W=33, R=2, S=5000, P=1, vl=None, hd=960))])
+                                            (None, 1, dict(C=255, W=33, R=2, S=5000, P=1, vl=None, hd=960)),
+                                            (None, 2, dict(C=64, W=6, R=2, S=8, P=2, vl=50, hd=37))])   # tail
 def test_dw_snapshot(idx, steps, case):
     """The compact snapshot: row (ti*P*C*W + p*C*W + j) holds the raw pre-write bank row of the valid
     group whose FIRST is at K-row position j (positions from the oracle's sorted K rows), every other
