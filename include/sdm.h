@@ -235,7 +235,8 @@ typedef struct sdm_read_io {
     const void* bank;       /* [rows, hd] SDM_F32 or SDM_BF16: the memory BEFORE this step's DW (read only) */
     int32_t bank_dtype;     /* sdm_dtype */
     int64_t rows;           /* bank rows (an id outside 0..rows-1 contributes nothing) */
-    int32_t hd;             /* row width, a multiple of 8 */
+    int32_t hd;             /* row width, 1..4096 (a multiple of 8 takes 16-byte vector rows; any other
+                               width element accesses, with element-aligned arrays) */
     const void* k_idx;      /* [N, C, W] absolute slot ids of the writes (Phase-1 input), int32 or int64 */
     const void* q_idx;      /* [N, C, R] absolute slot ids of the reads, same type */
     const void* k_eff;      /* [N, C, W] from sdm_phase1, float32 or bfloat16 (val_bytes) */
@@ -270,7 +271,8 @@ typedef struct sdm_read_io {
  *   pred[t] = p0[t] + sum_{j<t} A[t,j] dv[j],    read[t] = q0[t] + sum_{j<=t} QK[t,j] dv[j].
  * pred and read are what a token-by-token decay / predict / write / read evaluation of the chunk
  * sees; masked tokens get 0 in every output and none of their inputs is read. Two kernels on st.
- * Requires (ti + 1) * P <= N, C <= 256, hd a multiple of 8, 16-byte aligned bank, v, dv, pred, read.
+ * Requires (ti + 1) * P <= N, C <= 256, 1 <= hd <= 4096; bank, v, dv, pred and read 16-byte aligned
+ * when hd is a multiple of 8, element-aligned otherwise.
  */
 sdm_status sdm_read_step(const sdm_read_io* io, int64_t ti, hipStream_t st);
 

@@ -163,8 +163,7 @@ sdm_status sdm_read_step(const sdm_read_io* io, int64_t ti, hipStream_t st) {
         return fail(SDM_EINVAL, "sdm_read_step: val_bytes = %d (0 or 4: float32 k_eff / q_w; 2: bfloat16)", io->val_bytes);
     if (io->idx_bytes == 8 && (!aligned(io->k_idx, 8) || !aligned(io->q_idx, 8)))
         return fail(SDM_EALIGN, "sdm_read_step: int64 ids must be 8-byte aligned");
-    if (io->hd < 8 || io->hd > 4096 || io->hd % 8 != 0)
-        return fail(SDM_ESHAPE, "sdm_read_step: hd = %d (multiple of 8 in 8..4096)", io->hd);
+    if (io->hd < 1 || io->hd > 4096) return fail(SDM_ESHAPE, "sdm_read_step: hd = %d outside 1..4096", io->hd);
     if (io->rows < 0 || io->step_rows < 0 || io->out_rows < 0)
         return fail(SDM_EINVAL, "sdm_read_step: rows / step_rows / out_rows");
     if (ti * io->step_rows + static_cast<int64_t>(io->P) * io->C > io->out_rows)
@@ -175,9 +174,14 @@ sdm_status sdm_read_step(const sdm_read_io* io, int64_t ti, hipStream_t st) {
     for (const void* p : req) {
         if (p == nullptr) return fail(SDM_EINVAL, "sdm_read_step: every array is required");
     }
+    // hd a multiple of 8: 16-byte vector rows; any other hd: element accesses (element alignment).
+    const bool tail = io->hd % 8 != 0;
     const void* a16[] = {io->bank, io->v, io->dv, io->pred, io->read};
-    for (const void* p : a16) {
-        if (!aligned(p, 16)) return fail(SDM_EALIGN, "sdm_read_step: bank, v, dv, pred and read must be 16-byte aligned");
+    const uintptr_t es[] = {static_cast<uintptr_t>(io->bank_dtype == SDM_BF16 ? 2 : 4), 4, 4, 4, 4};
+    for (int i = 0; i < 5; ++i) {
+        if (!aligned(a16[i], tail ? es[i] : 16))
+            return fail(SDM_EALIGN, "sdm_read_step: bank, v, dv, pred and read must be %s aligned",
+                        tail ? "element" : "16-byte");
     }
     const void* a4[] = {io->k_idx, io->q_idx, io->a, io->qk, io->beta};
     for (const void* p : a4) {

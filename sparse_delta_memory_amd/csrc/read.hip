@@ -53,11 +53,34 @@ struct ReadArgs {
     int vbf;             // 1: k_eff / q_w are bfloat16
 };
 
-template <bool BF16>
-__device__ __forceinline__ void load_row8(const void* bank, int64_t slot, int hd, int col0, uint4 (&raw)[BF16 ? 1 : 2]) {
+// TAIL (hd not a multiple of 8): rows are only element-aligned; the lane's first nv (1..8) columns
+// are read element by element and the rest are zero.
+template <bool BF16, bool TAIL>
+__device__ __forceinline__ void load_row8(const void* bank, int64_t slot, int hd, int col0, int nv,
+                                          uint4 (&raw)[BF16 ? 1 : 2]) {
     const unsigned char* p = static_cast<const unsigned char*>(bank) + (slot * hd + col0) * (BF16 ? 2 : 4);
-    raw[0] = *reinterpret_cast<const uint4*>(p);
-    if constexpr (!BF16) raw[1] = *reinterpret_cast<const uint4*>(p + 16);
+    if constexpr (TAIL) {
+        uint32_t w[BF16 ? 4 : 8];
+        if constexpr (BF16) {
+            const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
+#pragma unroll
+            for (int e = 0; e < kGCols; e += 2) {
+                const uint32_t lo = e < nv ? q[e] : 0u;
+                const uint32_t hi = e + 1 < nv ? q[e + 1] : 0u;
+                w[e / 2] = lo | hi << 16;
+            }
+            raw[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+            const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+            for (int e = 0; e < kGCols; ++e) w[e] = e < nv ? q[e] : 0u;
+            raw[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            raw[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        }
+    } else {
+        raw[0] = *reinterpret_cast<const uint4*>(p);
+        if constexpr (!BF16) raw[1] = *reinterpret_cast<const uint4*>(p + 16);
+    }
 }
 
 template <bool BF16>
@@ -78,8 +101,8 @@ __device__ __forceinline__ void widen_row8(const uint4 (&raw)[BF16 ? 1 : 2], flo
 
 // sum_e w[e] M0[idx[e]] over n entries (idx: int32, or int64 when ID64), 8 columns of one token;
 // entries kGBatch at a time.
-template <bool BF16, bool ID64>
-__device__ __forceinline__ void gather_sum(const ReadArgs& a, const void* idx, const void* w, int n, int col0,
+template <bool BF16, bool ID64, bool TAIL>
+__device__ __forceinline__ void gather_sum(const ReadArgs& a, const void* idx, const void* w, int n, int col0, int nv,
                                            float (&acc)[kGCols]) {
     for (int e0 = 0; e0 < n; e0 += kGBatch) {
         int64_t s[kGBatch];
@@ -99,7 +122,7 @@ __device__ __forceinline__ void gather_sum(const ReadArgs& a, const void* idx, c
         for (int b = 0; b < kGBatch; ++b) {
             // A slot outside the bank contributes nothing (its row is not read).
             const bool ok = s[b] >= 0 && s[b] < a.rows;
-            load_row8<BF16>(a.bank, ok ? s[b] : 0, a.hd, col0, raw[b]);
+            load_row8<BF16, TAIL>(a.bank, ok ? s[b] : 0, a.hd, col0, nv, raw[b]);
             if (!ok) ws[b] = 0.0f;
         }
 #pragma unroll
@@ -112,7 +135,7 @@ __device__ __forceinline__ void gather_sum(const ReadArgs& a, const void* idx, c
     }
 }
 
-template <bool BF16, bool ID64>
+template <bool BF16, bool ID64, bool TAIL>
 __global__ void __launch_bounds__(256) read_gather_kernel(ReadArgs a) {
     const int tok_blocks = (a.C + kGTok - 1) / kGTok;
     const int col_blocks = (a.hd + kGTeam * kGCols - 1) / (kGTeam * kGCols);
@@ -122,6 +145,7 @@ __global__ void __launch_bounds__(256) read_gather_kernel(ReadArgs a) {
     const int t = (rem / col_blocks) * kGTok + static_cast<int>(threadIdx.x) / kGTeam;
     const int col0 = ((rem % col_blocks) * kGTeam + static_cast<int>(threadIdx.x) % kGTeam) * kGCols;
     if (t >= a.C || col0 >= a.hd) return;
+    const int nv = TAIL ? min(kGCols, a.hd - col0) : kGCols;   // the lane's columns
     const int64_t c = a.chunk0 + p;
     const int tv = c >= a.first_partial ? a.valid_last : a.C;
     const int64_t row = a.row0 + static_cast<int64_t>(p) * a.C + t;
@@ -132,17 +156,27 @@ __global__ void __launch_bounds__(256) read_gather_kernel(ReadArgs a) {
         const int64_t ko = (c * a.C + t) * a.W, qo = (c * a.C + t) * a.R;
         const int es = ID64 ? 8 : 4;
         const int vs = a.vbf ? 2 : 4;   // bytes per weight
-        gather_sum<BF16, ID64>(a, static_cast<const char*>(a.k_idx) + ko * es,
-                               static_cast<const char*>(a.k_eff) + ko * vs, a.W, col0, pk);
-        gather_sum<BF16, ID64>(a, static_cast<const char*>(a.q_idx) + qo * es,
-                               static_cast<const char*>(a.q_w) + qo * vs, a.R, col0, pq);
+        gather_sum<BF16, ID64, TAIL>(a, static_cast<const char*>(a.k_idx) + ko * es,
+                                     static_cast<const char*>(a.k_eff) + ko * vs, a.W, col0, nv, pk);
+        gather_sum<BF16, ID64, TAIL>(a, static_cast<const char*>(a.q_idx) + qo * es,
+                                     static_cast<const char*>(a.q_w) + qo * vs, a.R, col0, nv, pq);
     }
-    float4* op = reinterpret_cast<float4*>(a.pred + row * a.hd + col0);
-    float4* oq = reinterpret_cast<float4*>(a.read + row * a.hd + col0);
-    op[0] = make_float4(pk[0], pk[1], pk[2], pk[3]);
-    op[1] = make_float4(pk[4], pk[5], pk[6], pk[7]);
-    oq[0] = make_float4(pq[0], pq[1], pq[2], pq[3]);
-    oq[1] = make_float4(pq[4], pq[5], pq[6], pq[7]);
+    if constexpr (TAIL) {
+#pragma unroll
+        for (int q = 0; q < kGCols; ++q) {
+            if (q < nv) {
+                a.pred[row * a.hd + col0 + q] = pk[q];
+                a.read[row * a.hd + col0 + q] = pq[q];
+            }
+        }
+    } else {
+        float4* op = reinterpret_cast<float4*>(a.pred + row * a.hd + col0);
+        float4* oq = reinterpret_cast<float4*>(a.read + row * a.hd + col0);
+        op[0] = make_float4(pk[0], pk[1], pk[2], pk[3]);
+        op[1] = make_float4(pk[4], pk[5], pk[6], pk[7]);
+        oq[0] = make_float4(pq[0], pq[1], pq[2], pq[3]);
+        oq[1] = make_float4(pq[4], pq[5], pq[6], pq[7]);
+    }
 }
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -318,6 +352,14 @@ __global__ void __launch_bounds__(256) read_solve_kernel(ReadArgs a) {
     }
 }
 
+template <bool TAIL>
+const void* gather_fn(bool bf16, bool id64) {
+    return bf16 ? (id64 ? reinterpret_cast<const void*>(&read_gather_kernel<true, true, TAIL>)
+                        : reinterpret_cast<const void*>(&read_gather_kernel<true, false, TAIL>))
+                : (id64 ? reinterpret_cast<const void*>(&read_gather_kernel<false, true, TAIL>)
+                        : reinterpret_cast<const void*>(&read_gather_kernel<false, false, TAIL>));
+}
+
 }  // namespace
 
 hipError_t read_launch(const ReadLaunch& L, hipStream_t st) {
@@ -352,11 +394,8 @@ hipError_t read_launch(const ReadLaunch& L, hipStream_t st) {
                               io->events ? io->events[2] : nullptr, io->events ? io->events[3] : nullptr};
     void* kargs[] = {&a};
     const bool id64 = io->idx_bytes == 8;
-    const void* g = io->bank_dtype == SDM_BF16
-                        ? (id64 ? reinterpret_cast<const void*>(&read_gather_kernel<true, true>)
-                                : reinterpret_cast<const void*>(&read_gather_kernel<true, false>))
-                        : (id64 ? reinterpret_cast<const void*>(&read_gather_kernel<false, true>)
-                                : reinterpret_cast<const void*>(&read_gather_kernel<false, false>));
+    const void* g = io->hd % kGCols != 0 ? gather_fn<true>(io->bank_dtype == SDM_BF16, id64)
+                                         : gather_fn<false>(io->bank_dtype == SDM_BF16, id64);
     hipError_t e = hipExtLaunchKernel(g, dim3(static_cast<unsigned>(a.P * tok_blocks * col_blocks)), dim3(256), kargs, 0,
                                       st, ev[0], ev[1], 0);
     if (e != hipSuccess) return e;

@@ -153,7 +153,8 @@ def read_io(**kw):
 @pytest.mark.parametrize("kw,ti,status", [
     (dict(C=0), 0, _lib.SDM_ESHAPE), (dict(C=257), 0, _lib.SDM_ESHAPE), (dict(R=0), 0, _lib.SDM_ESHAPE),
     (dict(P=0), 0, _lib.SDM_ESHAPE), (dict(), 2, _lib.SDM_ESHAPE), (dict(), -1, _lib.SDM_ESHAPE),
-    (dict(hd=12), 0, _lib.SDM_ESHAPE), (dict(bank_dtype=7), 0, _lib.SDM_EINVAL),
+    (dict(hd=0), 0, _lib.SDM_ESHAPE), (dict(hd=5000), 0, _lib.SDM_ESHAPE), (dict(bank_dtype=7), 0, _lib.SDM_EINVAL),
+    (dict(hd=12, v=FAKE + 2), 0, _lib.SDM_EALIGN), (dict(hd=12, bank=FAKE + 1), 0, _lib.SDM_EALIGN),
     (dict(valid_last=129), 0, _lib.SDM_EINVAL), (dict(first_partial=9), 0, _lib.SDM_EINVAL),
     (dict(out_rows=100), 0, _lib.SDM_EINVAL), (dict(beta=None), 0, _lib.SDM_EINVAL),
     (dict(dv=FAKE + 4), 0, _lib.SDM_EALIGN), (dict(a=FAKE + 2), 0, _lib.SDM_EALIGN),

@@ -42,10 +42,14 @@ def test_read_side_matches_oracle(idx, steps, checked):
     dict(C=37, W=5, R=3, S=9, P=2, steps=2, vl=11),       # heavy sharing, ragged row and chunk
     dict(C=256, W=8, R=8, S=48, P=1, steps=1, vl=None),   # every group hot: dense A and QK
     dict(C=1, W=1, R=1, S=4, P=1, steps=2, vl=None),      # one token
+    dict(C=64, W=4, R=3, S=40, P=2, steps=2, vl=21, hd=37, bank="bf16"),   # head dims 8 does not divide
+    dict(C=96, W=8, R=8, S=64, P=1, steps=1, vl=None, hd=1, bank="f32"),
+    dict(C=128, W=4, R=4, S=300, P=1, steps=1, vl=None, hd=100, bank="f32"),
 ])
 def test_read_side_edge_shapes(case):
     sh = W.Shape("read_edge", P=case["P"], T=case["C"] * case["steps"], C=case["C"], W=case["W"], R=case["R"],
-                 S=case["S"], hd=64, bank_dtype="f32", dv_dtype="f32", slots="uniform", valid_last=case["vl"])
+                 S=case["S"], hd=case.get("hd", 64), bank_dtype=case.get("bank", "f32"), dv_dtype="f32",
+                 slots="uniform", valid_last=case["vl"])
     wl = W.make(sh, seed=779)
     say("read side edge", case)
     H.run_read_check(wl, list(range(wl.steps)))
