@@ -201,15 +201,19 @@ typedef struct sdm_dw_io {
     size_t workspace_bytes;
     hipEvent_t* events;     /* optional (NULL: none): 2 caller-created events bound to the start and end
                                of this call's kernel (hipExtLaunchKernel) */
-    void* snap;             /* optional (NULL: none) compact snapshot, [*, hd] in the bank dtype, aligned
+    void* snap;             /* optional (NULL: none) compact snapshot, [*, hd] (snap_dtype), aligned
                                as bank: for every valid group of chunk ti*P + p whose FIRST is at K-row
-                               position j, row (ti * snap_step_rows + p * C * W + j) receives the group's raw
+                               position j, row (ti * snap_step_rows + p * C * W + j) receives the group's
                                pre-write bank row (page "sparse_delta_memory/cuda/mover_da2_cuda.py", the
                                da2_dw kernel's compact snapshot; page "sparse_delta_memory/cuda/mover_fx_cuda.py",
                                module docstring: the saving forward's raw copies of the base rows). Other rows
                                are not written. */
     int64_t snap_step_rows; /* rows between steps in snap (P*C*W when every step is kept, 0 for one step) */
     int64_t snap_rows;      /* rows in snap: ti * snap_step_rows + P * C * W <= snap_rows */
+    int32_t snap_dtype;     /* element type of snap (sdm_dtype): the bank's own type gives the raw copy;
+                               SDM_BF16 with an SDM_F32 bank gives each row rounded to bf16, nearest even (page
+                               "sparse_delta_memory/cuda/mover_fx_cuda.py": the bf16 compact rows of a float32
+                               bank); SDM_F32 rows of a bf16 bank are refused */
 } sdm_dw_io;
 
 /* Workspace bytes sdm_dw_step can use for this shape (P * C * W * (4 * hd + 12), rounded). */

@@ -156,8 +156,9 @@ class DwPlan:
     bank [rows, hd] float32 or bfloat16 (updated in place); dv [*, hd] float32 or bfloat16 token rows,
     row ti*dv_step_rows + p*C + t; krec from phase1; workspace from alloc_dw_workspace (optional:
     without it every group is walked by one team of lanes); snapshot (optional) [*, hd] in the bank
-    dtype: row ti*snap_step_rows + p*C*W + j receives the pre-write row of the group whose FIRST is
-    at K-row position j. The plan keeps the tensors alive."""
+    dtype, or bfloat16 with a float32 bank (rows rounded to bfloat16): row ti*snap_step_rows + p*C*W + j
+    receives the pre-write row of the group whose FIRST is at K-row position j. The plan keeps the
+    tensors alive."""
 
     def __init__(self, bank, dv, krec, shape: P1Shape, dv_step_rows: int, workspace=None, snapshot=None,
                  snap_step_rows: int = 0):
@@ -167,8 +168,9 @@ class DwPlan:
             raise TypeError("DwPlan: bank and dv must be float32 or bfloat16")
         self._lib = _lib.load()
         self._keep = (bank, dv, krec, workspace, snapshot)
-        if snapshot is not None and (snapshot.dtype != bank.dtype or snapshot.shape[1] != bank.shape[1]):
-            raise TypeError("DwPlan: the snapshot must be [*, hd] in the bank dtype")
+        if snapshot is not None and (snapshot.shape[1] != bank.shape[1] or not (
+                snapshot.dtype == bank.dtype or (snapshot.dtype == torch.bfloat16 and bank.dtype == torch.float32))):
+            raise TypeError("DwPlan: the snapshot must be [*, hd] in the bank dtype, or bfloat16 for a float32 bank")
         io = _lib.DwIO()
         io.bank = bank.data_ptr()
         io.bank_dtype = _lib.SDM_BF16 if bank.dtype == torch.bfloat16 else _lib.SDM_F32
@@ -187,6 +189,7 @@ class DwPlan:
             io.snap = snapshot.data_ptr()
             io.snap_step_rows = int(snap_step_rows)
             io.snap_rows = snapshot.shape[0]
+            io.snap_dtype = _lib.SDM_BF16 if snapshot.dtype == torch.bfloat16 else _lib.SDM_F32
         self.io = io
         self._io_ref = ctypes.byref(io)
         self._device = bank.device

@@ -52,6 +52,7 @@ class DwIO(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("events", ctypes.c_void_p),
         ("snap", ctypes.c_void_p), ("snap_step_rows", ctypes.c_int64), ("snap_rows", ctypes.c_int64),
+        ("snap_dtype", ctypes.c_int32),
     ]
 
 

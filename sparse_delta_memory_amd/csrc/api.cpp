@@ -237,7 +237,11 @@ sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st) {
             return fail(SDM_EWORKSPACE, "sdm_dw_step: workspace needs %zu bytes, got %zu", need, io->workspace_bytes);
     }
     if (io->snap != nullptr) {
-        if (!aligned(io->snap, tail ? bank_es : 16)) return fail(SDM_EALIGN, "sdm_dw_step: snap is misaligned");
+        if (io->snap_dtype != io->bank_dtype && !(io->snap_dtype == SDM_BF16 && io->bank_dtype == SDM_F32))
+            return fail(SDM_EINVAL, "sdm_dw_step: snap_dtype %d (the bank's, or bf16 rows of a float32 bank)",
+                        io->snap_dtype);
+        const int snap_es = io->snap_dtype == SDM_BF16 ? 2 : bank_es;
+        if (!aligned(io->snap, tail ? snap_es : 16)) return fail(SDM_EALIGN, "sdm_dw_step: snap is misaligned");
         const int64_t pcw = static_cast<int64_t>(io->P) * io->C * io->W;
         if (io->snap_step_rows < 0 || ti * io->snap_step_rows + pcw > io->snap_rows)
             return fail(SDM_EINVAL, "sdm_dw_step: snap holds %lld rows, step %lld needs %lld",

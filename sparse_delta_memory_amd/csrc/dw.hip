@@ -159,6 +159,20 @@ __device__ __forceinline__ void store_cols(void* row, int col0, int nv, const fl
     store_raw<CPL, BF16, TAIL>(row, col0, nv, pack_cols<CPL, BF16>(x));
 }
 
+// One snapshot row's columns: SNAP 1 the raw bank bits; SNAP 2 (float32 bank, bf16 snapshot rows)
+// the row rounded to bf16, nearest even (mover_fx_cuda page: the bf16 compact rows of a float32
+// bank, each group's pre-write row rounded once).
+template <int CPL, bool BANK_BF16, int SNAP, bool TAIL>
+__device__ __forceinline__ void snap_store(const DwArgs& a, int64_t row, int col0, int nv, const RawCols<CPL, BANK_BF16>& raw) {
+    if constexpr (SNAP == 2) {
+        float f[CPL];
+        unpack_cols<CPL, BANK_BF16>(raw, f);
+        store_raw<CPL, true, TAIL>(static_cast<unsigned char*>(a.snap) + row * a.hd * 2, col0, nv, pack_cols<CPL, true>(f));
+    } else {
+        store_raw<CPL, BANK_BF16, TAIL>(static_cast<unsigned char*>(a.snap) + row * a.hd * (BANK_BF16 ? 2 : 4), col0, nv, raw);
+    }
+}
+
 // Members of a group per segment when the group is split (a workspace is given), and the last
 // in-group distance that still marks a segment start (the distance field saturates at 4095).
 constexpr int kSeg = 32;
@@ -168,7 +182,7 @@ constexpr int kSegLimit = (4095 / kSeg) * kSeg;
 // or, when groups are split, a segment start; other positions return at once. The members after
 // the first are read a team-wide batch at a time and summed per run of one token (the token row is
 // loaded once per run); the sum's order is fixed by the records, so results are reproducible.
-template <int CPL, bool BANK_BF16, bool DV_BF16, bool SNAP, bool TAIL>
+template <int CPL, bool BANK_BF16, bool DV_BF16, int SNAP, bool TAIL>
 __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0, int col0, int nv, int tl) {
     // Member records and token rows loaded together (fewer when the rows take more registers).
     constexpr int kBatch = (CPL == 8 && DV_BF16) ? 4 : 2;
@@ -311,10 +325,8 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
             done = true;
         }
     }
-    if (SNAP && first) {   // the raw pre-write row, before this team's arrival or store
-        store_raw<CPL, BANK_BF16, TAIL>(static_cast<unsigned char*>(a.snap) +
-                                            (a.snap_row0 + static_cast<int64_t>(p) * a.CW + j) * a.hd * kBankEs,
-                                        col0, nv, base_raw);
+    if (SNAP && first) {   // the pre-write row, before this team's arrival or store
+        snap_store<CPL, BANK_BF16, SNAP, TAIL>(a, a.snap_row0 + static_cast<int64_t>(p) * a.CW + j, col0, nv, base_raw);
     }
     if (first && last_seen) {   // the whole group in one segment
         float base[CPL];
@@ -405,7 +417,7 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
 // together: their records, base rows and token rows are all in flight at once. Every other valid
 // position goes through the general walk, one after the other.
 // SNAP: also write the compact snapshot (the raw pre-write row of every valid group at its FIRST).
-template <int CPL, bool BANK_BF16, bool DV_BF16, int U, bool SNAP, bool TAIL>
+template <int CPL, bool BANK_BF16, bool DV_BF16, int U, int SNAP, bool TAIL>
 __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
     static_assert(CPL % (BANK_BF16 ? 8 : 4) == 0 && CPL % (DV_BF16 ? 8 : 4) == 0, "16-byte column groups");
     constexpr int kBankEs = BANK_BF16 ? 2 : 4;
@@ -465,9 +477,8 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
     for (int u = 0; u < U; ++u) {
         const float sc = __uint_as_float(r[u].z), cpe = __uint_as_float(r[u].w);
         float b[CPL], x[CPL], o[CPL];
-        if (SNAP && (ones & (1u << u))) {   // the raw pre-write row of a one-member group
-            store_raw<CPL, BANK_BF16, TAIL>(static_cast<unsigned char*>(a.snap) + (a.snap_row0 + J0 + u) * a.hd * kBankEs,
-                                            col0, nv, braw[u]);
+        if (SNAP && (ones & (1u << u))) {   // the pre-write row of a one-member group
+            snap_store<CPL, BANK_BF16, SNAP, TAIL>(a, a.snap_row0 + J0 + u, col0, nv, braw[u]);
         }
         unpack_cols<CPL, BANK_BF16>(braw[u], b);
         unpack_cols<CPL, DV_BF16>(xraw[u], x);
@@ -499,9 +510,12 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
 constexpr int64_t kDwWavesForPairs = 32 * 256;
 
 template <int CPL, bool BB, bool DB, int U, bool TAIL>
-hipError_t launch_dw_u(DwArgs a, hipStream_t st, const hipEvent_t* ev) {
-    const void* fn = a.snap != nullptr ? reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U, true, TAIL>)
-                                       : reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U, false, TAIL>);
+hipError_t launch_dw_u(DwArgs a, bool snap_bf16, hipStream_t st, const hipEvent_t* ev) {
+    const void* fn = reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U, 0, TAIL>);
+    if (a.snap != nullptr) fn = reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U, 1, TAIL>);
+    if constexpr (!BB) {   // (a bf16 bank's rows are bf16 already: its bf16 snapshot is the raw one)
+        if (a.snap != nullptr && snap_bf16) fn = reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U, 2, TAIL>);
+    }
     const int64_t teams = (static_cast<int64_t>(a.P) * a.CW + U - 1) / U;
     const int64_t blocks = (teams + a.teams_per_block - 1) / a.teams_per_block;
     void* kargs[] = {&a};
@@ -509,18 +523,20 @@ hipError_t launch_dw_u(DwArgs a, hipStream_t st, const hipEvent_t* ev) {
 }
 
 template <int CPL, bool BB, bool DB>
-hipError_t launch_dw(const DwArgs& a, bool tail, hipStream_t st, const hipEvent_t* ev) {
-    if (tail) return launch_dw_u<CPL, BB, DB, 1, true>(a, st, ev);   // (element accesses: one position per team)
+hipError_t launch_dw(const DwArgs& a, bool tail, bool sbf, hipStream_t st, const hipEvent_t* ev) {
+    if (tail) return launch_dw_u<CPL, BB, DB, 1, true>(a, sbf, st, ev);   // (element accesses: one position per team)
     const int64_t waves = static_cast<int64_t>(a.P) * a.CW * (int64_t(1) << a.ts_log2) / kWave;
-    return waves >= kDwWavesForPairs ? launch_dw_u<CPL, BB, DB, 2, false>(a, st, ev)
-                                     : launch_dw_u<CPL, BB, DB, 1, false>(a, st, ev);
+    return waves >= kDwWavesForPairs ? launch_dw_u<CPL, BB, DB, 2, false>(a, sbf, st, ev)
+                                     : launch_dw_u<CPL, BB, DB, 1, false>(a, sbf, st, ev);
 }
 
 template <int CPL>
-hipError_t launch_dw_types(const DwArgs& a, bool bank_bf16, bool dv_bf16, bool tail, hipStream_t st,
+hipError_t launch_dw_types(const DwArgs& a, bool bank_bf16, bool dv_bf16, bool tail, bool sbf, hipStream_t st,
                            const hipEvent_t* ev) {
-    if (bank_bf16) return dv_bf16 ? launch_dw<CPL, true, true>(a, tail, st, ev) : launch_dw<CPL, true, false>(a, tail, st, ev);
-    return dv_bf16 ? launch_dw<CPL, false, true>(a, tail, st, ev) : launch_dw<CPL, false, false>(a, tail, st, ev);
+    if (bank_bf16) {
+        return dv_bf16 ? launch_dw<CPL, true, true>(a, tail, sbf, st, ev) : launch_dw<CPL, true, false>(a, tail, sbf, st, ev);
+    }
+    return dv_bf16 ? launch_dw<CPL, false, true>(a, tail, sbf, st, ev) : launch_dw<CPL, false, false>(a, tail, sbf, st, ev);
 }
 
 }  // namespace
@@ -581,8 +597,9 @@ hipError_t dw_launch(const DwLaunch& Lc, hipStream_t st) {
     const hipEvent_t ev[2] = {io->events != nullptr ? io->events[0] : nullptr,
                               io->events != nullptr ? io->events[1] : nullptr};
     const bool tail = dw_tail(io->hd);
-    if (cpl == 8) return launch_dw_types<8>(a, bb, db, tail, st, ev);
-    return launch_dw_types<16>(a, bb, db, tail, st, ev);
+    const bool sbf = io->snap_dtype == SDM_BF16;
+    if (cpl == 8) return launch_dw_types<8>(a, bb, db, tail, sbf, st, ev);
+    return launch_dw_types<16>(a, bb, db, tail, sbf, st, ev);
 }
 
 }  // namespace sdm

@@ -92,7 +92,7 @@ def test_phase1_argument_refusals():
 def dw(**kw):
     o = _lib.DwIO()
     d = dict(bank=FAKE, bank_dtype=_lib.SDM_BF16, rows=1 << 20, hd=128, dv=FAKE, dv_dtype=_lib.SDM_F32,
-             dv_step_rows=64, dv_rows=256, krec=FAKE, P=1, C=64, W=4, N=4)
+             dv_step_rows=64, dv_rows=256, krec=FAKE, P=1, C=64, W=4, N=4, snap_dtype=_lib.SDM_BF16)
     d.update(kw)
     for k, v in d.items():
         setattr(o, k, v)
@@ -107,6 +107,8 @@ def dw(**kw):
     (dict(hd=1032), 0, _lib.SDM_EUNSUPPORTED), (dict(hd=2048), 0, _lib.SDM_EUNSUPPORTED),
     (dict(hd=126, bank=FAKE + 1), 0, _lib.SDM_EALIGN), (dict(hd=126, dv=FAKE + 2), 0, _lib.SDM_EALIGN),
     (dict(hd=37, snap=FAKE + 1, snap_rows=1 << 20), 0, _lib.SDM_EALIGN),   # (bf16 bank: 2-byte rows)
+    (dict(snap=FAKE, snap_rows=1 << 20, snap_dtype=_lib.SDM_F32), 0, _lib.SDM_EINVAL),   # f32 rows of a bf16 bank
+    (dict(snap=FAKE, snap_rows=1 << 20, snap_dtype=9), 0, _lib.SDM_EINVAL),
     (dict(bank=None), 0, _lib.SDM_EINVAL), (dict(krec=None), 0, _lib.SDM_EINVAL),
     (dict(bank=FAKE + 8), 0, _lib.SDM_EALIGN), (dict(dv=FAKE + 4), 0, _lib.SDM_EALIGN),
     (dict(krec=FAKE + 8), 0, _lib.SDM_EALIGN), (dict(rows=0), 0, _lib.SDM_EINVAL),

@@ -315,16 +315,23 @@ def test_int64_ids(idx, steps):
 
 @pytest.mark.parametrize("idx,steps,case", [(0, 2, None), (1, 2, None), (2, 1, None),
                                             (None, 1, dict(C=255, W=33, R=2, S=5000, P=1, vl=None, hd=960)),
-                                            (None, 2, dict(C=64, W=6, R=2, S=8, P=2, vl=50, hd=37))])   # tail
+                                            (None, 2, dict(C=64, W=6, R=2, S=8, P=2, vl=50, hd=37)),   # tail
+                                            (0, 2, "bf16"),                                           # bf16 rows
+                                            (None, 2, dict(C=64, W=6, R=2, S=8, P=2, vl=50, hd=37, bank="f32",
+                                                           snap="bf16"))])
 def test_dw_snapshot(idx, steps, case):
     """The compact snapshot: row (ti*P*C*W + p*C*W + j) holds the raw pre-write bank row of the valid
     group whose FIRST is at K-row position j (positions from the oracle's sorted K rows), every other
-    row keeps its sentinel, and writing it changes no bank bit."""
+    row keeps its sentinel, and writing it changes no bank bit. bf16 snapshot rows of a float32 bank:
+    the pre-write row converted to bfloat16 (torch's round to nearest even)."""
+    snap_bf16 = case == "bf16" or (isinstance(case, dict) and case.get("snap") == "bf16")
+    if case == "bf16":
+        case = None
     if case is None:
         wl = W.make(idx, steps=steps)
     else:
         sh = W.Shape("snap_edge", P=case["P"], T=case["C"] * steps, C=case["C"], W=case["W"], R=case["R"],
-                     S=case["S"], hd=case["hd"], bank_dtype="bf16", dv_dtype="f32", slots="uniform",
+                     S=case["S"], hd=case["hd"], bank_dtype=case.get("bank", "bf16"), dv_dtype="f32", slots="uniform",
                      valid_last=case["vl"])
         wl = W.make(sh, seed=780)
     sh = wl.shape
@@ -333,7 +340,9 @@ def test_dw_snapshot(idx, steps, case):
     shape, out = H.run_phase1(wl)
     dv = H.device_dv(wl)
     bank0 = W.make_bank(wl, "cuda")
-    snap = torch.empty((wl.steps * P * CW, hd), dtype=bank0.dtype, device="cuda")
+    if snap_bf16:
+        assert bank0.dtype == torch.float32
+    snap = torch.empty((wl.steps * P * CW, hd), dtype=torch.bfloat16 if snap_bf16 else bank0.dtype, device="cuda")
     snap.view(torch.uint8).fill_(0xA5)
     sentinel = snap[0].clone()
     bank, bank_ref = bank0.clone(), bank0.clone()
@@ -357,6 +366,8 @@ def test_dw_snapshot(idx, steps, case):
             rows = ti * P * CW + p * CW
             got = snap[rows:rows + CW]
             want = bank0.index_select(0, torch.as_tensor(ref["krec_slot"][c][js], dtype=torch.long, device="cuda"))
+            if snap_bf16:
+                want = want.to(torch.bfloat16)
             assert torch.equal(got[torch.as_tensor(js, device="cuda")].view(torch.uint8), want.view(torch.uint8)), (ti, p)
             others = np.setdiff1d(np.arange(CW), js)
             if others.size:
