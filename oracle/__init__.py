@@ -49,7 +49,7 @@ class _ChunkIn(ctypes.Structure):
 _OUT_FIELDS = [
     "log_k", "rex", "cpe", "k_eff", "is_last", "is_only", "pos_k", "log_q", "q_w", "pos_q", "q_last", "q_only",
     "spay_k", "spay_q", "krec_slot", "krec_sc", "krec_cpe", "tiles_k", "a", "qk", "perm", "repeats",
-    "a_mag", "qk_mag", "a_cnt", "qk_cnt",
+    "a_mag", "qk_mag", "a_cnt", "qk_cnt", "gord_k",
 ]
 
 
@@ -125,7 +125,7 @@ def phase1(k_idx, q_idx, k_val, q_val, g, *, P=1, stream_offset=0, first_partial
         "krec_sc": ((nk,), np.float64), "krec_cpe": ((nk,), np.float64), "tiles_k": ((ntk + 1,), np.int32),
         "a": ((C, C), np.float64), "qk": ((C, C), np.float64), "perm": ((n,), np.int32), "repeats": ((1,), np.int64),
         "a_mag": ((C, C), np.float64), "qk_mag": ((C, C), np.float64), "a_cnt": ((C, C), np.int32),
-        "qk_cnt": ((C, C), np.int32),
+        "qk_cnt": ((C, C), np.int32), "gord_k": ((nk,), np.int32),
     }
     optional = {"a_mag", "qk_mag", "a_cnt", "qk_cnt"}   # evaluation-error scales: only when asked for
     want = (set(shapes) - optional) if fields is None else set(fields)

@@ -112,6 +112,10 @@ typedef struct {
     double* qk_mag;     /* [C, C] the same for QK */
     int32_t* a_cnt;     /* [C, C] number of terms per cell of A */
     int32_t* qk_cnt;    /* [C, C] the same for QK */
+    int32_t* gord_k;    /* [C*W] per K-row position: the ordinal of its group among the chunk's groups with
+                           a valid K entry, in K-row (slot) order; -1 for padding (the dense group
+                           ordinal of the compact rows, page "sparse_delta_memory/cuda/mover_fx_cuda.py",
+                           module docstring and the WR walk) */
 } oracle_chunk_out;
 
 typedef struct {
@@ -258,6 +262,7 @@ int oracle_phase1_chunk(const oracle_chunk_in* in, const oracle_chunk_out* out) 
     const int n = w.n;
     const int nk = C * W;
     int jk = 0, jq = 0;
+    int kgroups = 0;   /* groups with a valid K entry so far */
     for (int p = 0; p < n; ++p) {
         const int t = w.tok[p], lane = w.lane[p], q = w.isq[p];
         const int valid = !w.ent[p].invalid;
@@ -308,6 +313,8 @@ int oracle_phase1_chunk(const oracle_chunk_in* in, const oracle_chunk_out* out) 
             if (out->krec_slot) out->krec_slot[jk] = valid ? (int32_t)(w.ent[p].key + in->id_base) : 0;
             if (out->krec_sc) out->krec_sc[jk] = valid ? v * exp(rexv) : 0.0;
             if (out->krec_cpe) out->krec_cpe[jk] = valid ? cpe : 1.0;
+            if (valid && before == 0) ++kgroups;   /* the group's first valid K entry */
+            if (out->gord_k) out->gord_k[jk] = valid ? kgroups - 1 : -1;
             ++jk;
         }
     }

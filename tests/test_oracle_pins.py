@@ -386,3 +386,27 @@ def test_lane_gates_lowest_lane_applies():
     assert o["log_q"][0, 0, 0] == -0.5
     assert o["repeats"][0] == 1
     assert o["cpe"][0, 0, 0] == pytest.approx(math.exp(-0.5), rel=1e-15)
+
+
+@pytest.mark.parametrize("seed,S,vl", [(91, 5, None), (92, 40, 7), (93, 3000, None)])
+def test_group_ordinals_brute_force(seed, S, vl):
+    """gord_k: at every valid K-row position, the index of its slot among the chunk's distinct valid
+    write slots in ascending order (np.unique of the valid K ids, computed here), -1 at padding."""
+    rng = np.random.default_rng(seed)
+    N, C, W, R = 2, 24, 3, 2
+    k_idx = rng.integers(0, S, (N, C, W)).astype(np.int32)
+    q_idx = rng.integers(0, S, (N, C, R)).astype(np.int32)
+    k_val = rng.standard_normal((N, C, W)).astype(np.float32)
+    q_val = rng.standard_normal((N, C, R)).astype(np.float32)
+    g = (-rng.random((N, C)) * 0.5).astype(np.float32)
+    fp = N - 1 if vl is not None else N
+    o = oracle.phase1(k_idx, q_idx, k_val, q_val, g, first_partial=fp, valid_last=C if vl is None else vl,
+                      fields=["gord_k", "krec_slot", "spay_k"])
+    for c in range(N):
+        tv = vl if (vl is not None and c >= fp) else C
+        distinct = np.unique(k_idx[c, :tv].ravel())
+        pad = ((o["spay_k"][c].astype(np.int64) >> 17) & 1).astype(bool)
+        assert np.all(o["gord_k"][c][pad] == -1)
+        want = np.searchsorted(distinct, o["krec_slot"][c][~pad])
+        np.testing.assert_array_equal(o["gord_k"][c][~pad], want)
+        assert (~pad).sum() == tv * W
