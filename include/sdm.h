@@ -145,6 +145,11 @@ typedef struct sdm_p1_io {
                                device-side error cannot be a return code: nothing here synchronizes).
                                Out-of-range ids only reach the sort as masked keys, so Phase 1 stays in
                                bounds; the records they leave must not be given to sdm_dw_step. */
+    int32_t* gord_k;        /* optional [N, C*W] (NULL: skipped): per K-only-row position, the dense ordinal of
+                               its group among the chunk's groups with a valid write, in K-row (slot) order;
+                               -1 for padding. It is the row index of the dense compact snapshot (page
+                               "sparse_delta_memory/cuda/mover_fx_cuda.py", module docstring: a group's row
+                               at its dense ordinal in the chunk). Written by a small scan kernel on st. */
 } sdm_p1_io;
 
 /*
@@ -214,6 +219,10 @@ typedef struct sdm_dw_io {
                                SDM_BF16 with an SDM_F32 bank gives each row rounded to bf16, nearest even (page
                                "sparse_delta_memory/cuda/mover_fx_cuda.py": the bf16 compact rows of a float32
                                bank); SDM_F32 rows of a bf16 bank are refused */
+    const int32_t* snap_ord; /* optional (NULL: rows at FIRST positions, as above): gord_k from sdm_phase1; the
+                               group whose FIRST is at K-row position j then goes to row (ti * snap_step_rows +
+                               p * C * W + snap_ord[(ti*P + p) * C * W + j]), the dense layout: each chunk's
+                               groups in rows 0 .. groups - 1 of its C * W rows */
 } sdm_dw_io;
 
 /* Workspace bytes sdm_dw_step can use for this shape (P * C * W * (4 * hd + 12), rounded). */

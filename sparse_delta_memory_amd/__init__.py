@@ -55,10 +55,10 @@ def alloc_phase1_outputs(shape: P1Shape, device="cuda", fields=None):
         "spay_k": ((N, C * W), torch.int32), "spay_q": ((N, C * R), torch.int32),
         "krec": ((N, C * W, 4), torch.int32), "tiles_k": ((N, ntk + 1), torch.int32),
         "a": ((N, C, C), torch.float32), "qk": ((N, C, C), torch.float32), "repeats": ((N,), torch.int32),
-        "perm": ((N, C * (W + R)), torch.int32),
+        "perm": ((N, C * (W + R)), torch.int32), "gord_k": ((N, C * W), torch.int32),
     }
-    # perm (the sorted order itself) only when asked for
-    want = (set(spec) - {"perm"}) if fields is None else set(fields) | {"spay_k", "krec", "tiles_k"}
+    # perm (the sorted order itself) and gord_k (dense group ordinals) only when asked for
+    want = (set(spec) - {"perm", "gord_k"}) if fields is None else set(fields) | {"spay_k", "krec", "tiles_k"}
     return {k: torch.empty(s, dtype=dt, device=device) for k, (s, dt) in spec.items() if k in want}
 
 
@@ -103,6 +103,7 @@ def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=No
     io.events = None if arr is None else ctypes.cast(arr, ctypes.c_void_p).value
     if status is not None:
         io.status = status.data_ptr()
+    io.gord_k = _ptr(out.get("gord_k"))
     if pair_stream is not None:
         ready = _event_array([pair_ready] if pair_ready is not None else [], 1, "phase1 pair_ready")
         io.pair_stream = pair_stream.cuda_stream
@@ -157,17 +158,18 @@ class DwPlan:
     row ti*dv_step_rows + p*C + t; krec from phase1; workspace from alloc_dw_workspace (optional:
     without it every group is walked by one team of lanes); snapshot (optional) [*, hd] in the bank
     dtype, or bfloat16 with a float32 bank (rows rounded to bfloat16): row ti*snap_step_rows + p*C*W + j
-    receives the pre-write row of the group whose FIRST is at K-row position j. The plan keeps the
-    tensors alive."""
+    receives the pre-write row of the group whose FIRST is at K-row position j, or, with snap_ord (the
+    Phase-1 output gord_k), row ti*snap_step_rows + p*C*W + (the group's dense ordinal). The plan
+    keeps the tensors alive."""
 
     def __init__(self, bank, dv, krec, shape: P1Shape, dv_step_rows: int, workspace=None, snapshot=None,
-                 snap_step_rows: int = 0):
+                 snap_step_rows: int = 0, snap_ord=None):
         import torch
 
         if bank.dtype not in (torch.float32, torch.bfloat16) or dv.dtype not in (torch.float32, torch.bfloat16):
             raise TypeError("DwPlan: bank and dv must be float32 or bfloat16")
         self._lib = _lib.load()
-        self._keep = (bank, dv, krec, workspace, snapshot)
+        self._keep = (bank, dv, krec, workspace, snapshot, snap_ord)
         if snapshot is not None and (snapshot.shape[1] != bank.shape[1] or not (
                 snapshot.dtype == bank.dtype or (snapshot.dtype == torch.bfloat16 and bank.dtype == torch.float32))):
             raise TypeError("DwPlan: the snapshot must be [*, hd] in the bank dtype, or bfloat16 for a float32 bank")
@@ -190,6 +192,10 @@ class DwPlan:
             io.snap_step_rows = int(snap_step_rows)
             io.snap_rows = snapshot.shape[0]
             io.snap_dtype = _lib.SDM_BF16 if snapshot.dtype == torch.bfloat16 else _lib.SDM_F32
+            if snap_ord is not None:
+                if snap_ord.dtype != torch.int32 or snap_ord.numel() != krec.shape[0] * krec.shape[1]:
+                    raise TypeError("DwPlan: snap_ord must be the int32 [N, C*W] gord_k of these records")
+                io.snap_ord = snap_ord.data_ptr()
         self.io = io
         self._io_ref = ctypes.byref(io)
         self._device = bank.device

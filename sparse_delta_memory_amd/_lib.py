@@ -40,7 +40,8 @@ P1_IO_FIELDS = [
 class P1IO(ctypes.Structure):
     _fields_ = [(f, ctypes.c_void_p) for f in P1_IO_FIELDS] + [
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t), ("events", ctypes.c_void_p),
-        ("pair_stream", ctypes.c_void_p), ("pair_ready", ctypes.c_void_p), ("status", ctypes.c_void_p)]
+        ("pair_stream", ctypes.c_void_p), ("pair_ready", ctypes.c_void_p), ("status", ctypes.c_void_p),
+        ("gord_k", ctypes.c_void_p)]
 
 
 class DwIO(ctypes.Structure):
@@ -52,7 +53,7 @@ class DwIO(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("events", ctypes.c_void_p),
         ("snap", ctypes.c_void_p), ("snap_step_rows", ctypes.c_int64), ("snap_rows", ctypes.c_int64),
-        ("snap_dtype", ctypes.c_int32),
+        ("snap_dtype", ctypes.c_int32), ("snap_ord", ctypes.c_void_p),
     ]
 
 

@@ -102,7 +102,8 @@ sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st
         if (req[i] == nullptr) return fail(SDM_EINVAL, "sdm_phase1: %s is NULL", req_names[i]);
     }
     const void* a4[] = {io->k_idx, io->q_idx, io->g, io->log_k, io->rex, io->pos_k, io->log_q, io->pos_q,
-                        io->spay_k, io->spay_q, io->tiles_k, io->a, io->qk, io->repeats, io->perm, io->status};
+                        io->spay_k, io->spay_q, io->tiles_k, io->a, io->qk, io->repeats, io->perm, io->status,
+                        io->gord_k};
     for (const void* p : a4) {
         if (!aligned(p, 4)) return fail(SDM_EALIGN, "sdm_phase1: a 4-byte field is misaligned");
     }
@@ -240,6 +241,7 @@ sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st) {
         if (io->snap_dtype != io->bank_dtype && !(io->snap_dtype == SDM_BF16 && io->bank_dtype == SDM_F32))
             return fail(SDM_EINVAL, "sdm_dw_step: snap_dtype %d (the bank's, or bf16 rows of a float32 bank)",
                         io->snap_dtype);
+        if (!aligned(io->snap_ord, 4)) return fail(SDM_EALIGN, "sdm_dw_step: snap_ord is misaligned");
         const int snap_es = io->snap_dtype == SDM_BF16 ? 2 : bank_es;
         if (!aligned(io->snap, tail ? snap_es : 16)) return fail(SDM_EALIGN, "sdm_dw_step: snap is misaligned");
         const int64_t pcw = static_cast<int64_t>(io->P) * io->C * io->W;

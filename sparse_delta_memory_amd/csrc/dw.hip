@@ -34,6 +34,7 @@ struct DwArgs {
     void* snap;        // compact snapshot (NULL: none): row snap_row0 + p * CW + j_FIRST <- the group's pre-write row
     int64_t snap_row0; // ti * snap_step_rows
     int P, C, CW, hd, ts_log2, teams_per_block;
+    const int32_t* snap_ord;   // dense snapshot layout (NULL: rows at FIRST positions): gord_k of the records
 };
 
 // CPL consecutive columns of a row as raw 16-byte vectors: loads are issued apart from their
@@ -157,6 +158,13 @@ __device__ __forceinline__ void pin_raw(const RawCols<CPL, BF16>& r) {
 template <int CPL, bool BF16, bool TAIL>
 __device__ __forceinline__ void store_cols(void* row, int col0, int nv, const float (&x)[CPL]) {
     store_raw<CPL, BF16, TAIL>(row, col0, nv, pack_cols<CPL, BF16>(x));
+}
+
+// The snapshot row of the group whose FIRST is at K-row position j of stream p: j itself, or its
+// dense ordinal among the chunk's groups (snap_ord).
+__device__ __forceinline__ int64_t snap_row(const DwArgs& a, int p, int j) {
+    const int64_t pos = static_cast<int64_t>(p) * a.CW;
+    return a.snap_row0 + pos + (a.snap_ord != nullptr ? a.snap_ord[a.chunk0 * a.CW + pos + j] : j);
 }
 
 // One snapshot row's columns: SNAP 1 the raw bank bits; SNAP 2 (float32 bank, bf16 snapshot rows)
@@ -326,7 +334,7 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
         }
     }
     if (SNAP && first) {   // the pre-write row, before this team's arrival or store
-        snap_store<CPL, BANK_BF16, SNAP, TAIL>(a, a.snap_row0 + static_cast<int64_t>(p) * a.CW + j, col0, nv, base_raw);
+        snap_store<CPL, BANK_BF16, SNAP, TAIL>(a, snap_row(a, p, j), col0, nv, base_raw);
     }
     if (first && last_seen) {   // the whole group in one segment
         float base[CPL];
@@ -478,7 +486,8 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
         const float sc = __uint_as_float(r[u].z), cpe = __uint_as_float(r[u].w);
         float b[CPL], x[CPL], o[CPL];
         if (SNAP && (ones & (1u << u))) {   // the pre-write row of a one-member group
-            snap_store<CPL, BANK_BF16, SNAP, TAIL>(a, a.snap_row0 + J0 + u, col0, nv, braw[u]);
+            const int pu = (J0 + u) / a.CW;
+            snap_store<CPL, BANK_BF16, SNAP, TAIL>(a, snap_row(a, pu, J0 + u - pu * a.CW), col0, nv, braw[u]);
         }
         unpack_cols<CPL, BANK_BF16>(braw[u], b);
         unpack_cols<CPL, DV_BF16>(xraw[u], x);
@@ -576,6 +585,7 @@ hipError_t dw_launch(const DwLaunch& Lc, hipStream_t st) {
     a.meta = nullptr;
     a.snap = io->snap;
     a.snap_row0 = Lc.ti * io->snap_step_rows;
+    a.snap_ord = io->snap_ord;
     if (io->workspace != nullptr) {
         const DwWorkspace w = dw_workspace_layout(io);
         a.part = reinterpret_cast<float*>(static_cast<char*>(io->workspace) + w.part_off);

@@ -1529,6 +1529,42 @@ hipError_t launch_main(P1Args args, bool lane_gates, bool id64, bool vbf, size_t
     return hipExtLaunchKernel(fn, dim3(N), dim3(kNT), kargs, lds, st, start, stop, 0);
 }
 
+// Dense group ordinals of one chunk's K-only row (gord_k): a valid position gets the number of
+// valid FIRSTs at or before it, minus one (the ordinal of its group among the chunk's groups with a
+// valid write, in slot order); padding gets -1. One block per chunk walks the row 256 positions at
+// a time (coalesced): a block-wide inclusive scan of the FIRST flags plus the running count.
+constexpr int kOrdThreads = 256;
+
+__global__ void __launch_bounds__(kOrdThreads) p1_ordinal_kernel(const uint32_t* spay_k, int32_t* gord, int CW) {
+    __shared__ int wsum[kOrdThreads / kWave];
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * CW;
+    const int lane = static_cast<int>(lane_id());
+    const int w = static_cast<int>(threadIdx.x) / kWave;
+    int carry = 0;
+    for (int j0 = 0; j0 < CW; j0 += kOrdThreads) {
+        const int j = j0 + static_cast<int>(threadIdx.x);
+        const uint32_t x = j < CW ? spay_k[base + j] : kInvalid;
+        const bool valid = (x & kInvalid) == 0u;
+        int v = (valid && (x & kFirst)) ? 1 : 0;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int o = __shfl_up(v, d, kWave);
+            if (lane >= d) v += o;
+        }
+        if (lane == kWave - 1) wsum[w] = v;
+        __syncthreads();
+        int before = carry, total = 0;
+#pragma unroll
+        for (int k = 0; k < kOrdThreads / kWave; ++k) {
+            before += k < w ? wsum[k] : 0;
+            total += wsum[k];
+        }
+        if (j < CW) gord[base + j] = valid ? before + v - 1 : -1;
+        carry += total;
+        __syncthreads();   // wsum is rewritten by the next round
+    }
+}
+
 }  // namespace
 
 P1Workspace p1_workspace_layout(const sdm_p1_shape* s) {
@@ -1645,6 +1681,11 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
         case 4: e = launch_main<4>(a, s->g_lane_stride != 0, s->idx_bytes == 8, vbf, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
         case 8: e = launch_main<8>(a, s->g_lane_stride != 0, s->idx_bytes == 8, vbf, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
         default: e = launch_main<16>(a, s->g_lane_stride != 0, s->idx_bytes == 8, vbf, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
+    }
+    if (e == hipSuccess && io->gord_k != nullptr) {   // (on st, after the sort/scan kernel's spay_k)
+        hipLaunchKernelGGL(p1_ordinal_kernel, dim3(s->N), dim3(kOrdThreads), 0, st,
+                           reinterpret_cast<const uint32_t*>(io->spay_k), io->gord_k, s->C * s->W);
+        e = hipGetLastError();
     }
     if (e != hipSuccess || !pairs) return e;
     PairArgs pa;

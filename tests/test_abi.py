@@ -109,6 +109,7 @@ def dw(**kw):
     (dict(hd=37, snap=FAKE + 1, snap_rows=1 << 20), 0, _lib.SDM_EALIGN),   # (bf16 bank: 2-byte rows)
     (dict(snap=FAKE, snap_rows=1 << 20, snap_dtype=_lib.SDM_F32), 0, _lib.SDM_EINVAL),   # f32 rows of a bf16 bank
     (dict(snap=FAKE, snap_rows=1 << 20, snap_dtype=9), 0, _lib.SDM_EINVAL),
+    (dict(snap=FAKE, snap_rows=1 << 20, snap_ord=FAKE + 2), 0, _lib.SDM_EALIGN),
     (dict(bank=None), 0, _lib.SDM_EINVAL), (dict(krec=None), 0, _lib.SDM_EINVAL),
     (dict(bank=FAKE + 8), 0, _lib.SDM_EALIGN), (dict(dv=FAKE + 4), 0, _lib.SDM_EALIGN),
     (dict(krec=FAKE + 8), 0, _lib.SDM_EALIGN), (dict(rows=0), 0, _lib.SDM_EINVAL),
@@ -182,3 +183,4 @@ def test_phase1_value_alignment():
     assert call_p1(shape(), io(k_val=FAKE + 2)) == _lib.SDM_EALIGN
     assert call_p1(shape(), io(cpe=FAKE + 2)) == _lib.SDM_EALIGN
     assert call_p1(shape(val_bytes=2), io(q_w=FAKE + 1)) == _lib.SDM_EALIGN
+    assert call_p1(shape(), io(gord_k=FAKE + 2)) == _lib.SDM_EALIGN

@@ -269,6 +269,22 @@ def test_dw_tail_head_dims(case):
     H.run_dw_check(wl, out, shape, set(range(wl.steps)), sample_untouched=200, split=case["split"])
 
 
+@pytest.mark.parametrize("idx,steps", [(0, None), (1, 2), (2, 1), (4, 1)])
+def test_group_ordinals(idx, steps):
+    """gord_k (dense group ordinals of the K-only row) equals the oracle's bit for bit, and asking
+    for it changes no other output bit."""
+    wl = W.make(idx, steps=steps)
+    say("group ordinals", idx, steps)
+    shape, out = H.run_phase1(wl, fields=["gord_k"])
+    _, plain = H.run_phase1(wl)
+    for k in plain:
+        assert torch.equal(out[k].view(torch.uint8), plain[k].view(torch.uint8)), k
+    chunks = list(range(min(wl.N, 8))) + [wl.N - 1]
+    ref = H.oracle_phase1(wl, chunks, fields=["gord_k"])
+    got = out["gord_k"].index_select(0, torch.as_tensor(chunks, device="cuda")).cpu().numpy()
+    H.assert_exact("gord_k", got, ref["gord_k"])
+
+
 @pytest.mark.parametrize("idx,steps", [(0, None), (2, 1), (4, 1)])
 def test_perm_output(idx, steps):
     """The optional sorted order (entry index at each sorted position) equals the oracle's, and
@@ -318,14 +334,18 @@ def test_int64_ids(idx, steps):
                                             (None, 2, dict(C=64, W=6, R=2, S=8, P=2, vl=50, hd=37)),   # tail
                                             (0, 2, "bf16"),                                           # bf16 rows
                                             (None, 2, dict(C=64, W=6, R=2, S=8, P=2, vl=50, hd=37, bank="f32",
-                                                           snap="bf16"))])
+                                                           snap="bf16")),
+                                            (1, 2, "dense"), (2, 1, "dense"),                         # dense rows
+                                            (None, 2, dict(C=64, W=6, R=2, S=8, P=2, vl=50, hd=37, dense=True))])
 def test_dw_snapshot(idx, steps, case):
     """The compact snapshot: row (ti*P*C*W + p*C*W + j) holds the raw pre-write bank row of the valid
     group whose FIRST is at K-row position j (positions from the oracle's sorted K rows), every other
     row keeps its sentinel, and writing it changes no bank bit. bf16 snapshot rows of a float32 bank:
-    the pre-write row converted to bfloat16 (torch's round to nearest even)."""
+    the pre-write row converted to bfloat16 (torch's round to nearest even). Dense layout (the Phase-1
+    group ordinals as snap_ord): the chunk's groups in rows 0 .. groups - 1, ascending slot order."""
     snap_bf16 = case == "bf16" or (isinstance(case, dict) and case.get("snap") == "bf16")
-    if case == "bf16":
+    dense = case == "dense" or (isinstance(case, dict) and case.get("dense", False))
+    if case in ("bf16", "dense"):
         case = None
     if case is None:
         wl = W.make(idx, steps=steps)
@@ -336,8 +356,8 @@ def test_dw_snapshot(idx, steps, case):
         wl = W.make(sh, seed=780)
     sh = wl.shape
     P, C, hd, CW = sh.P, sh.C, sh.hd, sh.C * sh.W
-    say("dw snapshot", idx, case)
-    shape, out = H.run_phase1(wl)
+    say("dw snapshot", idx, case, "dense" if dense else "")
+    shape, out = H.run_phase1(wl, fields=["gord_k"] if dense else None)
     dv = H.device_dv(wl)
     bank0 = W.make_bank(wl, "cuda")
     if snap_bf16:
@@ -347,7 +367,8 @@ def test_dw_snapshot(idx, steps, case):
     sentinel = snap[0].clone()
     bank, bank_ref = bank0.clone(), bank0.clone()
     plan_s = sdm.DwPlan(bank, dv, out["krec"], shape, dv_step_rows=P * C,
-                        workspace=sdm.alloc_dw_workspace(shape, hd, device="cuda"), snapshot=snap, snap_step_rows=P * CW)
+                        workspace=sdm.alloc_dw_workspace(shape, hd, device="cuda"), snapshot=snap, snap_step_rows=P * CW,
+                        snap_ord=out["gord_k"] if dense else None)
     plan_n = sdm.DwPlan(bank_ref, dv, out["krec"], shape, dv_step_rows=P * C,
                         workspace=sdm.alloc_dw_workspace(shape, hd, device="cuda"))
     ref = H.oracle_phase1(wl, list(range(wl.N)), fields=["spay_k", "krec_slot"])
@@ -368,8 +389,9 @@ def test_dw_snapshot(idx, steps, case):
             want = bank0.index_select(0, torch.as_tensor(ref["krec_slot"][c][js], dtype=torch.long, device="cuda"))
             if snap_bf16:
                 want = want.to(torch.bfloat16)
-            assert torch.equal(got[torch.as_tensor(js, device="cuda")].view(torch.uint8), want.view(torch.uint8)), (ti, p)
-            others = np.setdiff1d(np.arange(CW), js)
+            at = np.arange(len(js)) if dense else js   # dense rows: the groups in FIRST (= slot) order
+            assert torch.equal(got[torch.as_tensor(at, device="cuda")].view(torch.uint8), want.view(torch.uint8)), (ti, p)
+            others = np.setdiff1d(np.arange(CW), at)
             if others.size:
                 rest = got[torch.as_tensor(others, device="cuda")]
                 assert torch.equal(rest.view(torch.uint8), sentinel.expand_as(rest).view(torch.uint8)), (ti, p)
