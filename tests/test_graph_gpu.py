@@ -24,22 +24,37 @@ sys.path.insert(0, os.path.dirname(__file__))
 import hip_harness as H  # noqa: E402
 
 
-@pytest.mark.parametrize("idx,steps", [(1, 4), (2, 2)])
-def test_graph_replays_match_eager(idx, steps):
-    wl = W.make(idx, steps=steps)
+@pytest.mark.parametrize("idx,steps,snap", [(1, 4, False), (2, 2, False), (0, 4, True), ("tail", 2, True)])
+def test_graph_replays_match_eager(idx, steps, snap):
+    """snap: also the group ordinals and the dense bf16 snapshot of a float32 bank ("tail": hd = 37,
+    bf16 values, so the element-access DW and the bf16-value sort/scan kernel are captured too)."""
+    if idx == "tail":
+        shp = W.Shape("graph_tail", P=2, T=64 * 3, C=64, W=6, R=2, S=40, hd=37, bank_dtype="f32", dv_dtype="f32",
+                      slots="uniform", valid_last=50)
+        wl = W.make(shp, steps=steps, seed=785, val_bf16=True)
+    else:
+        wl = W.make(idx, steps=steps)
     sh = wl.shape
-    print("graph replay: workload", idx, sh.name, "N =", wl.N, flush=True)
+    CW = sh.C * sh.W
+    print("graph replay: workload", idx, sh.name, "N =", wl.N, "snapshot" if snap else "", flush=True)
     shape = H.shape_of(wl)
     ins = H.device_inputs(wl)
     dv = H.device_dv(wl)
     bank0 = W.make_bank(wl, "cuda")
+    fields = None
+    if snap:
+        fields = set(sdm.alloc_phase1_outputs(sdm.make_shape(0, 1, 1, 1), device="cpu")) | {"gord_k"}
 
     def make_state():
-        out = sdm.alloc_phase1_outputs(shape, device="cuda")
+        out = sdm.alloc_phase1_outputs(shape, device="cuda", fields=fields)
         ws = torch.empty(sdm.phase1_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
         dw_ws = sdm.alloc_dw_workspace(shape, sh.hd, device="cuda")
         bank = bank0.clone()
-        plan = sdm.DwPlan(bank, dv, out["krec"], shape, dv_step_rows=wl.P * sh.C, workspace=dw_ws)
+        rows = torch.empty((wl.steps * wl.P * CW, sh.hd), dtype=torch.bfloat16, device="cuda") if snap else None
+        plan = sdm.DwPlan(bank, dv, out["krec"], shape, dv_step_rows=wl.P * sh.C, workspace=dw_ws, snapshot=rows,
+                          snap_step_rows=wl.P * CW, snap_ord=out["gord_k"] if snap else None)
+        if snap:
+            out["snapshot"] = rows   # compared with the outputs
 
         def step():
             sdm.phase1(shape, out=out, workspace=ws, **ins)
@@ -64,6 +79,8 @@ def test_graph_replays_match_eager(idx, steps):
         # Eager work of the same library between replays.
         step_e()
         bank_e.copy_(bank0)
+        if snap:   # rows no group writes keep the sentinel on both sides
+            out_e["snapshot"].view(torch.uint8).fill_(0xA5)
         step_e()
         torch.cuda.synchronize()
         graph.replay()

@@ -427,3 +427,41 @@ def test_slot_id_check():
     masked = wl.k_idx.copy()
     masked[wl.first_partial, wl.valid_last + 2, 0] = -7           # a masked token of the ragged chunk
     assert run(masked, wl.q_idx) == 0
+
+
+def test_fresh_process_reproducible():
+    """Two fresh processes produce the same bytes: Phase 1 outputs and the bank after every DW step
+    of the uniform workload, hashed in each (child processes, one after the other)."""
+    import hashlib
+    import subprocess
+
+    code = r"""
+import hashlib, sys, torch
+sys.path.insert(0, "tests")
+import hip_harness as H
+import sparse_delta_memory_amd as sdm
+from sparse_delta_memory_amd import workloads as W
+wl = W.make(1, steps=4)
+shape, out = H.run_phase1(wl)
+bank = W.make_bank(wl, "cuda")
+plan = sdm.DwPlan(bank, H.device_dv(wl), out["krec"], shape, dv_step_rows=wl.P * wl.shape.C,
+                  workspace=sdm.alloc_dw_workspace(shape, wl.shape.hd, device="cuda"))
+h = hashlib.sha256()
+for k in sorted(out):
+    h.update(out[k].cpu().view(torch.uint8).numpy().tobytes())
+for ti in range(wl.steps):
+    plan.step(ti)
+    torch.cuda.synchronize()
+    h.update(bank.cpu().view(torch.uint8).numpy().tobytes())
+print(h.hexdigest())
+"""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    say("fresh process: first child")
+    child = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=240)
+    assert child.returncode == 0, child.stderr[-2000:]
+    digest_child = child.stdout.strip().splitlines()[-1]
+    say("fresh process: second child")
+    here = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=240)
+    assert here.returncode == 0, here.stderr[-2000:]
+    assert here.stdout.strip().splitlines()[-1] == digest_child
+    assert len(digest_child) == 64 and hashlib.sha256(b"").hexdigest() != digest_child
