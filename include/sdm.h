@@ -289,6 +289,45 @@ typedef struct sdm_read_io {
  */
 sdm_status sdm_read_step(const sdm_read_io* io, int64_t ti, hipStream_t st);
 
+/* GDS of one step: the backward of the read gather for the chunks ti*P .. ti*P + P - 1. */
+typedef struct sdm_gds_io {
+    const void* bank;       /* [rows, hd] SDM_F32 or SDM_BF16: the memory BEFORE this step's DW (read only) */
+    int32_t bank_dtype;     /* sdm_dtype */
+    int64_t rows;           /* bank rows (an id outside 0..rows-1 contributes nothing) */
+    int32_t hd;             /* row width, a multiple of 4, 4..4096 */
+    const void* q_idx;      /* [N, C, R] absolute slot ids of the reads (Phase-1 input), int32 or int64 */
+    const void* q_w;        /* [N, C, R] from sdm_phase1, float32 or bf16 (val_bytes) */
+    const int32_t* spay_q;  /* [N, C*R] Q-only row elements from sdm_phase1 */
+    const float* gr;        /* gradient rows of the reads: row (ti * step_rows + p * C + t) of [*, hd], float32 */
+    int64_t step_rows;      /* rows between steps in gr (P*C, or 0 for a one-step buffer) */
+    int64_t gr_rows;        /* rows in gr: ti * step_rows + P * C <= gr_rows */
+    float* d_q_w;           /* OUT (NULL: skipped) [N, C, R]: the chunks of step ti, 0 for masked tokens */
+    void* grad;             /* IN/OUT (NULL: skipped) [rows, hd] SDM_F32 or SDM_BF16 gradient of the bank: every
+                               slot a valid read of the step names gains its sum, one read-modify-write per
+                               element (float32 add, then bf16 rounding to nearest even for a bf16 grad) */
+    int32_t grad_dtype;     /* sdm_dtype */
+    int32_t P, C, R, N;     /* the Phase-1 shape */
+    int32_t first_partial;  /* as in sdm_p1_shape: tokens >= valid_last of chunks >= first_partial are masked */
+    int32_t valid_last;
+    int32_t idx_bytes;      /* width of q_idx: 0 or 4 = int32, 8 = int64 */
+    int32_t val_bytes;      /* type of q_w: 0 or 4 = float32, 2 = bf16 */
+} sdm_gds_io;
+
+/*
+ * GDS (page "sparse_delta_memory/cuda/mover_da2_cuda.py": the GDS part of the module docstring and
+ * the comment of its scatter role): with the read gather q0[t] = sum_r q_w[t,r] M0[q_idx[t,r]] and
+ * the gradient rows gr[t] of the reads,
+ *   d_q_w[t, r] = <gr[t], M0[q_idx[t, r]]>                           (token order, no atomics),
+ *   grad[s]    += sum over valid (t, r) with q_idx[t, r] = s of q_w[t, r] gr[t]
+ * (sorted order: each valid Q group's members summed in order from +0, then one read-modify-write
+ * of the slot's row by the group's only writer; results are reproducible run to run). Masked tokens
+ * read nothing and contribute nothing. Within one step a slot appears in one group per chunk and
+ * the P chunks' streams own disjoint slots, so the writes never overlap. Two kernels on st.
+ * Requires (ti + 1) * P <= N, hd a multiple of 4, 16-byte aligned bank, gr and grad (8-byte for
+ * bf16 rows), 4-byte aligned ids (8 for int64), q_w, spay_q and d_q_w.
+ */
+sdm_status sdm_gds_step(const sdm_gds_io* io, int64_t ti, hipStream_t st);
+
 /* Static text for a status code. */
 const char* sdm_status_string(sdm_status s);
 

@@ -18,7 +18,7 @@ from . import _lib
 from ._lib import P1IO, P1Shape, SdmError  # noqa: F401
 
 __all__ = ["P1Shape", "phase1", "phase1_workspace_bytes", "alloc_phase1_outputs", "dw_step", "dw_workspace_bytes",
-           "alloc_dw_workspace", "DwPlan", "ReadPlan", "read_step", "SdmError", "make_shape",
+           "alloc_dw_workspace", "DwPlan", "ReadPlan", "read_step", "gds_step", "SdmError", "make_shape",
            "timing_events"]
 
 
@@ -277,3 +277,41 @@ class ReadPlan:
 def read_step(bank, p1, k_idx, q_idx, v, beta, dv, pred, read, shape: P1Shape, ti: int, step_rows: int, stream=None):
     """The read side of step `ti` through a plan built for this call (see ReadPlan)."""
     ReadPlan(bank, p1, k_idx, q_idx, v, beta, dv, pred, read, shape, step_rows).step(ti, stream=stream)
+
+
+def gds_step(bank, p1, q_idx, gr, shape: P1Shape, ti: int, step_rows: int, d_q_w=None, grad=None, stream=None):
+    """GDS of step `ti` (the backward of the read gather) on the current (or given) stream.
+
+    bank [rows, hd] float32 or bfloat16, the memory before the step (read only); p1: the Phase-1
+    outputs (q_w, spay_q); q_idx the Phase-1 read ids; gr [*, hd] float32 gradient rows of the reads,
+    row ti*step_rows + p*C + t. d_q_w [N, C, R] float32 (optional) receives the dots of the step's
+    chunks; grad [rows, hd] float32 or bfloat16 (optional) gains each read slot's sum in place."""
+    import torch
+
+    for name, t in (("gr", gr), ("d_q_w", d_q_w)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("gds_step: %s must be float32" % name)
+    for name, t in (("bank", bank), ("grad", grad)):
+        if t is not None and t.dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("gds_step: %s must be float32 or bfloat16" % name)
+    if grad is not None and tuple(grad.shape) != tuple(bank.shape):
+        raise TypeError("gds_step: grad must have the bank's shape")
+    lib = _lib.load()
+    io = _lib.GdsIO()
+    io.bank = bank.data_ptr()
+    io.bank_dtype = _lib.SDM_BF16 if bank.dtype == torch.bfloat16 else _lib.SDM_F32
+    io.rows, io.hd = bank.shape[0], bank.shape[1]
+    io.q_idx = q_idx.data_ptr()
+    io.q_w = p1["q_w"].data_ptr()
+    io.spay_q = p1["spay_q"].data_ptr()
+    io.gr = gr.data_ptr()
+    io.step_rows, io.gr_rows = int(step_rows), gr.shape[0]
+    io.d_q_w = _ptr(d_q_w)
+    io.grad = _ptr(grad)
+    io.grad_dtype = _lib.SDM_BF16 if (grad is not None and grad.dtype == torch.bfloat16) else _lib.SDM_F32
+    io.P, io.C, io.R, io.N = shape.P, shape.C, shape.R, shape.N
+    io.first_partial, io.valid_last = shape.first_partial, shape.valid_last
+    io.idx_bytes = q_idx.element_size()
+    io.val_bytes = p1["q_w"].element_size()
+    st = torch.cuda.current_stream(bank.device) if stream is None else stream
+    _lib.check(lib.sdm_gds_step(ctypes.byref(io), int(ti), ctypes.c_void_p(st.cuda_stream)))

@@ -70,8 +70,19 @@ class ReadIO(ctypes.Structure):
     ]
 
 
+class GdsIO(ctypes.Structure):
+    _fields_ = [
+        ("bank", ctypes.c_void_p), ("bank_dtype", ctypes.c_int32), ("rows", ctypes.c_int64), ("hd", ctypes.c_int32),
+        ("q_idx", ctypes.c_void_p), ("q_w", ctypes.c_void_p), ("spay_q", ctypes.c_void_p), ("gr", ctypes.c_void_p),
+        ("step_rows", ctypes.c_int64), ("gr_rows", ctypes.c_int64), ("d_q_w", ctypes.c_void_p), ("grad", ctypes.c_void_p),
+        ("grad_dtype", ctypes.c_int32), ("P", ctypes.c_int32), ("C", ctypes.c_int32), ("R", ctypes.c_int32),
+        ("N", ctypes.c_int32), ("first_partial", ctypes.c_int32), ("valid_last", ctypes.c_int32),
+        ("idx_bytes", ctypes.c_int32), ("val_bytes", ctypes.c_int32),
+    ]
+
+
 EXPORTS = ["sdm_phase1_workspace", "sdm_phase1", "sdm_dw_workspace", "sdm_dw_step", "sdm_read_step",
-           "sdm_status_string", "sdm_last_error"]
+           "sdm_gds_step", "sdm_status_string", "sdm_last_error"]
 
 _lock = threading.Lock()
 _lib = None
@@ -102,6 +113,8 @@ def load() -> ctypes.CDLL:
         lib.sdm_dw_step.restype = ctypes.c_int
         lib.sdm_read_step.argtypes = [ctypes.POINTER(ReadIO), ctypes.c_int64, ctypes.c_void_p]
         lib.sdm_read_step.restype = ctypes.c_int
+        lib.sdm_gds_step.argtypes = [ctypes.POINTER(GdsIO), ctypes.c_int64, ctypes.c_void_p]
+        lib.sdm_gds_step.restype = ctypes.c_int
         lib.sdm_status_string.argtypes = [ctypes.c_int]
         lib.sdm_status_string.restype = ctypes.c_char_p
         lib.sdm_last_error.argtypes = []

@@ -198,6 +198,43 @@ sdm_status sdm_read_step(const sdm_read_io* io, int64_t ti, hipStream_t st) {
     return SDM_OK;
 }
 
+sdm_status sdm_gds_step(const sdm_gds_io* io, int64_t ti, hipStream_t st) {
+    g_last_error.clear();
+    if (io == nullptr) return fail(SDM_EINVAL, "sdm_gds_step: io is NULL");
+    if (io->C < 1 || io->C > 256 || io->R < 1 || io->R > 256)
+        return fail(SDM_ESHAPE, "sdm_gds_step: C = %d, R = %d outside 1..256", io->C, io->R);
+    if (io->P < 1 || io->N < 0) return fail(SDM_ESHAPE, "sdm_gds_step: P = %d, N = %d", io->P, io->N);
+    if (ti < 0 || (ti + 1) * static_cast<int64_t>(io->P) > io->N)
+        return fail(SDM_ESHAPE, "sdm_gds_step: step %lld needs (ti+1)*P <= N = %d", static_cast<long long>(ti), io->N);
+    if (io->first_partial < 0 || io->first_partial > io->N || io->valid_last < 0 || io->valid_last > io->C)
+        return fail(SDM_EINVAL, "sdm_gds_step: first_partial = %d, valid_last = %d", io->first_partial, io->valid_last);
+    if (io->bank_dtype != SDM_F32 && io->bank_dtype != SDM_BF16)
+        return fail(SDM_EINVAL, "sdm_gds_step: bank_dtype %d", io->bank_dtype);
+    if (io->grad != nullptr && io->grad_dtype != SDM_F32 && io->grad_dtype != SDM_BF16)
+        return fail(SDM_EINVAL, "sdm_gds_step: grad_dtype %d", io->grad_dtype);
+    if (io->idx_bytes != 0 && io->idx_bytes != 4 && io->idx_bytes != 8)
+        return fail(SDM_EINVAL, "sdm_gds_step: idx_bytes = %d (0 or 4: int32 ids; 8: int64 ids)", io->idx_bytes);
+    if (io->val_bytes != 0 && io->val_bytes != 4 && io->val_bytes != 2)
+        return fail(SDM_EINVAL, "sdm_gds_step: val_bytes = %d (0 or 4: float32 q_w; 2: bf16)", io->val_bytes);
+    if (io->hd < 4 || io->hd > 4096 || io->hd % 4 != 0)
+        return fail(SDM_ESHAPE, "sdm_gds_step: hd = %d (a multiple of 4 in 4..4096)", io->hd);
+    if (io->rows < 0 || io->step_rows < 0 || io->gr_rows < 0) return fail(SDM_EINVAL, "sdm_gds_step: rows / step_rows / gr_rows");
+    if (ti * io->step_rows + static_cast<int64_t>(io->P) * io->C > io->gr_rows)
+        return fail(SDM_EINVAL, "sdm_gds_step: gr holds %lld rows, step %lld needs %lld", static_cast<long long>(io->gr_rows),
+                    static_cast<long long>(ti), static_cast<long long>(ti * io->step_rows + static_cast<int64_t>(io->P) * io->C));
+    if (io->bank == nullptr || io->q_idx == nullptr || io->q_w == nullptr || io->spay_q == nullptr || io->gr == nullptr)
+        return fail(SDM_EINVAL, "sdm_gds_step: bank, q_idx, q_w, spay_q and gr are required");
+    if (!aligned(io->bank, io->bank_dtype == SDM_BF16 ? 8 : 16) || !aligned(io->gr, 16) ||
+        (io->grad != nullptr && !aligned(io->grad, io->grad_dtype == SDM_BF16 ? 8 : 16)))
+        return fail(SDM_EALIGN, "sdm_gds_step: bank, gr and grad rows must be 16-byte aligned (8 for bf16)");
+    if (!aligned(io->q_idx, io->idx_bytes == 8 ? 8 : 4) || !aligned(io->q_w, io->val_bytes == 2 ? 2 : 4) ||
+        !aligned(io->spay_q, 4) || !aligned(io->d_q_w, 4))
+        return fail(SDM_EALIGN, "sdm_gds_step: q_idx, q_w, spay_q or d_q_w misaligned");
+    const hipError_t e = sdm::gds_launch(io, ti, st);
+    if (e != hipSuccess) return fail(SDM_EHIP, "sdm_gds_step: %s", hipGetErrorString(e));
+    return SDM_OK;
+}
+
 sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st) {
     g_last_error.clear();
     if (io == nullptr) return fail(SDM_EINVAL, "sdm_dw_step: io is NULL");

@@ -65,4 +65,7 @@ struct ReadLaunch {
 // Enqueue the read side of one step (gather kernel, then substitution kernel).
 hipError_t read_launch(const ReadLaunch& L, hipStream_t st);
 
+// GDS of step ti (validated by sdm_gds_step).
+hipError_t gds_launch(const sdm_gds_io* io, int64_t ti, hipStream_t st);
+
 }  // namespace sdm

@@ -184,3 +184,30 @@ def test_phase1_value_alignment():
     assert call_p1(shape(), io(cpe=FAKE + 2)) == _lib.SDM_EALIGN
     assert call_p1(shape(val_bytes=2), io(q_w=FAKE + 1)) == _lib.SDM_EALIGN
     assert call_p1(shape(), io(gord_k=FAKE + 2)) == _lib.SDM_EALIGN
+
+
+def gds_io(**kw):
+    o = _lib.GdsIO()
+    d = dict(bank=FAKE, bank_dtype=_lib.SDM_BF16, rows=1 << 20, hd=128, q_idx=FAKE, q_w=FAKE, spay_q=FAKE, gr=FAKE,
+             step_rows=512, gr_rows=1 << 20, d_q_w=FAKE, grad=FAKE, grad_dtype=_lib.SDM_F32, P=4, C=128, R=16, N=8,
+             first_partial=8, valid_last=128, idx_bytes=4, val_bytes=4)
+    d.update(kw)
+    for k, v in d.items():
+        setattr(o, k, v)
+    return o
+
+
+@pytest.mark.parametrize("kw,ti,status", [
+    (dict(), 2, _lib.SDM_ESHAPE), (dict(), -1, _lib.SDM_ESHAPE), (dict(C=0), 0, _lib.SDM_ESHAPE),
+    (dict(R=257), 0, _lib.SDM_ESHAPE), (dict(hd=126), 0, _lib.SDM_ESHAPE), (dict(bank_dtype=5), 0, _lib.SDM_EINVAL),
+    (dict(grad_dtype=5), 0, _lib.SDM_EINVAL), (dict(idx_bytes=2), 0, _lib.SDM_EINVAL),
+    (dict(val_bytes=8), 0, _lib.SDM_EINVAL), (dict(gr_rows=100), 0, _lib.SDM_EINVAL),
+    (dict(spay_q=None), 0, _lib.SDM_EINVAL), (dict(gr=FAKE + 8), 0, _lib.SDM_EALIGN),
+    (dict(bank=FAKE + 4), 0, _lib.SDM_EALIGN), (dict(grad=FAKE + 8), 0, _lib.SDM_EALIGN),
+    (dict(q_w=FAKE + 2), 0, _lib.SDM_EALIGN), (dict(valid_last=129), 0, _lib.SDM_EINVAL),
+])
+def test_gds_refusals(kw, ti, status):
+    lib = _lib.load()
+    assert lib.sdm_gds_step(ctypes.byref(gds_io(**kw)), ti, None) == status
+    assert len(lib.sdm_last_error()) > 0
+    assert lib.sdm_gds_step(None, 0, None) == _lib.SDM_EINVAL
