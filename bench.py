@@ -175,6 +175,7 @@ def main():
                     help="untimed steps for about S seconds before the warmup steps (clocks settle)")
     ap.add_argument("--pair-stream", action="store_true",
                     help="run the pair kernel on a second stream beside the DW steps (slower on uniform_bf16)")
+    ap.add_argument("--no-gds", action="store_true", help="skip the GDS (backward of the read gather) measurement")
     ap.add_argument("--no-read-side", action="store_true",
                     help="skip the separate measurement of the read side (gather + substitution) and the forward loop")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -336,6 +337,8 @@ def main():
     }
     if not args.no_read_side:
         res["read_side"] = measure_read_side(args, wl, shape, out, ins, bank, plan, stream, W, sdm, torch)
+    if not args.no_gds:
+        res["gds"] = measure_gds(wl, shape, out, ins, bank, stream, sdm, torch)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on host cores)...")
         res["cpu_baseline"] = cpu_baseline(wl, bank0)
@@ -389,6 +392,45 @@ def measure_read_side(args, wl, shape, out, ins, bank, dw_plan, stream, W, sdm, 
         "forward_loop_ms": wall * 1e3,
         "forward_loop": "every step: read side (2 kernels) then DW; %d steps, eager" % wl.steps,
     }
+
+
+def gds_bytes(P, C, R, hd, bank_es, groups_q, grad_es):
+    """Algorithmic bytes of one GDS step: the dots read per read its id (8 with the q_w/element
+    words counted in the scatter), its bank row, and write its dot, and read each gradient row once;
+    the scatter reads per Q-row position its element, id and q_w and a gradient row, and reads and
+    writes each group's grad row once."""
+    dots = P * C * R * (hd * bank_es + 8 + 4) + P * C * hd * 4
+    scatter = P * C * R * (4 + 8) + P * C * R * hd * 4 + 2 * groups_q * hd * grad_es
+    return dots + scatter
+
+
+def measure_gds(wl, shape, out, ins, bank, stream, sdm, torch):
+    """GDS of every step (dots + scatter kernels), timed by events on the launch stream around each
+    call; gradient rows seeded. Not part of the headline step."""
+    sh = wl.shape
+    P, C, R, hd = sh.P, sh.C, sh.R, sh.hd
+    dev = bank.device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.bank_seed + 23)
+    gr = torch.randn((wl.steps * P * C, hd), generator=gen, device=dev)
+    d = torch.zeros((wl.N, C, R), device=dev)
+    grad = torch.zeros_like(bank)
+    sp = out["spay_q"]
+    heads = ((sp & W_FIRST) != 0) & ((sp & W_INVALID) == 0)
+    groups_q = float(heads.view(wl.steps, P * C * R).sum(dim=1).float().mean())
+    for ti in range(min(2, wl.steps)):
+        sdm.gds_step(bank, out, ins["q_idx"], gr, shape, ti, step_rows=P * C, d_q_w=d, grad=grad, stream=stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(wl.steps)]
+    for ti in range(wl.steps):
+        ev[ti][0].record(stream)
+        sdm.gds_step(bank, out, ins["q_idx"], gr, shape, ti, step_rows=P * C, d_q_w=d, grad=grad, stream=stream)
+        ev[ti][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    b = gds_bytes(P, C, R, hd, 2 if sh.bank_dtype == "bf16" else 4, groups_q, 2 if sh.bank_dtype == "bf16" else 4)
+    return {"bytes_per_step": b, "ms_per_step": ms, "GBps": b / (ms * 1e-3) / 1e9, "frac": b / (ms * 1e-3) / HBM_PEAK_BYTES,
+            "note": "dots + scatter kernels per step, events around the call; grad in the bank dtype"}
 
 
 W_FIRST = -(1 << 31)      # bit 31 of the int32 record element
