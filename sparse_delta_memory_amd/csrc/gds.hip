@@ -2,12 +2,14 @@
 // chunks of one step (page "sparse_delta_memory/cuda/mover_da2_cuda.py": the GDS part of the module
 // docstring and the comment of its scatter role).
 //
-// gds_dots_kernel: d_q_w[t, r] = <gr[t], M0[q_idx[t, r]]>, token order, one wave per token: each
-// lane takes 4 columns of every 256, and a wave reduction gives each dot (no atomics).
+// gds_dots_kernel: d_q_w[t, r] = <gr[t], M0[q_idx[t, r]]>, token order, one wave per token: the
+// token's ids are loaded one per lane, then 4 reads' rows at a time; each lane takes 4 columns of
+// every 256 and a wave reduction gives each dot (no atomics).
 // gds_scatter_kernel: the gradient rows in sorted order, one wave per position of the Q-only rows:
-// at a valid group FIRST the wave walks the group's members in sorted order, acc = fma(q_w, gr[t],
-// acc) from +0, and at LAST adds acc to grad[slot] with one read-modify-write (the wave is that
-// row's only writer in the launch, so the result is deterministic).
+// at a valid group FIRST the wave walks the group's members in sorted order (64 records and
+// weights at a time, 8 gradient rows in flight), acc = fma(q_w, gr[t], acc) from +0, and at LAST
+// adds acc to grad[slot] with one read-modify-write (the wave is that row's only writer in the
+// launch, so the result is deterministic).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -54,6 +56,16 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// A 64-bit value of another lane.
+__device__ __forceinline__ int64_t shfl64(int64_t v, int src) {
+    const int lo = __shfl(static_cast<int>(static_cast<uint64_t>(v) & 0xFFFFFFFFull), src, kWave);
+    const int hi = __shfl(static_cast<int>(static_cast<uint64_t>(v) >> 32), src, kWave);
+    return static_cast<int64_t>(static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32 | static_cast<uint32_t>(lo));
+}
+
+constexpr int kDotReads = 4;   // reads whose rows are in flight together
+constexpr int kWalkRows = 8;   // member gradient rows in flight together
+
 __global__ void __launch_bounds__(kGdsThreads) gds_dots_kernel(GdsArgs a) {
     const int wv = static_cast<int>(threadIdx.x) / kWave;
     const int lane = static_cast<int>(lane_id());
@@ -68,18 +80,34 @@ __global__ void __launch_bounds__(kGdsThreads) gds_dots_kernel(GdsArgs a) {
         return;
     }
     const int64_t grow = a.row0 + static_cast<int64_t>(p) * a.C + t;
-    for (int r = 0; r < a.R; ++r) {
-        const int64_t s = gds_id(a, eo + r);
-        float acc = 0.0f;
-        if (s >= 0 && s < a.rows) {   // (a slot outside the bank contributes nothing)
+    for (int rb = 0; rb < a.R; rb += kWave) {   // the token's ids, one per lane, then kDotReads rows at a time
+        const int nr = min(kWave, a.R - rb);
+        const int64_t my_id = lane < nr ? gds_id(a, eo + rb + lane) : -1;
+        for (int r0 = 0; r0 < nr; r0 += kDotReads) {
+            int64_t s[kDotReads];
+            bool ok[kDotReads];
+#pragma unroll
+            for (int u = 0; u < kDotReads; ++u) {
+                s[u] = shfl64(my_id, min(r0 + u, nr - 1));
+                ok[u] = r0 + u < nr && s[u] >= 0 && s[u] < a.rows;   // (a slot outside the bank contributes nothing)
+            }
+            float acc[kDotReads] = {};
             for (int col = 4 * lane; col < a.hd; col += 4 * kWave) {
                 const float4 g = load4(a.gr, 0, grow, a.hd, col);
-                const float4 m = load4(a.bank, a.bank_bf16, s, a.hd, col);
-                acc = fmaf(g.w, m.w, fmaf(g.z, m.z, fmaf(g.y, m.y, fmaf(g.x, m.x, acc))));
+                float4 m[kDotReads];
+#pragma unroll
+                for (int u = 0; u < kDotReads; ++u) m[u] = load4(a.bank, a.bank_bf16, ok[u] ? s[u] : 0, a.hd, col);
+#pragma unroll
+                for (int u = 0; u < kDotReads; ++u) {
+                    if (ok[u]) acc[u] = fmaf(g.w, m[u].w, fmaf(g.z, m[u].z, fmaf(g.y, m[u].y, fmaf(g.x, m[u].x, acc[u]))));
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kDotReads; ++u) {
+                const float d = wave_sum(acc[u]);
+                if (lane == 0 && r0 + u < nr) a.d_q_w[eo + rb + r0 + u] = d;
             }
         }
-        acc = wave_sum(acc);
-        if (lane == 0) a.d_q_w[eo + r] = acc;
     }
 }
 
@@ -94,25 +122,49 @@ __global__ void __launch_bounds__(kGdsThreads) gds_scatter_kernel(GdsArgs a) {
     const uint32_t* row = a.spay_q + c * n;
     const uint32_t e0 = row[j];
     if (!(e0 & kFirst) || (e0 & kInvalid)) return;   // a valid group starts here
-    // The group's slot (every member reads it) and its bounds.
     const int64_t qbase = c * n;   // entry-order Q index of (t, lane) is t * R + lane
     auto entry = [&](uint32_t el) { return static_cast<int64_t>((el >> kTokShift) & 0xFFu) * a.R + (el & 0xFFu); };
-    const int64_t slot = gds_id(a, qbase + entry(e0));
+    const int64_t slot = gds_id(a, qbase + entry(e0));   // (every member reads it)
     if (slot < 0 || slot >= a.rows) return;
     const int64_t grow0 = a.row0 + static_cast<int64_t>(p) * a.C;
-    for (int col = 4 * lane; col < a.hd; col += 4 * kWave) {
+    for (int col0 = 0; col0 < a.hd; col0 += 4 * kWave) {
+        const int col = col0 + 4 * lane;
+        const bool con = col < a.hd;
         float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        for (int m = j; m < n; ++m) {   // the members in sorted order, up to LAST
-            const uint32_t el = row[m];
-            const int64_t ei = entry(el);
-            const float w = load_val(a.q_w, qbase + ei, a.vbf);
-            const float4 g = load4(a.gr, 0, grow0 + ((el >> kTokShift) & 0xFFu), a.hd, col);
-            acc.x = fmaf(w, g.x, acc.x);
-            acc.y = fmaf(w, g.y, acc.y);
-            acc.z = fmaf(w, g.z, acc.z);
-            acc.w = fmaf(w, g.w, acc.w);
-            if (el & kLast) break;
+        bool done = false;
+        // The members in sorted order, 64 records at a time (lane l: member m0 + l), their gradient
+        // rows kWalkRows at a time; the sum runs over the members in order from +0.
+        for (int m0 = j; !done && m0 < n; m0 += kWave) {
+            const int m = m0 + lane;
+            const uint32_t el = m < n ? row[m] : (kFirst | kLast | kInvalid);
+            const int tk = static_cast<int>((el >> kTokShift) & 0xFFu);
+            const bool in = m < n && !(el & kInvalid);
+            const float w = in ? load_val(a.q_w, qbase + entry(el), a.vbf) : 0.0f;
+            const uint64_t lastm = __ballot((el & kLast) != 0u);
+            const int cnt = lastm != 0ull ? __builtin_ctzll(lastm) + 1 : kWave;   // (LAST included)
+            done = lastm != 0ull;
+            for (int k0 = 0; k0 < cnt; k0 += kWalkRows) {
+                float wk[kWalkRows];
+                float4 g[kWalkRows];
+#pragma unroll
+                for (int u = 0; u < kWalkRows; ++u) {
+                    const int kk = min(k0 + u, cnt - 1);
+                    wk[u] = __shfl(w, kk, kWave);
+                    const int t = __shfl(tk, kk, kWave);
+                    g[u] = con ? load4(a.gr, 0, grow0 + t, a.hd, col) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                }
+#pragma unroll
+                for (int u = 0; u < kWalkRows; ++u) {
+                    if (k0 + u < cnt) {
+                        acc.x = fmaf(wk[u], g[u].x, acc.x);
+                        acc.y = fmaf(wk[u], g[u].y, acc.y);
+                        acc.z = fmaf(wk[u], g[u].z, acc.z);
+                        acc.w = fmaf(wk[u], g[u].w, acc.w);
+                    }
+                }
+            }
         }
+        if (!con) continue;
         // One read-modify-write of the lane's columns (this wave is the row's only writer).
         if (a.grad_bf16) {
             uint2* gp = reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.grad) + slot * a.hd + col);
