@@ -1,4 +1,4 @@
-"""Plain float64 oracle of GDS, the backward of the read gather (TEST INFRASTRUCTURE ONLY).
+"""Plain float64 oracles of the backward gathers GDS and GWR (TEST INFRASTRUCTURE ONLY).
 
 Only the tests use this module; the product path never imports it, and it shares no code with
 the HIP implementation.
@@ -45,3 +45,31 @@ def gds_chunk(q_idx, q_w, gr, m0_rows, t_valid):
             add[i] += w[t, r] * g[t]
             mag[i] += np.abs(w[t, r] * g[t])
     return dots, slots, add, mag
+
+
+def gwr_chunk(k_idx, w, dv, grad_rows, t_valid):
+    """GWR of one chunk (page "sparse_delta_memory/cuda/pa_dc_cuda.py", module docstring: the GWR
+    gather of the deterministic backward): with the DW step's write weights w[t, n] (k exp(rex) of
+    the entry) and token rows dv[t],
+
+      d_dv[t]     = sum_n w[t, n] grad[k_idx[t, n]]      (entries in order)
+      d_k_pd[t,n] = <dv[t], grad[k_idx[t, n]]>
+
+    k_idx [C, W] absolute slots; w [C, W]; dv [C, hd]; grad_rows(slots) -> rows of the gradient;
+    tokens at or past t_valid give zeros. Returns float64 d_dv [C, hd], d_k_pd [C, W] and the
+    magnitudes mag_dv (sum |w grad|) and mag_pd (sum |dv grad|)."""
+    ki = np.asarray(k_idx, np.int64)
+    ww = np.asarray(w, np.float64)
+    v = np.asarray(dv, np.float64)
+    C, W = ki.shape
+    hd = v.shape[1]
+    d_dv, mag_dv = np.zeros((C, hd)), np.zeros((C, hd))
+    d_pd, mag_pd = np.zeros((C, W)), np.zeros((C, W))
+    for t in range(t_valid):
+        rows = grad_rows(ki[t])
+        for n in range(W):
+            d_dv[t] += ww[t, n] * rows[n]
+            mag_dv[t] += np.abs(ww[t, n] * rows[n])
+            d_pd[t, n] = float(np.dot(v[t], rows[n]))
+            mag_pd[t, n] = float(np.dot(np.abs(v[t]), np.abs(rows[n])))
+    return d_dv, d_pd, mag_dv, mag_pd

@@ -39,3 +39,29 @@ def test_gds_is_the_gradient_of_the_read_gather(seed, S, C, R, tv):
     np.testing.assert_allclose(dots, want_dots, rtol=1e-12, atol=1e-12)
     assert np.all(mag >= np.abs(add) - 1e-12)
     assert np.all(dots[tv:] == 0)
+
+
+@pytest.mark.parametrize("seed,S,C,W,tv", [(81, 5, 12, 3, 12), (82, 40, 16, 4, 9), (83, 2, 8, 5, 0)])
+def test_gwr_is_the_gradient_of_the_dw_writes(seed, S, C, W, tv):
+    """GWR against autograd: the DW step's write terms new[s] += w[t, n] dv[t] (s = k_idx[t, n]),
+    contracted with a gradient G of the new rows; the gradients with respect to dv and w are d_dv
+    and d_k_pd."""
+    rng = np.random.default_rng(seed)
+    hd = 5
+    k_idx = rng.integers(0, S, (C, W))
+    w = rng.standard_normal((C, W))
+    dv = rng.standard_normal((C, hd))
+    G = rng.standard_normal((S, hd))
+    d_dv, d_pd, mag_dv, mag_pd = gds.gwr_chunk(k_idx, w, dv, lambda s: G[s], tv)
+    V = torch.tensor(dv, dtype=torch.float64, requires_grad=True)
+    Wt = torch.tensor(w, dtype=torch.float64, requires_grad=True)
+    new = torch.zeros((S, hd), dtype=torch.float64)
+    idx = torch.tensor(k_idx[:tv].reshape(-1), dtype=torch.long)
+    terms = (Wt[:tv].unsqueeze(-1) * V[:tv].unsqueeze(1)).reshape(-1, hd)
+    new = new.index_add(0, idx, terms)
+    (new * torch.tensor(G)).sum().backward()
+    want_dv = V.grad.numpy() if V.grad is not None else np.zeros_like(dv)
+    want_w = Wt.grad.numpy() if Wt.grad is not None else np.zeros_like(w)
+    np.testing.assert_allclose(d_dv, want_dv, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(d_pd, want_w, rtol=1e-12, atol=1e-12)
+    assert np.all(mag_dv >= np.abs(d_dv) - 1e-12) and np.all(mag_pd >= np.abs(d_pd) - 1e-12)
