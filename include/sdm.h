@@ -328,6 +328,37 @@ typedef struct sdm_gds_io {
  */
 sdm_status sdm_gds_step(const sdm_gds_io* io, int64_t ti, hipStream_t st);
 
+/* GWR of one step: the backward of DW's write terms for the tokens of chunks ti*P .. ti*P + P - 1. */
+typedef struct sdm_gwr_io {
+    const void* grad;       /* [rows, hd] SDM_F32 or SDM_BF16 gradient of the bank rows DW wrote (read only) */
+    int32_t grad_dtype;     /* sdm_dtype */
+    int64_t rows;           /* grad rows (an id outside 0..rows-1 contributes nothing) */
+    int32_t hd;             /* row width, a multiple of 4, 4..1024 */
+    const void* k_idx;      /* [N, C, W] absolute slot ids of the writes, int32 or int64 */
+    const float* w;         /* [N, C, W] write weights (the DW scale k exp(rex) of each entry) */
+    const float* dv;        /* token rows of the step: row (ti * step_rows + p * C + t) of [*, hd], float32 */
+    int64_t step_rows;      /* rows between steps in dv and d_dv (P*C, or 0 for one-step buffers) */
+    int64_t dv_rows;        /* rows in dv and d_dv: ti * step_rows + P * C <= dv_rows */
+    float* d_dv;            /* OUT (NULL: skipped): rows in dv's layout, 0 for masked tokens */
+    float* d_k_pd;          /* OUT (NULL: skipped) [N, C, W]: the chunks of step ti, 0 for masked tokens */
+    int32_t P, C, W, N;     /* the Phase-1 shape */
+    int32_t first_partial;  /* as in sdm_p1_shape */
+    int32_t valid_last;
+    int32_t idx_bytes;      /* width of k_idx: 0 or 4 = int32, 8 = int64 */
+} sdm_gwr_io;
+
+/*
+ * GWR (page "sparse_delta_memory/cuda/pa_dc_cuda.py", module docstring: the GWR gather of the
+ * deterministic backward step):
+ *   d_dv[t]      = sum_n w[t, n] grad[k_idx[t, n]]     (the token's entries in order, from +0),
+ *   d_k_pd[t, n] = <dv[t], grad[k_idx[t, n]]>.
+ * Masked tokens get zeros and none of their inputs is read. One kernel on st; no atomics, so the
+ * results are reproducible. Requires (ti + 1) * P <= N, hd a multiple of 4 up to 1024, 16-byte
+ * aligned dv and d_dv, grad rows 16-byte aligned (8 for bf16), 4-byte aligned w, d_k_pd and ids
+ * (8 for int64).
+ */
+sdm_status sdm_gwr_step(const sdm_gwr_io* io, int64_t ti, hipStream_t st);
+
 /* Static text for a status code. */
 const char* sdm_status_string(sdm_status s);
 

@@ -18,7 +18,7 @@ from . import _lib
 from ._lib import P1IO, P1Shape, SdmError  # noqa: F401
 
 __all__ = ["P1Shape", "phase1", "phase1_workspace_bytes", "alloc_phase1_outputs", "dw_step", "dw_workspace_bytes",
-           "alloc_dw_workspace", "DwPlan", "ReadPlan", "read_step", "gds_step", "SdmError", "make_shape",
+           "alloc_dw_workspace", "DwPlan", "ReadPlan", "read_step", "gds_step", "gwr_step", "SdmError", "make_shape",
            "timing_events"]
 
 
@@ -315,3 +315,37 @@ def gds_step(bank, p1, q_idx, gr, shape: P1Shape, ti: int, step_rows: int, d_q_w
     io.val_bytes = p1["q_w"].element_size()
     st = torch.cuda.current_stream(bank.device) if stream is None else stream
     _lib.check(lib.sdm_gds_step(ctypes.byref(io), int(ti), ctypes.c_void_p(st.cuda_stream)))
+
+
+def gwr_step(grad, k_idx, w, dv, shape: P1Shape, ti: int, step_rows: int, d_dv=None, d_k_pd=None, stream=None):
+    """GWR of step `ti` (the backward of DW's write terms) on the current (or given) stream.
+
+    grad [rows, hd] float32 or bfloat16 gradient of the bank rows DW wrote; k_idx the Phase-1 write
+    ids; w [N, C, W] float32 write weights (k exp(rex) per entry); dv [*, hd] float32 token rows, row
+    ti*step_rows + p*C + t. d_dv (same layout as dv) and d_k_pd [N, C, W] (both float32, optional)
+    receive the results."""
+    import torch
+
+    for name, t in (("w", w), ("dv", dv), ("d_dv", d_dv), ("d_k_pd", d_k_pd)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("gwr_step: %s must be float32" % name)
+    if grad.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("gwr_step: grad must be float32 or bfloat16")
+    if d_dv is not None and d_dv.shape[0] != dv.shape[0]:
+        raise TypeError("gwr_step: d_dv must have dv's rows")
+    lib = _lib.load()
+    io = _lib.GwrIO()
+    io.grad = grad.data_ptr()
+    io.grad_dtype = _lib.SDM_BF16 if grad.dtype == torch.bfloat16 else _lib.SDM_F32
+    io.rows, io.hd = grad.shape[0], grad.shape[1]
+    io.k_idx = k_idx.data_ptr()
+    io.w = w.data_ptr()
+    io.dv = dv.data_ptr()
+    io.step_rows, io.dv_rows = int(step_rows), dv.shape[0]
+    io.d_dv = _ptr(d_dv)
+    io.d_k_pd = _ptr(d_k_pd)
+    io.P, io.C, io.W, io.N = shape.P, shape.C, shape.W, shape.N
+    io.first_partial, io.valid_last = shape.first_partial, shape.valid_last
+    io.idx_bytes = k_idx.element_size()
+    st = torch.cuda.current_stream(grad.device) if stream is None else stream
+    _lib.check(lib.sdm_gwr_step(ctypes.byref(io), int(ti), ctypes.c_void_p(st.cuda_stream)))

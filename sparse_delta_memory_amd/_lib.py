@@ -81,8 +81,18 @@ class GdsIO(ctypes.Structure):
     ]
 
 
+class GwrIO(ctypes.Structure):
+    _fields_ = [
+        ("grad", ctypes.c_void_p), ("grad_dtype", ctypes.c_int32), ("rows", ctypes.c_int64), ("hd", ctypes.c_int32),
+        ("k_idx", ctypes.c_void_p), ("w", ctypes.c_void_p), ("dv", ctypes.c_void_p), ("step_rows", ctypes.c_int64),
+        ("dv_rows", ctypes.c_int64), ("d_dv", ctypes.c_void_p), ("d_k_pd", ctypes.c_void_p),
+        ("P", ctypes.c_int32), ("C", ctypes.c_int32), ("W", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("first_partial", ctypes.c_int32), ("valid_last", ctypes.c_int32), ("idx_bytes", ctypes.c_int32),
+    ]
+
+
 EXPORTS = ["sdm_phase1_workspace", "sdm_phase1", "sdm_dw_workspace", "sdm_dw_step", "sdm_read_step",
-           "sdm_gds_step", "sdm_status_string", "sdm_last_error"]
+           "sdm_gds_step", "sdm_gwr_step", "sdm_status_string", "sdm_last_error"]
 
 _lock = threading.Lock()
 _lib = None
@@ -115,6 +125,8 @@ def load() -> ctypes.CDLL:
         lib.sdm_read_step.restype = ctypes.c_int
         lib.sdm_gds_step.argtypes = [ctypes.POINTER(GdsIO), ctypes.c_int64, ctypes.c_void_p]
         lib.sdm_gds_step.restype = ctypes.c_int
+        lib.sdm_gwr_step.argtypes = [ctypes.POINTER(GwrIO), ctypes.c_int64, ctypes.c_void_p]
+        lib.sdm_gwr_step.restype = ctypes.c_int
         lib.sdm_status_string.argtypes = [ctypes.c_int]
         lib.sdm_status_string.restype = ctypes.c_char_p
         lib.sdm_last_error.argtypes = []

@@ -235,6 +235,37 @@ sdm_status sdm_gds_step(const sdm_gds_io* io, int64_t ti, hipStream_t st) {
     return SDM_OK;
 }
 
+sdm_status sdm_gwr_step(const sdm_gwr_io* io, int64_t ti, hipStream_t st) {
+    g_last_error.clear();
+    if (io == nullptr) return fail(SDM_EINVAL, "sdm_gwr_step: io is NULL");
+    if (io->C < 1 || io->C > 256 || io->W < 1 || io->W > 256)
+        return fail(SDM_ESHAPE, "sdm_gwr_step: C = %d, W = %d outside 1..256", io->C, io->W);
+    if (io->P < 1 || io->N < 0) return fail(SDM_ESHAPE, "sdm_gwr_step: P = %d, N = %d", io->P, io->N);
+    if (ti < 0 || (ti + 1) * static_cast<int64_t>(io->P) > io->N)
+        return fail(SDM_ESHAPE, "sdm_gwr_step: step %lld needs (ti+1)*P <= N = %d", static_cast<long long>(ti), io->N);
+    if (io->first_partial < 0 || io->first_partial > io->N || io->valid_last < 0 || io->valid_last > io->C)
+        return fail(SDM_EINVAL, "sdm_gwr_step: first_partial = %d, valid_last = %d", io->first_partial, io->valid_last);
+    if (io->grad_dtype != SDM_F32 && io->grad_dtype != SDM_BF16)
+        return fail(SDM_EINVAL, "sdm_gwr_step: grad_dtype %d", io->grad_dtype);
+    if (io->idx_bytes != 0 && io->idx_bytes != 4 && io->idx_bytes != 8)
+        return fail(SDM_EINVAL, "sdm_gwr_step: idx_bytes = %d (0 or 4: int32 ids; 8: int64 ids)", io->idx_bytes);
+    if (io->hd < 4 || io->hd > 1024 || io->hd % 4 != 0)
+        return fail(SDM_ESHAPE, "sdm_gwr_step: hd = %d (a multiple of 4 in 4..1024)", io->hd);
+    if (io->rows < 0 || io->step_rows < 0 || io->dv_rows < 0) return fail(SDM_EINVAL, "sdm_gwr_step: rows / step_rows / dv_rows");
+    if (ti * io->step_rows + static_cast<int64_t>(io->P) * io->C > io->dv_rows)
+        return fail(SDM_EINVAL, "sdm_gwr_step: dv holds %lld rows, step %lld needs %lld", static_cast<long long>(io->dv_rows),
+                    static_cast<long long>(ti), static_cast<long long>(ti * io->step_rows + static_cast<int64_t>(io->P) * io->C));
+    if (io->grad == nullptr || io->k_idx == nullptr || io->w == nullptr || io->dv == nullptr)
+        return fail(SDM_EINVAL, "sdm_gwr_step: grad, k_idx, w and dv are required");
+    if (!aligned(io->grad, io->grad_dtype == SDM_BF16 ? 8 : 16) || !aligned(io->dv, 16) || !aligned(io->d_dv, 16))
+        return fail(SDM_EALIGN, "sdm_gwr_step: grad, dv and d_dv rows must be 16-byte aligned (8 for bf16 grad)");
+    if (!aligned(io->k_idx, io->idx_bytes == 8 ? 8 : 4) || !aligned(io->w, 4) || !aligned(io->d_k_pd, 4))
+        return fail(SDM_EALIGN, "sdm_gwr_step: k_idx, w or d_k_pd misaligned");
+    const hipError_t e = sdm::gwr_launch(io, ti, st);
+    if (e != hipSuccess) return fail(SDM_EHIP, "sdm_gwr_step: %s", hipGetErrorString(e));
+    return SDM_OK;
+}
+
 sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st) {
     g_last_error.clear();
     if (io == nullptr) return fail(SDM_EINVAL, "sdm_dw_step: io is NULL");

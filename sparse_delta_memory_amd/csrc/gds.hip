@@ -1,5 +1,5 @@
-// GDS on gfx950: the backward of the read gather q0[t] = sum_r q_w[t, r] M0[q_idx[t, r]] for the
-// chunks of one step (page "sparse_delta_memory/cuda/mover_da2_cuda.py": the GDS part of the module
+// The backward gathers on gfx950. GDS: the backward of the read gather q0[t] = sum_r q_w[t, r]
+// M0[q_idx[t, r]] for the chunks of one step (page "sparse_delta_memory/cuda/mover_da2_cuda.py": the GDS part of the module
 // docstring and the comment of its scatter role).
 //
 // gds_dots_kernel: d_q_w[t, r] = <gr[t], M0[q_idx[t, r]]>, token order, one wave per token: the
@@ -180,6 +180,105 @@ __global__ void __launch_bounds__(kGdsThreads) gds_scatter_kernel(GdsArgs a) {
     }
 }
 
+// GWR (page "sparse_delta_memory/cuda/pa_dc_cuda.py", module docstring: the GWR gather of the
+// deterministic backward) for the tokens of one step: d_dv[t] = sum_n w[t, n] grad[k_idx[t, n]]
+// (entries in order, fma chain from +0) and d_k_pd[t, n] = <dv[t], grad[k_idx[t, n]]>. One wave
+// per token: each lane holds 4 columns of every 256 (hd <= 1024) of dv[t] and of the d_dv sum; the
+// token's ids and weights are loaded one per lane, then the gradient rows of 4 entries at a time.
+struct GwrArgs {
+    const void* grad;
+    const void* k_idx;
+    const float* w;
+    const float* dv;
+    float* d_dv;
+    float* d_k_pd;
+    int64_t rows, chunk0, row0;
+    int P, C, W, hd, first_partial, valid_last, id64, grad_bf16;
+};
+
+constexpr int kGwrColBlocks = 4;   // 256-column blocks per row (hd <= 1024)
+
+__global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
+    const int wv = static_cast<int>(threadIdx.x) / kWave;
+    const int lane = static_cast<int>(lane_id());
+    const int64_t tok = static_cast<int64_t>(blockIdx.x) * kGdsWaves + wv;
+    if (tok >= static_cast<int64_t>(a.P) * a.C) return;
+    const int p = static_cast<int>(tok / a.C), t = static_cast<int>(tok % a.C);
+    const int64_t c = a.chunk0 + p;
+    const int tv = c >= a.first_partial ? a.valid_last : a.C;
+    const int64_t eo = (c * a.C + t) * a.W;
+    const int64_t vrow = a.row0 + static_cast<int64_t>(p) * a.C + t;
+    if (t >= tv) {   // masked: zeros, nothing read
+        if (a.d_k_pd != nullptr) {
+            for (int n = lane; n < a.W; n += kWave) a.d_k_pd[eo + n] = 0.0f;
+        }
+        if (a.d_dv != nullptr) {
+            for (int col = 4 * lane; col < a.hd; col += 4 * kWave)
+                *reinterpret_cast<float4*>(a.d_dv + vrow * a.hd + col) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+        return;
+    }
+    float4 v[kGwrColBlocks], acc[kGwrColBlocks];
+#pragma unroll
+    for (int cb = 0; cb < kGwrColBlocks; ++cb) {
+        const int col = cb * 4 * kWave + 4 * lane;
+        v[cb] = col < a.hd ? *reinterpret_cast<const float4*>(a.dv + vrow * a.hd + col) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        acc[cb] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+    for (int nb = 0; nb < a.W; nb += kWave) {
+        const int nr = min(kWave, a.W - nb);
+        const int64_t my_id = lane < nr ? (a.id64 ? static_cast<const int64_t*>(a.k_idx)[eo + nb + lane]
+                                                  : static_cast<const int32_t*>(a.k_idx)[eo + nb + lane])
+                                        : -1;
+        const float my_w = lane < nr ? a.w[eo + nb + lane] : 0.0f;
+        for (int n0 = 0; n0 < nr; n0 += kDotReads) {
+            int64_t s[kDotReads];
+            bool ok[kDotReads];
+            float wu[kDotReads], part[kDotReads];
+#pragma unroll
+            for (int u = 0; u < kDotReads; ++u) {
+                const int src = min(n0 + u, nr - 1);
+                s[u] = shfl64(my_id, src);
+                wu[u] = __shfl(my_w, src, kWave);
+                ok[u] = n0 + u < nr && s[u] >= 0 && s[u] < a.rows;   // (a slot outside the bank contributes nothing)
+                part[u] = 0.0f;
+            }
+#pragma unroll
+            for (int cb = 0; cb < kGwrColBlocks; ++cb) {
+                const int col = cb * 4 * kWave + 4 * lane;
+                if (col >= a.hd) break;
+                float4 g[kDotReads];
+#pragma unroll
+                for (int u = 0; u < kDotReads; ++u) g[u] = load4(a.grad, a.grad_bf16, ok[u] ? s[u] : 0, a.hd, col);
+#pragma unroll
+                for (int u = 0; u < kDotReads; ++u) {
+                    if (ok[u]) {
+                        acc[cb].x = fmaf(wu[u], g[u].x, acc[cb].x);
+                        acc[cb].y = fmaf(wu[u], g[u].y, acc[cb].y);
+                        acc[cb].z = fmaf(wu[u], g[u].z, acc[cb].z);
+                        acc[cb].w = fmaf(wu[u], g[u].w, acc[cb].w);
+                        part[u] = fmaf(v[cb].w, g[u].w, fmaf(v[cb].z, g[u].z, fmaf(v[cb].y, g[u].y, fmaf(v[cb].x, g[u].x, part[u]))));
+                    }
+                }
+            }
+            if (a.d_k_pd != nullptr) {
+#pragma unroll
+                for (int u = 0; u < kDotReads; ++u) {
+                    const float d = wave_sum(part[u]);
+                    if (lane == 0 && n0 + u < nr) a.d_k_pd[eo + nb + n0 + u] = d;
+                }
+            }
+        }
+    }
+    if (a.d_dv != nullptr) {
+#pragma unroll
+        for (int cb = 0; cb < kGwrColBlocks; ++cb) {
+            const int col = cb * 4 * kWave + 4 * lane;
+            if (col < a.hd) *reinterpret_cast<float4*>(a.d_dv + vrow * a.hd + col) = acc[cb];
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t gds_launch(const sdm_gds_io* io, int64_t ti, hipStream_t st) {
@@ -218,6 +317,31 @@ hipError_t gds_launch(const sdm_gds_io* io, int64_t ti, hipStream_t st) {
                             dim3(static_cast<unsigned>((poss + kGdsWaves - 1) / kGdsWaves)), dim3(kGdsThreads), kargs, 0, st);
     }
     return e;
+}
+
+hipError_t gwr_launch(const sdm_gwr_io* io, int64_t ti, hipStream_t st) {
+    GwrArgs a;
+    a.grad = io->grad;
+    a.k_idx = io->k_idx;
+    a.w = io->w;
+    a.dv = io->dv;
+    a.d_dv = io->d_dv;
+    a.d_k_pd = io->d_k_pd;
+    a.rows = io->rows;
+    a.chunk0 = ti * io->P;
+    a.row0 = ti * io->step_rows;
+    a.P = io->P;
+    a.C = io->C;
+    a.W = io->W;
+    a.hd = io->hd;
+    a.first_partial = io->first_partial;
+    a.valid_last = io->valid_last;
+    a.id64 = io->idx_bytes == 8;
+    a.grad_bf16 = io->grad_dtype == SDM_BF16;
+    const int64_t toks = static_cast<int64_t>(io->P) * io->C;
+    void* kargs[] = {&a};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&gwr_kernel),
+                           dim3(static_cast<unsigned>((toks + kGdsWaves - 1) / kGdsWaves)), dim3(kGdsThreads), kargs, 0, st);
 }
 
 }  // namespace sdm

@@ -68,4 +68,7 @@ hipError_t read_launch(const ReadLaunch& L, hipStream_t st);
 // GDS of step ti (validated by sdm_gds_step).
 hipError_t gds_launch(const sdm_gds_io* io, int64_t ti, hipStream_t st);
 
+// GWR of step ti (validated by sdm_gwr_step).
+hipError_t gwr_launch(const sdm_gwr_io* io, int64_t ti, hipStream_t st);
+
 }  // namespace sdm

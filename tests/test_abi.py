@@ -211,3 +211,28 @@ def test_gds_refusals(kw, ti, status):
     assert lib.sdm_gds_step(ctypes.byref(gds_io(**kw)), ti, None) == status
     assert len(lib.sdm_last_error()) > 0
     assert lib.sdm_gds_step(None, 0, None) == _lib.SDM_EINVAL
+
+
+def gwr_io(**kw):
+    o = _lib.GwrIO()
+    d = dict(grad=FAKE, grad_dtype=_lib.SDM_BF16, rows=1 << 20, hd=128, k_idx=FAKE, w=FAKE, dv=FAKE, step_rows=512,
+             dv_rows=1 << 20, d_dv=FAKE, d_k_pd=FAKE, P=4, C=128, W=16, N=8, first_partial=8, valid_last=128,
+             idx_bytes=4)
+    d.update(kw)
+    for k, v in d.items():
+        setattr(o, k, v)
+    return o
+
+
+@pytest.mark.parametrize("kw,ti,status", [
+    (dict(), 2, _lib.SDM_ESHAPE), (dict(W=0), 0, _lib.SDM_ESHAPE), (dict(hd=1028), 0, _lib.SDM_ESHAPE),
+    (dict(hd=6), 0, _lib.SDM_ESHAPE), (dict(grad_dtype=3), 0, _lib.SDM_EINVAL), (dict(idx_bytes=5), 0, _lib.SDM_EINVAL),
+    (dict(dv_rows=100), 0, _lib.SDM_EINVAL), (dict(w=None), 0, _lib.SDM_EINVAL), (dict(dv=FAKE + 4), 0, _lib.SDM_EALIGN),
+    (dict(d_dv=FAKE + 8), 0, _lib.SDM_EALIGN), (dict(grad=FAKE + 4), 0, _lib.SDM_EALIGN),
+    (dict(d_k_pd=FAKE + 2), 0, _lib.SDM_EALIGN), (dict(first_partial=9), 0, _lib.SDM_EINVAL),
+])
+def test_gwr_refusals(kw, ti, status):
+    lib = _lib.load()
+    assert lib.sdm_gwr_step(ctypes.byref(gwr_io(**kw)), ti, None) == status
+    assert len(lib.sdm_last_error()) > 0
+    assert lib.sdm_gwr_step(None, 0, None) == _lib.SDM_EINVAL
