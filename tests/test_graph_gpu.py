@@ -202,3 +202,53 @@ def test_graph_forward_loop_with_read_side():
         torch.cuda.synchronize()
         for k in st_e:
             assert torch.equal(st_g[k].view(torch.uint8), st_e[k].view(torch.uint8)), (rep, k)
+
+
+def test_graph_backward_gathers():
+    """GDS and GWR of every step captured in one graph and replayed: every replay equals the eager
+    calls bit for bit (both write their outputs in full or by read-modify-write from a reset grad)."""
+    import numpy as np
+
+    wl = W.make(1, steps=3)
+    sh = wl.shape
+    P, C, hd = sh.P, sh.C, sh.hd
+    shape, out = H.run_phase1(wl)
+    ins = H.device_inputs(wl)
+    bank = W.make_bank(wl, "cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    gr = torch.randn((wl.steps * P * C, hd), generator=gen, device="cuda")
+    w = torch.randn((wl.N, C, sh.W), generator=gen, device="cuda")
+    dv = torch.from_numpy(wl.dv.reshape(-1, hd).astype(np.float32)).cuda()
+    g0 = (torch.randn(bank.shape, generator=gen, device="cuda") * 0.01).to(bank.dtype)
+
+    def make_state():
+        st = dict(d_q_w=torch.zeros((wl.N, C, sh.R), device="cuda"), grad=g0.clone(),
+                  d_dv=torch.zeros_like(dv), d_k_pd=torch.zeros((wl.N, C, sh.W), device="cuda"))
+
+        def run():
+            for ti in range(wl.steps):
+                sdm.gds_step(bank, out, ins["q_idx"], gr, shape, ti, step_rows=P * C, d_q_w=st["d_q_w"], grad=st["grad"])
+                sdm.gwr_step(st["grad"], ins["k_idx"], w, dv, shape, ti, step_rows=P * C, d_dv=st["d_dv"],
+                             d_k_pd=st["d_k_pd"])
+        return st, run
+
+    st_e, run_e = make_state()
+    run_e()
+    torch.cuda.synchronize()
+    st_g, run_g = make_state()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_g()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for k in ("d_q_w", "d_dv", "d_k_pd"):
+            st_g[k].fill_(float("nan"))
+        st_g["grad"].copy_(g0)
+        st_e["grad"].copy_(g0)   # eager work between replays
+        run_e()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in st_e:
+            assert torch.equal(st_g[k].view(torch.uint8), st_e[k].view(torch.uint8)), (rep, k)
