@@ -2,9 +2,9 @@
 // M0[q_idx[t, r]] for the chunks of one step (page "sparse_delta_memory/cuda/mover_da2_cuda.py": the GDS part of the module
 // docstring and the comment of its scatter role).
 //
-// gds_dots_kernel: d_q_w[t, r] = <gr[t], M0[q_idx[t, r]]>, token order, one wave per token: the
-// token's ids are loaded one per lane, then 4 reads' rows at a time; each lane takes 4 columns of
-// every 256 and a wave reduction gives each dot (no atomics).
+// gds_dots_kernel: d_q_w[t, r] = <gr[t], M0[q_idx[t, r]]>, token order, one wave per 4 reads of a
+// token (their ids one per lane, their rows in flight together); each lane takes 4 columns of every
+// 256 and a wave reduction gives each dot (no atomics).
 // gds_scatter_kernel: the gradient rows in sorted order, one wave per position of the Q-only rows:
 // at a valid group FIRST the wave walks the group's members in sorted order (64 records and
 // weights at a time, 8 gradient rows in flight), acc = fma(q_w, gr[t], acc) from +0, and at LAST
@@ -69,45 +69,44 @@ constexpr int kWalkRows = 8;   // member gradient rows in flight together
 __global__ void __launch_bounds__(kGdsThreads) gds_dots_kernel(GdsArgs a) {
     const int wv = static_cast<int>(threadIdx.x) / kWave;
     const int lane = static_cast<int>(lane_id());
-    const int64_t tok = static_cast<int64_t>(blockIdx.x) * kGdsWaves + wv;   // (p, t) of the step
-    if (tok >= static_cast<int64_t>(a.P) * a.C) return;
+    const int groups = (a.R + kDotReads - 1) / kDotReads;   // read groups per token
+    const int64_t item = static_cast<int64_t>(blockIdx.x) * kGdsWaves + wv;   // (p, t, read group) of the step
+    if (item >= static_cast<int64_t>(a.P) * a.C * groups) return;
+    const int64_t tok = item / groups;
+    const int r0 = static_cast<int>(item % groups) * kDotReads;
+    const int nr = min(kDotReads, a.R - r0);
     const int p = static_cast<int>(tok / a.C), t = static_cast<int>(tok % a.C);
     const int64_t c = a.chunk0 + p;
     const int tv = c >= a.first_partial ? a.valid_last : a.C;
-    const int64_t eo = (c * a.C + t) * a.R;   // the token's first Q entry
+    const int64_t eo = (c * a.C + t) * a.R + r0;   // the group's first Q entry
     if (t >= tv) {   // masked: no reads, dots 0
-        for (int r = lane; r < a.R; r += kWave) a.d_q_w[eo + r] = 0.0f;
+        if (lane < nr) a.d_q_w[eo + lane] = 0.0f;
         return;
     }
     const int64_t grow = a.row0 + static_cast<int64_t>(p) * a.C + t;
-    for (int rb = 0; rb < a.R; rb += kWave) {   // the token's ids, one per lane, then kDotReads rows at a time
-        const int nr = min(kWave, a.R - rb);
-        const int64_t my_id = lane < nr ? gds_id(a, eo + rb + lane) : -1;
-        for (int r0 = 0; r0 < nr; r0 += kDotReads) {
-            int64_t s[kDotReads];
-            bool ok[kDotReads];
+    const int64_t my_id = lane < nr ? gds_id(a, eo + lane) : -1;
+    int64_t s[kDotReads];
+    bool ok[kDotReads];
 #pragma unroll
-            for (int u = 0; u < kDotReads; ++u) {
-                s[u] = shfl64(my_id, min(r0 + u, nr - 1));
-                ok[u] = r0 + u < nr && s[u] >= 0 && s[u] < a.rows;   // (a slot outside the bank contributes nothing)
-            }
-            float acc[kDotReads] = {};
-            for (int col = 4 * lane; col < a.hd; col += 4 * kWave) {
-                const float4 g = load4(a.gr, 0, grow, a.hd, col);
-                float4 m[kDotReads];
+    for (int u = 0; u < kDotReads; ++u) {
+        s[u] = shfl64(my_id, min(u, nr - 1));
+        ok[u] = u < nr && s[u] >= 0 && s[u] < a.rows;   // (a slot outside the bank contributes nothing)
+    }
+    float acc[kDotReads] = {};
+    for (int col = 4 * lane; col < a.hd; col += 4 * kWave) {
+        const float4 g = load4(a.gr, 0, grow, a.hd, col);
+        float4 m[kDotReads];
 #pragma unroll
-                for (int u = 0; u < kDotReads; ++u) m[u] = load4(a.bank, a.bank_bf16, ok[u] ? s[u] : 0, a.hd, col);
+        for (int u = 0; u < kDotReads; ++u) m[u] = load4(a.bank, a.bank_bf16, ok[u] ? s[u] : 0, a.hd, col);
 #pragma unroll
-                for (int u = 0; u < kDotReads; ++u) {
-                    if (ok[u]) acc[u] = fmaf(g.w, m[u].w, fmaf(g.z, m[u].z, fmaf(g.y, m[u].y, fmaf(g.x, m[u].x, acc[u]))));
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < kDotReads; ++u) {
-                const float d = wave_sum(acc[u]);
-                if (lane == 0 && r0 + u < nr) a.d_q_w[eo + rb + r0 + u] = d;
-            }
+        for (int u = 0; u < kDotReads; ++u) {
+            if (ok[u]) acc[u] = fmaf(g.w, m[u].w, fmaf(g.z, m[u].z, fmaf(g.y, m[u].y, fmaf(g.x, m[u].x, acc[u]))));
         }
+    }
+#pragma unroll
+    for (int u = 0; u < kDotReads; ++u) {
+        const float d = wave_sum(acc[u]);
+        if (lane == 0 && u < nr) a.d_q_w[eo + u] = d;
     }
 }
 
@@ -305,11 +304,12 @@ hipError_t gds_launch(const sdm_gds_io* io, int64_t ti, hipStream_t st) {
     a.grad_bf16 = io->grad_dtype == SDM_BF16;
     const int64_t toks = static_cast<int64_t>(io->P) * io->C;
     const int64_t poss = toks * io->R;
+    const int64_t items = toks * ((io->R + kDotReads - 1) / kDotReads);   // (token, read group) waves
     void* kargs[] = {&a};
     hipError_t e = hipSuccess;
     if (io->d_q_w != nullptr) {
         e = hipLaunchKernel(reinterpret_cast<const void*>(&gds_dots_kernel),
-                            dim3(static_cast<unsigned>((toks + kGdsWaves - 1) / kGdsWaves)), dim3(kGdsThreads), kargs, 0, st);
+                            dim3(static_cast<unsigned>((items + kGdsWaves - 1) / kGdsWaves)), dim3(kGdsThreads), kargs, 0, st);
         if (e != hipSuccess) return e;
     }
     if (io->grad != nullptr) {
