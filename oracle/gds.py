@@ -1,4 +1,4 @@
-"""Plain float64 oracles of the backward gathers GDS and GWR (TEST INFRASTRUCTURE ONLY).
+"""Plain float64 oracles of the backward movers GDS, GWR and PA (TEST INFRASTRUCTURE ONLY).
 
 Only the tests use this module; the product path never imports it, and it shares no code with
 the HIP implementation.
@@ -73,3 +73,40 @@ def gwr_chunk(k_idx, w, dv, grad_rows, t_valid):
             d_pd[t, n] = float(np.dot(v[t], rows[n]))
             mag_pd[t, n] = float(np.dot(np.abs(v[t]), np.abs(rows[n])))
     return d_dv, d_pd, mag_dv, mag_pd
+
+
+def pa_chunk(k_idx, k_eff, beta, cpe_of_slot, d_dva, gdw_rows, snap_rows, t_valid):
+    """PA of one chunk (page "sparse_delta_memory/cuda/pa_dc_cuda.py", module docstring: Phase A of
+    the deterministic backward, the backward of DW): per write group (slot s, members m),
+
+      grad[s]         = gdw[s] cpe_s + sum_m sc_m d_dva[tok_m],   sc_m = -beta[tok_m] k_eff_m
+      bank[s]         = snap[s]                                    (restore)
+      grad_g_decay[e] = cpe_s <gdw[s], snap[s]>,   d_k_eff[e] = -beta[tok_e] <d_dva[tok_e], snap[s]>
+
+    with gdw the slot's gradient row before PA and snap its pre-write row. k_idx [C, W] absolute
+    slots, k_eff [C, W], beta [C]; cpe_of_slot(s) the group's cpe; d_dva [C, hd]; gdw_rows(slots)
+    and snap_rows(slots) -> rows. Returns (slots ascending, new grad rows, grad_g_decay [C, W],
+    d_k_eff [C, W], mag_grad (|gdw cpe| + sum |sc d_dva|), mag_dot [C, W] (sum |d_dva snap|))."""
+    ki = np.asarray(k_idx, np.int64)
+    ke = np.asarray(k_eff, np.float64)
+    b = np.asarray(beta, np.float64)
+    d = np.asarray(d_dva, np.float64)
+    C, W = ki.shape
+    slots = np.unique(ki[:t_valid].ravel()) if t_valid > 0 else np.zeros(0, np.int64)
+    gdw = gdw_rows(slots) if len(slots) else np.zeros((0, d.shape[1]))
+    snap = snap_rows(slots) if len(slots) else np.zeros((0, d.shape[1]))
+    where = {int(s): i for i, s in enumerate(slots)}
+    cpe = np.array([cpe_of_slot(int(s)) for s in slots], np.float64)
+    new = gdw * cpe[:, None]
+    mag = np.abs(new)
+    g_decay, d_keff, mag_dot = np.zeros((C, W)), np.zeros((C, W)), np.zeros((C, W))
+    for t in range(t_valid):
+        for n in range(W):
+            i = where[int(ki[t, n])]
+            sc = -b[t] * ke[t, n]
+            new[i] += sc * d[t]
+            mag[i] += np.abs(sc * d[t])
+            g_decay[t, n] = cpe[i] * float(np.dot(gdw[i], snap[i]))
+            d_keff[t, n] = -b[t] * float(np.dot(d[t], snap[i]))
+            mag_dot[t, n] = float(np.dot(np.abs(d[t]), np.abs(snap[i])))
+    return slots, new, g_decay, d_keff, mag, mag_dot

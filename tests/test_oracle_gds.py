@@ -65,3 +65,40 @@ def test_gwr_is_the_gradient_of_the_dw_writes(seed, S, C, W, tv):
     np.testing.assert_allclose(d_dv, want_dv, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(d_pd, want_w, rtol=1e-12, atol=1e-12)
     assert np.all(mag_dv >= np.abs(d_dv) - 1e-12) and np.all(mag_pd >= np.abs(d_pd) - 1e-12)
+
+
+@pytest.mark.parametrize("seed,S,C,W,tv", [(91, 5, 12, 3, 12), (92, 40, 16, 4, 9), (93, 2, 8, 5, 8)])
+def test_pa_is_the_gradient_of_dw_and_the_write_prediction(seed, S, C, W, tv):
+    """PA against autograd. With M0 the pre-write rows, G the gradient of the rows DW writes and
+    D the gradient of the token rows, L = sum_s <G[s], M0[s] exp(T_s)> + sum_t <D[t], -beta[t] p0[t]>,
+    p0[t] = sum_n k_eff[t, n] M0[k_idx[t, n]] (the token's prediction; dv = beta (v - p0 - ...)).
+    dL/dM0[s] is PA's grad row, dL/dT_s its grad_g_decay (each member of the group), dL/dk_eff its
+    d_k_eff; the gradient of the memory is taken only at slots the chunk writes."""
+    rng = np.random.default_rng(seed)
+    hd = 5
+    k_idx = rng.integers(0, S, (C, W))
+    k_eff = rng.standard_normal((C, W))
+    beta = rng.random(C)
+    m0 = rng.standard_normal((S, hd))
+    G = rng.standard_normal((S, hd))
+    D = rng.standard_normal((C, hd))
+    T = -rng.random(S)                       # the group's total gate (cpe = exp(T))
+    slots, new, g_decay, d_keff, mag, mag_dot = gds.pa_chunk(
+        k_idx, k_eff, beta, lambda s: float(np.exp(T[s])), D, lambda s: G[s], lambda s: m0[s], tv)
+    M = torch.tensor(m0, requires_grad=True)
+    Tt = torch.tensor(T, requires_grad=True)
+    Ke = torch.tensor(k_eff, requires_grad=True)
+    written = torch.zeros(S, dtype=torch.float64)
+    written[torch.tensor(slots, dtype=torch.long)] = 1.0
+    dw_term = (torch.tensor(G) * M * torch.exp(Tt).unsqueeze(-1) * written.unsqueeze(-1)).sum()
+    idx = torch.tensor(k_idx[:tv].reshape(-1), dtype=torch.long)
+    p0 = (Ke[:tv].unsqueeze(-1) * M.index_select(0, idx).reshape(tv, W, hd)).sum(dim=1)
+    pred_term = (torch.tensor(D[:tv]) * (-torch.tensor(beta[:tv]).unsqueeze(-1) * p0)).sum()
+    (dw_term + pred_term).backward()
+    np.testing.assert_allclose(new, M.grad.numpy()[slots], rtol=1e-12, atol=1e-12)
+    for t in range(tv):
+        for n in range(W):
+            assert abs(g_decay[t, n] - Tt.grad.numpy()[k_idx[t, n]]) <= 1e-12 * (1 + abs(g_decay[t, n]))
+    np.testing.assert_allclose(d_keff[:tv], Ke.grad.numpy()[:tv], rtol=1e-12, atol=1e-12)
+    assert np.all(g_decay[tv:] == 0) and np.all(d_keff[tv:] == 0)
+    assert np.all(mag >= np.abs(new) - 1e-12) and np.all(mag_dot >= 0)
