@@ -359,6 +359,43 @@ typedef struct sdm_gwr_io {
  */
 sdm_status sdm_gwr_step(const sdm_gwr_io* io, int64_t ti, hipStream_t st);
 
+/* PA of one step: the backward of DW for the write groups of chunks ti*P .. ti*P + P - 1. */
+typedef struct sdm_pa_io {
+    void* grad;             /* IN/OUT [rows, hd] SDM_F32 or SDM_BF16 bank gradient: each written slot's row
+                               becomes gdw * cpe + sum_m sc_m d_dva[tok_m] (gdw: its value before the call) */
+    int32_t grad_dtype;     /* sdm_dtype */
+    void* bank;             /* OUT (NULL: skipped) [rows, hd]: each written slot's row restored from snap */
+    int32_t bank_dtype;     /* sdm_dtype of bank and snap */
+    int64_t rows;           /* rows of grad and bank (a slot outside 0..rows-1 is skipped) */
+    int32_t hd;             /* row width, a multiple of 4, 4..1024 */
+    const void* snap;       /* the step's compact snapshot from sdm_dw_step (FIRST-position layout, raw rows) */
+    int64_t snap_step_rows; /* as given to sdm_dw_step */
+    int64_t snap_rows;      /* rows in snap: ti * snap_step_rows + P * C * W <= snap_rows */
+    const int32_t* krec;    /* [N, C*W, 4] records from sdm_phase1 */
+    const void* k_eff;      /* [N, C, W] from sdm_phase1, float32 or bf16 (val_bytes) */
+    const float* beta;      /* [N, C] per-token write strengths */
+    const float* d_dva;     /* gradient token rows: row (ti * step_rows + p * C + t) of [*, hd], float32 */
+    int64_t step_rows;      /* rows between steps in d_dva (P*C, or 0 for a one-step buffer) */
+    int64_t dva_rows;       /* rows in d_dva: ti * step_rows + P * C <= dva_rows */
+    float* g_decay;         /* OUT (NULL: skipped) [N, C, W]: grad_g_decay of the step's entries, 0 for padding */
+    float* d_k_eff;         /* OUT (NULL: skipped) [N, C, W]: d_k_eff of the step's entries, 0 for padding */
+    int32_t P, C, W, N;     /* the Phase-1 shape */
+    int32_t val_bytes;      /* type of k_eff: 0 or 4 = float32, 2 = bf16 */
+} sdm_pa_io;
+
+/*
+ * PA (page "sparse_delta_memory/cuda/pa_dc_cuda.py", module docstring: Phase A of the deterministic
+ * backward step): per valid write group (slot s, members m in sorted order), with gdw = grad[s]
+ * before the call, snap the group's pre-write row and cpe the group's record cpe,
+ *   grad[s]         = fma(gdw, cpe, sum_m sc_m d_dva[tok_m])   (sum from +0, sc_m = -beta k_eff_m),
+ *   bank[s]         = snap,
+ *   grad_g_decay[e] = cpe <gdw, snap>,   d_k_eff[e] = -beta[tok_e] <d_dva[tok_e], snap>.
+ * One wave per group (the only writer of its rows and entries): reproducible. Padding entries get
+ * zeros; masked tokens' rows are never read. Requires (ti + 1) * P <= N, hd a multiple of 4 up to
+ * 1024, 16-byte aligned grad, bank, snap and d_dva rows (8 for bf16 rows), 16-byte aligned krec.
+ */
+sdm_status sdm_pa_step(const sdm_pa_io* io, int64_t ti, hipStream_t st);
+
 /* Static text for a status code. */
 const char* sdm_status_string(sdm_status s);
 

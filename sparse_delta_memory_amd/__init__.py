@@ -18,7 +18,7 @@ from . import _lib
 from ._lib import P1IO, P1Shape, SdmError  # noqa: F401
 
 __all__ = ["P1Shape", "phase1", "phase1_workspace_bytes", "alloc_phase1_outputs", "dw_step", "dw_workspace_bytes",
-           "alloc_dw_workspace", "DwPlan", "ReadPlan", "read_step", "gds_step", "gwr_step", "SdmError", "make_shape",
+           "alloc_dw_workspace", "DwPlan", "ReadPlan", "read_step", "gds_step", "gwr_step", "pa_step", "SdmError", "make_shape",
            "timing_events"]
 
 
@@ -349,3 +349,43 @@ def gwr_step(grad, k_idx, w, dv, shape: P1Shape, ti: int, step_rows: int, d_dv=N
     io.idx_bytes = k_idx.element_size()
     st = torch.cuda.current_stream(grad.device) if stream is None else stream
     _lib.check(lib.sdm_gwr_step(ctypes.byref(io), int(ti), ctypes.c_void_p(st.cuda_stream)))
+
+
+def pa_step(grad, snap, p1, beta, d_dva, shape: P1Shape, ti: int, step_rows: int, snap_step_rows: int, bank=None,
+            g_decay=None, d_k_eff=None, stream=None):
+    """PA of step `ti` (the backward of DW) on the current (or given) stream.
+
+    grad [rows, hd] float32 or bfloat16 bank gradient, updated in place at the step's written slots;
+    snap: the step's compact snapshot from DwPlan (FIRST-position layout, raw rows in the bank dtype);
+    p1: the Phase-1 outputs (krec, k_eff); beta [N, C] float32; d_dva [*, hd] float32 gradient token
+    rows, row ti*step_rows + p*C + t. bank (optional) gets each written slot's row restored from the
+    snapshot; g_decay and d_k_eff [N, C, W] float32 (optional) receive the per-entry gradients."""
+    import torch
+
+    for name, t in (("beta", beta), ("d_dva", d_dva), ("g_decay", g_decay), ("d_k_eff", d_k_eff)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("pa_step: %s must be float32" % name)
+    if grad.dtype not in (torch.float32, torch.bfloat16) or snap.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("pa_step: grad and snap must be float32 or bfloat16")
+    if bank is not None and (bank.dtype != snap.dtype or tuple(bank.shape) != tuple(grad.shape)):
+        raise TypeError("pa_step: bank must have grad's shape and the snapshot's dtype")
+    lib = _lib.load()
+    io = _lib.PaIO()
+    io.grad = grad.data_ptr()
+    io.grad_dtype = _lib.SDM_BF16 if grad.dtype == torch.bfloat16 else _lib.SDM_F32
+    io.bank = _ptr(bank)
+    io.bank_dtype = _lib.SDM_BF16 if snap.dtype == torch.bfloat16 else _lib.SDM_F32
+    io.rows, io.hd = grad.shape[0], grad.shape[1]
+    io.snap = snap.data_ptr()
+    io.snap_step_rows, io.snap_rows = int(snap_step_rows), snap.shape[0]
+    io.krec = p1["krec"].data_ptr()
+    io.k_eff = p1["k_eff"].data_ptr()
+    io.beta = beta.data_ptr()
+    io.d_dva = d_dva.data_ptr()
+    io.step_rows, io.dva_rows = int(step_rows), d_dva.shape[0]
+    io.g_decay = _ptr(g_decay)
+    io.d_k_eff = _ptr(d_k_eff)
+    io.P, io.C, io.W, io.N = shape.P, shape.C, shape.W, shape.N
+    io.val_bytes = p1["k_eff"].element_size()
+    st = torch.cuda.current_stream(grad.device) if stream is None else stream
+    _lib.check(lib.sdm_pa_step(ctypes.byref(io), int(ti), ctypes.c_void_p(st.cuda_stream)))

@@ -91,8 +91,20 @@ class GwrIO(ctypes.Structure):
     ]
 
 
+class PaIO(ctypes.Structure):
+    _fields_ = [
+        ("grad", ctypes.c_void_p), ("grad_dtype", ctypes.c_int32), ("bank", ctypes.c_void_p),
+        ("bank_dtype", ctypes.c_int32), ("rows", ctypes.c_int64), ("hd", ctypes.c_int32), ("snap", ctypes.c_void_p),
+        ("snap_step_rows", ctypes.c_int64), ("snap_rows", ctypes.c_int64), ("krec", ctypes.c_void_p),
+        ("k_eff", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("d_dva", ctypes.c_void_p), ("step_rows", ctypes.c_int64),
+        ("dva_rows", ctypes.c_int64), ("g_decay", ctypes.c_void_p), ("d_k_eff", ctypes.c_void_p),
+        ("P", ctypes.c_int32), ("C", ctypes.c_int32), ("W", ctypes.c_int32), ("N", ctypes.c_int32),
+        ("val_bytes", ctypes.c_int32),
+    ]
+
+
 EXPORTS = ["sdm_phase1_workspace", "sdm_phase1", "sdm_dw_workspace", "sdm_dw_step", "sdm_read_step",
-           "sdm_gds_step", "sdm_gwr_step", "sdm_status_string", "sdm_last_error"]
+           "sdm_gds_step", "sdm_gwr_step", "sdm_pa_step", "sdm_status_string", "sdm_last_error"]
 
 _lock = threading.Lock()
 _lib = None
@@ -127,6 +139,8 @@ def load() -> ctypes.CDLL:
         lib.sdm_gds_step.restype = ctypes.c_int
         lib.sdm_gwr_step.argtypes = [ctypes.POINTER(GwrIO), ctypes.c_int64, ctypes.c_void_p]
         lib.sdm_gwr_step.restype = ctypes.c_int
+        lib.sdm_pa_step.argtypes = [ctypes.POINTER(PaIO), ctypes.c_int64, ctypes.c_void_p]
+        lib.sdm_pa_step.restype = ctypes.c_int
         lib.sdm_status_string.argtypes = [ctypes.c_int]
         lib.sdm_status_string.restype = ctypes.c_char_p
         lib.sdm_last_error.argtypes = []

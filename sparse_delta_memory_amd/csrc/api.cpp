@@ -266,6 +266,46 @@ sdm_status sdm_gwr_step(const sdm_gwr_io* io, int64_t ti, hipStream_t st) {
     return SDM_OK;
 }
 
+sdm_status sdm_pa_step(const sdm_pa_io* io, int64_t ti, hipStream_t st) {
+    g_last_error.clear();
+    if (io == nullptr) return fail(SDM_EINVAL, "sdm_pa_step: io is NULL");
+    if (io->C < 1 || io->C > 256 || io->W < 1 || io->W > 256)
+        return fail(SDM_ESHAPE, "sdm_pa_step: C = %d, W = %d outside 1..256", io->C, io->W);
+    if (io->P < 1 || io->N < 0) return fail(SDM_ESHAPE, "sdm_pa_step: P = %d, N = %d", io->P, io->N);
+    if (ti < 0 || (ti + 1) * static_cast<int64_t>(io->P) > io->N)
+        return fail(SDM_ESHAPE, "sdm_pa_step: step %lld needs (ti+1)*P <= N = %d", static_cast<long long>(ti), io->N);
+    if (io->grad_dtype != SDM_F32 && io->grad_dtype != SDM_BF16)
+        return fail(SDM_EINVAL, "sdm_pa_step: grad_dtype %d", io->grad_dtype);
+    if (io->bank_dtype != SDM_F32 && io->bank_dtype != SDM_BF16)
+        return fail(SDM_EINVAL, "sdm_pa_step: bank_dtype %d", io->bank_dtype);
+    if (io->val_bytes != 0 && io->val_bytes != 4 && io->val_bytes != 2)
+        return fail(SDM_EINVAL, "sdm_pa_step: val_bytes = %d (0 or 4: float32 k_eff; 2: bf16)", io->val_bytes);
+    if (io->hd < 4 || io->hd > 1024 || io->hd % 4 != 0)
+        return fail(SDM_ESHAPE, "sdm_pa_step: hd = %d (a multiple of 4 in 4..1024)", io->hd);
+    const int64_t pcw = static_cast<int64_t>(io->P) * io->C * io->W;
+    if (io->rows < 0 || io->step_rows < 0 || io->dva_rows < 0 || io->snap_step_rows < 0)
+        return fail(SDM_EINVAL, "sdm_pa_step: rows / step_rows / dva_rows / snap_step_rows");
+    if (ti * io->step_rows + static_cast<int64_t>(io->P) * io->C > io->dva_rows)
+        return fail(SDM_EINVAL, "sdm_pa_step: d_dva holds %lld rows, step %lld needs more", static_cast<long long>(io->dva_rows),
+                    static_cast<long long>(ti));
+    if (ti * io->snap_step_rows + pcw > io->snap_rows)
+        return fail(SDM_EINVAL, "sdm_pa_step: snap holds %lld rows, step %lld needs %lld", static_cast<long long>(io->snap_rows),
+                    static_cast<long long>(ti), static_cast<long long>(ti * io->snap_step_rows + pcw));
+    if (io->grad == nullptr || io->snap == nullptr || io->krec == nullptr || io->k_eff == nullptr || io->beta == nullptr ||
+        io->d_dva == nullptr)
+        return fail(SDM_EINVAL, "sdm_pa_step: grad, snap, krec, k_eff, beta and d_dva are required");
+    const uintptr_t ra = io->bank_dtype == SDM_BF16 ? 8 : 16;
+    if (!aligned(io->grad, io->grad_dtype == SDM_BF16 ? 8 : 16) || !aligned(io->bank, ra) || !aligned(io->snap, ra) ||
+        !aligned(io->d_dva, 16) || !aligned(io->krec, 16))
+        return fail(SDM_EALIGN, "sdm_pa_step: grad, bank, snap, d_dva or krec misaligned");
+    if (!aligned(io->k_eff, io->val_bytes == 2 ? 2 : 4) || !aligned(io->beta, 4) || !aligned(io->g_decay, 4) ||
+        !aligned(io->d_k_eff, 4))
+        return fail(SDM_EALIGN, "sdm_pa_step: k_eff, beta, g_decay or d_k_eff misaligned");
+    const hipError_t e = sdm::pa_launch(io, ti, st);
+    if (e != hipSuccess) return fail(SDM_EHIP, "sdm_pa_step: %s", hipGetErrorString(e));
+    return SDM_OK;
+}
+
 sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st) {
     g_last_error.clear();
     if (io == nullptr) return fail(SDM_EINVAL, "sdm_dw_step: io is NULL");

@@ -1,4 +1,4 @@
-// The backward gathers on gfx950. GDS: the backward of the read gather q0[t] = sum_r q_w[t, r]
+// The backward movers on gfx950 (GDS, GWR and PA below). GDS: the backward of the read gather q0[t] = sum_r q_w[t, r]
 // M0[q_idx[t, r]] for the chunks of one step (page "sparse_delta_memory/cuda/mover_da2_cuda.py": the GDS part of the module
 // docstring and the comment of its scatter role).
 //
@@ -278,6 +278,136 @@ __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
     }
 }
 
+// PA (page "sparse_delta_memory/cuda/pa_dc_cuda.py", module docstring: Phase A of the deterministic
+// backward, the backward of DW) for the chunks of one step. One wave per K-row position: a padding
+// entry writes its zeros; a valid group FIRST loads its slot's gradient row gdw and its snapshot row
+// (hd <= 1024: 4 columns of every 256 per lane), forms <gdw, snap> once, walks the members in
+// sorted order (token rows of 4 members in flight): acc = fma(-beta k_eff, d_dva[t], acc) from +0,
+// d_k_eff[e] = -beta <d_dva[t], snap>, grad_g_decay[e] = cpe <gdw, snap>; then grad[s] =
+// fma(gdw, cpe, acc) and bank[s] = snap. One writer per row and per entry: deterministic.
+struct PaArgs {
+    void* grad;
+    void* bank;
+    const void* snap;
+    const uint4* krec;
+    const void* k_eff;
+    const float* beta;
+    const float* d_dva;
+    float* g_decay;
+    float* d_k_eff;
+    int64_t rows, chunk0, row0, snap_row0;
+    int P, C, W, CW, hd, vbf, grad_bf16, bank_bf16;
+};
+
+constexpr int kPaMembers = 4;   // member token rows in flight together
+
+__device__ __forceinline__ void store4(void* base, int bf, int64_t row, int hd, int col, float4 v) {
+    if (bf) {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + row * hd + col) =
+            make_uint2(f32_to_bf16_rne(v.x) | f32_to_bf16_rne(v.y) << 16, f32_to_bf16_rne(v.z) | f32_to_bf16_rne(v.w) << 16);
+    } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(base) + row * hd + col) = v;
+    }
+}
+
+__global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
+    const int wv = static_cast<int>(threadIdx.x) / kWave;
+    const int lane = static_cast<int>(lane_id());
+    const int64_t pos = static_cast<int64_t>(blockIdx.x) * kGdsWaves + wv;   // p * CW + j
+    if (pos >= static_cast<int64_t>(a.P) * a.CW) return;
+    const int p = static_cast<int>(pos / a.CW), j = static_cast<int>(pos % a.CW);
+    const int64_t c = a.chunk0 + p;
+    const uint4* kr = a.krec + c * a.CW;
+    const uint4 r0 = kr[j];
+    auto eidx = [&](uint32_t el) {   // entry-order index [N, C, W] of a K-row element
+        return (c * a.C + static_cast<int64_t>((el >> kTokShift) & 0xFFu)) * a.W + (el & 0xFFu);
+    };
+    if (r0.x & kInvalid) {   // padding: its outputs are zero
+        if (lane == 0) {
+            if (a.g_decay != nullptr) a.g_decay[eidx(r0.x)] = 0.0f;
+            if (a.d_k_eff != nullptr) a.d_k_eff[eidx(r0.x)] = 0.0f;
+        }
+        return;
+    }
+    if (!(r0.x & kFirst)) return;   // a member: its group's wave writes it
+    const int64_t slot = static_cast<int64_t>(r0.y);
+    const bool in = slot < a.rows;   // (a slot outside the bank: zero rows, nothing written)
+    const float cpe = __uint_as_float(r0.w);
+    const int64_t srow = a.snap_row0 + static_cast<int64_t>(p) * a.CW + j;
+    float4 gdw[kGwrColBlocks], sn[kGwrColBlocks], acc[kGwrColBlocks];
+    float part0 = 0.0f;
+#pragma unroll
+    for (int cb = 0; cb < kGwrColBlocks; ++cb) {
+        const int col = cb * 4 * kWave + 4 * lane;
+        const bool con = in && col < a.hd;
+        gdw[cb] = con ? load4(a.grad, a.grad_bf16, slot, a.hd, col) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        sn[cb] = con ? load4(a.snap, a.bank_bf16, srow, a.hd, col) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        acc[cb] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        part0 = fmaf(gdw[cb].w, sn[cb].w, fmaf(gdw[cb].z, sn[cb].z, fmaf(gdw[cb].y, sn[cb].y, fmaf(gdw[cb].x, sn[cb].x, part0))));
+    }
+    const float dot0 = wave_sum(part0);
+    const int64_t grow0 = a.row0 + static_cast<int64_t>(p) * a.C;
+    bool done = false;
+    for (int m0 = j; !done && m0 < a.CW; m0 += kWave) {   // members 64 records at a time, in sorted order
+        const int m = m0 + lane;
+        const uint32_t el = m < a.CW ? kr[m].x : (kFirst | kLast | kInvalid);
+        const int tk = static_cast<int>((el >> kTokShift) & 0xFFu);
+        const bool valid = m < a.CW && !(el & kInvalid);
+        const float nb = valid ? -a.beta[c * a.C + tk] : 0.0f;
+        const float w = valid ? nb * load_val(a.k_eff, eidx(el), a.vbf) : 0.0f;
+        const int64_t ei = valid ? eidx(el) : 0;
+        const uint64_t lastm = __ballot((el & kLast) != 0u);
+        const int cnt = lastm != 0ull ? __builtin_ctzll(lastm) + 1 : kWave;   // (LAST included)
+        done = lastm != 0ull;
+        for (int k0 = 0; k0 < cnt; k0 += kPaMembers) {
+            float4 d[kPaMembers][kGwrColBlocks];
+            float wk[kPaMembers], bk[kPaMembers];
+            int64_t ek[kPaMembers];
+#pragma unroll
+            for (int u = 0; u < kPaMembers; ++u) {
+                const int kk = min(k0 + u, cnt - 1);
+                wk[u] = __shfl(w, kk, kWave);
+                bk[u] = __shfl(nb, kk, kWave);
+                ek[u] = shfl64(ei, kk);
+                const int t = __shfl(tk, kk, kWave);
+#pragma unroll
+                for (int cb = 0; cb < kGwrColBlocks; ++cb) {
+                    const int col = cb * 4 * kWave + 4 * lane;
+                    d[u][cb] = col < a.hd ? load4(a.d_dva, 0, grow0 + t, a.hd, col) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kPaMembers; ++u) {
+                if (k0 + u >= cnt) break;
+                float part = 0.0f;
+#pragma unroll
+                for (int cb = 0; cb < kGwrColBlocks; ++cb) {
+                    acc[cb].x = fmaf(wk[u], d[u][cb].x, acc[cb].x);
+                    acc[cb].y = fmaf(wk[u], d[u][cb].y, acc[cb].y);
+                    acc[cb].z = fmaf(wk[u], d[u][cb].z, acc[cb].z);
+                    acc[cb].w = fmaf(wk[u], d[u][cb].w, acc[cb].w);
+                    part = fmaf(d[u][cb].w, sn[cb].w, fmaf(d[u][cb].z, sn[cb].z, fmaf(d[u][cb].y, sn[cb].y, fmaf(d[u][cb].x, sn[cb].x, part))));
+                }
+                const float dot = wave_sum(part);
+                if (lane == 0) {
+                    if (a.d_k_eff != nullptr) a.d_k_eff[ek[u]] = bk[u] * dot;
+                    if (a.g_decay != nullptr) a.g_decay[ek[u]] = cpe * dot0;
+                }
+            }
+        }
+    }
+    if (!in) return;
+#pragma unroll
+    for (int cb = 0; cb < kGwrColBlocks; ++cb) {
+        const int col = cb * 4 * kWave + 4 * lane;
+        if (col >= a.hd) break;
+        const float4 g = make_float4(fmaf(gdw[cb].x, cpe, acc[cb].x), fmaf(gdw[cb].y, cpe, acc[cb].y),
+                                     fmaf(gdw[cb].z, cpe, acc[cb].z), fmaf(gdw[cb].w, cpe, acc[cb].w));
+        store4(a.grad, a.grad_bf16, slot, a.hd, col, g);
+        if (a.bank != nullptr) store4(a.bank, a.bank_bf16, slot, a.hd, col, sn[cb]);
+    }
+}
+
 }  // namespace
 
 hipError_t gds_launch(const sdm_gds_io* io, int64_t ti, hipStream_t st) {
@@ -342,6 +472,35 @@ hipError_t gwr_launch(const sdm_gwr_io* io, int64_t ti, hipStream_t st) {
     void* kargs[] = {&a};
     return hipLaunchKernel(reinterpret_cast<const void*>(&gwr_kernel),
                            dim3(static_cast<unsigned>((toks + kGdsWaves - 1) / kGdsWaves)), dim3(kGdsThreads), kargs, 0, st);
+}
+
+hipError_t pa_launch(const sdm_pa_io* io, int64_t ti, hipStream_t st) {
+    PaArgs a;
+    a.grad = io->grad;
+    a.bank = io->bank;
+    a.snap = io->snap;
+    a.krec = reinterpret_cast<const uint4*>(io->krec);
+    a.k_eff = io->k_eff;
+    a.beta = io->beta;
+    a.d_dva = io->d_dva;
+    a.g_decay = io->g_decay;
+    a.d_k_eff = io->d_k_eff;
+    a.rows = io->rows;
+    a.chunk0 = ti * io->P;
+    a.row0 = ti * io->step_rows;
+    a.snap_row0 = ti * io->snap_step_rows;
+    a.P = io->P;
+    a.C = io->C;
+    a.W = io->W;
+    a.CW = io->C * io->W;
+    a.hd = io->hd;
+    a.vbf = io->val_bytes == 2;
+    a.grad_bf16 = io->grad_dtype == SDM_BF16;
+    a.bank_bf16 = io->bank_dtype == SDM_BF16;
+    const int64_t poss = static_cast<int64_t>(io->P) * io->C * io->W;
+    void* kargs[] = {&a};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&pa_kernel),
+                           dim3(static_cast<unsigned>((poss + kGdsWaves - 1) / kGdsWaves)), dim3(kGdsThreads), kargs, 0, st);
 }
 
 }  // namespace sdm

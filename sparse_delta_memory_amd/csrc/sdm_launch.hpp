@@ -71,4 +71,7 @@ hipError_t gds_launch(const sdm_gds_io* io, int64_t ti, hipStream_t st);
 // GWR of step ti (validated by sdm_gwr_step).
 hipError_t gwr_launch(const sdm_gwr_io* io, int64_t ti, hipStream_t st);
 
+// PA of step ti (validated by sdm_pa_step).
+hipError_t pa_launch(const sdm_pa_io* io, int64_t ti, hipStream_t st);
+
 }  // namespace sdm

@@ -236,3 +236,28 @@ def test_gwr_refusals(kw, ti, status):
     assert lib.sdm_gwr_step(ctypes.byref(gwr_io(**kw)), ti, None) == status
     assert len(lib.sdm_last_error()) > 0
     assert lib.sdm_gwr_step(None, 0, None) == _lib.SDM_EINVAL
+
+
+def pa_io(**kw):
+    o = _lib.PaIO()
+    d = dict(grad=FAKE, grad_dtype=_lib.SDM_F32, bank=FAKE, bank_dtype=_lib.SDM_BF16, rows=1 << 20, hd=128, snap=FAKE,
+             snap_step_rows=0, snap_rows=1 << 16, krec=FAKE, k_eff=FAKE, beta=FAKE, d_dva=FAKE, step_rows=512,
+             dva_rows=1 << 20, g_decay=FAKE, d_k_eff=FAKE, P=4, C=128, W=16, N=8, val_bytes=4)
+    d.update(kw)
+    for k, v in d.items():
+        setattr(o, k, v)
+    return o
+
+
+@pytest.mark.parametrize("kw,ti,status", [
+    (dict(), 2, _lib.SDM_ESHAPE), (dict(C=300), 0, _lib.SDM_ESHAPE), (dict(hd=2048), 0, _lib.SDM_ESHAPE),
+    (dict(grad_dtype=4), 0, _lib.SDM_EINVAL), (dict(bank_dtype=4), 0, _lib.SDM_EINVAL), (dict(val_bytes=3), 0, _lib.SDM_EINVAL),
+    (dict(snap_rows=100), 0, _lib.SDM_EINVAL), (dict(dva_rows=100), 0, _lib.SDM_EINVAL), (dict(beta=None), 0, _lib.SDM_EINVAL),
+    (dict(snap=FAKE + 4), 0, _lib.SDM_EALIGN), (dict(krec=FAKE + 8), 0, _lib.SDM_EALIGN),
+    (dict(d_k_eff=FAKE + 2), 0, _lib.SDM_EALIGN),
+])
+def test_pa_refusals(kw, ti, status):
+    lib = _lib.load()
+    assert lib.sdm_pa_step(ctypes.byref(pa_io(**kw)), ti, None) == status
+    assert len(lib.sdm_last_error()) > 0
+    assert lib.sdm_pa_step(None, 0, None) == _lib.SDM_EINVAL

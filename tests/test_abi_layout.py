@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HIP_INCLUDE = "/opt/rocm/include"
 STRUCTS = [("sdm_p1_shape", _lib.P1Shape), ("sdm_p1_io", _lib.P1IO), ("sdm_dw_io", _lib.DwIO),
            ("sdm_read_io", _lib.ReadIO), ("sdm_gds_io", _lib.GdsIO),
-           ("sdm_gwr_io", _lib.GwrIO)]
+           ("sdm_gwr_io", _lib.GwrIO), ("sdm_pa_io", _lib.PaIO)]
 
 pytestmark = pytest.mark.skipif(shutil.which("gcc") is None or
                                 not os.path.exists(os.path.join(HIP_INCLUDE, "hip", "hip_runtime_api.h")),
