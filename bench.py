@@ -339,6 +339,7 @@ def main():
         res["read_side"] = measure_read_side(args, wl, shape, out, ins, bank, plan, stream, W, sdm, torch)
     if not args.no_gds:
         res["gds"] = measure_gds(wl, shape, out, ins, bank, stream, sdm, torch)
+        res["gwr_pa"] = measure_gwr_pa(wl, shape, out, ins, bank, stream, sdm, torch, W)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on host cores)...")
         res["cpu_baseline"] = cpu_baseline(wl, bank0)
@@ -431,6 +432,57 @@ def measure_gds(wl, shape, out, ins, bank, stream, sdm, torch):
     b = gds_bytes(P, C, R, hd, 2 if sh.bank_dtype == "bf16" else 4, groups_q, 2 if sh.bank_dtype == "bf16" else 4)
     return {"bytes_per_step": b, "ms_per_step": ms, "GBps": b / (ms * 1e-3) / 1e9, "frac": b / (ms * 1e-3) / HBM_PEAK_BYTES,
             "note": "dots + scatter kernels per step, events around the call; grad in the bank dtype"}
+
+
+def measure_gwr_pa(wl, shape, out, ins, bank, stream, sdm, torch, W):
+    """GWR and PA of every step, each timed by events on the launch stream around its call (PA after
+    the step's DW has written its snapshot); seeded gradient inputs. Not part of the headline step.
+    Algorithmic bytes: GWR P C W (hd es + 12) + 2 P C hd 4; PA P C W 36 + G hd (2 es_grad + 2 es_bank)
+    + P C W hd 4 (G the step's write groups)."""
+    sh = wl.shape
+    P, C, Wn, hd = sh.P, sh.C, sh.W, sh.hd
+    dev = bank.device
+    es = 2 if sh.bank_dtype == "bf16" else 4
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.bank_seed + 43)
+    rows = wl.steps * P * C
+    dv = torch.randn((rows, hd), generator=gen, device=dev)
+    d_dva = torch.randn((rows, hd), generator=gen, device=dev)
+    w = torch.randn((wl.N, C, Wn), generator=gen, device=dev)
+    beta = torch.rand((wl.N, C), generator=gen, device=dev)
+    grad = (torch.randn(bank.shape, generator=gen, device=dev) * 0.01).to(bank.dtype)
+    d_dv = torch.zeros_like(dv)
+    d_k_pd = torch.zeros((wl.N, C, Wn), device=dev)
+    g_decay = torch.zeros((wl.N, C, Wn), device=dev)
+    d_k_eff = torch.zeros((wl.N, C, Wn), device=dev)
+    snap = torch.zeros((P * C * Wn, hd), dtype=bank.dtype, device=dev)
+    work = bank.clone()
+    plan = sdm.DwPlan(work, dv, out["krec"], shape, dv_step_rows=P * C, snapshot=snap, snap_step_rows=0)
+    kr = out["krec"][..., 0]
+    groups = float((((kr & W_FIRST) != 0) & ((kr & W_INVALID) == 0)).view(wl.steps, -1).sum(dim=1).float().mean())
+    ev_g, ev_p = [], []
+    for ti in range(wl.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        sdm.gwr_step(grad, ins["k_idx"], w, dv, shape, ti, step_rows=P * C, d_dv=d_dv, d_k_pd=d_k_pd, stream=stream)
+        b.record(stream)
+        ev_g.append((a, b))
+        plan.step(ti, stream=stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        sdm.pa_step(grad, snap, out, beta, d_dva, shape, ti, step_rows=P * C, snap_step_rows=0, bank=work,
+                    g_decay=g_decay, d_k_eff=d_k_eff, stream=stream)
+        b.record(stream)
+        ev_p.append((a, b))
+    torch.cuda.synchronize()
+    skip = 1 if wl.steps > 1 else 0   # the first calls include their one-time costs
+    ms_g = float(np.mean([a.elapsed_time(b) for a, b in ev_g[skip:]]))
+    ms_p = float(np.mean([a.elapsed_time(b) for a, b in ev_p[skip:]]))
+    bg = P * C * Wn * (hd * es + 12) + 2 * P * C * hd * 4
+    bp = P * C * Wn * 36 + groups * hd * (2 * es + 2 * es) + P * C * Wn * hd * 4
+    return {"gwr": {"bytes_per_step": bg, "ms_per_step": ms_g, "frac": bg / (ms_g * 1e-3) / HBM_PEAK_BYTES},
+            "pa": {"bytes_per_step": bp, "ms_per_step": ms_p, "frac": bp / (ms_p * 1e-3) / HBM_PEAK_BYTES},
+            "note": "events around each call on the launch stream; grad and bank in the bank dtype"}
 
 
 W_FIRST = -(1 << 31)      # bit 31 of the int32 record element
