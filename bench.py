@@ -3,19 +3,19 @@
 
 One step = the whole hot path over one batch: Phase 1 of every chunk of the workload (sort, scans,
 records, tile bounds, A / QK) followed by every DW step of the workload, all enqueued on one stream
-with the inputs already in HBM, launched eagerly (--graph: replayed from a HIP graph;
---pair-stream: the pair kernel on a second stream beside the DW steps). Before the W warmup
+with the inputs already in HBM, launched eagerly (--graph: replayed from a HIP graph). Before the W warmup
 steps, untimed steps run for about --settle seconds so that the GPU clocks leave idle. `value` is
 the step's throughput in Phase-1 K+Q entries per second. Kernel durations for the roofline come
 from a second, eager pass of the same steps with HIP events bound to each kernel's own start and
 end.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I] [--no-cpu-baseline] [--graph]
-                    [--pair-stream] [--settle S]
+                    [--settle S]
     python bench.py --copy-calibration MIB   # a plain device copy, for scaling HBM byte counters
 
-The default workload is the uniform bf16 shape (index 1); the others are parity cases that can
-also be timed with --workload. Prints ONE JSON line.
+The default workload is the largest one-GPU configuration, the large bank with a ragged tail
+(index 4: P=16, T=16384, C=256, W=R=32, S=4194304 per stream, hd=128, bf16 bank); the others are
+parity cases that can also be timed with --workload. Prints ONE JSON line.
 """
 
 from __future__ import annotations
@@ -103,63 +103,97 @@ def read_traffic(workload_name, kernel):
     return float(vals[key]) if key in vals else None
 
 
-def cpu_baseline(wl, bank0, n_chunks_target_s=15.0):
-    """The oracle, as it stands, on a bounded sample of the same workload (host cores)."""
+def host_threads():
+    """Threads for the oracle: OMP_NUM_THREADS when set (the host's share of cores), else the CPUs
+    this process may run on, at most 16."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(wl, bank0, target_s=12.0, target_1core_s=5.0):
+    """The oracle, as it stands, on a bounded sample of the same workload: Phase 1 of a sample of
+    chunks plus the DW of the same chunks from the initial bank, on `host_threads()` threads
+    (chunks spread over them), and a smaller sample on one thread."""
     import torch
 
     import oracle
 
     sh = wl.shape
-    threads = os.cpu_count() or 1
+    threads = host_threads()
     n = sh.C * (sh.W + sh.R)
-    # Calibrate on one chunk, then size the sample for about n_chunks_target_s seconds.
-    t0 = time.perf_counter()
-    oracle.phase1(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, P=wl.P, stream_offset=wl.stream_offset,
-                  first_partial=wl.first_partial, valid_last=wl.valid_last, chunks=[0])
-    one = max(time.perf_counter() - t0, 1e-4)
-    m = int(min(wl.N, max(threads, n_chunks_target_s * threads / one / 2)))
-    chunks = list(range(m))
-    t0 = time.perf_counter()
-    oracle.phase1(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, P=wl.P, stream_offset=wl.stream_offset,
-                  first_partial=wl.first_partial, valid_last=wl.valid_last, chunks=chunks, threads=threads)
-    t_p1 = time.perf_counter() - t0
-    # DW of the same chunks from the initial bank (rows gathered outside the timed region).
-    jobs = []
     dv = wl.dv.reshape(-1, sh.hd)
-    for c in chunks:
-        slots = oracle.dw_slots(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, c, P=wl.P, stream_offset=sh.S,
-                                first_partial=wl.first_partial, valid_last=wl.valid_last)
-        base = bank0.index_select(0, torch.as_tensor(slots, device=bank0.device)).float().cpu().numpy()
-        jobs.append((c, base.astype(np.float64), dv[c * sh.C:(c + 1) * sh.C].astype(np.float64)))
-    from concurrent.futures import ThreadPoolExecutor
+    okw = dict(P=wl.P, stream_offset=sh.S, first_partial=wl.first_partial, valid_last=wl.valid_last)
 
-    def run(job):
+    def jobs_for(chunks):   # DW inputs gathered outside the timed region
+        jobs = []
+        for c in chunks:
+            slots = oracle.dw_slots(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, c, **okw)
+            base = bank0.index_select(0, torch.as_tensor(slots, device=bank0.device)).float().cpu().numpy()
+            jobs.append((c, base.astype(np.float64), dv[c * sh.C:(c + 1) * sh.C].astype(np.float64)))
+        return jobs
+
+    def run_dw(job):
         c, base, rows = job
-        oracle.dw_apply(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, c, rows, base, P=wl.P, stream_offset=sh.S,
-                        first_partial=wl.first_partial, valid_last=wl.valid_last)
+        oracle.dw_apply(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, c, rows, base, **okw)
 
-    t0 = time.perf_counter()
-    with ThreadPoolExecutor(max_workers=threads) as ex:
-        list(ex.map(run, jobs))
-    t_dw = time.perf_counter() - t0
-    # A short sample (the whole workload can take well under a second) is repeated, whole passes
-    # only, until about 10 s of oracle work have been timed (at most 30 s).
+    def timed(chunks, jobs, nthreads):
+        from concurrent.futures import ThreadPoolExecutor
+
+        t0 = time.perf_counter()
+        oracle.phase1(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, chunks=chunks, threads=nthreads, **okw)
+        t_p1 = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        if nthreads == 1:
+            for j in jobs:
+                run_dw(j)
+        else:
+            with ThreadPoolExecutor(max_workers=nthreads) as ex:
+                list(ex.map(run_dw, jobs))
+        return t_p1, time.perf_counter() - t0
+
+    # Calibrate on one chunk, then size each sample for its target time.
+    one_p1, one_dw = timed([0], jobs_for([0]), 1)
+    one = max(one_p1 + one_dw, 1e-4)
+    m1 = int(min(wl.N, max(1, target_1core_s / one)))
+    t1_p1, t1_dw = timed(list(range(m1)), jobs_for(range(m1)), 1)
+    m = int(min(wl.N, max(threads, target_s * threads / one)))
+    chunks = list(range(m))
+    jobs = jobs_for(chunks)
+    t_p1, t_dw = timed(chunks, jobs, threads)
+    # A short sample (a small workload can finish in well under a second) is repeated, whole
+    # passes only, until about 10 s of oracle work have been timed (at most 30 s).
     passes = 1
-    one = t_p1 + t_dw
-    while t_p1 + t_dw < 10.0 and t_p1 + t_dw + one <= 30.0:
-        t0 = time.perf_counter()
-        oracle.phase1(wl.k_idx, wl.q_idx, wl.k_val, wl.q_val, wl.g, P=wl.P, stream_offset=wl.stream_offset,
-                      first_partial=wl.first_partial, valid_last=wl.valid_last, chunks=chunks, threads=threads)
-        t_p1 += time.perf_counter() - t0
-        t0 = time.perf_counter()
-        with ThreadPoolExecutor(max_workers=threads) as ex:
-            list(ex.map(run, jobs))
-        t_dw += time.perf_counter() - t0
+    once = t_p1 + t_dw
+    while t_p1 + t_dw < 10.0 and t_p1 + t_dw + once <= 30.0:
+        a, b = timed(chunks, jobs, threads)
+        t_p1 += a
+        t_dw += b
         passes += 1
     return {
         "value": passes * m * n / (t_p1 + t_dw), "unit": "entries/s", "cores": threads, "kind": "oracle",
-        "sample": "%d of %d chunks (Phase 1 + the DW of the same chunks from the initial bank), %d passes; "
-                  "phase1 %.2f s, dw %.2f s" % (m, wl.N, passes, t_p1, t_dw),
+        "sample": "%d of %d chunks (Phase 1 + the DW of the same chunks from the initial bank), %d passes on %d "
+                  "threads: phase1 %.2f s, dw %.2f s" % (m, wl.N, passes, threads, t_p1, t_dw),
+        "value_1core": m1 * n / (t1_p1 + t1_dw),
+        "sample_1core": "%d chunks on 1 thread: phase1 %.2f s, dw %.2f s" % (m1, t1_p1, t1_dw),
+        "cpu_model": cpu_model(),
     }
 
 
@@ -168,13 +202,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step from a HIP graph in the timed region")
     ap.add_argument("--settle", type=float, default=0.25, metavar="S",
                     help="untimed steps for about S seconds before the warmup steps (clocks settle)")
-    ap.add_argument("--pair-stream", action="store_true",
-                    help="run the pair kernel on a second stream beside the DW steps (slower on uniform_bf16)")
     ap.add_argument("--no-gds", action="store_true", help="skip the GDS (backward of the read gather) measurement")
     ap.add_argument("--no-read-side", action="store_true",
                     help="skip the separate measurement of the read side (gather + substitution) and the forward loop")
@@ -221,20 +253,11 @@ def main():
     P, C = sh.P, sh.C
     plan = sdm.DwPlan(bank, dv, out["krec"], shape, dv_step_rows=P * C, workspace=dw_ws)
     n_ev = 4 + 2 * wl.steps   # start / end of the sort-scan kernel, the pair kernel, every DW launch
-    # Optionally the pair kernel (it reads only what the sort/scan kernel wrote; the DW steps never
-    # read its output) on a second stream beside the DW steps; the step then ends with a join.
-    pair_stream = torch.cuda.Stream(device=dev) if args.pair_stream else None
-    pair_ready, joined = torch.cuda.Event(), torch.cuda.Event()
-    pair_ready.record(stream)
 
     def step(ev=None):
-        sdm.phase1(shape, out=out, workspace=ws, events=None if ev is None else ev[0:4], pair_stream=pair_stream,
-                   pair_ready=pair_ready if pair_stream is not None else None, **ins)
+        sdm.phase1(shape, out=out, workspace=ws, events=None if ev is None else ev[0:4], **ins)
         for ti in range(wl.steps):
             plan.step(ti, events=None if ev is None else ev[4 + 2 * ti:6 + 2 * ti])
-        if pair_stream is not None:
-            joined.record(pair_stream)
-            stream.wait_event(joined)
 
     # Untimed settling: steps for about --settle seconds (the GPU leaves its idle clocks; a cold
     # first timed region measured up to 20 % slow), then the W warmup steps proper.
@@ -321,8 +344,7 @@ def main():
             "workload": "%s: P=%d T=%d C=%d W=%d R=%d S=%d hd=%d bank %s dv %s slots %s" % (
                 sh.name, sh.P, sh.T, sh.C, sh.W, sh.R, sh.S, sh.hd, sh.bank_dtype, sh.dv_dtype, sh.slots),
             "chunks": wl.N, "dw_steps": wl.steps, "global_batch": wl.N * sh.C, "seq_len": sh.T,
-            "parallelism": "single GPU", "launch": ("hipGraph replay" if args.graph else "eager") +
-            ("; pair kernel on a second stream beside the DW steps" if args.pair_stream else ""),
+            "parallelism": "single GPU", "launch": "hipGraph replay" if args.graph else "eager",
         },
         "phase1_entries_per_s": entries / ((ms_main + ms_pairs) * 1e-3),
         "phase1_hbm_frac": (main_bytes + pairs_bytes) / ((ms_main + ms_pairs) * 1e-3) / HBM_PEAK_BYTES,
@@ -397,12 +419,25 @@ def measure_read_side(args, wl, shape, out, ins, bank, dw_plan, stream, W, sdm, 
 
 def gds_bytes(P, C, R, hd, bank_es, groups_q, grad_es):
     """Algorithmic bytes of one GDS step: the dots read per read its id (8 with the q_w/element
-    words counted in the scatter), its bank row, and write its dot, and read each gradient row once;
-    the scatter reads per Q-row position its element, id and q_w and a gradient row, and reads and
-    writes each group's grad row once."""
-    dots = P * C * R * (hd * bank_es + 8 + 4) + P * C * hd * 4
-    scatter = P * C * R * (4 + 8) + P * C * R * hd * 4 + 2 * groups_q * hd * grad_es
-    return dots + scatter
+    words counted in the scatter), its bank row, and write its dot; the scatter reads per Q-row
+    position its element, id and q_w, and reads and writes each group's grad row once; each token's
+    gradient row is read once for the step."""
+    dots = P * C * R * (hd * bank_es + 8 + 4)
+    scatter = P * C * R * (4 + 8) + 2 * groups_q * hd * grad_es
+    return dots + scatter + P * C * hd * 4
+
+
+def gwr_bytes(P, C, W, hd, grad_es):
+    """One GWR step: per write its id and weight (8 B), its gradient row and its dot (4 B); each
+    token row read and its d_dv row written once (float32)."""
+    return P * C * W * (hd * grad_es + 12) + 2 * P * C * hd * 4
+
+
+def pa_bytes(P, C, W, hd, groups, grad_es, bank_es):
+    """One PA step: per K-row position its record (16 B), k_eff and beta (8 B) and its two
+    gradient outputs (4 B + 8 B of element bookkeeping); per write group its grad row read and
+    written, its snapshot row read and its bank row restored; each token's d_dva row read once."""
+    return P * C * W * 36 + groups * hd * (2 * grad_es + 2 * bank_es) + P * C * hd * 4
 
 
 def measure_gds(wl, shape, out, ins, bank, stream, sdm, torch):
@@ -437,8 +472,7 @@ def measure_gds(wl, shape, out, ins, bank, stream, sdm, torch):
 def measure_gwr_pa(wl, shape, out, ins, bank, stream, sdm, torch, W):
     """GWR and PA of every step, each timed by events on the launch stream around its call (PA after
     the step's DW has written its snapshot); seeded gradient inputs. Not part of the headline step.
-    Algorithmic bytes: GWR P C W (hd es + 12) + 2 P C hd 4; PA P C W 36 + G hd (2 es_grad + 2 es_bank)
-    + P C W hd 4 (G the step's write groups)."""
+    Algorithmic bytes: gwr_bytes and pa_bytes (each token row counted once)."""
     sh = wl.shape
     P, C, Wn, hd = sh.P, sh.C, sh.W, sh.hd
     dev = bank.device
@@ -478,8 +512,8 @@ def measure_gwr_pa(wl, shape, out, ins, bank, stream, sdm, torch, W):
     skip = 1 if wl.steps > 1 else 0   # the first calls include their one-time costs
     ms_g = float(np.mean([a.elapsed_time(b) for a, b in ev_g[skip:]]))
     ms_p = float(np.mean([a.elapsed_time(b) for a, b in ev_p[skip:]]))
-    bg = P * C * Wn * (hd * es + 12) + 2 * P * C * hd * 4
-    bp = P * C * Wn * 36 + groups * hd * (2 * es + 2 * es) + P * C * Wn * hd * 4
+    bg = gwr_bytes(P, C, Wn, hd, es)
+    bp = pa_bytes(P, C, Wn, hd, groups, es, es)
     return {"gwr": {"bytes_per_step": bg, "ms_per_step": ms_g, "frac": bg / (ms_g * 1e-3) / HBM_PEAK_BYTES},
             "pa": {"bytes_per_step": bp, "ms_per_step": ms_p, "frac": bp / (ms_p * 1e-3) / HBM_PEAK_BYTES},
             "note": "events around each call on the launch stream; grad and bank in the bank dtype"}

@@ -7,9 +7,13 @@
  *  - All array arguments are DEVICE pointers owned by the caller. The library allocates no
  *    memory, keeps no pointer after returning and never synchronizes: work is enqueued on the
  *    caller's stream `st` (hipStream_t; 0 = the null stream).
- *  - The shape and argument checks run on the host before anything is enqueued. Any non-zero
- *    status means nothing was launched; sdm_last_error() then returns a message naming the
- *    failed check (thread-local, valid until the next call on that thread).
+ *  - The shape and argument checks, and the once-per-device set-up (the device's LDS limit, the
+ *    kernels' dynamic-LDS attributes), run on the host before anything is enqueued. Any non-zero
+ *    status from a check or the set-up means nothing was launched; sdm_last_error() then returns
+ *    a message naming the failed check (thread-local, valid until the next call on that thread).
+ *    An entry point that enqueues several kernels makes no other runtime call between them, so
+ *    the only later failure is a launch the runtime itself rejects (SDM_EHIP), which the checks
+ *    rule out for shapes they accept.
  *  - Device code never traps on inputs that pass the checks. Slot ids outside the ranges
  *    stated below are the caller's contract (results are unspecified, memory stays in bounds
  *    for Phase 1; DW writes the rows the records name).
@@ -132,12 +136,6 @@ typedef struct sdm_p1_io {
                                own start and end (hipExtLaunchKernel): [0], [1] the sort/scan kernel,
                                [2], [3] the pair kernel (an event of a kernel that is not launched,
                                such as the pair kernel when a and qk are both NULL, is not recorded) */
-    hipStream_t pair_stream; /* optional (NULL: st): stream for the pair kernel, which then waits for
-                               the sort/scan kernel through pair_ready and may run beside work the
-                               caller enqueues on st next (the DW steps read nothing it writes). The
-                               caller must make st wait for pair_stream before reusing the workspace
-                               or reading a / qk. Default priority, same device. */
-    hipEvent_t pair_ready;  /* caller-created event, required with pair_stream (recorded on st) */
     int32_t* status;        /* debug, optional (NULL: off): when set, the sort/scan kernel checks every
                                valid entry's slot id (local slot in [0, 2^key_bits), id >= 0) and sets bit
                                0 of *status (an atomic OR) if one is out of range. The caller zeroes the

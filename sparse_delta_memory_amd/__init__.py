@@ -63,17 +63,15 @@ def alloc_phase1_outputs(shape: P1Shape, device="cuda", fields=None):
 
 
 def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=None, stream=None, events=None,
-           pair_stream=None, pair_ready=None, status=None):
+           status=None):
     """Enqueue Phase 1 of shape.N chunks on the current (or given) stream; returns the outputs.
 
     Inputs are contiguous device tensors: k_idx [N,C,W] / q_idx [N,C,R] int32 (int64 with
     shape.idx_bytes = 8), k_val / q_val
     float32 (bfloat16 with shape.val_bytes = 2) of the same shapes, g [N,C] float32 ([N,C,W] when shape.g_lane_stride = 1). `out` is a dict from alloc_phase1_outputs (a
     missing key skips that optional output). events: optional 4 torch.cuda.Events (timing_events)
-    bound to the two kernels. pair_stream / pair_ready: optional torch stream and recorded event:
-    the pair kernel then runs on pair_stream after the sort/scan kernel; the caller makes the main
-    stream wait for pair_stream before reusing the workspace or reading a / qk. status: optional
-    zeroed int32 device tensor (debug): bit 0 is set when a valid entry's slot id is out of range."""
+    bound to the two kernels. status: optional zeroed int32 device tensor (debug): bit 0 is set
+    when a valid entry's slot id is out of range."""
     import torch
 
     lib = _lib.load()
@@ -104,10 +102,6 @@ def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=No
     if status is not None:
         io.status = status.data_ptr()
     io.gord_k = _ptr(out.get("gord_k"))
-    if pair_stream is not None:
-        ready = _event_array([pair_ready] if pair_ready is not None else [], 1, "phase1 pair_ready")
-        io.pair_stream = pair_stream.cuda_stream
-        io.pair_ready = ready[0]
     st = torch.cuda.current_stream(k_idx.device) if stream is None else stream
     _lib.check(lib.sdm_phase1(ctypes.byref(shape), ctypes.byref(io), ctypes.c_void_p(st.cuda_stream)))
     return out

@@ -40,7 +40,7 @@ P1_IO_FIELDS = [
 class P1IO(ctypes.Structure):
     _fields_ = [(f, ctypes.c_void_p) for f in P1_IO_FIELDS] + [
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t), ("events", ctypes.c_void_p),
-        ("pair_stream", ctypes.c_void_p), ("pair_ready", ctypes.c_void_p), ("status", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
         ("gord_k", ctypes.c_void_p)]
 
 

@@ -28,26 +28,51 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
 def command(out: str = LIB) -> list[str]:
-    return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wno-unused-command-line-argument",
-        "-I", INCLUDE, "-I", CSRC, "-o", out,
-    ] + [os.path.join(CSRC, s) for s in SOURCES]
+    """One hipcc call that compiles and links every source (for reference and the CPU tests)."""
+    return [hipcc()] + FLAGS + ["-shared", "-I", INCLUDE, "-I", CSRC, "-o", out] + [os.path.join(CSRC, s) for s in SOURCES]
 
 
 def build(verbose: bool = False) -> str:
-    """Compile the library (always; the caller decides when). Returns its path."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building %s" % LIB)
-    os.replace(tmp, LIB)
+    """Compile the library (always; the caller decides when): each source to an object file in
+    parallel under a private build folder, then one link. Returns its path."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    work = tempfile.mkdtemp(prefix="sdm_build_")
+    try:
+        def compile_one(src):
+            obj = os.path.join(work, src + ".o")
+            cmd = [hipcc()] + FLAGS + ["-c", "-I", INCLUDE, "-I", CSRC, "-o", obj, os.path.join(CSRC, src)]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                sys.stderr.write(res.stdout + res.stderr)
+                raise RuntimeError("hipcc failed compiling %s" % src)
+            return obj
+
+        jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", "0") or 0) or (os.cpu_count() or 1)))
+        with ThreadPoolExecutor(max_workers=jobs) as ex:
+            objs = list(ex.map(compile_one, SOURCES))
+        tmp = LIB + ".tmp%d" % os.getpid()
+        cmd = [hipcc()] + FLAGS + ["-shared", "-o", tmp] + objs
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError("hipcc failed linking %s" % LIB)
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(work, ignore_errors=True)
     return LIB
 
 

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
+#include <mutex>
 #include <string>
 
 #include "sdm.h"
@@ -32,6 +33,38 @@ sdm_status fail(sdm_status s, const char* fmt, ...) {
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Once per device, before the first launch there: the device's LDS bytes per workgroup, and every
+// dynamic-LDS kernel's limit raised to it. Entry points call this after their argument checks and
+// before their first enqueue.
+constexpr int kMaxDevices = 64;
+struct DeviceSetup {
+    std::once_flag once;
+    hipError_t err = hipSuccess;
+    int lds_max = 0;
+};
+DeviceSetup g_setup[kMaxDevices];
+
+hipError_t device_setup(int* lds_max) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    DeviceSetup& d = g_setup[dev];
+    std::call_once(d.once, [&d, dev]() {
+        int lds = 0;
+        d.err = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+        if (d.err != hipSuccess) return;
+        const void* fns[128];
+        int n = sdm::p1_lds_kernels(fns, 128);
+        n += sdm::read_lds_kernels(fns + n, 128 - n);
+        for (int i = 0; i < n && d.err == hipSuccess; ++i)
+            d.err = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        d.lds_max = lds;
+    });
+    if (lds_max != nullptr) *lds_max = d.lds_max;
+    return d.err;
+}
 
 sdm_status check_p1_shape(const sdm_p1_shape* s) {
     if (s == nullptr) return fail(SDM_EINVAL, "sdm_phase1: shape is NULL");
@@ -119,10 +152,9 @@ sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st
         return fail(SDM_EWORKSPACE, "sdm_phase1: workspace needs %zu bytes, got %zu", ws.total,
                     io->workspace == nullptr ? size_t(0) : io->workspace_bytes);
     if (!aligned(io->workspace, 16)) return fail(SDM_EALIGN, "sdm_phase1: workspace is not 16-byte aligned");
-    int dev = 0, lds_max = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
-        return fail(SDM_EHIP, "sdm_phase1: no HIP device");
+    int lds_max = 0;
+    const hipError_t se = device_setup(&lds_max);
+    if (se != hipSuccess) return fail(SDM_EHIP, "sdm_phase1: device set-up: %s", hipGetErrorString(se));
     const size_t main_lds = sdm::p1_lds_bytes(s, io);
     if (main_lds > static_cast<size_t>(lds_max))
         return fail(SDM_EUNSUPPORTED, "sdm_phase1: the sort/scan kernel needs %zu B of LDS per block, the device has %d",
@@ -131,8 +163,6 @@ sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st
     if ((io->a != nullptr || io->qk != nullptr) && tri > static_cast<size_t>(lds_max))
         return fail(SDM_EUNSUPPORTED, "sdm_phase1: the C=%d pair kernel (%zu B) exceeds the %d B of LDS per block", s->C,
                     tri, lds_max);
-    if (io->pair_stream != nullptr && io->pair_ready == nullptr)
-        return fail(SDM_EINVAL, "sdm_phase1: pair_stream needs a pair_ready event");
     sdm::P1Launch L;
     L.s = s;
     L.io = io;
@@ -190,6 +220,8 @@ sdm_status sdm_read_step(const sdm_read_io* io, int64_t ti, hipStream_t st) {
     }
     if (!aligned(io->k_eff, io->val_bytes == 2 ? 2 : 4) || !aligned(io->q_w, io->val_bytes == 2 ? 2 : 4))
         return fail(SDM_EALIGN, "sdm_read_step: k_eff / q_w misaligned for their type");
+    const hipError_t se = device_setup(nullptr);
+    if (se != hipSuccess) return fail(SDM_EHIP, "sdm_read_step: device set-up: %s", hipGetErrorString(se));
     sdm::ReadLaunch L;
     L.io = io;
     L.ti = ti;

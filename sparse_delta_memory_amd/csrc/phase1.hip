@@ -1523,8 +1523,6 @@ hipError_t launch_main(P1Args args, bool lane_gates, bool id64, bool vbf, size_t
     // (The value type is a template parameter: a run-time switch in the staging loads costs the
     // float32 path about a sixth of its time.)
     const void* fn = vbf ? main_fn<IPT, true>(lane_gates, id64) : main_fn<IPT, false>(lane_gates, id64);
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
     void* kargs[] = {&args};
     return hipExtLaunchKernel(fn, dim3(N), dim3(kNT), kargs, lds, st, start, stop, 0);
 }
@@ -1702,21 +1700,36 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     pa.R = s->R;
     pa.first_partial = s->first_partial;
     pa.valid_last = s->valid_last;
-    // The pair kernel on its own stream, after the sort/scan kernel, when the caller gives one.
-    hipStream_t pst = st;
-    if (io->pair_stream != nullptr) {
-        if ((e = hipEventRecord(io->pair_ready, st)) != hipSuccess) return e;
-        if ((e = hipStreamWaitEvent(io->pair_stream, io->pair_ready, 0)) != hipSuccess) return e;
-        pst = io->pair_stream;
-    }
     const size_t lds = pair_lds_layout(s->C, hot_cap, pa.gb).total;
     const int threads = blocks_cu == 1 ? 1024 : 512;
     const void* fn = threads == 1024 ? reinterpret_cast<const void*>(&p1_pairs_kernel<1024>)
                                      : reinterpret_cast<const void*>(&p1_pairs_kernel<512>);
-    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
     void* kargs[] = {&pa};
-    return hipExtLaunchKernel(fn, dim3(s->N, 2), dim3(threads), kargs, lds, pst, ev[2], ev[3], 0);
+    return hipExtLaunchKernel(fn, dim3(s->N, 2), dim3(threads), kargs, lds, st, ev[2], ev[3], 0);
+}
+
+int p1_lds_kernels(const void** fns, int cap) {
+    int n = 0;
+    auto add = [&](const void* f) {
+        if (n < cap) fns[n++] = f;
+    };
+    for (int lg = 0; lg < 2; ++lg) {
+        for (int id64 = 0; id64 < 2; ++id64) {
+            add(main_fn<1, false>(lg, id64));
+            add(main_fn<2, false>(lg, id64));
+            add(main_fn<4, false>(lg, id64));
+            add(main_fn<8, false>(lg, id64));
+            add(main_fn<16, false>(lg, id64));
+            add(main_fn<1, true>(lg, id64));
+            add(main_fn<2, true>(lg, id64));
+            add(main_fn<4, true>(lg, id64));
+            add(main_fn<8, true>(lg, id64));
+            add(main_fn<16, true>(lg, id64));
+        }
+    }
+    add(reinterpret_cast<const void*>(&p1_pairs_kernel<1024>));
+    add(reinterpret_cast<const void*>(&p1_pairs_kernel<512>));
+    return n;
 }
 
 }  // namespace sdm

@@ -401,11 +401,14 @@ hipError_t read_launch(const ReadLaunch& L, hipStream_t st) {
     if (e != hipSuccess) return e;
     const int solve_blocks = a.P * ((a.hd + kMCols - 1) / kMCols);
     const size_t lds = solve_lds_bytes(a.C);
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&read_solve_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(lds));
-    if (e != hipSuccess) return e;
     return hipExtLaunchKernel(reinterpret_cast<const void*>(&read_solve_kernel), dim3(static_cast<unsigned>(solve_blocks)),
                               dim3(256), kargs, lds, st, ev[2], ev[3], 0);
+}
+
+int read_lds_kernels(const void** fns, int cap) {
+    if (cap < 1) return 0;
+    fns[0] = reinterpret_cast<const void*>(&read_solve_kernel);
+    return 1;
 }
 
 }  // namespace sdm

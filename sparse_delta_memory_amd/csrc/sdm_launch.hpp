@@ -16,6 +16,12 @@ constexpr int kP1Threads = 1024;
 // Valid K entries that make a slot group "hot": the pair kernel sums such groups densely.
 constexpr int kHotMin = 16;
 
+// Kernels launched with dynamic LDS, each file listing its own (fills fns, returns the count, at
+// most cap). The ABI raises their dynamic-LDS limit to the device's maximum once per device, before
+// the first launch there, so no launch sequence makes another runtime call between its kernels.
+int p1_lds_kernels(const void** fns, int cap);
+int read_lds_kernels(const void** fns, int cap);
+
 struct P1Launch {
     const sdm_p1_shape* s;
     const sdm_p1_io* io;

@@ -315,3 +315,78 @@ def run_read_check(wl, steps_checked, chunks_per_step=None, dev="cuda"):
                 # masked tokens: exactly zero
                 assert np.all(g[tv:] == 0), name
     return worst
+
+
+U32 = 2.0 ** -24   # unit roundoff of float32
+
+
+def read_fed_tolerance(C, W, R, mag):
+    """Float32 evaluation bound of the read side on exact float32 inputs: each output is a chain of
+    dots (a gather of at most max(W, R) terms, then a forward substitution and products with A and
+    QK of at most C terms) whose every rounding error is propagated by the same triangular
+    recursion that builds the oracle's magnitude bound `mag` (the recursion on absolute values
+    majorizes the inverse of the unit lower triangular system elementwise). So the error is at most
+    gamma_n mag per stage, with n = C + max(W, R); twice that for the two stages that can compound
+    (the blocked substitution applies an inverted diagonal block, then the off-diagonal products)."""
+    n = C + max(W, R)
+    gamma = n * U32 / (1.0 - n * U32)
+    return 2.0 * gamma * mag
+
+
+def run_read_check_fed(wl, steps_checked, dev="cuda"):
+    """The read side fed the ORACLE's Phase-1 quantities (k_eff, q_w, A, QK, each rounded once to
+    float32) instead of the GPU's, so the comparison isolates the read kernels: the oracle's read
+    side is evaluated in float64 on the same float32 inputs and the same pre-step bank rows, and
+    every dv / pred / read element must lie within read_fed_tolerance. Returns the worst error as a
+    fraction of that tolerance."""
+    import torch
+
+    sh = wl.shape
+    P, C, W, R, hd = sh.P, sh.C, sh.W, sh.R, sh.hd
+    shape = shape_of(wl)
+    ins = device_inputs(wl, dev)
+    fed = {"k_eff": np.zeros((wl.N, C, W), np.float32), "q_w": np.zeros((wl.N, C, R), np.float32),
+           "a": np.zeros((wl.N, C, C), np.float32), "qk": np.zeros((wl.N, C, C), np.float32)}
+    chunks = [ti * P + p for ti in steps_checked for p in range(P)]
+    o = oracle_phase1(wl, chunks, fields=["k_eff", "q_w", "a", "qk"])
+    for i, c in enumerate(chunks):
+        for k in fed:
+            fed[k][c] = np.asarray(o[k][i], np.float64).astype(np.float32)
+    p1 = {k: torch.from_numpy(v).to(dev) for k, v in fed.items()}
+    v_host, beta_host = W.make_read_inputs(wl)
+    v = torch.from_numpy(v_host).to(dev)
+    beta = torch.from_numpy(beta_host).to(dev)
+    rows = v.shape[0]
+    dv = torch.full((rows, hd), float("nan"), device=dev)
+    pred = torch.full_like(dv, float("nan"))
+    read = torch.full_like(dv, float("nan"))
+    bank = W.make_bank(wl, dev)
+    plan = sdm.ReadPlan(bank, p1, ins["k_idx"], ins["q_idx"], v, beta, dv, pred, read, shape, step_rows=P * C)
+    for ti in steps_checked:
+        plan.step(ti)
+    torch.cuda.synchronize()
+    worst = 0.0
+    rows_of = lambda s: bank.index_select(0, torch.as_tensor(s, device=dev)).float().cpu().numpy().astype(np.float64)  # noqa: E731
+    for c in chunks:
+        ti, p = divmod(c, P)
+        tv = wl.valid_last if c >= wl.first_partial else C
+        r = read_side.read_step(wl.k_idx[c], wl.q_idx[c], fed["k_eff"][c], fed["q_w"][c], fed["a"][c], fed["qk"][c],
+                                v_host[c * C:(c + 1) * C], beta_host[c], rows_of, tv)
+        sl = slice(ti * P * C + p * C, ti * P * C + (p + 1) * C)
+        for name, got in (("dv", dv), ("pred", pred), ("read", read)):
+            g = got[sl].cpu().numpy().astype(np.float64)
+            want = r[name]
+            tol = read_fed_tolerance(C, W, R, r["mag_" + name])
+            err = np.abs(g - want)
+            bad = ~(err <= tol)
+            if bad.any():
+                i = np.argwhere(bad)[:4]
+                raise AssertionError("%s (oracle-fed) step %d stream %d: %d of %d outside the float32 bound; e.g. %s" % (
+                    name, ti, p, bad.sum(), bad.size,
+                    ", ".join("%s gpu %r oracle %r tol %r" % (tuple(k), g[tuple(k)], want[tuple(k)], tol[tuple(k)])
+                              for k in i)))
+            nz = tol > 0
+            if nz.any():
+                worst = max(worst, float(np.max(err[nz] / tol[nz])))
+            assert np.all(g[tv:] == 0), name
+    return worst

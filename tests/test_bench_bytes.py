@@ -26,3 +26,14 @@ def test_dw_bytes_per_step():
 def test_read_side_bytes():
     assert bench.read_gather_bytes(8, 128, 16, 16, 128, 2) == 8 * 128 * 32 * (256 + 8) + 2 * 8 * 128 * 128 * 4
     assert bench.read_solve_bytes(8, 128, 128) == 2 * 8 * 128 * 128 * 4 + 6 * 8 * 128 * 128 * 4 + 8 * 128 * 4
+
+
+def test_backward_bytes_count_token_rows_once():
+    # Workload 1's shape: P = 8, C = 128, W = R = 16, hd = 128, bf16 bank and gradient rows.
+    P, C, W, R, hd = 8, 128, 16, 16, 128
+    gq = 8 * 2000
+    assert bench.gds_bytes(P, C, R, hd, 2, gq, 2) == (P * C * R * (hd * 2 + 12) + P * C * R * 12 + 2 * gq * hd * 2
+                                                      + P * C * hd * 4)
+    assert bench.gwr_bytes(P, C, W, hd, 2) == P * C * W * (hd * 2 + 12) + 2 * P * C * hd * 4
+    g = 8 * 2015
+    assert bench.pa_bytes(P, C, W, hd, g, 2, 2) == P * C * W * 36 + g * hd * 8 + P * C * hd * 4

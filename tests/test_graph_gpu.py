@@ -121,37 +121,6 @@ def test_kernel_bound_events():
         sdm.phase1(shape, events=[torch.cuda.Event(enable_timing=True) for _ in range(4)], **ins)
 
 
-def test_pair_stream_matches_one_stream():
-    """The pair kernel on its own stream (beside DW steps on the main stream) gives the same bits."""
-    wl = W.make(2, steps=2)
-    sh = wl.shape
-    shape = H.shape_of(wl)
-    ins = H.device_inputs(wl)
-    dv = H.device_dv(wl)
-    ref_out = sdm.phase1(shape, **ins)
-    ref_bank = W.make_bank(wl, "cuda")
-    for ti in range(wl.steps):
-        sdm.dw_step(ref_bank, dv, ref_out["krec"], shape, ti, dv_step_rows=wl.P * sh.C)
-    torch.cuda.synchronize()
-    main = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
-    ready, joined = torch.cuda.Event(), torch.cuda.Event()
-    ready.record(main)
-    out = sdm.alloc_phase1_outputs(shape, device="cuda")
-    for t in out.values():
-        t.view(torch.uint8).fill_(0xA5)
-    bank = W.make_bank(wl, "cuda")
-    sdm.phase1(shape, out=out, pair_stream=side, pair_ready=ready, **ins)
-    for ti in range(wl.steps):
-        sdm.dw_step(bank, dv, out["krec"], shape, ti, dv_step_rows=wl.P * sh.C)
-    joined.record(side)
-    main.wait_event(joined)
-    torch.cuda.synchronize()
-    for k in ref_out:
-        assert torch.equal(out[k].view(torch.uint8), ref_out[k].view(torch.uint8)), k
-    assert torch.equal(bank.view(torch.uint8), ref_bank.view(torch.uint8))
-
-
 def test_graph_forward_loop_with_read_side():
     """Phase 1 and, step after step, the read side then DW (the read side's dv feeding DW), captured
     once and replayed: every replay equals the eager loop bit for bit."""

@@ -119,11 +119,16 @@ def test_sort_matches_brute_force_and_lexsort(seed):
 @pytest.mark.parametrize("seed,lane_gates", [(4, False), (5, False), (41, True), (42, True)])
 def test_scan_fields_match_brute_force(seed, lane_gates):
     d = tiny(seed, N=2, C=11, W=4, R=3, S=6, P=2, valid_last=7, lane_gates=lane_gates)
-    o = run_oracle(d)
+    o = run_oracle(d, fields=list(oracle._OUT_FIELDS))
     C, W = d["k_idx"].shape[1:]
     R = d["q_idx"].shape[2]
     for c in range(2):
         E, res = brute(d, c)
+        # repeats: valid K entries whose token writes the same slot from a lower K lane (so the
+        # entry before it in its group is a K entry of its own token, and its gate is not applied).
+        reps = sum(1 for e in E if e["valid"] and not e["q"] and any(
+            f["valid"] and not f["q"] and f["t"] == e["t"] and f["s"] == e["s"] and f["lane"] < e["lane"] for f in E))
+        assert int(o["repeats"][c]) == reps
         for e, b in zip(E, res):
             o_idx = (e["t"], e["lane"])
             packed = b["rho"]

@@ -148,7 +148,10 @@ def test_masked_tokens_do_not_leak():
     dict(C=37, W=5, R=3, S=9, P=2, steps=2, vl=11),       # ragged row (296 entries), heavy sharing
     dict(C=1, W=1, R=1, S=4, P=1, steps=3, vl=None),      # one token
     dict(C=64, W=2, R=3, S=1, P=1, steps=2, vl=0),        # one slot; last chunk fully masked
-    dict(C=256, W=17, R=3, S=1, P=1, steps=1, vl=None),   # one group of 5120: saturated counts
+    # One group of 5120 entries: saturated counts. The only stress shape: its cells sum up to 289
+    # terms that cancel (a 289-term cell of about 0.13 differs by 2.7e-6 in any float32 summation),
+    # so A / QK take the float32 evaluation bound there (hip_harness.assert_pair_sums).
+    dict(C=256, W=17, R=3, S=1, P=1, steps=1, vl=None, stress=True),
     dict(C=100, W=7, R=9, S=3000, P=3, steps=2, vl=50),   # 1600 entries: two radix tiles
     # An odd K row (8415 positions) in a DW launch wide enough for two positions per team of lanes.
     dict(C=255, W=33, R=2, S=5000, P=1, steps=1, vl=None, hd=960, bank="bf16"),
@@ -168,7 +171,7 @@ def test_edge_shapes(case):
     wl = W.make(sh, seed=777)
     say("edge shape", case)
     shape, out = H.run_phase1(wl)
-    ref = H.oracle_phase1(wl, list(range(wl.N)), with_magnitudes=True)
+    ref = H.oracle_phase1(wl, list(range(wl.N)), with_magnitudes=case.get("stress", False))
     H.compare_phase1(out, ref, range(wl.N))
     H.run_dw_check(wl, out, shape, set(range(wl.steps)), sample_untouched=0)
 
@@ -207,7 +210,7 @@ def test_lane_gates(case):
     say("lane gates", case)
     shape, out = H.run_phase1(wl)
     chunks = list(range(min(wl.N, 16)))
-    ref = H.oracle_phase1(wl, chunks, with_magnitudes=True)
+    ref = H.oracle_phase1(wl, chunks)
     H.compare_phase1(out, ref, chunks)
     H.run_dw_check(wl, out, shape, set(range(min(wl.steps, 2))), sample_untouched=0)
 
@@ -234,7 +237,7 @@ def test_bf16_values(case):
     shape, out = H.run_phase1(wl)
     assert out["k_eff"].dtype == torch.bfloat16 and out["cpe"].dtype == torch.bfloat16
     chunks = list(range(min(wl.N, 12))) + ([wl.N - 1] if wl.N > 12 else [])
-    ref = H.oracle_phase1(wl, chunks, with_magnitudes=True)
+    ref = H.oracle_phase1(wl, chunks)
     H.compare_phase1(out, ref, chunks)
     # The float32-value path on the same values: identical except the value-typed fields.
     f32_wl = W.Workload(**{**wl.__dict__, "meta": {k: v for k, v in wl.meta.items() if k != "val_bf16"}})

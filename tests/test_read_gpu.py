@@ -111,3 +111,25 @@ def test_read_side_bf16_weights(idx, steps):
     for a, b in zip(res[0], res[1]):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
     assert torch.isfinite(res[0][0]).all() and torch.isfinite(res[0][2]).all()   # (masked tokens: 0)
+
+
+@pytest.mark.parametrize("idx,steps,checked,case", [
+    (0, None, [0, 3], None), (1, 2, [1], None), (2, 1, [0], None), (3, 1, [0], None), (4, 64, [63], None),
+    (None, 2, [0, 1], dict(C=37, W=5, R=3, S=9, P=2, vl=11)),             # heavy sharing, ragged
+    (None, 1, [0], dict(C=256, W=8, R=8, S=48, P=1, vl=None)),            # dense A and QK
+    (None, 2, [0, 1], dict(C=64, W=4, R=3, S=40, P=2, vl=21, hd=37, bank="bf16")),
+])
+def test_read_side_oracle_fed(idx, steps, checked, case):
+    """The read kernels alone: fed the oracle's float32-rounded k_eff, q_w, A and QK, dv / pred /
+    read are within the float32 evaluation bound of the oracle's float64 read side on those same
+    inputs (hip_harness.read_fed_tolerance), so no Phase-1 error is in the comparison."""
+    if case is None:
+        wl = W.make(idx, steps=steps)
+    else:
+        sh = W.Shape("read_fed", P=case["P"], T=case["C"] * steps, C=case["C"], W=case["W"], R=case["R"],
+                     S=case["S"], hd=case.get("hd", 64), bank_dtype=case.get("bank", "f32"), dv_dtype="f32",
+                     slots="uniform", valid_last=case["vl"])
+        wl = W.make(sh, seed=785)
+    say("read side, oracle-fed:", idx, case, "steps", checked)
+    worst = H.run_read_check_fed(wl, checked)
+    say("worst error as a fraction of the bound %.3g" % worst)
