@@ -58,8 +58,15 @@ hipError_t device_setup(int* lds_max) {
         const void* fns[128];
         int n = sdm::p1_lds_kernels(fns, 128);
         n += sdm::read_lds_kernels(fns + n, 128 - n);
-        for (int i = 0; i < n && d.err == hipSuccess; ++i)
-            d.err = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        for (int i = 0; i < n && d.err == hipSuccess; ++i) {
+            // The dynamic limit is what the device holds beside the kernel's static LDS.
+            hipFuncAttributes fa;
+            d.err = hipFuncGetAttributes(&fa, fns[i]);
+            if (d.err != hipSuccess) break;
+            const int dyn = lds - static_cast<int>(fa.sharedSizeBytes);
+            if (dyn > 0) d.err = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
+        }
+        if (d.err != hipSuccess) (void)hipGetLastError();   // reported through the status, not left pending
         d.lds_max = lds;
     });
     if (lds_max != nullptr) *lds_max = d.lds_max;
