@@ -223,7 +223,9 @@ typedef struct sdm_dw_io {
                                groups in rows 0 .. groups - 1 of its C * W rows */
 } sdm_dw_io;
 
-/* Workspace bytes sdm_dw_step can use for this shape (P * C * W * (4 * hd + 12), rounded). */
+/* Workspace bytes sdm_dw_step can use for this shape: per block of 32 K-row positions of the step
+   (B = ceil(P * C * W / 32) blocks) an arrival counter and a metadata pair (12 B) and two float32
+   partial rows (8 hd B), each region rounded up to 256 bytes. */
 size_t sdm_dw_workspace(const sdm_dw_io* io);
 
 /*

@@ -101,6 +101,59 @@ sdm_status check_p1_shape(const sdm_p1_shape* s) {
     return SDM_OK;
 }
 
+sdm_status check_dw_io(const sdm_dw_io* io, int64_t ti, const char* fn) {
+    if (io->C < 1 || io->C > 256 || io->W < 1 || io->W > 256)
+        return fail(SDM_ESHAPE, "%s: C = %d, W = %d outside 1..256", fn, io->C, io->W);
+    if (io->P < 1 || io->N < 0) return fail(SDM_ESHAPE, "%s: P = %d, N = %d", fn, io->P, io->N);
+    if (static_cast<int64_t>(io->P) * io->C * io->W > (int64_t(1) << 30))
+        return fail(SDM_ESHAPE, "%s: P*C*W = %lld > 2^30 positions per step", fn,
+                    static_cast<long long>(static_cast<int64_t>(io->P) * io->C * io->W));
+    if (ti < 0 || (ti + 1) * static_cast<int64_t>(io->P) > io->N)
+        return fail(SDM_ESHAPE, "%s: step %lld needs (ti+1)*P <= N = %d", fn, static_cast<long long>(ti), io->N);
+    if (io->bank_dtype != SDM_F32 && io->bank_dtype != SDM_BF16)
+        return fail(SDM_EINVAL, "%s: bank_dtype %d", fn, io->bank_dtype);
+    if (io->dv_dtype != SDM_F32 && io->dv_dtype != SDM_BF16)
+        return fail(SDM_EINVAL, "%s: dv_dtype %d", fn, io->dv_dtype);
+    if (io->hd < 1 || io->hd > 4096) return fail(SDM_ESHAPE, "%s: hd = %d outside 1..4096", fn, io->hd);
+    if (sdm::dw_cols_per_lane(io->hd) == 0)
+        return fail(SDM_EUNSUPPORTED, "%s: hd = %d (this build: up to 1024)", fn, io->hd);
+    if (io->rows < 1 || io->dv_step_rows < 0 || io->dv_rows < 0)
+        return fail(SDM_EINVAL, "%s: rows / dv_step_rows / dv_rows", fn);
+    if (ti * io->dv_step_rows + static_cast<int64_t>(io->P) * io->C > io->dv_rows)
+        return fail(SDM_EINVAL, "%s: dv holds %lld rows, step %lld needs %lld", fn, static_cast<long long>(io->dv_rows),
+                    static_cast<long long>(ti), static_cast<long long>(ti * io->dv_step_rows + static_cast<int64_t>(io->P) * io->C));
+    if (io->bank == nullptr || io->dv == nullptr || io->krec == nullptr)
+        return fail(SDM_EINVAL, "%s: bank, dv and krec are required", fn);
+    // Head dims that 16-byte vectors divide (multiples of 8 up to 512, of 16 up to 1024) use vector
+    // accesses and need 16-byte aligned rows; any other takes element accesses (element alignment).
+    const bool tail = sdm::dw_tail(io->hd);
+    const int bank_es = io->bank_dtype == SDM_BF16 ? 2 : 4;
+    const int dv_es = io->dv_dtype == SDM_BF16 ? 2 : 4;
+    if (!aligned(io->krec, 16)) return fail(SDM_EALIGN, "%s: krec must be 16-byte aligned", fn);
+    if (!aligned(io->bank, tail ? bank_es : 16) || !aligned(io->dv, tail ? dv_es : 16))
+        return fail(SDM_EALIGN, "%s: bank and dv must be %s aligned", fn, tail ? "element" : "16-byte");
+    if (io->workspace != nullptr) {
+        if (!aligned(io->workspace, 16)) return fail(SDM_EALIGN, "%s: workspace is not 16-byte aligned", fn);
+        const size_t need = sdm::dw_workspace_layout(io).total;
+        if (io->workspace_bytes < need)
+            return fail(SDM_EWORKSPACE, "%s: workspace needs %zu bytes, got %zu", fn, need, io->workspace_bytes);
+    }
+    if (io->snap != nullptr) {
+        if (io->snap_dtype != io->bank_dtype && !(io->snap_dtype == SDM_BF16 && io->bank_dtype == SDM_F32))
+            return fail(SDM_EINVAL, "%s: snap_dtype %d (the bank's, or bf16 rows of a float32 bank)", fn,
+                        io->snap_dtype);
+        if (!aligned(io->snap_ord, 4)) return fail(SDM_EALIGN, "%s: snap_ord is misaligned", fn);
+        const int snap_es = io->snap_dtype == SDM_BF16 ? 2 : bank_es;
+        if (!aligned(io->snap, tail ? snap_es : 16)) return fail(SDM_EALIGN, "%s: snap is misaligned", fn);
+        const int64_t pcw = static_cast<int64_t>(io->P) * io->C * io->W;
+        if (io->snap_step_rows < 0 || ti * io->snap_step_rows + pcw > io->snap_rows)
+            return fail(SDM_EINVAL, "%s: snap holds %lld rows, step %lld needs %lld", fn,
+                        static_cast<long long>(io->snap_rows), static_cast<long long>(ti),
+                        static_cast<long long>(ti * io->snap_step_rows + pcw));
+    }
+    return SDM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -348,55 +401,8 @@ sdm_status sdm_pa_step(const sdm_pa_io* io, int64_t ti, hipStream_t st) {
 sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st) {
     g_last_error.clear();
     if (io == nullptr) return fail(SDM_EINVAL, "sdm_dw_step: io is NULL");
-    if (io->C < 1 || io->C > 256 || io->W < 1 || io->W > 256)
-        return fail(SDM_ESHAPE, "sdm_dw_step: C = %d, W = %d outside 1..256", io->C, io->W);
-    if (io->P < 1 || io->N < 0) return fail(SDM_ESHAPE, "sdm_dw_step: P = %d, N = %d", io->P, io->N);
-    if (static_cast<int64_t>(io->P) * io->C * io->W > (int64_t(1) << 30))
-        return fail(SDM_ESHAPE, "sdm_dw_step: P*C*W = %lld > 2^30 positions per step",
-                    static_cast<long long>(static_cast<int64_t>(io->P) * io->C * io->W));
-    if (ti < 0 || (ti + 1) * static_cast<int64_t>(io->P) > io->N)
-        return fail(SDM_ESHAPE, "sdm_dw_step: step %lld needs (ti+1)*P <= N = %d", static_cast<long long>(ti), io->N);
-    if (io->bank_dtype != SDM_F32 && io->bank_dtype != SDM_BF16)
-        return fail(SDM_EINVAL, "sdm_dw_step: bank_dtype %d", io->bank_dtype);
-    if (io->dv_dtype != SDM_F32 && io->dv_dtype != SDM_BF16)
-        return fail(SDM_EINVAL, "sdm_dw_step: dv_dtype %d", io->dv_dtype);
-    if (io->hd < 1 || io->hd > 4096) return fail(SDM_ESHAPE, "sdm_dw_step: hd = %d outside 1..4096", io->hd);
-    if (sdm::dw_cols_per_lane(io->hd) == 0)
-        return fail(SDM_EUNSUPPORTED, "sdm_dw_step: hd = %d (this build: up to 1024)", io->hd);
-    if (io->rows < 1 || io->dv_step_rows < 0 || io->dv_rows < 0)
-        return fail(SDM_EINVAL, "sdm_dw_step: rows / dv_step_rows / dv_rows");
-    if (ti * io->dv_step_rows + static_cast<int64_t>(io->P) * io->C > io->dv_rows)
-        return fail(SDM_EINVAL, "sdm_dw_step: dv holds %lld rows, step %lld needs %lld", static_cast<long long>(io->dv_rows),
-                    static_cast<long long>(ti), static_cast<long long>(ti * io->dv_step_rows + static_cast<int64_t>(io->P) * io->C));
-    if (io->bank == nullptr || io->dv == nullptr || io->krec == nullptr)
-        return fail(SDM_EINVAL, "sdm_dw_step: bank, dv and krec are required");
-    // Head dims that 16-byte vectors divide (multiples of 8 up to 512, of 16 up to 1024) use vector
-    // accesses and need 16-byte aligned rows; any other takes element accesses (element alignment).
-    const bool tail = sdm::dw_tail(io->hd);
-    const int bank_es = io->bank_dtype == SDM_BF16 ? 2 : 4;
-    const int dv_es = io->dv_dtype == SDM_BF16 ? 2 : 4;
-    if (!aligned(io->krec, 16)) return fail(SDM_EALIGN, "sdm_dw_step: krec must be 16-byte aligned");
-    if (!aligned(io->bank, tail ? bank_es : 16) || !aligned(io->dv, tail ? dv_es : 16))
-        return fail(SDM_EALIGN, "sdm_dw_step: bank and dv must be %s aligned", tail ? "element" : "16-byte");
-    if (io->workspace != nullptr) {
-        if (!aligned(io->workspace, 16)) return fail(SDM_EALIGN, "sdm_dw_step: workspace is not 16-byte aligned");
-        const size_t need = sdm::dw_workspace_layout(io).total;
-        if (io->workspace_bytes < need)
-            return fail(SDM_EWORKSPACE, "sdm_dw_step: workspace needs %zu bytes, got %zu", need, io->workspace_bytes);
-    }
-    if (io->snap != nullptr) {
-        if (io->snap_dtype != io->bank_dtype && !(io->snap_dtype == SDM_BF16 && io->bank_dtype == SDM_F32))
-            return fail(SDM_EINVAL, "sdm_dw_step: snap_dtype %d (the bank's, or bf16 rows of a float32 bank)",
-                        io->snap_dtype);
-        if (!aligned(io->snap_ord, 4)) return fail(SDM_EALIGN, "sdm_dw_step: snap_ord is misaligned");
-        const int snap_es = io->snap_dtype == SDM_BF16 ? 2 : bank_es;
-        if (!aligned(io->snap, tail ? snap_es : 16)) return fail(SDM_EALIGN, "sdm_dw_step: snap is misaligned");
-        const int64_t pcw = static_cast<int64_t>(io->P) * io->C * io->W;
-        if (io->snap_step_rows < 0 || ti * io->snap_step_rows + pcw > io->snap_rows)
-            return fail(SDM_EINVAL, "sdm_dw_step: snap holds %lld rows, step %lld needs %lld",
-                        static_cast<long long>(io->snap_rows), static_cast<long long>(ti),
-                        static_cast<long long>(ti * io->snap_step_rows + pcw));
-    }
+    const sdm_status rc = check_dw_io(io, ti, "sdm_dw_step");
+    if (rc != SDM_OK) return rc;
     sdm::DwLaunch L;
     L.io = io;
     L.ti = ti;

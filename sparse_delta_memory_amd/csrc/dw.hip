@@ -28,9 +28,9 @@ struct DwArgs {
     int64_t dv_row0;   // ti * dv_step_rows
     int64_t chunk0;    // ti * P
     int64_t rows;      // bank rows
-    float* part;       // split groups: one partial row per K-row position (NULL: groups are not split)
-    int* cnt;          // per group FIRST: arrival counter, zero between calls
-    int2* meta;        // per group FIRST: {segments, cpe bits of LAST}
+    float* part;       // split groups: partial rows, two per block of 32 K-row positions (NULL: groups are not split)
+    int* cnt;          // per block of 32 positions (a split group's FIRST): arrival counter, zero between calls
+    int2* meta;        // per block of 32 positions (a split group's FIRST): {segments, cpe bits of LAST}
     void* snap;        // compact snapshot (NULL: none): row snap_row0 + p * CW + j_FIRST <- the group's pre-write row
     int64_t snap_row0; // ti * snap_step_rows
     int P, C, CW, hd, ts_log2, teams_per_block;
@@ -185,6 +185,17 @@ __device__ __forceinline__ void snap_store(const DwArgs& a, int64_t row, int col
 // in-group distance that still marks a segment start (the distance field saturates at 4095).
 constexpr int kSeg = 32;
 constexpr int kSegLimit = (4095 / kSeg) * kSeg;
+
+// Workspace slots of split groups, by step-wide K-row position G (stream p's position j is
+// p * CW + j). A split group has more than kSeg members, so two split groups' FIRSTs are more than
+// kSeg apart: at most one falls in each aligned block of kSeg positions, which indexes the group's
+// counter and metadata. Its segments start at FIRST + kSeg k; in one block there is at most one
+// later segment start (k >= 1, of the group running through the block) and at most one first
+// segment (k = 0, of a group starting there): two partial rows per block.
+__device__ __forceinline__ int64_t seg_group_slot(int64_t g_first) { return g_first / kSeg; }
+__device__ __forceinline__ int64_t seg_part_row(int64_t g_start, bool first_segment) {
+    return 2 * (g_start / kSeg) + (first_segment ? 0 : 1);
+}
 
 // The general walk of the team at K-row position j of stream p (record r0, valid): a group's FIRST
 // or, when groups are split, a segment start; other positions return at once. The members after
@@ -354,8 +365,8 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
     // loads after seeing the last arrival.
     const int64_t prow = static_cast<int64_t>(p) * a.CW;
     const int first_pos = j - dist;
-    const int64_t gslot = prow + first_pos;
-    float* part = a.part + (prow + j) * a.hd;
+    const int64_t gslot = seg_group_slot(prow + first_pos);
+    float* part = a.part + seg_part_row(prow + j, dist == 0) * a.hd;
 #pragma unroll
     for (int q = 0; q < CPL; ++q) {
         if (!TAIL || q < nv) __hip_atomic_store(part + col0 + q, acc[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -392,7 +403,10 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
         float pv[kPartBatch][CPL];
 #pragma unroll
         for (int b = 0; b < kPartBatch; ++b) {
-            const float* pp = a.part + (prow + min(first_pos + (sg0 + b) * kSeg, a.CW - 1)) * a.hd + col0;
+            // (before the count has arrived, a segment past it reads a row of this block range,
+            // clamped to the stream's row, and is dropped)
+            const int sgb = sg0 + b;
+            const float* pp = a.part + seg_part_row(prow + min(first_pos + sgb * kSeg, a.CW - 1), sgb == 0) * a.hd + col0;
 #pragma unroll
             for (int q = 0; q < CPL; ++q) {
                 pv[b][q] = (!TAIL || q < nv) ? __hip_atomic_load(pp + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.0f;
@@ -433,7 +447,8 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
     const int team = threadIdx.x >> a.ts_log2;
     const int tl = threadIdx.x & ((1 << a.ts_log2) - 1);
     const int total = a.P * a.CW;   // < 2^31 (host checked)
-    const int J0 = (static_cast<int>(blockIdx.x) * a.teams_per_block + team) * U;
+    // Positions by logical block: a stream's K row runs on one XCD, whose L2 then holds its token rows.
+    const int J0 = (xcd_block(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x)) * a.teams_per_block + team) * U;
     if (J0 >= total) return;
     const int col0 = tl * CPL;
     if (col0 >= a.hd) return;   // lanes past the row (the team's lane 0 always stays)
@@ -552,12 +567,14 @@ hipError_t launch_dw_types(const DwArgs& a, bool bank_bf16, bool dv_bf16, bool t
 
 DwWorkspace dw_workspace_layout(const sdm_dw_io* io) {
     const size_t pos = static_cast<size_t>(io->P) * static_cast<size_t>(io->C) * static_cast<size_t>(io->W);
+    const size_t blocks = (pos + kSeg - 1) / kSeg;
     auto up = [](size_t b) { return (b + 255) / 256 * 256; };
     DwWorkspace w;
     w.cnt_off = 0;
-    w.meta_off = up(pos * sizeof(int));
-    w.part_off = w.meta_off + up(pos * sizeof(int2));
-    w.total = w.part_off + up(pos * static_cast<size_t>(io->hd) * sizeof(float));
+    w.cnt_bytes = blocks * sizeof(int);
+    w.meta_off = up(w.cnt_bytes);
+    w.part_off = w.meta_off + up(blocks * sizeof(int2));
+    w.total = w.part_off + up(2 * blocks * static_cast<size_t>(io->hd) * sizeof(float));
     return w;
 }
 
@@ -571,7 +588,9 @@ int dw_cols_per_lane(int hd) {
 
 bool dw_tail(int hd) { return !(hd % 8 == 0 && hd <= 8 * kWave) && !(hd % 16 == 0 && hd <= 16 * kWave); }
 
-hipError_t dw_launch(const DwLaunch& Lc, hipStream_t st) {
+namespace {
+
+hipError_t dw_launch_ws(const DwLaunch& Lc, hipStream_t st, int* cnt, int2* meta, float* part) {
     const sdm_dw_io* io = Lc.io;
     DwArgs a;
     a.bank = io->bank;
@@ -580,18 +599,12 @@ hipError_t dw_launch(const DwLaunch& Lc, hipStream_t st) {
     a.dv_row0 = Lc.ti * io->dv_step_rows;
     a.chunk0 = Lc.ti * io->P;
     a.rows = io->rows;
-    a.part = nullptr;
-    a.cnt = nullptr;
-    a.meta = nullptr;
+    a.part = part;
+    a.cnt = cnt;
+    a.meta = meta;
     a.snap = io->snap;
     a.snap_row0 = Lc.ti * io->snap_step_rows;
     a.snap_ord = io->snap_ord;
-    if (io->workspace != nullptr) {
-        const DwWorkspace w = dw_workspace_layout(io);
-        a.part = reinterpret_cast<float*>(static_cast<char*>(io->workspace) + w.part_off);
-        a.cnt = reinterpret_cast<int*>(static_cast<char*>(io->workspace) + w.cnt_off);
-        a.meta = reinterpret_cast<int2*>(static_cast<char*>(io->workspace) + w.meta_off);
-    }
     a.P = io->P;
     a.C = io->C;
     a.CW = io->C * io->W;
@@ -610,6 +623,17 @@ hipError_t dw_launch(const DwLaunch& Lc, hipStream_t st) {
     const bool sbf = io->snap_dtype == SDM_BF16;
     if (cpl == 8) return launch_dw_types<8>(a, bb, db, tail, sbf, st, ev);
     return launch_dw_types<16>(a, bb, db, tail, sbf, st, ev);
+}
+
+}  // namespace
+
+hipError_t dw_launch(const DwLaunch& Lc, hipStream_t st) {
+    const sdm_dw_io* io = Lc.io;
+    if (io->workspace == nullptr) return dw_launch_ws(Lc, st, nullptr, nullptr, nullptr);
+    const DwWorkspace w = dw_workspace_layout(io);
+    char* ws = static_cast<char*>(io->workspace);
+    return dw_launch_ws(Lc, st, reinterpret_cast<int*>(ws + w.cnt_off), reinterpret_cast<int2*>(ws + w.meta_off),
+                        reinterpret_cast<float*>(ws + w.part_off));
 }
 
 }  // namespace sdm

@@ -45,6 +45,20 @@ __device__ __forceinline__ float load_val(const void* p, int64_t i, int bf) {
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
 
+// The compute dies (XCDs) of the device: a launch's workgroups are dealt to them in turn
+// (workgroup b runs on XCD b % kXcds), and each has its own L2.
+constexpr int kXcds = 8;
+
+// Logical block of workgroup b among nb: consecutive logical blocks run on one XCD, so work laid
+// out by logical block keeps neighbouring data (rows that several blocks read) in one L2. XCD x
+// takes the logical blocks [x q + min(x, r), ...) of length q + (x < r), with q = nb / 8,
+// r = nb % 8: a bijection of [0, nb).
+__device__ __forceinline__ int xcd_block(int b, int nb) {
+    const int x = b % kXcds, k = b / kXcds;
+    const int q = nb / kXcds, r = nb % kXcds;
+    return x * q + min(x, r) + k;
+}
+
 // Barrier for LDS hazards only: LDS operations complete, global stores may stay in flight.
 __device__ __forceinline__ void lds_barrier() {
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");

@@ -57,9 +57,11 @@ struct DwLaunch {
 
 hipError_t dw_launch(const DwLaunch& L, hipStream_t st);
 
-// Workspace of sdm_dw_step: arrival counters (zero between calls), group metadata, partial rows.
+
+// Workspace of sdm_dw_step: per block of 32 K-row positions an arrival counter (zero between
+// calls) and group metadata, and two partial rows.
 struct DwWorkspace {
-    size_t cnt_off, meta_off, part_off, total;
+    size_t cnt_off, cnt_bytes, meta_off, part_off, total;
 };
 DwWorkspace dw_workspace_layout(const sdm_dw_io* io);
 

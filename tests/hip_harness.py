@@ -262,7 +262,7 @@ def run_dw_check(wl: W.Workload, out, shape, check_steps, dev="cuda", sample_unt
         assert torch.equal(bank.index_select(0, idx), init), "untouched rows changed"
     if ws is not None:   # the split path leaves its counters at zero
         torch.cuda.synchronize()
-        cnt_bytes = shape.P * shape.C * shape.W * 4
+        cnt_bytes = (shape.P * shape.C * shape.W + 31) // 32 * 4   # one counter per block of 32 positions
         assert int(ws[:cnt_bytes].view(torch.int32).abs().sum()) == 0, "DW arrival counters not reset"
     return compared, bank
 
@@ -342,10 +342,10 @@ def run_read_check_fed(wl, steps_checked, dev="cuda"):
     import torch
 
     sh = wl.shape
-    P, C, W, R, hd = sh.P, sh.C, sh.W, sh.R, sh.hd
+    P, C, Wn, R, hd = sh.P, sh.C, sh.W, sh.R, sh.hd
     shape = shape_of(wl)
     ins = device_inputs(wl, dev)
-    fed = {"k_eff": np.zeros((wl.N, C, W), np.float32), "q_w": np.zeros((wl.N, C, R), np.float32),
+    fed = {"k_eff": np.zeros((wl.N, C, Wn), np.float32), "q_w": np.zeros((wl.N, C, R), np.float32),
            "a": np.zeros((wl.N, C, C), np.float32), "qk": np.zeros((wl.N, C, C), np.float32)}
     chunks = [ti * P + p for ti in steps_checked for p in range(P)]
     o = oracle_phase1(wl, chunks, fields=["k_eff", "q_w", "a", "qk"])
@@ -376,7 +376,7 @@ def run_read_check_fed(wl, steps_checked, dev="cuda"):
         for name, got in (("dv", dv), ("pred", pred), ("read", read)):
             g = got[sl].cpu().numpy().astype(np.float64)
             want = r[name]
-            tol = read_fed_tolerance(C, W, R, r["mag_" + name])
+            tol = read_fed_tolerance(C, Wn, R, r["mag_" + name])
             err = np.abs(g - want)
             bad = ~(err <= tol)
             if bad.any():

@@ -136,7 +136,9 @@ def test_dw_workspace_size():
     lib = _lib.load()
     o = dw(P=2, C=64, W=4, hd=128)
     need = lib.sdm_dw_workspace(ctypes.byref(o))
-    assert need >= 2 * 64 * 4 * (4 * 128 + 12)
+    blocks = (2 * 64 * 4 + 31) // 32   # one counter, one metadata pair and two partial rows per 32 positions
+    up = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    assert need == up(4 * blocks) + up(8 * blocks) + up(2 * blocks * 128 * 4)
     assert lib.sdm_dw_workspace(ctypes.byref(dw(P=0))) == 0
 
 
