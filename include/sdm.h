@@ -243,6 +243,21 @@ size_t sdm_dw_workspace(const sdm_dw_io* io);
  */
 sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st);
 
+/*
+ * sdm_dw_step for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same step, the same kernels and the same
+ * bits as sdm_dw_step with a workspace, but the split-group workspace is a fixed 16 MiB array
+ * inside the library (one copy per device, held until the process ends). io->workspace must be
+ * NULL. Each call first clears the counters it uses (a small fill kernel on st), then enqueues the
+ * step; it calls no allocating routine. Limits: P*C*W <= 4194304 K-row positions per step, and
+ * 8 * hd * ceil(P*C*W / 32) bytes of partial rows <= 14.5 MiB (every workload shape up to
+ * P*C*W = 131072 at hd = 128, or 8192 at hd = 960, fits); larger steps are refused with
+ * SDM_EWORKSPACE before anything is enqueued. All calls on one device share the array: calls
+ * that may overlap on one device (different streams without ordering, several host threads)
+ * race and must be serialized by the caller.
+ */
+sdm_status sdm_dw_step_noalloc(const sdm_dw_io* io, int64_t ti, hipStream_t st);
+
 /* One read-side step: the chunks ti*P .. ti*P + P - 1, before their DW step. */
 typedef struct sdm_read_io {
     const void* bank;       /* [rows, hd] SDM_F32 or SDM_BF16: the memory BEFORE this step's DW (read only) */

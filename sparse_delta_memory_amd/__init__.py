@@ -153,12 +153,17 @@ class DwPlan:
     without it every group is walked by one team of lanes); snapshot (optional) [*, hd] in the bank
     dtype, or bfloat16 with a float32 bank (rows rounded to bfloat16): row ti*snap_step_rows + p*C*W + j
     receives the pre-write row of the group whose FIRST is at K-row position j, or, with snap_ord (the
-    Phase-1 output gord_k), row ti*snap_step_rows + p*C*W + (the group's dense ordinal). The plan
-    keeps the tensors alive."""
+    Phase-1 output gord_k), row ti*snap_step_rows + p*C*W + (the group's dense ordinal). noalloc:
+    step through sdm_dw_step_noalloc (the split workspace is the library's fixed device array; no
+    workspace argument). The plan keeps the tensors alive."""
 
     def __init__(self, bank, dv, krec, shape: P1Shape, dv_step_rows: int, workspace=None, snapshot=None,
-                 snap_step_rows: int = 0, snap_ord=None):
+                 snap_step_rows: int = 0, snap_ord=None, noalloc: bool = False):
         import torch
+
+        if noalloc and workspace is not None:
+            raise ValueError("DwPlan: noalloc uses the library's fixed workspace; pass no workspace")
+        self._noalloc = bool(noalloc)
 
         if bank.dtype not in (torch.float32, torch.bfloat16) or dv.dtype not in (torch.float32, torch.bfloat16):
             raise TypeError("DwPlan: bank and dv must be float32 or bfloat16")
@@ -203,7 +208,8 @@ class DwPlan:
         arr = _event_array(events, 2, "DwPlan.step")
         self.io.events = None if arr is None else ctypes.cast(arr, ctypes.c_void_p).value
         try:
-            _lib.check(self._lib.sdm_dw_step(self._io_ref, int(ti), ctypes.c_void_p(st.cuda_stream)))
+            fn = self._lib.sdm_dw_step_noalloc if self._noalloc else self._lib.sdm_dw_step
+            _lib.check(fn(self._io_ref, int(ti), ctypes.c_void_p(st.cuda_stream)))
         finally:
             self.io.events = None
 

@@ -103,7 +103,7 @@ class PaIO(ctypes.Structure):
     ]
 
 
-EXPORTS = ["sdm_phase1_workspace", "sdm_phase1", "sdm_dw_workspace", "sdm_dw_step", "sdm_read_step",
+EXPORTS = ["sdm_phase1_workspace", "sdm_phase1", "sdm_dw_workspace", "sdm_dw_step", "sdm_dw_step_noalloc", "sdm_read_step",
            "sdm_gds_step", "sdm_gwr_step", "sdm_pa_step", "sdm_status_string", "sdm_last_error"]
 
 _lock = threading.Lock()
@@ -133,6 +133,8 @@ def load() -> ctypes.CDLL:
         lib.sdm_dw_workspace.restype = ctypes.c_size_t
         lib.sdm_dw_step.argtypes = [ctypes.POINTER(DwIO), ctypes.c_int64, ctypes.c_void_p]
         lib.sdm_dw_step.restype = ctypes.c_int
+        lib.sdm_dw_step_noalloc.argtypes = [ctypes.POINTER(DwIO), ctypes.c_int64, ctypes.c_void_p]
+        lib.sdm_dw_step_noalloc.restype = ctypes.c_int
         lib.sdm_read_step.argtypes = [ctypes.POINTER(ReadIO), ctypes.c_int64, ctypes.c_void_p]
         lib.sdm_read_step.restype = ctypes.c_int
         lib.sdm_gds_step.argtypes = [ctypes.POINTER(GdsIO), ctypes.c_int64, ctypes.c_void_p]

@@ -411,4 +411,28 @@ sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st) {
     return SDM_OK;
 }
 
+sdm_status sdm_dw_step_noalloc(const sdm_dw_io* io, int64_t ti, hipStream_t st) {
+    g_last_error.clear();
+    if (io == nullptr) return fail(SDM_EINVAL, "sdm_dw_step_noalloc: io is NULL");
+    if (io->workspace != nullptr)
+        return fail(SDM_EINVAL, "sdm_dw_step_noalloc: workspace must be NULL (the library's fixed device array is used)");
+    const sdm_status rc = check_dw_io(io, ti, "sdm_dw_step_noalloc");
+    if (rc != SDM_OK) return rc;
+    size_t need = 0, cap = 0;
+    if (!sdm::dw_static_fits(io, &need, &cap))
+        return fail(SDM_EWORKSPACE,
+                    "sdm_dw_step_noalloc: P*C*W = %lld positions and %zu bytes of partial rows exceed the fixed array "
+                    "(at most 4194304 positions and %zu bytes); use sdm_dw_step with a workspace",
+                    static_cast<long long>(static_cast<int64_t>(io->P) * io->C * io->W), need, cap);
+    hipError_t e = device_setup(nullptr);
+    if (e == hipSuccess) e = sdm::dw_static_setup();
+    if (e != hipSuccess) return fail(SDM_EHIP, "sdm_dw_step_noalloc: set-up: %s", hipGetErrorString(e));
+    sdm::DwLaunch L;
+    L.io = io;
+    L.ti = ti;
+    e = sdm::dw_launch_static(L, st);
+    if (e != hipSuccess) return fail(SDM_EHIP, "sdm_dw_step_noalloc: %s", hipGetErrorString(e));
+    return SDM_OK;
+}
+
 }  // extern "C"

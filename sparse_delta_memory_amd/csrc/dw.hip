@@ -13,6 +13,8 @@
 // every load issued before the first use; positions that start no work exit.
 #include <hip/hip_ext.h>
 
+#include <mutex>
+
 #include "sdm_device.hpp"
 #include "sdm_launch.hpp"
 
@@ -625,6 +627,33 @@ hipError_t dw_launch_ws(const DwLaunch& Lc, hipStream_t st, int* cnt, int2* meta
     return launch_dw_types<16>(a, bb, db, tail, sbf, st, ev);
 }
 
+// ---- Allocation-free variant: the split-group workspace in a fixed device array of the library.
+// Fixed layout (independent of the call's shape, so one call's partial rows never fall where a
+// later call's counters are): counters for up to kScratchPositions K-row positions per step at
+// offset 0, then their metadata pairs, then the partial rows.
+constexpr int64_t kScratchPositions = int64_t(1) << 22;
+constexpr size_t kScratchBlocks = static_cast<size_t>(kScratchPositions / kSeg);
+constexpr size_t kScratchCntBytes = kScratchBlocks * sizeof(int);
+constexpr size_t kScratchMetaBytes = kScratchBlocks * sizeof(int2);
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr size_t kScratchPartBytes = kScratchBytes - kScratchCntBytes - kScratchMetaBytes;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Per device: the array's device address (hipGetSymbolAddress with that device current), found once.
+constexpr int kScratchDevices = 64;
+struct ScratchDev {
+    std::once_flag once;
+    hipError_t err = hipSuccess;
+    unsigned char* ptr = nullptr;
+};
+ScratchDev g_scratch[kScratchDevices];
+
+__global__ void __launch_bounds__(256) dw_clear_counters(int* cnt, int n) {
+    const int i = static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x);
+    if (i < n) cnt[i] = 0;
+}
+
 }  // namespace
 
 hipError_t dw_launch(const DwLaunch& Lc, hipStream_t st) {
@@ -634,6 +663,48 @@ hipError_t dw_launch(const DwLaunch& Lc, hipStream_t st) {
     char* ws = static_cast<char*>(io->workspace);
     return dw_launch_ws(Lc, st, reinterpret_cast<int*>(ws + w.cnt_off), reinterpret_cast<int2*>(ws + w.meta_off),
                         reinterpret_cast<float*>(ws + w.part_off));
+}
+
+bool dw_static_fits(const sdm_dw_io* io, size_t* need, size_t* cap) {
+    const int64_t pos = static_cast<int64_t>(io->P) * io->C * io->W;
+    const size_t blocks = static_cast<size_t>((pos + kSeg - 1) / kSeg);
+    *need = 2 * blocks * static_cast<size_t>(io->hd) * sizeof(float);
+    *cap = kScratchPartBytes;
+    return pos <= kScratchPositions && *need <= kScratchPartBytes;
+}
+
+hipError_t dw_static_setup() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    ScratchDev& d = g_scratch[dev];
+    std::call_once(d.once, [&d]() {
+        void* ptr = nullptr;
+        d.err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (d.err == hipSuccess) d.ptr = static_cast<unsigned char*>(ptr);
+        else (void)hipGetLastError();
+    });
+    return d.err;
+}
+
+hipError_t dw_launch_static(const DwLaunch& Lc, hipStream_t st) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    unsigned char* base = g_scratch[dev].ptr;   // (dw_static_setup succeeded on this device)
+    int* cnt = reinterpret_cast<int*>(base);
+    int2* meta = reinterpret_cast<int2*>(base + kScratchCntBytes);
+    float* part = reinterpret_cast<float*>(base + kScratchCntBytes + kScratchMetaBytes);
+    const sdm_dw_io* io = Lc.io;
+    const int64_t pos = static_cast<int64_t>(io->P) * io->C * io->W;
+    if (pos == 0) return hipSuccess;
+    // The counters this call uses start at zero: a fill kernel (not a memset node, so the pair
+    // replays correctly from a captured graph), then the step.
+    const int nblk = static_cast<int>((pos + kSeg - 1) / kSeg);
+    hipLaunchKernelGGL(dw_clear_counters, dim3((nblk + 255) / 256), dim3(256), 0, st, cnt, nblk);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return dw_launch_ws(Lc, st, cnt, meta, part);
 }
 
 }  // namespace sdm

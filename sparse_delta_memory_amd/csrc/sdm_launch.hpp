@@ -57,6 +57,13 @@ struct DwLaunch {
 
 hipError_t dw_launch(const DwLaunch& L, hipStream_t st);
 
+// Allocation-free DW: the split workspace in the library's fixed device array. dw_static_fits says
+// whether a step of this shape fits it (need / cap: partial-row bytes); dw_static_setup finds the
+// array's address on the current device (once per device); dw_launch_static clears the call's
+// counters with a fill kernel and enqueues the step.
+bool dw_static_fits(const sdm_dw_io* io, size_t* need, size_t* cap);
+hipError_t dw_static_setup();
+hipError_t dw_launch_static(const DwLaunch& L, hipStream_t st);
 
 // Workspace of sdm_dw_step: per block of 32 K-row positions an arrival counter (zero between
 // calls) and group metadata, and two partial rows.
