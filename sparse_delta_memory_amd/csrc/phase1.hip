@@ -182,70 +182,114 @@ __device__ __forceinline__ Seg seg_combine(Seg a, Seg b) {
     return Seg{s, (a.c + b.c) + err, ((a.f & ~kSegHead) + (b.f & ~kSegHead)) | (a.f & kSegHead)};
 }
 
-template <bool REV>
-__device__ __forceinline__ Seg seg_shfl(Seg v, int d) {
-    Seg o;
-    if (REV) {
-        o.s = __shfl_down(v.s, d, kWave);
-        o.c = __shfl_down(v.c, d, kWave);
-        o.f = __shfl_down(v.f, d, kWave);
-    } else {
-        o.s = __shfl_up(v.s, d, kWave);
-        o.c = __shfl_up(v.c, d, kWave);
-        o.f = __shfl_up(v.f, d, kWave);
-    }
-    return o;
+// Lane moves by DPP (GFX9 encodings): inside rows of 16 lanes row_shr:n (0x110 + n) reads lane
+// l - n and row_shl:n (0x100 + n) lane l + n; row_bcast:15 (0x142) gives rows 1 and 3 the last lane
+// of the row before, row_bcast:31 (0x143) gives rows 2 and 3 lane 31; wave_shr:1 (0x138) and
+// wave_shl:1 (0x130) move the whole wave by one lane. A lane with no source (or in a row the mask
+// leaves out) reads 0, which is the zero scan element: seg_combine(zero, b) == b bit for bit.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROWS, 0xF, true));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ Seg seg_dpp(Seg v) {
+    return Seg{__uint_as_float(dpp_u32<CTRL, ROWS>(__float_as_uint(v.s))),
+               __uint_as_float(dpp_u32<CTRL, ROWS>(__float_as_uint(v.c))), dpp_u32<CTRL, ROWS>(v.f)};
+}
+__device__ __forceinline__ Seg seg_from_lane(Seg v, int src) {
+    return Seg{__shfl(v.s, src, kWave), __shfl(v.c, src, kWave), static_cast<uint32_t>(__shfl(static_cast<int>(v.f), src, kWave))};
 }
 
+// Inclusive segmented scan over the lanes of a wave in scan order (REV: descending lanes). Fixed
+// tree: doubling steps inside each row of 16 lanes, then the rows in order (forward: the last lane
+// of the row before, by row broadcasts; reverse: the first lane of the row after, then lane 32).
+template <bool REV>
+__device__ __forceinline__ Seg wave_inclusive_seg(Seg x) {
+    if constexpr (!REV) {
+        x = seg_combine(seg_dpp<0x111, 0xF>(x), x);
+        x = seg_combine(seg_dpp<0x112, 0xF>(x), x);
+        x = seg_combine(seg_dpp<0x114, 0xF>(x), x);
+        x = seg_combine(seg_dpp<0x118, 0xF>(x), x);
+        x = seg_combine(seg_dpp<0x142, 0xA>(x), x);
+        x = seg_combine(seg_dpp<0x143, 0xC>(x), x);
+    } else {
+        const int lane = static_cast<int>(lane_id());
+        x = seg_combine(seg_dpp<0x101, 0xF>(x), x);
+        x = seg_combine(seg_dpp<0x102, 0xF>(x), x);
+        x = seg_combine(seg_dpp<0x104, 0xF>(x), x);
+        x = seg_combine(seg_dpp<0x108, 0xF>(x), x);
+        Seg o = seg_from_lane(x, (lane | 15) + 1);   // rows 0 and 2: the first lane of the next row
+        if ((lane & 16) == 0) x = seg_combine(o, x);
+        o = seg_from_lane(x, 32);                    // rows 0 and 1: lane 32 (rows 2 and 3 summed)
+        if (lane < 32) x = seg_combine(o, x);
+    }
+    return x;
+}
+
+// Inclusive sum over the lanes of a wave (the same doubling steps and row order).
+__device__ __forceinline__ uint32_t wave_inclusive_add(uint32_t x) {
+    x += dpp_u32<0x111, 0xF>(x);
+    x += dpp_u32<0x112, 0xF>(x);
+    x += dpp_u32<0x114, 0xF>(x);
+    x += dpp_u32<0x118, 0xF>(x);
+    x += dpp_u32<0x142, 0xA>(x);
+    x += dpp_u32<0x143, 0xC>(x);
+    return x;
+}
+
+__device__ __forceinline__ Seg seg_readlane(Seg v, int l) {
+    return Seg{__uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v.s), l)),
+               __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v.c), l)),
+               static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v.f), l))};
+}
 
 // Exclusive segmented scan of one element per thread over the block, in thread order
-// (REV: descending). Fixed tree: lane doubling, then the wave totals in scan order. `total`
-// receives the block's combined element. wtot: kNW elements of LDS.
+// (REV: descending). Fixed tree: the wave scans above; then every wave scans the 16 wave totals
+// itself in the first row of its lanes (doubling steps in scan order) and takes its own prefix by
+// readlane, so one barrier suffices. The totals alternate between two LDS buffers (`phase`, the
+// same count in every thread): a wave that runs ahead writes the other buffer, and cannot get two
+// scans ahead, since writing again needs every wave past the barrier of the scan in between.
+// `total` receives the block's combined element. wtot: 2 kNW elements of LDS.
 template <bool REV>
-__device__ __forceinline__ Seg block_exclusive_seg(Seg agg, Seg* wtot, Seg& total) {
+__device__ __forceinline__ Seg block_exclusive_seg(Seg agg, Seg* wtot, uint32_t& phase, Seg& total) {
+    static_assert(kNW == 16, "one DPP row of wave totals");
     const int lane = static_cast<int>(lane_id());
     const int w = threadIdx.x / kWave;
-    Seg incl = agg;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const Seg o = seg_shfl<REV>(incl, d);
-        if (REV ? (lane + d < kWave) : (lane >= d)) incl = seg_combine(o, incl);
-    }
-    Seg ex = seg_shfl<REV>(incl, 1);
-    if (REV ? (lane == kWave - 1) : (lane == 0)) ex = seg_zero();
-    if (REV ? (lane == 0) : (lane == kWave - 1)) wtot[w] = incl;
+    Seg* buf = wtot + (phase & 1u) * kNW;
+    ++phase;
+    const Seg incl = wave_inclusive_seg<REV>(agg);
+    const Seg ex = REV ? seg_dpp<0x130, 0xF>(incl) : seg_dpp<0x138, 0xF>(incl);
+    if (REV ? (lane == 0) : (lane == kWave - 1)) buf[w] = incl;
     lds_barrier();
-    Seg pre = seg_zero(), tot = seg_zero();
-    for (int i = 0; i < kNW; ++i) {
-        const int ww = REV ? kNW - 1 - i : i;
-        if (ww == w) pre = tot;
-        tot = seg_combine(tot, wtot[ww]);
-    }
-    lds_barrier();
-    total = tot;
-    return seg_combine(pre, ex);
+    // Lane i < 16 holds the i-th wave total in scan order.
+    const Seg v = lane < kNW ? buf[REV ? kNW - 1 - lane : lane] : seg_zero();
+    Seg inc = seg_combine(seg_dpp<0x111, 0xF>(v), v);
+    inc = seg_combine(seg_dpp<0x112, 0xF>(inc), inc);
+    inc = seg_combine(seg_dpp<0x114, 0xF>(inc), inc);
+    inc = seg_combine(seg_dpp<0x118, 0xF>(inc), inc);
+    const Seg exw = seg_dpp<0x111, 0xF>(inc);
+    total = seg_readlane(inc, kNW - 1);
+    return seg_combine(seg_readlane(exw, REV ? kNW - 1 - w : w), ex);
 }
 
 // Exclusive integer sum over the block in thread order; `total` receives the block sum.
-__device__ __forceinline__ uint32_t block_exclusive_add(uint32_t v, uint32_t* wsum, uint32_t& total) {
+// wsum: 2 kNW words of LDS, used in alternation as in block_exclusive_seg.
+__device__ __forceinline__ uint32_t block_exclusive_add(uint32_t v, uint32_t* wsum, uint32_t& phase, uint32_t& total) {
     const int lane = static_cast<int>(lane_id());
     const int w = threadIdx.x / kWave;
-    uint32_t incl = v;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const uint32_t o = __shfl_up(incl, d, kWave);
-        if (lane >= d) incl += o;
-    }
-    if (lane == kWave - 1) wsum[w] = incl;
+    uint32_t* buf = wsum + (phase & 1u) * kNW;
+    ++phase;
+    const uint32_t incl = wave_inclusive_add(v);
+    if (lane == kWave - 1) buf[w] = incl;
     lds_barrier();
-    uint32_t pre = 0, tot = 0;
-    for (int ww = 0; ww < kNW; ++ww) {
-        const uint32_t x = wsum[ww];
-        pre += ww < w ? x : 0u;
-        tot += x;
-    }
-    lds_barrier();
-    total = tot;
+    const uint32_t x = lane < kNW ? buf[lane & (kNW - 1)] : 0u;
+    uint32_t inc = x;
+    inc += dpp_u32<0x111, 0xF>(inc);
+    inc += dpp_u32<0x112, 0xF>(inc);
+    inc += dpp_u32<0x114, 0xF>(inc);
+    inc += dpp_u32<0x118, 0xF>(inc);
+    total = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(inc), kNW - 1));
+    const uint32_t pre = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(inc - x), w));
     return pre + incl - v;
 }
 
@@ -257,7 +301,7 @@ __device__ __forceinline__ uint32_t block_exclusive_add(uint32_t v, uint32_t* ws
 // scatter into skey / sval. On return skey / sval hold the sorted sequence.
 template <int IPT>
 __device__ void block_radix_sort(uint32_t (&key)[IPT], uint32_t (&val)[IPT], int bits, int dmax, uint32_t* skey,
-                                 uint16_t* sval, uint32_t* hist, uint32_t* wsum) {
+                                 uint16_t* sval, uint32_t* hist, uint32_t* wsum, uint32_t& phase) {
     const int lane = static_cast<int>(lane_id());
     const int w = threadIdx.x / kWave;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
@@ -298,7 +342,7 @@ __device__ void block_radix_sort(uint32_t (&key)[IPT], uint32_t (&val)[IPT], int
             if (e < nd * kNW) local += hist[(e % kNW) * stride + e / kNW];
         }
         uint32_t tot;
-        uint32_t run = block_exclusive_add(local, wsum, tot);
+        uint32_t run = block_exclusive_add(local, wsum, phase, tot);
         for (int u = 0; u < per; ++u) {
             const int e = threadIdx.x * per + u;
             if (e < nd * kNW) {
@@ -373,8 +417,10 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     float* vals_k = reinterpret_cast<float*>(smem + a.vals_off);          // resident: staged values
     uint16_t* sval = reinterpret_cast<uint16_t*>(smem + a.stage_bytes);
     float* gates = reinterpret_cast<float*>(smem + a.stage_bytes + NP * 2);
-    __shared__ Seg wtot[kNW];
-    __shared__ uint32_t wsum[kNW];
+    __shared__ Seg wtot[2 * kNW];
+    __shared__ uint32_t wsum[2 * kNW];
+    // Alternation of the scan-total buffers, one count per buffer pair (the same in every thread).
+    uint32_t seg_phase = 0, add_phase = 0;
     __shared__ uint32_t tile_kind[NTILE + 1];   // kind counts (K | Q << 16) before each tile
     __shared__ uint32_t hot_n;                   // hot groups found so far
     __shared__ uint64_t optr[kNumOut];           // entry-order destinations (0: skipped)
@@ -476,7 +522,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             }
         }
         // Invalid entries need one more key bit only in a ragged chunk.
-        block_radix_sort<IPT>(key, val, tv < C ? kb + 1 : kb, a.digit_bits, skey, sval, hist, wsum);
+        block_radix_sort<IPT>(key, val, tv < C ? kb + 1 : kb, a.digit_bits, skey, sval, hist, wsum, add_phase);
     }
 
     // Per-thread state carried from the scans to the output sweeps (registers, tile-indexed).
@@ -540,7 +586,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                                                            (((ends >> k) & 1u) ? kSegHead : 0u)});
             }
             Seg total;
-            rpre[T] = seg_combine(rcarry, block_exclusive_seg<true>(agg, wtot, total));
+            rpre[T] = seg_combine(rcarry, block_exclusive_seg<true>(agg, wtot, seg_phase, total));
             rcarry = seg_combine(rcarry, total);
 #pragma unroll
             for (int k = 0; k < kTileItems; ++k) {
@@ -620,16 +666,16 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                 if (p0 + k < n) kind_cnt += (r - t * wr >= W) ? kSegQOne : 1u;
             }
             Seg total;
-            fpre[T] = seg_combine(fcarry, block_exclusive_seg<false>(agg, wtot, total));
+            fpre[T] = seg_combine(fcarry, block_exclusive_seg<false>(agg, wtot, seg_phase, total));
             fcarry = seg_combine(fcarry, total);
             uint32_t kind_total;
-            kpre[T] = kind_carry + block_exclusive_add(kind_cnt, wsum, kind_total);
+            kpre[T] = kind_carry + block_exclusive_add(kind_cnt, wsum, add_phase, kind_total);
             if (threadIdx.x == 0) tile_kind[T] = kind_carry;
             kind_carry += kind_total;
         }
         if (threadIdx.x == 0) tile_kind[ntiles] = kind_carry;
         uint32_t rep_total;
-        (void)block_exclusive_add(repeat_count, wsum, rep_total);
+        (void)block_exclusive_add(repeat_count, wsum, add_phase, rep_total);
         if (threadIdx.x == 0 && a.repeats != nullptr) a.repeats[c] = static_cast<int32_t>(rep_total);
     }
     lds_barrier();   // LDS only: the repeats (and perm) stores stay in flight; nothing here reads them
