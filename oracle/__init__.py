@@ -27,13 +27,28 @@ _lock = threading.Lock()
 _lib = None
 
 
-def build(force: bool = False) -> str:
-    """Compile sdm_oracle.c with gcc into oracle/libsdm_oracle.so (plain -O2, no fast-math)."""
-    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+_SAN_LIB_PATH = os.path.join(_HERE, "libsdm_oracle_san.so")
+
+
+def build(force: bool = False, sanitize: bool = False) -> str:
+    """Compile sdm_oracle.c with gcc into oracle/libsdm_oracle.so (plain -O2, no fast-math).
+    sanitize: with clang (the ROCm toolchain's, whose ASan runtime the sanitized HIP library also
+    uses) and -fsanitize=address,undefined (UB traps) into libsdm_oracle_san.so. SDM_ORACLE_LIB,
+    when set, names the library to load instead of building."""
+    if os.environ.get("SDM_ORACLE_LIB") and not sanitize:
+        return os.environ["SDM_ORACLE_LIB"]
+    path = _SAN_LIB_PATH if sanitize else _LIB_PATH
+    if force or sanitize or not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+        tmp = path + ".tmp%d" % os.getpid()
+        if sanitize:
+            cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
+                   "-fsanitize=address,undefined", "-fsanitize-trap=undefined", "-fno-omit-frame-pointer",
+                   "-o", tmp, _SRC, "-lm"]
+        else:
+            cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, path)
+    return path
 
 
 class _ChunkIn(ctypes.Structure):

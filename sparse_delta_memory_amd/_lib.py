@@ -7,7 +7,8 @@ import os
 import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsdm_amd.so")
+# SDM_LIB selects another build of the same library (the host-sanitized one, libsdm_amd_san.so).
+LIB_PATH = os.environ.get("SDM_LIB") or os.path.join(HERE, "libsdm_amd.so")
 
 SDM_OK = 0
 SDM_EINVAL = -1

@@ -40,9 +40,21 @@ def command(out: str = LIB) -> list[str]:
     return [hipcc()] + FLAGS + ["-shared", "-I", INCLUDE, "-I", CSRC, "-o", out] + [os.path.join(CSRC, s) for s in SOURCES]
 
 
-def build(verbose: bool = False) -> str:
+# Host-only sanitizers (AddressSanitizer, and UndefinedBehaviorSanitizer with traps, so no runtime
+# beyond the ASan one is needed): each flag goes to the host compilation only, never to the gfx950
+# device code.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fsanitize-trap=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_LIB = os.path.join(HERE, "libsdm_amd_san.so")
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
     """Compile the library (always; the caller decides when): each source to an object file in
-    parallel under a private build folder, then one link. Returns its path."""
+    parallel under a private build folder, then one link. Returns its path. sanitize: the host code
+    built with ASan and UBSan into libsdm_amd_san.so instead (CPU checks of the host side; the
+    process must preload the ASan runtime, see sanitize.py)."""
+    flags = FLAGS + (SAN_FLAGS if sanitize else [])
+    out_lib = SAN_LIB if sanitize else LIB
     import tempfile
     from concurrent.futures import ThreadPoolExecutor
 
@@ -50,7 +62,7 @@ def build(verbose: bool = False) -> str:
     try:
         def compile_one(src):
             obj = os.path.join(work, src + ".o")
-            cmd = [hipcc()] + FLAGS + ["-c", "-I", INCLUDE, "-I", CSRC, "-o", obj, os.path.join(CSRC, src)]
+            cmd = [hipcc()] + flags + ["-c", "-I", INCLUDE, "-I", CSRC, "-o", obj, os.path.join(CSRC, src)]
             if verbose:
                 print(" ".join(cmd), flush=True)
             res = subprocess.run(cmd, capture_output=True, text=True)
@@ -62,18 +74,18 @@ def build(verbose: bool = False) -> str:
         jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", "0") or 0) or (os.cpu_count() or 1)))
         with ThreadPoolExecutor(max_workers=jobs) as ex:
             objs = list(ex.map(compile_one, SOURCES))
-        tmp = LIB + ".tmp%d" % os.getpid()
-        cmd = [hipcc()] + FLAGS + ["-shared", "-o", tmp] + objs
+        tmp = out_lib + ".tmp%d" % os.getpid()
+        cmd = [hipcc()] + flags + ["-shared", "-o", tmp] + objs
         if verbose:
             print(" ".join(cmd), flush=True)
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             sys.stderr.write(res.stdout + res.stderr)
-            raise RuntimeError("hipcc failed linking %s" % LIB)
-        os.replace(tmp, LIB)
+            raise RuntimeError("hipcc failed linking %s" % out_lib)
+        os.replace(tmp, out_lib)
     finally:
         shutil.rmtree(work, ignore_errors=True)
-    return LIB
+    return out_lib
 
 
 if __name__ == "__main__":
