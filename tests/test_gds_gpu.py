@@ -52,6 +52,7 @@ def gds_inputs(wl, grad_dtype):
     dict(idx=2, steps=1, checked=[0]),                  # Zipf: long read groups
     dict(idx=4, steps=2, checked=[1]),                  # ragged last step
     dict(shape=dict(C=37, W=5, R=3, S=9, P=2, vl=11, hd=36), steps=2, checked=[0, 1], val_bf16=True),
+    dict(idx=3, steps=1, checked=[0]),                  # hd = 960: the dots' column loop, multi-block scatter
 ])
 def test_gds_matches_oracle(case):
     if "shape" in case:
