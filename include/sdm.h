@@ -82,6 +82,15 @@ typedef struct sdm_p1_shape {
                                rounded to bfloat16 (nearest even), krec's cpe field holds that rounded
                                cpe widened to float32 (so sdm_dw_step scales by it), and every other
                                output is computed from the values widened exactly to float32. */
+    int32_t tiled;          /* 0: rows of up to 16384 entries are sorted and scanned on chip by one
+                               workgroup per chunk, longer rows (up to 2^17 entries) take the tiled
+                               path; 1: every row takes the tiled path. The tiled path (page
+                               "sparse_delta_memory/cuda/phase1_cuda.py": the merge rounds of rows too
+                               long for one on-chip sort) works from global memory in tiles of 16384
+                               entries: a stable radix sort through two workspace buffers, then the
+                               reverse and forward scans tile by tile with carries. Its integer outputs
+                               equal the on-chip path's bit for bit; its float outputs meet the same
+                               tolerance. */
 } sdm_p1_shape;
 
 /*
@@ -170,7 +179,7 @@ size_t sdm_phase1_workspace(const sdm_p1_shape* shape);
  * q_e k_f exp(log_q_e - log_k_f) over Q entries e of token i and earlier K entries f of token j.
  * Invalid entries: log 0, rex 0, cpe 1, k_eff / q_w 0, flags 0, pos = sorted position.
  *
- * Requirements: C*(W+R) <= 16384 (longer rows: SDM_EUNSUPPORTED); 4-byte aligned inputs
+ * Requirements: C*(W+R) <= 2^17 (rows past 16384 entries take the tiled path); 4-byte aligned inputs
  * (bfloat16 value-typed fields: 2-byte); krec 16-byte aligned; for P > 1 every local slot of a
  * stream is < stream_offset.
  * Floating outputs agree with the exact (real-arithmetic) values within

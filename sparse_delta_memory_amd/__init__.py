@@ -23,13 +23,14 @@ __all__ = ["P1Shape", "phase1", "phase1_workspace_bytes", "alloc_phase1_outputs"
 
 
 def make_shape(N, C, W, R, P=1, key_bits=16, stream_offset=0, first_partial=None, valid_last=None, tile_len=128,
-               g_lane_stride=0, idx_bytes=4, val_bytes=4):
+               g_lane_stride=0, idx_bytes=4, val_bytes=4, tiled=False):
     """Phase-1 shape. g_lane_stride 0: gates g [N, C] (per token); 1: g [N, C, W] (per token and K lane).
     idx_bytes 4: int32 slot ids; 8: int64. val_bytes 4: float32 values; 2: bfloat16 values (and
-    bfloat16 cpe, k_eff, q_w)."""
+    bfloat16 cpe, k_eff, q_w). tiled: every row through the tiled path (rows past 16384 entries
+    always take it)."""
     return P1Shape(int(N), int(C), int(W), int(R), int(P), int(key_bits), int(stream_offset),
                    int(N if first_partial is None else first_partial), int(C if valid_last is None else valid_last),
-                   int(tile_len), int(g_lane_stride), int(idx_bytes), int(val_bytes))
+                   int(tile_len), int(g_lane_stride), int(idx_bytes), int(val_bytes), int(bool(tiled)))
 
 
 def phase1_workspace_bytes(shape: P1Shape) -> int:

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsdm_amd.so")
-SOURCES = ["api.cpp", "phase1.hip", "dw.hip", "read.hip", "gds.hip"]
+SOURCES = ["api.cpp", "phase1.hip", "phase1_tiled.hip", "dw.hip", "read.hip", "gds.hip"]
 ARCH = "gfx950"
 
 

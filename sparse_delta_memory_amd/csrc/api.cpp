@@ -94,10 +94,8 @@ sdm_status check_p1_shape(const sdm_p1_shape* s) {
     if (s->g_lane_stride != 0 && s->g_lane_stride != 1)
         return fail(SDM_EINVAL, "sdm_phase1: g_lane_stride = %d (0: gates [N, C]; 1: gates [N, C, W])", s->g_lane_stride);
     const int64_t n = static_cast<int64_t>(s->C) * (s->W + s->R);
-    if (n > (1 << 17)) return fail(SDM_ESHAPE, "sdm_phase1: C*(W+R) = %lld > 2^17", static_cast<long long>(n));
-    if (n > sdm::kP1MaxRow)
-        return fail(SDM_EUNSUPPORTED, "sdm_phase1: C*(W+R) = %lld > %d (on-chip row limit of this build)",
-                    static_cast<long long>(n), sdm::kP1MaxRow);
+    if (n > sdm::kP1MaxTiledRow) return fail(SDM_ESHAPE, "sdm_phase1: C*(W+R) = %lld > 2^17", static_cast<long long>(n));
+    if (s->tiled != 0 && s->tiled != 1) return fail(SDM_EINVAL, "sdm_phase1: tiled = %d (0 or 1)", s->tiled);
     return SDM_OK;
 }
 
@@ -230,9 +228,15 @@ sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st
     L.inv_k = static_cast<char*>(io->workspace) + ws.inv_k_off;
     L.inv_q = static_cast<char*>(io->workspace) + ws.inv_q_off;
     L.hot = static_cast<char*>(io->workspace) + ws.hot_off;
+    L.sort = ws.tiled ? static_cast<char*>(io->workspace) + ws.sort_off : nullptr;
+    L.rev = ws.tiled ? static_cast<char*>(io->workspace) + ws.rev_off : nullptr;
     L.lds_max = lds_max;
+    sdm::g_p1_stage = "";
     const hipError_t e = sdm::p1_launch(L, st);
-    if (e != hipSuccess) return fail(SDM_EHIP, "sdm_phase1: %s", hipGetErrorString(e));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();   // the launch's error is reported through the status, not left pending
+        return fail(SDM_EHIP, "sdm_phase1: %s: %s", sdm::g_p1_stage, hipGetErrorString(e));
+    }
     return SDM_OK;
 }
 
@@ -286,7 +290,10 @@ sdm_status sdm_read_step(const sdm_read_io* io, int64_t ti, hipStream_t st) {
     L.io = io;
     L.ti = ti;
     const hipError_t e = sdm::read_launch(L, st);
-    if (e != hipSuccess) return fail(SDM_EHIP, "sdm_read_step: %s", hipGetErrorString(e));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(SDM_EHIP, "sdm_read_step: %s", hipGetErrorString(e));
+    }
     return SDM_OK;
 }
 
@@ -323,7 +330,10 @@ sdm_status sdm_gds_step(const sdm_gds_io* io, int64_t ti, hipStream_t st) {
         !aligned(io->spay_q, 4) || !aligned(io->d_q_w, 4))
         return fail(SDM_EALIGN, "sdm_gds_step: q_idx, q_w, spay_q or d_q_w misaligned");
     const hipError_t e = sdm::gds_launch(io, ti, st);
-    if (e != hipSuccess) return fail(SDM_EHIP, "sdm_gds_step: %s", hipGetErrorString(e));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(SDM_EHIP, "sdm_gds_step: %s", hipGetErrorString(e));
+    }
     return SDM_OK;
 }
 
@@ -354,7 +364,10 @@ sdm_status sdm_gwr_step(const sdm_gwr_io* io, int64_t ti, hipStream_t st) {
     if (!aligned(io->k_idx, io->idx_bytes == 8 ? 8 : 4) || !aligned(io->w, 4) || !aligned(io->d_k_pd, 4))
         return fail(SDM_EALIGN, "sdm_gwr_step: k_idx, w or d_k_pd misaligned");
     const hipError_t e = sdm::gwr_launch(io, ti, st);
-    if (e != hipSuccess) return fail(SDM_EHIP, "sdm_gwr_step: %s", hipGetErrorString(e));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(SDM_EHIP, "sdm_gwr_step: %s", hipGetErrorString(e));
+    }
     return SDM_OK;
 }
 
@@ -394,7 +407,10 @@ sdm_status sdm_pa_step(const sdm_pa_io* io, int64_t ti, hipStream_t st) {
         !aligned(io->d_k_eff, 4))
         return fail(SDM_EALIGN, "sdm_pa_step: k_eff, beta, g_decay or d_k_eff misaligned");
     const hipError_t e = sdm::pa_launch(io, ti, st);
-    if (e != hipSuccess) return fail(SDM_EHIP, "sdm_pa_step: %s", hipGetErrorString(e));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(SDM_EHIP, "sdm_pa_step: %s", hipGetErrorString(e));
+    }
     return SDM_OK;
 }
 
@@ -407,7 +423,10 @@ sdm_status sdm_dw_step(const sdm_dw_io* io, int64_t ti, hipStream_t st) {
     L.io = io;
     L.ti = ti;
     const hipError_t e = sdm::dw_launch(L, st);
-    if (e != hipSuccess) return fail(SDM_EHIP, "sdm_dw_step: %s", hipGetErrorString(e));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(SDM_EHIP, "sdm_dw_step: %s", hipGetErrorString(e));
+    }
     return SDM_OK;
 }
 
@@ -431,7 +450,10 @@ sdm_status sdm_dw_step_noalloc(const sdm_dw_io* io, int64_t ti, hipStream_t st) 
     L.io = io;
     L.ti = ti;
     e = sdm::dw_launch_static(L, st);
-    if (e != hipSuccess) return fail(SDM_EHIP, "sdm_dw_step_noalloc: %s", hipGetErrorString(e));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(SDM_EHIP, "sdm_dw_step_noalloc: %s", hipGetErrorString(e));
+    }
     return SDM_OK;
 }
 

@@ -702,8 +702,10 @@ hipError_t dw_launch_static(const DwLaunch& Lc, hipStream_t st) {
     // The counters this call uses start at zero: a fill kernel (not a memset node, so the pair
     // replays correctly from a captured graph), then the step.
     const int nblk = static_cast<int>((pos + kSeg - 1) / kSeg);
-    hipLaunchKernelGGL(dw_clear_counters, dim3((nblk + 255) / 256), dim3(256), 0, st, cnt, nblk);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    int n_clear = nblk;
+    void* cargs[] = {&cnt, &n_clear};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&dw_clear_counters), dim3((nblk + 255) / 256), dim3(256), cargs, 0, st);
+    if (e != hipSuccess) return e;
     return dw_launch_ws(Lc, st, cnt, meta, part);
 }
 

@@ -24,14 +24,13 @@
 
 #include <type_traits>
 
+#include "p1_scan.hpp"
 #include "sdm_device.hpp"
 #include "sdm_launch.hpp"
 
 namespace sdm {
 namespace {
 
-constexpr int kNT = kP1Threads;   // 1024 threads = 16 waves per chunk
-constexpr int kNW = kNT / kWave;
 constexpr int kTileItems = 4;     // scan items per thread per tile
 constexpr int kTile = kNT * kTileItems;
 constexpr uint32_t kFlagHead = 1u << 14;   // group head, kept beside r (< 2^14) in the sorted row
@@ -59,8 +58,8 @@ constexpr uint32_t kMetaPos = (1u << 14) - 1u;
 // Entry-order workspace word of the pair kernel: sorted position | kInvWalk when the entry starts
 // its token's run with earlier valid K entries in an ordinary group, kInvHot when it does so in a
 // hot group (walked only if the pair kernel cannot sum that group densely).
-constexpr uint32_t kInvWalk = 1u << 15;
-constexpr uint32_t kInvHot = 1u << 14;
+constexpr uint32_t kInvWalk = InvBits<uint16_t>::kWalk;
+constexpr uint32_t kInvHot = InvBits<uint16_t>::kHot;
 
 // Entry-order destinations, kept in an LDS table from the kernel's start to the sweeps (their
 // kernel-argument copies would otherwise hold scalar registers through the sort and the scans).
@@ -68,42 +67,6 @@ enum OutPtr : int {
     kOLogK, kORex, kOCpe, kOKEff, kOIsLast, kOIsOnly, kOPosK, kOInvK,
     kOLogQ, kOQW, kOPosQ, kOQLast, kOQOnly, kOInvQ, kNumOut
 };
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// Store of element i (a 32-bit index) of a T array in the global address space (a pointer read from
-// the LDS table would otherwise make a flat store, and a 64-bit index 64-bit address arithmetic).
-template <typename T>
-__device__ __forceinline__ void gstore(const void* base, uint32_t i, T v) {
-    typedef __attribute__((address_space(1))) T GT;
-    reinterpret_cast<GT*>(reinterpret_cast<uintptr_t>(base))[i] = v;
-}
-
-// Value-typed outputs (cpe, k_eff, q_w) with bfloat16 values: the float32 result rounded to
-// bfloat16, nearest even.
-__device__ __forceinline__ uint32_t bf16_rn(float x) { return f32_to_bf16_rne(x); }
-// Four values from element i (a multiple of 4; 16-byte / 8-byte aligned rows).
-__device__ __forceinline__ f32x4 load_val4(const void* p, int64_t i, int bf) {
-    if (bf) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p) + i);
-        return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
-                     __uint_as_float(w.y & 0xFFFF0000u)};
-    }
-    return *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
-}
-// The 32-bit pattern a float32 record field holds for a value-typed quantity.
-__device__ __forceinline__ uint32_t val_bits32(float x, int bf) { return bf ? bf16_rn(x) << 16 : __float_as_uint(x); }
-__device__ __forceinline__ void store_val(const void* base, uint32_t i, float v, int bf) {
-    if (bf) gstore<uint16_t>(base, i, static_cast<uint16_t>(bf16_rn(v)));
-    else gstore<float>(base, i, v);
-}
-// Entries 4 i4 .. 4 i4 + 3.
-__device__ __forceinline__ void store_val4(const void* base, uint32_t i4, f32x4 v, int bf) {
-    if (bf) gstore<u32x2>(base, i4, u32x2{bf16_rn(v.x) | bf16_rn(v.y) << 16, bf16_rn(v.z) | bf16_rn(v.w) << 16});
-    else gstore<f32x4>(base, i4, v);
-}
 
 struct P1Args {
     const void* k_idx;   // int32 or int64 ids
@@ -154,144 +117,6 @@ struct P1Args {
     int64_t stream_offset;
     Sweeps sweeps;
 };
-
-// r / (W + R) for entry indices r < 2^17 and W + R <= 512 (multiply-high by a rounded-up
-// reciprocal; the error term r / 2^32 stays below 1 / (W + R)).
-__device__ __forceinline__ int token_of_entry(int r, uint32_t magic) {
-    return static_cast<int>(__umulhi(static_cast<uint32_t>(r), magic));
-}
-
-// Segmented-scan element: a TwoSum-compensated float sum (s + c), the valid K count (bits 0-15),
-// the valid Q count (bits 16-30) and a segment-start flag (bit 31).
-struct Seg {
-    float s;
-    float c;
-    uint32_t f;
-};
-constexpr uint32_t kSegHead = 0x80000000u;
-constexpr uint32_t kSegQOne = 1u << 16;
-
-__device__ __forceinline__ Seg seg_zero() { return Seg{0.0f, 0.0f, 0u}; }
-
-// a precedes b in scan order. A segment start in b discards a.
-__device__ __forceinline__ Seg seg_combine(Seg a, Seg b) {
-    if (b.f & kSegHead) return b;
-    const float s = a.s + b.s;
-    const float bb = s - a.s;
-    const float err = (a.s - (s - bb)) + (b.s - bb);
-    return Seg{s, (a.c + b.c) + err, ((a.f & ~kSegHead) + (b.f & ~kSegHead)) | (a.f & kSegHead)};
-}
-
-// Lane moves by DPP (GFX9 encodings): inside rows of 16 lanes row_shr:n (0x110 + n) reads lane
-// l - n and row_shl:n (0x100 + n) lane l + n; row_bcast:15 (0x142) gives rows 1 and 3 the last lane
-// of the row before, row_bcast:31 (0x143) gives rows 2 and 3 lane 31; wave_shr:1 (0x138) and
-// wave_shl:1 (0x130) move the whole wave by one lane. A lane with no source (or in a row the mask
-// leaves out) reads 0, which is the zero scan element: seg_combine(zero, b) == b bit for bit.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROWS, 0xF, true));
-}
-template <int CTRL, int ROWS>
-__device__ __forceinline__ Seg seg_dpp(Seg v) {
-    return Seg{__uint_as_float(dpp_u32<CTRL, ROWS>(__float_as_uint(v.s))),
-               __uint_as_float(dpp_u32<CTRL, ROWS>(__float_as_uint(v.c))), dpp_u32<CTRL, ROWS>(v.f)};
-}
-__device__ __forceinline__ Seg seg_from_lane(Seg v, int src) {
-    return Seg{__shfl(v.s, src, kWave), __shfl(v.c, src, kWave), static_cast<uint32_t>(__shfl(static_cast<int>(v.f), src, kWave))};
-}
-
-// Inclusive segmented scan over the lanes of a wave in scan order (REV: descending lanes). Fixed
-// tree: doubling steps inside each row of 16 lanes, then the rows in order (forward: the last lane
-// of the row before, by row broadcasts; reverse: the first lane of the row after, then lane 32).
-template <bool REV>
-__device__ __forceinline__ Seg wave_inclusive_seg(Seg x) {
-    if constexpr (!REV) {
-        x = seg_combine(seg_dpp<0x111, 0xF>(x), x);
-        x = seg_combine(seg_dpp<0x112, 0xF>(x), x);
-        x = seg_combine(seg_dpp<0x114, 0xF>(x), x);
-        x = seg_combine(seg_dpp<0x118, 0xF>(x), x);
-        x = seg_combine(seg_dpp<0x142, 0xA>(x), x);
-        x = seg_combine(seg_dpp<0x143, 0xC>(x), x);
-    } else {
-        const int lane = static_cast<int>(lane_id());
-        x = seg_combine(seg_dpp<0x101, 0xF>(x), x);
-        x = seg_combine(seg_dpp<0x102, 0xF>(x), x);
-        x = seg_combine(seg_dpp<0x104, 0xF>(x), x);
-        x = seg_combine(seg_dpp<0x108, 0xF>(x), x);
-        Seg o = seg_from_lane(x, (lane | 15) + 1);   // rows 0 and 2: the first lane of the next row
-        if ((lane & 16) == 0) x = seg_combine(o, x);
-        o = seg_from_lane(x, 32);                    // rows 0 and 1: lane 32 (rows 2 and 3 summed)
-        if (lane < 32) x = seg_combine(o, x);
-    }
-    return x;
-}
-
-// Inclusive sum over the lanes of a wave (the same doubling steps and row order).
-__device__ __forceinline__ uint32_t wave_inclusive_add(uint32_t x) {
-    x += dpp_u32<0x111, 0xF>(x);
-    x += dpp_u32<0x112, 0xF>(x);
-    x += dpp_u32<0x114, 0xF>(x);
-    x += dpp_u32<0x118, 0xF>(x);
-    x += dpp_u32<0x142, 0xA>(x);
-    x += dpp_u32<0x143, 0xC>(x);
-    return x;
-}
-
-__device__ __forceinline__ Seg seg_readlane(Seg v, int l) {
-    return Seg{__uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v.s), l)),
-               __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v.c), l)),
-               static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v.f), l))};
-}
-
-// Exclusive segmented scan of one element per thread over the block, in thread order
-// (REV: descending). Fixed tree: the wave scans above; then every wave scans the 16 wave totals
-// itself in the first row of its lanes (doubling steps in scan order) and takes its own prefix by
-// readlane, so one barrier suffices. The totals alternate between two LDS buffers (`phase`, the
-// same count in every thread): a wave that runs ahead writes the other buffer, and cannot get two
-// scans ahead, since writing again needs every wave past the barrier of the scan in between.
-// `total` receives the block's combined element. wtot: 2 kNW elements of LDS.
-template <bool REV>
-__device__ __forceinline__ Seg block_exclusive_seg(Seg agg, Seg* wtot, uint32_t& phase, Seg& total) {
-    static_assert(kNW == 16, "one DPP row of wave totals");
-    const int lane = static_cast<int>(lane_id());
-    const int w = threadIdx.x / kWave;
-    Seg* buf = wtot + (phase & 1u) * kNW;
-    ++phase;
-    const Seg incl = wave_inclusive_seg<REV>(agg);
-    const Seg ex = REV ? seg_dpp<0x130, 0xF>(incl) : seg_dpp<0x138, 0xF>(incl);
-    if (REV ? (lane == 0) : (lane == kWave - 1)) buf[w] = incl;
-    lds_barrier();
-    // Lane i < 16 holds the i-th wave total in scan order.
-    const Seg v = lane < kNW ? buf[REV ? kNW - 1 - lane : lane] : seg_zero();
-    Seg inc = seg_combine(seg_dpp<0x111, 0xF>(v), v);
-    inc = seg_combine(seg_dpp<0x112, 0xF>(inc), inc);
-    inc = seg_combine(seg_dpp<0x114, 0xF>(inc), inc);
-    inc = seg_combine(seg_dpp<0x118, 0xF>(inc), inc);
-    const Seg exw = seg_dpp<0x111, 0xF>(inc);
-    total = seg_readlane(inc, kNW - 1);
-    return seg_combine(seg_readlane(exw, REV ? kNW - 1 - w : w), ex);
-}
-
-// Exclusive integer sum over the block in thread order; `total` receives the block sum.
-// wsum: 2 kNW words of LDS, used in alternation as in block_exclusive_seg.
-__device__ __forceinline__ uint32_t block_exclusive_add(uint32_t v, uint32_t* wsum, uint32_t& phase, uint32_t& total) {
-    const int lane = static_cast<int>(lane_id());
-    const int w = threadIdx.x / kWave;
-    uint32_t* buf = wsum + (phase & 1u) * kNW;
-    ++phase;
-    const uint32_t incl = wave_inclusive_add(v);
-    if (lane == kWave - 1) buf[w] = incl;
-    lds_barrier();
-    const uint32_t x = lane < kNW ? buf[lane & (kNW - 1)] : 0u;
-    uint32_t inc = x;
-    inc += dpp_u32<0x111, 0xF>(inc);
-    inc += dpp_u32<0x112, 0xF>(inc);
-    inc += dpp_u32<0x114, 0xF>(inc);
-    inc += dpp_u32<0x118, 0xF>(inc);
-    total = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(inc), kNW - 1));
-    const uint32_t pre = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(inc - x), w));
-    return pre + incl - v;
-}
 
 // Stable LSD radix sort of the block's kNT * IPT (key, value) pairs over key bits [0, bits), in
 // the fewest passes of at most `dmax` bits, the bits shared out evenly among them. Items live in registers in striped order (item k of lane l of wave
@@ -393,16 +218,6 @@ struct Entry {
     uint32_t gsize;  // valid entries of its group
     float v;
 };
-
-// Slot id i of an int32 or int64 id array (absolute slots are below 2^31 either way).
-template <bool ID64>
-__device__ __forceinline__ int64_t load_id(const void* ids, int64_t i) {
-    if constexpr (ID64) {
-        return static_cast<const int64_t*>(ids)[i];
-    } else {
-        return static_cast<const int32_t*>(ids)[i];
-    }
-}
 
 // LG: gates per (token, K lane), [N, C, W], read from global memory where a scan needs one;
 // otherwise per token, [N, C], staged in LDS. ID64: slot ids are int64 (else int32).
@@ -1064,8 +879,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
 // order fixed by the input (hot batches in position order, then the walks).
 struct PairArgs {
     const uint4* rec;
-    const uint16_t* inv_k;   // entry-order sorted positions | kInvWalk, per kind
-    const uint16_t* inv_q;
+    const void* inv_k;   // entry-order words per kind (InvBits: 16-bit, or 32-bit for long rows)
+    const void* inv_q;
     const uint2* hot;   // per chunk: {count, 0}, then {head position, size} in position order (NULL: none)
     float* a;
     float* qk;
@@ -1110,7 +925,7 @@ __host__ __device__ inline PairLds pair_lds_layout(int C, int hot_cap, int gb) {
     return l;
 }
 
-template <int kPairThreads>
+template <int kPairThreads, typename InvT>
 __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
     constexpr int kPairWaves = kPairThreads / kWave;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -1352,7 +1167,7 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
     if (i < tv) {
         float* row = tri + tri_row(i);
         const int lanes = q ? R : W;
-        const uint16_t* iv = (q ? a.inv_q : a.inv_k) + (static_cast<int64_t>(c) * C + i) * lanes;
+        const InvT* iv = static_cast<const InvT*>(q ? a.inv_q : a.inv_k) + (static_cast<int64_t>(c) * C + i) * lanes;
         // Token i's entries of this kind: (Q flag, token) bits of the payload.
         const uint32_t own_tag = (q ? kIsQ : 0u) | (static_cast<uint32_t>(i) << kTokShift);
         const uint32_t tag_mask = kIsQ | (0xFFu << kTokShift);
@@ -1361,8 +1176,8 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
         auto walk_start = [&](int ln) {
             const uint32_t word = iv[ln];
             // A walk start has an earlier entry in its group, so 1 <= rho (the clamp only guards).
-            const int rho = min(static_cast<int>(word & kMetaPos), n - 1);
-            if (word & kInvHot) {   // walked only if its group was too wide for the dense pass
+            const int rho = min(static_cast<int>(word & InvBits<InvT>::kPos), n - 1);
+            if (word & InvBits<InvT>::kHot) {   // walked only if its group was too wide for the dense pass
                 int lo_g = 0, hi_g = nh - 1;   // the last hot group with head <= rho
                 while (lo_g < hi_g) {
                     const int mid = (lo_g + hi_g + 1) >> 1;
@@ -1432,7 +1247,7 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
         };
         for (int lb = 0; lb < lanes; lb += 32) {
           uint32_t flags = 0;
-          const uint32_t walk_bits = any_wide ? (kInvWalk | kInvHot) : kInvWalk;
+          const uint32_t walk_bits = any_wide ? (InvBits<InvT>::kWalk | InvBits<InvT>::kHot) : InvBits<InvT>::kWalk;
 #pragma unroll
           for (int u = 0; u < 32; ++u) {
               const int ln = lb + u;
@@ -1611,6 +1426,12 @@ __global__ void __launch_bounds__(kOrdThreads) p1_ordinal_kernel(const uint32_t*
 
 }  // namespace
 
+thread_local const char* g_p1_stage = "";
+
+bool p1_tiled(const sdm_p1_shape* s) {
+    return s->tiled != 0 || static_cast<int64_t>(s->C) * (s->W + s->R) > kP1MaxRow;
+}
+
 P1Workspace p1_workspace_layout(const sdm_p1_shape* s) {
     const size_t n = static_cast<size_t>(s->C) * static_cast<size_t>(s->W + s->R);
     const size_t N = static_cast<size_t>(s->N);
@@ -1618,27 +1439,99 @@ P1Workspace p1_workspace_layout(const sdm_p1_shape* s) {
     const size_t nq = N * static_cast<size_t>(s->C) * static_cast<size_t>(s->R);
     auto up = [](size_t b) { return (b + 255) / 256 * 256; };
     P1Workspace w;
+    w.tiled = p1_tiled(s);
+    const size_t ib = w.tiled ? sizeof(uint32_t) : sizeof(uint16_t);   // entry-order pair words
     w.rec_off = 0;
     w.inv_k_off = up(N * n * sizeof(uint4));
-    w.inv_q_off = w.inv_k_off + up(nk * sizeof(uint16_t));
+    w.inv_q_off = w.inv_k_off + up(nk * ib);
     w.hot_cap = s->C * s->W / kHotMin;
-    w.hot_off = w.inv_q_off + up(nq * sizeof(uint16_t));
+    w.hot_off = w.inv_q_off + up(nq * ib);
     w.total = w.hot_off + up(N * static_cast<size_t>(w.hot_cap + 1) * sizeof(uint2));
+    w.sort_off = w.rev_off = 0;
+    if (w.tiled) {   // the tiled path's sort buffers (keys and entry indices, two of each) and reverse-scan results
+        w.sort_off = w.total;
+        w.rev_off = w.sort_off + up(N * n * 4 * sizeof(uint32_t));
+        w.total = w.rev_off + up(N * n * 3 * sizeof(uint32_t));
+    }
     return w;
 }
 
-size_t p1_pair_lds_min(const sdm_p1_shape* s) {
-    return pair_lds_layout(s->C, s->C * s->W / kHotMin, 0).total + kPairStaticLds;
-}
+// (Without hot groups the pair kernel keeps only its triangle and a few words in LDS.)
+size_t p1_pair_lds_min(const sdm_p1_shape* s) { return pair_lds_layout(s->C, 0, 0).total + kPairStaticLds; }
 
 size_t p1_lds_bytes(const sdm_p1_shape* s, const sdm_p1_io* io) {
+    if (p1_tiled(s)) return p1_tiled_lds_bytes(s);
     return plan_main(s, io->a != nullptr || io->qk != nullptr).lds_bytes;
+}
+
+PairPlan pair_plan(const sdm_p1_shape* s, bool pairs, int lds_max) {
+    // Hot groups only when the pair kernel's x and y tables hold at least 4 groups beside the rest.
+    // Groups per batch: as many as the blocks per compute unit that 4 groups allow still fit.
+    PairPlan pp;
+    pp.hot_cap = s->C * s->W / kHotMin;
+    const size_t pair_fixed = pair_lds_layout(s->C, pp.hot_cap, 0).total + kPairStaticLds;
+    const size_t per_group = 2 * static_cast<size_t>((s->C + 3) & ~3) * sizeof(float);
+    const size_t pair_min = pair_fixed + 4 * per_group;
+    pp.blocks_cu = pair_min <= static_cast<size_t>(lds_max) ? static_cast<int>(lds_max / pair_min) : 0;
+    pp.gb = pp.blocks_cu > 0 ? min(kPairBatchGroups,
+                                   static_cast<int>((static_cast<size_t>(lds_max) / pp.blocks_cu - pair_fixed) / per_group))
+                             : 0;
+    // (A hot list too long for LDS beside the triangle, as with C = 256, W = 256: every group walked.)
+    pp.hot_on = pairs && pp.hot_cap > 0 && pp.gb >= 4;
+    if (!pp.hot_on) {   // the triangle alone per block
+        pp.gb = 0;
+        pp.blocks_cu = max(1, static_cast<int>(static_cast<size_t>(lds_max) / (pair_lds_layout(s->C, 0, 0).total + kPairStaticLds)));
+    }
+    return pp;
+}
+
+hipError_t p1_ordinal_launch(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st) {
+    if (io->gord_k == nullptr) return hipSuccess;   // (on st, after the kernel that writes spay_k)
+    g_p1_stage = "group ordinal kernel";
+    const uint32_t* sp = reinterpret_cast<const uint32_t*>(io->spay_k);
+    int32_t* gord = io->gord_k;
+    int cw = s->C * s->W;
+    void* kargs[] = {&sp, &gord, &cw};
+    // (the launch's own status: a pending error of an earlier call is not this launch's)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&p1_ordinal_kernel), dim3(s->N), dim3(kOrdThreads), kargs, 0, st);
+}
+
+hipError_t pair_launch(const P1Launch& Lc, const PairPlan& pp, bool inv32, hipStream_t st) {
+    const sdm_p1_shape* s = Lc.s;
+    const sdm_p1_io* io = Lc.io;
+    PairArgs pa;
+    pa.rec = static_cast<const uint4*>(Lc.rec);
+    pa.inv_k = Lc.inv_k;
+    pa.inv_q = Lc.inv_q;
+    // Hot groups off: no list (the Phase-1 kernels flag no entry as hot), and no LDS for one.
+    pa.hot = pp.hot_on ? static_cast<const uint2*>(Lc.hot) : nullptr;
+    pa.hot_cap = pp.hot_on ? pp.hot_cap : 0;
+    pa.gb = pp.hot_on ? pp.gb : 0;
+    pa.a = io->a;
+    pa.qk = io->qk;
+    pa.C = s->C;
+    pa.W = s->W;
+    pa.R = s->R;
+    pa.first_partial = s->first_partial;
+    pa.valid_last = s->valid_last;
+    const size_t lds = pair_lds_layout(s->C, pa.hot_cap, pa.gb).total;
+    const int threads = pp.blocks_cu == 1 ? 1024 : 512;
+    const void* fn = inv32 ? (threads == 1024 ? reinterpret_cast<const void*>(&p1_pairs_kernel<1024, uint32_t>)
+                                              : reinterpret_cast<const void*>(&p1_pairs_kernel<512, uint32_t>))
+                           : (threads == 1024 ? reinterpret_cast<const void*>(&p1_pairs_kernel<1024, uint16_t>)
+                                              : reinterpret_cast<const void*>(&p1_pairs_kernel<512, uint16_t>));
+    void* kargs[] = {&pa};
+    g_p1_stage = "pair kernel";
+    hipEvent_t e0 = io->events != nullptr ? io->events[2] : nullptr, e1 = io->events != nullptr ? io->events[3] : nullptr;
+    return hipExtLaunchKernel(fn, dim3(s->N, 2), dim3(threads), kargs, lds, st, e0, e1, 0);
 }
 
 hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     const sdm_p1_shape* s = Lc.s;
     const sdm_p1_io* io = Lc.io;
     if (s->N == 0) return hipSuccess;
+    if (p1_tiled(s)) return p1_tiled_launch(Lc, st);
+    g_p1_stage = "sort/scan kernel";
     const bool pairs = io->a != nullptr || io->qk != nullptr;
     P1Args a;
     a.k_idx = io->k_idx;
@@ -1680,20 +1573,10 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
     a.perm = io->perm;
     a.status = io->status;
     a.rec = pairs ? static_cast<uint4*>(Lc.rec) : nullptr;
-    // Hot groups only when the pair kernel's x and y tables hold at least 4 groups beside the rest.
-    // Groups per batch: as many as the blocks per compute unit that 4 groups allow still fit.
-    const int hot_cap = s->C * s->W / kHotMin;
-    const size_t pair_fixed = pair_lds_layout(s->C, hot_cap, 0).total + kPairStaticLds;
-    const size_t per_group = 2 * static_cast<size_t>((s->C + 3) & ~3) * sizeof(float);
-    const size_t pair_min = pair_fixed + 4 * per_group;
-    const int blocks_cu = pair_min <= static_cast<size_t>(Lc.lds_max) ? static_cast<int>(Lc.lds_max / pair_min) : 0;
-    const int gb = blocks_cu > 0 ? min(kPairBatchGroups,
-                                       static_cast<int>((static_cast<size_t>(Lc.lds_max) / blocks_cu - pair_fixed) / per_group))
-                                 : 0;
-    const bool hot_on = pairs && hot_cap > 0 && gb >= 4;
+    const PairPlan pp = pair_plan(s, pairs, Lc.lds_max);
     a.hot = pairs ? static_cast<uint2*>(Lc.hot) : nullptr;
-    a.hot_min = hot_on ? kHotMin : 0x7FFFFFFF;
-    a.hot_cap = hot_cap;
+    a.hot_min = pp.hot_on ? kHotMin : 0x7FFFFFFF;
+    a.hot_cap = pp.hot_cap;
     a.C = s->C;
     a.W = s->W;
     a.R = s->R;
@@ -1726,32 +1609,9 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
         case 8: e = launch_main<8>(a, s->g_lane_stride != 0, s->idx_bytes == 8, vbf, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
         default: e = launch_main<16>(a, s->g_lane_stride != 0, s->idx_bytes == 8, vbf, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
     }
-    if (e == hipSuccess && io->gord_k != nullptr) {   // (on st, after the sort/scan kernel's spay_k)
-        hipLaunchKernelGGL(p1_ordinal_kernel, dim3(s->N), dim3(kOrdThreads), 0, st,
-                           reinterpret_cast<const uint32_t*>(io->spay_k), io->gord_k, s->C * s->W);
-        e = hipGetLastError();
-    }
+    if (e == hipSuccess) e = p1_ordinal_launch(s, io, st);
     if (e != hipSuccess || !pairs) return e;
-    PairArgs pa;
-    pa.rec = static_cast<const uint4*>(Lc.rec);
-    pa.inv_k = static_cast<const uint16_t*>(Lc.inv_k);
-    pa.inv_q = static_cast<const uint16_t*>(Lc.inv_q);
-    pa.hot = static_cast<const uint2*>(Lc.hot);
-    pa.hot_cap = hot_cap;
-    pa.gb = hot_on ? gb : 0;
-    pa.a = io->a;
-    pa.qk = io->qk;
-    pa.C = s->C;
-    pa.W = s->W;
-    pa.R = s->R;
-    pa.first_partial = s->first_partial;
-    pa.valid_last = s->valid_last;
-    const size_t lds = pair_lds_layout(s->C, hot_cap, pa.gb).total;
-    const int threads = blocks_cu == 1 ? 1024 : 512;
-    const void* fn = threads == 1024 ? reinterpret_cast<const void*>(&p1_pairs_kernel<1024>)
-                                     : reinterpret_cast<const void*>(&p1_pairs_kernel<512>);
-    void* kargs[] = {&pa};
-    return hipExtLaunchKernel(fn, dim3(s->N, 2), dim3(threads), kargs, lds, st, ev[2], ev[3], 0);
+    return pair_launch(Lc, pp, false, st);
 }
 
 int p1_lds_kernels(const void** fns, int cap) {
@@ -1773,8 +1633,11 @@ int p1_lds_kernels(const void** fns, int cap) {
             add(main_fn<16, true>(lg, id64));
         }
     }
-    add(reinterpret_cast<const void*>(&p1_pairs_kernel<1024>));
-    add(reinterpret_cast<const void*>(&p1_pairs_kernel<512>));
+    add(reinterpret_cast<const void*>(&p1_pairs_kernel<1024, uint16_t>));
+    add(reinterpret_cast<const void*>(&p1_pairs_kernel<512, uint16_t>));
+    add(reinterpret_cast<const void*>(&p1_pairs_kernel<1024, uint32_t>));
+    add(reinterpret_cast<const void*>(&p1_pairs_kernel<512, uint32_t>));
+    n += p1_tiled_lds_kernels(fns + n, cap - n);
     return n;
 }
 

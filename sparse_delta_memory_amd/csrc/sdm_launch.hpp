@@ -9,8 +9,10 @@
 
 namespace sdm {
 
-// Longest chunk row (C * (W + R)) one Phase-1 workgroup sorts and scans on chip.
+// Longest chunk row (C * (W + R)) one Phase-1 workgroup sorts and scans on chip; longer rows (up
+// to 2^17 entries) take the tiled path.
 constexpr int kP1MaxRow = 16384;
+constexpr int kP1MaxTiledRow = 1 << 17;
 constexpr int kP1Threads = 1024;
 
 // Valid K entries that make a slot group "hot": the pair kernel sums such groups densely.
@@ -22,6 +24,9 @@ constexpr int kHotMin = 16;
 int p1_lds_kernels(const void** fns, int cap);
 int read_lds_kernels(const void** fns, int cap);
 
+// The kernel a Phase-1 launch sequence was enqueuing when it failed (for the error message).
+extern thread_local const char* g_p1_stage;
+
 struct P1Launch {
     const sdm_p1_shape* s;
     const sdm_p1_io* io;
@@ -31,15 +36,39 @@ struct P1Launch {
                       // ordinary (not hot) group
     void* inv_q;      // [N, C*R] the same for the Q entries
     void* hot;        // [N, hot_cap + 1] uint2: count, then {head position, size} of each hot group
+    void* sort;       // tiled path: [N, 4, n] uint32 key and entry-index buffers (two of each)
+    void* rev;        // tiled path: [N, n, 3] uint32 reverse-scan results per sorted position
     int lds_max;      // LDS bytes per block of the device
 };
 
-// Workspace layout of sdm_phase1: byte offsets of the regions and the total.
+// The pair kernel's plan: hot groups per chunk, groups per batch, blocks per compute unit, and
+// whether hot groups are summed densely (the Phase-1 kernels then list them).
+struct PairPlan {
+    int hot_cap, gb, blocks_cu;
+    bool hot_on;
+};
+PairPlan pair_plan(const sdm_p1_shape* s, bool pairs, int lds_max);
+// The pair kernel on st (inv32: 32-bit entry-order words of the tiled path).
+hipError_t pair_launch(const P1Launch& L, const PairPlan& pp, bool inv32, hipStream_t st);
+// The dense group ordinals (gord_k) on st, when asked for.
+hipError_t p1_ordinal_launch(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st);
+// The tiled path: its kernel, then the ordinals and the pair kernel.
+hipError_t p1_tiled_launch(const P1Launch& L, hipStream_t st);
+size_t p1_tiled_lds_bytes(const sdm_p1_shape* s);
+int p1_tiled_lds_kernels(const void** fns, int cap);
+
+// Workspace layout of sdm_phase1: byte offsets of the regions and the total. The tiled path
+// (rows longer than kP1MaxRow, or shape->tiled) adds its sort buffers and reverse-scan results and
+// keeps 32-bit entry-order pair words.
 struct P1Workspace {
-    size_t rec_off, inv_k_off, inv_q_off, hot_off, total;
+    size_t rec_off, inv_k_off, inv_q_off, hot_off, sort_off, rev_off, total;
     int hot_cap;      // hot groups a chunk can hold: C * W / kHotMin
+    bool tiled;
 };
 P1Workspace p1_workspace_layout(const sdm_p1_shape* s);
+
+// Whether a shape goes through the tiled (long-row) path.
+bool p1_tiled(const sdm_p1_shape* s);
 
 // Dynamic LDS bytes of the Phase-1 sort/scan kernel for this shape and output set.
 size_t p1_lds_bytes(const sdm_p1_shape* s, const sdm_p1_io* io);

@@ -19,12 +19,12 @@ F32_REL, F32_ABS = 1e-5, 1e-6
 READ_RTOL_MAG = 1e-4   # read side: times the oracle's magnitude bound, plus 1e-6
 
 
-def shape_of(wl: W.Workload, tile_len: int = 128):
+def shape_of(wl: W.Workload, tile_len: int = 128, tiled: bool = False):
     s = wl.shape
     return sdm.make_shape(wl.N, s.C, s.W, s.R, P=s.P, key_bits=s.key_bits, stream_offset=s.S,
                           first_partial=wl.first_partial, valid_last=wl.valid_last, tile_len=tile_len,
                           g_lane_stride=1 if wl.g.ndim == 3 else 0, idx_bytes=wl.k_idx.dtype.itemsize,
-                          val_bytes=2 if wl.val_bf16 else 4)
+                          val_bytes=2 if wl.val_bf16 else 4, tiled=tiled)
 
 
 def device_inputs(wl: W.Workload, dev="cuda"):
@@ -42,11 +42,12 @@ def device_dv(wl: W.Workload, dev="cuda"):
     return dv.to(torch.bfloat16) if wl.shape.dv_dtype == "bf16" else dv
 
 
-def run_phase1(wl: W.Workload, dev="cuda", tile_len=128, fields=None):
-    """Phase 1 of every chunk on the device; `fields` adds optional outputs (e.g. "perm")."""
+def run_phase1(wl: W.Workload, dev="cuda", tile_len=128, fields=None, tiled=False):
+    """Phase 1 of every chunk on the device; `fields` adds optional outputs (e.g. "perm"); tiled:
+    through the tiled path whatever the row length."""
     import torch
 
-    shape = shape_of(wl, tile_len)
+    shape = shape_of(wl, tile_len, tiled)
     ins = device_inputs(wl, dev)
     out = None
     if fields is not None:

@@ -31,7 +31,7 @@ def test_exports_every_declared_function():
 
 def shape(**kw):
     d = dict(N=4, C=64, W=4, R=4, P=1, key_bits=12, stream_offset=0, first_partial=4, valid_last=64, tile_len=128,
-             g_lane_stride=0, idx_bytes=4, val_bytes=4)
+             g_lane_stride=0, idx_bytes=4, val_bytes=4, tiled=0)
     d.update(kw)
     return _lib.P1Shape(*[d[f] for f, _ in _lib.P1Shape._fields_])
 
@@ -64,13 +64,31 @@ def call_p1(s, o):
     (dict(g_lane_stride=2), _lib.SDM_EINVAL), (dict(g_lane_stride=-1), _lib.SDM_EINVAL),
     (dict(idx_bytes=2), _lib.SDM_EINVAL), (dict(idx_bytes=16), _lib.SDM_EINVAL),
     (dict(val_bytes=1), _lib.SDM_EINVAL), (dict(val_bytes=8), _lib.SDM_EINVAL),
-    (dict(C=256, W=256, R=256), _lib.SDM_EUNSUPPORTED), (dict(C=256, W=40, R=40), _lib.SDM_EUNSUPPORTED),
+    (dict(tiled=2), _lib.SDM_EINVAL), (dict(tiled=-1), _lib.SDM_EINVAL),
 ])
 def test_phase1_shape_refusals(kw, status):
     s = shape(**kw)
     assert call_p1(s, io()) == status
     assert _lib.load().sdm_phase1_workspace(ctypes.byref(s)) == 0
     assert len(_lib.load().sdm_last_error()) > 0
+
+
+def test_long_rows_take_the_tiled_path():
+    """Rows past 16384 entries (up to C (W + R) = 2^17) are accepted and sized with the tiled path's
+    workspace: its sort buffers and reverse-scan results on top of the pair records and 32-bit
+    entry-order words; tiled = 1 asks for the same layout at any size."""
+    lib = _lib.load()
+    up = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    for C, W, R, tiled in ((256, 256, 256, 0), (256, 48, 48, 0), (64, 4, 4, 1)):
+        s = shape(N=2, C=C, W=W, R=R, first_partial=2, valid_last=C, tiled=tiled)
+        n, N = C * (W + R), 2
+        hot = C * W // 16
+        want = (up(N * n * 16) + up(N * C * W * 4) + up(N * C * R * 4) + up(N * (hot + 1) * 8)
+                + up(N * n * 16) + up(N * n * 12))
+        assert lib.sdm_phase1_workspace(ctypes.byref(s)) == want
+    s = shape(N=2, C=64, W=4, R=4, first_partial=2, valid_last=64)   # on chip: 16-bit words, no sort buffers
+    n = 64 * 8
+    assert lib.sdm_phase1_workspace(ctypes.byref(s)) == up(2 * n * 16) + 2 * up(2 * 64 * 4 * 2) + up(2 * 17 * 8)
 
 
 def test_phase1_argument_refusals():
