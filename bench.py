@@ -492,6 +492,7 @@ def measure_gwr_pa(wl, shape, out, ins, bank, stream, sdm, torch, W):
     snap = torch.zeros((P * C * Wn, hd), dtype=bank.dtype, device=dev)
     work = bank.clone()
     plan = sdm.DwPlan(work, dv, out["krec"], shape, dv_step_rows=P * C, snapshot=snap, snap_step_rows=0)
+    pa_ws = sdm.alloc_pa_workspace(shape, hd, device=dev)   # long write groups split across waves
     kr = out["krec"][..., 0]
     groups = float((((kr & W_FIRST) != 0) & ((kr & W_INVALID) == 0)).view(wl.steps, -1).sum(dim=1).float().mean())
     ev_g, ev_p = [], []
@@ -505,7 +506,7 @@ def measure_gwr_pa(wl, shape, out, ins, bank, stream, sdm, torch, W):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         sdm.pa_step(grad, snap, out, beta, d_dva, shape, ti, step_rows=P * C, snap_step_rows=0, bank=work,
-                    g_decay=g_decay, d_k_eff=d_k_eff, stream=stream)
+                    g_decay=g_decay, d_k_eff=d_k_eff, stream=stream, workspace=pa_ws)
         b.record(stream)
         ev_p.append((a, b))
     torch.cuda.synchronize()

@@ -405,7 +405,20 @@ typedef struct sdm_pa_io {
     float* d_k_eff;         /* OUT (NULL: skipped) [N, C, W]: d_k_eff of the step's entries, 0 for padding */
     int32_t P, C, W, N;     /* the Phase-1 shape */
     int32_t val_bytes;      /* type of k_eff: 0 or 4 = float32, 2 = bf16 */
+    void* workspace;        /* optional (NULL: every group is walked by one wave): device memory of
+                               sdm_pa_workspace() bytes, 16-byte aligned, ZERO-FILLED before its first
+                               use; every call leaves it zero-filled where it must be. With it, a group
+                               longer than 32 members is split into 32-member segments walked by waves
+                               of their own; the segments' partial sums are added in segment order by
+                               the last segment to finish. Calls sharing one workspace must not run
+                               concurrently. */
+    size_t workspace_bytes;
 } sdm_pa_io;
+
+/* Workspace bytes sdm_pa_step can use for this shape: per block of 32 K-row positions of the step
+   (B = ceil(P * C * W / 32) blocks) an arrival counter and a segment count (8 B) and two float32
+   partial rows (8 hd B), each region rounded up to 256 bytes. */
+size_t sdm_pa_workspace(const sdm_pa_io* io);
 
 /*
  * PA (page "sparse_delta_memory/cuda/pa_dc_cuda.py", module docstring: Phase A of the deterministic
@@ -414,7 +427,9 @@ typedef struct sdm_pa_io {
  *   grad[s]         = fma(gdw, cpe, sum_m sc_m d_dva[tok_m])   (sum from +0, sc_m = -beta k_eff_m),
  *   bank[s]         = snap,
  *   grad_g_decay[e] = cpe <gdw, snap>,   d_k_eff[e] = -beta[tok_e] <d_dva[tok_e], snap>.
- * One wave per group (the only writer of its rows and entries): reproducible. Padding entries get
+ * With a workspace, a group longer than 32 members sums sc_m d_dva[tok_m] per 32-member segment
+ * (each from +0) and adds the partials in segment order before the final fma.
+ * One writer per row and per entry, fixed sum orders: reproducible. Padding entries get
  * zeros; masked tokens' rows are never read. Requires (ti + 1) * P <= N, hd a multiple of 4 up to
  * 1024, 16-byte aligned grad, bank, snap and d_dva rows (8 for bf16 rows), 16-byte aligned krec.
  */

@@ -18,7 +18,8 @@ from . import _lib
 from ._lib import P1IO, P1Shape, SdmError  # noqa: F401
 
 __all__ = ["P1Shape", "phase1", "phase1_workspace_bytes", "alloc_phase1_outputs", "dw_step", "dw_workspace_bytes",
-           "alloc_dw_workspace", "DwPlan", "ReadPlan", "read_step", "gds_step", "gwr_step", "pa_step", "SdmError", "make_shape",
+           "alloc_dw_workspace", "DwPlan", "ReadPlan", "read_step", "gds_step", "gwr_step", "pa_step", "pa_workspace_bytes",
+           "alloc_pa_workspace", "SdmError", "make_shape",
            "timing_events"]
 
 
@@ -352,15 +353,30 @@ def gwr_step(grad, k_idx, w, dv, shape: P1Shape, ti: int, step_rows: int, d_dv=N
     _lib.check(lib.sdm_gwr_step(ctypes.byref(io), int(ti), ctypes.c_void_p(st.cuda_stream)))
 
 
+def pa_workspace_bytes(shape: P1Shape, hd: int) -> int:
+    """Bytes of the (zero-filled) PA workspace that lets long write groups be split across waves."""
+    io = _lib.PaIO()
+    io.P, io.C, io.W, io.N, io.hd = shape.P, shape.C, shape.W, shape.N, int(hd)
+    return int(_lib.load().sdm_pa_workspace(ctypes.byref(io)))
+
+
+def alloc_pa_workspace(shape: P1Shape, hd: int, device="cuda"):
+    """A zero-filled PA workspace (reusable by every step of the same shape)."""
+    import torch
+
+    return torch.zeros(max(pa_workspace_bytes(shape, hd), 1), dtype=torch.uint8, device=device)
+
+
 def pa_step(grad, snap, p1, beta, d_dva, shape: P1Shape, ti: int, step_rows: int, snap_step_rows: int, bank=None,
-            g_decay=None, d_k_eff=None, stream=None):
+            g_decay=None, d_k_eff=None, stream=None, workspace=None):
     """PA of step `ti` (the backward of DW) on the current (or given) stream.
 
     grad [rows, hd] float32 or bfloat16 bank gradient, updated in place at the step's written slots;
     snap: the step's compact snapshot from DwPlan (FIRST-position layout, raw rows in the bank dtype);
     p1: the Phase-1 outputs (krec, k_eff); beta [N, C] float32; d_dva [*, hd] float32 gradient token
     rows, row ti*step_rows + p*C + t. bank (optional) gets each written slot's row restored from the
-    snapshot; g_decay and d_k_eff [N, C, W] float32 (optional) receive the per-entry gradients."""
+    snapshot; g_decay and d_k_eff [N, C, W] float32 (optional) receive the per-entry gradients.
+    workspace (optional, alloc_pa_workspace): long write groups are split across waves."""
     import torch
 
     for name, t in (("beta", beta), ("d_dva", d_dva), ("g_decay", g_decay), ("d_k_eff", d_k_eff)):
@@ -388,5 +404,8 @@ def pa_step(grad, snap, p1, beta, d_dva, shape: P1Shape, ti: int, step_rows: int
     io.d_k_eff = _ptr(d_k_eff)
     io.P, io.C, io.W, io.N = shape.P, shape.C, shape.W, shape.N
     io.val_bytes = p1["k_eff"].element_size()
+    if workspace is not None:
+        io.workspace = workspace.data_ptr()
+        io.workspace_bytes = workspace.numel() * workspace.element_size()
     st = torch.cuda.current_stream(grad.device) if stream is None else stream
     _lib.check(lib.sdm_pa_step(ctypes.byref(io), int(ti), ctypes.c_void_p(st.cuda_stream)))

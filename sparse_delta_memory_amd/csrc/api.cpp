@@ -176,6 +176,11 @@ size_t sdm_dw_workspace(const sdm_dw_io* io) {
     return sdm::dw_workspace_layout(io).total;
 }
 
+size_t sdm_pa_workspace(const sdm_pa_io* io) {
+    if (io == nullptr || io->P < 1 || io->C < 1 || io->W < 1 || io->hd < 1) return 0;
+    return sdm::pa_workspace_layout(io).total;
+}
+
 size_t sdm_phase1_workspace(const sdm_p1_shape* s) {
     if (check_p1_shape(s) != SDM_OK) return 0;
     return sdm::p1_workspace_layout(s).total;
@@ -406,6 +411,12 @@ sdm_status sdm_pa_step(const sdm_pa_io* io, int64_t ti, hipStream_t st) {
     if (!aligned(io->k_eff, io->val_bytes == 2 ? 2 : 4) || !aligned(io->beta, 4) || !aligned(io->g_decay, 4) ||
         !aligned(io->d_k_eff, 4))
         return fail(SDM_EALIGN, "sdm_pa_step: k_eff, beta, g_decay or d_k_eff misaligned");
+    if (io->workspace != nullptr) {
+        if (!aligned(io->workspace, 16)) return fail(SDM_EALIGN, "sdm_pa_step: workspace is not 16-byte aligned");
+        const size_t need = sdm::pa_workspace_layout(io).total;
+        if (io->workspace_bytes < need)
+            return fail(SDM_EWORKSPACE, "sdm_pa_step: workspace needs %zu bytes, got %zu", need, io->workspace_bytes);
+    }
     const hipError_t e = sdm::pa_launch(io, ti, st);
     if (e != hipSuccess) {
         (void)hipGetLastError();

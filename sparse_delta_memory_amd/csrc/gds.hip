@@ -195,8 +195,9 @@ struct GwrArgs {
     int P, C, W, hd, first_partial, valid_last, id64, grad_bf16;
 };
 
-constexpr int kGwrColBlocks = 4;   // 256-column blocks per row (hd <= 1024)
-
+// NCB: the 256-column blocks a lane's registers hold (1, 2 or 4: hd <= 256, 512, 1024), so that
+// narrow rows keep few registers and many waves per SIMD.
+template <int NCB>
 __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
     const int wv = static_cast<int>(threadIdx.x) / kWave;
     const int lane = static_cast<int>(lane_id());
@@ -217,9 +218,9 @@ __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
         }
         return;
     }
-    float4 v[kGwrColBlocks], acc[kGwrColBlocks];
+    float4 v[NCB], acc[NCB];
 #pragma unroll
-    for (int cb = 0; cb < kGwrColBlocks; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb) {
         const int col = cb * 4 * kWave + 4 * lane;
         v[cb] = col < a.hd ? *reinterpret_cast<const float4*>(a.dv + vrow * a.hd + col) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         acc[cb] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -243,7 +244,7 @@ __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
                 part[u] = 0.0f;
             }
 #pragma unroll
-            for (int cb = 0; cb < kGwrColBlocks; ++cb) {
+            for (int cb = 0; cb < NCB; ++cb) {
                 const int col = cb * 4 * kWave + 4 * lane;
                 if (col >= a.hd) break;
                 float4 g[kDotReads];
@@ -271,7 +272,7 @@ __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
     }
     if (a.d_dv != nullptr) {
 #pragma unroll
-        for (int cb = 0; cb < kGwrColBlocks; ++cb) {
+        for (int cb = 0; cb < NCB; ++cb) {
             const int col = cb * 4 * kWave + 4 * lane;
             if (col < a.hd) *reinterpret_cast<float4*>(a.d_dv + vrow * a.hd + col) = acc[cb];
         }
@@ -279,12 +280,13 @@ __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
 }
 
 // PA (page "sparse_delta_memory/cuda/pa_dc_cuda.py", module docstring: Phase A of the deterministic
-// backward, the backward of DW) for the chunks of one step. One wave per K-row position: a padding
-// entry writes its zeros; a valid group FIRST loads its slot's gradient row gdw and its snapshot row
-// (hd <= 1024: 4 columns of every 256 per lane), forms <gdw, snap> once, walks the members in
-// sorted order (token rows of 4 members in flight): acc = fma(-beta k_eff, d_dva[t], acc) from +0,
-// d_k_eff[e] = -beta <d_dva[t], snap>, grad_g_decay[e] = cpe <gdw, snap>; then grad[s] =
-// fma(gdw, cpe, acc) and bank[s] = snap. One writer per row and per entry: deterministic.
+// backward, the backward of DW) for the chunks of one step. A padding entry writes its zeros; a valid
+// group's gradient row gdw and snapshot row (hd <= 1024: 4 columns of every 256 per lane) give
+// <gdw, snap>; its members, in sorted order, give acc = fma(-beta k_eff, d_dva[t], acc) from +0,
+// d_k_eff[e] = -beta <d_dva[t], snap> and grad_g_decay[e] = cpe <gdw, snap>; then grad[s] =
+// fma(gdw, cpe, acc) and bank[s] = snap. A long group (more than 32 members, with a workspace) is
+// walked in segments of 32 members whose partial sums are added in segment order: one writer per row
+// and per entry, the same bits run to run.
 struct PaArgs {
     void* grad;
     void* bank;
@@ -295,11 +297,27 @@ struct PaArgs {
     const float* d_dva;
     float* g_decay;
     float* d_k_eff;
+    float* part;       // split groups (NULL: not split): two partial rows per block of kPaSeg positions
+    int* cnt;          // per block of kPaSeg positions (a split group's FIRST): arrival counter, zero between calls
+    int* meta;         // per block of kPaSeg positions: the group's segment count
     int64_t rows, chunk0, row0, snap_row0;
     int P, C, W, CW, hd, vbf, grad_bf16, bank_bf16;
 };
 
 constexpr int kPaMembers = 4;   // member token rows in flight together
+// Members per segment when long groups are split (a workspace is given), and the last in-group
+// distance that still marks a segment start (the distance field saturates at 4095).
+constexpr int kPaSeg = 32;
+constexpr int kPaSegLimit = (4095 / kPaSeg) * kPaSeg;
+// Workspace slots, by step-wide K-row position G (stream p's position j is p * CW + j): a split
+// group has more than kPaSeg members, so at most one split group's FIRST falls in each aligned
+// block of kPaSeg positions (its counter and segment count), and at most two segment starts (the
+// first segment of a group starting there, a later one of the group running through): two partial
+// rows per block.
+__device__ __forceinline__ int64_t pa_group_slot(int64_t g_first) { return g_first / kPaSeg; }
+__device__ __forceinline__ int64_t pa_part_row(int64_t g_start, bool first_segment) {
+    return 2 * (g_start / kPaSeg) + (first_segment ? 0 : 1);
+}
 
 __device__ __forceinline__ void store4(void* base, int bf, int64_t row, int hd, int col, float4 v) {
     if (bf) {
@@ -310,6 +328,13 @@ __device__ __forceinline__ void store4(void* base, int bf, int64_t row, int hd, 
     }
 }
 
+// One wave per K-row position that starts work: a group's FIRST or, with a workspace, every kPaSeg-th
+// member of a longer group. The wave walks its members in sorted order (64 records at a time,
+// kPaMembers token rows in flight): per member d_k_eff and g_decay, and acc = fma(sc, d_dva[tok], acc)
+// from +0. A group in one segment then writes grad = fma(gdw, cpe, acc) and restores the bank row;
+// a split group's segments publish their partial rows, and the last to arrive adds them in segment
+// order and writes the rows (the same sums whichever segment arrives last).
+template <int NCB>
 __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
     const int wv = static_cast<int>(threadIdx.x) / kWave;
     const int lane = static_cast<int>(lane_id());
@@ -329,15 +354,20 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
         }
         return;
     }
-    if (!(r0.x & kFirst)) return;   // a member: its group's wave writes it
+    const bool split = a.part != nullptr;
+    const int dist = static_cast<int>((r0.x >> kDistShift) & kDistMax);   // valid K entries before, in the group
+    const bool first = (r0.x & kFirst) != 0u;
+    if (!first && (!split || dist % kPaSeg != 0 || dist > kPaSegLimit)) return;   // a member another wave walks
+    const bool unbounded = !split || dist == kPaSegLimit;   // the last segment start runs to LAST
+    const int first_pos = j - dist;                          // the group's FIRST (its snapshot row)
     const int64_t slot = static_cast<int64_t>(r0.y);
     const bool in = slot < a.rows;   // (a slot outside the bank: zero rows, nothing written)
-    const float cpe = __uint_as_float(r0.w);
-    const int64_t srow = a.snap_row0 + static_cast<int64_t>(p) * a.CW + j;
-    float4 gdw[kGwrColBlocks], sn[kGwrColBlocks], acc[kGwrColBlocks];
+    const float cpe = __uint_as_float(r0.w);   // (every member's record holds the group's cpe)
+    const int64_t srow = a.snap_row0 + static_cast<int64_t>(p) * a.CW + first_pos;
+    float4 gdw[NCB], sn[NCB], acc[NCB];
     float part0 = 0.0f;
 #pragma unroll
-    for (int cb = 0; cb < kGwrColBlocks; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb) {
         const int col = cb * 4 * kWave + 4 * lane;
         const bool con = in && col < a.hd;
         gdw[cb] = con ? load4(a.grad, a.grad_bf16, slot, a.hd, col) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -347,8 +377,10 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
     }
     const float dot0 = wave_sum(part0);
     const int64_t grow0 = a.row0 + static_cast<int64_t>(p) * a.C;
-    bool done = false;
+    bool done = false, last_seen = false;
+    int taken = 0;
     for (int m0 = j; !done && m0 < a.CW; m0 += kWave) {   // members 64 records at a time, in sorted order
+        const int budget = unbounded ? kWave : min(kWave, kPaSeg - taken);   // members this segment may still take
         const int m = m0 + lane;
         const uint32_t el = m < a.CW ? kr[m].x : (kFirst | kLast | kInvalid);
         const int tk = static_cast<int>((el >> kTokShift) & 0xFFu);
@@ -356,11 +388,13 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
         const float nb = valid ? -a.beta[c * a.C + tk] : 0.0f;
         const float w = valid ? nb * load_val(a.k_eff, eidx(el), a.vbf) : 0.0f;
         const int64_t ei = valid ? eidx(el) : 0;
-        const uint64_t lastm = __ballot((el & kLast) != 0u);
-        const int cnt = lastm != 0ull ? __builtin_ctzll(lastm) + 1 : kWave;   // (LAST included)
-        done = lastm != 0ull;
+        const uint64_t lastm = __ballot(lane < budget && (el & kLast) != 0u);
+        const int cnt = lastm != 0ull ? __builtin_ctzll(lastm) + 1 : budget;   // (LAST included)
+        last_seen = lastm != 0ull;
+        taken += cnt;
+        done = last_seen || (!unbounded && taken == kPaSeg);
         for (int k0 = 0; k0 < cnt; k0 += kPaMembers) {
-            float4 d[kPaMembers][kGwrColBlocks];
+            float4 d[kPaMembers][NCB];
             float wk[kPaMembers], bk[kPaMembers];
             int64_t ek[kPaMembers];
 #pragma unroll
@@ -371,7 +405,7 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
                 ek[u] = shfl64(ei, kk);
                 const int t = __shfl(tk, kk, kWave);
 #pragma unroll
-                for (int cb = 0; cb < kGwrColBlocks; ++cb) {
+                for (int cb = 0; cb < NCB; ++cb) {
                     const int col = cb * 4 * kWave + 4 * lane;
                     d[u][cb] = col < a.hd ? load4(a.d_dva, 0, grow0 + t, a.hd, col) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                 }
@@ -381,7 +415,7 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
                 if (k0 + u >= cnt) break;
                 float part = 0.0f;
 #pragma unroll
-                for (int cb = 0; cb < kGwrColBlocks; ++cb) {
+                for (int cb = 0; cb < NCB; ++cb) {
                     acc[cb].x = fmaf(wk[u], d[u][cb].x, acc[cb].x);
                     acc[cb].y = fmaf(wk[u], d[u][cb].y, acc[cb].y);
                     acc[cb].z = fmaf(wk[u], d[u][cb].z, acc[cb].z);
@@ -396,13 +430,75 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
             }
         }
     }
+    if (first && last_seen) {   // the whole group in one segment
+        if (!in) return;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int col = cb * 4 * kWave + 4 * lane;
+            if (col >= a.hd) break;
+            const float4 g = make_float4(fmaf(gdw[cb].x, cpe, acc[cb].x), fmaf(gdw[cb].y, cpe, acc[cb].y),
+                                         fmaf(gdw[cb].z, cpe, acc[cb].z), fmaf(gdw[cb].w, cpe, acc[cb].w));
+            store4(a.grad, a.grad_bf16, slot, a.hd, col, g);
+            if (a.bank != nullptr) store4(a.bank, a.bank_bf16, slot, a.hd, col, sn[cb]);
+        }
+        return;
+    }
+    // Split group: publish this segment's partial; the last segment to arrive combines the partials
+    // in segment order. The segments run in blocks on different XCDs, whose L2 caches are not
+    // coherent with each other: the partial and the segment count are written with device-scope
+    // atomic stores, the wave waits until they have completed, and only then adds to the arrival
+    // counter (a device-scope atomic); the combining wave reads them with device-scope atomic loads
+    // after seeing the last arrival.
+    const int64_t prow = static_cast<int64_t>(p) * a.CW;
+    const int64_t gslot = pa_group_slot(prow + first_pos);
+    float* part = a.part + pa_part_row(prow + j, dist == 0) * a.hd;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int col = cb * 4 * kWave + 4 * lane;
+        if (col < a.hd) {
+            __hip_atomic_store(part + col, acc[cb].x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(part + col + 1, acc[cb].y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(part + col + 2, acc[cb].z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(part + col + 3, acc[cb].w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    const int seg = dist / kPaSeg;
+    // The segment holding LAST publishes the segment count.
+    if (last_seen && lane == 0) __hip_atomic_store(a.meta + gslot, seg + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stores above have completed
+    // The segment holding LAST adds 1 - (segments), every other adds 1: the counter returns to 0
+    // exactly at the last arrival (and is left at 0 for the next call).
+    const int delta = last_seen ? -seg : 1;
+    int after = 0;
+    if (lane == 0) after = atomicAdd(a.cnt + gslot, delta) + delta;
+    after = __shfl(after, 0, kWave);
+    if (after != 0) return;
+    // (clamped to the segment starts the row holds, so no read can leave the workspace)
+    const int nseg = min(max(__hip_atomic_load(a.meta + gslot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), 0),
+                         (a.CW - first_pos + kPaSeg - 1) / kPaSeg);
+    float4 tot[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) tot[cb] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int sg = 0; sg < nseg; ++sg) {
+        const float* pp = a.part + pa_part_row(prow + first_pos + static_cast<int64_t>(sg) * kPaSeg, sg == 0) * a.hd;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int col = cb * 4 * kWave + 4 * lane;
+            if (col < a.hd) {
+                tot[cb].x = tot[cb].x + __hip_atomic_load(pp + col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                tot[cb].y = tot[cb].y + __hip_atomic_load(pp + col + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                tot[cb].z = tot[cb].z + __hip_atomic_load(pp + col + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                tot[cb].w = tot[cb].w + __hip_atomic_load(pp + col + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
     if (!in) return;
 #pragma unroll
-    for (int cb = 0; cb < kGwrColBlocks; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb) {
         const int col = cb * 4 * kWave + 4 * lane;
         if (col >= a.hd) break;
-        const float4 g = make_float4(fmaf(gdw[cb].x, cpe, acc[cb].x), fmaf(gdw[cb].y, cpe, acc[cb].y),
-                                     fmaf(gdw[cb].z, cpe, acc[cb].z), fmaf(gdw[cb].w, cpe, acc[cb].w));
+        const float4 g = make_float4(fmaf(gdw[cb].x, cpe, tot[cb].x), fmaf(gdw[cb].y, cpe, tot[cb].y),
+                                     fmaf(gdw[cb].z, cpe, tot[cb].z), fmaf(gdw[cb].w, cpe, tot[cb].w));
         store4(a.grad, a.grad_bf16, slot, a.hd, col, g);
         if (a.bank != nullptr) store4(a.bank, a.bank_bf16, slot, a.hd, col, sn[cb]);
     }
@@ -470,8 +566,23 @@ hipError_t gwr_launch(const sdm_gwr_io* io, int64_t ti, hipStream_t st) {
     a.grad_bf16 = io->grad_dtype == SDM_BF16;
     const int64_t toks = static_cast<int64_t>(io->P) * io->C;
     void* kargs[] = {&a};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&gwr_kernel),
+    const void* fn = io->hd <= 256 ? reinterpret_cast<const void*>(&gwr_kernel<1>)
+                   : io->hd <= 512 ? reinterpret_cast<const void*>(&gwr_kernel<2>)
+                                   : reinterpret_cast<const void*>(&gwr_kernel<4>);
+    return hipLaunchKernel(fn,
                            dim3(static_cast<unsigned>((toks + kGdsWaves - 1) / kGdsWaves)), dim3(kGdsThreads), kargs, 0, st);
+}
+
+PaWorkspace pa_workspace_layout(const sdm_pa_io* io) {
+    const size_t pos = static_cast<size_t>(io->P) * static_cast<size_t>(io->C) * static_cast<size_t>(io->W);
+    const size_t blocks = (pos + kPaSeg - 1) / kPaSeg;
+    auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+    PaWorkspace w;
+    w.cnt_off = 0;
+    w.meta_off = up(blocks * sizeof(int));
+    w.part_off = w.meta_off + up(blocks * sizeof(int));
+    w.total = w.part_off + up(2 * blocks * static_cast<size_t>(io->hd) * sizeof(float));
+    return w;
 }
 
 hipError_t pa_launch(const sdm_pa_io* io, int64_t ti, hipStream_t st) {
@@ -497,9 +608,22 @@ hipError_t pa_launch(const sdm_pa_io* io, int64_t ti, hipStream_t st) {
     a.vbf = io->val_bytes == 2;
     a.grad_bf16 = io->grad_dtype == SDM_BF16;
     a.bank_bf16 = io->bank_dtype == SDM_BF16;
+    a.part = nullptr;
+    a.cnt = nullptr;
+    a.meta = nullptr;
+    if (io->workspace != nullptr) {
+        const PaWorkspace w = pa_workspace_layout(io);
+        char* ws = static_cast<char*>(io->workspace);
+        a.part = reinterpret_cast<float*>(ws + w.part_off);
+        a.cnt = reinterpret_cast<int*>(ws + w.cnt_off);
+        a.meta = reinterpret_cast<int*>(ws + w.meta_off);
+    }
     const int64_t poss = static_cast<int64_t>(io->P) * io->C * io->W;
     void* kargs[] = {&a};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&pa_kernel),
+    const void* fn = io->hd <= 256 ? reinterpret_cast<const void*>(&pa_kernel<1>)
+                   : io->hd <= 512 ? reinterpret_cast<const void*>(&pa_kernel<2>)
+                                   : reinterpret_cast<const void*>(&pa_kernel<4>);
+    return hipLaunchKernel(fn,
                            dim3(static_cast<unsigned>((poss + kGdsWaves - 1) / kGdsWaves)), dim3(kGdsThreads), kargs, 0, st);
 }
 

@@ -118,4 +118,11 @@ hipError_t gwr_launch(const sdm_gwr_io* io, int64_t ti, hipStream_t st);
 // PA of step ti (validated by sdm_pa_step).
 hipError_t pa_launch(const sdm_pa_io* io, int64_t ti, hipStream_t st);
 
+// Workspace of sdm_pa_step: per block of 32 K-row positions an arrival counter (zero between
+// calls) and a segment count, and two partial rows.
+struct PaWorkspace {
+    size_t cnt_off, meta_off, part_off, total;
+};
+PaWorkspace pa_workspace_layout(const sdm_pa_io* io);
+
 }  // namespace sdm

@@ -391,3 +391,9 @@ def run_read_check_fed(wl, steps_checked, dev="cuda"):
                 worst = max(worst, float(np.max(err[nz] / tol[nz])))
             assert np.all(g[tv:] == 0), name
     return worst
+
+
+def pa_counter_bytes(shape):
+    """Bytes of the PA workspace's arrival counters (its first region): one int per block of 32 K-row
+    positions of a step."""
+    return -(-shape.P * shape.C * shape.W // 32) * 4

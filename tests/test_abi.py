@@ -275,9 +275,21 @@ def pa_io(**kw):
     (dict(snap_rows=100), 0, _lib.SDM_EINVAL), (dict(dva_rows=100), 0, _lib.SDM_EINVAL), (dict(beta=None), 0, _lib.SDM_EINVAL),
     (dict(snap=FAKE + 4), 0, _lib.SDM_EALIGN), (dict(krec=FAKE + 8), 0, _lib.SDM_EALIGN),
     (dict(d_k_eff=FAKE + 2), 0, _lib.SDM_EALIGN),
+    (dict(workspace=FAKE, workspace_bytes=16), 0, _lib.SDM_EWORKSPACE),
+    (dict(workspace=FAKE + 4, workspace_bytes=1 << 40), 0, _lib.SDM_EALIGN),
 ])
 def test_pa_refusals(kw, ti, status):
     lib = _lib.load()
     assert lib.sdm_pa_step(ctypes.byref(pa_io(**kw)), ti, None) == status
     assert len(lib.sdm_last_error()) > 0
     assert lib.sdm_pa_step(None, 0, None) == _lib.SDM_EINVAL
+
+
+def test_pa_workspace_size():
+    lib = _lib.load()
+    o = pa_io(P=2, C=64, W=4, hd=96)
+    need = lib.sdm_pa_workspace(ctypes.byref(o))
+    blocks = (2 * 64 * 4 + 31) // 32   # one counter, one segment count and two partial rows per 32 positions
+    up = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    assert need == up(4 * blocks) + up(4 * blocks) + up(2 * blocks * 96 * 4)
+    assert lib.sdm_pa_workspace(ctypes.byref(pa_io(P=0))) == 0

@@ -10,7 +10,9 @@ read), and the oracle works from its own Phase-1 k_eff and cpe. Tolerances: a gr
 |products| plus 1e-5 of it and 1e-6; with bfloat16 values (k_eff, cpe) both add 2^-7 of their
 magnitude (either bfloat16 neighbour of the exact value is correct). Restored bank rows equal the
 pre-write rows bit for bit; padding entries get zeros; gradient rows of slots the step does not
-write keep their bits. PA is also bitwise reproducible run to run.
+write keep their bits. With a workspace (long groups split into 32-member segments) the same bounds
+hold: a member's term passes through at most its segment's chain and the segment additions, fewer
+roundings than the m + 4 the bound allows. PA is also bitwise reproducible run to run.
 """
 
 import os
@@ -47,6 +49,16 @@ def say(*a):
     dict(idx=3, steps=1, checked=[0]),                  # hd = 960: every column block of a group's wave
     dict(idx=1, steps=2, checked=[1], val_bf16=True),   # bfloat16 k_eff (and cpe) from Phase 1
     dict(shape=dict(C=37, W=5, S=9, P=2, vl=11, hd=36), steps=2, checked=[1], val_bf16=True),
+    # With a workspace: groups of more than 32 members are split into segments.
+    dict(idx=2, steps=1, checked=[0], ws=True),         # Zipf: hot slots with hundreds of members
+    dict(idx=0, steps=None, checked=[0, 2], ws=True),
+    dict(shape=dict(C=37, W=5, S=9, P=2, vl=11, hd=36), steps=2, checked=[0, 1], ws=True),
+    # One group of 4352 members: the in-group distance saturates, the segment starting at 4064 runs
+    # to the group's end.
+    dict(shape=dict(C=256, W=17, S=1, P=1, vl=None, hd=64), steps=1, checked=[0], ws=True),
+    # One slot per chunk and a fully masked last chunk.
+    dict(shape=dict(C=64, W=2, S=1, P=1, vl=0, hd=40), steps=2, checked=[0, 1], ws=True),
+    dict(idx=1, steps=2, checked=[1], val_bf16=True, ws=True),
 ])
 def test_pa_matches_oracle(case):
     vbf = case.get("val_bf16", False)
@@ -84,9 +96,12 @@ def test_pa_matches_oracle(case):
         grad = grad0.clone()
         g_decay = torch.full((wl.N, C, Wn), float("nan"), device="cuda")
         d_k_eff = torch.full((wl.N, C, Wn), float("nan"), device="cuda")
+        ws = sdm.alloc_pa_workspace(shape, hd) if case.get("ws") else None
         sdm.pa_step(grad, snap, out, beta, d_dva, shape, ti, step_rows=P * C, snap_step_rows=0, bank=bank,
-                    g_decay=g_decay, d_k_eff=d_k_eff)
+                    g_decay=g_decay, d_k_eff=d_k_eff, workspace=ws)
         torch.cuda.synchronize()
+        if ws is not None:   # the arrival counters are back at zero
+            assert not ws[:H.pa_counter_bytes(shape)].any()
         touched = []
         for p in range(P):
             cidx = ti * P + p
@@ -132,9 +147,12 @@ def test_pa_matches_oracle(case):
             assert torch.equal(grad.index_select(0, ci).view(torch.uint8), grad0.index_select(0, ci).view(torch.uint8))
 
 
-def test_pa_bitwise_reproducible():
+@pytest.mark.parametrize("split", [False, True])
+def test_pa_bitwise_reproducible(split):
     """Two PA runs on the same inputs (the Zipf workload: long write groups) give the same bits in
-    every output: gradient rows, restored bank rows, decay and k_eff gradients."""
+    every output: gradient rows, restored bank rows, decay and k_eff gradients. With a workspace the
+    long groups are split, and whichever segment arrives last the partial sums are added in the same
+    order (the workspace is reused by the second run: its counters are back at zero)."""
     wl = W.make(2, steps=1)
     sh = wl.shape
     P, C, Wn, hd, CW = sh.P, sh.C, sh.W, sh.hd, sh.C * sh.W
@@ -147,6 +165,7 @@ def test_pa_bitwise_reproducible():
     grad0 = (torch.randn(bank0.shape, generator=gen, device="cuda") * 0.01).to(bank0.dtype)
     beta = torch.rand((wl.N, C), generator=gen, device="cuda")
     d_dva = torch.randn((wl.steps * P * C, hd), generator=gen, device="cuda")
+    ws = sdm.alloc_pa_workspace(shape, hd) if split else None
     results = []
     for _ in range(2):
         bank = bank0.clone()
@@ -156,7 +175,7 @@ def test_pa_bitwise_reproducible():
         g_decay = torch.zeros((wl.N, C, Wn), device="cuda")
         d_k_eff = torch.zeros((wl.N, C, Wn), device="cuda")
         sdm.pa_step(grad, snap, out, beta, d_dva, shape, 0, step_rows=P * C, snap_step_rows=0, bank=bank,
-                    g_decay=g_decay, d_k_eff=d_k_eff)
+                    g_decay=g_decay, d_k_eff=d_k_eff, workspace=ws)
         torch.cuda.synchronize()
         results.append((grad, bank, g_decay, d_k_eff))
     for a, b in zip(*results):
