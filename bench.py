@@ -454,13 +454,16 @@ def measure_gds(wl, shape, out, ins, bank, stream, sdm, torch):
     sp = out["spay_q"]
     heads = ((sp & W_FIRST) != 0) & ((sp & W_INVALID) == 0)
     groups_q = float(heads.view(wl.steps, P * C * R).sum(dim=1).float().mean())
+    ws = sdm.alloc_gds_workspace(shape, hd, device=dev)   # long read groups split across waves
     for ti in range(min(2, wl.steps)):
-        sdm.gds_step(bank, out, ins["q_idx"], gr, shape, ti, step_rows=P * C, d_q_w=d, grad=grad, stream=stream)
+        sdm.gds_step(bank, out, ins["q_idx"], gr, shape, ti, step_rows=P * C, d_q_w=d, grad=grad, stream=stream,
+                     workspace=ws)
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(wl.steps)]
     for ti in range(wl.steps):
         ev[ti][0].record(stream)
-        sdm.gds_step(bank, out, ins["q_idx"], gr, shape, ti, step_rows=P * C, d_q_w=d, grad=grad, stream=stream)
+        sdm.gds_step(bank, out, ins["q_idx"], gr, shape, ti, step_rows=P * C, d_q_w=d, grad=grad, stream=stream,
+                     workspace=ws)
         ev[ti][1].record(stream)
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))

@@ -335,6 +335,12 @@ typedef struct sdm_gds_io {
     int32_t valid_last;
     int32_t idx_bytes;      /* width of q_idx: 0 or 4 = int32, 8 = int64 */
     int32_t val_bytes;      /* type of q_w: 0 or 4 = float32, 2 = bf16 */
+    void* workspace;        /* optional (NULL: none), 16-byte aligned, sdm_gds_workspace(io) bytes, zero-filled
+                               before its first use and left so by every call: read groups of more than 32
+                               members are then summed in 32-member segments by separate waves, their partial
+                               rows added in segment order by the last to finish (the same sums whichever
+                               finishes last). Calls that share a workspace must not overlap. */
+    size_t workspace_bytes;
 } sdm_gds_io;
 
 /*
@@ -351,6 +357,11 @@ typedef struct sdm_gds_io {
  * bf16 rows), 4-byte aligned ids (8 for int64), q_w, spay_q and d_q_w.
  */
 sdm_status sdm_gds_step(const sdm_gds_io* io, int64_t ti, hipStream_t st);
+
+/* Bytes of the optional GDS workspace for this io's shape (P, C, R, hd): per block of 32 Q-row
+ * positions of a step an arrival counter and a segment count (4 B each), and two float32 partial
+ * rows. 0 for an invalid shape. */
+size_t sdm_gds_workspace(const sdm_gds_io* io);
 
 /* GWR of one step: the backward of DW's write terms for the tokens of chunks ti*P .. ti*P + P - 1. */
 typedef struct sdm_gwr_io {

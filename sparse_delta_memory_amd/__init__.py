@@ -18,7 +18,7 @@ from . import _lib
 from ._lib import P1IO, P1Shape, SdmError  # noqa: F401
 
 __all__ = ["P1Shape", "phase1", "phase1_workspace_bytes", "alloc_phase1_outputs", "dw_step", "dw_workspace_bytes",
-           "alloc_dw_workspace", "DwPlan", "ReadPlan", "read_step", "gds_step", "gwr_step", "pa_step", "pa_workspace_bytes",
+           "alloc_dw_workspace", "DwPlan", "ReadPlan", "read_step", "gds_step", "gds_workspace_bytes", "alloc_gds_workspace", "gwr_step", "pa_step", "pa_workspace_bytes",
            "alloc_pa_workspace", "SdmError", "make_shape",
            "timing_events"]
 
@@ -281,13 +281,29 @@ def read_step(bank, p1, k_idx, q_idx, v, beta, dv, pred, read, shape: P1Shape, t
     ReadPlan(bank, p1, k_idx, q_idx, v, beta, dv, pred, read, shape, step_rows).step(ti, stream=stream)
 
 
-def gds_step(bank, p1, q_idx, gr, shape: P1Shape, ti: int, step_rows: int, d_q_w=None, grad=None, stream=None):
+def gds_workspace_bytes(shape: P1Shape, hd: int) -> int:
+    """Bytes of the (zero-filled) GDS workspace that lets long read groups be split across waves."""
+    io = _lib.GdsIO()
+    io.P, io.C, io.R, io.N, io.hd = shape.P, shape.C, shape.R, shape.N, int(hd)
+    return int(_lib.load().sdm_gds_workspace(ctypes.byref(io)))
+
+
+def alloc_gds_workspace(shape: P1Shape, hd: int, device="cuda"):
+    """A zero-filled GDS workspace (reusable by every step of the same shape)."""
+    import torch
+
+    return torch.zeros(max(gds_workspace_bytes(shape, hd), 1), dtype=torch.uint8, device=device)
+
+
+def gds_step(bank, p1, q_idx, gr, shape: P1Shape, ti: int, step_rows: int, d_q_w=None, grad=None, stream=None,
+             workspace=None):
     """GDS of step `ti` (the backward of the read gather) on the current (or given) stream.
 
     bank [rows, hd] float32 or bfloat16, the memory before the step (read only); p1: the Phase-1
     outputs (q_w, spay_q); q_idx the Phase-1 read ids; gr [*, hd] float32 gradient rows of the reads,
     row ti*step_rows + p*C + t. d_q_w [N, C, R] float32 (optional) receives the dots of the step's
-    chunks; grad [rows, hd] float32 or bfloat16 (optional) gains each read slot's sum in place."""
+    chunks; grad [rows, hd] float32 or bfloat16 (optional) gains each read slot's sum in place.
+    workspace (optional, alloc_gds_workspace): long read groups are split across waves."""
     import torch
 
     for name, t in (("gr", gr), ("d_q_w", d_q_w)):
@@ -315,6 +331,9 @@ def gds_step(bank, p1, q_idx, gr, shape: P1Shape, ti: int, step_rows: int, d_q_w
     io.first_partial, io.valid_last = shape.first_partial, shape.valid_last
     io.idx_bytes = q_idx.element_size()
     io.val_bytes = p1["q_w"].element_size()
+    if workspace is not None:
+        io.workspace = workspace.data_ptr()
+        io.workspace_bytes = workspace.numel() * workspace.element_size()
     st = torch.cuda.current_stream(bank.device) if stream is None else stream
     _lib.check(lib.sdm_gds_step(ctypes.byref(io), int(ti), ctypes.c_void_p(st.cuda_stream)))
 

@@ -79,7 +79,8 @@ class GdsIO(ctypes.Structure):
         ("step_rows", ctypes.c_int64), ("gr_rows", ctypes.c_int64), ("d_q_w", ctypes.c_void_p), ("grad", ctypes.c_void_p),
         ("grad_dtype", ctypes.c_int32), ("P", ctypes.c_int32), ("C", ctypes.c_int32), ("R", ctypes.c_int32),
         ("N", ctypes.c_int32), ("first_partial", ctypes.c_int32), ("valid_last", ctypes.c_int32),
-        ("idx_bytes", ctypes.c_int32), ("val_bytes", ctypes.c_int32),
+        ("idx_bytes", ctypes.c_int32), ("val_bytes", ctypes.c_int32), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -106,7 +107,7 @@ class PaIO(ctypes.Structure):
 
 
 EXPORTS = ["sdm_phase1_workspace", "sdm_phase1", "sdm_dw_workspace", "sdm_dw_step", "sdm_dw_step_noalloc", "sdm_read_step",
-           "sdm_gds_step", "sdm_gwr_step", "sdm_pa_workspace", "sdm_pa_step", "sdm_status_string", "sdm_last_error"]
+           "sdm_gds_workspace", "sdm_gds_step", "sdm_gwr_step", "sdm_pa_workspace", "sdm_pa_step", "sdm_status_string", "sdm_last_error"]
 
 _lock = threading.Lock()
 _lib = None
@@ -143,6 +144,8 @@ def load() -> ctypes.CDLL:
         lib.sdm_gds_step.restype = ctypes.c_int
         lib.sdm_gwr_step.argtypes = [ctypes.POINTER(GwrIO), ctypes.c_int64, ctypes.c_void_p]
         lib.sdm_gwr_step.restype = ctypes.c_int
+        lib.sdm_gds_workspace.argtypes = [ctypes.POINTER(GdsIO)]
+        lib.sdm_gds_workspace.restype = ctypes.c_size_t
         lib.sdm_pa_workspace.argtypes = [ctypes.POINTER(PaIO)]
         lib.sdm_pa_workspace.restype = ctypes.c_size_t
         lib.sdm_pa_step.argtypes = [ctypes.POINTER(PaIO), ctypes.c_int64, ctypes.c_void_p]

@@ -176,6 +176,11 @@ size_t sdm_dw_workspace(const sdm_dw_io* io) {
     return sdm::dw_workspace_layout(io).total;
 }
 
+size_t sdm_gds_workspace(const sdm_gds_io* io) {
+    if (io == nullptr || io->P < 1 || io->C < 1 || io->R < 1 || io->hd < 1) return 0;
+    return sdm::gds_workspace_layout(io).total;
+}
+
 size_t sdm_pa_workspace(const sdm_pa_io* io) {
     if (io == nullptr || io->P < 1 || io->C < 1 || io->W < 1 || io->hd < 1) return 0;
     return sdm::pa_workspace_layout(io).total;
@@ -334,6 +339,12 @@ sdm_status sdm_gds_step(const sdm_gds_io* io, int64_t ti, hipStream_t st) {
     if (!aligned(io->q_idx, io->idx_bytes == 8 ? 8 : 4) || !aligned(io->q_w, io->val_bytes == 2 ? 2 : 4) ||
         !aligned(io->spay_q, 4) || !aligned(io->d_q_w, 4))
         return fail(SDM_EALIGN, "sdm_gds_step: q_idx, q_w, spay_q or d_q_w misaligned");
+    if (io->workspace != nullptr) {
+        if (!aligned(io->workspace, 16)) return fail(SDM_EALIGN, "sdm_gds_step: workspace is not 16-byte aligned");
+        const size_t need = sdm::gds_workspace_layout(io).total;
+        if (io->workspace_bytes < need)
+            return fail(SDM_EWORKSPACE, "sdm_gds_step: workspace needs %zu bytes, got %zu", need, io->workspace_bytes);
+    }
     const hipError_t e = sdm::gds_launch(io, ti, st);
     if (e != hipSuccess) {
         (void)hipGetLastError();

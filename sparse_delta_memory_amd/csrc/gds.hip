@@ -9,7 +9,9 @@
 // at a valid group FIRST the wave walks the group's members in sorted order (64 records and
 // weights at a time, 8 gradient rows in flight), acc = fma(q_w, gr[t], acc) from +0, and at LAST
 // adds acc to grad[slot] with one read-modify-write (the wave is that row's only writer in the
-// launch, so the result is deterministic).
+// launch, so the result is deterministic). With a workspace, a group of more than 32 members is
+// walked in 32-member segments by separate waves; the last to finish adds their partial rows in
+// segment order and makes the read-modify-write (the same sums whichever finishes last).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -29,9 +31,26 @@ struct GdsArgs {
     const float* gr;
     float* d_q_w;
     void* grad;
+    float* part;       // split groups (NULL: not split): two partial rows per block of kSplitSeg positions
+    int* cnt;          // per block of kSplitSeg positions (a split group's FIRST): arrival counter, zero between calls
+    int* meta;         // per block of kSplitSeg positions: the group's segment count
     int64_t rows, chunk0, row0;
     int P, C, R, hd, first_partial, valid_last, id64, vbf, bank_bf16, grad_bf16;
 };
+
+// Long groups (GDS read groups, PA write groups; with a workspace): members per segment, and the
+// last in-group distance that still marks a segment start (the distance field saturates at 4095).
+constexpr int kSplitSeg = 32;
+constexpr int kSplitSegLimit = (4095 / kSplitSeg) * kSplitSeg;
+// Workspace slots, by step-wide row position G (stream p's position j is p * (its row length) + j):
+// a split group has more than kSplitSeg members, so at most one split group's FIRST falls in each
+// aligned block of kSplitSeg positions (its counter and segment count), and at most two segment
+// starts (the first segment of a group starting there, a later one of the group running through):
+// two partial rows per block.
+__device__ __forceinline__ int64_t split_group_slot(int64_t g_first) { return g_first / kSplitSeg; }
+__device__ __forceinline__ int64_t split_part_row(int64_t g_start, bool first_segment) {
+    return 2 * (g_start / kSplitSeg) + (first_segment ? 0 : 1);
+}
 
 constexpr int kGdsThreads = 256;
 constexpr int kGdsWaves = kGdsThreads / kWave;
@@ -110,6 +129,8 @@ __global__ void __launch_bounds__(kGdsThreads) gds_dots_kernel(GdsArgs a) {
     }
 }
 
+// ONE: hd <= 256, a single column block (no column loop).
+template <bool ONE>
 __global__ void __launch_bounds__(kGdsThreads) gds_scatter_kernel(GdsArgs a) {
     const int wv = static_cast<int>(threadIdx.x) / kWave;
     const int lane = static_cast<int>(lane_id());
@@ -120,28 +141,55 @@ __global__ void __launch_bounds__(kGdsThreads) gds_scatter_kernel(GdsArgs a) {
     const int64_t c = a.chunk0 + p;
     const uint32_t* row = a.spay_q + c * n;
     const uint32_t e0 = row[j];
-    if (!(e0 & kFirst) || (e0 & kInvalid)) return;   // a valid group starts here
+    if (e0 & kInvalid) return;
+    // Work starts at a valid group's FIRST and, when long groups are split, at every kSplitSeg-th
+    // member (distance counts the group's valid entries before this one).
+    const bool split = a.part != nullptr;
+    const int dist = static_cast<int>((e0 >> kDistShift) & kDistMax);
+    const bool first = (e0 & kFirst) != 0u;
+    if (!first && (!split || dist % kSplitSeg != 0 || dist > kSplitSegLimit)) return;
+    const bool unbounded = !split || dist == kSplitSegLimit;   // the last segment start runs to LAST
     const int64_t qbase = c * n;   // entry-order Q index of (t, lane) is t * R + lane
     auto entry = [&](uint32_t el) { return static_cast<int64_t>((el >> kTokShift) & 0xFFu) * a.R + (el & 0xFFu); };
-    const int64_t slot = gds_id(a, qbase + entry(e0));   // (every member reads it)
+    const int64_t slot = gds_id(a, qbase + entry(e0));   // (every member, so every segment, reads it)
     if (slot < 0 || slot >= a.rows) return;
     const int64_t grow0 = a.row0 + static_cast<int64_t>(p) * a.C;
-    for (int col0 = 0; col0 < a.hd; col0 += 4 * kWave) {
+    // One read-modify-write of 4 columns of the slot's row (this wave is the row's only writer).
+    auto add_row = [&](int col, float4 v) {
+        if (a.grad_bf16) {
+            uint2* gp = reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.grad) + slot * a.hd + col);
+            const uint2 o = *gp;
+            const float x = bf16_bits_to_f32(o.x & 0xFFFFu) + v.x, y = bf16_bits_to_f32(o.x >> 16) + v.y;
+            const float z = bf16_bits_to_f32(o.y & 0xFFFFu) + v.z, u = bf16_bits_to_f32(o.y >> 16) + v.w;
+            *gp = make_uint2(f32_to_bf16_rne(x) | f32_to_bf16_rne(y) << 16, f32_to_bf16_rne(z) | f32_to_bf16_rne(u) << 16);
+        } else {
+            float4* gp = reinterpret_cast<float4*>(static_cast<float*>(a.grad) + slot * a.hd + col);
+            const float4 o = *gp;
+            *gp = make_float4(o.x + v.x, o.y + v.y, o.z + v.z, o.w + v.w);
+        }
+    };
+    const int64_t prow = static_cast<int64_t>(p) * n;
+    bool last_seen = false;
+    for (int col0 = 0; col0 < (ONE ? 1 : a.hd); col0 += 4 * kWave) {
         const int col = col0 + 4 * lane;
         const bool con = col < a.hd;
         float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         bool done = false;
+        int taken = 0;
         // The members in sorted order, 64 records at a time (lane l: member m0 + l), their gradient
         // rows kWalkRows at a time; the sum runs over the members in order from +0.
         for (int m0 = j; !done && m0 < n; m0 += kWave) {
+            const int budget = unbounded ? kWave : min(kWave, kSplitSeg - taken);   // members still in the segment
             const int m = m0 + lane;
             const uint32_t el = m < n ? row[m] : (kFirst | kLast | kInvalid);
             const int tk = static_cast<int>((el >> kTokShift) & 0xFFu);
             const bool in = m < n && !(el & kInvalid);
             const float w = in ? load_val(a.q_w, qbase + entry(el), a.vbf) : 0.0f;
-            const uint64_t lastm = __ballot((el & kLast) != 0u);
-            const int cnt = lastm != 0ull ? __builtin_ctzll(lastm) + 1 : kWave;   // (LAST included)
-            done = lastm != 0ull;
+            const uint64_t lastm = __ballot(lane < budget && (el & kLast) != 0u);
+            const int cnt = lastm != 0ull ? __builtin_ctzll(lastm) + 1 : budget;   // (LAST included)
+            last_seen = lastm != 0ull;
+            taken += cnt;
+            done = last_seen || (!unbounded && taken == kSplitSeg);
             for (int k0 = 0; k0 < cnt; k0 += kWalkRows) {
                 float wk[kWalkRows];
                 float4 g[kWalkRows];
@@ -164,18 +212,49 @@ __global__ void __launch_bounds__(kGdsThreads) gds_scatter_kernel(GdsArgs a) {
             }
         }
         if (!con) continue;
-        // One read-modify-write of the lane's columns (this wave is the row's only writer).
-        if (a.grad_bf16) {
-            uint2* gp = reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.grad) + slot * a.hd + col);
-            const uint2 o = *gp;
-            const float x = bf16_bits_to_f32(o.x & 0xFFFFu) + acc.x, y = bf16_bits_to_f32(o.x >> 16) + acc.y;
-            const float z = bf16_bits_to_f32(o.y & 0xFFFFu) + acc.z, u = bf16_bits_to_f32(o.y >> 16) + acc.w;
-            *gp = make_uint2(f32_to_bf16_rne(x) | f32_to_bf16_rne(y) << 16, f32_to_bf16_rne(z) | f32_to_bf16_rne(u) << 16);
-        } else {
-            float4* gp = reinterpret_cast<float4*>(static_cast<float*>(a.grad) + slot * a.hd + col);
-            const float4 o = *gp;
-            *gp = make_float4(o.x + acc.x, o.y + acc.y, o.z + acc.z, o.w + acc.w);
+        if (first && last_seen) {   // the whole group in one segment
+            add_row(col, acc);
+        } else {   // a segment of a split group: its partial row (device-scope stores, see below)
+            float* part = a.part + split_part_row(prow + j, dist == 0) * a.hd + col;
+            __hip_atomic_store(part, acc.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(part + 1, acc.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(part + 2, acc.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(part + 3, acc.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+    }
+    if (first && last_seen) return;
+    // Split group: the last segment to arrive adds the partial rows in segment order and updates
+    // the row. Segments run in blocks on different XCDs, whose L2 caches are not coherent with each
+    // other: partials and the segment count are device-scope atomic stores, the wave waits for
+    // their completion before it adds to the arrival counter (a device-scope atomic), and the
+    // combining wave reads them with device-scope atomic loads after seeing the last arrival.
+    const int first_pos = j - dist;
+    const int64_t gslot = split_group_slot(prow + first_pos);
+    const int seg = dist / kSplitSeg;
+    if (last_seen && lane == 0) __hip_atomic_store(a.meta + gslot, seg + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stores above have completed
+    // The segment holding LAST adds 1 - (segments), every other adds 1: the counter returns to 0
+    // exactly at the last arrival (and is left at 0 for the next call).
+    const int delta = last_seen ? -seg : 1;
+    int after = 0;
+    if (lane == 0) after = atomicAdd(a.cnt + gslot, delta) + delta;
+    after = __shfl(after, 0, kWave);
+    if (after != 0) return;
+    // (clamped to the segment starts the row holds, so no read can leave the workspace)
+    const int nseg = min(max(__hip_atomic_load(a.meta + gslot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), 0),
+                         (n - first_pos + kSplitSeg - 1) / kSplitSeg);
+    for (int col0 = 0; col0 < (ONE ? 1 : a.hd); col0 += 4 * kWave) {
+        const int col = col0 + 4 * lane;
+        if (col >= a.hd) continue;
+        float4 tot = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        for (int sg = 0; sg < nseg; ++sg) {
+            const float* pp = a.part + split_part_row(prow + first_pos + static_cast<int64_t>(sg) * kSplitSeg, sg == 0) * a.hd + col;
+            tot.x = tot.x + __hip_atomic_load(pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            tot.y = tot.y + __hip_atomic_load(pp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            tot.z = tot.z + __hip_atomic_load(pp + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            tot.w = tot.w + __hip_atomic_load(pp + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        add_row(col, tot);
     }
 }
 
@@ -297,27 +376,14 @@ struct PaArgs {
     const float* d_dva;
     float* g_decay;
     float* d_k_eff;
-    float* part;       // split groups (NULL: not split): two partial rows per block of kPaSeg positions
-    int* cnt;          // per block of kPaSeg positions (a split group's FIRST): arrival counter, zero between calls
-    int* meta;         // per block of kPaSeg positions: the group's segment count
+    float* part;       // split groups (NULL: not split): two partial rows per block of kSplitSeg positions
+    int* cnt;          // per block of kSplitSeg positions (a split group's FIRST): arrival counter, zero between calls
+    int* meta;         // per block of kSplitSeg positions: the group's segment count
     int64_t rows, chunk0, row0, snap_row0;
     int P, C, W, CW, hd, vbf, grad_bf16, bank_bf16;
 };
 
 constexpr int kPaMembers = 4;   // member token rows in flight together
-// Members per segment when long groups are split (a workspace is given), and the last in-group
-// distance that still marks a segment start (the distance field saturates at 4095).
-constexpr int kPaSeg = 32;
-constexpr int kPaSegLimit = (4095 / kPaSeg) * kPaSeg;
-// Workspace slots, by step-wide K-row position G (stream p's position j is p * CW + j): a split
-// group has more than kPaSeg members, so at most one split group's FIRST falls in each aligned
-// block of kPaSeg positions (its counter and segment count), and at most two segment starts (the
-// first segment of a group starting there, a later one of the group running through): two partial
-// rows per block.
-__device__ __forceinline__ int64_t pa_group_slot(int64_t g_first) { return g_first / kPaSeg; }
-__device__ __forceinline__ int64_t pa_part_row(int64_t g_start, bool first_segment) {
-    return 2 * (g_start / kPaSeg) + (first_segment ? 0 : 1);
-}
 
 __device__ __forceinline__ void store4(void* base, int bf, int64_t row, int hd, int col, float4 v) {
     if (bf) {
@@ -328,7 +394,7 @@ __device__ __forceinline__ void store4(void* base, int bf, int64_t row, int hd, 
     }
 }
 
-// One wave per K-row position that starts work: a group's FIRST or, with a workspace, every kPaSeg-th
+// One wave per K-row position that starts work: a group's FIRST or, with a workspace, every kSplitSeg-th
 // member of a longer group. The wave walks its members in sorted order (64 records at a time,
 // kPaMembers token rows in flight): per member d_k_eff and g_decay, and acc = fma(sc, d_dva[tok], acc)
 // from +0. A group in one segment then writes grad = fma(gdw, cpe, acc) and restores the bank row;
@@ -357,8 +423,8 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
     const bool split = a.part != nullptr;
     const int dist = static_cast<int>((r0.x >> kDistShift) & kDistMax);   // valid K entries before, in the group
     const bool first = (r0.x & kFirst) != 0u;
-    if (!first && (!split || dist % kPaSeg != 0 || dist > kPaSegLimit)) return;   // a member another wave walks
-    const bool unbounded = !split || dist == kPaSegLimit;   // the last segment start runs to LAST
+    if (!first && (!split || dist % kSplitSeg != 0 || dist > kSplitSegLimit)) return;   // a member another wave walks
+    const bool unbounded = !split || dist == kSplitSegLimit;   // the last segment start runs to LAST
     const int first_pos = j - dist;                          // the group's FIRST (its snapshot row)
     const int64_t slot = static_cast<int64_t>(r0.y);
     const bool in = slot < a.rows;   // (a slot outside the bank: zero rows, nothing written)
@@ -380,7 +446,7 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
     bool done = false, last_seen = false;
     int taken = 0;
     for (int m0 = j; !done && m0 < a.CW; m0 += kWave) {   // members 64 records at a time, in sorted order
-        const int budget = unbounded ? kWave : min(kWave, kPaSeg - taken);   // members this segment may still take
+        const int budget = unbounded ? kWave : min(kWave, kSplitSeg - taken);   // members this segment may still take
         const int m = m0 + lane;
         const uint32_t el = m < a.CW ? kr[m].x : (kFirst | kLast | kInvalid);
         const int tk = static_cast<int>((el >> kTokShift) & 0xFFu);
@@ -392,7 +458,7 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
         const int cnt = lastm != 0ull ? __builtin_ctzll(lastm) + 1 : budget;   // (LAST included)
         last_seen = lastm != 0ull;
         taken += cnt;
-        done = last_seen || (!unbounded && taken == kPaSeg);
+        done = last_seen || (!unbounded && taken == kSplitSeg);
         for (int k0 = 0; k0 < cnt; k0 += kPaMembers) {
             float4 d[kPaMembers][NCB];
             float wk[kPaMembers], bk[kPaMembers];
@@ -450,8 +516,8 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
     // counter (a device-scope atomic); the combining wave reads them with device-scope atomic loads
     // after seeing the last arrival.
     const int64_t prow = static_cast<int64_t>(p) * a.CW;
-    const int64_t gslot = pa_group_slot(prow + first_pos);
-    float* part = a.part + pa_part_row(prow + j, dist == 0) * a.hd;
+    const int64_t gslot = split_group_slot(prow + first_pos);
+    float* part = a.part + split_part_row(prow + j, dist == 0) * a.hd;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         const int col = cb * 4 * kWave + 4 * lane;
@@ -462,7 +528,7 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
             __hip_atomic_store(part + col + 3, acc[cb].w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    const int seg = dist / kPaSeg;
+    const int seg = dist / kSplitSeg;
     // The segment holding LAST publishes the segment count.
     if (last_seen && lane == 0) __hip_atomic_store(a.meta + gslot, seg + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stores above have completed
@@ -475,12 +541,12 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
     if (after != 0) return;
     // (clamped to the segment starts the row holds, so no read can leave the workspace)
     const int nseg = min(max(__hip_atomic_load(a.meta + gslot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), 0),
-                         (a.CW - first_pos + kPaSeg - 1) / kPaSeg);
+                         (a.CW - first_pos + kSplitSeg - 1) / kSplitSeg);
     float4 tot[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) tot[cb] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     for (int sg = 0; sg < nseg; ++sg) {
-        const float* pp = a.part + pa_part_row(prow + first_pos + static_cast<int64_t>(sg) * kPaSeg, sg == 0) * a.hd;
+        const float* pp = a.part + split_part_row(prow + first_pos + static_cast<int64_t>(sg) * kSplitSeg, sg == 0) * a.hd;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
             const int col = cb * 4 * kWave + 4 * lane;
@@ -506,6 +572,18 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
 
 }  // namespace
 
+GdsWorkspace gds_workspace_layout(const sdm_gds_io* io) {
+    const size_t pos = static_cast<size_t>(io->P) * static_cast<size_t>(io->C) * static_cast<size_t>(io->R);
+    const size_t blocks = (pos + kSplitSeg - 1) / kSplitSeg;
+    auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+    GdsWorkspace w;
+    w.cnt_off = 0;
+    w.meta_off = up(blocks * sizeof(int));
+    w.part_off = w.meta_off + up(blocks * sizeof(int));
+    w.total = w.part_off + up(2 * blocks * static_cast<size_t>(io->hd) * sizeof(float));
+    return w;
+}
+
 hipError_t gds_launch(const sdm_gds_io* io, int64_t ti, hipStream_t st) {
     GdsArgs a;
     a.bank = io->bank;
@@ -528,6 +606,16 @@ hipError_t gds_launch(const sdm_gds_io* io, int64_t ti, hipStream_t st) {
     a.vbf = io->val_bytes == 2;
     a.bank_bf16 = io->bank_dtype == SDM_BF16;
     a.grad_bf16 = io->grad_dtype == SDM_BF16;
+    a.part = nullptr;
+    a.cnt = nullptr;
+    a.meta = nullptr;
+    if (io->workspace != nullptr) {
+        const GdsWorkspace w = gds_workspace_layout(io);
+        char* ws = static_cast<char*>(io->workspace);
+        a.part = reinterpret_cast<float*>(ws + w.part_off);
+        a.cnt = reinterpret_cast<int*>(ws + w.cnt_off);
+        a.meta = reinterpret_cast<int*>(ws + w.meta_off);
+    }
     const int64_t toks = static_cast<int64_t>(io->P) * io->C;
     const int64_t poss = toks * io->R;
     const int64_t items = toks * ((io->R + kDotReads - 1) / kDotReads);   // (token, read group) waves
@@ -539,7 +627,8 @@ hipError_t gds_launch(const sdm_gds_io* io, int64_t ti, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     if (io->grad != nullptr) {
-        e = hipLaunchKernel(reinterpret_cast<const void*>(&gds_scatter_kernel),
+        e = hipLaunchKernel(io->hd <= 4 * kWave ? reinterpret_cast<const void*>(&gds_scatter_kernel<true>)
+                                                : reinterpret_cast<const void*>(&gds_scatter_kernel<false>),
                             dim3(static_cast<unsigned>((poss + kGdsWaves - 1) / kGdsWaves)), dim3(kGdsThreads), kargs, 0, st);
     }
     return e;
@@ -575,7 +664,7 @@ hipError_t gwr_launch(const sdm_gwr_io* io, int64_t ti, hipStream_t st) {
 
 PaWorkspace pa_workspace_layout(const sdm_pa_io* io) {
     const size_t pos = static_cast<size_t>(io->P) * static_cast<size_t>(io->C) * static_cast<size_t>(io->W);
-    const size_t blocks = (pos + kPaSeg - 1) / kPaSeg;
+    const size_t blocks = (pos + kSplitSeg - 1) / kSplitSeg;
     auto up = [](size_t b) { return (b + 255) / 256 * 256; };
     PaWorkspace w;
     w.cnt_off = 0;

@@ -112,6 +112,13 @@ hipError_t read_launch(const ReadLaunch& L, hipStream_t st);
 // GDS of step ti (validated by sdm_gds_step).
 hipError_t gds_launch(const sdm_gds_io* io, int64_t ti, hipStream_t st);
 
+// Workspace of sdm_gds_step: per block of 32 Q-row positions an arrival counter (zero between
+// calls) and a segment count, and two partial rows.
+struct GdsWorkspace {
+    size_t cnt_off, meta_off, part_off, total;
+};
+GdsWorkspace gds_workspace_layout(const sdm_gds_io* io);
+
 // GWR of step ti (validated by sdm_gwr_step).
 hipError_t gwr_launch(const sdm_gwr_io* io, int64_t ti, hipStream_t st);
 

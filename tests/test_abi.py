@@ -293,3 +293,32 @@ def test_pa_workspace_size():
     up = lambda b: (b + 255) // 256 * 256  # noqa: E731
     assert need == up(4 * blocks) + up(4 * blocks) + up(2 * blocks * 96 * 4)
     assert lib.sdm_pa_workspace(ctypes.byref(pa_io(P=0))) == 0
+
+
+def gds_io(**kw):
+    o = _lib.GdsIO()
+    d = dict(bank=FAKE, bank_dtype=_lib.SDM_BF16, rows=1 << 20, hd=128, q_idx=FAKE, q_w=FAKE, spay_q=FAKE, gr=FAKE,
+             step_rows=512, gr_rows=1 << 20, d_q_w=FAKE, grad=FAKE, grad_dtype=_lib.SDM_F32, P=4, C=128, R=16, N=8,
+             first_partial=8, valid_last=128, idx_bytes=4, val_bytes=4)
+    d.update(kw)
+    for k, v in d.items():
+        setattr(o, k, v)
+    return o
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(workspace=FAKE, workspace_bytes=16), _lib.SDM_EWORKSPACE),
+    (dict(workspace=FAKE + 4, workspace_bytes=1 << 40), _lib.SDM_EALIGN),
+    (dict(hd=6), _lib.SDM_ESHAPE),
+])
+def test_gds_workspace_refusals(kw, status):
+    assert _lib.load().sdm_gds_step(ctypes.byref(gds_io(**kw)), 0, None) == status
+
+
+def test_gds_workspace_size():
+    lib = _lib.load()
+    need = lib.sdm_gds_workspace(ctypes.byref(gds_io(P=2, C=64, R=4, hd=96)))
+    blocks = (2 * 64 * 4 + 31) // 32   # one counter, one segment count and two partial rows per 32 positions
+    up = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    assert need == up(4 * blocks) + up(4 * blocks) + up(2 * blocks * 96 * 4)
+    assert lib.sdm_gds_workspace(ctypes.byref(gds_io(R=0))) == 0

@@ -8,6 +8,8 @@ rows (seeded, drawn on the device and read back as the oracle's input).
 Tolerances: a dot of hd float32 products within (hd + 8) 2^-23 sum |g m| + 1e-6; a grad row within
 (m + 4) 2^-23 (|grad0| + sum |q_w g|) + 1e-5 sum |q_w g| (m members; q_w carries at most 1e-5
 relative error from Phase 1), plus one bf16 ulp for a bf16 grad. Untouched grad rows keep their bits.
+With a workspace (read groups of more than 32 members summed in segments) the same bound holds: a
+term passes through at most its segment's chain, the segment additions and the final add.
 """
 
 import os
@@ -53,6 +55,15 @@ def gds_inputs(wl, grad_dtype):
     dict(idx=4, steps=2, checked=[1]),                  # ragged last step
     dict(shape=dict(C=37, W=5, R=3, S=9, P=2, vl=11, hd=36), steps=2, checked=[0, 1], val_bf16=True),
     dict(idx=3, steps=1, checked=[0]),                  # hd = 960: the dots' column loop, multi-block scatter
+    # With a workspace: read groups of more than 32 members are split into segments.
+    dict(idx=2, steps=1, checked=[0], ws=True),         # Zipf: hot slots read hundreds of times
+    dict(idx=3, steps=1, checked=[0], ws=True),         # hd = 960: every column block of a split group
+    dict(shape=dict(C=37, W=5, R=3, S=9, P=2, vl=11, hd=36), steps=2, checked=[0, 1], ws=True),
+    # One read group of 4352 members: the in-group distance saturates, the segment starting at 4064
+    # runs to the group's end.
+    dict(shape=dict(C=256, W=2, R=17, S=1, P=1, vl=None, hd=64), steps=1, checked=[0], ws=True),
+    # One slot per chunk and a fully masked last chunk.
+    dict(shape=dict(C=64, W=2, R=2, S=1, P=1, vl=0, hd=40), steps=2, checked=[0, 1], ws=True),
 ])
 def test_gds_matches_oracle(case):
     if "shape" in case:
@@ -74,8 +85,11 @@ def test_gds_matches_oracle(case):
     for ti in case["checked"]:
         d = torch.full((wl.N, C, R), float("nan"), device="cuda")
         grad = grad0.clone()
-        sdm.gds_step(bank, out, ins["q_idx"], gr, shape, ti, step_rows=P * C, d_q_w=d, grad=grad)
+        ws = sdm.alloc_gds_workspace(shape, hd) if case.get("ws") else None
+        sdm.gds_step(bank, out, ins["q_idx"], gr, shape, ti, step_rows=P * C, d_q_w=d, grad=grad, workspace=ws)
         torch.cuda.synchronize()
+        if ws is not None:   # the arrival counters are back at zero
+            assert not ws[:-(-P * C * R // 32) * 4].any()
         touched = []
         for p in range(P):
             cidx = ti * P + p
@@ -116,8 +130,11 @@ def test_gds_matches_oracle(case):
             assert torch.equal(grad.index_select(0, ci).view(torch.uint8), grad0.index_select(0, ci).view(torch.uint8))
 
 
-def test_gds_reproducible():
-    """Two runs of the same step give the same bytes (sorted-order sums, one writer per row)."""
+@pytest.mark.parametrize("split", [False, True])
+def test_gds_reproducible(split):
+    """Two runs of the same step give the same bytes (sorted-order sums, one writer per row; with a
+    workspace, the long groups' partial rows added in segment order whichever segment finishes last,
+    the second run reusing the workspace the first left)."""
     wl = W.make(2, steps=1)
     sh = wl.shape
     shape, out = H.run_phase1(wl)
@@ -125,11 +142,12 @@ def test_gds_reproducible():
     bank = W.make_bank(wl, "cuda")
     gr_host, grad0 = gds_inputs(wl, bank.dtype)
     gr = torch.from_numpy(gr_host).cuda()
+    ws = sdm.alloc_gds_workspace(shape, sh.hd) if split else None
     res = []
     for _ in range(2):
         d = torch.zeros((wl.N, sh.C, sh.R), device="cuda")
         grad = grad0.clone()
-        sdm.gds_step(bank, out, ins["q_idx"], gr, shape, 0, step_rows=sh.P * sh.C, d_q_w=d, grad=grad)
+        sdm.gds_step(bank, out, ins["q_idx"], gr, shape, 0, step_rows=sh.P * sh.C, d_q_w=d, grad=grad, workspace=ws)
         torch.cuda.synchronize()
         res.append((d, grad))
     assert torch.equal(res[0][0].view(torch.int32), res[1][0].view(torch.int32))
