@@ -91,6 +91,17 @@ typedef struct sdm_p1_shape {
                                reverse and forward scans tile by tile with carries. Its integer outputs
                                equal the on-chip path's bit for bit; its float outputs meet the same
                                tolerance. */
+    int32_t lds_budget;     /* LDS bytes per workgroup the on-chip sort/scan kernel plans with: 0 = the
+                               whole 160 KB; a smaller value (16384 .. 163840) makes it take narrower radix
+                               digits, stage fewer values in LDS and write its outputs in more sweeps, with
+                               every output bit for bit the same (a test knob for those paths). A budget
+                               the shape cannot fit in is refused with SDM_EUNSUPPORTED. The tiled path
+                               and the pair kernel ignore it. */
+    int32_t pair_walk;      /* 0: slot groups with at least 16 valid K entries are summed as a dense
+                               contraction when LDS allows (page "sparse_delta_memory/cuda/phase1_cuda.py",
+                               p1_pairs_hc_kernel: the hot/cold form); 1: every group is walked in the
+                               ordered form. A and QK of the two forms agree within the float32 bound,
+                               not bit for bit; every other output is the same. */
 } sdm_p1_shape;
 
 /*

@@ -24,14 +24,17 @@ __all__ = ["P1Shape", "phase1", "phase1_workspace_bytes", "alloc_phase1_outputs"
 
 
 def make_shape(N, C, W, R, P=1, key_bits=16, stream_offset=0, first_partial=None, valid_last=None, tile_len=128,
-               g_lane_stride=0, idx_bytes=4, val_bytes=4, tiled=False):
+               g_lane_stride=0, idx_bytes=4, val_bytes=4, tiled=False, lds_budget=0, pair_walk=False):
     """Phase-1 shape. g_lane_stride 0: gates g [N, C] (per token); 1: g [N, C, W] (per token and K lane).
     idx_bytes 4: int32 slot ids; 8: int64. val_bytes 4: float32 values; 2: bfloat16 values (and
     bfloat16 cpe, k_eff, q_w). tiled: every row through the tiled path (rows past 16384 entries
-    always take it)."""
+    always take it). lds_budget: LDS bytes the sort/scan kernel plans with (0: all of it; a smaller
+    budget takes its narrower-digit, unstaged and multi-sweep paths, with the same bits). pair_walk:
+    every slot group walked by the pair kernel (no dense hot-group contraction)."""
     return P1Shape(int(N), int(C), int(W), int(R), int(P), int(key_bits), int(stream_offset),
                    int(N if first_partial is None else first_partial), int(C if valid_last is None else valid_last),
-                   int(tile_len), int(g_lane_stride), int(idx_bytes), int(val_bytes), int(bool(tiled)))
+                   int(tile_len), int(g_lane_stride), int(idx_bytes), int(val_bytes), int(bool(tiled)),
+                   int(lds_budget), int(bool(pair_walk)))
 
 
 def phase1_workspace_bytes(shape: P1Shape) -> int:

@@ -27,7 +27,7 @@ class P1Shape(ctypes.Structure):
         ("P", ctypes.c_int32), ("key_bits", ctypes.c_int32), ("stream_offset", ctypes.c_int64),
         ("first_partial", ctypes.c_int32), ("valid_last", ctypes.c_int32), ("tile_len", ctypes.c_int32),
         ("g_lane_stride", ctypes.c_int32), ("idx_bytes", ctypes.c_int32), ("val_bytes", ctypes.c_int32),
-        ("tiled", ctypes.c_int32),
+        ("tiled", ctypes.c_int32), ("lds_budget", ctypes.c_int32), ("pair_walk", ctypes.c_int32),
     ]
 
 

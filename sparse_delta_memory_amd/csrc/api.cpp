@@ -96,6 +96,9 @@ sdm_status check_p1_shape(const sdm_p1_shape* s) {
     const int64_t n = static_cast<int64_t>(s->C) * (s->W + s->R);
     if (n > sdm::kP1MaxTiledRow) return fail(SDM_ESHAPE, "sdm_phase1: C*(W+R) = %lld > 2^17", static_cast<long long>(n));
     if (s->tiled != 0 && s->tiled != 1) return fail(SDM_EINVAL, "sdm_phase1: tiled = %d (0 or 1)", s->tiled);
+    if (s->lds_budget != 0 && (s->lds_budget < 16384 || s->lds_budget > 163840))
+        return fail(SDM_EINVAL, "sdm_phase1: lds_budget = %d (0, or 16384..163840)", s->lds_budget);
+    if (s->pair_walk != 0 && s->pair_walk != 1) return fail(SDM_EINVAL, "sdm_phase1: pair_walk = %d (0 or 1)", s->pair_walk);
     return SDM_OK;
 }
 
@@ -220,10 +223,13 @@ sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st
         return fail(SDM_EWORKSPACE, "sdm_phase1: workspace needs %zu bytes, got %zu", ws.total,
                     io->workspace == nullptr ? size_t(0) : io->workspace_bytes);
     if (!aligned(io->workspace, 16)) return fail(SDM_EALIGN, "sdm_phase1: workspace is not 16-byte aligned");
+    const size_t main_lds = sdm::p1_lds_bytes(s, io);
+    if (main_lds == SIZE_MAX)
+        return fail(SDM_EUNSUPPORTED, "sdm_phase1: the sort/scan kernel's plan does not fit the LDS budget of %d B",
+                    s->lds_budget);
     int lds_max = 0;
     const hipError_t se = device_setup(&lds_max);
     if (se != hipSuccess) return fail(SDM_EHIP, "sdm_phase1: device set-up: %s", hipGetErrorString(se));
-    const size_t main_lds = sdm::p1_lds_bytes(s, io);
     if (main_lds > static_cast<size_t>(lds_max))
         return fail(SDM_EUNSUPPORTED, "sdm_phase1: the sort/scan kernel needs %zu B of LDS per block, the device has %d",
                     main_lds, lds_max);

@@ -276,7 +276,7 @@ struct GwrArgs {
 
 // NCB: the 256-column blocks a lane's registers hold (1, 2 or 4: hd <= 256, 512, 1024), so that
 // narrow rows keep few registers and many waves per SIMD.
-template <int NCB>
+template <int NCB, int GR>
 __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
     const int wv = static_cast<int>(threadIdx.x) / kWave;
     const int lane = static_cast<int>(lane_id());
@@ -310,12 +310,12 @@ __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
                                                   : static_cast<const int32_t*>(a.k_idx)[eo + nb + lane])
                                         : -1;
         const float my_w = lane < nr ? a.w[eo + nb + lane] : 0.0f;
-        for (int n0 = 0; n0 < nr; n0 += kDotReads) {
-            int64_t s[kDotReads];
-            bool ok[kDotReads];
-            float wu[kDotReads], part[kDotReads];
+        for (int n0 = 0; n0 < nr; n0 += GR) {
+            int64_t s[GR];
+            bool ok[GR];
+            float wu[GR], part[GR];
 #pragma unroll
-            for (int u = 0; u < kDotReads; ++u) {
+            for (int u = 0; u < GR; ++u) {
                 const int src = min(n0 + u, nr - 1);
                 s[u] = shfl64(my_id, src);
                 wu[u] = __shfl(my_w, src, kWave);
@@ -326,11 +326,11 @@ __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
             for (int cb = 0; cb < NCB; ++cb) {
                 const int col = cb * 4 * kWave + 4 * lane;
                 if (col >= a.hd) break;
-                float4 g[kDotReads];
+                float4 g[GR];
 #pragma unroll
-                for (int u = 0; u < kDotReads; ++u) g[u] = load4(a.grad, a.grad_bf16, ok[u] ? s[u] : 0, a.hd, col);
+                for (int u = 0; u < GR; ++u) g[u] = load4(a.grad, a.grad_bf16, ok[u] ? s[u] : 0, a.hd, col);
 #pragma unroll
-                for (int u = 0; u < kDotReads; ++u) {
+                for (int u = 0; u < GR; ++u) {
                     if (ok[u]) {
                         acc[cb].x = fmaf(wu[u], g[u].x, acc[cb].x);
                         acc[cb].y = fmaf(wu[u], g[u].y, acc[cb].y);
@@ -342,7 +342,7 @@ __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
             }
             if (a.d_k_pd != nullptr) {
 #pragma unroll
-                for (int u = 0; u < kDotReads; ++u) {
+                for (int u = 0; u < GR; ++u) {
                     const float d = wave_sum(part[u]);
                     if (lane == 0 && n0 + u < nr) a.d_k_pd[eo + nb + n0 + u] = d;
                 }
@@ -655,9 +655,9 @@ hipError_t gwr_launch(const sdm_gwr_io* io, int64_t ti, hipStream_t st) {
     a.grad_bf16 = io->grad_dtype == SDM_BF16;
     const int64_t toks = static_cast<int64_t>(io->P) * io->C;
     void* kargs[] = {&a};
-    const void* fn = io->hd <= 256 ? reinterpret_cast<const void*>(&gwr_kernel<1>)
-                   : io->hd <= 512 ? reinterpret_cast<const void*>(&gwr_kernel<2>)
-                                   : reinterpret_cast<const void*>(&gwr_kernel<4>);
+    const void* fn = io->hd <= 256 ? reinterpret_cast<const void*>(&gwr_kernel<1, 8>)
+                   : io->hd <= 512 ? reinterpret_cast<const void*>(&gwr_kernel<2, 4>)
+                                   : reinterpret_cast<const void*>(&gwr_kernel<4, 4>);
     return hipLaunchKernel(fn,
                            dim3(static_cast<unsigned>((toks + kGdsWaves - 1) / kGdsWaves)), dim3(kGdsThreads), kargs, 0, st);
 }

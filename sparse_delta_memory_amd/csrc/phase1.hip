@@ -1323,7 +1323,8 @@ MainPlan plan_main(const sdm_p1_shape* s, bool with_pairs_ws) {
     // Sorted row, gates and (with pair sums) the chunk's hot-group list.
     const int fixed = np * 2 + 256 * static_cast<int>(sizeof(float)) +
                       (with_pairs_ws ? s->C * s->W / kHotMin * static_cast<int>(sizeof(uint2)) : 0);
-    const int cap_max = (kLdsTotal - kStaticReserve - fixed) / 16 * 16;
+    const int total = s->lds_budget > 0 ? min(kLdsTotal, s->lds_budget) : kLdsTotal;   // (a test budget)
+    const int cap_max = (total - kStaticReserve - fixed) / 16 * 16;
     // Widest digit (<= 10 bits) whose per-wave counts fit beside the keys (and, in the resident
     // layout, beside the keys and the staged values, with the records fitting there too).
     const int vals_bytes = (((s->C * s->W + 3) & ~3) + ((s->C * s->R + 3) & ~3)) * 4;
@@ -1461,7 +1462,11 @@ size_t p1_pair_lds_min(const sdm_p1_shape* s) { return pair_lds_layout(s->C, 0, 
 
 size_t p1_lds_bytes(const sdm_p1_shape* s, const sdm_p1_io* io) {
     if (p1_tiled(s)) return p1_tiled_lds_bytes(s);
-    return plan_main(s, io->a != nullptr || io->qk != nullptr).lds_bytes;
+    const MainPlan m = plan_main(s, io->a != nullptr || io->qk != nullptr);
+    const size_t budget = s->lds_budget > 0 ? static_cast<size_t>(min(kLdsTotal, s->lds_budget)) : static_cast<size_t>(kLdsTotal);
+    // (a plan over the budget, or with more sweeps than the kernel takes, is refused)
+    if (m.sweeps.count > kMaxSweeps || m.lds_bytes + kStaticReserve > budget) return SIZE_MAX;
+    return m.lds_bytes;
 }
 
 PairPlan pair_plan(const sdm_p1_shape* s, bool pairs, int lds_max) {
@@ -1477,7 +1482,7 @@ PairPlan pair_plan(const sdm_p1_shape* s, bool pairs, int lds_max) {
                                    static_cast<int>((static_cast<size_t>(lds_max) / pp.blocks_cu - pair_fixed) / per_group))
                              : 0;
     // (A hot list too long for LDS beside the triangle, as with C = 256, W = 256: every group walked.)
-    pp.hot_on = pairs && pp.hot_cap > 0 && pp.gb >= 4;
+    pp.hot_on = pairs && pp.hot_cap > 0 && pp.gb >= 4 && s->pair_walk == 0;   // (pair_walk: every group walked)
     if (!pp.hot_on) {   // the triangle alone per block
         pp.gb = 0;
         pp.blocks_cu = max(1, static_cast<int>(static_cast<size_t>(lds_max) / (pair_lds_layout(s->C, 0, 0).total + kPairStaticLds)));

@@ -31,7 +31,7 @@ def test_exports_every_declared_function():
 
 def shape(**kw):
     d = dict(N=4, C=64, W=4, R=4, P=1, key_bits=12, stream_offset=0, first_partial=4, valid_last=64, tile_len=128,
-             g_lane_stride=0, idx_bytes=4, val_bytes=4, tiled=0)
+             g_lane_stride=0, idx_bytes=4, val_bytes=4, tiled=0, lds_budget=0, pair_walk=0)
     d.update(kw)
     return _lib.P1Shape(*[d[f] for f, _ in _lib.P1Shape._fields_])
 
@@ -322,3 +322,21 @@ def test_gds_workspace_size():
     up = lambda b: (b + 255) // 256 * 256  # noqa: E731
     assert need == up(4 * blocks) + up(4 * blocks) + up(2 * blocks * 96 * 4)
     assert lib.sdm_gds_workspace(ctypes.byref(gds_io(R=0))) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lds_budget=1000), _lib.SDM_EINVAL), (dict(lds_budget=200000), _lib.SDM_EINVAL),
+    (dict(lds_budget=-1), _lib.SDM_EINVAL), (dict(pair_walk=2), _lib.SDM_EINVAL),
+])
+def test_phase1_knob_refusals(kw, status):
+    assert call_p1(shape(**kw), io()) == status
+    assert len(_lib.load().sdm_last_error()) > 0
+
+
+def test_phase1_lds_budget_too_small_is_refused_before_any_device_call():
+    """A budget the sort/scan kernel's plan cannot fit in (a 16384-entry row needs its 64 KB of keys
+    and more) is refused on the host, without touching the device."""
+    s = shape(N=2, C=256, W=32, R=32, first_partial=2, valid_last=256, lds_budget=65536)
+    need = _lib.load().sdm_phase1_workspace(ctypes.byref(s))
+    assert call_p1(s, io(workspace_bytes=need)) == _lib.SDM_EUNSUPPORTED
+    assert b"budget" in _lib.load().sdm_last_error()
