@@ -1,7 +1,8 @@
 /*
  * sdm.h - C ABI of the MI355X (gfx950) forward hot path of the chunked sparse-delta-memory
  * (SDM) recurrence: Phase 1 (the memory-independent per-chunk quantities) and the DW
- * decay-and-write step.
+ * decay-and-write step; beside them the read side of a step and the backward movers (GDS, GWR,
+ * PA).
  *
  * Conventions shared by every entry point
  *  - All array arguments are DEVICE pointers owned by the caller. The library allocates no
