@@ -947,6 +947,18 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
     uint32_t* bmask = reinterpret_cast<uint32_t*>(smem + lay.bmask);    // per group: x blocks (2 words), y blocks (2)
     float* xt = reinterpret_cast<float*>(smem + lay.xt);
     float* yt = reinterpret_cast<float*>(smem + lay.yt);
+    // The walkers' first 32 entry-order words (16-bit words, rows of a multiple of 8 lanes): loaded
+    // before anything else, so that the walks find them in registers.
+    const int pre_lanes = q ? R : W;
+    const bool pre = sizeof(InvT) == 2 && pre_lanes % 8 == 0 && static_cast<int>(threadIdx.x) < tv;
+    uint4 ivp[4] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u),
+                    make_uint4(0u, 0u, 0u, 0u)};
+    if (pre) {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const InvT*>(q ? a.inv_q : a.inv_k) +
+                                                          (static_cast<int64_t>(c) * C + threadIdx.x) * pre_lanes);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) ivp[v] = v * 8 < pre_lanes ? src[v] : make_uint4(0u, 0u, 0u, 0u);
+    }
     const int tri_size = tri_row(C);
     for (int e = threadIdx.x; e < tri_size / 4; e += kPairThreads) reinterpret_cast<float4*>(tri)[e] = make_float4(0.f, 0.f, 0.f, 0.f);
     const int64_t crow = static_cast<int64_t>(c) * n;
@@ -1248,10 +1260,20 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
         for (int lb = 0; lb < lanes; lb += 32) {
           uint32_t flags = 0;
           const uint32_t walk_bits = any_wide ? (InvBits<InvT>::kWalk | InvBits<InvT>::kHot) : InvBits<InvT>::kWalk;
+          if (pre && lb == 0) {   // (the preloaded words: lanes 0..31, zeros past the row)
 #pragma unroll
-          for (int u = 0; u < 32; ++u) {
-              const int ln = lb + u;
-              flags |= (ln < lanes && (iv[min(ln, lanes - 1)] & walk_bits)) ? (1u << u) : 0u;
+              for (int u = 0; u < 32; ++u) {
+                  const uint4 v4 = ivp[u / 8];
+                  const uint32_t w2 = (u % 8) < 2 ? v4.x : (u % 8) < 4 ? v4.y : (u % 8) < 6 ? v4.z : v4.w;
+                  const uint32_t word = (u % 2) ? (w2 >> 16) : (w2 & 0xFFFFu);
+                  flags |= (u < lanes && (word & walk_bits)) ? (1u << u) : 0u;
+              }
+          } else {
+#pragma unroll
+              for (int u = 0; u < 32; ++u) {
+                  const int ln = lb + u;
+                  flags |= (ln < lanes && (iv[min(ln, lanes - 1)] & walk_bits)) ? (1u << u) : 0u;
+              }
           }
           // Walks two at a time: both record windows in flight before either is walked (the terms
           // still reach the row in lane order).
