@@ -75,10 +75,24 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// A 64-bit value of another lane.
-__device__ __forceinline__ int64_t shfl64(int64_t v, int src) {
-    const int lo = __shfl(static_cast<int>(static_cast<uint64_t>(v) & 0xFFFFFFFFull), src, kWave);
-    const int hi = __shfl(static_cast<int>(static_cast<uint64_t>(v) >> 32), src, kWave);
+// Sum over a team of TEAM lanes (the wave's 32-lane halves, or the whole wave).
+template <int TEAM>
+__device__ __forceinline__ float team_sum(float v) {
+#pragma unroll
+    for (int d = TEAM / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
+// A ballot restricted to the lane's team, shifted so that bit i is team lane i.
+template <int TEAM>
+__device__ __forceinline__ uint64_t team_bits(uint64_t ballot, int lane) {
+    return TEAM == kWave ? ballot : (ballot >> (lane / TEAM * TEAM)) & ((1ull << TEAM) - 1ull);
+}
+
+// A 64-bit value of another lane (src counted within segments of `width` lanes).
+__device__ __forceinline__ int64_t shfl64(int64_t v, int src, int width = kWave) {
+    const int lo = __shfl(static_cast<int>(static_cast<uint64_t>(v) & 0xFFFFFFFFull), src, width);
+    const int hi = __shfl(static_cast<int>(static_cast<uint64_t>(v) >> 32), src, width);
     return static_cast<int64_t>(static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32 | static_cast<uint32_t>(lo));
 }
 
@@ -400,11 +414,12 @@ __device__ __forceinline__ void store4(void* base, int bf, int64_t row, int hd, 
 // from +0. A group in one segment then writes grad = fma(gdw, cpe, acc) and restores the bank row;
 // a split group's segments publish their partial rows, and the last to arrive adds them in segment
 // order and writes the rows (the same sums whichever segment arrives last).
-template <int NCB>
+template <int NCB, int TEAM>
 __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
     const int wv = static_cast<int>(threadIdx.x) / kWave;
     const int lane = static_cast<int>(lane_id());
-    const int64_t pos = static_cast<int64_t>(blockIdx.x) * kGdsWaves + wv;   // p * CW + j
+    const int tl = lane % TEAM;   // lane in the team (TEAM lanes per K-row position)
+    const int64_t pos = (static_cast<int64_t>(blockIdx.x) * kGdsWaves + wv) * (kWave / TEAM) + lane / TEAM;   // p * CW + j
     if (pos >= static_cast<int64_t>(a.P) * a.CW) return;
     const int p = static_cast<int>(pos / a.CW), j = static_cast<int>(pos % a.CW);
     const int64_t c = a.chunk0 + p;
@@ -414,7 +429,7 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
         return (c * a.C + static_cast<int64_t>((el >> kTokShift) & 0xFFu)) * a.W + (el & 0xFFu);
     };
     if (r0.x & kInvalid) {   // padding: its outputs are zero
-        if (lane == 0) {
+        if (tl == 0) {
             if (a.g_decay != nullptr) a.g_decay[eidx(r0.x)] = 0.0f;
             if (a.d_k_eff != nullptr) a.d_k_eff[eidx(r0.x)] = 0.0f;
         }
@@ -434,27 +449,27 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
     float part0 = 0.0f;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-        const int col = cb * 4 * kWave + 4 * lane;
+        const int col = cb * 4 * TEAM + 4 * tl;
         const bool con = in && col < a.hd;
         gdw[cb] = con ? load4(a.grad, a.grad_bf16, slot, a.hd, col) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         sn[cb] = con ? load4(a.snap, a.bank_bf16, srow, a.hd, col) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         acc[cb] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         part0 = fmaf(gdw[cb].w, sn[cb].w, fmaf(gdw[cb].z, sn[cb].z, fmaf(gdw[cb].y, sn[cb].y, fmaf(gdw[cb].x, sn[cb].x, part0))));
     }
-    const float dot0 = wave_sum(part0);
+    const float dot0 = team_sum<TEAM>(part0);
     const int64_t grow0 = a.row0 + static_cast<int64_t>(p) * a.C;
     bool done = false, last_seen = false;
     int taken = 0;
-    for (int m0 = j; !done && m0 < a.CW; m0 += kWave) {   // members 64 records at a time, in sorted order
-        const int budget = unbounded ? kWave : min(kWave, kSplitSeg - taken);   // members this segment may still take
-        const int m = m0 + lane;
+    for (int m0 = j; !done && m0 < a.CW; m0 += TEAM) {   // members TEAM records at a time, in sorted order
+        const int budget = unbounded ? TEAM : min(TEAM, kSplitSeg - taken);   // members this segment may still take
+        const int m = m0 + tl;
         const uint32_t el = m < a.CW ? kr[m].x : (kFirst | kLast | kInvalid);
         const int tk = static_cast<int>((el >> kTokShift) & 0xFFu);
         const bool valid = m < a.CW && !(el & kInvalid);
         const float nb = valid ? -a.beta[c * a.C + tk] : 0.0f;
         const float w = valid ? nb * load_val(a.k_eff, eidx(el), a.vbf) : 0.0f;
         const int64_t ei = valid ? eidx(el) : 0;
-        const uint64_t lastm = __ballot(lane < budget && (el & kLast) != 0u);
+        const uint64_t lastm = team_bits<TEAM>(__ballot(tl < budget && (el & kLast) != 0u), lane);
         const int cnt = lastm != 0ull ? __builtin_ctzll(lastm) + 1 : budget;   // (LAST included)
         last_seen = lastm != 0ull;
         taken += cnt;
@@ -466,13 +481,13 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
 #pragma unroll
             for (int u = 0; u < kPaMembers; ++u) {
                 const int kk = min(k0 + u, cnt - 1);
-                wk[u] = __shfl(w, kk, kWave);
-                bk[u] = __shfl(nb, kk, kWave);
-                ek[u] = shfl64(ei, kk);
-                const int t = __shfl(tk, kk, kWave);
+                wk[u] = __shfl(w, kk, TEAM);
+                bk[u] = __shfl(nb, kk, TEAM);
+                ek[u] = shfl64(ei, kk, TEAM);
+                const int t = __shfl(tk, kk, TEAM);
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) {
-                    const int col = cb * 4 * kWave + 4 * lane;
+                    const int col = cb * 4 * TEAM + 4 * tl;
                     d[u][cb] = col < a.hd ? load4(a.d_dva, 0, grow0 + t, a.hd, col) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                 }
             }
@@ -488,8 +503,8 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
                     acc[cb].w = fmaf(wk[u], d[u][cb].w, acc[cb].w);
                     part = fmaf(d[u][cb].w, sn[cb].w, fmaf(d[u][cb].z, sn[cb].z, fmaf(d[u][cb].y, sn[cb].y, fmaf(d[u][cb].x, sn[cb].x, part))));
                 }
-                const float dot = wave_sum(part);
-                if (lane == 0) {
+                const float dot = team_sum<TEAM>(part);
+                if (tl == 0) {
                     if (a.d_k_eff != nullptr) a.d_k_eff[ek[u]] = bk[u] * dot;
                     if (a.g_decay != nullptr) a.g_decay[ek[u]] = cpe * dot0;
                 }
@@ -500,7 +515,7 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
         if (!in) return;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-            const int col = cb * 4 * kWave + 4 * lane;
+            const int col = cb * 4 * TEAM + 4 * tl;
             if (col >= a.hd) break;
             const float4 g = make_float4(fmaf(gdw[cb].x, cpe, acc[cb].x), fmaf(gdw[cb].y, cpe, acc[cb].y),
                                          fmaf(gdw[cb].z, cpe, acc[cb].z), fmaf(gdw[cb].w, cpe, acc[cb].w));
@@ -520,7 +535,7 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
     float* part = a.part + split_part_row(prow + j, dist == 0) * a.hd;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-        const int col = cb * 4 * kWave + 4 * lane;
+        const int col = cb * 4 * TEAM + 4 * tl;
         if (col < a.hd) {
             __hip_atomic_store(part + col, acc[cb].x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(part + col + 1, acc[cb].y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -530,14 +545,14 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
     }
     const int seg = dist / kSplitSeg;
     // The segment holding LAST publishes the segment count.
-    if (last_seen && lane == 0) __hip_atomic_store(a.meta + gslot, seg + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (last_seen && tl == 0) __hip_atomic_store(a.meta + gslot, seg + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stores above have completed
     // The segment holding LAST adds 1 - (segments), every other adds 1: the counter returns to 0
     // exactly at the last arrival (and is left at 0 for the next call).
     const int delta = last_seen ? -seg : 1;
     int after = 0;
-    if (lane == 0) after = atomicAdd(a.cnt + gslot, delta) + delta;
-    after = __shfl(after, 0, kWave);
+    if (tl == 0) after = atomicAdd(a.cnt + gslot, delta) + delta;
+    after = __shfl(after, 0, TEAM);
     if (after != 0) return;
     // (clamped to the segment starts the row holds, so no read can leave the workspace)
     const int nseg = min(max(__hip_atomic_load(a.meta + gslot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), 0),
@@ -549,7 +564,7 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
         const float* pp = a.part + split_part_row(prow + first_pos + static_cast<int64_t>(sg) * kSplitSeg, sg == 0) * a.hd;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-            const int col = cb * 4 * kWave + 4 * lane;
+            const int col = cb * 4 * TEAM + 4 * tl;
             if (col < a.hd) {
                 tot[cb].x = tot[cb].x + __hip_atomic_load(pp + col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 tot[cb].y = tot[cb].y + __hip_atomic_load(pp + col + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -561,7 +576,7 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
     if (!in) return;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-        const int col = cb * 4 * kWave + 4 * lane;
+        const int col = cb * 4 * TEAM + 4 * tl;
         if (col >= a.hd) break;
         const float4 g = make_float4(fmaf(gdw[cb].x, cpe, tot[cb].x), fmaf(gdw[cb].y, cpe, tot[cb].y),
                                      fmaf(gdw[cb].z, cpe, tot[cb].z), fmaf(gdw[cb].w, cpe, tot[cb].w));
@@ -709,11 +724,14 @@ hipError_t pa_launch(const sdm_pa_io* io, int64_t ti, hipStream_t st) {
     }
     const int64_t poss = static_cast<int64_t>(io->P) * io->C * io->W;
     void* kargs[] = {&a};
-    const void* fn = io->hd <= 256 ? reinterpret_cast<const void*>(&pa_kernel<1>)
-                   : io->hd <= 512 ? reinterpret_cast<const void*>(&pa_kernel<2>)
-                                   : reinterpret_cast<const void*>(&pa_kernel<4>);
-    return hipLaunchKernel(fn,
-                           dim3(static_cast<unsigned>((poss + kGdsWaves - 1) / kGdsWaves)), dim3(kGdsThreads), kargs, 0, st);
+    // Rows of up to 128 columns: a 32-lane team per K-row position, two per wave.
+    const bool half = io->hd <= 4 * 32;
+    const void* fn = half ? reinterpret_cast<const void*>(&pa_kernel<1, 32>)
+                   : io->hd <= 256 ? reinterpret_cast<const void*>(&pa_kernel<1, kWave>)
+                   : io->hd <= 512 ? reinterpret_cast<const void*>(&pa_kernel<2, kWave>)
+                                   : reinterpret_cast<const void*>(&pa_kernel<4, kWave>);
+    const int64_t per_block = static_cast<int64_t>(kGdsWaves) * (half ? 2 : 1);
+    return hipLaunchKernel(fn, dim3(static_cast<unsigned>((poss + per_block - 1) / per_block)), dim3(kGdsThreads), kargs, 0, st);
 }
 
 }  // namespace sdm
