@@ -99,11 +99,14 @@ __device__ __forceinline__ int64_t shfl64(int64_t v, int src, int width = kWave)
 constexpr int kDotReads = 4;   // reads whose rows are in flight together
 constexpr int kWalkRows = 8;   // member gradient rows in flight together
 
+// TEAM: lanes per item (32 for rows of up to 128 columns: two items per wave).
+template <int TEAM>
 __global__ void __launch_bounds__(kGdsThreads) gds_dots_kernel(GdsArgs a) {
     const int wv = static_cast<int>(threadIdx.x) / kWave;
     const int lane = static_cast<int>(lane_id());
+    const int tl = lane % TEAM;
     const int groups = (a.R + kDotReads - 1) / kDotReads;   // read groups per token
-    const int64_t item = static_cast<int64_t>(blockIdx.x) * kGdsWaves + wv;   // (p, t, read group) of the step
+    const int64_t item = (static_cast<int64_t>(blockIdx.x) * kGdsWaves + wv) * (kWave / TEAM) + lane / TEAM;   // (p, t, read group)
     if (item >= static_cast<int64_t>(a.P) * a.C * groups) return;
     const int64_t tok = item / groups;
     const int r0 = static_cast<int>(item % groups) * kDotReads;
@@ -113,20 +116,20 @@ __global__ void __launch_bounds__(kGdsThreads) gds_dots_kernel(GdsArgs a) {
     const int tv = c >= a.first_partial ? a.valid_last : a.C;
     const int64_t eo = (c * a.C + t) * a.R + r0;   // the group's first Q entry
     if (t >= tv) {   // masked: no reads, dots 0
-        if (lane < nr) a.d_q_w[eo + lane] = 0.0f;
+        if (tl < nr) a.d_q_w[eo + tl] = 0.0f;
         return;
     }
     const int64_t grow = a.row0 + static_cast<int64_t>(p) * a.C + t;
-    const int64_t my_id = lane < nr ? gds_id(a, eo + lane) : -1;
+    const int64_t my_id = tl < nr ? gds_id(a, eo + tl) : -1;
     int64_t s[kDotReads];
     bool ok[kDotReads];
 #pragma unroll
     for (int u = 0; u < kDotReads; ++u) {
-        s[u] = shfl64(my_id, min(u, nr - 1));
+        s[u] = shfl64(my_id, min(u, nr - 1), TEAM);
         ok[u] = u < nr && s[u] >= 0 && s[u] < a.rows;   // (a slot outside the bank contributes nothing)
     }
     float acc[kDotReads] = {};
-    for (int col = 4 * lane; col < a.hd; col += 4 * kWave) {
+    for (int col = 4 * tl; col < a.hd; col += 4 * TEAM) {
         const float4 g = load4(a.gr, 0, grow, a.hd, col);
         float4 m[kDotReads];
 #pragma unroll
@@ -138,18 +141,20 @@ __global__ void __launch_bounds__(kGdsThreads) gds_dots_kernel(GdsArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < kDotReads; ++u) {
-        const float d = wave_sum(acc[u]);
-        if (lane == 0 && u < nr) a.d_q_w[eo + u] = d;
+        const float d = team_sum<TEAM>(acc[u]);
+        if (tl == 0 && u < nr) a.d_q_w[eo + u] = d;
     }
 }
 
-// ONE: hd <= 256, a single column block (no column loop).
-template <bool ONE>
+// ONE: hd <= 4 TEAM, a single column block (no column loop); TEAM: lanes per Q-row position (32 for
+// rows of up to 128 columns: two positions per wave).
+template <bool ONE, int TEAM>
 __global__ void __launch_bounds__(kGdsThreads) gds_scatter_kernel(GdsArgs a) {
     const int wv = static_cast<int>(threadIdx.x) / kWave;
     const int lane = static_cast<int>(lane_id());
+    const int tl = lane % TEAM;
     const int n = a.C * a.R;
-    const int64_t pos = static_cast<int64_t>(blockIdx.x) * kGdsWaves + wv;   // p * C * R + j
+    const int64_t pos = (static_cast<int64_t>(blockIdx.x) * kGdsWaves + wv) * (kWave / TEAM) + lane / TEAM;   // p * C * R + j
     if (pos >= static_cast<int64_t>(a.P) * n) return;
     const int p = static_cast<int>(pos / n), j = static_cast<int>(pos % n);
     const int64_t c = a.chunk0 + p;
@@ -184,22 +189,22 @@ __global__ void __launch_bounds__(kGdsThreads) gds_scatter_kernel(GdsArgs a) {
     };
     const int64_t prow = static_cast<int64_t>(p) * n;
     bool last_seen = false;
-    for (int col0 = 0; col0 < (ONE ? 1 : a.hd); col0 += 4 * kWave) {
-        const int col = col0 + 4 * lane;
+    for (int col0 = 0; col0 < (ONE ? 1 : a.hd); col0 += 4 * TEAM) {
+        const int col = col0 + 4 * tl;
         const bool con = col < a.hd;
         float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         bool done = false;
         int taken = 0;
         // The members in sorted order, 64 records at a time (lane l: member m0 + l), their gradient
         // rows kWalkRows at a time; the sum runs over the members in order from +0.
-        for (int m0 = j; !done && m0 < n; m0 += kWave) {
-            const int budget = unbounded ? kWave : min(kWave, kSplitSeg - taken);   // members still in the segment
-            const int m = m0 + lane;
+        for (int m0 = j; !done && m0 < n; m0 += TEAM) {
+            const int budget = unbounded ? TEAM : min(TEAM, kSplitSeg - taken);   // members still in the segment
+            const int m = m0 + tl;
             const uint32_t el = m < n ? row[m] : (kFirst | kLast | kInvalid);
             const int tk = static_cast<int>((el >> kTokShift) & 0xFFu);
             const bool in = m < n && !(el & kInvalid);
             const float w = in ? load_val(a.q_w, qbase + entry(el), a.vbf) : 0.0f;
-            const uint64_t lastm = __ballot(lane < budget && (el & kLast) != 0u);
+            const uint64_t lastm = team_bits<TEAM>(__ballot(tl < budget && (el & kLast) != 0u), lane);
             const int cnt = lastm != 0ull ? __builtin_ctzll(lastm) + 1 : budget;   // (LAST included)
             last_seen = lastm != 0ull;
             taken += cnt;
@@ -210,8 +215,8 @@ __global__ void __launch_bounds__(kGdsThreads) gds_scatter_kernel(GdsArgs a) {
 #pragma unroll
                 for (int u = 0; u < kWalkRows; ++u) {
                     const int kk = min(k0 + u, cnt - 1);
-                    wk[u] = __shfl(w, kk, kWave);
-                    const int t = __shfl(tk, kk, kWave);
+                    wk[u] = __shfl(w, kk, TEAM);
+                    const int t = __shfl(tk, kk, TEAM);
                     g[u] = con ? load4(a.gr, 0, grow0 + t, a.hd, col) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                 }
 #pragma unroll
@@ -245,20 +250,20 @@ __global__ void __launch_bounds__(kGdsThreads) gds_scatter_kernel(GdsArgs a) {
     const int first_pos = j - dist;
     const int64_t gslot = split_group_slot(prow + first_pos);
     const int seg = dist / kSplitSeg;
-    if (last_seen && lane == 0) __hip_atomic_store(a.meta + gslot, seg + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (last_seen && tl == 0) __hip_atomic_store(a.meta + gslot, seg + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stores above have completed
     // The segment holding LAST adds 1 - (segments), every other adds 1: the counter returns to 0
     // exactly at the last arrival (and is left at 0 for the next call).
     const int delta = last_seen ? -seg : 1;
     int after = 0;
-    if (lane == 0) after = atomicAdd(a.cnt + gslot, delta) + delta;
-    after = __shfl(after, 0, kWave);
+    if (tl == 0) after = atomicAdd(a.cnt + gslot, delta) + delta;
+    after = __shfl(after, 0, TEAM);
     if (after != 0) return;
     // (clamped to the segment starts the row holds, so no read can leave the workspace)
     const int nseg = min(max(__hip_atomic_load(a.meta + gslot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), 0),
                          (n - first_pos + kSplitSeg - 1) / kSplitSeg);
-    for (int col0 = 0; col0 < (ONE ? 1 : a.hd); col0 += 4 * kWave) {
-        const int col = col0 + 4 * lane;
+    for (int col0 = 0; col0 < (ONE ? 1 : a.hd); col0 += 4 * TEAM) {
+        const int col = col0 + 4 * tl;
         if (col >= a.hd) continue;
         float4 tot = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         for (int sg = 0; sg < nseg; ++sg) {
@@ -290,11 +295,12 @@ struct GwrArgs {
 
 // NCB: the 256-column blocks a lane's registers hold (1, 2 or 4: hd <= 256, 512, 1024), so that
 // narrow rows keep few registers and many waves per SIMD.
-template <int NCB, int GR>
+template <int NCB, int GR, int TEAM>
 __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
     const int wv = static_cast<int>(threadIdx.x) / kWave;
     const int lane = static_cast<int>(lane_id());
-    const int64_t tok = static_cast<int64_t>(blockIdx.x) * kGdsWaves + wv;
+    const int tl = lane % TEAM;   // lane in the token's team (TEAM lanes per token)
+    const int64_t tok = (static_cast<int64_t>(blockIdx.x) * kGdsWaves + wv) * (kWave / TEAM) + lane / TEAM;
     if (tok >= static_cast<int64_t>(a.P) * a.C) return;
     const int p = static_cast<int>(tok / a.C), t = static_cast<int>(tok % a.C);
     const int64_t c = a.chunk0 + p;
@@ -303,10 +309,10 @@ __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
     const int64_t vrow = a.row0 + static_cast<int64_t>(p) * a.C + t;
     if (t >= tv) {   // masked: zeros, nothing read
         if (a.d_k_pd != nullptr) {
-            for (int n = lane; n < a.W; n += kWave) a.d_k_pd[eo + n] = 0.0f;
+            for (int n = tl; n < a.W; n += TEAM) a.d_k_pd[eo + n] = 0.0f;
         }
         if (a.d_dv != nullptr) {
-            for (int col = 4 * lane; col < a.hd; col += 4 * kWave)
+            for (int col = 4 * tl; col < a.hd; col += 4 * TEAM)
                 *reinterpret_cast<float4*>(a.d_dv + vrow * a.hd + col) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
         return;
@@ -314,16 +320,16 @@ __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
     float4 v[NCB], acc[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-        const int col = cb * 4 * kWave + 4 * lane;
+        const int col = cb * 4 * TEAM + 4 * tl;
         v[cb] = col < a.hd ? *reinterpret_cast<const float4*>(a.dv + vrow * a.hd + col) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         acc[cb] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
-    for (int nb = 0; nb < a.W; nb += kWave) {
-        const int nr = min(kWave, a.W - nb);
-        const int64_t my_id = lane < nr ? (a.id64 ? static_cast<const int64_t*>(a.k_idx)[eo + nb + lane]
-                                                  : static_cast<const int32_t*>(a.k_idx)[eo + nb + lane])
+    for (int nb = 0; nb < a.W; nb += TEAM) {
+        const int nr = min(TEAM, a.W - nb);
+        const int64_t my_id = tl < nr ? (a.id64 ? static_cast<const int64_t*>(a.k_idx)[eo + nb + tl]
+                                                  : static_cast<const int32_t*>(a.k_idx)[eo + nb + tl])
                                         : -1;
-        const float my_w = lane < nr ? a.w[eo + nb + lane] : 0.0f;
+        const float my_w = tl < nr ? a.w[eo + nb + tl] : 0.0f;
         for (int n0 = 0; n0 < nr; n0 += GR) {
             int64_t s[GR];
             bool ok[GR];
@@ -331,14 +337,14 @@ __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
 #pragma unroll
             for (int u = 0; u < GR; ++u) {
                 const int src = min(n0 + u, nr - 1);
-                s[u] = shfl64(my_id, src);
-                wu[u] = __shfl(my_w, src, kWave);
+                s[u] = shfl64(my_id, src, TEAM);
+                wu[u] = __shfl(my_w, src, TEAM);
                 ok[u] = n0 + u < nr && s[u] >= 0 && s[u] < a.rows;   // (a slot outside the bank contributes nothing)
                 part[u] = 0.0f;
             }
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
-                const int col = cb * 4 * kWave + 4 * lane;
+                const int col = cb * 4 * TEAM + 4 * tl;
                 if (col >= a.hd) break;
                 float4 g[GR];
 #pragma unroll
@@ -357,8 +363,8 @@ __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
             if (a.d_k_pd != nullptr) {
 #pragma unroll
                 for (int u = 0; u < GR; ++u) {
-                    const float d = wave_sum(part[u]);
-                    if (lane == 0 && n0 + u < nr) a.d_k_pd[eo + nb + n0 + u] = d;
+                    const float d = team_sum<TEAM>(part[u]);
+                    if (tl == 0 && n0 + u < nr) a.d_k_pd[eo + nb + n0 + u] = d;
                 }
             }
         }
@@ -366,7 +372,7 @@ __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
     if (a.d_dv != nullptr) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-            const int col = cb * 4 * kWave + 4 * lane;
+            const int col = cb * 4 * TEAM + 4 * tl;
             if (col < a.hd) *reinterpret_cast<float4*>(a.d_dv + vrow * a.hd + col) = acc[cb];
         }
     }
@@ -633,18 +639,23 @@ hipError_t gds_launch(const sdm_gds_io* io, int64_t ti, hipStream_t st) {
     }
     const int64_t toks = static_cast<int64_t>(io->P) * io->C;
     const int64_t poss = toks * io->R;
-    const int64_t items = toks * ((io->R + kDotReads - 1) / kDotReads);   // (token, read group) waves
+    const int64_t items = toks * ((io->R + kDotReads - 1) / kDotReads);   // (token, read group) items
+    // Rows of up to 128 columns: 32-lane teams, two items (positions) per wave.
+    const bool half = io->hd <= 4 * 32;
+    const int64_t per_block = static_cast<int64_t>(kGdsWaves) * (half ? 2 : 1);
     void* kargs[] = {&a};
     hipError_t e = hipSuccess;
     if (io->d_q_w != nullptr) {
-        e = hipLaunchKernel(reinterpret_cast<const void*>(&gds_dots_kernel),
-                            dim3(static_cast<unsigned>((items + kGdsWaves - 1) / kGdsWaves)), dim3(kGdsThreads), kargs, 0, st);
+        e = hipLaunchKernel(half ? reinterpret_cast<const void*>(&gds_dots_kernel<32>)
+                                 : reinterpret_cast<const void*>(&gds_dots_kernel<kWave>),
+                            dim3(static_cast<unsigned>((items + per_block - 1) / per_block)), dim3(kGdsThreads), kargs, 0, st);
         if (e != hipSuccess) return e;
     }
     if (io->grad != nullptr) {
-        e = hipLaunchKernel(io->hd <= 4 * kWave ? reinterpret_cast<const void*>(&gds_scatter_kernel<true>)
-                                                : reinterpret_cast<const void*>(&gds_scatter_kernel<false>),
-                            dim3(static_cast<unsigned>((poss + kGdsWaves - 1) / kGdsWaves)), dim3(kGdsThreads), kargs, 0, st);
+        e = hipLaunchKernel(half ? reinterpret_cast<const void*>(&gds_scatter_kernel<true, 32>)
+                            : io->hd <= 4 * kWave ? reinterpret_cast<const void*>(&gds_scatter_kernel<true, kWave>)
+                                                  : reinterpret_cast<const void*>(&gds_scatter_kernel<false, kWave>),
+                            dim3(static_cast<unsigned>((poss + per_block - 1) / per_block)), dim3(kGdsThreads), kargs, 0, st);
     }
     return e;
 }
@@ -670,11 +681,14 @@ hipError_t gwr_launch(const sdm_gwr_io* io, int64_t ti, hipStream_t st) {
     a.grad_bf16 = io->grad_dtype == SDM_BF16;
     const int64_t toks = static_cast<int64_t>(io->P) * io->C;
     void* kargs[] = {&a};
-    const void* fn = io->hd <= 256 ? reinterpret_cast<const void*>(&gwr_kernel<1, 8>)
-                   : io->hd <= 512 ? reinterpret_cast<const void*>(&gwr_kernel<2, 4>)
-                                   : reinterpret_cast<const void*>(&gwr_kernel<4, 4>);
-    return hipLaunchKernel(fn,
-                           dim3(static_cast<unsigned>((toks + kGdsWaves - 1) / kGdsWaves)), dim3(kGdsThreads), kargs, 0, st);
+    // Rows of up to 128 columns: a 32-lane team per token, two per wave.
+    const bool half = io->hd <= 4 * 32;
+    const void* fn = half ? reinterpret_cast<const void*>(&gwr_kernel<1, 8, 32>)
+                   : io->hd <= 256 ? reinterpret_cast<const void*>(&gwr_kernel<1, 8, kWave>)
+                   : io->hd <= 512 ? reinterpret_cast<const void*>(&gwr_kernel<2, 4, kWave>)
+                                   : reinterpret_cast<const void*>(&gwr_kernel<4, 4, kWave>);
+    const int64_t per_block = static_cast<int64_t>(kGdsWaves) * (half ? 2 : 1);
+    return hipLaunchKernel(fn, dim3(static_cast<unsigned>((toks + per_block - 1) / per_block)), dim3(kGdsThreads), kargs, 0, st);
 }
 
 PaWorkspace pa_workspace_layout(const sdm_pa_io* io) {
