@@ -681,7 +681,7 @@ hipError_t gwr_launch(const sdm_gwr_io* io, int64_t ti, hipStream_t st) {
     a.grad_bf16 = io->grad_dtype == SDM_BF16;
     const int64_t toks = static_cast<int64_t>(io->P) * io->C;
     void* kargs[] = {&a};
-    // Rows of up to 128 columns: a 32-lane team per token, two per wave.
+    // Rows of up to 128 columns: a 32-lane team per token, two per wave (16-lane teams measured slower).
     const bool half = io->hd <= 4 * 32;
     const void* fn = half ? reinterpret_cast<const void*>(&gwr_kernel<1, 8, 32>)
                    : io->hd <= 256 ? reinterpret_cast<const void*>(&gwr_kernel<1, 8, kWave>)
@@ -738,13 +738,14 @@ hipError_t pa_launch(const sdm_pa_io* io, int64_t ti, hipStream_t st) {
     }
     const int64_t poss = static_cast<int64_t>(io->P) * io->C * io->W;
     void* kargs[] = {&a};
-    // Rows of up to 128 columns: a 32-lane team per K-row position, two per wave.
+    // Rows of up to 128 columns: a 16-lane team per K-row position (8 columns per lane), four per
+    // wave (faster than 32-lane teams where groups are short; long groups walk more record rounds).
     const bool half = io->hd <= 4 * 32;
-    const void* fn = half ? reinterpret_cast<const void*>(&pa_kernel<1, 32>)
+    const void* fn = half ? reinterpret_cast<const void*>(&pa_kernel<2, 16>)
                    : io->hd <= 256 ? reinterpret_cast<const void*>(&pa_kernel<1, kWave>)
                    : io->hd <= 512 ? reinterpret_cast<const void*>(&pa_kernel<2, kWave>)
                                    : reinterpret_cast<const void*>(&pa_kernel<4, kWave>);
-    const int64_t per_block = static_cast<int64_t>(kGdsWaves) * (half ? 2 : 1);
+    const int64_t per_block = static_cast<int64_t>(kGdsWaves) * (half ? 4 : 1);
     return hipLaunchKernel(fn, dim3(static_cast<unsigned>((poss + per_block - 1) / per_block)), dim3(kGdsThreads), kargs, 0, st);
 }
 
