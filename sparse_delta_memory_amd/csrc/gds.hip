@@ -38,18 +38,53 @@ struct GdsArgs {
     int P, C, R, hd, first_partial, valid_last, id64, vbf, bank_bf16, grad_bf16;
 };
 
-// Long groups (GDS read groups, PA write groups; with a workspace): members per segment, and the
-// last in-group distance that still marks a segment start (the distance field saturates at 4095).
+// Long groups (GDS read groups, PA write groups; with a workspace) are walked in segments of SEG =
+// 32 members (16-member segments measured slower on skewed slots: twice the partial rows for the
+// last segment to add). The last in-group distance that still marks a segment start: the distance
+// field saturates at 4095.
 constexpr int kSplitSeg = 32;
-constexpr int kSplitSegLimit = (4095 / kSplitSeg) * kSplitSeg;
+template <int SEG>
+constexpr int split_seg_limit() { return (4095 / SEG) * SEG; }
 // Workspace slots, by step-wide row position G (stream p's position j is p * (its row length) + j):
-// a split group has more than kSplitSeg members, so at most one split group's FIRST falls in each
-// aligned block of kSplitSeg positions (its counter and segment count), and at most two segment
-// starts (the first segment of a group starting there, a later one of the group running through):
-// two partial rows per block.
-__device__ __forceinline__ int64_t split_group_slot(int64_t g_first) { return g_first / kSplitSeg; }
+// a split group has more than SEG members, so at most one split group's FIRST falls in each
+// aligned block of SEG positions (its counter and segment count), and at most two segment starts
+// (the first segment of a group starting there, a later one of the group running through): two
+// partial rows per block.
+template <int SEG>
+__device__ __forceinline__ int64_t split_group_slot(int64_t g_first) { return g_first / SEG; }
+template <int SEG>
 __device__ __forceinline__ int64_t split_part_row(int64_t g_start, bool first_segment) {
-    return 2 * (g_start / kSplitSeg) + (first_segment ? 0 : 1);
+    return 2 * (g_start / SEG) + (first_segment ? 0 : 1);
+}
+
+// The combining team's sum of a split group's partial rows (columns col .. col + 3), in segment
+// order from +0: device-scope atomic loads (the partials come from other XCDs), four segments'
+// loads in flight together.
+template <int SEG>
+__device__ __forceinline__ float4 sum_partials(const float* part, int64_t g_first, int nseg, int hd, int col) {
+    float4 tot = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int sg0 = 0; sg0 < nseg; sg0 += 4) {
+        float4 pv[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int sg = min(sg0 + b, nseg - 1);   // (past the count: the last segment again, not added)
+            const float* pp = part + split_part_row<SEG>(g_first + static_cast<int64_t>(sg) * SEG, sg == 0) * hd + col;
+            pv[b].x = __hip_atomic_load(pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            pv[b].y = __hip_atomic_load(pp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            pv[b].z = __hip_atomic_load(pp + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            pv[b].w = __hip_atomic_load(pp + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if (sg0 + b < nseg) {
+                tot.x = tot.x + pv[b].x;
+                tot.y = tot.y + pv[b].y;
+                tot.z = tot.z + pv[b].z;
+                tot.w = tot.w + pv[b].w;
+            }
+        }
+    }
+    return tot;
 }
 
 constexpr int kGdsThreads = 256;
@@ -146,10 +181,13 @@ __global__ void __launch_bounds__(kGdsThreads) gds_dots_kernel(GdsArgs a) {
     }
 }
 
-// ONE: hd <= 4 TEAM, a single column block (no column loop); TEAM: lanes per Q-row position (32 for
-// rows of up to 128 columns: two positions per wave).
-template <bool ONE, int TEAM>
+// TEAM lanes per Q-row position (two or four positions per wave for narrow rows). ONE: each lane's
+// NCB 4-column blocks (cb * 4 TEAM + 4 lane) cover the row, else (NCB = 1) a column loop over the
+// row, the members walked again per block of 4 TEAM columns.
+template <bool ONE, int TEAM, int NCB>
 __global__ void __launch_bounds__(kGdsThreads) gds_scatter_kernel(GdsArgs a) {
+    constexpr int kRows = NCB == 1 ? kWalkRows : 4;   // member gradient rows in flight together
+    constexpr int SEG = kSplitSeg;   // members per segment of a split group
     const int wv = static_cast<int>(threadIdx.x) / kWave;
     const int lane = static_cast<int>(lane_id());
     const int tl = lane % TEAM;
@@ -161,13 +199,13 @@ __global__ void __launch_bounds__(kGdsThreads) gds_scatter_kernel(GdsArgs a) {
     const uint32_t* row = a.spay_q + c * n;
     const uint32_t e0 = row[j];
     if (e0 & kInvalid) return;
-    // Work starts at a valid group's FIRST and, when long groups are split, at every kSplitSeg-th
+    // Work starts at a valid group's FIRST and, when long groups are split, at every SEG-th
     // member (distance counts the group's valid entries before this one).
     const bool split = a.part != nullptr;
     const int dist = static_cast<int>((e0 >> kDistShift) & kDistMax);
     const bool first = (e0 & kFirst) != 0u;
-    if (!first && (!split || dist % kSplitSeg != 0 || dist > kSplitSegLimit)) return;
-    const bool unbounded = !split || dist == kSplitSegLimit;   // the last segment start runs to LAST
+    if (!first && (!split || dist % SEG != 0 || dist > split_seg_limit<SEG>())) return;
+    const bool unbounded = !split || dist == split_seg_limit<SEG>();   // the last segment start runs to LAST
     const int64_t qbase = c * n;   // entry-order Q index of (t, lane) is t * R + lane
     auto entry = [&](uint32_t el) { return static_cast<int64_t>((el >> kTokShift) & 0xFFu) * a.R + (el & 0xFFu); };
     const int64_t slot = gds_id(a, qbase + entry(e0));   // (every member, so every segment, reads it)
@@ -190,15 +228,15 @@ __global__ void __launch_bounds__(kGdsThreads) gds_scatter_kernel(GdsArgs a) {
     const int64_t prow = static_cast<int64_t>(p) * n;
     bool last_seen = false;
     for (int col0 = 0; col0 < (ONE ? 1 : a.hd); col0 += 4 * TEAM) {
-        const int col = col0 + 4 * tl;
-        const bool con = col < a.hd;
-        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        float4 acc[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[cb] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         bool done = false;
         int taken = 0;
-        // The members in sorted order, 64 records at a time (lane l: member m0 + l), their gradient
-        // rows kWalkRows at a time; the sum runs over the members in order from +0.
+        // The members in sorted order, TEAM records at a time (team lane l: member m0 + l), their
+        // gradient rows kRows at a time; the sum runs over the members in order from +0.
         for (int m0 = j; !done && m0 < n; m0 += TEAM) {
-            const int budget = unbounded ? TEAM : min(TEAM, kSplitSeg - taken);   // members still in the segment
+            const int budget = unbounded ? TEAM : min(TEAM, SEG - taken);   // members still in the segment
             const int m = m0 + tl;
             const uint32_t el = m < n ? row[m] : (kFirst | kLast | kInvalid);
             const int tk = static_cast<int>((el >> kTokShift) & 0xFFu);
@@ -208,37 +246,50 @@ __global__ void __launch_bounds__(kGdsThreads) gds_scatter_kernel(GdsArgs a) {
             const int cnt = lastm != 0ull ? __builtin_ctzll(lastm) + 1 : budget;   // (LAST included)
             last_seen = lastm != 0ull;
             taken += cnt;
-            done = last_seen || (!unbounded && taken == kSplitSeg);
-            for (int k0 = 0; k0 < cnt; k0 += kWalkRows) {
-                float wk[kWalkRows];
-                float4 g[kWalkRows];
+            done = last_seen || (!unbounded && taken == SEG);
+            for (int k0 = 0; k0 < cnt; k0 += kRows) {
+                float wk[kRows];
+                float4 g[kRows][NCB];
 #pragma unroll
-                for (int u = 0; u < kWalkRows; ++u) {
+                for (int u = 0; u < kRows; ++u) {
                     const int kk = min(k0 + u, cnt - 1);
                     wk[u] = __shfl(w, kk, TEAM);
                     const int t = __shfl(tk, kk, TEAM);
-                    g[u] = con ? load4(a.gr, 0, grow0 + t, a.hd, col) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        const int col = col0 + cb * 4 * TEAM + 4 * tl;
+                        // (rows past the group's end are not loaded: most groups have one member)
+                        g[u][cb] = (col < a.hd && k0 + u < cnt) ? load4(a.gr, 0, grow0 + t, a.hd, col)
+                                                                : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    }
                 }
 #pragma unroll
-                for (int u = 0; u < kWalkRows; ++u) {
+                for (int u = 0; u < kRows; ++u) {
                     if (k0 + u < cnt) {
-                        acc.x = fmaf(wk[u], g[u].x, acc.x);
-                        acc.y = fmaf(wk[u], g[u].y, acc.y);
-                        acc.z = fmaf(wk[u], g[u].z, acc.z);
-                        acc.w = fmaf(wk[u], g[u].w, acc.w);
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb) {
+                            acc[cb].x = fmaf(wk[u], g[u][cb].x, acc[cb].x);
+                            acc[cb].y = fmaf(wk[u], g[u][cb].y, acc[cb].y);
+                            acc[cb].z = fmaf(wk[u], g[u][cb].z, acc[cb].z);
+                            acc[cb].w = fmaf(wk[u], g[u][cb].w, acc[cb].w);
+                        }
                     }
                 }
             }
         }
-        if (!con) continue;
-        if (first && last_seen) {   // the whole group in one segment
-            add_row(col, acc);
-        } else {   // a segment of a split group: its partial row (device-scope stores, see below)
-            float* part = a.part + split_part_row(prow + j, dist == 0) * a.hd + col;
-            __hip_atomic_store(part, acc.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(part + 1, acc.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(part + 2, acc.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(part + 3, acc.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int col = col0 + cb * 4 * TEAM + 4 * tl;
+            if (col >= a.hd) continue;
+            if (first && last_seen) {   // the whole group in one segment
+                add_row(col, acc[cb]);
+            } else {   // a segment of a split group: its partial row (device-scope stores, see below)
+                float* part = a.part + split_part_row<SEG>(prow + j, dist == 0) * a.hd + col;
+                __hip_atomic_store(part, acc[cb].x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(part + 1, acc[cb].y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(part + 2, acc[cb].z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(part + 3, acc[cb].w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
     if (first && last_seen) return;
@@ -248,8 +299,8 @@ __global__ void __launch_bounds__(kGdsThreads) gds_scatter_kernel(GdsArgs a) {
     // their completion before it adds to the arrival counter (a device-scope atomic), and the
     // combining wave reads them with device-scope atomic loads after seeing the last arrival.
     const int first_pos = j - dist;
-    const int64_t gslot = split_group_slot(prow + first_pos);
-    const int seg = dist / kSplitSeg;
+    const int64_t gslot = split_group_slot<SEG>(prow + first_pos);
+    const int seg = dist / SEG;
     if (last_seen && tl == 0) __hip_atomic_store(a.meta + gslot, seg + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stores above have completed
     // The segment holding LAST adds 1 - (segments), every other adds 1: the counter returns to 0
@@ -261,19 +312,15 @@ __global__ void __launch_bounds__(kGdsThreads) gds_scatter_kernel(GdsArgs a) {
     if (after != 0) return;
     // (clamped to the segment starts the row holds, so no read can leave the workspace)
     const int nseg = min(max(__hip_atomic_load(a.meta + gslot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), 0),
-                         (n - first_pos + kSplitSeg - 1) / kSplitSeg);
+                         (n - first_pos + SEG - 1) / SEG);
     for (int col0 = 0; col0 < (ONE ? 1 : a.hd); col0 += 4 * TEAM) {
-        const int col = col0 + 4 * tl;
-        if (col >= a.hd) continue;
-        float4 tot = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        for (int sg = 0; sg < nseg; ++sg) {
-            const float* pp = a.part + split_part_row(prow + first_pos + static_cast<int64_t>(sg) * kSplitSeg, sg == 0) * a.hd + col;
-            tot.x = tot.x + __hip_atomic_load(pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            tot.y = tot.y + __hip_atomic_load(pp + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            tot.z = tot.z + __hip_atomic_load(pp + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            tot.w = tot.w + __hip_atomic_load(pp + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int col = col0 + cb * 4 * TEAM + 4 * tl;
+            if (col >= a.hd) continue;
+            const float4 tot = sum_partials<SEG>(a.part, prow + first_pos, nseg, a.hd, col);
+            add_row(col, tot);
         }
-        add_row(col, tot);
     }
 }
 
@@ -414,7 +461,7 @@ __device__ __forceinline__ void store4(void* base, int bf, int64_t row, int hd, 
     }
 }
 
-// One wave per K-row position that starts work: a group's FIRST or, with a workspace, every kSplitSeg-th
+// One wave per K-row position that starts work: a group's FIRST or, with a workspace, every SEG-th
 // member of a longer group. The wave walks its members in sorted order (64 records at a time,
 // kPaMembers token rows in flight): per member d_k_eff and g_decay, and acc = fma(sc, d_dva[tok], acc)
 // from +0. A group in one segment then writes grad = fma(gdw, cpe, acc) and restores the bank row;
@@ -422,6 +469,7 @@ __device__ __forceinline__ void store4(void* base, int bf, int64_t row, int hd, 
 // order and writes the rows (the same sums whichever segment arrives last).
 template <int NCB, int TEAM>
 __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
+    constexpr int SEG = kSplitSeg;   // members per segment of a split group
     const int wv = static_cast<int>(threadIdx.x) / kWave;
     const int lane = static_cast<int>(lane_id());
     const int tl = lane % TEAM;   // lane in the team (TEAM lanes per K-row position)
@@ -444,8 +492,8 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
     const bool split = a.part != nullptr;
     const int dist = static_cast<int>((r0.x >> kDistShift) & kDistMax);   // valid K entries before, in the group
     const bool first = (r0.x & kFirst) != 0u;
-    if (!first && (!split || dist % kSplitSeg != 0 || dist > kSplitSegLimit)) return;   // a member another wave walks
-    const bool unbounded = !split || dist == kSplitSegLimit;   // the last segment start runs to LAST
+    if (!first && (!split || dist % SEG != 0 || dist > split_seg_limit<SEG>())) return;   // a member another wave walks
+    const bool unbounded = !split || dist == split_seg_limit<SEG>();   // the last segment start runs to LAST
     const int first_pos = j - dist;                          // the group's FIRST (its snapshot row)
     const int64_t slot = static_cast<int64_t>(r0.y);
     const bool in = slot < a.rows;   // (a slot outside the bank: zero rows, nothing written)
@@ -467,7 +515,7 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
     bool done = false, last_seen = false;
     int taken = 0;
     for (int m0 = j; !done && m0 < a.CW; m0 += TEAM) {   // members TEAM records at a time, in sorted order
-        const int budget = unbounded ? TEAM : min(TEAM, kSplitSeg - taken);   // members this segment may still take
+        const int budget = unbounded ? TEAM : min(TEAM, SEG - taken);   // members this segment may still take
         const int m = m0 + tl;
         const uint32_t el = m < a.CW ? kr[m].x : (kFirst | kLast | kInvalid);
         const int tk = static_cast<int>((el >> kTokShift) & 0xFFu);
@@ -479,7 +527,7 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
         const int cnt = lastm != 0ull ? __builtin_ctzll(lastm) + 1 : budget;   // (LAST included)
         last_seen = lastm != 0ull;
         taken += cnt;
-        done = last_seen || (!unbounded && taken == kSplitSeg);
+        done = last_seen || (!unbounded && taken == SEG);
         for (int k0 = 0; k0 < cnt; k0 += kPaMembers) {
             float4 d[kPaMembers][NCB];
             float wk[kPaMembers], bk[kPaMembers];
@@ -537,8 +585,8 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
     // counter (a device-scope atomic); the combining wave reads them with device-scope atomic loads
     // after seeing the last arrival.
     const int64_t prow = static_cast<int64_t>(p) * a.CW;
-    const int64_t gslot = split_group_slot(prow + first_pos);
-    float* part = a.part + split_part_row(prow + j, dist == 0) * a.hd;
+    const int64_t gslot = split_group_slot<SEG>(prow + first_pos);
+    float* part = a.part + split_part_row<SEG>(prow + j, dist == 0) * a.hd;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         const int col = cb * 4 * TEAM + 4 * tl;
@@ -549,7 +597,7 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
             __hip_atomic_store(part + col + 3, acc[cb].w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    const int seg = dist / kSplitSeg;
+    const int seg = dist / SEG;
     // The segment holding LAST publishes the segment count.
     if (last_seen && tl == 0) __hip_atomic_store(a.meta + gslot, seg + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the stores above have completed
@@ -562,22 +610,12 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
     if (after != 0) return;
     // (clamped to the segment starts the row holds, so no read can leave the workspace)
     const int nseg = min(max(__hip_atomic_load(a.meta + gslot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), 0),
-                         (a.CW - first_pos + kSplitSeg - 1) / kSplitSeg);
+                         (a.CW - first_pos + SEG - 1) / SEG);
     float4 tot[NCB];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) tot[cb] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (int sg = 0; sg < nseg; ++sg) {
-        const float* pp = a.part + split_part_row(prow + first_pos + static_cast<int64_t>(sg) * kSplitSeg, sg == 0) * a.hd;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-            const int col = cb * 4 * TEAM + 4 * tl;
-            if (col < a.hd) {
-                tot[cb].x = tot[cb].x + __hip_atomic_load(pp + col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                tot[cb].y = tot[cb].y + __hip_atomic_load(pp + col + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                tot[cb].z = tot[cb].z + __hip_atomic_load(pp + col + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                tot[cb].w = tot[cb].w + __hip_atomic_load(pp + col + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int col = cb * 4 * TEAM + 4 * tl;
+        tot[cb] = col < a.hd ? sum_partials<SEG>(a.part, prow + first_pos, nseg, a.hd, col) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
     if (!in) return;
 #pragma unroll
@@ -652,10 +690,12 @@ hipError_t gds_launch(const sdm_gds_io* io, int64_t ti, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     if (io->grad != nullptr) {
-        e = hipLaunchKernel(half ? reinterpret_cast<const void*>(&gds_scatter_kernel<true, 32>)
-                            : io->hd <= 4 * kWave ? reinterpret_cast<const void*>(&gds_scatter_kernel<true, kWave>)
-                                                  : reinterpret_cast<const void*>(&gds_scatter_kernel<false, kWave>),
-                            dim3(static_cast<unsigned>((poss + per_block - 1) / per_block)), dim3(kGdsThreads), kargs, 0, st);
+        // (the scatter: 16-lane teams of 8 columns per lane, four positions per wave)
+        const int64_t per_block_s = static_cast<int64_t>(kGdsWaves) * (half ? 4 : 1);
+        e = hipLaunchKernel(half ? reinterpret_cast<const void*>(&gds_scatter_kernel<true, 16, 2>)
+                            : io->hd <= 4 * kWave ? reinterpret_cast<const void*>(&gds_scatter_kernel<true, kWave, 1>)
+                                                  : reinterpret_cast<const void*>(&gds_scatter_kernel<false, kWave, 1>),
+                            dim3(static_cast<unsigned>((poss + per_block_s - 1) / per_block_s)), dim3(kGdsThreads), kargs, 0, st);
     }
     return e;
 }
