@@ -542,7 +542,9 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) {
                     const int col = cb * 4 * TEAM + 4 * tl;
-                    d[u][cb] = col < a.hd ? load4(a.d_dva, 0, grow0 + t, a.hd, col) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    // (rows past the group's end are not loaded: most groups have one member)
+                    d[u][cb] = (col < a.hd && k0 + u < cnt) ? load4(a.d_dva, 0, grow0 + t, a.hd, col)
+                                                            : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                 }
             }
 #pragma unroll
