@@ -2,15 +2,18 @@
 // M0[q_idx[t, r]] for the chunks of one step (page "sparse_delta_memory/cuda/mover_da2_cuda.py": the GDS part of the module
 // docstring and the comment of its scatter role).
 //
-// gds_dots_kernel: d_q_w[t, r] = <gr[t], M0[q_idx[t, r]]>, token order, one wave per 4 reads of a
-// token (their ids one per lane, their rows in flight together); each lane takes 4 columns of every
-// 256 and a wave reduction gives each dot (no atomics).
-// gds_scatter_kernel: the gradient rows in sorted order, one wave per position of the Q-only rows:
-// at a valid group FIRST the wave walks the group's members in sorted order (64 records and
-// weights at a time, 8 gradient rows in flight), acc = fma(q_w, gr[t], acc) from +0, and at LAST
-// adds acc to grad[slot] with one read-modify-write (the wave is that row's only writer in the
+// Every kernel here works in teams of TEAM lanes (16, 32 or 64), one item per team: rows of up to
+// 128 columns leave most of a 64-lane wave idle, so narrow teams put several items' memory round
+// trips in flight per wave. A team sum is a butterfly of xor shuffles inside the team.
+//
+// gds_dots_kernel: d_q_w[t, r] = <gr[t], M0[q_idx[t, r]]>, token order, one team per 4 reads of a
+// token (their rows in flight together), a team sum per dot (no atomics).
+// gds_scatter_kernel: the gradient rows in sorted order, one team per position of the Q-only rows:
+// at a valid group FIRST the team walks the group's members in sorted order (TEAM records and
+// weights at a time, 4 or 8 gradient rows in flight), acc = fma(q_w, gr[t], acc) from +0, and at
+// LAST adds acc to grad[slot] with one read-modify-write (the team is that row's only writer in the
 // launch, so the result is deterministic). With a workspace, a group of more than 32 members is
-// walked in 32-member segments by separate waves; the last to finish adds their partial rows in
+// walked in 32-member segments by separate teams; the last to finish adds their partial rows in
 // segment order and makes the read-modify-write (the same sums whichever finishes last).
 
 #include <hip/hip_runtime.h>
@@ -110,7 +113,7 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// Sum over a team of TEAM lanes (the wave's 32-lane halves, or the whole wave).
+// Sum over a team of TEAM lanes (an aligned group of 16 or 32 lanes, or the whole wave).
 template <int TEAM>
 __device__ __forceinline__ float team_sum(float v) {
 #pragma unroll
@@ -211,7 +214,7 @@ __global__ void __launch_bounds__(kGdsThreads) gds_scatter_kernel(GdsArgs a) {
     const int64_t slot = gds_id(a, qbase + entry(e0));   // (every member, so every segment, reads it)
     if (slot < 0 || slot >= a.rows) return;
     const int64_t grow0 = a.row0 + static_cast<int64_t>(p) * a.C;
-    // One read-modify-write of 4 columns of the slot's row (this wave is the row's only writer).
+    // One read-modify-write of 4 columns of the slot's row (this team is the row's only writer).
     auto add_row = [&](int col, float4 v) {
         if (a.grad_bf16) {
             uint2* gp = reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.grad) + slot * a.hd + col);
@@ -326,9 +329,9 @@ __global__ void __launch_bounds__(kGdsThreads) gds_scatter_kernel(GdsArgs a) {
 
 // GWR (page "sparse_delta_memory/cuda/pa_dc_cuda.py", module docstring: the GWR gather of the
 // deterministic backward) for the tokens of one step: d_dv[t] = sum_n w[t, n] grad[k_idx[t, n]]
-// (entries in order, fma chain from +0) and d_k_pd[t, n] = <dv[t], grad[k_idx[t, n]]>. One wave
-// per token: each lane holds 4 columns of every 256 (hd <= 1024) of dv[t] and of the d_dv sum; the
-// token's ids and weights are loaded one per lane, then the gradient rows of 4 entries at a time.
+// (entries in order, fma chain from +0) and d_k_pd[t, n] = <dv[t], grad[k_idx[t, n]]>. One team
+// per token: each lane holds 4 columns of every 4 * TEAM (hd <= 1024) of dv[t] and of the d_dv sum;
+// the token's ids and weights are loaded one per lane, then its gradient rows a few at a time.
 struct GwrArgs {
     const void* grad;
     const void* k_idx;
@@ -340,8 +343,8 @@ struct GwrArgs {
     int P, C, W, hd, first_partial, valid_last, id64, grad_bf16;
 };
 
-// NCB: the 256-column blocks a lane's registers hold (1, 2 or 4: hd <= 256, 512, 1024), so that
-// narrow rows keep few registers and many waves per SIMD.
+// NCB: the blocks of 4 * TEAM columns a lane's registers hold (with 64-lane teams 1, 2 or 4: hd <=
+// 256, 512, 1024), so that narrow rows keep few registers and many waves per SIMD.
 template <int NCB, int GR, int TEAM>
 __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
     const int wv = static_cast<int>(threadIdx.x) / kWave;
@@ -427,7 +430,7 @@ __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
 
 // PA (page "sparse_delta_memory/cuda/pa_dc_cuda.py", module docstring: Phase A of the deterministic
 // backward, the backward of DW) for the chunks of one step. A padding entry writes its zeros; a valid
-// group's gradient row gdw and snapshot row (hd <= 1024: 4 columns of every 256 per lane) give
+// group's gradient row gdw and snapshot row (hd <= 1024: 4 columns of every 4 * TEAM per lane) give
 // <gdw, snap>; its members, in sorted order, give acc = fma(-beta k_eff, d_dva[t], acc) from +0,
 // d_k_eff[e] = -beta <d_dva[t], snap> and grad_g_decay[e] = cpe <gdw, snap>; then grad[s] =
 // fma(gdw, cpe, acc) and bank[s] = snap. A long group (more than 32 members, with a workspace) is
@@ -461,8 +464,8 @@ __device__ __forceinline__ void store4(void* base, int bf, int64_t row, int hd, 
     }
 }
 
-// One wave per K-row position that starts work: a group's FIRST or, with a workspace, every SEG-th
-// member of a longer group. The wave walks its members in sorted order (64 records at a time,
+// One team per K-row position that starts work: a group's FIRST or, with a workspace, every SEG-th
+// member of a longer group. The team walks its members in sorted order (TEAM records at a time,
 // kPaMembers token rows in flight): per member d_k_eff and g_decay, and acc = fma(sc, d_dva[tok], acc)
 // from +0. A group in one segment then writes grad = fma(gdw, cpe, acc) and restores the bank row;
 // a split group's segments publish their partial rows, and the last to arrive adds them in segment
