@@ -36,6 +36,7 @@ struct DwArgs {
     void* snap;        // compact snapshot (NULL: none): row snap_row0 + p * CW + j_FIRST <- the group's pre-write row
     int64_t snap_row0; // ti * snap_step_rows
     int P, C, CW, hd, ts_log2, teams_per_block;
+    int stream_bank;   // host side only: the launch takes the STREAM kernel (a bank far larger than the caches)
     const int32_t* snap_ord;   // dense snapshot layout (NULL: rows at FIRST positions): gord_k of the records
 };
 
@@ -47,10 +48,21 @@ struct RawCols {
     uint4 v[kVec];
 };
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// A 16-byte load marked non-temporal: the line is not kept in the caches for reuse. Rows of a large
+// bank are touched once per step (their one group's team reads and writes them) and rarely in the
+// next steps, so they stream past the token rows and records, which are reused.
+__device__ __forceinline__ uint4 load_stream16(const uint4* p) {
+    const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // TAIL (a head dim the 16-byte vectors do not divide, as in the mover pages' scalar variant): rows
 // are only element-aligned, so a lane moves its first nv (1..CPL) columns element by element, with
 // zeros in the rest of the raw vector; the values and roundings are those of the vector path.
-template <int CPL, bool BF16, bool TAIL>
+// STREAM: vector loads marked non-temporal (bank rows).
+template <int CPL, bool BF16, bool TAIL, bool STREAM = false>
 __device__ __forceinline__ RawCols<CPL, BF16> load_raw(const void* row, int col0, int nv) {
     RawCols<CPL, BF16> r;
     if constexpr (TAIL) {
@@ -73,7 +85,7 @@ __device__ __forceinline__ RawCols<CPL, BF16> load_raw(const void* row, int col0
     } else {
         const uint4* p = reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(row) + col0 * (BF16 ? 2 : 4));
 #pragma unroll
-        for (int v = 0; v < RawCols<CPL, BF16>::kVec; ++v) r.v[v] = p[v];
+        for (int v = 0; v < RawCols<CPL, BF16>::kVec; ++v) r.v[v] = STREAM ? load_stream16(p + v) : p[v];
     }
     return r;
 }
@@ -441,7 +453,8 @@ __device__ __forceinline__ void dw_walk(const DwArgs& a, int p, int j, uint4 r0,
 // together: their records, base rows and token rows are all in flight at once. Every other valid
 // position goes through the general walk, one after the other.
 // SNAP: also write the compact snapshot (the raw pre-write row of every valid group at its FIRST).
-template <int CPL, bool BANK_BF16, bool DV_BF16, int U, int SNAP, bool TAIL>
+// STREAM: one-member groups load their bank rows non-temporally.
+template <int CPL, bool BANK_BF16, bool DV_BF16, int U, int SNAP, bool TAIL, bool STREAM>
 __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
     static_assert(CPL % (BANK_BF16 ? 8 : 4) == 0 && CPL % (DV_BF16 ? 8 : 4) == 0, "16-byte column groups");
     constexpr int kBankEs = BANK_BF16 ? 2 : 4;
@@ -488,9 +501,8 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
         if (ones & (1u << u)) {
             const int pu = (J0 + u) / a.CW;
             const int64_t tok_row = static_cast<int64_t>(pu) * a.C + ((r[u].x >> kTokShift) & 0xFFu);
-            braw[u] = load_raw<CPL, BANK_BF16, TAIL>(static_cast<const unsigned char*>(a.bank) +
-                                                         static_cast<int64_t>(r[u].y) * a.hd * kBankEs,
-                                                     col0, nv);
+            const unsigned char* brow = static_cast<const unsigned char*>(a.bank) + static_cast<int64_t>(r[u].y) * a.hd * kBankEs;
+            braw[u] = load_raw<CPL, BANK_BF16, TAIL, STREAM>(brow, col0, nv);
             xraw[u] = load_raw<CPL, DV_BF16, TAIL>(
                 static_cast<const unsigned char*>(a.dv) + (a.dv_row0 + tok_row) * a.hd * kDvEs, col0, nv);
         }
@@ -535,12 +547,12 @@ __global__ void __launch_bounds__(kDwThreads) dw_kernel(DwArgs a) {
 // per team then outweigh the shorter grid), else 1.
 constexpr int64_t kDwWavesForPairs = 32 * 256;
 
-template <int CPL, bool BB, bool DB, int U, bool TAIL>
+template <int CPL, bool BB, bool DB, int U, bool TAIL, bool STREAM>
 hipError_t launch_dw_u(DwArgs a, bool snap_bf16, hipStream_t st, const hipEvent_t* ev) {
-    const void* fn = reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U, 0, TAIL>);
-    if (a.snap != nullptr) fn = reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U, 1, TAIL>);
+    const void* fn = reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U, 0, TAIL, STREAM>);
+    if (a.snap != nullptr) fn = reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U, 1, TAIL, STREAM>);
     if constexpr (!BB) {   // (a bf16 bank's rows are bf16 already: its bf16 snapshot is the raw one)
-        if (a.snap != nullptr && snap_bf16) fn = reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U, 2, TAIL>);
+        if (a.snap != nullptr && snap_bf16) fn = reinterpret_cast<const void*>(&dw_kernel<CPL, BB, DB, U, 2, TAIL, STREAM>);
     }
     const int64_t teams = (static_cast<int64_t>(a.P) * a.CW + U - 1) / U;
     const int64_t blocks = (teams + a.teams_per_block - 1) / a.teams_per_block;
@@ -550,10 +562,11 @@ hipError_t launch_dw_u(DwArgs a, bool snap_bf16, hipStream_t st, const hipEvent_
 
 template <int CPL, bool BB, bool DB>
 hipError_t launch_dw(const DwArgs& a, bool tail, bool sbf, hipStream_t st, const hipEvent_t* ev) {
-    if (tail) return launch_dw_u<CPL, BB, DB, 1, true>(a, sbf, st, ev);   // (element accesses: one position per team)
+    if (tail) return launch_dw_u<CPL, BB, DB, 1, true, false>(a, sbf, st, ev);   // (element accesses: one position per team)
     const int64_t waves = static_cast<int64_t>(a.P) * a.CW * (int64_t(1) << a.ts_log2) / kWave;
-    return waves >= kDwWavesForPairs ? launch_dw_u<CPL, BB, DB, 2, false>(a, sbf, st, ev)
-                                     : launch_dw_u<CPL, BB, DB, 1, false>(a, sbf, st, ev);
+    if (waves < kDwWavesForPairs) return launch_dw_u<CPL, BB, DB, 1, false, false>(a, sbf, st, ev);
+    return a.stream_bank ? launch_dw_u<CPL, BB, DB, 2, false, true>(a, sbf, st, ev)
+                         : launch_dw_u<CPL, BB, DB, 2, false, false>(a, sbf, st, ev);
 }
 
 template <int CPL>
@@ -611,6 +624,12 @@ hipError_t dw_launch_ws(const DwLaunch& Lc, hipStream_t st, int* cnt, int2* meta
     a.C = io->C;
     a.CW = io->C * io->W;
     a.hd = io->hd;
+    // Rows of a bank of a GiB or more (four times the last-level cache and more) are not kept in the
+    // caches: they are not touched again before they would be evicted. Smaller banks keep theirs
+    // (measured: non-temporal loads cost 2-3 % per step on a 0.13-0.25 GiB bank and gain 3-7 % on
+    // 7.5-16 GiB banks).
+    const int es = io->bank_dtype == SDM_BF16 ? 2 : 4;
+    a.stream_bank = static_cast<double>(io->rows) * io->hd * es >= double(1 << 30) ? 1 : 0;
     const int cpl = dw_cols_per_lane(io->hd);
     const int lanes = (io->hd + cpl - 1) / cpl;
     int ts = 1;

@@ -333,6 +333,7 @@ def test_int64_ids(idx, steps):
 
 
 @pytest.mark.parametrize("idx,steps,case", [(0, 2, None), (1, 2, None), (2, 1, None),
+                                            (3, 1, None),   # a 7.5 GiB bank: rows loaded non-temporally
                                             (None, 1, dict(C=255, W=33, R=2, S=5000, P=1, vl=None, hd=960)),
                                             (None, 2, dict(C=64, W=6, R=2, S=8, P=2, vl=50, hd=37)),   # tail
                                             (0, 2, "bf16"),                                           # bf16 rows
