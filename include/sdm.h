@@ -169,6 +169,10 @@ typedef struct sdm_p1_io {
                                -1 for padding. It is the row index of the dense compact snapshot (page
                                "sparse_delta_memory/cuda/mover_fx_cuda.py", module docstring: a group's row
                                at its dense ordinal in the chunk). Written by a small scan kernel on st. */
+    int32_t defer_pairs;    /* 0: the pair sums (a, qk) are computed by this call. 1: this call leaves
+                               them for sdm_phase1_pairs (the sort/scan kernel still writes their inputs
+                               into the workspace), so that a caller can run them on another stream
+                               beside work that needs only the other outputs (DW needs krec alone). */
 } sdm_p1_io;
 
 /*
@@ -200,6 +204,17 @@ size_t sdm_phase1_workspace(const sdm_p1_shape* shape);
  * midpoint), and so is the cpe in krec.
  */
 sdm_status sdm_phase1(const sdm_p1_shape* shape, const sdm_p1_io* io, hipStream_t st);
+
+/*
+ * The pair sums A and QK of a Phase-1 call made with defer_pairs = 1 (page
+ * "sparse_delta_memory/cuda/phase1_cuda.py": the pair kernels of its kernel plan, the same sums as
+ * an sdm_phase1 call that computes them). `shape` and `io` are those of that call (the same
+ * workspace, a and qk; at least one of a and qk set); st must be ordered after the call's stream
+ * (an event, or the same stream), and the workspace must not be given to another sdm_phase1 call
+ * until this call's kernel has run. Outputs and refusals as in sdm_phase1 (any non-zero status:
+ * nothing was launched).
+ */
+sdm_status sdm_phase1_pairs(const sdm_p1_shape* shape, const sdm_p1_io* io, hipStream_t st);
 
 /* One DW step: the chunks ti*P .. ti*P + P - 1 of the Phase-1 records. */
 typedef struct sdm_dw_io {

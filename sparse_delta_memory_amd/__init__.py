@@ -17,7 +17,7 @@ import ctypes
 from . import _lib
 from ._lib import P1IO, P1Shape, SdmError  # noqa: F401
 
-__all__ = ["P1Shape", "phase1", "phase1_workspace_bytes", "alloc_phase1_outputs", "dw_step", "dw_workspace_bytes",
+__all__ = ["P1Shape", "phase1", "phase1_pairs", "phase1_workspace_bytes", "alloc_phase1_outputs", "dw_step", "dw_workspace_bytes",
            "alloc_dw_workspace", "DwPlan", "ReadPlan", "read_step", "gds_step", "gds_workspace_bytes", "alloc_gds_workspace", "gwr_step", "pa_step", "pa_workspace_bytes",
            "alloc_pa_workspace", "SdmError", "make_shape",
            "timing_events"]
@@ -68,7 +68,7 @@ def alloc_phase1_outputs(shape: P1Shape, device="cuda", fields=None):
 
 
 def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=None, stream=None, events=None,
-           status=None):
+           status=None, defer_pairs=False):
     """Enqueue Phase 1 of shape.N chunks on the current (or given) stream; returns the outputs.
 
     Inputs are contiguous device tensors: k_idx [N,C,W] / q_idx [N,C,R] int32 (int64 with
@@ -76,7 +76,8 @@ def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=No
     float32 (bfloat16 with shape.val_bytes = 2) of the same shapes, g [N,C] float32 ([N,C,W] when shape.g_lane_stride = 1). `out` is a dict from alloc_phase1_outputs (a
     missing key skips that optional output). events: optional 4 torch.cuda.Events (timing_events)
     bound to the two kernels. status: optional zeroed int32 device tensor (debug): bit 0 is set
-    when a valid entry's slot id is out of range."""
+    when a valid entry's slot id is out of range. defer_pairs: leave A and QK to phase1_pairs (same
+    shape, out and workspace), which may then run on another stream."""
     import torch
 
     lib = _lib.load()
@@ -107,8 +108,29 @@ def phase1(shape: P1Shape, k_idx, q_idx, k_val, q_val, g, out=None, workspace=No
     if status is not None:
         io.status = status.data_ptr()
     io.gord_k = _ptr(out.get("gord_k"))
+    io.defer_pairs = 1 if defer_pairs else 0
     st = torch.cuda.current_stream(k_idx.device) if stream is None else stream
     _lib.check(lib.sdm_phase1(ctypes.byref(shape), ctypes.byref(io), ctypes.c_void_p(st.cuda_stream)))
+    return out
+
+
+def phase1_pairs(shape: P1Shape, out, workspace, stream=None, events=None):
+    """Enqueue the pair sums (out["a"], out["qk"]) of an earlier phase1(..., defer_pairs=True) call
+    with the same shape, out and workspace. `stream` must be ordered after that call's stream.
+    events: optional 4 timing events (the pair kernel takes the last two)."""
+    import torch
+
+    lib = _lib.load()
+    io = P1IO()
+    io.a = _ptr(out.get("a"))
+    io.qk = _ptr(out.get("qk"))
+    io.workspace = workspace.data_ptr()
+    io.workspace_bytes = workspace.numel() * workspace.element_size()
+    arr = _event_array(events, 4, "phase1_pairs")
+    io.events = None if arr is None else ctypes.cast(arr, ctypes.c_void_p).value
+    dev = workspace.device
+    st = torch.cuda.current_stream(dev) if stream is None else stream
+    _lib.check(lib.sdm_phase1_pairs(ctypes.byref(shape), ctypes.byref(io), ctypes.c_void_p(st.cuda_stream)))
     return out
 
 

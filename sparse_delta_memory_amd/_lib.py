@@ -43,7 +43,7 @@ class P1IO(ctypes.Structure):
     _fields_ = [(f, ctypes.c_void_p) for f in P1_IO_FIELDS] + [
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t), ("events", ctypes.c_void_p),
         ("status", ctypes.c_void_p),
-        ("gord_k", ctypes.c_void_p)]
+        ("gord_k", ctypes.c_void_p), ("defer_pairs", ctypes.c_int32)]
 
 
 class DwIO(ctypes.Structure):
@@ -106,7 +106,7 @@ class PaIO(ctypes.Structure):
     ]
 
 
-EXPORTS = ["sdm_phase1_workspace", "sdm_phase1", "sdm_dw_workspace", "sdm_dw_step", "sdm_dw_step_noalloc", "sdm_read_step",
+EXPORTS = ["sdm_phase1_workspace", "sdm_phase1", "sdm_phase1_pairs", "sdm_dw_workspace", "sdm_dw_step", "sdm_dw_step_noalloc", "sdm_read_step",
            "sdm_gds_workspace", "sdm_gds_step", "sdm_gwr_step", "sdm_pa_workspace", "sdm_pa_step", "sdm_status_string", "sdm_last_error"]
 
 _lock = threading.Lock()
@@ -132,6 +132,8 @@ def load() -> ctypes.CDLL:
         lib.sdm_phase1_workspace.restype = ctypes.c_size_t
         lib.sdm_phase1.argtypes = [ctypes.POINTER(P1Shape), ctypes.POINTER(P1IO), ctypes.c_void_p]
         lib.sdm_phase1.restype = ctypes.c_int
+        lib.sdm_phase1_pairs.argtypes = [ctypes.POINTER(P1Shape), ctypes.POINTER(P1IO), ctypes.c_void_p]
+        lib.sdm_phase1_pairs.restype = ctypes.c_int
         lib.sdm_dw_workspace.argtypes = [ctypes.POINTER(DwIO)]
         lib.sdm_dw_workspace.restype = ctypes.c_size_t
         lib.sdm_dw_step.argtypes = [ctypes.POINTER(DwIO), ctypes.c_int64, ctypes.c_void_p]

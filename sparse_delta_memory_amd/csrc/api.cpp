@@ -223,6 +223,10 @@ sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st
         return fail(SDM_EWORKSPACE, "sdm_phase1: workspace needs %zu bytes, got %zu", ws.total,
                     io->workspace == nullptr ? size_t(0) : io->workspace_bytes);
     if (!aligned(io->workspace, 16)) return fail(SDM_EALIGN, "sdm_phase1: workspace is not 16-byte aligned");
+    if (io->defer_pairs != 0 && io->defer_pairs != 1)
+        return fail(SDM_EINVAL, "sdm_phase1: defer_pairs = %d (0 or 1)", io->defer_pairs);
+    if (io->defer_pairs == 1 && io->a == nullptr && io->qk == nullptr)
+        return fail(SDM_EINVAL, "sdm_phase1: defer_pairs = 1 without a or qk");
     const size_t main_lds = sdm::p1_lds_bytes(s, io);
     if (main_lds == SIZE_MAX)
         return fail(SDM_EUNSUPPORTED, "sdm_phase1: the sort/scan kernel's plan does not fit the LDS budget of %d B",
@@ -252,6 +256,44 @@ sdm_status sdm_phase1(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st
     if (e != hipSuccess) {
         (void)hipGetLastError();   // the launch's error is reported through the status, not left pending
         return fail(SDM_EHIP, "sdm_phase1: %s: %s", sdm::g_p1_stage, hipGetErrorString(e));
+    }
+    return SDM_OK;
+}
+
+sdm_status sdm_phase1_pairs(const sdm_p1_shape* s, const sdm_p1_io* io, hipStream_t st) {
+    g_last_error.clear();
+    sdm_status rc = check_p1_shape(s);
+    if (rc != SDM_OK) return rc;
+    if (io == nullptr) return fail(SDM_EINVAL, "sdm_phase1_pairs: io is NULL");
+    if (io->a == nullptr && io->qk == nullptr) return fail(SDM_EINVAL, "sdm_phase1_pairs: neither a nor qk is set");
+    if (!aligned(io->a, 4) || !aligned(io->qk, 4)) return fail(SDM_EALIGN, "sdm_phase1_pairs: a or qk is misaligned");
+    if (s->N == 0) return SDM_OK;
+    const sdm::P1Workspace ws = sdm::p1_workspace_layout(s);
+    if (io->workspace == nullptr || io->workspace_bytes < ws.total)
+        return fail(SDM_EWORKSPACE, "sdm_phase1_pairs: workspace needs %zu bytes, got %zu", ws.total,
+                    io->workspace == nullptr ? size_t(0) : io->workspace_bytes);
+    if (!aligned(io->workspace, 16)) return fail(SDM_EALIGN, "sdm_phase1_pairs: workspace is not 16-byte aligned");
+    int lds_max = 0;
+    const hipError_t se = device_setup(&lds_max);
+    if (se != hipSuccess) return fail(SDM_EHIP, "sdm_phase1_pairs: device set-up: %s", hipGetErrorString(se));
+    const size_t tri = sdm::p1_pair_lds_min(s);
+    if (tri > static_cast<size_t>(lds_max))
+        return fail(SDM_EUNSUPPORTED, "sdm_phase1_pairs: the C=%d pair kernel (%zu B) exceeds the %d B of LDS per block",
+                    s->C, tri, lds_max);
+    sdm::P1Launch L;
+    L.s = s;
+    L.io = io;
+    L.rec = static_cast<char*>(io->workspace) + ws.rec_off;
+    L.inv_k = static_cast<char*>(io->workspace) + ws.inv_k_off;
+    L.inv_q = static_cast<char*>(io->workspace) + ws.inv_q_off;
+    L.hot = static_cast<char*>(io->workspace) + ws.hot_off;
+    L.sort = nullptr;
+    L.rev = nullptr;
+    L.lds_max = lds_max;
+    const hipError_t e = sdm::p1_pairs_launch(L, st);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(SDM_EHIP, "sdm_phase1_pairs: pair kernel: %s", hipGetErrorString(e));
     }
     return SDM_OK;
 }

@@ -1637,8 +1637,15 @@ hipError_t p1_launch(const P1Launch& Lc, hipStream_t st) {
         default: e = launch_main<16>(a, s->g_lane_stride != 0, s->idx_bytes == 8, vbf, m.lds_bytes, s->N, st, ev[0], ev[1]); break;
     }
     if (e == hipSuccess) e = p1_ordinal_launch(s, io, st);
-    if (e != hipSuccess || !pairs) return e;
+    if (e != hipSuccess || !pairs || io->defer_pairs) return e;
     return pair_launch(Lc, pp, false, st);
+}
+
+hipError_t p1_pairs_launch(const P1Launch& Lc, hipStream_t st) {
+    // The plan the sort/scan (or tiled) kernel of the same shape followed (it is a function of the
+    // shape and the device alone), so the hot-group lists it left are read as it wrote them.
+    const PairPlan pp = pair_plan(Lc.s, true, Lc.lds_max);
+    return pair_launch(Lc, pp, p1_tiled(Lc.s), st);
 }
 
 int p1_lds_kernels(const void** fns, int cap) {

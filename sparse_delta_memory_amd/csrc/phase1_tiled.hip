@@ -524,7 +524,7 @@ hipError_t p1_tiled_launch(const P1Launch& Lc, hipStream_t st) {
     hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(&p1_tiled_kernel), dim3(s->N), dim3(kNT), kargs, lds, st,
                                       e0, e1, 0);
     if (e == hipSuccess) e = p1_ordinal_launch(s, io, st);
-    if (e != hipSuccess || !pairs) return e;
+    if (e != hipSuccess || !pairs || io->defer_pairs) return e;
     return pair_launch(Lc, pp, true, st);
 }
 

@@ -76,8 +76,11 @@ size_t p1_lds_bytes(const sdm_p1_shape* s, const sdm_p1_io* io);
 // LDS bytes the pair kernel needs without hot-group tables (the triangle and the hot list).
 size_t p1_pair_lds_min(const sdm_p1_shape* s);
 
-// Enqueue the Phase-1 kernels; returns hipSuccess or the first launch error.
+// Enqueue the Phase-1 kernels; returns hipSuccess or the first launch error. With io->defer_pairs the
+// pair kernel is left out (its inputs are still written) for p1_pairs_launch.
 hipError_t p1_launch(const P1Launch& L, hipStream_t st);
+// The pair kernel alone, from the workspace of an earlier p1_launch of the same shape and io.
+hipError_t p1_pairs_launch(const P1Launch& L, hipStream_t st);
 
 struct DwLaunch {
     const sdm_dw_io* io;

@@ -340,3 +340,28 @@ def test_phase1_lds_budget_too_small_is_refused_before_any_device_call():
     need = _lib.load().sdm_phase1_workspace(ctypes.byref(s))
     assert call_p1(s, io(workspace_bytes=need)) == _lib.SDM_EUNSUPPORTED
     assert b"budget" in _lib.load().sdm_last_error()
+
+
+def call_pairs(s, o):
+    lib = _lib.load()
+    return lib.sdm_phase1_pairs(ctypes.byref(s) if s is not None else None, ctypes.byref(o) if o is not None else None,
+                                None)
+
+
+def test_deferred_pair_refusals():
+    """defer_pairs is 0 or 1 and defers something (a or qk set); sdm_phase1_pairs refuses a bad
+    shape, a missing io, no pair output, misaligned outputs and a short workspace, all on the host."""
+    s = shape()
+    assert call_p1(s, io(defer_pairs=2)) == _lib.SDM_EINVAL
+    assert call_p1(s, io(defer_pairs=-1)) == _lib.SDM_EINVAL
+    assert call_p1(s, io(defer_pairs=1, a=None, qk=None)) == _lib.SDM_EINVAL
+    assert call_pairs(None, io()) == _lib.SDM_EINVAL
+    assert call_pairs(shape(C=0), io()) == _lib.SDM_ESHAPE
+    assert call_pairs(s, None) == _lib.SDM_EINVAL
+    assert call_pairs(s, io(a=None, qk=None)) == _lib.SDM_EINVAL
+    assert call_pairs(s, io(a=FAKE + 2)) == _lib.SDM_EALIGN
+    need = _lib.load().sdm_phase1_workspace(ctypes.byref(s))
+    assert call_pairs(s, io(workspace_bytes=need - 1)) == _lib.SDM_EWORKSPACE
+    assert call_pairs(s, io(workspace=None)) == _lib.SDM_EWORKSPACE
+    assert call_pairs(s, io(workspace=FAKE + 8)) == _lib.SDM_EALIGN
+    assert call_pairs(shape(N=0, first_partial=0), io()) == _lib.SDM_OK   # nothing to launch

@@ -5,6 +5,9 @@ and so more passes, values and ids read from global memory instead of staged in 
 sweeps of token ranges); every output must be the default run's bit for bit, the pair sums included
 (the pair kernel does not see the budget).
 
+defer_pairs: the sort/scan call leaves the pair sums to a second call (sdm_phase1_pairs) that runs
+on another stream; every output must be the one-call run's bit for bit.
+
 pair_walk: every slot group walked by the pair kernel instead of the dense contraction of hot groups
 (the phase1_cuda page's hot/cold note: the two forms agree within the evaluation bound, not bit for
 bit). A and QK of the walked form meet the strict max(1e-5|o|, 1e-6) bound against the oracle, as
@@ -101,3 +104,35 @@ def test_pair_walk_matches_the_oracle_and_the_dense_form(case):
         w = walk[f].index_select(0, idx).cpu().numpy().astype(np.float64)
         tol = 2 * np.maximum(1e-5 * np.abs(o), 1e-6)
         assert np.all(np.abs(d - w) <= tol), f
+
+
+@pytest.mark.parametrize("case", [
+    dict(idx=1, steps=2),                      # uniform rows on chip
+    dict(idx=2, steps=1),                      # Zipf: hot-group lists written by the first call
+    dict(idx=4, steps=1, knobs=dict(pair_walk=1)),
+    dict(edge=(64, 6, 3, 40, 2, 2, 50), knobs=dict(tiled=1)),   # the tiled path (32-bit entry words)
+])
+def test_deferred_pairs_give_the_same_bits(case):
+    wl = W.make(case["idx"], steps=case["steps"]) if "idx" in case else edge(*case["edge"])
+    knobs = case.get("knobs", {})
+    say("deferred pairs", case)
+    ref = run(wl, **knobs)
+    shape = H.shape_of(wl)
+    for k, v in knobs.items():
+        setattr(shape, k, int(v))
+    ins = H.device_inputs(wl)
+    every = set(sdm.alloc_phase1_outputs(sdm.make_shape(0, 1, 1, 1), device="cpu"))
+    out = sdm.alloc_phase1_outputs(shape, device="cuda", fields=every | {"perm", "gord_k"})
+    for f in ("a", "qk"):
+        out[f].fill_(float("nan"))
+    ws = torch.empty(sdm.phase1_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    done = torch.cuda.Event()
+    sdm.phase1(shape, out=out, workspace=ws, defer_pairs=True, **ins)
+    done.record(main)
+    side.wait_event(done)
+    sdm.phase1_pairs(shape, out, ws, stream=side)
+    torch.cuda.synchronize()
+    for k in ref:
+        same_bits(k, out[k], ref[k])
