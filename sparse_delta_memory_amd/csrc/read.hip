@@ -12,13 +12,14 @@
 // Two kernels per step. read_gather_kernel: a team of 16 lanes per token, 8 columns per lane (16-byte
 // bf16 or two 16-byte float32 loads per row), entries taken 8 at a time with every row load in flight
 // before the first is used; p0 and q0 go to the pred and read outputs. read_solve_kernel: one block
-// per (chunk, 64 columns), one wave per 16 columns. It first inverts every 16 x 16 diagonal block of
+// of four waves per (chunk, 16 columns). It first inverts every 16 x 16 diagonal block of
 // I + diag(beta) A (one column of one block per lane, by substitution); then it takes the tokens in
-// blocks of 16: the block's A and QK rows (loaded one block ahead by all lanes) are staged in LDS,
-// and each wave forms with 16 x 16 x 4 float32 matrix (MFMA) steps the earlier blocks' terms
-// A[block, :b0] dv, the block's dv as its inverse times the scaled right-hand sides, the block's own
-// A terms for pred, and QK[block, :b0+16] dv for read; dv of every token stays in the wave's LDS.
-// Sums run in a fixed order: results are reproducible.
+// blocks of 16, the block's A rows staged in LDS (loaded one block ahead): the earlier blocks'
+// terms A[block, :b0] dv are formed with 16 x 16 x 4 float32 matrix (MFMA) steps, shared out among
+// the four waves, and wave 0 adds the four shares, forms the block's dv as its inverse times the
+// scaled right-hand sides and the block's own A terms for pred. Only that chain is sequential: the
+// reads QK[block, :b0+16] dv follow for every block at once, once all of dv is in LDS. Sums run in
+// a fixed order: results are reproducible.
 #include <hip/hip_ext.h>
 
 #include "sdm_device.hpp"
@@ -181,8 +182,9 @@ __global__ void __launch_bounds__(256) read_gather_kernel(ReadArgs a) {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMW = 4;                // waves per substitution block, 16 columns each
-constexpr int kMCols = kMW * kSB;     // columns per substitution block
+constexpr int kMW = 4;    // waves per substitution block, all on the block's 16 columns
+constexpr int kTLd = 20;  // row stride (floats) of the inverse, dv and partial tiles in LDS: the four
+                          // lane groups of a wave (rows 4 apart) then read 64 distinct banks
 
 // One 16 x 16 x 4 float32 matrix step: lane l gives A[l % 16][k] and B[k][l % 16] for the k its
 // lane group (l / 16) stands for; D row 4 (l / 16) + r, column l % 16 is register r of lane l.
@@ -190,52 +192,58 @@ __device__ __forceinline__ floatx4 mfma4(float av, float bv, floatx4 acc) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
 }
 
-// Row stride of the staged panels: every column a token block reaches (C rounded up to 16) plus 4,
-// so that rows are 16-byte aligned and start 4 or 20 banks apart.
+// Row stride of the staged A panels: every column a token block reaches (C rounded up to 16) plus
+// 4, so that rows are 16-byte aligned and start 4 banks apart.
 __host__ __device__ inline int panel_ld(int C) { return (C + kSB - 1) / kSB * kSB + 4; }
 
-// Dynamic LDS of the substitution kernel (floats): the inverses of the diagonal blocks (rows x 16),
-// per wave dv of every token for its 16 columns (rows x 16 each), and the current token block's A
-// and QK rows (16 x panel_ld each); rows = C rounded up to 16.
+constexpr int kPanels = 3;   // A panels in LDS: block b is read while block b + 1 is written
+
+// Dynamic LDS of the substitution kernel (floats): the inverses of the diagonal blocks and dv of
+// every token for the block's 16 columns (rows x kTLd each, rows = C rounded up to 16), a ring of
+// kPanels A panels (a token block's rows, 16 x panel_ld), and one 16 x 16 partial tile per wave.
 size_t solve_lds_bytes(int C) {
     const size_t rows = static_cast<size_t>((C + kSB - 1) / kSB) * kSB;
-    return sizeof(float) * (rows * kSB * (1 + kMW) + 2 * static_cast<size_t>(kSB) * panel_ld(C));
+    return sizeof(float) * (2 * rows * kTLd + kPanels * static_cast<size_t>(kSB) * panel_ld(C) + kMW * kSB * kTLd);
 }
 
-// panel[0..16) x [0, K) times dv rows [0, K) of the wave's 16 columns, added to acc: lane (group g,
-// lane m) takes k = g * K/4 + s, s < K/4 (a contiguous run of its panel row), K a multiple of 16.
-__device__ __forceinline__ floatx4 panel_times_dv(const float* panel, int ld, int K, const float* wdv, int g, int m,
+// The terms of earlier token block j: panel columns [16 j, 16 j + 16) times dv rows of block j, added
+// to acc (lane group g takes k = 16 j + 4 g + s).
+__device__ __forceinline__ floatx4 block_times_dv(const float* panel, int ld, int j, const float* sdv, int g, int m,
                                                   floatx4 acc) {
-    const int kq = K / 4;
-    const float* prow = panel + m * ld + g * kq;
-    const float* dcol = wdv + g * kq * kSB + m;
-    for (int s0 = 0; s0 < kq; s0 += 4) {
-        const floatx4 av = *reinterpret_cast<const floatx4*>(prow + s0);   // 16-byte aligned: ld, kq, s0 multiples of 4
+    const floatx4 av = *reinterpret_cast<const floatx4*>(panel + m * ld + j * kSB + 4 * g);   // 16-byte aligned
+    const float* dcol = sdv + (j * kSB + 4 * g) * kTLd + m;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma4(av[s], dcol[(s0 + s) * kSB], acc);
-    }
+    for (int s = 0; s < 4; ++s) acc = mfma4(av[s], dcol[s * kTLd], acc);
     return acc;
 }
 
+// Block (chunk p, 16 columns), four waves. The substitution runs over the token blocks in order; per
+// block the earlier blocks' terms A[block, :b0] dv are shared out among the waves (wave w takes the
+// earlier blocks j = w mod 4, in order) and summed in wave order by wave 0, which then solves the
+// block with its inverted diagonal block and writes dv and pred. A rows and token inputs are
+// loaded two blocks ahead (one block's substitution is shorter than a load's round trip). The
+// reads, which nothing in the substitution needs, follow for all token blocks at once (wave w
+// takes blocks w mod 4): QK rows straight from global memory (VEC: C a multiple of 4, 16-byte
+// loads), all of a block's in flight together, times the dv tile in LDS.
+template <bool VEC>
 __global__ void __launch_bounds__(256) read_solve_kernel(ReadArgs a) {
     extern __shared__ float lds[];
     const int C = a.C;
     const int nblk = (C + kSB - 1) / kSB;
     const int rows = nblk * kSB;
     const int ld = panel_ld(C);
-    float* sT = lds;                                    // [rows][16]: row t holds row (t mod 16) of its block's inverse
-    float* sdv = sT + rows * kSB;                       // [kMW][rows][16]
-    float* sA = sdv + kMW * rows * kSB;                 // [16][ld]: the current token block's A rows
-    float* sQ = sA + kSB * ld;                          // [16][ld]: its QK rows
+    float* sT = lds;                       // [rows][kTLd]: row t holds row (t mod 16) of its block's inverse
+    float* sdv = sT + rows * kTLd;         // [rows][kTLd]: dv of every token, the block's 16 columns
+    float* sA = sdv + rows * kTLd;         // kPanels x [16][ld]: token block b's A rows in panel b mod kPanels
+    float* spart = sA + kPanels * kSB * ld;   // [kMW][16][kTLd]: per wave, its share of the earlier blocks' terms
     const int tid = static_cast<int>(threadIdx.x);
     const int wv = tid / kWave, l = tid % kWave;
-    const int g = l / kSB, m = l % kSB;                 // lane group (k / D row quarter), lane in group
-    float* wdv = sdv + wv * rows * kSB;                 // this wave's dv [rows][16]
-    const int sr = tid / kSB, sl = tid % kSB;           // staging / inverse lanes: row (block) sr, lane sl
+    const int g = l / kSB, m = l % kSB;    // lane group (k / D row quarter), lane in group
+    const int sr = tid / kSB, sl = tid % kSB;   // staging / inverse lanes: row (block) sr, lane sl
     // Block b is (chunk b mod P, column group b / P): consecutive blocks go round the XCDs, so a
     // chunk's column groups share an XCD's L2 when P is a multiple of 8.
     const int p = static_cast<int>(blockIdx.x) % a.P;
-    const int col = (static_cast<int>(blockIdx.x) / a.P) * kMCols + wv * kSB + m;   // this lane's column
+    const int col = (static_cast<int>(blockIdx.x) / a.P) * kSB + m;   // this lane's column
     const bool col_ok = col < a.hd;
     const int64_t c = a.chunk0 + p;
     const int tv = c >= a.first_partial ? a.valid_last : C;
@@ -243,6 +251,43 @@ __global__ void __launch_bounds__(256) read_solve_kernel(ReadArgs a) {
     const float* QK = a.qk + c * C * C;
     const float* beta = a.beta + c * C;
     const int64_t rbase = a.row0 + static_cast<int64_t>(p) * C;
+
+    // Panel rows of token block b (row sr, columns sl + 16u up to the block's diagonal; zero past
+    // C or past the last block) and, for wave 0, its lanes' token inputs (D rows b0 + 4g + r).
+    struct Ahead {
+        float a[kSB];
+        float p0[4], v[4], bt[4];
+    };
+    auto fetch = [&](int b, Ahead& f) {
+        const int b0 = b * kSB;
+        const int tr = b0 + sr;
+#pragma unroll
+        for (int u = 0; u < kSB; ++u) {
+            const int j = sl + kSB * u;
+            f.a[u] = (b < nblk && tr < C && u <= b && j < C) ? A[static_cast<int64_t>(tr) * C + j] : 0.0f;
+        }
+        if (wv == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = b0 + 4 * g + r;
+                const bool ok = b < nblk && t < tv && col_ok;
+                const int64_t o = (rbase + (ok ? t : 0)) * a.hd + (col_ok ? col : 0);
+                f.p0[r] = ok ? a.pred[o] : 0.0f;
+                f.v[r] = ok ? a.v[o] : 0.0f;
+                f.bt[r] = ok ? beta[t] : 0.0f;
+            }
+        }
+    };
+    auto stage = [&](int b, const Ahead& f) {   // block b's panel into its ring slot
+        float* pan = sA + (b % kPanels) * kSB * ld;
+#pragma unroll
+        for (int u = 0; u < kSB; ++u) {
+            if (u <= b) pan[sr * ld + sl + kSB * u] = f.a[u];   // columns up to the block's diagonal
+        }
+    };
+    Ahead f0, f1, f2;   // blocks b, b + 1, b + 2
+    fetch(0, f0);
+    fetch(1, f1);
 
     // Inverse of every diagonal block T_b = I + diag(beta_b) A_bb (unit lower triangular): lane
     // (block sr, column sl) solves T_b x = e_sl by substitution; masked tokens have beta taken as 0.
@@ -264,91 +309,122 @@ __global__ void __launch_bounds__(256) read_solve_kernel(ReadArgs a) {
 #pragma unroll
             for (int k = 0; k < i; ++k) sacc = fmaf(al[i][k], x[k], sacc);
             x[i] = (i == sl ? 1.0f : 0.0f) - bt[i] * sacc;
-            sT[(t0 + i) * kSB + sl] = t0 + i < C ? x[i] : 0.0f;
+            sT[(t0 + i) * kTLd + sl] = t0 + i < C ? x[i] : 0.0f;
         }
     }
+    stage(0, f0);
 
-    // Panel rows of token block b (row sr, columns sl + 16u up to the block's diagonal; zero past C)
-    // and this lane's token inputs (D rows b0 + 4g + r), loaded one block ahead.
-    float stA[kSB], stQ[kSB];
-    float nx_p0[4], nx_v[4], nx_q0[4], nx_b[4];
-    auto prefetch = [&](int b) {
+    // One token block of the substitution: cur holds block b's token inputs, nxt block b + 1's
+    // panel (loaded a block ago) and nxt2 receives block b + 2's loads. The three register sets
+    // rotate by unrolling (a copy between them would wait for the loads in flight).
+    auto solve_block = [&](int b, const Ahead& cur, const Ahead& nxt, Ahead& nxt2) {
         const int b0 = b * kSB;
-        const int tr = b0 + sr;
+        const float* pan = sA + (b % kPanels) * kSB * ld;
+        // Block b + 1's panel goes into its slot now, and block b + 2's loads are issued. Block
+        // b + 1's slot last held block b - 2, read before the barriers of block b - 1.
+        if (b + 1 < nblk) stage(b + 1, nxt);
+        fetch(b + 2, nxt2);
+        lds_barrier();   // panel b and every earlier block's dv are in LDS
+        // This wave's share of A[block, :b0] dv.
+        floatx4 part = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = wv; j < b; j += kMW) part = block_times_dv(pan, ld, j, sdv, g, m, part);
 #pragma unroll
-        for (int u = 0; u < kSB; ++u) {
-            const int j = sl + kSB * u;
-            const bool in = tr < C && u <= b && j < C;
-            stA[u] = in ? A[static_cast<int64_t>(tr) * C + j] : 0.0f;
-            stQ[u] = in ? QK[static_cast<int64_t>(tr) * C + j] : 0.0f;
-        }
+        for (int r = 0; r < 4; ++r) spart[(wv * kSB + 4 * g + r) * kTLd + m] = part[r];
+        lds_barrier();   // the partial tiles are in LDS
+        if (wv == 0) {
+            float far[4], rhs[4];
+            bool ok[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = b0 + 4 * g + r;
-            const bool ok = t < tv && col_ok;
-            const int64_t o = (rbase + (ok ? t : 0)) * a.hd + (col_ok ? col : 0);
-            nx_p0[r] = ok ? a.pred[o] : 0.0f;
-            nx_v[r] = ok ? a.v[o] : 0.0f;
-            nx_q0[r] = ok ? a.read[o] : 0.0f;
-            nx_b[r] = ok ? beta[t] : 0.0f;
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * g + r;
+                far[r] = ((spart[row * kTLd + m] + spart[(kSB + row) * kTLd + m]) + spart[(2 * kSB + row) * kTLd + m]) +
+                         spart[(3 * kSB + row) * kTLd + m];
+                ok[r] = b0 + row < tv && col_ok;
+                rhs[r] = ok[r] ? cur.bt[r] * ((cur.v[r] - cur.p0[r]) - far[r]) : 0.0f;
+            }
+            // dv = (block inverse) x (right-hand sides): the B operand of step s is the lane's own
+            // register s (k = 4 g + s).
+            floatx4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) x = mfma4(sT[(b0 + m) * kTLd + 4 * g + s], rhs[s], x);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                x[r] = ok[r] ? x[r] : 0.0f;
+                sdv[(b0 + 4 * g + r) * kTLd + m] = x[r];
+            }
+            // pred: the block's own A terms (B operand again the lane's registers).
+            floatx4 near = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) near = mfma4(pan[m * ld + b0 + 4 * g + s], x[s], near);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = b0 + 4 * g + r;
+                if (t < C && col_ok) {
+                    const int64_t o = (rbase + t) * a.hd + col;
+                    a.dv[o] = x[r];
+                    a.pred[o] = ok[r] ? (cur.p0[r] + far[r]) + near[r] : 0.0f;
+                }
+            }
         }
     };
-    prefetch(0);
-    for (int b = 0; b < nblk; ++b) {
+    for (int b = 0; b < nblk; b += 3) {
+        solve_block(b, f0, f1, f2);
+        if (b + 1 < nblk) solve_block(b + 1, f1, f2, f0);
+        if (b + 2 < nblk) solve_block(b + 2, f2, f0, f1);
+    }
+    lds_barrier();   // dv of every token is in LDS
+    // read = q0 + QK[block, :b0+16] dv, token blocks w mod 4, two blocks' QK rows and q0 in flight
+    // together; each block's terms in order of the earlier blocks.
+    struct QRows {
+        float q[kSB][4];
+        float q0[4];
+    };
+    auto load_q = [&](int b, QRows& f) {   // (b >= nblk: zeros, nothing loaded)
         const int b0 = b * kSB;
+        const int tr = b0 + m;   // the QK row this lane gives
+        const float* qrow = QK + static_cast<int64_t>(tr < C ? tr : 0) * C;
 #pragma unroll
-        for (int u = 0; u < kSB; ++u) {
-            if (u <= b) {   // columns up to the block's diagonal (those past C hold zeros)
-                sA[sr * ld + sl + kSB * u] = stA[u];
-                sQ[sr * ld + sl + kSB * u] = stQ[u];
+        for (int j = 0; j < kSB; ++j) {
+            const int k0 = j * kSB + 4 * g;
+            const bool in = b < nblk && tr < C && j <= b;
+            if constexpr (VEC) {
+                const floatx4 v4 = in && k0 < C ? *reinterpret_cast<const floatx4*>(qrow + k0) : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) f.q[j][s] = v4[s];
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) f.q[j][s] = in && k0 + s < C ? qrow[k0 + s] : 0.0f;
             }
         }
-        float p0[4], vv[4], q0[4], bt[4];
-        bool ok[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            p0[r] = nx_p0[r];
-            vv[r] = nx_v[r];
-            q0[r] = nx_q0[r];
-            bt[r] = nx_b[r];
-            ok[r] = b0 + 4 * g + r < tv && col_ok;
-        }
-        if (b + 1 < nblk) prefetch(b + 1);
-        lds_barrier();   // the block's panels (and, first time, the inverses) are in LDS (loads and stores stay in flight)
-        // Terms of the earlier blocks: A[block, :b0] dv.
-        floatx4 far = {0.0f, 0.0f, 0.0f, 0.0f};
-        far = panel_times_dv(sA, ld, b0, wdv, g, m, far);
-        // Scaled right-hand sides, then dv = (block inverse) x (right-hand sides): the B operand of
-        // step s is the lane's own register s (k = 4 g + s).
-        float rhs[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) rhs[r] = ok[r] ? bt[r] * ((vv[r] - p0[r]) - far[r]) : 0.0f;
-        floatx4 x = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) x = mfma4(sT[(b0 + m) * kSB + 4 * g + s], rhs[s], x);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            x[r] = ok[r] ? x[r] : 0.0f;
-            wdv[(b0 + 4 * g + r) * kSB + m] = x[r];
-        }
-        // pred: the block's own A terms (B operand again the lane's registers).
-        floatx4 near = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) near = mfma4(sA[m * ld + b0 + 4 * g + s], x[s], near);
-        // read: QK[block, :b0+16] dv (this block's dv was just written by this wave).
-        floatx4 rd = {0.0f, 0.0f, 0.0f, 0.0f};
-        rd = panel_times_dv(sQ, ld, b0 + kSB, wdv, g, m, rd);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = b0 + 4 * g + r;
-            if (t < C && col_ok) {
-                const int64_t o = (rbase + t) * a.hd + col;
-                a.dv[o] = x[r];
-                a.pred[o] = ok[r] ? (p0[r] + far[r]) + near[r] : 0.0f;
-                a.read[o] = ok[r] ? q0[r] + rd[r] : 0.0f;
+            f.q0[r] = (b < nblk && t < C && col_ok) ? a.read[(rbase + t) * a.hd + col] : 0.0f;
+        }
+    };
+    auto read_block = [&](int b, const QRows& f) {
+        const int b0 = b * kSB;
+        floatx4 rd = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < kSB; ++j) {
+            if (j <= b) {   // (block-uniform)
+                const float* dcol = sdv + (j * kSB + 4 * g) * kTLd + m;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) rd = mfma4(f.q[j][s], dcol[s * kTLd], rd);
             }
         }
-        lds_barrier();   // the panels are replaced next
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = b0 + 4 * g + r;
+            if (t < C && col_ok) a.read[(rbase + t) * a.hd + col] = t < tv ? f.q0[r] + rd[r] : 0.0f;
+        }
+    };
+    for (int b = wv; b < nblk; b += 2 * kMW) {
+        QRows fa, fb;
+        load_q(b, fa);
+        load_q(b + kMW, fb);
+        read_block(b, fa);
+        if (b + kMW < nblk) read_block(b + kMW, fb);
     }
 }
 
@@ -399,16 +475,18 @@ hipError_t read_launch(const ReadLaunch& L, hipStream_t st) {
     hipError_t e = hipExtLaunchKernel(g, dim3(static_cast<unsigned>(a.P * tok_blocks * col_blocks)), dim3(256), kargs, 0,
                                       st, ev[0], ev[1], 0);
     if (e != hipSuccess) return e;
-    const int solve_blocks = a.P * ((a.hd + kMCols - 1) / kMCols);
+    const int solve_blocks = a.P * ((a.hd + kSB - 1) / kSB);
     const size_t lds = solve_lds_bytes(a.C);
-    return hipExtLaunchKernel(reinterpret_cast<const void*>(&read_solve_kernel), dim3(static_cast<unsigned>(solve_blocks)),
-                              dim3(256), kargs, lds, st, ev[2], ev[3], 0);
+    const void* sf = a.C % 4 == 0 ? reinterpret_cast<const void*>(&read_solve_kernel<true>)
+                                  : reinterpret_cast<const void*>(&read_solve_kernel<false>);
+    return hipExtLaunchKernel(sf, dim3(static_cast<unsigned>(solve_blocks)), dim3(256), kargs, lds, st, ev[2], ev[3], 0);
 }
 
 int read_lds_kernels(const void** fns, int cap) {
-    if (cap < 1) return 0;
-    fns[0] = reinterpret_cast<const void*>(&read_solve_kernel);
-    return 1;
+    if (cap < 2) return 0;
+    fns[0] = reinterpret_cast<const void*>(&read_solve_kernel<true>);
+    fns[1] = reinterpret_cast<const void*>(&read_solve_kernel<false>);
+    return 2;
 }
 
 }  // namespace sdm
