@@ -298,7 +298,7 @@ sdm_status sdm_dw_step_noalloc(const sdm_dw_io* io, int64_t ti, hipStream_t st);
 typedef struct sdm_read_io {
     const void* bank;       /* [rows, hd] SDM_F32 or SDM_BF16: the memory BEFORE this step's DW (read only) */
     int32_t bank_dtype;     /* sdm_dtype */
-    int64_t rows;           /* bank rows (an id outside 0..rows-1 contributes nothing) */
+    int64_t rows;           /* bank rows, >= 1 (an id outside 0..rows-1 contributes nothing) */
     int32_t hd;             /* row width, 1..4096 (a multiple of 8 takes 16-byte vector rows; any other
                                width element accesses, with element-aligned arrays) */
     const void* k_idx;      /* [N, C, W] absolute slot ids of the writes (Phase-1 input), int32 or int64 */
@@ -344,7 +344,7 @@ sdm_status sdm_read_step(const sdm_read_io* io, int64_t ti, hipStream_t st);
 typedef struct sdm_gds_io {
     const void* bank;       /* [rows, hd] SDM_F32 or SDM_BF16: the memory BEFORE this step's DW (read only) */
     int32_t bank_dtype;     /* sdm_dtype */
-    int64_t rows;           /* bank rows (an id outside 0..rows-1 contributes nothing) */
+    int64_t rows;           /* bank rows, >= 1 (an id outside 0..rows-1 contributes nothing) */
     int32_t hd;             /* row width, a multiple of 4, 4..4096 */
     const void* q_idx;      /* [N, C, R] absolute slot ids of the reads (Phase-1 input), int32 or int64 */
     const void* q_w;        /* [N, C, R] from sdm_phase1, float32 or bf16 (val_bytes) */
@@ -394,7 +394,7 @@ size_t sdm_gds_workspace(const sdm_gds_io* io);
 typedef struct sdm_gwr_io {
     const void* grad;       /* [rows, hd] SDM_F32 or SDM_BF16 gradient of the bank rows DW wrote (read only) */
     int32_t grad_dtype;     /* sdm_dtype */
-    int64_t rows;           /* grad rows (an id outside 0..rows-1 contributes nothing) */
+    int64_t rows;           /* grad rows, >= 1 (an id outside 0..rows-1 contributes nothing) */
     int32_t hd;             /* row width, a multiple of 4, 4..1024 */
     const void* k_idx;      /* [N, C, W] absolute slot ids of the writes, int32 or int64 */
     const float* w;         /* [N, C, W] write weights (the DW scale k exp(rex) of each entry) */
@@ -428,7 +428,7 @@ typedef struct sdm_pa_io {
     int32_t grad_dtype;     /* sdm_dtype */
     void* bank;             /* OUT (NULL: skipped) [rows, hd]: each written slot's row restored from snap */
     int32_t bank_dtype;     /* sdm_dtype of bank and snap */
-    int64_t rows;           /* rows of grad and bank (a slot outside 0..rows-1 is skipped) */
+    int64_t rows;           /* rows of grad and bank, >= 1 (a slot outside 0..rows-1 is skipped) */
     int32_t hd;             /* row width, a multiple of 4, 4..1024 */
     const void* snap;       /* the step's compact snapshot from sdm_dw_step (FIRST-position layout, raw rows) */
     int64_t snap_step_rows; /* as given to sdm_dw_step */

@@ -317,7 +317,7 @@ sdm_status sdm_read_step(const sdm_read_io* io, int64_t ti, hipStream_t st) {
     if (io->idx_bytes == 8 && (!aligned(io->k_idx, 8) || !aligned(io->q_idx, 8)))
         return fail(SDM_EALIGN, "sdm_read_step: int64 ids must be 8-byte aligned");
     if (io->hd < 1 || io->hd > 4096) return fail(SDM_ESHAPE, "sdm_read_step: hd = %d outside 1..4096", io->hd);
-    if (io->rows < 0 || io->step_rows < 0 || io->out_rows < 0)
+    if (io->rows < 1 || io->step_rows < 0 || io->out_rows < 0)
         return fail(SDM_EINVAL, "sdm_read_step: rows / step_rows / out_rows");
     if (ti * io->step_rows + static_cast<int64_t>(io->P) * io->C > io->out_rows)
         return fail(SDM_EINVAL, "sdm_read_step: %lld rows, step %lld needs %lld", static_cast<long long>(io->out_rows),
@@ -375,7 +375,7 @@ sdm_status sdm_gds_step(const sdm_gds_io* io, int64_t ti, hipStream_t st) {
         return fail(SDM_EINVAL, "sdm_gds_step: val_bytes = %d (0 or 4: float32 q_w; 2: bf16)", io->val_bytes);
     if (io->hd < 4 || io->hd > 4096 || io->hd % 4 != 0)
         return fail(SDM_ESHAPE, "sdm_gds_step: hd = %d (a multiple of 4 in 4..4096)", io->hd);
-    if (io->rows < 0 || io->step_rows < 0 || io->gr_rows < 0) return fail(SDM_EINVAL, "sdm_gds_step: rows / step_rows / gr_rows");
+    if (io->rows < 1 || io->step_rows < 0 || io->gr_rows < 0) return fail(SDM_EINVAL, "sdm_gds_step: rows / step_rows / gr_rows");
     if (ti * io->step_rows + static_cast<int64_t>(io->P) * io->C > io->gr_rows)
         return fail(SDM_EINVAL, "sdm_gds_step: gr holds %lld rows, step %lld needs %lld", static_cast<long long>(io->gr_rows),
                     static_cast<long long>(ti), static_cast<long long>(ti * io->step_rows + static_cast<int64_t>(io->P) * io->C));
@@ -417,7 +417,7 @@ sdm_status sdm_gwr_step(const sdm_gwr_io* io, int64_t ti, hipStream_t st) {
         return fail(SDM_EINVAL, "sdm_gwr_step: idx_bytes = %d (0 or 4: int32 ids; 8: int64 ids)", io->idx_bytes);
     if (io->hd < 4 || io->hd > 1024 || io->hd % 4 != 0)
         return fail(SDM_ESHAPE, "sdm_gwr_step: hd = %d (a multiple of 4 in 4..1024)", io->hd);
-    if (io->rows < 0 || io->step_rows < 0 || io->dv_rows < 0) return fail(SDM_EINVAL, "sdm_gwr_step: rows / step_rows / dv_rows");
+    if (io->rows < 1 || io->step_rows < 0 || io->dv_rows < 0) return fail(SDM_EINVAL, "sdm_gwr_step: rows / step_rows / dv_rows");
     if (ti * io->step_rows + static_cast<int64_t>(io->P) * io->C > io->dv_rows)
         return fail(SDM_EINVAL, "sdm_gwr_step: dv holds %lld rows, step %lld needs %lld", static_cast<long long>(io->dv_rows),
                     static_cast<long long>(ti), static_cast<long long>(ti * io->step_rows + static_cast<int64_t>(io->P) * io->C));
@@ -452,7 +452,7 @@ sdm_status sdm_pa_step(const sdm_pa_io* io, int64_t ti, hipStream_t st) {
     if (io->hd < 4 || io->hd > 1024 || io->hd % 4 != 0)
         return fail(SDM_ESHAPE, "sdm_pa_step: hd = %d (a multiple of 4 in 4..1024)", io->hd);
     const int64_t pcw = static_cast<int64_t>(io->P) * io->C * io->W;
-    if (io->rows < 0 || io->step_rows < 0 || io->dva_rows < 0 || io->snap_step_rows < 0)
+    if (io->rows < 1 || io->step_rows < 0 || io->dva_rows < 0 || io->snap_step_rows < 0)
         return fail(SDM_EINVAL, "sdm_pa_step: rows / step_rows / dva_rows / snap_step_rows");
     if (ti * io->step_rows + static_cast<int64_t>(io->P) * io->C > io->dva_rows)
         return fail(SDM_EINVAL, "sdm_pa_step: d_dva holds %lld rows, step %lld needs more", static_cast<long long>(io->dva_rows),

@@ -107,6 +107,20 @@ __device__ __forceinline__ float4 load4(const void* base, int bf, int64_t row, i
     return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + row * hd + col);
 }
 
+// load4 with the row dtype fixed at compile time: a run-time dtype branch around each load makes
+// the compiler wait for every load before the next (the bf16 path widens its data at once), which
+// serialises the rows a loop means to keep in flight together.
+template <bool BF>
+__device__ __forceinline__ float4 load4t(const void* base, int64_t row, int hd, int col) {
+    if constexpr (BF) {
+        const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + row * hd + col);
+        return make_float4(bf16_bits_to_f32(w.x & 0xFFFFu), bf16_bits_to_f32(w.x >> 16), bf16_bits_to_f32(w.y & 0xFFFFu),
+                           bf16_bits_to_f32(w.y >> 16));
+    } else {
+        return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + row * hd + col);
+    }
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
@@ -137,8 +151,8 @@ __device__ __forceinline__ int64_t shfl64(int64_t v, int src, int width = kWave)
 constexpr int kDotReads = 4;   // reads whose rows are in flight together
 constexpr int kWalkRows = 8;   // member gradient rows in flight together
 
-// TEAM: lanes per item (32 for rows of up to 128 columns: two items per wave).
-template <int TEAM>
+// TEAM: lanes per item (32 for rows of up to 128 columns: two items per wave). BBF: bf16 bank rows.
+template <int TEAM, bool BBF>
 __global__ void __launch_bounds__(kGdsThreads) gds_dots_kernel(GdsArgs a) {
     const int wv = static_cast<int>(threadIdx.x) / kWave;
     const int lane = static_cast<int>(lane_id());
@@ -171,7 +185,7 @@ __global__ void __launch_bounds__(kGdsThreads) gds_dots_kernel(GdsArgs a) {
         const float4 g = load4(a.gr, 0, grow, a.hd, col);
         float4 m[kDotReads];
 #pragma unroll
-        for (int u = 0; u < kDotReads; ++u) m[u] = load4(a.bank, a.bank_bf16, ok[u] ? s[u] : 0, a.hd, col);
+        for (int u = 0; u < kDotReads; ++u) m[u] = load4t<BBF>(a.bank, ok[u] ? s[u] : 0, a.hd, col);
 #pragma unroll
         for (int u = 0; u < kDotReads; ++u) {
             if (ok[u]) acc[u] = fmaf(g.w, m[u].w, fmaf(g.z, m[u].z, fmaf(g.y, m[u].y, fmaf(g.x, m[u].x, acc[u]))));
@@ -345,7 +359,7 @@ struct GwrArgs {
 
 // NCB: the blocks of 4 * TEAM columns a lane's registers hold (with 64-lane teams 1, 2 or 4: hd <=
 // 256, 512, 1024), so that narrow rows keep few registers and many waves per SIMD.
-template <int NCB, int GR, int TEAM>
+template <int NCB, int GR, int TEAM, bool GBF>
 __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
     const int wv = static_cast<int>(threadIdx.x) / kWave;
     const int lane = static_cast<int>(lane_id());
@@ -398,7 +412,7 @@ __global__ void __launch_bounds__(kGdsThreads) gwr_kernel(GwrArgs a) {
                 if (col >= a.hd) break;
                 float4 g[GR];
 #pragma unroll
-                for (int u = 0; u < GR; ++u) g[u] = load4(a.grad, a.grad_bf16, ok[u] ? s[u] : 0, a.hd, col);
+                for (int u = 0; u < GR; ++u) g[u] = load4t<GBF>(a.grad, ok[u] ? s[u] : 0, a.hd, col);
 #pragma unroll
                 for (int u = 0; u < GR; ++u) {
                     if (ok[u]) {
@@ -470,7 +484,8 @@ __device__ __forceinline__ void store4(void* base, int bf, int64_t row, int hd, 
 // from +0. A group in one segment then writes grad = fma(gdw, cpe, acc) and restores the bank row;
 // a split group's segments publish their partial rows, and the last to arrive adds them in segment
 // order and writes the rows (the same sums whichever segment arrives last).
-template <int NCB, int TEAM>
+// GBF, BBF: bf16 gradient rows, bf16 bank (and snapshot) rows.
+template <int NCB, int TEAM, bool GBF, bool BBF>
 __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
     constexpr int SEG = kSplitSeg;   // members per segment of a split group
     const int wv = static_cast<int>(threadIdx.x) / kWave;
@@ -504,12 +519,23 @@ __global__ void __launch_bounds__(kGdsThreads) pa_kernel(PaArgs a) {
     const int64_t srow = a.snap_row0 + static_cast<int64_t>(p) * a.CW + first_pos;
     float4 gdw[NCB], sn[NCB], acc[NCB];
     float part0 = 0.0f;
+    // (every load issued, from row 0 / the row's last 4 columns where its value is not used, so
+    // that the group's rows are in flight together)
+    const int64_t slot_c = in ? slot : 0;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int col = cb * 4 * TEAM + 4 * tl;
+        gdw[cb] = load4t<GBF>(a.grad, slot_c, a.hd, min(col, a.hd - 4));
+        sn[cb] = load4t<BBF>(a.snap, srow, a.hd, min(col, a.hd - 4));
+    }
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         const int col = cb * 4 * TEAM + 4 * tl;
         const bool con = in && col < a.hd;
-        gdw[cb] = con ? load4(a.grad, a.grad_bf16, slot, a.hd, col) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        sn[cb] = con ? load4(a.snap, a.bank_bf16, srow, a.hd, col) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (!con) {
+            gdw[cb] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            sn[cb] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
         acc[cb] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         part0 = fmaf(gdw[cb].w, sn[cb].w, fmaf(gdw[cb].z, sn[cb].z, fmaf(gdw[cb].y, sn[cb].y, fmaf(gdw[cb].x, sn[cb].x, part0))));
     }
@@ -689,8 +715,11 @@ hipError_t gds_launch(const sdm_gds_io* io, int64_t ti, hipStream_t st) {
     void* kargs[] = {&a};
     hipError_t e = hipSuccess;
     if (io->d_q_w != nullptr) {
-        e = hipLaunchKernel(half ? reinterpret_cast<const void*>(&gds_dots_kernel<32>)
-                                 : reinterpret_cast<const void*>(&gds_dots_kernel<kWave>),
+        const bool bbf = io->bank_dtype == SDM_BF16;
+        e = hipLaunchKernel(half ? (bbf ? reinterpret_cast<const void*>(&gds_dots_kernel<32, true>)
+                                        : reinterpret_cast<const void*>(&gds_dots_kernel<32, false>))
+                                 : (bbf ? reinterpret_cast<const void*>(&gds_dots_kernel<kWave, true>)
+                                        : reinterpret_cast<const void*>(&gds_dots_kernel<kWave, false>)),
                             dim3(static_cast<unsigned>((items + per_block - 1) / per_block)), dim3(kGdsThreads), kargs, 0, st);
         if (e != hipSuccess) return e;
     }
@@ -704,6 +733,28 @@ hipError_t gds_launch(const sdm_gds_io* io, int64_t ti, hipStream_t st) {
     }
     return e;
 }
+
+namespace {
+
+// The GWR and PA kernels for a head dim and the rows' dtypes: rows of up to 128 columns take
+// 32-lane (GWR) or 16-lane (PA) teams, wider rows a wave per item with 1, 2 or 4 column blocks.
+template <bool GBF>
+const void* gwr_fn(int hd) {
+    return hd <= 4 * 32 ? reinterpret_cast<const void*>(&gwr_kernel<1, 8, 32, GBF>)
+         : hd <= 256    ? reinterpret_cast<const void*>(&gwr_kernel<1, 8, kWave, GBF>)
+         : hd <= 512    ? reinterpret_cast<const void*>(&gwr_kernel<2, 4, kWave, GBF>)
+                        : reinterpret_cast<const void*>(&gwr_kernel<4, 4, kWave, GBF>);
+}
+
+template <bool GBF, bool BBF>
+const void* pa_fn(int hd) {
+    return hd <= 4 * 32 ? reinterpret_cast<const void*>(&pa_kernel<2, 16, GBF, BBF>)
+         : hd <= 256    ? reinterpret_cast<const void*>(&pa_kernel<1, kWave, GBF, BBF>)
+         : hd <= 512    ? reinterpret_cast<const void*>(&pa_kernel<2, kWave, GBF, BBF>)
+                        : reinterpret_cast<const void*>(&pa_kernel<4, kWave, GBF, BBF>);
+}
+
+}  // namespace
 
 hipError_t gwr_launch(const sdm_gwr_io* io, int64_t ti, hipStream_t st) {
     GwrArgs a;
@@ -728,10 +779,7 @@ hipError_t gwr_launch(const sdm_gwr_io* io, int64_t ti, hipStream_t st) {
     void* kargs[] = {&a};
     // Rows of up to 128 columns: a 32-lane team per token, two per wave (16-lane teams measured slower).
     const bool half = io->hd <= 4 * 32;
-    const void* fn = half ? reinterpret_cast<const void*>(&gwr_kernel<1, 8, 32>)
-                   : io->hd <= 256 ? reinterpret_cast<const void*>(&gwr_kernel<1, 8, kWave>)
-                   : io->hd <= 512 ? reinterpret_cast<const void*>(&gwr_kernel<2, 4, kWave>)
-                                   : reinterpret_cast<const void*>(&gwr_kernel<4, 4, kWave>);
+    const void* fn = a.grad_bf16 ? gwr_fn<true>(io->hd) : gwr_fn<false>(io->hd);
     const int64_t per_block = static_cast<int64_t>(kGdsWaves) * (half ? 2 : 1);
     return hipLaunchKernel(fn, dim3(static_cast<unsigned>((toks + per_block - 1) / per_block)), dim3(kGdsThreads), kargs, 0, st);
 }
@@ -786,10 +834,9 @@ hipError_t pa_launch(const sdm_pa_io* io, int64_t ti, hipStream_t st) {
     // Rows of up to 128 columns: a 16-lane team per K-row position (8 columns per lane), four per
     // wave (faster than 32-lane teams where groups are short; long groups walk more record rounds).
     const bool half = io->hd <= 4 * 32;
-    const void* fn = half ? reinterpret_cast<const void*>(&pa_kernel<2, 16>)
-                   : io->hd <= 256 ? reinterpret_cast<const void*>(&pa_kernel<1, kWave>)
-                   : io->hd <= 512 ? reinterpret_cast<const void*>(&pa_kernel<2, kWave>)
-                                   : reinterpret_cast<const void*>(&pa_kernel<4, kWave>);
+    const bool gbf = a.grad_bf16 != 0, bbf = a.bank_bf16 != 0;
+    const void* fn = gbf ? (bbf ? pa_fn<true, true>(io->hd) : pa_fn<true, false>(io->hd))
+                         : (bbf ? pa_fn<false, true>(io->hd) : pa_fn<false, false>(io->hd));
     const int64_t per_block = static_cast<int64_t>(kGdsWaves) * (half ? 4 : 1);
     return hipLaunchKernel(fn, dim3(static_cast<unsigned>((poss + per_block - 1) / per_block)), dim3(kGdsThreads), kargs, 0, st);
 }

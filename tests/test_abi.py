@@ -183,7 +183,7 @@ def read_io(**kw):
     (dict(dv=FAKE + 4), 0, _lib.SDM_EALIGN), (dict(a=FAKE + 2), 0, _lib.SDM_EALIGN),
     (dict(idx_bytes=3), 0, _lib.SDM_EINVAL), (dict(idx_bytes=8, k_idx=FAKE + 4), 0, _lib.SDM_EALIGN),
     (dict(val_bytes=3), 0, _lib.SDM_EINVAL), (dict(k_eff=FAKE + 2), 0, _lib.SDM_EALIGN),
-    (dict(val_bytes=2, q_w=FAKE + 1), 0, _lib.SDM_EALIGN),
+    (dict(val_bytes=2, q_w=FAKE + 1), 0, _lib.SDM_EALIGN), (dict(rows=0), 0, _lib.SDM_EINVAL),
 ])
 def test_read_step_refusals(kw, ti, status):
     lib = _lib.load()
@@ -225,6 +225,7 @@ def gds_io(**kw):
     (dict(spay_q=None), 0, _lib.SDM_EINVAL), (dict(gr=FAKE + 8), 0, _lib.SDM_EALIGN),
     (dict(bank=FAKE + 4), 0, _lib.SDM_EALIGN), (dict(grad=FAKE + 8), 0, _lib.SDM_EALIGN),
     (dict(q_w=FAKE + 2), 0, _lib.SDM_EALIGN), (dict(valid_last=129), 0, _lib.SDM_EINVAL),
+    (dict(rows=0), 0, _lib.SDM_EINVAL),
 ])
 def test_gds_refusals(kw, ti, status):
     lib = _lib.load()
@@ -250,6 +251,7 @@ def gwr_io(**kw):
     (dict(dv_rows=100), 0, _lib.SDM_EINVAL), (dict(w=None), 0, _lib.SDM_EINVAL), (dict(dv=FAKE + 4), 0, _lib.SDM_EALIGN),
     (dict(d_dv=FAKE + 8), 0, _lib.SDM_EALIGN), (dict(grad=FAKE + 4), 0, _lib.SDM_EALIGN),
     (dict(d_k_pd=FAKE + 2), 0, _lib.SDM_EALIGN), (dict(first_partial=9), 0, _lib.SDM_EINVAL),
+    (dict(rows=0), 0, _lib.SDM_EINVAL),
 ])
 def test_gwr_refusals(kw, ti, status):
     lib = _lib.load()
@@ -276,7 +278,7 @@ def pa_io(**kw):
     (dict(snap=FAKE + 4), 0, _lib.SDM_EALIGN), (dict(krec=FAKE + 8), 0, _lib.SDM_EALIGN),
     (dict(d_k_eff=FAKE + 2), 0, _lib.SDM_EALIGN),
     (dict(workspace=FAKE, workspace_bytes=16), 0, _lib.SDM_EWORKSPACE),
-    (dict(workspace=FAKE + 4, workspace_bytes=1 << 40), 0, _lib.SDM_EALIGN),
+    (dict(workspace=FAKE + 4, workspace_bytes=1 << 40), 0, _lib.SDM_EALIGN), (dict(rows=0), 0, _lib.SDM_EINVAL),
 ])
 def test_pa_refusals(kw, ti, status):
     lib = _lib.load()
