@@ -1268,12 +1268,12 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
                   const uint32_t word = (u % 2) ? (w2 >> 16) : (w2 & 0xFFFFu);
                   flags |= (u < lanes && (word & walk_bits)) ? (1u << u) : 0u;
               }
-          } else {
+          } else {   // (all 32 words loaded before any is tested, so that they are in flight together)
+              uint32_t wd[32];
 #pragma unroll
-              for (int u = 0; u < 32; ++u) {
-                  const int ln = lb + u;
-                  flags |= (ln < lanes && (iv[min(ln, lanes - 1)] & walk_bits)) ? (1u << u) : 0u;
-              }
+              for (int u = 0; u < 32; ++u) wd[u] = iv[min(lb + u, lanes - 1)];
+#pragma unroll
+              for (int u = 0; u < 32; ++u) flags |= (lb + u < lanes && (wd[u] & walk_bits)) ? (1u << u) : 0u;
           }
           // Walks two at a time: both record windows in flight before either is walked (the terms
           // still reach the row in lane order).
