@@ -33,7 +33,7 @@
 namespace sdm {
 namespace {
 
-constexpr int kTI = 16;                                   // items per thread per tile
+constexpr int kTI = 8;                                    // items per thread per tile
 constexpr int kTT = kNT * kTI;                            // entries per tile
 constexpr int kTDigit = 6;                                // key bits per radix pass
 constexpr int kTUnits = (kP1MaxTiledRow / kTT) * kNW;     // (tile, wave) units of the longest row
