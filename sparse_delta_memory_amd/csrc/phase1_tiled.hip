@@ -168,9 +168,19 @@ __global__ void __launch_bounds__(kNT) p1_tiled_kernel(TiledArgs a) {
         for (int sweep = 0; sweep < 2; ++sweep) {
             for (int T = 0; T < ntiles; ++T) {
                 uint32_t* uh = hist + (T * kNW + w) * nd;
+                // The tile's keys (and, when scattering, entry indices) all loaded before the first
+                // is ranked, from clamped positions past the row: one round trip per tile.
+                uint32_t kt[kTI], rt[kTI];
+#pragma unroll
+                for (int k = 0; k < kTI; ++k) {
+                    const int i = min(T * kTT + w * kWave * kTI + k * kWave + lane, n - 1);
+                    kt[k] = ks[i];
+                    rt[k] = sweep == 1 ? rs[i] : 0u;
+                }
+#pragma unroll
                 for (int k = 0; k < kTI; ++k) {
                     const int i = T * kTT + w * kWave * kTI + k * kWave + lane;
-                    const uint32_t key = i < n ? ks[i] : kTPad;
+                    const uint32_t key = i < n ? kt[k] : kTPad;
                     const uint32_t d = (key >> sh) & dmask;
                     uint64_t peers = ~0ull;
                     for (int b = 0; b < db; ++b) {
@@ -183,7 +193,7 @@ __global__ void __launch_bounds__(kNT) p1_tiled_kernel(TiledArgs a) {
                     const uint32_t base = uh[d];
                     if (sweep == 1 && i < n) {
                         kd[base + below] = key;
-                        rd[base + below] = rs[i];
+                        rd[base + below] = rt[k];
                     }
                     if (below == 0) uh[d] = base + cnt;   // the lowest lane of the digit in this item
                 }
@@ -232,16 +242,28 @@ __global__ void __launch_bounds__(kNT) p1_tiled_kernel(TiledArgs a) {
     };
     auto load_items = [&](int T, Items& it) {
         const int p0 = T * kTT + tid * kTI;
+        // (every load issued from a clamped position, the values past the row dropped after: the
+        // loads are in flight together)
 #pragma unroll
         for (int k = 0; k < kTI; ++k) {
-            const int p = p0 + k;
-            it.key[k] = p < n ? skey[p] : kTPad;
-            it.rr[k] = p < n ? sr[p] : 0u;
+            const int pc = min(p0 + k, n - 1);
+            it.key[k] = skey[pc];
+            it.rr[k] = sr[pc];
         }
         const bool has_prev = p0 > 0 && p0 <= n;
-        const uint32_t pkey = has_prev ? skey[p0 - 1] : kTPad;
-        it.prev_r = has_prev ? sr[p0 - 1] : 0u;
-        const uint32_t nkey = p0 + kTI < n ? skey[p0 + kTI] : kTPad;
+        const int pp = min(max(p0 - 1, 0), n - 1);
+        const uint32_t pkey_l = skey[pp], prev_l = sr[pp];
+        const uint32_t nkey_l = skey[min(p0 + kTI, n - 1)];
+#pragma unroll
+        for (int k = 0; k < kTI; ++k) {
+            if (p0 + k >= n) {
+                it.key[k] = kTPad;
+                it.rr[k] = 0u;
+            }
+        }
+        const uint32_t pkey = has_prev ? pkey_l : kTPad;
+        it.prev_r = has_prev ? prev_l : 0u;
+        const uint32_t nkey = p0 + kTI < n ? nkey_l : kTPad;
         it.valid = it.isk = it.head = it.end = it.rep = 0u;
 #pragma unroll
         for (int k = 0; k < kTI; ++k) {
