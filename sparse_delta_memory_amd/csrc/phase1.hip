@@ -1275,20 +1275,23 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
 #pragma unroll
               for (int u = 0; u < 32; ++u) flags |= (lb + u < lanes && (wd[u] & walk_bits)) ? (1u << u) : 0u;
           }
-          // Walks two at a time: both record windows in flight before either is walked (the terms
+          // Walks three at a time: their record windows in flight before any is walked (the terms
           // still reach the row in lane order).
           for (; flags != 0u;) {
-            const int ln1 = lb + __builtin_ctz(flags);
-            flags &= flags - 1u;
-            const int ln2 = flags != 0u ? lb + __builtin_ctz(flags) : -1;
-            if (flags != 0u) flags &= flags - 1u;
-            const int rho1 = walk_start(ln1);
-            const int rho2 = ln2 >= 0 ? walk_start(ln2) : -1;
-            uint4 w1[kWin], w2[kWin];
-            load_window(rho1, w1);
-            load_window(rho2, w2);
-            if (rho1 >= 0) walk(rho1, w1);
-            if (rho2 >= 0) walk(rho2, w2);
+            int rh[3];
+#pragma unroll
+            for (int q3 = 0; q3 < 3; ++q3) {
+                const int ln = flags != 0u ? lb + __builtin_ctz(flags) : -1;
+                if (flags != 0u) flags &= flags - 1u;
+                rh[q3] = ln >= 0 ? walk_start(ln) : -1;
+            }
+            uint4 w1[kWin], w2[kWin], w3[kWin];
+            load_window(rh[0], w1);
+            load_window(rh[1], w2);
+            load_window(rh[2], w3);
+            if (rh[0] >= 0) walk(rh[0], w1);
+            if (rh[1] >= 0) walk(rh[1], w2);
+            if (rh[2] >= 0) walk(rh[2], w3);
           }
         }
     }
