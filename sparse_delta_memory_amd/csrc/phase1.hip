@@ -129,7 +129,6 @@ __device__ void block_radix_sort(uint32_t (&key)[IPT], uint32_t (&val)[IPT], int
                                  uint16_t* sval, uint32_t* hist, uint32_t* wsum, uint32_t& phase) {
     const int lane = static_cast<int>(lane_id());
     const int w = threadIdx.x / kWave;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
     const int stride = (1 << dmax) + 1;   // rows padded by a word: the (digit, wave) scan spreads over the banks
     uint32_t* my_hist = hist + w * stride;
     const int passes = (bits + dmax - 1) / dmax;
@@ -145,14 +144,8 @@ __device__ void block_radix_sort(uint32_t (&key)[IPT], uint32_t (&val)[IPT], int
 #pragma unroll
         for (int k = 0; k < IPT; ++k) {
             const uint32_t d = (key[k] >> sh) & dmask;
-            uint64_t peers = ~0ull;
-            for (int b = 0; b < db; ++b) {
-                const bool bit = (d >> b) & 1u;
-                const uint64_t m = __ballot(bit);
-                peers &= bit ? m : ~m;
-            }
-            const uint32_t below = static_cast<uint32_t>(__popcll(peers & lt_mask));
-            const uint32_t cnt = static_cast<uint32_t>(__popcll(peers));
+            uint32_t below, cnt;
+            digit_peers(d, db, below, cnt);
             const uint32_t base = my_hist[d];
             val[k] = (val[k] & 0xFFFFu) | (base + below) << 16;
             if (below == 0) my_hist[d] = base + cnt;   // the slice's lowest lane of this digit

@@ -150,7 +150,6 @@ __global__ void __launch_bounds__(kNT) p1_tiled_kernel(TiledArgs a) {
     const int bits = tv < C ? a.key_bits + 1 : a.key_bits;
     const int passes = (bits + kTDigit - 1) / kTDigit;
     const int width = (bits + passes - 1) / passes;
-    const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
     const int units = ntiles * kNW;
     uint32_t* ks = keys0;
     uint32_t* rs = rr0;
@@ -182,14 +181,8 @@ __global__ void __launch_bounds__(kNT) p1_tiled_kernel(TiledArgs a) {
                     const int i = T * kTT + w * kWave * kTI + k * kWave + lane;
                     const uint32_t key = i < n ? kt[k] : kTPad;
                     const uint32_t d = (key >> sh) & dmask;
-                    uint64_t peers = ~0ull;
-                    for (int b = 0; b < db; ++b) {
-                        const bool bit = (d >> b) & 1u;
-                        const uint64_t m = __ballot(bit);
-                        peers &= bit ? m : ~m;
-                    }
-                    const uint32_t below = static_cast<uint32_t>(__popcll(peers & lt_mask));
-                    const uint32_t cnt = static_cast<uint32_t>(__popcll(peers));
+                    uint32_t below, cnt;
+                    digit_peers(d, db, below, cnt);
                     const uint32_t base = uh[d];
                     if (sweep == 1 && i < n) {
                         kd[base + below] = key;

@@ -45,6 +45,22 @@ __device__ __forceinline__ float load_val(const void* p, int64_t i, int bf) {
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
 
+// The lanes of the wave whose digit (the db low bits of d, db < 32) equals this lane's: `below` of
+// them in lower lanes, `cnt` in all (every lane of the wave active). One ballot per bit: with the
+// lane's bit replicated over a word (sel), it keeps the ballot's lanes that agree with it,
+// peers &= ~(ballot ^ sel) per 32-lane half (one 3-input bit operation each on gfx950).
+__device__ __forceinline__ void digit_peers(uint32_t d, int db, uint32_t& below, uint32_t& cnt) {
+    uint32_t plo = ~0u, phi = ~0u;
+    for (int b = 0; b < db; ++b) {
+        const uint32_t sel = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int32_t>(d), b, 1));
+        const uint64_t m = __ballot(sel != 0u);
+        plo &= ~(static_cast<uint32_t>(m) ^ sel);
+        phi &= ~(static_cast<uint32_t>(m >> 32) ^ sel);
+    }
+    below = __builtin_amdgcn_mbcnt_hi(phi, __builtin_amdgcn_mbcnt_lo(plo, 0u));   // set bits under the lane
+    cnt = static_cast<uint32_t>(__popc(plo) + __popc(phi));
+}
+
 // The compute dies (XCDs) of the device: a launch's workgroups are dealt to them in turn
 // (workgroup b runs on XCD b % kXcds), and each has its own L2.
 constexpr int kXcds = 8;
