@@ -57,6 +57,12 @@ __device__ __forceinline__ int token_of_entry(int r, uint32_t magic) {
     return static_cast<int>(__umulhi(static_cast<uint32_t>(r), magic));
 }
 
+// t * m for the factors of entry decoding and row offsets (tokens and lane counts: both below 2^24,
+// the product below 2^31), on the full-rate 24-bit multiply.
+__device__ __forceinline__ int mul24(int t, int m) {
+    return static_cast<int>(__umul24(static_cast<unsigned>(t), static_cast<unsigned>(m)));
+}
+
 // Segmented-scan element: a TwoSum-compensated float sum (s + c), the valid K count (bits 0-15),
 // the valid Q count (bits 16-30) and a segment-start flag (bit 31).
 struct Seg {

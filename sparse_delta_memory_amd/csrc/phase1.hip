@@ -218,6 +218,16 @@ template <int IPT, bool LG, bool ID64, bool VBF>
 __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     constexpr int NP = kNT * IPT;
     constexpr int NTILE = (NP + kTile - 1) / kTile;
+    // Products of tokens and lane counts: at 16 items per thread on the full-rate 24-bit multiply;
+    // at fewer items the plain multiply, which leaves the compiler's scalar registers in a better
+    // state there (measured: with the 24-bit form it spilled far more of them into vector lanes).
+    auto imul = [](int t, int m) {
+        if constexpr (IPT >= 16) {
+            return mul24(t, m);
+        } else {
+            return t * m;
+        }
+    };
     extern __shared__ __align__(16) unsigned char smem[];
     uint32_t* skey = reinterpret_cast<uint32_t*>(smem);                   // sort keys
     uint32_t* hist = reinterpret_cast<uint32_t*>(smem + a.hist_off);      // digit counts
@@ -257,7 +267,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     // The gate of valid token t's K lane j (the scans read it for non-repeated valid K entries only).
     auto gate = [&](int t, int j) -> float {
         if constexpr (LG) {
-            return a.g[cw + t * W + j];
+            return a.g[cw + imul(t, W) + j];
         } else {
             return gates[t];
         }
@@ -285,8 +295,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             val[k] = static_cast<uint32_t>(i);
             const int ic = i < n ? i : 0;
             const int t = token_of_entry(ic, a.wr_magic);
-            const int j = ic - t * wr;
-            ids[k] = load_id<ID64>(j < W ? a.k_idx : a.q_idx, j < W ? cw + t * W + j : cr + t * R + (j - W));
+            const int j = ic - imul(t, wr);
+            ids[k] = load_id<ID64>(j < W ? a.k_idx : a.q_idx, j < W ? cw + imul(t, W) + j : cr + imul(t, R) + (j - W));
         }
         // Resident layout: the entries' values in entry order (coalesced, issued beside the ids;
         // the invalid tokens' values, which may be anything, are not used).
@@ -368,10 +378,10 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                 const bool pvalid = pk < key_lim && (p0 + k) > 0;
                 const bool head = !valid || !pvalid || kk[k] != pk;
                 const int t = token_of_entry(static_cast<int>(rr[k]), a.wr_magic);
-                const int j = static_cast<int>(rr[k]) - t * wr;
+                const int j = static_cast<int>(rr[k]) - imul(t, wr);
                 const bool is_k = valid && j < W;
                 const int pt = token_of_entry(static_cast<int>(pr), a.wr_magic);
-                const int pj = static_cast<int>(pr) - pt * wr;
+                const int pj = static_cast<int>(pr) - imul(pt, wr);
                 const bool rep = !head && is_k && pj < W && pt == t;
                 heads |= (head ? 1u : 0u) << k;
                 reps |= (rep ? 1u : 0u) << k;
@@ -389,7 +399,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             for (int k = kTileItems - 1; k >= 0; --k) {
                 const bool valid = kk[k] < key_lim;
                 const int t = token_of_entry(static_cast<int>(rr[k]), a.wr_magic);
-                const bool q = static_cast<int>(rr[k]) - t * wr >= W;
+                const bool q = static_cast<int>(rr[k]) - imul(t, wr) >= W;
                 agg = seg_combine(agg, Seg{x[k], 0.0f, (valid ? (q ? kSegQOne : 1u) : 0u) |
                                                            (((ends >> k) & 1u) ? kSegHead : 0u)});
             }
@@ -428,9 +438,9 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             rr[k] = p < n ? sval[p] : kFlagHead;   // padding: a group of its own
             const int r = static_cast<int>(rr[k] & kRMask);
             const int t = token_of_entry(r, a.wr_magic);
-            const bool q = r - t * wr >= W;
+            const bool q = r - imul(t, wr) >= W;
             const bool valid = p < n && t < tv;
-            x[k] = (valid && !q && !(rr[k] & kFlagRep)) ? gate(t, r - t * wr) : 0.0f;
+            x[k] = (valid && !q && !(rr[k] & kFlagRep)) ? gate(t, r - imul(t, wr)) : 0.0f;
             heads |= ((rr[k] & kFlagHead) ? 1u : 0u) << k;
         }
         const int pn = p0 + kTileItems;
@@ -446,7 +456,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
         const int p = T * kTile + threadIdx.x * kTileItems + k;
         const int r = static_cast<int>(rr[k] & kRMask);
         const int t = token_of_entry(r, a.wr_magic);
-        const bool q = r - t * wr >= W;
+        const bool q = r - imul(t, wr) >= W;
         const bool valid = p < n && t < tv;
         return Seg{x[k], 0.0f, (valid ? (q ? kSegQOne : 1u) : 0u) | (seg_start ? kSegHead : 0u)};
     };
@@ -471,7 +481,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                 agg = seg_combine(agg, tile_item(T, k, rr, x, (heads >> k) & 1u));
                 const int r = static_cast<int>(rr[k] & kRMask);
                 const int t = token_of_entry(r, a.wr_magic);
-                if (p0 + k < n) kind_cnt += (r - t * wr >= W) ? kSegQOne : 1u;
+                if (p0 + k < n) kind_cnt += (r - imul(t, wr) >= W) ? kSegQOne : 1u;
             }
             Seg total;
             fpre[T] = seg_combine(fcarry, block_exclusive_seg<false>(agg, wtot, seg_phase, total));
@@ -518,7 +528,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             e.live = p0 + k < n;
             e.r = static_cast<int>(rr[k] & kRMask);
             e.t = token_of_entry(e.r, a.wr_magic);
-            const int j = e.r - e.t * wr;
+            const int j = e.r - imul(e.t, wr);
             e.q = j >= W;
             e.ln = e.q ? j - W : j;
             e.valid = e.live && e.t < tv;
@@ -535,7 +545,7 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             // Same token and kind as the previous position (inside the group): not a run start.
             const uint32_t pr = k ? (rr[k - 1] & kRMask) : prev_r;
             const int pt = token_of_entry(static_cast<int>(pr), a.wr_magic);
-            const bool pq = static_cast<int>(pr) - pt * wr >= W;
+            const bool pq = static_cast<int>(pr) - imul(pt, wr) >= W;
             const bool same_run = !head && pt == e.t && pq == e.q;
             e.walk = e.valid && !same_run && (before.f & 0xFFFFu) != 0u;
             const bool prev_head = k ? ((heads >> (k - 1)) & 1u) : ((prev_raw & kFlagHead) != 0u);
@@ -607,18 +617,18 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                     const int p = p0 + k;
                     const int r = p < n ? static_cast<int>(sval[p] & kRMask) : 0;
                     const int t = token_of_entry(r, a.wr_magic);
-                    const int j = r - t * wr;
+                    const int j = r - imul(t, wr);
                     const bool q = j >= W;
                     if (res) {   // staged values (zero for invalid tokens); the slot from the sorted key
-                        vl[k] = q ? vals_q[t * R + (j - W)] : vals_k[t * W + j];
+                        vl[k] = q ? vals_q[imul(t, R) + (j - W)] : vals_k[imul(t, W) + j];
                         if constexpr (sk) kid[k] = static_cast<int32_t>(p < n ? skey[p] : 0u);
                     } else {
                         // (a select of the entry's address, then one load)
                         using VT = std::conditional_t<VBF, uint16_t, float>;
-                        const VT* vp = q ? static_cast<const VT*>(a.q_val) + cr + t * R + (j - W)
-                                         : static_cast<const VT*>(a.k_val) + cw + t * W + j;
+                        const VT* vp = q ? static_cast<const VT*>(a.q_val) + cr + imul(t, R) + (j - W)
+                                         : static_cast<const VT*>(a.k_val) + cw + imul(t, W) + j;
                         vl[k] = load_val(vp, 0, VBF);
-                        if constexpr (sk) kid[k] = static_cast<int32_t>(load_id<ID64>(a.k_idx, cw + ((!q && t < tv) ? t * W + j : 0)));
+                        if constexpr (sk) kid[k] = static_cast<int32_t>(load_id<ID64>(a.k_idx, cw + ((!q && t < tv) ? imul(t, W) + j : 0)));
                     }
                 }
                 if (!res) {
@@ -651,12 +661,12 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                                                  (e.bcnt == 0 ? kFirst : 0u) | (e.acnt == 0 ? kLast : 0u))
                                               : (e.pay | kFirst | kLast);
                 if (sq && (!sk || e.q)) {
-                    const int o = (e.t - t0) * R + e.ln;
+                    const int o = imul(e.t - t0, R) + e.ln;
                     ql[o] = Lv;
                     qm[o] = meta;
                     if (a.spay_q != nullptr) gstore<uint32_t>(a.spay_q + cr, e.jkind, elem);
                 } else {
-                    const int o = (e.t - t0) * W + e.ln;
+                    const int o = imul(e.t - t0, W) + e.ln;
                     kl[o] = Lv;
                     kx[o] = e.rex;
                     km[o] = meta;
