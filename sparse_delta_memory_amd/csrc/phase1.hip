@@ -260,6 +260,16 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
     const int lane = static_cast<int>(lane_id());
     const int w = threadIdx.x / kWave;
     const int ntiles = (n + kTile - 1) / kTile;
+    // A tile position as an index of the sorted row's LDS arrays (NP entries, every one written by
+    // the sort): positions past the row are read there too, and their values are not used; tiles
+    // longer than the row (fewer than 4 items per thread) read its last entry instead.
+    auto in_row = [](int p) {
+        if constexpr (NP % kTile == 0) {
+            return p;
+        } else {
+            return min(p, NP - 1);
+        }
+    };
 
     if constexpr (!LG) {
         for (int t = threadIdx.x; t < C; t += kNT) gates[t] = t < tv ? a.g[static_cast<int64_t>(c) * C + t] : 0.0f;
@@ -361,8 +371,9 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
 #pragma unroll
             for (int k = 0; k < kTileItems; ++k) {
                 const int p = p0 + k;
-                kk[k] = p < n ? skey[p] : pad_key;
-                rr[k] = p < n ? (sval[p] & kRMask) : 0u;
+                const uint32_t kv = skey[in_row(p)], sv = sval[in_row(p)];
+                kk[k] = p < n ? kv : pad_key;
+                rr[k] = p < n ? (sv & kRMask) : 0u;
             }
             const bool has_prev = p0 > 0 && p0 <= n;
             const uint32_t prev_key = has_prev ? skey[p0 - 1] : pad_key;
@@ -435,7 +446,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
 #pragma unroll
         for (int k = 0; k < kTileItems; ++k) {
             const int p = p0 + k;
-            rr[k] = p < n ? sval[p] : kFlagHead;   // padding: a group of its own
+            const uint32_t sv = sval[in_row(p)];
+            rr[k] = p < n ? sv : kFlagHead;   // padding: a group of its own
             const int r = static_cast<int>(rr[k] & kRMask);
             const int t = token_of_entry(r, a.wr_magic);
             const bool q = r - imul(t, wr) >= W;
@@ -444,7 +456,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             heads |= ((rr[k] & kFlagHead) ? 1u : 0u) << k;
         }
         const int pn = p0 + kTileItems;
-        const bool next_head = pn >= n || (sval[pn] & kFlagHead);
+        const uint32_t svn = sval[min(pn, NP - 1)];
+        const bool next_head = pn >= n || (svn & kFlagHead);
 #pragma unroll
         for (int k = 0; k < kTileItems; ++k) {
             const bool end = k + 1 < kTileItems ? ((heads >> (k + 1)) & 1u) : next_head;
@@ -515,7 +528,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             afts[k] = after.f & ~kSegHead;
             run = seg_combine(run, tile_item(T, k, rr, x, end));
         }
-        const uint32_t prev_raw = p0 > 0 && p0 <= n ? sval[p0 - 1] : (0xFFFFu & ~kFlagHead);
+        const uint32_t svp = sval[in_row(max(p0 - 1, 0))];
+        const uint32_t prev_raw = p0 > 0 && p0 <= n ? svp : (0xFFFFu & ~kFlagHead);
         const uint32_t prev_r = prev_raw & kRMask;
         run = fp;
         uint32_t jk = kp & 0xFFFFu, jq = kp >> 16;
@@ -615,7 +629,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
 #pragma unroll
                 for (int k = 0; k < kTileItems; ++k) {
                     const int p = p0 + k;
-                    const int r = p < n ? static_cast<int>(sval[p] & kRMask) : 0;
+                    const uint32_t sv = sval[in_row(p)];
+                    const int r = p < n ? static_cast<int>(sv & kRMask) : 0;
                     const int t = token_of_entry(r, a.wr_magic);
                     const int j = r - imul(t, wr);
                     const bool q = j >= W;
@@ -635,7 +650,8 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
 #pragma unroll
                     for (int k = 0; k < kTileItems; ++k) {   // invalid tokens' values are not used
                         const int p = p0 + k;
-                        const int r = p < n ? static_cast<int>(sval[p] & kRMask) : 0;
+                        const uint32_t sv = sval[in_row(p)];
+                    const int r = p < n ? static_cast<int>(sv & kRMask) : 0;
                         vl[k] = (p < n && token_of_entry(r, a.wr_magic) < tv) ? vl[k] : 0.0f;
                     }
                 }
