@@ -638,12 +638,23 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                         vl[k] = q ? vals_q[imul(t, R) + (j - W)] : vals_k[imul(t, W) + j];
                         if constexpr (sk) kid[k] = static_cast<int32_t>(p < n ? skey[p] : 0u);
                     } else {
-                        // (a select of the entry's address, then one load)
-                        using VT = std::conditional_t<VBF, uint16_t, float>;
-                        const VT* vp = q ? static_cast<const VT*>(a.q_val) + cr + imul(t, R) + (j - W)
-                                         : static_cast<const VT*>(a.k_val) + cw + imul(t, W) + j;
-                        vl[k] = load_val(vp, 0, VBF);
-                        if constexpr (sk) kid[k] = static_cast<int32_t>(load_id<ID64>(a.k_idx, cw + ((!q && t < tv) ? imul(t, W) + j : 0)));
+                        // Selects of the array and of the element (a K entry's index in its kind's rows
+                        // is t W + j = r - t R, a Q entry's t R + j - W = r - (t + 1) W), then one load.
+                        // At 16 items per thread the compiler's branch over the two address forms
+                        // measured faster; at fewer items the selects (far fewer scalar registers
+                        // spilled into vector lanes).
+                        const int ek = r - imul(t, R);
+                        if constexpr (IPT >= 16) {
+                            using VT = std::conditional_t<VBF, uint16_t, float>;
+                            const VT* vp = q ? static_cast<const VT*>(a.q_val) + cr + imul(t, R) + (j - W)
+                                             : static_cast<const VT*>(a.k_val) + cw + ek;
+                            vl[k] = load_val(vp, 0, VBF);
+                        } else {
+                            const int64_t e = q ? cr + (r - imul(t + 1, W)) : cw + ek;
+                            const uintptr_t vb = q ? reinterpret_cast<uintptr_t>(a.q_val) : reinterpret_cast<uintptr_t>(a.k_val);
+                            vl[k] = load_val(reinterpret_cast<const void*>(vb), e, VBF);
+                        }
+                        if constexpr (sk) kid[k] = static_cast<int32_t>(load_id<ID64>(a.k_idx, cw + ((!q && t < tv) ? ek : 0)));
                     }
                 }
                 if (!res) {
