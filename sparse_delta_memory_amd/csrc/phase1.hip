@@ -708,8 +708,20 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                     int nk, L;
                     int64_t tb;
                     tile_bounds(nk, L, tb);
-                    if (static_cast<int>(e.jkind) % L == 0) {
-                        gstore<int32_t>(a.tiles_k + tb, e.jkind / static_cast<uint32_t>(L),
+                    // Does the entry start a tile (and which)? A power-of-two tile length (a uniform
+                    // test) takes a mask and a shift instead of a division.
+                    const uint32_t uL = static_cast<uint32_t>(L);
+                    bool tile_start;
+                    uint32_t ti;
+                    if ((uL & (uL - 1u)) == 0u) {
+                        tile_start = (e.jkind & (uL - 1u)) == 0u;
+                        ti = e.jkind >> __builtin_ctz(uL);
+                    } else {
+                        tile_start = e.jkind % uL == 0u;
+                        ti = e.jkind / uL;
+                    }
+                    if (tile_start) {
+                        gstore<int32_t>(a.tiles_k + tb, ti,
                                         (elem & kFirst) ? static_cast<int>(e.jkind)
                                                         : min(static_cast<int>(e.jkind + e.acnt + 1u), nk));
                     }

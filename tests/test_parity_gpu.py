@@ -177,11 +177,14 @@ def test_edge_shapes(case):
 
 
 def test_tile_len_variants():
-    wl = W.make(1, steps=1)
-    for L in (1, 32, 100, 4096):
-        shape, out = H.run_phase1(wl, tile_len=L)
-        ref = H.oracle_phase1(wl, list(range(wl.N)), tile_len=L)
-        H.assert_exact("tiles_k L=%d" % L, out["tiles_k"].cpu().numpy(), ref["tiles_k"])
+    # Powers of two (a mask and a shift in the kernel) and other lengths (a division), at 4 and at
+    # 16 items per thread (workloads 1 and 2).
+    for idx, lens in ((1, (1, 32, 100, 4096)), (2, (1, 100, 384))):
+        wl = W.make(idx, steps=1)
+        for L in lens:
+            shape, out = H.run_phase1(wl, tile_len=L)
+            ref = H.oracle_phase1(wl, list(range(wl.N)), tile_len=L)
+            H.assert_exact("tiles_k w%d L=%d" % (idx, L), out["tiles_k"].cpu().numpy(), ref["tiles_k"])
 
 
 def test_empty_call():
