@@ -1346,9 +1346,10 @@ __global__ void __launch_bounds__(kPairThreads) p1_pairs_kernel(PairArgs a) {
             const int j0 = (e - ii * c4) << 2;
             // Cells past the triangle read as zeros: the row padding is never written, and A's
             // diagonal cell is never written either.
-            float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (j0 <= ii) v4 = *reinterpret_cast<const float4*>(tri + tri_row(ii) + j0);
-            reinterpret_cast<float4*>(out + ob)[e] = v4;
+            f32x4 v4 = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (j0 <= ii) v4 = *reinterpret_cast<const f32x4*>(tri + tri_row(ii) + j0);
+            // Non-temporal: the matrices stream past the caches (nothing in the step reads them back).
+            __builtin_nontemporal_store(v4, reinterpret_cast<f32x4*>(out + ob) + e);
         }
     } else {
         for (int e = threadIdx.x; e < C * C; e += kPairThreads) {
