@@ -27,6 +27,13 @@ __device__ __forceinline__ void gstore(const void* base, uint32_t i, T v) {
     reinterpret_cast<GT*>(reinterpret_cast<uintptr_t>(base))[i] = v;
 }
 
+// The same store marked non-temporal (outputs that nothing in the step reads back).
+template <typename T>
+__device__ __forceinline__ void gstore_nt(const void* base, uint32_t i, T v) {
+    typedef __attribute__((address_space(1))) T GT;
+    __builtin_nontemporal_store(v, reinterpret_cast<GT*>(reinterpret_cast<uintptr_t>(base)) + i);
+}
+
 // Value-typed outputs (cpe, k_eff, q_w) with bfloat16 values: the float32 result rounded to
 // bfloat16, nearest even.
 __device__ __forceinline__ uint32_t bf16_rn(float x) { return f32_to_bf16_rne(x); }
@@ -45,10 +52,10 @@ __device__ __forceinline__ void store_val(const void* base, uint32_t i, float v,
     if (bf) gstore<uint16_t>(base, i, static_cast<uint16_t>(bf16_rn(v)));
     else gstore<float>(base, i, v);
 }
-// Entries 4 i4 .. 4 i4 + 3.
+// Entries 4 i4 .. 4 i4 + 3 (non-temporal stores).
 __device__ __forceinline__ void store_val4(const void* base, uint32_t i4, f32x4 v, int bf) {
-    if (bf) gstore<u32x2>(base, i4, u32x2{bf16_rn(v.x) | bf16_rn(v.y) << 16, bf16_rn(v.z) | bf16_rn(v.w) << 16});
-    else gstore<f32x4>(base, i4, v);
+    if (bf) gstore_nt<u32x2>(base, i4, u32x2{bf16_rn(v.x) | bf16_rn(v.y) << 16, bf16_rn(v.z) | bf16_rn(v.w) << 16});
+    else gstore_nt<f32x4>(base, i4, v);
 }
 
 // r / (W + R) for entry indices r < 2^17 and W + R <= 512 (multiply-high by a rounded-up

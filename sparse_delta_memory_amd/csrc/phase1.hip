@@ -790,15 +790,16 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                     const uint32_t wc = (m >> kMetaWalkShift) & 3u;
                     iw[u] = (m & kMetaPos) | (wc == 1u ? kInvWalk : 0u) | (wc == 2u ? kInvHot : 0u);
                 }
-                if (vec && cnt == 4) {
+                if (vec && cnt == 4) {   // (non-temporal: nothing in the step reads these fields back;
+                                         // the pair kernel reads inv_k, which keeps plain stores)
                     const uint32_t g4 = g / 4;
-                    if (log_k != nullptr) gstore<f32x4>(log_k, g4, L4);
-                    if (rex_o != nullptr) gstore<f32x4>(rex_o, g4, X4);
+                    if (log_k != nullptr) gstore_nt<f32x4>(log_k, g4, L4);
+                    if (rex_o != nullptr) gstore_nt<f32x4>(rex_o, g4, X4);
                     if (cpe_o != nullptr) store_val4(cpe_o, g4, cp, VBF);
                     if (k_eff != nullptr) store_val4(k_eff, g4, ke, VBF);
-                    if (pos_k != nullptr) gstore<u32x4>(pos_k, g4, ps);
-                    if (is_last != nullptr) gstore<uint32_t>(is_last, g4, fl);
-                    if (is_only != nullptr) gstore<uint32_t>(is_only, g4, fo);
+                    if (pos_k != nullptr) gstore_nt<u32x4>(pos_k, g4, ps);
+                    if (is_last != nullptr) gstore_nt<uint32_t>(is_last, g4, fl);
+                    if (is_only != nullptr) gstore_nt<uint32_t>(is_only, g4, fo);
                     if (inv_k != nullptr) gstore<u32x2>(inv_k, g4, u32x2{iw[0] | iw[1] << 16, iw[2] | iw[3] << 16});
                 } else {
 #pragma unroll
@@ -857,11 +858,11 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                 }
                 if (vec && cnt == 4) {
                     const uint32_t g4 = g / 4;
-                    if (log_q != nullptr) gstore<f32x4>(log_q, g4, L4);
+                    if (log_q != nullptr) gstore_nt<f32x4>(log_q, g4, L4);
                     if (q_w != nullptr) store_val4(q_w, g4, qw, VBF);
-                    if (pos_q != nullptr) gstore<u32x4>(pos_q, g4, ps);
-                    if (q_last != nullptr) gstore<uint32_t>(q_last, g4, fl);
-                    if (q_only != nullptr) gstore<uint32_t>(q_only, g4, fo);
+                    if (pos_q != nullptr) gstore_nt<u32x4>(pos_q, g4, ps);
+                    if (q_last != nullptr) gstore_nt<uint32_t>(q_last, g4, fl);
+                    if (q_only != nullptr) gstore_nt<uint32_t>(q_only, g4, fo);
                     if (inv_q != nullptr) gstore<u32x2>(inv_q, g4, u32x2{iw[0] | iw[1] << 16, iw[2] | iw[3] << 16});
                 } else {
 #pragma unroll
