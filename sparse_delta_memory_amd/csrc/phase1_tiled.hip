@@ -1,8 +1,8 @@
 // Phase 1 of a chunk through the tiled path: rows longer than one workgroup sorts on chip (up to
 // 2^17 entries), or any row when the shape asks for it (shape->tiled).
 //
-// One 1024-thread workgroup per chunk works from global memory (the workspace) in tiles of 16384
-// entries, 16 per thread:
+// One 1024-thread workgroup per chunk works from global memory (the workspace) in tiles of 8192
+// entries, 8 per thread:
 //   1. keys: every entry's key (its local slot, or the invalid key for a masked token) and its entry
 //      index go to buffer 0;
 //   2. a stable LSD radix sort between the two buffers, passes of at most 6 key bits. Per pass,
