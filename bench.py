@@ -33,8 +33,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_BYTES = 8.0e12
 METRIC = "Phase-1 K+Q entries/sec and DW bank GB/s (fraction of HBM roofline), 1 GPU"
 KERNEL_SOURCES = {   # the files each kernel's code comes from (traffic counters are keyed on them)
-    "p1_main_kernel": ["phase1.hip", "sdm_device.hpp"],
-    "p1_pairs_kernel": ["phase1.hip", "sdm_device.hpp"],
+    "p1_main_kernel": ["phase1.hip", "p1_scan.hpp", "sdm_device.hpp"],
+    "p1_pairs_kernel": ["phase1.hip", "p1_scan.hpp", "sdm_device.hpp"],
     "dw_kernel": ["dw.hip", "sdm_device.hpp"],
     "read_gather_kernel": ["read.hip", "sdm_device.hpp"],
     "read_solve_kernel": ["read.hip", "sdm_device.hpp"],
