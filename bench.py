@@ -259,9 +259,9 @@ def main():
     # --pair-stream: the pair sums (A, QK) feed nothing in the step and DW needs only the sort/scan
     # kernel's records, so the pair kernel may run on a second stream (default priority, like every
     # stream here) beside the DW launches; the launch stream waits for it at the end of the step.
-    # Measured: Zipf 0.81 -> 0.77 ms per step, large_ragged 2.084 -> 2.067, but uniform 0.186 ->
-    # 0.217 and wide rows 0.408 -> 0.424 (the pair kernel then competes with DW for the compute
-    # units), so one stream stays the default.
+    # Measured: Zipf 0.81 -> 0.77 ms per step, but uniform 0.186 -> 0.217, wide rows 0.408 -> 0.424
+    # and large_ragged 2.004 -> 2.006 (the pair kernel then competes with DW for the compute units),
+    # so one stream stays the default.
     side = torch.cuda.Stream(device=dev)
     p1_done = torch.cuda.Event()
     pairs_done = torch.cuda.Event()
