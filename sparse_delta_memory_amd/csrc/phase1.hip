@@ -645,10 +645,16 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                         // spilled into vector lanes).
                         const int ek = r - imul(t, R);
                         if constexpr (IPT >= 16) {
+                            // (a sweep of one kind loads only that kind's values: the others are
+                            // never used in it)
                             using VT = std::conditional_t<VBF, uint16_t, float>;
-                            const VT* vp = q ? static_cast<const VT*>(a.q_val) + cr + imul(t, R) + (j - W)
-                                             : static_cast<const VT*>(a.k_val) + cw + ek;
-                            vl[k] = load_val(vp, 0, VBF);
+                            if ((sk && !sq && q) || (sq && !sk && !q)) {
+                                vl[k] = 0.0f;
+                            } else {
+                                const VT* vp = q ? static_cast<const VT*>(a.q_val) + cr + imul(t, R) + (j - W)
+                                                 : static_cast<const VT*>(a.k_val) + cw + ek;
+                                vl[k] = load_val(vp, 0, VBF);
+                            }
                         } else {
                             const int64_t e = q ? cr + (r - imul(t + 1, W)) : cw + ek;
                             const uintptr_t vb = q ? reinterpret_cast<uintptr_t>(a.q_val) : reinterpret_cast<uintptr_t>(a.k_val);
