@@ -555,7 +555,9 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
             e.bcnt = e.q ? ((before.f >> 16) & 0x7FFFu) : (before.f & 0xFFFFu);
             e.acnt = e.q ? ((afts[k] >> 16) & 0x7FFFu) : (afts[k] & 0xFFFFu);
             e.jkind = e.q ? jq : jk;
-            e.v = vl[k];
+            // (an invalid token's value, which may be anything, is dropped here, where the entry is
+            // first used: a select right after the loads would wait for them before the recompute)
+            e.v = e.valid ? vl[k] : 0.0f;
             // Same token and kind as the previous position (inside the group): not a run start.
             const uint32_t pr = k ? (rr[k - 1] & kRMask) : prev_r;
             const int pt = token_of_entry(static_cast<int>(pr), a.wr_magic);
@@ -661,15 +663,6 @@ __global__ void __launch_bounds__(kNT) p1_main_kernel(P1Args a) {
                             vl[k] = load_val(reinterpret_cast<const void*>(vb), e, VBF);
                         }
                         if constexpr (sk) kid[k] = static_cast<int32_t>(load_id<ID64>(a.k_idx, cw + ((!q && t < tv) ? ek : 0)));
-                    }
-                }
-                if (!res) {
-#pragma unroll
-                    for (int k = 0; k < kTileItems; ++k) {   // invalid tokens' values are not used
-                        const int p = p0 + k;
-                        const uint32_t sv = sval[in_row(p)];
-                    const int r = p < n ? static_cast<int>(sv & kRMask) : 0;
-                        vl[k] = (p < n && token_of_entry(r, a.wr_magic) < tv) ? vl[k] : 0.0f;
                     }
                 }
             }
